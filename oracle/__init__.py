@@ -1,0 +1,155 @@
+"""CPU oracle for MXFP4 fake quantization -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
+this package.  The product path (mxfp4_fake_quantization_amd) never does.
+
+Thin ctypes wrapper over liboracle.so (mxfp4_oracle.c).  Arrays are numpy:
+bf16 tensors are carried as uint16 bit patterns, fp32 as float32.  Masks are
+one bool per element (the pages' saturation mask is a bool tensor).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F32, BF16 = 0, 1
+FLOOR, AMCT = 0, 1
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        # MXFP4_ORACLE_LIB points the wrapper at another build of the oracle
+        # (used by the mutation test, which plants mistakes in a copy).
+        path = os.environ.get("MXFP4_ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and (not os.path.exists(path)
+                                   or os.path.getmtime(path) < os.path.getmtime(_build.SRC)):
+            _build.build()
+        lib = ctypes.CDLL(path)
+        i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+        lib.oracle_qdq_rows.argtypes = [i32, i64, i64, i32, i32, f32, vp, vp, vp, vp]
+        lib.oracle_qdq_cols.argtypes = [i32, i64, i64, i32, i32, f32, vp, vp, vp, vp]
+        lib.oracle_grouped_cols.argtypes = [i32, i64, i64, i32, i32, f32, vp, vp, i32, i32,
+                                            vp, vp, vp]
+        lib.oracle_ste_bwd.argtypes = [i32, i64, vp, vp, vp]
+        lib.oracle_pack_rows.argtypes = [i32, i64, i64, i32, i32, f32, vp, vp, vp]
+        lib.oracle_unpack_rows.argtypes = [i32, i64, i64, i32, vp, vp, vp]
+        for fn in ("oracle_qdq_rows", "oracle_qdq_cols", "oracle_grouped_cols",
+                   "oracle_ste_bwd", "oracle_pack_rows", "oracle_unpack_rows"):
+            getattr(lib, fn).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _dtype_code(x: np.ndarray) -> int:
+    if x.dtype == np.float32:
+        return F32
+    if x.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle arrays are float32 or uint16 (bf16 bits), got {x.dtype}")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _rule_code(rule) -> int:
+    if rule in (FLOOR, "floor"):
+        return FLOOR
+    if rule in (AMCT, "amct"):
+        return AMCT
+    raise ValueError(f"unknown rule {rule!r}")
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"{what}: oracle returned {rc}")
+
+
+def qdq_rows(x: np.ndarray, block: int = 32, rule="floor", scale_factor: float = 6.0):
+    """Row-wise QDQ of a 2-D array.  Returns (y, clip_bool, e8m0)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    nb = -(-cols // block)
+    y = np.empty_like(x)
+    clip = np.empty((rows, cols), np.uint8)
+    e8 = np.empty((rows, nb), np.uint8)
+    _check(_load().oracle_qdq_rows(_dtype_code(x), rows, cols, block, _rule_code(rule),
+                                   scale_factor, _ptr(x), _ptr(y), _ptr(clip), _ptr(e8)),
+           "qdq_rows")
+    return y, clip.astype(bool), e8
+
+
+def qdq_cols(x: np.ndarray, block: int = 32, rule="floor", scale_factor: float = 6.0):
+    """Column-wise QDQ (blocks along dim 0).  Returns (y, clip_bool, e8m0)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    nb = -(-rows // block)
+    y = np.empty_like(x)
+    clip = np.empty((rows, cols), np.uint8)
+    e8 = np.empty((nb, cols), np.uint8)
+    _check(_load().oracle_qdq_cols(_dtype_code(x), rows, cols, block, _rule_code(rule),
+                                   scale_factor, _ptr(x), _ptr(y), _ptr(clip), _ptr(e8)),
+           "qdq_cols")
+    return y, clip.astype(bool), e8
+
+
+def grouped_cols(x: np.ndarray, group_list, block: int = 32, rule="floor",
+                 scale_factor: float = 6.0, list_type: int = 1):
+    """Grouped column-wise QDQ.  Returns (y, clip_bool, e8m0[block_rows, cols]).
+
+    Rows past the groups' total keep y = x's bits and clip = False (untouched)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    gl = np.ascontiguousarray(np.asarray(group_list, dtype=np.int64))
+    counts = gl if list_type == 1 else np.diff(np.concatenate([[0], gl]))
+    nbt = int(sum(-(-int(c) // block) for c in counts if c > 0))
+    y = x.copy()
+    clip = np.zeros((rows, cols), np.uint8)
+    e8 = np.empty((nbt, cols), np.uint8)
+    _check(_load().oracle_grouped_cols(_dtype_code(x), rows, cols, block, _rule_code(rule),
+                                       scale_factor, _ptr(x), _ptr(gl), len(gl), list_type,
+                                       _ptr(y), _ptr(clip), _ptr(e8)),
+           "grouped_cols")
+    return y, clip.astype(bool), e8
+
+
+def ste_bwd(grad_out: np.ndarray, clip=None):
+    """Clipped STE backward (clip given) or plain STE (clip None)."""
+    g = np.ascontiguousarray(grad_out)
+    out = np.empty_like(g)
+    c = None if clip is None else np.ascontiguousarray(clip, dtype=np.uint8)
+    _check(_load().oracle_ste_bwd(_dtype_code(g), g.size, _ptr(g), _ptr(c), _ptr(out)),
+           "ste_bwd")
+    return out
+
+
+def pack_rows(x: np.ndarray, block: int = 32, rule="floor", scale_factor: float = 6.0):
+    """Packed row-wise quantization.  Returns (codes[rows, ceil(cols/2)], e8m0)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    codes = np.empty((rows, (cols + 1) // 2), np.uint8)
+    e8 = np.empty((rows, -(-cols // block)), np.uint8)
+    _check(_load().oracle_pack_rows(_dtype_code(x), rows, cols, block, _rule_code(rule),
+                                    scale_factor, _ptr(x), _ptr(codes), _ptr(e8)),
+           "pack_rows")
+    return codes, e8
+
+
+def unpack_rows(codes: np.ndarray, scales: np.ndarray, cols: int, block: int = 32,
+                dtype=np.uint16):
+    """Decode packed codes + E8M0 scales back to values of `dtype`."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows = codes.shape[0]
+    y = np.empty((rows, cols), dtype)
+    _check(_load().oracle_unpack_rows(_dtype_code(y), rows, cols, block, _ptr(codes),
+                                      _ptr(scales), _ptr(y)),
+           "unpack_rows")
+    return y

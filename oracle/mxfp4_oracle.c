@@ -1,0 +1,293 @@
+/*
+ * mxfp4_oracle.c -- plain, slow, single-threaded CPU oracle for MXFP4 fake
+ * quantization.  TEST INFRASTRUCTURE ONLY: nothing on the product path may
+ * link, load or call it; only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py use it.  It shares no code with the HIP
+ * library (mxfp4_fake_quantization_amd/csrc).
+ *
+ * What it computes follows the pages of the "MXFP4 QAT fake-quant Linear (with
+ * STE)" pull request (gitcode cann/amct #264):
+ *   - README "1. MXFP4 and STE": per-block power-of-two scale, E2M1 codebook
+ *     {0, .5, 1, 1.5, 2, 3, 4, 6}, plain and clipped STE formulas;
+ *   - fake_quant.py _block_view/_unpad (zero padding of the last dim per row,
+ *     so blocks never straddle rows), _block_scale, _round_to_e2m1 (midpoint
+ *     thresholds), _quant_dequant_torch (divide, snap, sign, multiply, cast),
+ *     mxfp4_saturation_mask (|x| > 6*scale) and _MXFP4FakeQuantSTE.backward
+ *     (masked_fill of the gradient with 0).
+ * The grouped (per-expert) column-wise blocking follows the MindSpore
+ * hyper-parallel page "fake_w4a8_gmm_func.py" (normalize_group_list: counts
+ * -> cumulative sums), and the packed form follows the sglang "mxfp4_npu.py"
+ * page (two FP4 codes per byte).
+ *
+ * Two scale rules ("profiles"):
+ *   FLOOR (default): k = floor(log2 amax) - 2, clamped below at -127; an
+ *                    all-zero block takes k = -127.  Midpoint ties go to the
+ *                    lower-magnitude code (a value is snapped by counting the
+ *                    midpoints it strictly exceeds).
+ *   AMCT:            r = fl32(amax / scale_factor), r = max(r, 2^-30),
+ *                    k = nearest integer to log2(r) (fake_quant.py
+ *                    _block_scale).  Ties go to the higher-magnitude code,
+ *                    as torch.bucketize(..., right=True) does.
+ *
+ * Arithmetic: every input element is widened exactly to double.  Division by
+ * 2^k, the midpoint comparisons and the product code*2^k are exact in double,
+ * and every produced value is exactly representable in the output dtype, so
+ * the final narrowing cast does not round.  The only rounded operation of the
+ * method is AMCT's fp32 quotient amax/scale_factor, done here in float as the
+ * pages do it (fp32 tensors).  Built without fast-math (see build.py).
+ *
+ * Signs: the pages multiply torch.sign(x/scale) by the code.  sign(+-0) is +0,
+ * so a zero input gives +0.0, while a negative input that snaps to code 0
+ * gives -0.0.  This oracle writes that out literally.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+#define OR_FLOOR 0
+#define OR_AMCT 1
+
+/* E2M1 codebook and the midpoints between adjacent entries (fake_quant.py
+ * module constants; README section 1). */
+static const double kCodes[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+static const double kMids[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+/* Largest E2M1 magnitude: the clip limit is 6*scale (MXFP4_E2M1_MAX). */
+static const double kE2M1Max = 6.0;
+/* Smallest raw scale of the AMCT rule (_MIN_SCALE_RAW = 2^-30). */
+static const float kMinScaleRaw = 0x1p-30f;
+
+/* ---- element access ------------------------------------------------------ */
+
+static double get_elem(int dtype, const void *p, int64_t i) {
+  if (dtype == OR_F32) return (double)((const float *)p)[i];
+  /* bf16 is the upper half of an IEEE binary32: widening is exact. */
+  uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static void put_elem(int dtype, void *p, int64_t i, double v) {
+  float f = (float)v; /* exact for every value this oracle produces */
+  if (dtype == OR_F32) {
+    ((float *)p)[i] = f;
+    return;
+  }
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  /* binary32 -> bf16 with round-to-nearest-even (exact here as well). */
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  ((uint16_t *)p)[i] = (uint16_t)(u >> 16);
+}
+
+/* ---- the per-block method ------------------------------------------------ */
+
+/* FLOOR: the shared exponent is floor(log2 amax) minus E2M1's emax (2). */
+static int scale_exp_floor(double amax) {
+  if (amax == 0.0) return -127;
+  int e;
+  (void)frexp(amax, &e); /* amax = f * 2^e with f in [0.5, 1): floor(log2) = e-1 */
+  int k = (e - 1) - 2;
+  return k < -127 ? -127 : k;
+}
+
+/* AMCT: power of two nearest to max(fl32(amax/sf), 2^-30) in the log domain.
+ * log2(r) of a binary32 r is never a half-integer (that would need
+ * r = 2^(k+1/2), irrational), and its distance to the nearest half-integer is
+ * far above double log2's error, so lround(log2(r)) is the exact answer. */
+static int scale_exp_amct(double amax, float sf) {
+  float r = (float)amax / sf; /* amax is a binary32 value: the cast is exact */
+  if (r < kMinScaleRaw) r = kMinScaleRaw;
+  return (int)lround(log2((double)r));
+}
+
+/*
+ * Quantize-dequantize one block.  idx[] lists the n element positions of the
+ * block in x/y (row-wise: consecutive columns; column-wise: consecutive rows).
+ * Outputs (each optional): y (same dtype), clip (1 byte per element, the
+ * saturation mask), nib (E2M1 nibble per element: sign<<3 | magnitude code).
+ * Returns k, the block's scale exponent (scale = 2^k).
+ */
+static int qdq_block(int dtype, int rule, float sf, const void *x,
+                     const int64_t *idx, int n, void *y, uint8_t *clip,
+                     uint8_t *nib) {
+  double amax = 0.0;
+  for (int j = 0; j < n; ++j) {
+    double a = fabs(get_elem(dtype, x, idx[j]));
+    if (a > amax) amax = a;
+  }
+  int k = (rule == OR_FLOOR) ? scale_exp_floor(amax) : scale_exp_amct(amax, sf);
+  double scale = ldexp(1.0, k);
+  for (int j = 0; j < n; ++j) {
+    double v = get_elem(dtype, x, idx[j]);
+    double q_in = v / scale; /* exact: division by a power of two */
+    double mag = fabs(q_in);
+    int code = 0; /* number of midpoints passed = index of the E2M1 code */
+    for (int i = 0; i < 7; ++i) {
+      int passed = (rule == OR_FLOOR) ? (mag > kMids[i]) : (mag >= kMids[i]);
+      code += passed;
+    }
+    double sgn = q_in > 0.0 ? 1.0 : (q_in < 0.0 ? -1.0 : 0.0); /* torch.sign */
+    double q = sgn * kCodes[code];
+    if (sgn == 0.0) q = 0.0; /* sign(+-0) * 0 is +0 */
+    double out = q * scale;
+    if (y) put_elem(dtype, y, idx[j], out);
+    if (clip) clip[idx[j]] = (uint8_t)(fabs(v) > kE2M1Max * scale);
+    if (nib) nib[idx[j]] = (uint8_t)((signbit(out) ? 8 : 0) | code);
+  }
+  return k;
+}
+
+/* ---- exported drivers ---------------------------------------------------- */
+
+/* Row-wise: blocks of `block` consecutive elements along each row of the
+ * rows x cols row-major tensor; the last block of a row may be shorter.
+ * e8m0 (optional) is [rows, ceil(cols/block)] with byte = k + 127. */
+int oracle_qdq_rows(int dtype, int64_t rows, int64_t cols, int block, int rule,
+                    float sf, const void *x, void *y, uint8_t *clip,
+                    uint8_t *e8m0) {
+  if (block <= 0 || rows < 0 || cols < 0) return 1;
+  int64_t nb = (cols + block - 1) / block;
+  int64_t *idx = (int64_t *)malloc(sizeof(int64_t) * (size_t)block);
+  if (!idx) return 2;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      int64_t c0 = b * block;
+      int n = (int)((cols - c0) < block ? (cols - c0) : block);
+      for (int j = 0; j < n; ++j) idx[j] = r * cols + c0 + j;
+      int k = qdq_block(dtype, rule, sf, x, idx, n, y, clip, NULL);
+      if (e8m0) e8m0[r * nb + b] = (uint8_t)(k + 127);
+    }
+  }
+  free(idx);
+  return 0;
+}
+
+/* Column-wise: blocks of `block` consecutive rows of one column.  y keeps the
+ * row-major rows x cols layout; e8m0 (optional) is [ceil(rows/block), cols]. */
+int oracle_qdq_cols(int dtype, int64_t rows, int64_t cols, int block, int rule,
+                    float sf, const void *x, void *y, uint8_t *clip,
+                    uint8_t *e8m0) {
+  if (block <= 0 || rows < 0 || cols < 0) return 1;
+  int64_t nb = (rows + block - 1) / block;
+  int64_t *idx = (int64_t *)malloc(sizeof(int64_t) * (size_t)block);
+  if (!idx) return 2;
+  for (int64_t b = 0; b < nb; ++b) {
+    int64_t r0 = b * block;
+    int n = (int)((rows - r0) < block ? (rows - r0) : block);
+    for (int64_t c = 0; c < cols; ++c) {
+      for (int j = 0; j < n; ++j) idx[j] = (r0 + j) * cols + c;
+      int k = qdq_block(dtype, rule, sf, x, idx, n, y, clip, NULL);
+      if (e8m0) e8m0[b * cols + c] = (uint8_t)(k + 127);
+    }
+  }
+  free(idx);
+  return 0;
+}
+
+/* Grouped column-wise: the rows are split into num_groups consecutive groups
+ * given by group_list (list_type 1: row counts; 0: cumulative row ends, as
+ * normalize_group_list accepts).  Column-wise blocks restart at every group
+ * start and never cross a group boundary; a group's last block may be short.
+ * e8m0 (optional) has one row per block-row: block-rows are numbered group by
+ * group, block by block, i.e. [sum_g ceil(c_g/block), cols].
+ * Rows past the last group's end are not touched.  Returns 1 when the groups
+ * are inconsistent (negative count, decreasing ends, or past `rows`). */
+int oracle_grouped_cols(int dtype, int64_t rows, int64_t cols, int block,
+                        int rule, float sf, const void *x,
+                        const int64_t *group_list, int num_groups,
+                        int list_type, void *y, uint8_t *clip, uint8_t *e8m0) {
+  if (block <= 0 || rows < 0 || cols < 0 || num_groups < 1) return 1;
+  int64_t *idx = (int64_t *)malloc(sizeof(int64_t) * (size_t)block);
+  if (!idx) return 2;
+  int64_t start = 0, brow = 0;
+  for (int g = 0; g < num_groups; ++g) {
+    int64_t end = list_type == 1 ? start + group_list[g] : group_list[g];
+    if (end < start || end > rows) {
+      free(idx);
+      return 1;
+    }
+    for (int64_t r0 = start; r0 < end; r0 += block, ++brow) {
+      int n = (int)((end - r0) < block ? (end - r0) : block);
+      for (int64_t c = 0; c < cols; ++c) {
+        for (int j = 0; j < n; ++j) idx[j] = (r0 + j) * cols + c;
+        int k = qdq_block(dtype, rule, sf, x, idx, n, y, clip, NULL);
+        if (e8m0) e8m0[brow * cols + c] = (uint8_t)(k + 127);
+      }
+    }
+    start = end;
+  }
+  free(idx);
+  return 0;
+}
+
+/* Straight-through estimator backward: clipped (clip != NULL) zeroes the
+ * gradient where the forward saturated (masked_fill with 0.0, i.e. +0);
+ * plain (clip == NULL) passes the gradient through unchanged. */
+int oracle_ste_bwd(int dtype, int64_t n, const void *grad_out,
+                   const uint8_t *clip, void *grad_in) {
+  for (int64_t i = 0; i < n; ++i) {
+    double g = get_elem(dtype, grad_out, i);
+    if (clip && clip[i]) g = 0.0;
+    put_elem(dtype, grad_in, i, g);
+  }
+  return 0;
+}
+
+/* Real (packed) row-wise quantization: codes is [rows, ceil(cols/2)] bytes,
+ * element 2t in the low nibble and 2t+1 in the high nibble (an odd row's last
+ * high nibble is 0); a nibble is sign<<3 | E2M1 magnitude code.  scales is
+ * [rows, ceil(cols/block)] E8M0 bytes (k + 127). */
+int oracle_pack_rows(int dtype, int64_t rows, int64_t cols, int block, int rule,
+                     float sf, const void *x, uint8_t *codes, uint8_t *scales) {
+  if (block <= 0 || rows < 0 || cols < 0) return 1;
+  int64_t nb = (cols + block - 1) / block;
+  int64_t half = (cols + 1) / 2;
+  uint8_t *nib = (uint8_t *)calloc((size_t)(rows * cols) + 1, 1);
+  int64_t *idx = (int64_t *)malloc(sizeof(int64_t) * (size_t)block);
+  if (!nib || !idx) {
+    free(nib);
+    free(idx);
+    return 2;
+  }
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      int64_t c0 = b * block;
+      int n = (int)((cols - c0) < block ? (cols - c0) : block);
+      for (int j = 0; j < n; ++j) idx[j] = r * cols + c0 + j;
+      int k = qdq_block(dtype, rule, sf, x, idx, n, NULL, NULL, nib);
+      scales[r * nb + b] = (uint8_t)(k + 127);
+    }
+    for (int64_t t = 0; t < half; ++t) {
+      uint8_t lo = nib[r * cols + 2 * t];
+      uint8_t hi = (2 * t + 1 < cols) ? nib[r * cols + 2 * t + 1] : 0;
+      codes[r * half + t] = (uint8_t)(lo | (hi << 4));
+    }
+  }
+  free(nib);
+  free(idx);
+  return 0;
+}
+
+/* Decode the packed form: value = (-1)^s * code[m] * 2^(e8m0 - 127). */
+int oracle_unpack_rows(int dtype, int64_t rows, int64_t cols, int block,
+                       const uint8_t *codes, const uint8_t *scales, void *y) {
+  if (block <= 0 || rows < 0 || cols < 0) return 1;
+  int64_t nb = (cols + block - 1) / block;
+  int64_t half = (cols + 1) / 2;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t c = 0; c < cols; ++c) {
+      uint8_t byte = codes[r * half + c / 2];
+      uint8_t nibble = (c & 1) ? (byte >> 4) : (byte & 15);
+      int k = (int)scales[r * nb + c / block] - 127;
+      double v = kCodes[nibble & 7] * ldexp(1.0, k);
+      if (nibble & 8) v = -v;
+      put_elem(dtype, y, r * cols + c, v);
+    }
+  }
+  return 0;
+}

@@ -1,0 +1,55 @@
+"""Mutation check of the oracle pins: each case plants one plausible mistake in
+a copy of the oracle source (a wrong comparison, exponent, clamp, constant,
+index or nibble order), builds it, and runs the pin suite against it.  Every
+mutant must make the pins fail; a surviving mutant means a gap in the pins."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "mxfp4_oracle.c")
+
+MUTANTS = {
+    "tie_rule_floor": ("(rule == OR_FLOOR) ? (mag > kMids[i])", "(rule == OR_FLOOR) ? (mag >= kMids[i])"),
+    "tie_rule_amct": (": (mag >= kMids[i])", ": (mag > kMids[i])"),
+    "floor_exponent": ("int k = (e - 1) - 2;", "int k = (e - 1) - 1;"),
+    "floor_clamp": ("return k < -127 ? -127 : k;", "return k < -126 ? -126 : k;"),
+    "amct_clamp": ("kMinScaleRaw = 0x1p-30f", "kMinScaleRaw = 0x1p-31f"),
+    "amct_round": ("return (int)lround(log2((double)r));", "return (int)floor(log2((double)r));"),
+    "codebook_value": ("{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}", "{0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 4.0, 6.0}"),
+    "midpoint_value": ("{0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0}", "{0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 4.5}"),
+    "mask_strictness": ("(fabs(v) > kE2M1Max * scale)", "(fabs(v) >= kE2M1Max * scale)"),
+    "clip_limit": ("static const double kE2M1Max = 6.0;", "static const double kE2M1Max = 4.0;"),
+    "sign_of_negative_zero_code": ("double q = sgn * kCodes[code];", "double q = (sgn < 0 && code == 0) ? 0.0 : sgn * kCodes[code];"),
+    # a short tail block that runs on into the next row (a flattened view)
+    "row_tail_crosses_rows": ("int n = (int)((cols - c0) < block ? (cols - c0) : block);\n      for (int j = 0; j < n; ++j) idx[j] = r * cols + c0 + j;",
+                              "int n = (int)((cols - c0) < block ? (cols - c0) : block);\n      if (n < block && r + 1 < rows) n += 1;\n      for (int j = 0; j < n; ++j) idx[j] = r * cols + c0 + j;"),
+    "column_index": ("for (int j = 0; j < n; ++j) idx[j] = (r0 + j) * cols + c;\n      int k = qdq_block(dtype, rule, sf, x, idx, n, y, clip, NULL);\n      if (e8m0) e8m0[b * cols + c]",
+                     "for (int j = 0; j < n; ++j) idx[j] = (r0 + j) * cols + (cols - 1 - c);\n      int k = qdq_block(dtype, rule, sf, x, idx, n, y, clip, NULL);\n      if (e8m0) e8m0[b * cols + c]"),
+    "group_restart": ("for (int64_t r0 = start; r0 < end; r0 += block, ++brow) {",
+                      "for (int64_t r0 = start; r0 < end; r0 = (r0 / block + 1) * block, ++brow) {"),
+    "ste_negative_zero": ("if (clip && clip[i]) g = 0.0;", "if (clip && clip[i]) g = -0.0;"),
+    "nibble_order": ("codes[r * half + t] = (uint8_t)(lo | (hi << 4));", "codes[r * half + t] = (uint8_t)(hi | (lo << 4));"),
+    "e8m0_bias": ("if (e8m0) e8m0[r * nb + b] = (uint8_t)(k + 127);", "if (e8m0) e8m0[r * nb + b] = (uint8_t)(k + 128);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_kill_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mutated = src.replace(old, new, 1)
+    csrc = tmp_path / "m.c"
+    csrc.write_text(mutated)
+    lib = tmp_path / "libm.so"
+    sys.path.insert(0, ROOT)
+    from oracle import build as B
+    subprocess.run(["gcc", *B.CFLAGS, str(csrc), "-o", str(lib), "-lm"], check=True)
+    env = dict(os.environ, MXFP4_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
