@@ -1,0 +1,321 @@
+"""Benchmark of the fused MXFP4 fake-quant hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S] [--all OUT.json]
+
+One step = the whole hot path over one batch of the weight_4k workload: bf16
+4096x4096 weight (N(0, 0.02^2), outliers, zero blocks, planted blocks),
+row-wise block-32 FLOOR QDQ forward emitting y and the clip bitmap, then the
+clipped-STE backward of a bf16 N(0,1) gradient.  Inputs are resident in HBM
+before the timed region; S buffer sets (default 8, >1 GiB in total) are used
+in rotation so every step reads data that is not in the 256 MB Infinity Cache.
+
+Prints one JSON line.  value = algorithmic bytes per second (GB/s = 1e9 B/s):
+forward reads x (2 B/elt) and writes y (2 B) + bitmap (1/8 B); backward reads
+g (2 B) + bitmap (1/8 B) and writes g_in (2 B).  roofline = the forward kernel
+against the 8 TB/s HBM peak, its duration from HIP events around every forward
+launch of the timed loop.  cpu_baseline = the CPU oracle (single thread) on
+the same workload, repeated for about 10 s.
+
+--all OUT.json additionally times the other workloads (full sizes) and a
+plain device copy, and writes them to OUT.json (stdout keeps one line).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_fwd_weight4k_traffic.json")
+KERNEL_SOURCES = ["mxfp4_fake_quantization_amd/csrc/row_kernels.hip",
+                  "mxfp4_fake_quantization_amd/csrc/mxfp4_device.h",
+                  "mxfp4_fake_quantization_amd/csrc/mxfp4_math.h"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(per_launch_alg_bytes: float):
+    """HBM bytes per forward launch from the committed rocprofv3 counter run
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
+    when the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return float(t["traffic_bytes_per_launch"])
+
+
+class Call:
+    """A pre-marshalled C-ABI call (argument tuple built once)."""
+
+    def __init__(self, fn, *args):
+        self.fn, self.args = fn, args
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            import mxfp4_fake_quantization_amd as M
+            raise RuntimeError(M.mxfp4_last_error())
+
+
+def cpu_baseline(x, g, min_seconds=10.0):
+    import oracle
+    rows, cols = x.shape
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        _, clip, _ = oracle.qdq_rows(x, 32, "floor")
+        oracle.ste_bwd(g, clip)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    nbytes = rows * cols * 8.25
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole weight_4k workload ({rows}x{cols} bf16 fwd+bwd), {reps} reps, "
+                      f"{dt * 1e3:.1f} ms per step, single-threaded C oracle"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--sets", type=int, default=8)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--all", metavar="OUT", default=None)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run only a 512 MiB device copy (rocprofv3 counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the hot path has no "
+              "cross-GPU step, and this build runs on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import mxfp4_fake_quantization_amd as M
+
+    if args.calib_copy:
+        a = torch.empty(256 << 20, dtype=torch.int16, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": a.numel() * 2, "calib_copy_bytes_written": a.numel() * 2}))
+        return
+
+    lib = M._load()
+    x_np, g_np, _ = W.weight_4k()
+    rows, cols = x_np.shape
+    n = rows * cols
+    fwd_bytes = n * (2 + 2 + 1 / 8)
+    bwd_bytes = n * (2 + 1 / 8 + 2)
+    step_bytes = fwd_bytes + bwd_bytes
+
+    xs, gs, ys, ms, gis = [], [], [], [], []
+    x0 = torch.from_numpy(x_np).view(torch.bfloat16).cuda()
+    g0 = torch.from_numpy(g_np).view(torch.bfloat16).cuda()
+    for s in range(args.sets):
+        xs.append(x0.clone())
+        gs.append(g0.clone())
+        ys.append(torch.empty_like(x0))
+        gis.append(torch.empty_like(g0))
+        ms.append(torch.empty((rows, cols // 32), dtype=torch.int32, device="cuda"))
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    desc = M._Desc(1, 32, 0, 0, rows, cols, 6.0, 0)
+    vp = ctypes.c_void_p
+    fwd = [Call(lib.mxfp4_qdq_fwd, ctypes.byref(desc), M.ROW, vp(xs[s].data_ptr()), vp(ys[s].data_ptr()),
+                vp(ms[s].data_ptr()), None, None, None, None, stream) for s in range(args.sets)]
+    bwd = [Call(lib.mxfp4_ste_bwd, ctypes.byref(desc), M.ROW, vp(gs[s].data_ptr()), vp(ms[s].data_ptr()),
+                vp(gis[s].data_ptr()), None, 0, 1, stream) for s in range(args.sets)]
+
+    for i in range(args.warmup):
+        fwd[i % args.sets]()
+        bwd[i % args.sets]()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record()
+    for i in range(K):
+        s = i % args.sets
+        e = ev[i]
+        e[0].record()
+        fwd[s]()
+        e[1].record()
+        e[2].record()
+        bwd[s]()
+        e[3].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t_start.elapsed_time(t_end)
+    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    ms_per_step = total_ms / K
+    value = step_bytes * K / (total_ms * 1e-3) / 1e9
+
+    fwd_avg_s = float(fwd_ms.mean()) * 1e-3
+    achieved = fwd_bytes / fwd_avg_s / 1e9
+    traffic = measured_traffic(fwd_bytes)
+    result = {
+        "metric": "fused MXFP4 QDQ+STE GB/s and % of MI355X HBM peak (1 GPU)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded weight_4k: N(0,0.02^2) + outliers, zero blocks, planted blocks)",
+        "config": {"workload": "weight_4k: bf16 4096x4096 row-wise block-32 QDQ fwd (y + clip "
+                               "bitmap) + clipped-STE bwd", "rows": rows, "cols": cols,
+                   "block": 32, "rule": "floor", "buffer_sets": args.sets,
+                   "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "elements_per_s": round(2 * n * K / (total_ms * 1e-3), 1),
+        "fwd_us": round(float(fwd_ms.mean()) * 1e3, 3),
+        "bwd_us": round(float(bwd_ms.mean()) * 1e3, 3),
+        "fwd_us_median": round(float(np.median(fwd_ms)) * 1e3, 3),
+        "bwd_us_median": round(float(np.median(bwd_ms)) * 1e3, 3),
+        "wall_s": round(wall, 4),
+        "roofline": {"bound": "hbm", "kernel": "row_fwd_kernel<bf16,32,floor,flat>",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "alg_bytes_per_launch": fwd_bytes},
+    }
+    if args.all:
+        result["other_workloads_file"] = args.all
+        other = bench_all(M, lib, W, torch, args)
+        with open(args.all, "w") as f:
+            json.dump(other, f, indent=1)
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(x_np, g_np)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def _time_calls(torch, calls, reps, warm=3):
+    for i in range(warm):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        evs[i][0].record()
+        calls[i % len(calls)]()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
+    return float(np.median(t)), float(t.min())
+
+
+def bench_all(M, lib, W, torch, args):
+    """Full-size runs of the other workloads (two buffer sets each, so
+    consecutive launches do not hit the same data) and a device copy."""
+    vp = ctypes.c_void_p
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = {}
+
+    def rec(name, nbytes, nelem, t):
+        med, best = t
+        out[name] = {"alg_bytes": nbytes, "median_us": round(med * 1e6, 2), "best_us": round(best * 1e6, 2),
+                     "GBps": round(nbytes / med / 1e9, 1), "pct_peak": round(100 * nbytes / med / 1e9 / HBM_PEAK_GBS, 2),
+                     "elements_per_s": round(nelem / med, 1)}
+
+    # plain device copy of 512 MiB (achievable-bandwidth context)
+    a = [torch.empty(256 << 20, dtype=torch.int16, device="cuda") for _ in range(2)]
+    b = [torch.empty_like(a[0]) for _ in range(2)]
+    rec("device_copy_512MiB", 2 * a[0].numel() * 2, a[0].numel(),
+        _time_calls(torch, [lambda i=i: b[i].copy_(a[i]) for i in range(2)], 20))
+    del a, b
+
+    def tens(np_arr):
+        return torch.from_numpy(np_arr).view(torch.bfloat16).cuda()
+
+    # row-wise fwd at the large weight shape (28672 x 8192)
+    xw = W.weight_pack()
+    R, C = xw.shape
+    xs = [tens(xw) for _ in range(2)]
+    ys = [torch.empty_like(xs[0]) for _ in range(2)]
+    mk = [torch.empty((R, C // 32), dtype=torch.int32, device="cuda") for _ in range(2)]
+    d = M._Desc(1, 32, 0, 0, R, C, 6.0, 0)
+    calls = [Call(lib.mxfp4_qdq_fwd, ctypes.byref(d), M.ROW, vp(xs[i].data_ptr()), vp(ys[i].data_ptr()),
+                  vp(mk[i].data_ptr()), None, None, None, None, stream) for i in range(2)]
+    rec("row_fwd_28672x8192_y_mask", R * C * 4.125, R * C, _time_calls(torch, calls, 30))
+    gis = ys
+    bcalls = [Call(lib.mxfp4_ste_bwd, ctypes.byref(d), M.ROW, vp(xs[i].data_ptr()), vp(mk[i].data_ptr()),
+                   vp(gis[i].data_ptr()), None, 0, 1, stream) for i in range(2)]
+    rec("ste_bwd_28672x8192", R * C * 4.125, R * C, _time_calls(torch, bcalls, 30))
+    # packed output, block 32 and 128
+    for blk in (32, 128):
+        codes = [torch.empty((R, C // 2), dtype=torch.uint8, device="cuda") for _ in range(2)]
+        scs = [torch.empty((R, C // blk), dtype=torch.uint8, device="cuda") for _ in range(2)]
+        dp = M._Desc(1, blk, 0, 0, R, C, 6.0, 0)
+        pcalls = [Call(lib.mxfp4_quant_pack, ctypes.byref(dp), vp(xs[i].data_ptr()), vp(codes[i].data_ptr()),
+                       vp(scs[i].data_ptr()), None, None, stream) for i in range(2)]
+        rec(f"pack_28672x8192_b{blk}", R * C * (2 + 0.5 + 1 / blk), R * C, _time_calls(torch, pcalls, 30))
+        del codes, scs
+    del xs, ys, mk
+
+    # dual direction (16384 x 8192)
+    xa = W.act_dual()
+    R, C = xa.shape
+    xs = [tens(xa) for _ in range(2)]
+    yr = [torch.empty_like(xs[0]) for _ in range(2)]
+    yc = [torch.empty_like(xs[0]) for _ in range(2)]
+    mr = [torch.empty((R, C // 32), dtype=torch.int32, device="cuda") for _ in range(2)]
+    mc = [torch.empty((R // 32, C), dtype=torch.int32, device="cuda") for _ in range(2)]
+    d = M._Desc(1, 32, 0, 0, R, C, 6.0, 0)
+    calls = [Call(lib.mxfp4_qdq_fwd, ctypes.byref(d), M.ROW | M.COL, vp(xs[i].data_ptr()), vp(yr[i].data_ptr()),
+                  vp(mr[i].data_ptr()), None, vp(yc[i].data_ptr()), vp(mc[i].data_ptr()), None, stream)
+             for i in range(2)]
+    rec("dual_16384x8192", R * C * 6.25, R * C, _time_calls(torch, calls, 30))
+    ccalls = [Call(lib.mxfp4_qdq_fwd, ctypes.byref(d), M.COL, vp(xs[i].data_ptr()), None, None, None,
+                   vp(yc[i].data_ptr()), vp(mc[i].data_ptr()), None, stream) for i in range(2)]
+    rec("col_16384x8192_y_mask", R * C * 4.125, R * C, _time_calls(torch, ccalls, 30))
+    del xs, yr, yc, mr, mc
+
+    # grouped (32768 x 7168, 8 groups)
+    xg, counts = W.moe_grouped()
+    R, C = xg.shape
+    xs = [tens(xg) for _ in range(2)]
+    ys = [torch.empty_like(xs[0]) for _ in range(2)]
+    gl = torch.from_numpy(counts).cuda()
+    d = M._Desc(1, 32, 0, 0, R, C, 6.0, 0)
+    calls = [Call(lib.mxfp4_grouped_qdq, ctypes.byref(d), vp(xs[i].data_ptr()), vp(gl.data_ptr()), 8, 1,
+                  vp(ys[i].data_ptr()), None, None, stream) for i in range(2)]
+    rec("grouped_32768x7168_y", R * C * 4.0, R * C, _time_calls(torch, calls, 30))
+    del xs, ys
+    return out
+
+
+if __name__ == "__main__":
+    main()

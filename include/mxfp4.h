@@ -1,0 +1,186 @@
+/*
+ * mxfp4.h -- C ABI of libmxfp4, MXFP4 fake quantization on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method (amct PR "feat: add MXFP4 QAT fake-quant Linear (with STE)",
+ * README section "1. MXFP4 and STE", fake_quant.py):  a tensor is cut into
+ * blocks of `block` consecutive elements along a chosen axis; every block
+ * shares one power-of-two scale 2^k (stored as an E8M0 byte k + 127); each
+ * element x is replaced by sign(x) * c * 2^k where c is the E2M1 code
+ * {0, 0.5, 1, 1.5, 2, 3, 4, 6} nearest to |x| / 2^k (decided by the midpoints
+ * 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5), so the block is clipped at 6 * 2^k.
+ * The backward pass is the straight-through estimator: the gradient passes
+ * unchanged (plain) or is zeroed where |x| > 6 * 2^k (clipped STE,
+ * _MXFP4FakeQuantSTE.backward / mxfp4_saturation_mask).
+ *
+ * Scale rules (mxfp4_desc_t.rule):
+ *   MXFP4_RULE_FLOOR (default) -- k = floor(log2 amax) - 2, clamped below at
+ *       -127 (an all-zero block gets k = -127, E8M0 byte 0); a magnitude
+ *       exactly on a midpoint goes to the lower code.
+ *   MXFP4_RULE_AMCT -- the pages' _block_scale: r = fl32(amax / scale_factor)
+ *       (IEEE binary32 division), r = max(r, 2^-30), k = the integer nearest
+ *       to log2(r); a magnitude exactly on a midpoint goes to the higher code
+ *       (torch.bucketize(..., right=True)).  Results are specified while
+ *       k <= 127 (always true for scale_factor >= 6 and finite input).
+ * Zeros: x = -0.0 gives +0.0; a negative x that snaps to code 0 gives -0.0
+ * (torch.sign(x/scale) * code; torch.sign(-0.0) is +0).  NaN and Inf inputs
+ * are outside the contract (the kernels still run and do not fault).
+ *
+ * Tensors are 2-D, `rows` x `cols`, row-major and contiguous (leading
+ * dimension = cols); higher-rank tensors are flattened to rows = prod(leading
+ * dims).  Element dtype: MXFP4_BF16 (bf16 bit patterns) or MXFP4_F32.
+ * Output values have the input's dtype and are exact (every produced value is
+ * representable), so results are bit-for-bit reproducible.
+ *
+ * Memory and streams: every pointer is caller-owned device memory.  The
+ * library allocates nothing, keeps no state between calls, never
+ * synchronizes, and enqueues its kernels on `stream` (a hipStream_t; NULL is
+ * the null stream).  Outputs are fully written inside their documented
+ * shapes; no byte past a shape is touched.  Element arrays (x, y, grads),
+ * packed codes and COL / GROUPED bitmaps must be 16-byte aligned, ROW bitmaps
+ * 4-byte aligned, group_list 8-byte aligned; scale arrays need no alignment.
+ *
+ * Errors: every call validates its arguments on the host before launching
+ * anything.  MXFP4_EINVAL: NULL where a pointer is required, misalignment,
+ * negative sizes, rows*cols overflow, unknown axis/layout/rule, scale_factor
+ * <= 0 (AMCT), num_groups < 1, unknown group_list_type, or an output that
+ * aliases another argument where that is not allowed.  MXFP4_EUNSUPPORTED:
+ * block not 32 or 128, dtype not bf16/f32, or an axis combination a call
+ * does not offer.  MXFP4_EHIP: a launch failed (the HIP error text is kept).
+ * mxfp4_last_error() returns a message for the calling thread's last failed
+ * call.  rows*cols == 0 returns MXFP4_OK without launching.
+ *
+ * Bitmap layouts (uint32 words; the saturation mask |x| > 6 * 2^k, one bit
+ * per element, replacing the pages' bool tensor):
+ *   ROW      [rows, ceil(cols/32)]: bit b of word (r, w) is column 32w + b.
+ *   COL      [ceil(rows/32), cols]: bit b of word (w, c) is row 32w + b.
+ *   GROUPED  [NBT * block/32, cols]: word (t*block/32 + q, c) bit b is row
+ *            start_t + 32q + b of block-row t (see mxfp4_grouped_qdq).
+ * Bits for positions outside the tensor (or outside a short block) are 0.
+ * E8M0 scale layouts (one byte per block, k + 127):
+ *   ROW [rows, ceil(cols/block)];  COL [ceil(rows/block), cols];
+ *   GROUPED [NBT, cols].
+ */
+#ifndef MXFP4_H
+#define MXFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXFP4_OK = 0,
+  MXFP4_EINVAL = 1,
+  MXFP4_EUNSUPPORTED = 2,
+  MXFP4_EHIP = 3
+} mxfp4_status_t;
+
+enum { MXFP4_F32 = 0, MXFP4_BF16 = 1 };                 /* element dtype      */
+enum { MXFP4_ROW = 1, MXFP4_COL = 2, MXFP4_GROUPED = 4 }; /* axis / layout bits */
+enum { MXFP4_RULE_FLOOR = 0, MXFP4_RULE_AMCT = 1 };      /* scale + tie rule   */
+
+typedef struct mxfp4_desc {
+  int32_t dtype;        /* MXFP4_BF16 or MXFP4_F32                             */
+  int32_t block;        /* 32 or 128 elements per shared scale                 */
+  int32_t rule;         /* MXFP4_RULE_FLOOR or MXFP4_RULE_AMCT                 */
+  int32_t reserved0;    /* must be 0                                           */
+  int64_t rows;         /* x is rows x cols, row-major, contiguous             */
+  int64_t cols;
+  float scale_factor;   /* AMCT only (the pages' default 6.0); must be > 0     */
+  int32_t reserved1;    /* must be 0                                           */
+} mxfp4_desc_t;
+
+/*
+ * Quantize-dequantize (fake quant) forward: fake_quant.py
+ * mxfp4_quant_dequant + mxfp4_saturation_mask, fused in one pass over x.
+ *
+ * axis = MXFP4_ROW: blocks along each row (the pages' last-dim blocking,
+ *   _block_view: the last block of a row is short when cols % block != 0).
+ * axis = MXFP4_COL: blocks along each column (rows 0..block-1, ...), the
+ *   hyper-parallel page's column-wise operand direction; y_col keeps x's
+ *   row-major layout.
+ * axis = MXFP4_ROW | MXFP4_COL: both views from one read of x.
+ * For each direction in `axis`, at least one of its outputs must be
+ * non-NULL; outputs of a direction not in `axis` must be NULL.
+ *   y_*      dequantized values, x's dtype and layout (NULL: not written);
+ *   mask_*   saturation bitmap, ROW / COL layout (NULL: clip off);
+ *   scales_* E8M0 bytes, ROW / COL layout (NULL: not written).
+ * y_row may equal x when axis == MXFP4_ROW and y_col may equal x when
+ * axis == MXFP4_COL (in place); no other aliasing is allowed.
+ */
+mxfp4_status_t mxfp4_qdq_fwd(const mxfp4_desc_t *desc, int32_t axis,
+                             const void *x, void *y_row, uint32_t *mask_row,
+                             uint8_t *scales_row, void *y_col,
+                             uint32_t *mask_col, uint8_t *scales_col,
+                             void *stream);
+
+/*
+ * Straight-through-estimator backward (_MXFP4FakeQuantSTE.backward):
+ * grad_in = grad_out where the mask bit is 0 and +0.0 where it is 1 (clipped
+ * STE).  mask == NULL is the plain STE: grad_in = grad_out (a copy, or
+ * nothing when grad_in == grad_out).  `layout` names the bitmap layout the
+ * forward wrote: MXFP4_ROW, MXFP4_COL, or MXFP4_GROUPED (then group_list,
+ * num_groups and group_list_type are those given to mxfp4_grouped_qdq and
+ * desc->block must match it; they are ignored for ROW and COL).
+ * grad_out / grad_in are rows x cols of desc->dtype; grad_in may equal
+ * grad_out.  desc->rule and scale_factor are ignored.
+ */
+mxfp4_status_t mxfp4_ste_bwd(const mxfp4_desc_t *desc, int32_t layout,
+                             const void *grad_out, const uint32_t *mask,
+                             void *grad_in, const int64_t *group_list,
+                             int32_t num_groups, int32_t group_list_type,
+                             void *stream);
+
+/*
+ * Real quantization to the packed MXFP4 form (the sglang page's
+ * "float4_e2m1fn_x2": two FP4 codes per byte), row-wise blocks.
+ *   codes  [rows, ceil(cols/2)] bytes: element 2t in the low nibble, 2t+1 in
+ *          the high nibble (the last high nibble of an odd row is 0); a
+ *          nibble is sign << 3 | E2M1 magnitude code (0..7 in codebook order).
+ *   scales [rows, ceil(cols/block)] E8M0 bytes.
+ * Optional in the same pass: y_opt (the QDQ values, may equal x) and
+ * mask_opt (ROW bitmap).  Decoding codes with scales gives y exactly.
+ */
+mxfp4_status_t mxfp4_quant_pack(const mxfp4_desc_t *desc, const void *x,
+                                uint8_t *codes, uint8_t *scales, void *y_opt,
+                                uint32_t *mask_opt, void *stream);
+
+/*
+ * Grouped column-wise QDQ (the hyper-parallel page's per-expert operand:
+ * rows are tokens split into num_groups consecutive expert groups).
+ * group_list is a device array of num_groups int64: row counts
+ * (group_list_type = 1, the default on the pages) or cumulative row ends
+ * (group_list_type = 0), as normalize_group_list accepts.  Column blocks of
+ * desc->block rows start at every group start and never cross a group
+ * boundary; a group's last block is short when its count is not a multiple
+ * of block; empty groups are allowed.
+ * Block-rows are numbered group by group: group g owns ceil(c_g / block)
+ * block-rows.  NBT = sum_g ceil(c_g / block) <= ceil(rows/block) + num_groups
+ * - 1; size the mask to (ceil(rows/block) + num_groups) * block/32 word-rows
+ * and scales to ceil(rows/block) + num_groups byte-rows; rows past NBT are
+ * not touched.  The counts must be >= 0 and sum to rows (the caller's
+ * contract: the device cannot check it without a host sync); the kernel
+ * clamps group ends into [previous end, rows], so an inconsistent list never
+ * causes out-of-bounds access, and rows past the last end are not touched.
+ * y (required, may equal x), mask_opt (GROUPED bitmap), scales_opt (GROUPED
+ * E8M0 bytes).
+ */
+mxfp4_status_t mxfp4_grouped_qdq(const mxfp4_desc_t *desc, const void *x,
+                                 const int64_t *group_list, int32_t num_groups,
+                                 int32_t group_list_type, void *y,
+                                 uint32_t *mask_opt, uint8_t *scales_opt,
+                                 void *stream);
+
+/* Message for the calling thread's most recent failed call ("" if none). */
+const char *mxfp4_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t mxfp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H */

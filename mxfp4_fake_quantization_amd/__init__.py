@@ -1,0 +1,222 @@
+"""MXFP4 fake quantization on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over libmxfp4.so (include/mxfp4.h): argument marshalling
+only -- every step of the method runs in the library's HIP kernels.  torch is
+used for device memory and streams.  There is no CPU fallback: if the library
+is missing, or a tensor is not on the GPU, the calls raise.
+
+Functions with the C names take torch tensors (or None) for every pointer
+argument and enqueue on torch's current stream:
+
+    mxfp4_qdq_fwd(x, axis, y_row, mask_row, scales_row, y_col, mask_col, scales_col,
+                  block=32, rule="floor", scale_factor=6.0)
+    mxfp4_ste_bwd(grad_out, mask, grad_in, layout, block=32, group_list=None,
+                  group_list_type=1)
+    mxfp4_quant_pack(x, codes, scales, y=None, mask=None, block=32, rule="floor",
+                     scale_factor=6.0)
+    mxfp4_grouped_qdq(x, group_list, y, mask=None, scales=None, block=32,
+                      rule="floor", scale_factor=6.0, group_list_type=1)
+
+Tensor conventions: x / y / grads are bfloat16 or float32, 2-D contiguous
+(higher ranks are viewed as rows x last-dim); bitmaps are int32 tensors (the
+uint32 bit patterns); scales and codes are uint8; group_list is int64 on the
+device.  The alloc_* helpers allocate outputs of the documented shapes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "ROW", "COL", "GROUPED", "FLOOR", "AMCT",
+    "mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
+    "mxfp4_last_error", "mxfp4_version", "library_path",
+    "row_mask_shape", "col_mask_shape", "grouped_mask_rows_max", "grouped_scale_rows_max",
+]
+
+ROW, COL, GROUPED = 1, 2, 4
+FLOOR, AMCT = 0, 1
+_F32, _BF16 = 0, 1
+_OK, _EINVAL, _EUNSUPPORTED, _EHIP = 0, 1, 2, 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.environ.get("MXFP4_LIBRARY") or os.path.join(_HERE, "libmxfp4.so")
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("block", ctypes.c_int32), ("rule", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("scale_factor", ctypes.c_float), ("reserved1", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"libmxfp4.so not found at {_LIB_PATH}; build it with "
+                "`python -m mxfp4_fake_quantization_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        dp = ctypes.POINTER(_Desc)
+        lib.mxfp4_qdq_fwd.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.mxfp4_ste_bwd.argtypes = [dp, i32, vp, vp, vp, vp, i32, i32, vp]
+        lib.mxfp4_quant_pack.argtypes = [dp, vp, vp, vp, vp, vp, vp]
+        lib.mxfp4_grouped_qdq.argtypes = [dp, vp, vp, i32, i32, vp, vp, vp, vp]
+        for f in ("mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
+                  "mxfp4_version"):
+            getattr(lib, f).restype = ctypes.c_int32
+        lib.mxfp4_last_error.restype = ctypes.c_char_p
+        lib.mxfp4_last_error.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def mxfp4_last_error() -> str:
+    return _load().mxfp4_last_error().decode()
+
+
+def mxfp4_version() -> int:
+    return int(_load().mxfp4_version())
+
+
+# ------------------------------------------------------------ marshalling
+
+def _rule(rule) -> int:
+    if rule in ("floor", FLOOR):
+        return FLOOR
+    if rule in ("amct", AMCT):
+        return AMCT
+    raise ValueError(f"rule must be 'floor' or 'amct', got {rule!r}")
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    if t.dtype == torch.float32:
+        return _F32
+    raise ValueError(f"element dtype must be bfloat16 or float32, got {t.dtype}")
+
+
+def _shape2d(t: torch.Tensor):
+    if t.dim() == 0:
+        raise ValueError("x must have at least 1 dimension")
+    cols = t.shape[-1]
+    rows = t.numel() // cols if cols else 0
+    return rows, cols
+
+
+def _ptr(t, kind=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"expected a torch.Tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU (no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    if kind == "mask" and t.dtype != torch.int32:
+        raise ValueError(f"bitmaps are int32 tensors, got {t.dtype}")
+    if kind == "u8" and t.dtype != torch.uint8:
+        raise ValueError(f"scales / codes are uint8 tensors, got {t.dtype}")
+    if kind == "i64" and t.dtype != torch.int64:
+        raise ValueError(f"group_list is an int64 tensor, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _desc(x: torch.Tensor, block: int, rule, scale_factor: float) -> _Desc:
+    rows, cols = _shape2d(x)
+    return _Desc(_dtype(x), int(block), _rule(rule), 0, rows, cols, float(scale_factor), 0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status == _OK:
+        return
+    msg = f"{what}: {mxfp4_last_error()}"
+    if status in (_EINVAL, _EUNSUPPORTED):
+        raise ValueError(msg)
+    raise RuntimeError(msg)
+
+
+def _same_elems(x, *ys):
+    for y in ys:
+        if y is not None and (y.dtype != x.dtype or y.numel() != x.numel()):
+            raise ValueError("outputs must have x's dtype and number of elements")
+
+
+# ------------------------------------------------------------ entry points
+
+def mxfp4_qdq_fwd(x, axis=ROW, y_row=None, mask_row=None, scales_row=None, y_col=None,
+                  mask_col=None, scales_col=None, block=32, rule="floor", scale_factor=6.0):
+    """Fused QDQ forward (+ clip bitmap, + E8M0 scales); see include/mxfp4.h."""
+    _same_elems(x, y_row, y_col)
+    d = _desc(x, block, rule, scale_factor)
+    st = _load().mxfp4_qdq_fwd(ctypes.byref(d), int(axis), _ptr(x), _ptr(y_row),
+                               _ptr(mask_row, "mask"), _ptr(scales_row, "u8"), _ptr(y_col),
+                               _ptr(mask_col, "mask"), _ptr(scales_col, "u8"), _stream())
+    _check(st, "mxfp4_qdq_fwd")
+
+
+def mxfp4_ste_bwd(grad_out, mask, grad_in, layout=ROW, block=32, group_list=None,
+                  group_list_type=1):
+    """Clipped (mask given) or plain (mask None) STE backward."""
+    _same_elems(grad_out, grad_in)
+    d = _desc(grad_out, block, "floor", 6.0)
+    n_groups = group_list.numel() if group_list is not None else 0
+    st = _load().mxfp4_ste_bwd(ctypes.byref(d), int(layout), _ptr(grad_out), _ptr(mask, "mask"),
+                               _ptr(grad_in), _ptr(group_list, "i64"), n_groups,
+                               int(group_list_type), _stream())
+    _check(st, "mxfp4_ste_bwd")
+
+
+def mxfp4_quant_pack(x, codes, scales, y=None, mask=None, block=32, rule="floor",
+                     scale_factor=6.0):
+    """Packed E2M1 codes (two per byte) + E8M0 scales, row-wise blocks."""
+    _same_elems(x, y)
+    d = _desc(x, block, rule, scale_factor)
+    st = _load().mxfp4_quant_pack(ctypes.byref(d), _ptr(x), _ptr(codes, "u8"), _ptr(scales, "u8"),
+                                  _ptr(y), _ptr(mask, "mask"), _stream())
+    _check(st, "mxfp4_quant_pack")
+
+
+def mxfp4_grouped_qdq(x, group_list, y, mask=None, scales=None, block=32, rule="floor",
+                      scale_factor=6.0, group_list_type=1):
+    """Grouped column-wise QDQ; group_list = per-group row counts (type 1)
+    or cumulative row ends (type 0), int64 on the device."""
+    _same_elems(x, y)
+    d = _desc(x, block, rule, scale_factor)
+    st = _load().mxfp4_grouped_qdq(ctypes.byref(d), _ptr(x), _ptr(group_list, "i64"),
+                                   group_list.numel(), int(group_list_type), _ptr(y),
+                                   _ptr(mask, "mask"), _ptr(scales, "u8"), _stream())
+    _check(st, "mxfp4_grouped_qdq")
+
+
+# ------------------------------------------------------------ shapes
+
+def row_mask_shape(rows: int, cols: int):
+    return rows, -(-cols // 32)
+
+
+def col_mask_shape(rows: int, cols: int):
+    return -(-rows // 32), cols
+
+
+def grouped_scale_rows_max(rows: int, block: int, num_groups: int) -> int:
+    return -(-rows // block) + num_groups
+
+
+def grouped_mask_rows_max(rows: int, block: int, num_groups: int) -> int:
+    return grouped_scale_rows_max(rows, block, num_groups) * (block // 32)

@@ -1,0 +1,199 @@
+// api.hip -- the extern "C" entry points declared in include/mxfp4.h.
+// Arguments are validated on the host before anything is enqueued; the
+// kernels run on the caller's stream; nothing is allocated or synchronized.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/mxfp4.h"
+#include "mxfp4_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mxfp4_status_t fail(mxfp4_status_t st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+mxfp4_status_t ok() {
+  g_last_error.clear();
+  return MXFP4_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Common descriptor checks; sets *n to rows * cols.
+mxfp4_status_t check_desc(const mxfp4_desc_t *d, bool need_rule, int64_t *n) {
+  if (!d) return fail(MXFP4_EINVAL, "desc is NULL");
+  if (d->dtype != MXFP4_BF16 && d->dtype != MXFP4_F32)
+    return fail(MXFP4_EUNSUPPORTED, "dtype %d is not MXFP4_BF16 or MXFP4_F32", d->dtype);
+  if (d->block != 32 && d->block != 128)
+    return fail(MXFP4_EUNSUPPORTED, "block %d is not 32 or 128", d->block);
+  if (d->reserved0 != 0 || d->reserved1 != 0) return fail(MXFP4_EINVAL, "reserved fields must be 0");
+  if (d->rows < 0 || d->cols < 0) return fail(MXFP4_EINVAL, "negative shape %lld x %lld",
+                                              (long long)d->rows, (long long)d->cols);
+  if (d->cols > 0 && d->rows > INT64_MAX / 4 / d->cols)
+    return fail(MXFP4_EINVAL, "rows * cols overflows");
+  if (need_rule) {
+    if (d->rule != MXFP4_RULE_FLOOR && d->rule != MXFP4_RULE_AMCT)
+      return fail(MXFP4_EINVAL, "unknown rule %d", d->rule);
+    if (d->rule == MXFP4_RULE_AMCT && !(d->scale_factor > 0.0f))
+      return fail(MXFP4_EINVAL, "scale_factor must be > 0 (got %g)", (double)d->scale_factor);
+  }
+  *n = d->rows * d->cols;
+  return MXFP4_OK;
+}
+
+mxfp4_status_t check_ptr(const void *p, uintptr_t align, const char *what) {
+  if (!p) return fail(MXFP4_EINVAL, "%s is NULL", what);
+  if (!aligned(p, align)) return fail(MXFP4_EINVAL, "%s is not %u-byte aligned", what, (unsigned)align);
+  return MXFP4_OK;
+}
+
+mxfp4_status_t check_opt(const void *p, uintptr_t align, const char *what) {
+  return p ? check_ptr(p, align, what) : MXFP4_OK;
+}
+
+mxfp4_status_t hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(MXFP4_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+#define MXFP4_TRY(expr)                      \
+  do {                                       \
+    mxfp4_status_t st_ = (expr);             \
+    if (st_ != MXFP4_OK) return st_;         \
+  } while (0)
+
+// Distinct non-NULL pointers (NULL entries are skipped).
+bool distinct(std::initializer_list<const void *> ps) {
+  const void *seen[16];
+  int n = 0;
+  for (const void *p : ps) {
+    if (!p) continue;
+    for (int i = 0; i < n; ++i)
+      if (seen[i] == p) return false;
+    seen[n++] = p;
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+mxfp4_status_t mxfp4_qdq_fwd(const mxfp4_desc_t *desc, int32_t axis, const void *x, void *y_row,
+                             uint32_t *mask_row, uint8_t *scales_row, void *y_col,
+                             uint32_t *mask_col, uint8_t *scales_col, void *stream) {
+  int64_t n;
+  MXFP4_TRY(check_desc(desc, true, &n));
+  if (axis != MXFP4_ROW && axis != MXFP4_COL && axis != (MXFP4_ROW | MXFP4_COL))
+    return fail(MXFP4_EINVAL, "axis %d is not MXFP4_ROW, MXFP4_COL or both", axis);
+  const bool row = axis & MXFP4_ROW, col = axis & MXFP4_COL;
+  if (!row && (y_row || mask_row || scales_row))
+    return fail(MXFP4_EINVAL, "row outputs given but axis has no MXFP4_ROW");
+  if (!col && (y_col || mask_col || scales_col))
+    return fail(MXFP4_EINVAL, "column outputs given but axis has no MXFP4_COL");
+  if (row && !y_row && !mask_row && !scales_row) return fail(MXFP4_EINVAL, "no row output given");
+  if (col && !y_col && !mask_col && !scales_col) return fail(MXFP4_EINVAL, "no column output given");
+  MXFP4_TRY(check_ptr(x, 16, "x"));
+  MXFP4_TRY(check_opt(y_row, 16, "y_row"));
+  MXFP4_TRY(check_opt(y_col, 16, "y_col"));
+  MXFP4_TRY(check_opt(mask_row, 4, "mask_row"));
+  MXFP4_TRY(check_opt(mask_col, 16, "mask_col"));
+  // in place is allowed for a single direction only
+  const void *xin = (axis == MXFP4_ROW && y_row == x) || (axis == MXFP4_COL && y_col == x) ? nullptr : x;
+  if (!distinct({xin, y_row, mask_row, scales_row, y_col, mask_col, scales_col}))
+    return fail(MXFP4_EINVAL, "outputs alias each other or x");
+  if (n == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (axis == MXFP4_ROW) {
+    mxfp4::RowLaunch L{desc->dtype, desc->block, desc->rule, desc->rows, desc->cols,
+                       desc->scale_factor, x, y_row, mask_row, scales_row, nullptr};
+    return hip_status(mxfp4::launch_row_fwd(L, st), "row-wise forward launch");
+  }
+  mxfp4::ColLaunch L{desc->dtype, desc->block, desc->rule, desc->rows, desc->cols,
+                     desc->scale_factor, x, y_col, mask_col, scales_col,
+                     y_row, mask_row, scales_row, nullptr, 0, 1};
+  return hip_status(mxfp4::launch_col_fwd(L, st), "column-wise forward launch");
+}
+
+mxfp4_status_t mxfp4_ste_bwd(const mxfp4_desc_t *desc, int32_t layout, const void *grad_out,
+                             const uint32_t *mask, void *grad_in, const int64_t *group_list,
+                             int32_t num_groups, int32_t group_list_type, void *stream) {
+  int64_t n;
+  MXFP4_TRY(check_desc(desc, false, &n));
+  if (layout != MXFP4_ROW && layout != MXFP4_COL && layout != MXFP4_GROUPED)
+    return fail(MXFP4_EINVAL, "layout %d is not MXFP4_ROW, MXFP4_COL or MXFP4_GROUPED", layout);
+  MXFP4_TRY(check_ptr(grad_out, 16, "grad_out"));
+  MXFP4_TRY(check_ptr(grad_in, 16, "grad_in"));
+  MXFP4_TRY(check_opt(mask, layout == MXFP4_ROW ? 4 : 16, "mask"));
+  if (mask && layout == MXFP4_GROUPED) {
+    if (!group_list) return fail(MXFP4_EINVAL, "group_list is NULL");
+    if (!aligned(group_list, 8)) return fail(MXFP4_EINVAL, "group_list is not 8-byte aligned");
+    if (num_groups < 1) return fail(MXFP4_EINVAL, "num_groups must be >= 1 (got %d)", num_groups);
+    if (group_list_type != 0 && group_list_type != 1)
+      return fail(MXFP4_EINVAL, "group_list_type must be 0 or 1 (got %d)", group_list_type);
+  }
+  if (mask && (mask == grad_out || mask == grad_in)) return fail(MXFP4_EINVAL, "mask aliases a gradient");
+  if (n == 0) return ok();
+  if (!mask && grad_in == grad_out) return ok();  // plain STE in place: nothing to do
+  mxfp4::SteLaunch L{desc->dtype, desc->block, layout, desc->rows, desc->cols, grad_out, mask,
+                     grad_in, group_list, num_groups, group_list_type};
+  return hip_status(mxfp4::launch_ste_bwd(L, static_cast<hipStream_t>(stream)), "STE backward launch");
+}
+
+mxfp4_status_t mxfp4_quant_pack(const mxfp4_desc_t *desc, const void *x, uint8_t *codes,
+                                uint8_t *scales, void *y_opt, uint32_t *mask_opt, void *stream) {
+  int64_t n;
+  MXFP4_TRY(check_desc(desc, true, &n));
+  MXFP4_TRY(check_ptr(x, 16, "x"));
+  MXFP4_TRY(check_ptr(codes, 16, "codes"));
+  MXFP4_TRY(check_ptr(scales, 1, "scales"));
+  MXFP4_TRY(check_opt(y_opt, 16, "y_opt"));
+  MXFP4_TRY(check_opt(mask_opt, 4, "mask_opt"));
+  if (!distinct({y_opt == x ? nullptr : x, codes, scales, y_opt, mask_opt}))
+    return fail(MXFP4_EINVAL, "outputs alias each other or x");
+  if (n == 0) return ok();
+  mxfp4::RowLaunch L{desc->dtype, desc->block, desc->rule, desc->rows, desc->cols,
+                     desc->scale_factor, x, y_opt, mask_opt, scales, codes};
+  return hip_status(mxfp4::launch_row_fwd(L, static_cast<hipStream_t>(stream)), "pack launch");
+}
+
+mxfp4_status_t mxfp4_grouped_qdq(const mxfp4_desc_t *desc, const void *x,
+                                 const int64_t *group_list, int32_t num_groups,
+                                 int32_t group_list_type, void *y, uint32_t *mask_opt,
+                                 uint8_t *scales_opt, void *stream) {
+  int64_t n;
+  MXFP4_TRY(check_desc(desc, true, &n));
+  MXFP4_TRY(check_ptr(x, 16, "x"));
+  MXFP4_TRY(check_ptr(y, 16, "y"));
+  MXFP4_TRY(check_opt(mask_opt, 16, "mask_opt"));
+  if (!group_list) return fail(MXFP4_EINVAL, "group_list is NULL");
+  if (!aligned(group_list, 8)) return fail(MXFP4_EINVAL, "group_list is not 8-byte aligned");
+  if (num_groups < 1) return fail(MXFP4_EINVAL, "num_groups must be >= 1 (got %d)", num_groups);
+  if (group_list_type != 0 && group_list_type != 1)
+    return fail(MXFP4_EINVAL, "group_list_type must be 0 or 1 (got %d)", group_list_type);
+  if (!distinct({y == x ? nullptr : x, y, mask_opt, scales_opt, group_list}))
+    return fail(MXFP4_EINVAL, "outputs alias each other, x or group_list");
+  if (n == 0) return ok();
+  mxfp4::ColLaunch L{desc->dtype, desc->block, desc->rule, desc->rows, desc->cols,
+                     desc->scale_factor, x, y, mask_opt, scales_opt,
+                     nullptr, nullptr, nullptr, group_list, num_groups, group_list_type};
+  return hip_status(mxfp4::launch_col_fwd(L, static_cast<hipStream_t>(stream)), "grouped launch");
+}
+
+const char *mxfp4_last_error(void) { return g_last_error.c_str(); }
+
+int32_t mxfp4_version(void) { return 100; }
+
+}  // extern "C"

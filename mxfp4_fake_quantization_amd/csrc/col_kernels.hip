@@ -1,0 +1,374 @@
+// col_kernels.hip -- column-wise, dual-direction and grouped MXFP4 fake
+// quantization on gfx950.
+//
+// Column-wise blocks are `block` consecutive rows of one column (the
+// hyper-parallel page's column-direction operand); grouped blocks restart at
+// every expert-group start (its "grouped dynamic quantization" along tokens);
+// the dual-direction launch produces the row-wise and the column-wise view of
+// the same tensor from one read of x.
+//
+// Tiling: a wave owns 32 rows x 128 columns.  Lane = rg + 4*cc holds rows
+// 8*rg .. 8*rg+7 of the slab and the 8 columns 8*cc .. 8*cc+7 (one 16-byte bf16
+// piece per row, i.e. 256-byte row segments per load instruction).
+//   - column max: in-register max over the lane's 8 rows, then a DPP quad
+//     reduction over rg; for 128-row blocks the four waves of the workgroup
+//     (stacked vertically) exchange their partial maxima through LDS;
+//   - row max (dual): DPP row_ror 4/8 over the 4 lanes of a 32-column block
+//     (plus ds_swizzle / ds_bpermute steps for 128-column blocks);
+//   - column bitmap words (bit = row) are assembled by OR-ing each lane's
+//     8-row byte across the quad, then every lane stores 2 words so the wave
+//     writes one contiguous 512-byte stretch.
+// For block 32 the workgroup is 4 waves side by side (32 x 512), for block
+// 128 4 waves stacked (128 x 128): one workgroup = one block-row x one column
+// tile, which makes grouped block-rows (arbitrary start rows) free of any
+// alignment constraint on the loads.
+#include "mxfp4_device.h"
+#include "mxfp4_groups.h"
+#include "mxfp4_kernels.h"
+
+namespace mxfp4 {
+namespace {
+
+enum { kKindCol = 0, kKindDual = 1, kKindGrouped = 2 };
+constexpr int kWaveCols = 128;
+
+struct ColArgs {
+  const uint8_t *x;
+  uint8_t *y_col;
+  uint32_t *mask_col;
+  uint8_t *scales_col;
+  uint8_t *y_row;
+  uint32_t *mask_row;
+  uint8_t *scales_row;
+  const int64_t *group_list;
+  int64_t rows, cols;
+  int64_t nct;     // column tiles per block-row
+  int64_t nw_row;  // row-bitmap words per row
+  int64_t nb_row;  // row-wise blocks per row
+  int num_groups, list_type;
+  float sf;
+};
+
+template <int DT>
+struct ColT {
+  static constexpr int NW = DT == kBF16 ? 4 : 8;  // words per 8-element piece
+  static constexpr int ES = DT == kBF16 ? 2 : 4;
+};
+
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_piece(uint32_t *w, const uint8_t *p, int n) {
+  constexpr int NW = ColT<DT>::NW;
+  if (VEC) {
+    if (n == 8) {
+      uint4 v = ld16(p);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+      if (DT == kF32) {
+        uint4 v2 = ld16(p + 16);
+        w[4] = v2.x; w[5] = v2.y; w[6] = v2.z; w[7] = v2.w;
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NW; ++k) w[k] = 0;
+  if (!VEC) {
+    for (int j = 0; j < n; ++j) {
+      if (DT == kBF16) w[j >> 1] |= (uint32_t)reinterpret_cast<const uint16_t *>(p)[j] << (16 * (j & 1));
+      else w[j] = reinterpret_cast<const uint32_t *>(p)[j];
+    }
+  }
+}
+
+template <int DT, bool VEC>
+__device__ __forceinline__ void store_piece(uint8_t *p, const uint32_t *w, int n) {
+  if (VEC) {
+    if (n == 8) {
+      st16(p, make_uint4(w[0], w[1], w[2], w[3]));
+      if (DT == kF32) st16(p + 16, make_uint4(w[4], w[5], w[6], w[7]));
+    }
+    return;
+  }
+  for (int j = 0; j < n; ++j) {
+    if (DT == kBF16) reinterpret_cast<uint16_t *>(p)[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+    else reinterpret_cast<uint32_t *>(p)[j] = w[j];
+  }
+}
+
+// Pick word k = 2*rg (+1) of 8 per-lane words without dynamic indexing.
+__device__ __forceinline__ uint32_t pick4(const uint32_t *v, int sel) {
+  uint32_t r = v[0];
+  r = sel == 1 ? v[1] : r;
+  r = sel == 2 ? v[2] : r;
+  r = sel == 3 ? v[3] : r;
+  return r;
+}
+
+template <int DT, int B, int RULE, int KIND, bool VEC>
+__global__ __launch_bounds__(kThreads) void col_fwd_kernel(ColArgs A) {
+  constexpr int NW = ColT<DT>::NW;
+  constexpr int ES = ColT<DT>::ES;
+  constexpr int WX = B == 32 ? 4 : 1;  // waves side by side
+  constexpr int G_ROW = B / 8;         // lanes per row-wise block (dual)
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int rg = lane & 3;
+  const int cc = lane >> 2;
+  const int wx = B == 32 ? wave : 0;
+  const int wy = B == 32 ? 0 : wave;
+
+  const int64_t bt = blockIdx.x / A.nct;
+  const int64_t ct = blockIdx.x - bt * A.nct;
+
+  int64_t start, len;
+  if (KIND == kKindGrouped) {
+    __shared__ int64_t s_blk[2];
+    if (wave == 0)
+      find_block_row(A.group_list, A.num_groups, A.list_type, A.rows, B == 32 ? 5 : 7, bt, s_blk);
+    __syncthreads();
+    start = s_blk[0];
+    len = s_blk[1];
+    if (len <= 0) return;  // whole workgroup: past the last block-row
+  } else {
+    start = bt * B;
+    len = A.rows - start < B ? A.rows - start : B;
+  }
+
+  const int64_t col0 = ct * (kWaveCols * WX) + kWaveCols * wx;
+  const int64_t c0 = col0 + 8 * cc;
+  const int64_t crem = A.cols - c0;
+  const int ncol = crem >= 8 ? 8 : (crem > 0 ? (int)crem : 0);
+  const int slab = 32 * wy;
+
+  // ---- load 8 rows x 8 columns per lane ---------------------------------
+  uint32_t w[8][NW];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rr = slab + 8 * rg + i;
+    const int n = rr < len ? ncol : 0;
+    load_piece<DT, VEC>(w[i], A.x + ((start + rr) * A.cols + c0) * ES, n);
+  }
+
+  // ---- column direction ---------------------------------------------------
+  // column maxima: bf16 packed per word (2 columns), fp32 one per word
+  uint32_t cm[NW];
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (DT == kBF16) m = pk_max(m, w[i][k] & 0x7FFF7FFFu);
+      else m = max32(m, w[i][k] & 0x7FFFFFFFu);
+    }
+    cm[k] = DT == kBF16 ? pkmax_quad(m) : max_quad(m);
+  }
+  if (B == 128) {
+    __shared__ uint32_t s_cm[4][16][NW];
+    if (rg == 0) {
+#pragma unroll
+      for (int k = 0; k < NW; ++k) s_cm[wave][cc][k] = cm[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      uint32_t m = s_cm[0][cc][k];
+#pragma unroll
+      for (int v = 1; v < 4; ++v) m = DT == kBF16 ? pk_max(m, s_cm[v][cc][k]) : max32(m, s_cm[v][cc][k]);
+      cm[k] = m;
+    }
+  }
+
+  // per-column parameters
+  uint32_t pt[NW], ph[NW], ps[NW], pe[NW];  // bf16: packed halves; fp32: per column
+  uint32_t slow_any = 0;
+  BlockParams cbp[DT == kF32 ? 8 : 1];
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    if (DT == kBF16) {
+      const BlockParams lo = block_params<DT, RULE>(cm[k] & 0xFFFFu, A.sf);
+      const BlockParams hi = block_params<DT, RULE>(cm[k] >> 16, A.sf);
+      pt[k] = lo.t025 | (hi.t025 << 16);
+      ph[k] = lo.half | (hi.half << 16);
+      ps[k] = lo.six | (hi.six << 16);
+      pe[k] = lo.e8 | (hi.e8 << 16) | (lo.slow ? 0x100u : 0u) | (hi.slow ? 0x1000000u : 0u);
+      slow_any |= (lo.slow || hi.slow) ? 1u : 0u;
+    } else {
+      cbp[DT == kF32 ? k : 0] = block_params<DT, RULE>(cm[k], A.sf);
+      pe[k] = cbp[DT == kF32 ? k : 0].e8;
+    }
+  }
+
+  const bool slab_live = KIND == kKindGrouped ? true : (slab < len);
+  const int64_t wrow = bt * (B / 32) + wy;  // bitmap word-row of this slab
+
+  if (A.y_col || A.mask_col) {
+    uint32_t macc[8];  // per column: bits of this lane's 8 rows
+#pragma unroll
+    for (int k = 0; k < 8; ++k) macc[k] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t yv[NW];
+      const int rr = slab + 8 * rg + i;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) {
+        if (DT == kBF16) {
+          yv[k] = y_bf16(w[i][k], pt[k], ph[k]);
+          uint32_t mb = m_bf16(w[i][k], ps[k]);
+          if (slow_any && (pe[k] & 0x1000100u)) {
+            if (pe[k] & 0x100u) {
+              HalfOut o = half_bf16_slow(w[i][k] & 0xFFFFu, pe[k] & 0xFFu);
+              yv[k] = (yv[k] & 0xFFFF0000u) | o.y;
+              mb = (mb & 0xFFFF0000u) | o.m;
+            }
+            if (pe[k] & 0x1000000u) {
+              HalfOut o = half_bf16_slow(w[i][k] >> 16, (pe[k] >> 16) & 0xFFu);
+              yv[k] = (yv[k] & 0xFFFFu) | (o.y << 16);
+              mb = (mb & 0xFFFFu) | (o.m << 16);
+            }
+          }
+          macc[2 * k] |= (mb & 1u) << i;
+          macc[2 * k + 1] |= (mb >> 16) << i;
+        } else {
+          yv[k] = y_f32(w[i][k], cbp[DT == kF32 ? k : 0]);
+          macc[k] |= m_f32(w[i][k], cbp[DT == kF32 ? k : 0]) << i;
+        }
+      }
+      if (A.y_col && rr < len) store_piece<DT, VEC>(A.y_col + ((start + rr) * A.cols + c0) * ES, yv, ncol);
+    }
+    if (A.mask_col) {
+      uint32_t mw[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) mw[k] = or_quad(macc[k] << (8 * rg));
+      // lane rg stores the words of columns 2rg and 2rg+1
+      const uint32_t ev[4] = {mw[0], mw[2], mw[4], mw[6]};
+      const uint32_t od[4] = {mw[1], mw[3], mw[5], mw[7]};
+      const uint32_t a0 = pick4(ev, rg), a1 = pick4(od, rg);
+      const int64_t cw = c0 + 2 * rg;
+      if (slab_live) {
+        uint32_t *dst = A.mask_col + wrow * A.cols + cw;
+        if (VEC) {
+          if (cw + 1 < A.cols) *reinterpret_cast<uint2 *>(dst) = make_uint2(a0, a1);
+        } else {
+          if (cw < A.cols) dst[0] = a0;
+          if (cw + 1 < A.cols) dst[1] = a1;
+        }
+      }
+    }
+  }
+  if (A.scales_col && rg == 0 && wy == 0) {
+    uint8_t *dst = A.scales_col + bt * A.cols + c0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      if (DT == kBF16) {
+        if (2 * k < ncol) dst[2 * k] = (uint8_t)(pe[k] & 0xFFu);
+        if (2 * k + 1 < ncol) dst[2 * k + 1] = (uint8_t)((pe[k] >> 16) & 0xFFu);
+      } else {
+        if (k < ncol) dst[k] = (uint8_t)pe[k];
+      }
+    }
+  }
+
+  // ---- row direction (dual) ----------------------------------------------
+  if (KIND == kKindDual) {
+    uint32_t rw[8];  // row-bitmap partial words
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = slab + 8 * rg + i;
+      uint32_t am;
+      if (DT == kBF16) {
+        uint32_t m = pk_max(pk_max(w[i][0] & 0x7FFF7FFFu, w[i][1] & 0x7FFF7FFFu),
+                            pk_max(w[i][2] & 0x7FFF7FFFu, w[i][3] & 0x7FFF7FFFu));
+        am = max32(m & 0xFFFFu, m >> 16);
+      } else {
+        am = 0;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) am = max32(am, w[i][k] & 0x7FFFFFFFu);
+      }
+      am = B == 32 ? max_stride4_row(am) : max_stride4_wave(am);
+      const BlockParams bp = block_params<DT, RULE>(am, A.sf);
+      if (A.y_row) {
+        uint32_t yv[NW];
+        chunk_y<DT>(w[i], bp, yv);
+        if (rr < len) store_piece<DT, VEC>(A.y_row + ((start + rr) * A.cols + c0) * ES, yv, ncol);
+      }
+      rw[i] = A.mask_row ? or_stride4_row(chunk_mask<DT>(w[i], bp) << (8 * (cc & 3))) : 0;
+      if (A.scales_row && (cc % G_ROW) == 0 && rr < len && ncol > 0)
+        A.scales_row[(start + rr) * A.nb_row + c0 / B] = (uint8_t)bp.e8;
+    }
+    if (A.mask_row) {
+      // the 4 lanes of a 32-column word hold all 8 rows' words: lane j stores
+      // rows j and j + 4
+      const int j = cc & 3;
+      const int64_t wi = c0 >> 5;
+      const uint32_t lo = pick4(rw, j);
+      const uint32_t hi = pick4(rw + 4, j);
+      const int r_lo = slab + 8 * rg + j, r_hi = r_lo + 4;
+      if (wi < A.nw_row) {
+        if (r_lo < len) A.mask_row[(start + r_lo) * A.nw_row + wi] = lo;
+        if (r_hi < len) A.mask_row[(start + r_hi) * A.nw_row + wi] = hi;
+      }
+    }
+  }
+}
+
+template <int DT, int B, int RULE, int KIND>
+hipError_t launch_kind(bool vec, const ColArgs &a, dim3 grid, hipStream_t st) {
+  if (vec) hipLaunchKernelGGL((col_fwd_kernel<DT, B, RULE, KIND, true>), grid, dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((col_fwd_kernel<DT, B, RULE, KIND, false>), grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DT, int B, int RULE>
+hipError_t launch_rule(int kind, bool vec, const ColArgs &a, dim3 grid, hipStream_t st) {
+  switch (kind) {
+    case kKindCol: return launch_kind<DT, B, RULE, kKindCol>(vec, a, grid, st);
+    case kKindDual: return launch_kind<DT, B, RULE, kKindDual>(vec, a, grid, st);
+    default: return launch_kind<DT, B, RULE, kKindGrouped>(vec, a, grid, st);
+  }
+}
+
+template <int DT, int B>
+hipError_t launch_b(int rule, int kind, bool vec, const ColArgs &a, dim3 grid, hipStream_t st) {
+  return rule == kFloor ? launch_rule<DT, B, kFloor>(kind, vec, a, grid, st)
+                        : launch_rule<DT, B, kAmct>(kind, vec, a, grid, st);
+}
+
+}  // namespace
+
+hipError_t launch_col_fwd(const ColLaunch &L, hipStream_t st) {
+  ColArgs a;
+  a.x = static_cast<const uint8_t *>(L.x);
+  a.y_col = static_cast<uint8_t *>(L.y_col);
+  a.mask_col = L.mask_col;
+  a.scales_col = L.scales_col;
+  a.y_row = static_cast<uint8_t *>(L.y_row);
+  a.mask_row = L.mask_row;
+  a.scales_row = L.scales_row;
+  a.group_list = L.group_list;
+  a.rows = L.rows;
+  a.cols = L.cols;
+  const int64_t tile_cols = L.block == 32 ? 4 * kWaveCols : kWaveCols;
+  a.nct = (L.cols + tile_cols - 1) / tile_cols;
+  a.nw_row = (L.cols + 31) / 32;
+  a.nb_row = (L.cols + L.block - 1) / L.block;
+  a.num_groups = L.num_groups;
+  a.list_type = L.list_type;
+  a.sf = L.sf;
+  const bool grouped = L.group_list != nullptr;
+  const bool dual = !grouped && (L.y_row || L.mask_row || L.scales_row);
+  const int kind = grouped ? kKindGrouped : (dual ? kKindDual : kKindCol);
+  const int64_t nbr = grouped ? (L.rows + L.block - 1) / L.block + L.num_groups
+                              : (L.rows + L.block - 1) / L.block;
+  const int64_t nwg = nbr * a.nct;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const bool vec = L.cols % 8 == 0;
+  dim3 grid((unsigned)nwg);
+  if (L.dtype == kBF16)
+    return L.block == 32 ? launch_b<kBF16, 32>(L.rule, kind, vec, a, grid, st)
+                         : launch_b<kBF16, 128>(L.rule, kind, vec, a, grid, st);
+  return L.block == 32 ? launch_b<kF32, 32>(L.rule, kind, vec, a, grid, st)
+                       : launch_b<kF32, 128>(L.rule, kind, vec, a, grid, st);
+}
+
+}  // namespace mxfp4

@@ -1,0 +1,54 @@
+// mxfp4_kernels.h -- host-side launch descriptors of the gfx950 kernels.
+// The C-ABI layer (api.hip) validates arguments and calls these launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxfp4 {
+
+enum { kEmitY = 1, kEmitMask = 2, kEmitScales = 4, kEmitCodes = 8 };
+
+// Row-wise forward: y / mask / scales / codes in one pass.
+struct RowLaunch {
+  int dtype, block, rule;
+  int64_t rows, cols;
+  float sf;
+  const void *x;
+  void *y;
+  uint32_t *mask;
+  uint8_t *scales;
+  uint8_t *codes;
+};
+hipError_t launch_row_fwd(const RowLaunch &L, hipStream_t stream);
+
+// Column-wise / dual-direction / grouped forward (block-row tiles).
+struct ColLaunch {
+  int dtype, block, rule;
+  int64_t rows, cols;
+  float sf;
+  const void *x;
+  void *y_col;          // column-direction outputs
+  uint32_t *mask_col;
+  uint8_t *scales_col;
+  void *y_row;          // row-direction outputs (dual only)
+  uint32_t *mask_row;
+  uint8_t *scales_row;
+  const int64_t *group_list;  // grouped only
+  int num_groups, list_type;
+};
+hipError_t launch_col_fwd(const ColLaunch &L, hipStream_t stream);
+
+// STE backward.
+struct SteLaunch {
+  int dtype, block, layout;  // layout: 1 row, 2 col, 4 grouped
+  int64_t rows, cols;
+  const void *g;
+  const uint32_t *mask;  // NULL: plain STE (copy)
+  void *g_in;
+  const int64_t *group_list;
+  int num_groups, list_type;
+};
+hipError_t launch_ste_bwd(const SteLaunch &L, hipStream_t stream);
+
+}  // namespace mxfp4

@@ -1,0 +1,232 @@
+// mxfp4_math.h -- integer-domain MXFP4 arithmetic shared by the gfx950 kernels.
+//
+// Everything here works on IEEE bit patterns of |x| ("magnitude bits" a), so
+// the block maximum, the scale exponent, the E2M1 snap, the clip mask, the
+// sign and the packed nibble are integer operations with no rounding at all.
+// bf16 elements are processed two per 32-bit register with packed 16-bit ALU
+// ops (v_pk_*_u16); fp32 elements one per register.  The functions are
+// __host__ __device__ so the same code can be checked on the CPU.
+//
+// Method (amct PR "MXFP4 QAT fake-quant Linear (with STE)", README section 1
+// and fake_quant.py _block_scale / _round_to_e2m1 / _quant_dequant_torch):
+// with block scale 2^k, |x|/2^k is snapped to the E2M1 code nearest to it by
+// the midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5 and the result is clipped at
+// 6 * 2^k; the clipped-STE mask is |x| > 6 * 2^k.
+//
+// Notation: MB = mantissa bits (bf16 7, fp32 23), Q = 2^(MB-1) = one step of a
+// 1-bit mantissa, E = biased scale exponent (E8M0 byte, k = E - 127).
+// For E >= 3 every threshold and code c*2^k (c >= 0.25) is a normal number
+// and the snap has a closed form in a-space:
+//   T025 = (E-2) << MB        bits of 0.25*2^k  (HALF - 2Q, ONE - 4Q)
+//   HALF = T025 + 2Q          bits of 0.5*2^k
+//   SIX  = T025 + 9Q          bits of 6*2^k
+//   u = sat(a - (T025 - tau))          tau = 0 (FLOOR, ties down) / 1 (AMCT, ties up)
+//   r = (u + Q/2 - 1) & ~(Q-1)         keep one mantissa bit of 2^? >= 1.0 values
+//   h = min(sat(r - 4Q), 5Q)           offset above 1.0*2^k, clipped at 6*2^k
+//   z = min(u, 1)                      |x| passes the 0.25 midpoint
+//   c = min(sat(u - 3Q), 1)            |x| passes the 0.75 midpoint
+//   mag = h + z*HALF + c*2Q            bits of code*2^k
+//   idx = z + c + h/Q                  E2M1 magnitude code 0..7
+// (T025 is a multiple of Q, so rounding u rounds a.)  For E < 3 (only FLOOR
+// blocks with amax < 2^-122) a generic threshold count is used instead.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#include <hip/hip_runtime.h>
+#define MXFP4_HD __host__ __device__ __forceinline__
+#else
+#define MXFP4_HD inline
+#endif
+
+namespace mxfp4 {
+
+enum { kF32 = 0, kBF16 = 1 };
+enum { kFloor = 0, kAmct = 1 };
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+MXFP4_HD u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
+MXFP4_HD uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// ---- packed 16-bit helpers (two bf16 per register) -------------------------
+MXFP4_HD uint32_t pk_subsat(uint32_t a, uint32_t b) {
+  return as_u32(__builtin_elementwise_sub_sat(as_u16x2(a), as_u16x2(b)));
+}
+MXFP4_HD uint32_t pk_min(uint32_t a, uint32_t b) {
+  return as_u32(__builtin_elementwise_min(as_u16x2(a), as_u16x2(b)));
+}
+MXFP4_HD uint32_t pk_max(uint32_t a, uint32_t b) {
+  return as_u32(__builtin_elementwise_max(as_u16x2(a), as_u16x2(b)));
+}
+MXFP4_HD uint32_t pk_add(uint32_t a, uint32_t b) { return as_u32(as_u16x2(a) + as_u16x2(b)); }
+MXFP4_HD uint32_t pk_sub(uint32_t a, uint32_t b) { return as_u32(as_u16x2(a) - as_u16x2(b)); }
+MXFP4_HD uint32_t pk_mad(uint32_t a, uint32_t b, uint32_t c) {
+  return as_u32(as_u16x2(a) * as_u16x2(b) + as_u16x2(c));
+}
+MXFP4_HD uint32_t pk_shr(uint32_t a, unsigned s) {
+  u16x2 sh = {(unsigned short)s, (unsigned short)s};
+  return as_u32(as_u16x2(a) >> sh);
+}
+MXFP4_HD uint32_t splat16(uint32_t v) { return (v & 0xFFFFu) | (v << 16); }
+
+MXFP4_HD uint32_t subsat32(uint32_t a, uint32_t b) { return a > b ? a - b : 0u; }
+MXFP4_HD uint32_t min32(uint32_t a, uint32_t b) { return a < b ? a : b; }
+MXFP4_HD uint32_t max32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// ---- per-dtype constants -----------------------------------------------------
+template <int DT> struct Fmt;
+template <> struct Fmt<kBF16> {
+  static constexpr int MB = 7;
+  static constexpr uint32_t Q = 1u << 6;
+  static constexpr uint32_t ABS = 0x7FFFu;
+  static constexpr uint32_t SIGN = 0x8000u;
+};
+template <> struct Fmt<kF32> {
+  static constexpr int MB = 23;
+  static constexpr uint32_t Q = 1u << 22;
+  static constexpr uint32_t ABS = 0x7FFFFFFFu;
+  static constexpr uint32_t SIGN = 0x80000000u;
+};
+
+// Block parameters derived from the block's max magnitude bits.
+struct BlockParams {
+  uint32_t e8;    // E8M0 byte (k + 127) reported for the block
+  uint32_t t025;  // T025 - tau  (u threshold)
+  uint32_t half;  // bits of 0.5 * 2^k
+  uint32_t six;   // bits of 6 * 2^k (mask: a > six)
+  bool slow;      // FLOOR with 0 < amax < 2^-122: use the generic snap
+};
+
+// FLOOR scale: k = floor(log2 amax) - 2 clamped at -127.  From the bits,
+// E = max(Eb - 2, 0) with Eb the biased exponent field of amax (0 for
+// subnormal or zero amax).  The closed-form snap is used with Ec = max(E, 3);
+// for a zero block any Ec >= 3 gives zeros, other E < 3 blocks go slow.
+template <int DT>
+MXFP4_HD BlockParams floor_params(uint32_t amax) {
+  constexpr int MB = Fmt<DT>::MB;
+  constexpr uint32_t Q = Fmt<DT>::Q;
+  uint32_t eb = amax >> MB;
+  BlockParams p;
+  p.e8 = eb > 2 ? eb - 2 : 0;
+  uint32_t ec = (eb > 5 ? eb : 5) - 2;
+  p.t025 = (ec - 2) << MB;
+  p.half = p.t025 + 2 * Q;
+  p.six = p.t025 + 9 * Q;
+  p.slow = (amax != 0) && (eb < 5);
+  return p;
+}
+
+// AMCT E8M0 byte from the block max: r = fl32(amax / sf) with IEEE division,
+// r = max(r, 2^-30), E = exponent(r) + (mantissa(r) > sqrt(2)), i.e. the
+// nearest integer to log2 r (log2 r is never a half-integer for binary32 r).
+// 0x3504F3 is the largest 23-bit mantissa fraction below sqrt(2) - 1.
+MXFP4_HD uint32_t amct_e8(float amax_f, float sf) {
+  float r = amax_f / sf;
+  if (!(r >= 0x1p-30f)) r = 0x1p-30f;
+  uint32_t rb = __builtin_bit_cast(uint32_t, r);
+  uint32_t e = (rb >> 23) + ((rb & 0x7FFFFFu) > 0x3504F3u ? 1u : 0u);
+  return e > 254u ? 254u : e;
+}
+
+template <int DT>
+MXFP4_HD BlockParams amct_params(uint32_t e8) {
+  constexpr int MB = Fmt<DT>::MB;
+  constexpr uint32_t Q = Fmt<DT>::Q;
+  BlockParams p;
+  p.e8 = e8;  // >= 97 always, so the closed form applies
+  uint32_t t025 = (e8 - 2) << MB;
+  p.t025 = t025 - 1;
+  p.half = t025 + 2 * Q;
+  p.six = t025 + 9 * Q;
+  p.slow = false;
+  return p;
+}
+
+// ---- closed-form snap --------------------------------------------------------
+// bf16: two elements per register, constants replicated (or per-half).
+struct SnapBF16 {
+  uint32_t mag;  // packed magnitude bits of code * 2^k
+  uint32_t idx;  // packed E2M1 magnitude codes (0..7)
+};
+
+MXFP4_HD uint32_t snap_mag_bf16(uint32_t a, uint32_t t025p2, uint32_t half2) {
+  uint32_t u = pk_subsat(a, t025p2);
+  uint32_t r = pk_add(u, 0x001F001Fu) & 0xFFC0FFC0u;
+  uint32_t h = pk_min(pk_subsat(r, 0x01000100u), 0x01400140u);
+  uint32_t z = pk_min(u, 0x00010001u);
+  uint32_t c = pk_min(pk_subsat(u, 0x00C000C0u), 0x00010001u);
+  return pk_mad(c, 0x00800080u, pk_mad(z, half2, h));
+}
+
+MXFP4_HD uint32_t snap_idx_bf16(uint32_t a, uint32_t t025p2) {
+  uint32_t u = pk_subsat(a, t025p2);
+  uint32_t r = pk_add(u, 0x001F001Fu) & 0xFFC0FFC0u;
+  uint32_t h = pk_min(pk_subsat(r, 0x01000100u), 0x01400140u);
+  uint32_t z = pk_min(u, 0x00010001u);
+  uint32_t c = pk_min(pk_subsat(u, 0x00C000C0u), 0x00010001u);
+  return pk_add(pk_add(z, c), pk_shr(h, 6));
+}
+
+// sign bit kept for negative non-zero inputs only (-0.0 -> +0.0)
+MXFP4_HD uint32_t sign_bf16(uint32_t p) { return p & pk_sub(p, 0x00010001u) & 0x80008000u; }
+MXFP4_HD uint32_t mask_bits_bf16(uint32_t a, uint32_t six2) {
+  return pk_min(pk_subsat(a, six2), 0x00010001u);
+}
+
+// fp32: one element per register.
+MXFP4_HD uint32_t snap_mag_f32(uint32_t a, uint32_t t025p, uint32_t half) {
+  constexpr uint32_t Q = Fmt<kF32>::Q;
+  uint32_t u = subsat32(a, t025p);
+  uint32_t r = (u + (Q / 2 - 1)) & ~(Q - 1);
+  uint32_t h = min32(subsat32(r, 4 * Q), 5 * Q);
+  uint32_t z = min32(u, 1u);
+  uint32_t c = min32(subsat32(u, 3 * Q), 1u);
+  return h + z * half + c * (2 * Q);
+}
+MXFP4_HD uint32_t snap_idx_f32(uint32_t a, uint32_t t025p) {
+  constexpr uint32_t Q = Fmt<kF32>::Q;
+  uint32_t u = subsat32(a, t025p);
+  uint32_t r = (u + (Q / 2 - 1)) & ~(Q - 1);
+  uint32_t h = min32(subsat32(r, 4 * Q), 5 * Q);
+  uint32_t z = min32(u, 1u);
+  uint32_t c = min32(subsat32(u, 3 * Q), 1u);
+  return z + c + (h >> 22);
+}
+MXFP4_HD uint32_t sign_f32(uint32_t p) { return p & (p - 1u) & 0x80000000u; }
+
+// ---- generic snap for FLOOR blocks with E8M0 byte 0, 1 or 2 ------------------
+// Values are handled as integer multiples L of the dtype's smallest subnormal
+// (bf16 2^-133, fp32 2^-149); lin_to_bits turns such an L (with at most MB+1
+// significant bits) into IEEE magnitude bits, subnormal or normal.
+template <int DT>
+MXFP4_HD uint32_t lin_to_bits(uint32_t L) {
+  constexpr int MB = Fmt<DT>::MB;
+  if (L < (2u << MB)) return L;
+  int msb = 31 - __builtin_clz(L);
+  int e = msb - MB;
+  return ((uint32_t)e << MB) + (L >> e);
+}
+
+// Snap one magnitude (32-bit, low bits) for E8M0 byte e8 in {0,1,2}: count the
+// midpoints m*2^k (m = n/4, n = 1 3 5 7 10 14 20) that |x| exceeds, then
+// return the bits of code*2^k (code*4 = 0 2 4 6 8 12 16 24).
+template <int DT>
+MXFP4_HD uint32_t slow_snap(uint32_t a, uint32_t e8, uint32_t *idx_out) {
+  constexpr int MB = Fmt<DT>::MB;
+  const unsigned sh = e8 + MB - 3;  // 2^(k-2) in subnormal units
+  const uint32_t n[7] = {1, 3, 5, 7, 10, 14, 20};
+  const uint32_t c4[8] = {0, 2, 4, 6, 8, 12, 16, 24};
+  uint32_t idx = 0;
+  for (int i = 0; i < 7; ++i) idx += (a > lin_to_bits<DT>(n[i] << sh)) ? 1u : 0u;
+  if (idx_out) *idx_out = idx;
+  return lin_to_bits<DT>(c4[idx] << sh);
+}
+template <int DT>
+MXFP4_HD uint32_t slow_six(uint32_t e8) {
+  constexpr int MB = Fmt<DT>::MB;
+  return lin_to_bits<DT>(24u << (e8 + MB - 3));
+}
+
+}  // namespace mxfp4

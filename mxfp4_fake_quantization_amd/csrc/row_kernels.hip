@@ -1,0 +1,239 @@
+// row_kernels.hip -- row-wise MXFP4 fake quantization on gfx950.
+//
+// Blocks of 32 or 128 consecutive elements along each row (the pages'
+// last-dim blocking, fake_quant.py _block_view; a row's last block is short
+// when cols % block != 0 and blocks never straddle rows).  One pass reads x
+// once and emits any of: the dequantized values y, the clipped-STE bitmap,
+// the E8M0 scale bytes, and the packed E2M1 nibbles (two per byte).
+//
+// Work split: a "chunk" is 8 consecutive elements of one row (16 bytes of
+// bf16, 32 bytes of fp32) held by one lane; a block is 4 (block 32) or 16
+// (block 128) consecutive lanes, reduced with DPP.  Each thread issues all of
+// its U chunk loads before any arithmetic, and consecutive lanes read
+// consecutive 16-byte pieces, so every load instruction covers one contiguous
+// 1 KiB (bf16) stretch of HBM.
+#include "mxfp4_device.h"
+#include "mxfp4_kernels.h"
+
+namespace mxfp4 {
+namespace {
+
+constexpr int kRowUnroll = 4;
+
+enum { kModeFlat = 0, kModeRowsVec = 1, kModeRowsScalar = 2 };
+
+struct RowArgs {
+  const uint8_t *x;
+  uint8_t *y;
+  uint8_t *mask;    // bitmap as bytes: byte (r, j) holds columns 8j..8j+7
+  uint8_t *scales;
+  uint8_t *codes;
+  int64_t cols;
+  int64_t nchunks;  // chunks in the launch (a multiple of the group size)
+  int64_t cpr;      // chunks per row, padded to whole blocks (row modes)
+  int64_t nb;       // blocks per row
+  int64_t mask_row_bytes;  // 4 * ceil(cols / 32)
+  int64_t code_row_bytes;  // ceil(cols / 2)
+  float sf;
+  uint32_t emit;
+};
+
+template <int DT>
+struct ChunkT {
+  static constexpr int NW = DT == kBF16 ? 4 : 8;  // 32-bit words per chunk
+  static constexpr int ES = DT == kBF16 ? 2 : 4;  // element bytes
+};
+
+template <int DT>
+__device__ __forceinline__ void load_vec(uint32_t *w, const uint8_t *p) {
+  uint4 v = ld16(p);
+  w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  if (DT == kF32) {
+    uint4 v2 = ld16(p + 16);
+    w[4] = v2.x; w[5] = v2.y; w[6] = v2.z; w[7] = v2.w;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_vec(uint8_t *p, const uint32_t *w) {
+  st16(p, make_uint4(w[0], w[1], w[2], w[3]));
+  if (DT == kF32) st16(p + 16, make_uint4(w[4], w[5], w[6], w[7]));
+}
+
+template <int DT>
+__device__ __forceinline__ void load_scalar(uint32_t *w, const uint8_t *p, int n) {
+  constexpr int NW = ChunkT<DT>::NW;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) w[k] = 0;
+  for (int j = 0; j < n; ++j) {
+    if (DT == kBF16) w[j >> 1] |= (uint32_t)reinterpret_cast<const uint16_t *>(p)[j] << (16 * (j & 1));
+    else w[j] = reinterpret_cast<const uint32_t *>(p)[j];
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_scalar(uint8_t *p, const uint32_t *w, int n) {
+  for (int j = 0; j < n; ++j) {
+    if (DT == kBF16) reinterpret_cast<uint16_t *>(p)[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+    else reinterpret_cast<uint32_t *>(p)[j] = w[j];
+  }
+}
+
+template <int DT, int B, int RULE, int MODE, bool FULL>
+__device__ __forceinline__ void row_fwd_body(const RowArgs &A) {
+  constexpr int G = B / 8;
+  constexpr int NW = ChunkT<DT>::NW;
+  constexpr int ES = ChunkT<DT>::ES;
+  constexpr int U = kRowUnroll;
+  const int tid = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * U);
+
+  uint32_t w[U][NW];
+  int64_t off[U], row[U], cr[U];
+  int nval[U];
+#pragma unroll
+  for (int s = 0; s < U; ++s) {
+    const int64_t i = base + s * kThreads + tid;
+    if (MODE == kModeFlat) {
+      row[s] = 0;
+      cr[s] = i;
+      off[s] = i * 8;
+      nval[s] = (FULL || i < A.nchunks) ? 8 : 0;
+    } else {
+      const int64_t r = i / A.cpr;
+      const int64_t c = i - r * A.cpr;
+      row[s] = r;
+      cr[s] = c;
+      off[s] = r * A.cols + c * 8;
+      const int64_t rem = A.cols - c * 8;
+      nval[s] = i < A.nchunks ? (int)(rem >= 8 ? 8 : (rem > 0 ? rem : 0)) : 0;
+    }
+    if (MODE == kModeRowsScalar) {
+      load_scalar<DT>(w[s], A.x + off[s] * ES, nval[s]);
+    } else if (FULL || nval[s] == 8) {
+      load_vec<DT>(w[s], A.x + off[s] * ES);
+    } else {
+#pragma unroll
+      for (int k = 0; k < NW; ++k) w[s][k] = 0;
+    }
+  }
+
+  const uint32_t emit = A.emit;
+#pragma unroll
+  for (int s = 0; s < U; ++s) {
+    // block max of the magnitude bits (integer max == float max for finite x)
+    uint32_t am;
+    if (DT == kBF16) {
+      uint32_t m = pk_max(pk_max(w[s][0] & 0x7FFF7FFFu, w[s][1] & 0x7FFF7FFFu),
+                          pk_max(w[s][2] & 0x7FFF7FFFu, w[s][3] & 0x7FFF7FFFu));
+      am = max32(m & 0xFFFFu, m >> 16);
+    } else {
+      am = 0;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) am = max32(am, w[s][k] & 0x7FFFFFFFu);
+    }
+    am = group_max<G>(am);
+    const BlockParams bp = block_params<DT, RULE>(am, A.sf);
+
+    const bool live = nval[s] > 0;
+    if (emit & kEmitY) {
+      uint32_t yv[NW];
+      chunk_y<DT>(w[s], bp, yv);
+      uint8_t *dst = A.y + off[s] * ES;
+      if (MODE == kModeRowsScalar) {
+        if (live) store_scalar<DT>(dst, yv, nval[s]);
+      } else if (nval[s] == 8) {
+        store_vec<DT>(dst, yv);
+      }
+    }
+    if (emit & kEmitMask) {
+      const uint32_t byte = chunk_mask<DT>(w[s], bp);
+      if (MODE == kModeFlat) {
+        if (live) A.mask[cr[s]] = (uint8_t)byte;
+      } else if (base + s * kThreads + tid < A.nchunks && cr[s] < A.mask_row_bytes) {
+        A.mask[row[s] * A.mask_row_bytes + cr[s]] = (uint8_t)byte;
+      }
+    }
+    if (emit & kEmitCodes) {
+      const uint32_t nib = chunk_codes<DT>(w[s], bp);
+      if (MODE == kModeFlat) {
+        if (live) reinterpret_cast<uint32_t *>(A.codes)[cr[s]] = nib;
+      } else if (MODE == kModeRowsVec) {
+        if (nval[s] == 8)
+          *reinterpret_cast<uint32_t *>(A.codes + row[s] * A.code_row_bytes + 4 * cr[s]) = nib;
+      } else if (live) {
+        uint8_t *dst = A.codes + row[s] * A.code_row_bytes + 4 * cr[s];
+        for (int j = 0; j < (nval[s] + 1) / 2; ++j) dst[j] = (uint8_t)(nib >> (8 * j));
+      }
+    }
+    if ((emit & kEmitScales) && (tid % G) == 0 && base + s * kThreads + tid < A.nchunks) {
+      const int64_t bi = MODE == kModeFlat ? cr[s] / G : row[s] * A.nb + cr[s] / G;
+      A.scales[bi] = (uint8_t)bp.e8;
+    }
+  }
+}
+
+// A workgroup whose chunks are all in range (every one but possibly the
+// last, in the flat layout) takes the branch-free load path.
+template <int DT, int B, int RULE, int MODE>
+__global__ __launch_bounds__(kThreads) void row_fwd_kernel(RowArgs A) {
+  if (MODE == kModeFlat &&
+      (int64_t)(blockIdx.x + 1) * (kThreads * kRowUnroll) <= A.nchunks)
+    row_fwd_body<DT, B, RULE, MODE, true>(A);
+  else
+    row_fwd_body<DT, B, RULE, MODE, false>(A);
+}
+
+template <int DT, int B, int RULE>
+hipError_t dispatch_mode(int mode, const RowArgs &a, dim3 grid, hipStream_t st) {
+  switch (mode) {
+    case kModeFlat: hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, kModeFlat>), grid, dim3(kThreads), 0, st, a); break;
+    case kModeRowsVec: hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, kModeRowsVec>), grid, dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, kModeRowsScalar>), grid, dim3(kThreads), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <int DT, int B>
+hipError_t dispatch_rule(int rule, int mode, const RowArgs &a, dim3 grid, hipStream_t st) {
+  return rule == kFloor ? dispatch_mode<DT, B, kFloor>(mode, a, grid, st)
+                        : dispatch_mode<DT, B, kAmct>(mode, a, grid, st);
+}
+
+}  // namespace
+
+hipError_t launch_row_fwd(const RowLaunch &L, hipStream_t st) {
+  RowArgs a;
+  a.x = static_cast<const uint8_t *>(L.x);
+  a.y = static_cast<uint8_t *>(L.y);
+  a.mask = reinterpret_cast<uint8_t *>(L.mask);
+  a.scales = L.scales;
+  a.codes = L.codes;
+  a.cols = L.cols;
+  a.nb = (L.cols + L.block - 1) / L.block;
+  a.cpr = a.nb * (L.block / 8);
+  a.mask_row_bytes = 4 * ((L.cols + 31) / 32);
+  a.code_row_bytes = (L.cols + 1) / 2;
+  a.sf = L.sf;
+  a.emit = (L.y ? kEmitY : 0) | (L.mask ? kEmitMask : 0) | (L.scales ? kEmitScales : 0) |
+           (L.codes ? kEmitCodes : 0);
+  int mode;
+  if (L.cols % L.block == 0) {
+    mode = kModeFlat;
+    a.nchunks = L.rows * L.cols / 8;
+  } else {
+    mode = (L.cols % 8 == 0) ? kModeRowsVec : kModeRowsScalar;
+    a.nchunks = L.rows * a.cpr;
+  }
+  const int64_t per_wg = (int64_t)kThreads * kRowUnroll;
+  const int64_t nwg = (a.nchunks + per_wg - 1) / per_wg;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  dim3 grid((unsigned)nwg);
+  if (L.dtype == kBF16)
+    return L.block == 32 ? dispatch_rule<kBF16, 32>(L.rule, mode, a, grid, st)
+                         : dispatch_rule<kBF16, 128>(L.rule, mode, a, grid, st);
+  return L.block == 32 ? dispatch_rule<kF32, 32>(L.rule, mode, a, grid, st)
+                       : dispatch_rule<kF32, 128>(L.rule, mode, a, grid, st);
+}
+
+}  // namespace mxfp4

@@ -1,0 +1,261 @@
+// ste_kernels.hip -- straight-through-estimator backward on gfx950.
+//
+// _MXFP4FakeQuantSTE.backward of the amct PR: the clipped STE returns
+// grad_output.masked_fill(saturated, 0.0); the plain STE returns grad_output
+// unchanged.  Here the saturation mask is the bitmap the forward wrote, so the
+// backward is one streaming pass: read g (16 B per lane-piece) and the mask
+// bits, write +0.0 where a bit is set and g elsewhere.
+//   ROW bitmaps: one mask byte per 8-element piece, same chunk walk as the
+//     row-wise forward.
+//   COL / GROUPED bitmaps: 32-row slabs; a lane loads the 8 words of its 8
+//     columns once and serves its 8 rows from them.
+#include "mxfp4_device.h"
+#include "mxfp4_groups.h"
+#include "mxfp4_kernels.h"
+
+namespace mxfp4 {
+namespace {
+
+constexpr int kSteUnroll = 4;
+enum { kModeFlat = 0, kModeRowsVec = 1, kModeRowsScalar = 2 };
+
+// Clear the elements whose bit is set.  bf16 word k holds elements 2k, 2k+1
+// (bits 2k, 2k+1 of `bits`); fp32 word k holds element k.
+template <int DT>
+__device__ __forceinline__ void apply_bits(uint32_t *w, uint32_t bits) {
+  if (DT == kBF16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_sbfe((int)bits, 2 * k, 1);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_sbfe((int)bits, 2 * k + 1, 1);
+      const uint32_t sel = (lo & 0xFFFFu) | (hi & 0xFFFF0000u);
+      w[k] &= ~sel;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] &= ~(uint32_t)__builtin_amdgcn_sbfe((int)bits, k, 1);
+  }
+}
+
+struct SteRowArgs {
+  const uint8_t *g;
+  uint8_t *gi;
+  const uint8_t *mask;  // NULL: plain STE
+  int64_t cols, nchunks, cpr, mask_row_bytes;
+};
+
+template <int DT, int MODE>
+__global__ __launch_bounds__(kThreads) void ste_row_kernel(SteRowArgs A) {
+  constexpr int NW = DT == kBF16 ? 4 : 8;
+  constexpr int ES = DT == kBF16 ? 2 : 4;
+  constexpr int U = kSteUnroll;
+  const int tid = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * U);
+  uint32_t w[U][NW];
+  uint32_t bits[U];
+  int64_t off[U];
+  int nval[U];
+#pragma unroll
+  for (int s = 0; s < U; ++s) {
+    const int64_t i = base + s * kThreads + tid;
+    int64_t mb;
+    if (MODE == kModeFlat) {
+      off[s] = i * 8;
+      nval[s] = i < A.nchunks ? 8 : 0;
+      mb = i;
+    } else {
+      const int64_t r = i / A.cpr, c = i - r * A.cpr;
+      off[s] = r * A.cols + c * 8;
+      const int64_t rem = A.cols - c * 8;
+      nval[s] = i < A.nchunks ? (int)(rem >= 8 ? 8 : (rem > 0 ? rem : 0)) : 0;
+      mb = r * A.mask_row_bytes + c;
+    }
+#pragma unroll
+    for (int k = 0; k < NW; ++k) w[s][k] = 0;
+    bits[s] = 0;
+    if (nval[s] > 0) {
+      const uint8_t *p = A.g + off[s] * ES;
+      if (MODE != kModeRowsScalar) {
+        uint4 v = ld16(p);
+        w[s][0] = v.x; w[s][1] = v.y; w[s][2] = v.z; w[s][3] = v.w;
+        if (DT == kF32) {
+          uint4 v2 = ld16(p + 16);
+          w[s][4] = v2.x; w[s][5] = v2.y; w[s][6] = v2.z; w[s][7] = v2.w;
+        }
+      } else {
+        for (int j = 0; j < nval[s]; ++j) {
+          if (DT == kBF16) w[s][j >> 1] |= (uint32_t)reinterpret_cast<const uint16_t *>(p)[j] << (16 * (j & 1));
+          else w[s][j] = reinterpret_cast<const uint32_t *>(p)[j];
+        }
+      }
+      if (A.mask) bits[s] = A.mask[mb];
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < U; ++s) {
+    if (nval[s] == 0) continue;
+    apply_bits<DT>(w[s], bits[s]);
+    uint8_t *p = A.gi + off[s] * ES;
+    if (MODE != kModeRowsScalar) {
+      st16(p, make_uint4(w[s][0], w[s][1], w[s][2], w[s][3]));
+      if (DT == kF32) st16(p + 16, make_uint4(w[s][4], w[s][5], w[s][6], w[s][7]));
+    } else {
+      for (int j = 0; j < nval[s]; ++j) {
+        if (DT == kBF16) reinterpret_cast<uint16_t *>(p)[j] = (uint16_t)(w[s][j >> 1] >> (16 * (j & 1)));
+        else reinterpret_cast<uint32_t *>(p)[j] = w[s][j];
+      }
+    }
+  }
+}
+
+struct SteColArgs {
+  const uint8_t *g;
+  uint8_t *gi;
+  const uint32_t *mask;
+  const int64_t *group_list;
+  int64_t rows, cols, nct;
+  int num_groups, list_type, block_log2;
+};
+
+// One workgroup = one 32-row slab x 512 columns (4 waves side by side).
+template <int DT, bool GROUPED, bool VEC>
+__global__ __launch_bounds__(kThreads) void ste_col_kernel(SteColArgs A) {
+  constexpr int NW = DT == kBF16 ? 4 : 8;
+  constexpr int ES = DT == kBF16 ? 2 : 4;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int rg = lane & 3, cc = lane >> 2;
+  const int64_t ts = blockIdx.x / A.nct;
+  const int64_t ct = blockIdx.x - ts * A.nct;
+  int64_t start, len;
+  if (GROUPED) {
+    __shared__ int64_t s_blk[2];
+    const int sub_log2 = A.block_log2 - 5;  // 32-row slabs per block-row (log2)
+    const int64_t t = ts >> sub_log2;
+    const int64_t q = ts - (t << sub_log2);
+    if (wave == 0) find_block_row(A.group_list, A.num_groups, A.list_type, A.rows, A.block_log2, t, s_blk);
+    __syncthreads();
+    start = s_blk[0] + 32 * q;
+    len = s_blk[1] - 32 * q;
+    if (len <= 0) return;  // whole workgroup
+    if (len > 32) len = 32;
+  } else {
+    start = 32 * ts;
+    len = A.rows - start < 32 ? A.rows - start : 32;
+  }
+  const int64_t c0 = ct * 512 + 128 * wave + 8 * cc;
+  const int64_t crem = A.cols - c0;
+  const int ncol = crem >= 8 ? 8 : (crem > 0 ? (int)crem : 0);
+  if (ncol == 0) return;  // no barrier follows
+
+  // the 8 bitmap words of this lane's columns
+  uint32_t mw[8];
+  const uint32_t *mp = A.mask + ts * A.cols + c0;
+  if (VEC) {
+    uint4 a = *reinterpret_cast<const uint4 *>(mp);
+    uint4 b = *reinterpret_cast<const uint4 *>(mp + 4);
+    mw[0] = a.x; mw[1] = a.y; mw[2] = a.z; mw[3] = a.w;
+    mw[4] = b.x; mw[5] = b.y; mw[6] = b.z; mw[7] = b.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mw[k] = k < ncol ? mp[k] : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rr = 8 * rg + i;
+    if (rr >= len) continue;
+    const uint8_t *p = A.g + ((start + rr) * A.cols + c0) * ES;
+    uint8_t *q = A.gi + ((start + rr) * A.cols + c0) * ES;
+    uint32_t w[NW];
+    uint32_t bits = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) bits |= ((mw[k] >> rr) & 1u) << k;
+    if (VEC) {
+      uint4 v = ld16(p);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+      if (DT == kF32) {
+        uint4 v2 = ld16(p + 16);
+        w[4] = v2.x; w[5] = v2.y; w[6] = v2.z; w[7] = v2.w;
+      }
+      apply_bits<DT>(w, bits);
+      st16(q, make_uint4(w[0], w[1], w[2], w[3]));
+      if (DT == kF32) st16(q + 16, make_uint4(w[4], w[5], w[6], w[7]));
+    } else {
+      for (int j = 0; j < ncol; ++j) {
+        uint32_t e = DT == kBF16 ? reinterpret_cast<const uint16_t *>(p)[j] : reinterpret_cast<const uint32_t *>(p)[j];
+        if ((bits >> j) & 1u) e = 0;
+        if (DT == kBF16) reinterpret_cast<uint16_t *>(q)[j] = (uint16_t)e;
+        else reinterpret_cast<uint32_t *>(q)[j] = e;
+      }
+    }
+  }
+}
+
+template <int DT>
+hipError_t launch_row(const SteLaunch &L, hipStream_t st) {
+  SteRowArgs a;
+  a.g = static_cast<const uint8_t *>(L.g);
+  a.gi = static_cast<uint8_t *>(L.g_in);
+  a.mask = reinterpret_cast<const uint8_t *>(L.mask);
+  a.cols = L.cols;
+  a.cpr = (L.cols + 7) / 8;
+  a.mask_row_bytes = 4 * ((L.cols + 31) / 32);
+  int mode;
+  if (L.cols % 32 == 0) {
+    mode = kModeFlat;
+    a.nchunks = L.rows * L.cols / 8;
+  } else {
+    mode = L.cols % 8 == 0 ? kModeRowsVec : kModeRowsScalar;
+    a.nchunks = L.rows * a.cpr;
+  }
+  const int64_t per = (int64_t)kThreads * kSteUnroll;
+  const int64_t nwg = (a.nchunks + per - 1) / per;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  dim3 grid((unsigned)nwg);
+  switch (mode) {
+    case kModeFlat: hipLaunchKernelGGL((ste_row_kernel<DT, kModeFlat>), grid, dim3(kThreads), 0, st, a); break;
+    case kModeRowsVec: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsVec>), grid, dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsScalar>), grid, dim3(kThreads), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_col(const SteLaunch &L, hipStream_t st) {
+  SteColArgs a;
+  a.g = static_cast<const uint8_t *>(L.g);
+  a.gi = static_cast<uint8_t *>(L.g_in);
+  a.mask = L.mask;
+  a.group_list = L.group_list;
+  a.rows = L.rows;
+  a.cols = L.cols;
+  a.nct = (L.cols + 511) / 512;
+  a.num_groups = L.num_groups;
+  a.list_type = L.list_type;
+  a.block_log2 = L.block == 32 ? 5 : 7;
+  const bool grouped = L.layout == 4;
+  int64_t slabs = (L.rows + 31) / 32;
+  if (grouped) slabs = ((L.rows + L.block - 1) / L.block + L.num_groups) * (L.block / 32);
+  const int64_t nwg = slabs * a.nct;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  dim3 grid((unsigned)nwg);
+  const bool vec = L.cols % 8 == 0;
+  if (grouped) {
+    if (vec) hipLaunchKernelGGL((ste_col_kernel<DT, true, true>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((ste_col_kernel<DT, true, false>), grid, dim3(kThreads), 0, st, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((ste_col_kernel<DT, false, true>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((ste_col_kernel<DT, false, false>), grid, dim3(kThreads), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ste_bwd(const SteLaunch &L, hipStream_t st) {
+  // plain STE and ROW bitmaps share the chunk walk (mask NULL = copy)
+  if (L.mask == nullptr || L.layout == 1)
+    return L.dtype == kBF16 ? launch_row<kBF16>(L, st) : launch_row<kF32>(L, st);
+  return L.dtype == kBF16 ? launch_col<kBF16>(L, st) : launch_col<kF32>(L, st);
+}
+
+}  // namespace mxfp4

@@ -1,0 +1,83 @@
+// Host build of the kernels' integer MXFP4 math (csrc/mxfp4_math.h), driven
+// row-wise exactly as a kernel lane does it: block max of magnitude bits, block
+// parameters, closed-form or generic snap, sign, mask, nibble.  Compiled for
+// the CPU by tests/test_host_math.py and compared with the oracle; it shares
+// no code with the oracle.
+#include <stdint.h>
+#include <string.h>
+
+#include "mxfp4_math.h"
+
+using namespace mxfp4;
+
+template <int DT>
+static void run_block(const uint32_t *p, int n, int rule, float sf, uint32_t *y,
+                      uint8_t *clip, uint8_t *nib, uint8_t *e8out) {
+  constexpr uint32_t ABS = Fmt<DT>::ABS;
+  uint32_t amax = 0;
+  for (int j = 0; j < n; ++j) amax = max32(amax, p[j] & ABS);
+  BlockParams bp;
+  if (rule == kFloor) {
+    bp = floor_params<DT>(amax);
+  } else {
+    float af = __builtin_bit_cast(float, DT == kBF16 ? amax << 16 : amax);
+    bp = amct_params<DT>(amct_e8(af, sf));
+  }
+  *e8out = (uint8_t)bp.e8;
+  for (int j = 0; j < n; ++j) {
+    uint32_t a = p[j] & ABS;
+    uint32_t mag, idx, six, sgn;
+    if (bp.slow) {
+      mag = slow_snap<DT>(a, bp.e8, &idx);
+      six = slow_six<DT>(bp.e8);
+    } else if (DT == kBF16) {
+      // run the packed form with the element in the high half and a zero in
+      // the low half, so both lanes of the packed ops are exercised
+      uint32_t a2 = a << 16;
+      uint32_t m2 = snap_mag_bf16(a2, splat16(bp.t025), splat16(bp.half));
+      uint32_t i2 = snap_idx_bf16(a2, splat16(bp.t025));
+      if ((m2 & 0xFFFF) != 0 || (i2 & 0xFFFF) != 0) { mag = 0xDEAD; idx = 15; six = 0; }
+      else { mag = m2 >> 16; idx = i2 >> 16; six = bp.six; }
+      uint32_t mb = mask_bits_bf16(a2, splat16(bp.six));
+      if ((mb >> 16) != (a > bp.six ? 1u : 0u)) mag = 0xBEEF;
+    } else {
+      mag = snap_mag_f32(a, bp.t025, bp.half);
+      idx = snap_idx_f32(a, bp.t025);
+      six = bp.six;
+    }
+    if (DT == kBF16) {
+      uint32_t s2 = sign_bf16(p[j] << 16 | p[j]);
+      sgn = s2 & 0x8000u;
+      if ((s2 >> 16) != sgn) sgn = 0x4000;  // both halves must agree
+    } else {
+      sgn = sign_f32(p[j]);
+    }
+    y[j] = mag | sgn;
+    clip[j] = a > six;
+    nib[j] = (uint8_t)(idx | (sgn ? 8 : 0));
+  }
+}
+
+extern "C" int host_qdq_rows(int dtype, int64_t rows, int64_t cols, int block, int rule,
+                             float sf, const void *x, void *y, uint8_t *clip, uint8_t *e8,
+                             uint8_t *nib) {
+  int64_t nb = (cols + block - 1) / block;
+  uint32_t p[128], q[128];
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < nb; ++b) {
+      int64_t c0 = b * block;
+      int n = (int)((cols - c0) < block ? (cols - c0) : block);
+      int64_t o = r * cols + c0;
+      for (int j = 0; j < n; ++j)
+        p[j] = dtype == kBF16 ? ((const uint16_t *)x)[o + j] : ((const uint32_t *)x)[o + j];
+      if (dtype == kBF16)
+        run_block<kBF16>(p, n, rule, sf, q, clip + o, nib + o, e8 + r * nb + b);
+      else
+        run_block<kF32>(p, n, rule, sf, q, clip + o, nib + o, e8 + r * nb + b);
+      for (int j = 0; j < n; ++j) {
+        if (dtype == kBF16) ((uint16_t *)y)[o + j] = (uint16_t)q[j];
+        else ((uint32_t *)y)[o + j] = q[j];
+      }
+    }
+  return 0;
+}

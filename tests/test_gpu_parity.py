@@ -1,0 +1,429 @@
+"""GPU parity: every output of the HIP library, called through the C-ABI
+binding, equals the CPU oracle bit for bit (tolerance 0 ULP: every produced
+value is exact) on the same seeded inputs.  Small shapes span several tiles
+and ragged tails; the full-size workloads are checked on sampled rows /
+columns (the oracle recomputes exactly those blocks).  Every output buffer
+carries a canary past its end."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import (Guarded, dev, grouped_rows, host, like_bf16_or_f32, unpack_col_bitmap,
+                      unpack_grouped_bitmap, unpack_row_bitmap)
+
+pytestmark = pytest.mark.gpu
+
+M = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    global M
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mxfp4_fake_quantization_amd as mod
+    mod._load()
+    M = mod
+    yield
+
+
+def make_x(shape, dtype, seed, kind="t3"):
+    g = np.random.default_rng(seed)
+    if kind == "t3":
+        a = (g.standard_t(3, size=shape) * np.exp2(g.uniform(-8, 8, (shape[0], 1)))).astype(np.float32)
+    else:
+        a = g.standard_normal(shape).astype(np.float32)
+    a.reshape(-1)[:: 97] = 0.0
+    a.reshape(-1)[5:: 113] = -0.0
+    return W.f32_to_bf16_bits(a) if dtype == "bf16" else a
+
+
+def elem_dtype(x):
+    return like_bf16_or_f32(x)
+
+
+# ------------------------------------------------------------------ row-wise
+
+ROW_SHAPES = [(1, 1), (3, 8), (9, 77), (17, 200), (33, 96), (64, 4096), (5, 1000), (130, 384)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("block", [32, 128])
+@pytest.mark.parametrize("rule", ["floor", "amct"])
+@pytest.mark.parametrize("shape", ROW_SHAPES)
+def test_row_fwd(oracle, dtype, block, rule, shape):
+    x = make_x(shape, dtype, seed=hash((shape, block)) % 1000)
+    rows, cols = shape
+    nw = -(-cols // 32)
+    nb = -(-cols // block)
+    y = Guarded(shape, elem_dtype(x))
+    m = Guarded((rows, nw), torch.int32)
+    s = Guarded((rows, nb), torch.uint8)
+    M.mxfp4_qdq_fwd(dev(x), M.ROW, y_row=y.t, mask_row=m.t, scales_row=s.t, block=block, rule=rule)
+    torch.cuda.synchronize()
+    yo, co, eo = oracle.qdq_rows(x, block, rule)
+    assert np.array_equal(host(y.t), yo)
+    bits, clean = unpack_row_bitmap(host(m.t), cols)
+    assert np.array_equal(bits, co) and clean
+    assert np.array_equal(host(s.t), eo)
+    for g in (y, m, s):
+        g.check_tail()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rule", ["floor", "amct"])
+def test_row_fwd_edge_blocks(oracle, dtype, rule):
+    """Planted ties, codebook points, clipped maxima, signed zeros and tiny /
+    subnormal scales (the generic snap path for FLOOR blocks with k = -127)."""
+    e = W.edge_blocks_f32(32)
+    x = W.f32_to_bf16_bits(e) if dtype == "bf16" else e
+    for block in (32, 128):
+        xx = x if block == 32 else np.ascontiguousarray(x[: (x.shape[0] // 4) * 4].reshape(-1, 128))
+        rows, cols = xx.shape
+        y = Guarded(xx.shape, elem_dtype(xx))
+        m = Guarded((rows, cols // 32), torch.int32)
+        s = Guarded((rows, cols // block), torch.uint8)
+        M.mxfp4_qdq_fwd(dev(xx), M.ROW, y_row=y.t, mask_row=m.t, scales_row=s.t, block=block,
+                        rule=rule)
+        torch.cuda.synchronize()
+        yo, co, eo = oracle.qdq_rows(xx, block, rule)
+        assert np.array_equal(host(y.t), yo)
+        assert np.array_equal(unpack_row_bitmap(host(m.t), cols)[0], co)
+        assert np.array_equal(host(s.t), eo)
+
+
+def test_row_fwd_every_bf16_value(oracle):
+    """All 65536 bf16 patterns (finite ones) under a spread of block maxima."""
+    allb = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    allb = allb[(allb & 0x7F80) != 0x7F80]                     # finite only
+    g = np.random.default_rng(5)
+    rows = []
+    for mx in (0x0001, 0x0080, 0x0180, 0x0200, 0x0280, 0x3000, 0x3F80, 0x3FC0, 0x4A00, 0x7F7F):
+        v = allb[(allb & 0x7FFF) <= mx]
+        v = g.permutation(v)
+        n = len(v) - len(v) % 31
+        blk = np.empty((n // 31, 32), np.uint16)
+        blk[:, 0] = mx
+        blk[:, 1:] = v[:n].reshape(-1, 31)
+        rows.append(blk)
+    x = np.concatenate(rows)
+    for rule in ("floor", "amct"):
+        y = torch.empty(x.shape, dtype=torch.bfloat16, device="cuda")
+        m = torch.empty((x.shape[0], 1), dtype=torch.int32, device="cuda")
+        M.mxfp4_qdq_fwd(dev(x), M.ROW, y_row=y, mask_row=m, rule=rule)
+        yo, co, _ = oracle.qdq_rows(x, 32, rule)
+        assert np.array_equal(host(y), yo)
+        assert np.array_equal(unpack_row_bitmap(host(m), 32)[0], co)
+
+
+def test_row_fwd_in_place(oracle):
+    x = make_x((40, 160), "bf16", 3)
+    t = dev(x)
+    M.mxfp4_qdq_fwd(t, M.ROW, y_row=t)
+    yo, _, _ = oracle.qdq_rows(x, 32, "floor")
+    assert np.array_equal(host(t), yo)
+
+
+# ------------------------------------------------------ column-wise / dual
+
+COL_SHAPES = [(1, 8), (100, 70), (33, 9), (256, 512), (130, 136), (300, 1030), (64, 1)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("block", [32, 128])
+@pytest.mark.parametrize("rule", ["floor", "amct"])
+@pytest.mark.parametrize("shape", COL_SHAPES)
+def test_col_fwd(oracle, dtype, block, rule, shape):
+    x = make_x(shape, dtype, seed=7 + shape[0])
+    rows, cols = shape
+    y = Guarded(shape, elem_dtype(x))
+    m = Guarded((-(-rows // 32), cols), torch.int32)
+    s = Guarded((-(-rows // block), cols), torch.uint8)
+    M.mxfp4_qdq_fwd(dev(x), M.COL, y_col=y.t, mask_col=m.t, scales_col=s.t, block=block, rule=rule)
+    torch.cuda.synchronize()
+    yo, co, eo = oracle.qdq_cols(x, block, rule)
+    assert np.array_equal(host(y.t), yo)
+    bits, clean = unpack_col_bitmap(host(m.t), rows)
+    assert np.array_equal(bits, co) and clean
+    assert np.array_equal(host(s.t), eo)
+    for g in (y, m, s):
+        g.check_tail()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("block", [32, 128])
+@pytest.mark.parametrize("rule", ["floor", "amct"])
+@pytest.mark.parametrize("shape", [(100, 70), (256, 512), (130, 1030), (40, 13)])
+def test_dual_fwd(oracle, dtype, block, rule, shape):
+    x = make_x(shape, dtype, seed=11 + shape[1])
+    rows, cols = shape
+    yr = Guarded(shape, elem_dtype(x))
+    yc = Guarded(shape, elem_dtype(x))
+    mr = Guarded((rows, -(-cols // 32)), torch.int32)
+    mc = Guarded((-(-rows // 32), cols), torch.int32)
+    sr = Guarded((rows, -(-cols // block)), torch.uint8)
+    sc = Guarded((-(-rows // block), cols), torch.uint8)
+    M.mxfp4_qdq_fwd(dev(x), M.ROW | M.COL, y_row=yr.t, mask_row=mr.t, scales_row=sr.t,
+                    y_col=yc.t, mask_col=mc.t, scales_col=sc.t, block=block, rule=rule)
+    torch.cuda.synchronize()
+    yro, cro, ero = oracle.qdq_rows(x, block, rule)
+    yco, cco, eco = oracle.qdq_cols(x, block, rule)
+    assert np.array_equal(host(yr.t), yro)
+    assert np.array_equal(host(yc.t), yco)
+    b, clean = unpack_row_bitmap(host(mr.t), cols)
+    assert np.array_equal(b, cro) and clean
+    b, clean = unpack_col_bitmap(host(mc.t), rows)
+    assert np.array_equal(b, cco) and clean
+    assert np.array_equal(host(sr.t), ero)
+    assert np.array_equal(host(sc.t), eco)
+    for g in (yr, yc, mr, mc, sr, sc):
+        g.check_tail()
+
+
+# ------------------------------------------------------------------ grouped
+
+GROUP_CASES = [
+    (700, 24, [100, 0, 37, 300, 1, 262]),
+    (512, 136, [64, 64, 128, 0, 256]),
+    (97, 40, [0, 97]),
+    (1000, 520, None),
+    (33, 8, [33]),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("block", [32, 128])
+@pytest.mark.parametrize("rule", ["floor", "amct"])
+@pytest.mark.parametrize("case", range(len(GROUP_CASES)))
+@pytest.mark.parametrize("list_type", [1, 0])
+def test_grouped(oracle, dtype, block, rule, case, list_type):
+    rows, cols, counts = GROUP_CASES[case]
+    if counts is None:
+        counts = W.ragged_counts(rows, 9, seed=case, zero_groups=2)
+    counts = np.asarray(counts, np.int64)
+    gl = counts if list_type == 1 else np.cumsum(counts)
+    x = make_x((rows, cols), dtype, seed=case + 50)
+    G = len(counts)
+    nbt = sum(-(-int(c) // block) for c in counts)
+    y = Guarded((rows, cols), elem_dtype(x))
+    m = Guarded((M.grouped_mask_rows_max(rows, block, G), cols), torch.int32, fill=0x5A)
+    s = Guarded((M.grouped_scale_rows_max(rows, block, G), cols), torch.uint8, fill=0x5A)
+    M.mxfp4_grouped_qdq(dev(x), dev(gl), y.t, m.t, s.t, block=block, rule=rule,
+                        group_list_type=list_type)
+    torch.cuda.synchronize()
+    yo, co, eo = oracle.grouped_cols(x, counts, block, rule)
+    assert np.array_equal(host(y.t), yo)
+    mw = host(m.t)
+    bits, clean = unpack_grouped_bitmap(mw[: nbt * (block // 32)], rows, counts, block)
+    assert np.array_equal(bits, co) and clean
+    assert (mw[nbt * (block // 32):].view(np.uint8) == 0x5A).all()   # rows past NBT untouched
+    sh = host(s.t)
+    assert np.array_equal(sh[:nbt], eo)
+    assert (sh[nbt:] == 0x5A).all()
+    for g in (y, m, s):
+        g.check_tail()
+
+
+def test_grouped_rows_past_total_untouched(oracle):
+    """Rows past the groups' total are not written (caller's contract
+    violated on purpose: the list sums to less than rows)."""
+    x = make_x((200, 64), "bf16", 9)
+    counts = np.array([50, 70], np.int64)
+    y = torch.full((200, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    M.mxfp4_grouped_qdq(dev(x), dev(counts), y)
+    yo, _, _ = oracle.grouped_cols(x[:120], counts, 32)
+    yh = host(y)
+    assert np.array_equal(yh[:120], yo)
+    assert (yh[120:] == W.f32_to_bf16_bits(np.float32([7.0]))[0]).all()
+
+
+# ---------------------------------------------------------------- backward
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(9, 77), (33, 96), (17, 200), (300, 1030)])
+@pytest.mark.parametrize("layout", ["row", "col", "grouped"])
+def test_ste_bwd(oracle, dtype, shape, layout):
+    rows, cols = shape
+    x = make_x(shape, dtype, seed=rows * cols)
+    g = make_x(shape, dtype, seed=rows + cols, kind="normal")
+    block = 32 if rows % 2 else 128
+    if layout == "row":
+        m = torch.empty((rows, -(-cols // 32)), dtype=torch.int32, device="cuda")
+        M.mxfp4_qdq_fwd(dev(x), M.ROW, mask_row=m, block=block)
+        _, clip, _ = oracle.qdq_rows(x, block)
+        lay, gl = M.ROW, None
+    elif layout == "col":
+        m = torch.empty((-(-rows // 32), cols), dtype=torch.int32, device="cuda")
+        M.mxfp4_qdq_fwd(dev(x), M.COL, mask_col=m, block=block)
+        _, clip, _ = oracle.qdq_cols(x, block)
+        lay, gl = M.COL, None
+    else:
+        counts = W.ragged_counts(rows, 4, seed=rows, zero_groups=1)
+        gl = dev(counts)
+        m = torch.zeros((M.grouped_mask_rows_max(rows, block, 4), cols), dtype=torch.int32,
+                        device="cuda")
+        y = torch.empty(shape, dtype=elem_dtype(x), device="cuda")
+        M.mxfp4_grouped_qdq(dev(x), gl, y, m, block=block)
+        _, clip, _ = oracle.grouped_cols(x, counts, block)
+        lay = M.GROUPED
+    gi = Guarded(shape, elem_dtype(g))
+    M.mxfp4_ste_bwd(dev(g), m, gi.t, layout=lay, block=block, group_list=gl)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(gi.t), oracle.ste_bwd(g, clip))
+    gi.check_tail()
+    # plain STE: identity; in place with a mask
+    gp = torch.empty(shape, dtype=elem_dtype(g), device="cuda")
+    M.mxfp4_ste_bwd(dev(g), None, gp, layout=lay, block=block, group_list=gl)
+    assert np.array_equal(host(gp), g)
+    gd = dev(g)
+    M.mxfp4_ste_bwd(gd, m, gd, layout=lay, block=block, group_list=gl)
+    assert np.array_equal(host(gd), oracle.ste_bwd(g, clip))
+
+
+# -------------------------------------------------------------------- pack
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("block", [32, 128])
+@pytest.mark.parametrize("rule", ["floor", "amct"])
+@pytest.mark.parametrize("shape", [(3, 8), (9, 77), (33, 96), (17, 200), (64, 4096), (5, 129)])
+def test_pack(oracle, dtype, block, rule, shape):
+    x = make_x(shape, dtype, seed=shape[1] + block)
+    rows, cols = shape
+    codes = Guarded((rows, (cols + 1) // 2), torch.uint8)
+    sc = Guarded((rows, -(-cols // block)), torch.uint8)
+    y = Guarded(shape, elem_dtype(x))
+    m = Guarded((rows, -(-cols // 32)), torch.int32)
+    M.mxfp4_quant_pack(dev(x), codes.t, sc.t, y.t, m.t, block=block, rule=rule)
+    torch.cuda.synchronize()
+    co, so = oracle.pack_rows(x, block, rule)
+    yo, clo, _ = oracle.qdq_rows(x, block, rule)
+    assert np.array_equal(host(codes.t), co)
+    assert np.array_equal(host(sc.t), so)
+    assert np.array_equal(host(y.t), yo)
+    assert np.array_equal(unpack_row_bitmap(host(m.t), cols)[0], clo)
+    # the packed form decodes to the QDQ values
+    dec = oracle.unpack_rows(host(codes.t), host(sc.t), cols, block,
+                             dtype=np.uint16 if dtype == "bf16" else np.float32)
+    assert np.array_equal(dec, yo)
+    for g in (codes, sc, y, m):
+        g.check_tail()
+    # codes + scales only
+    c2 = torch.empty_like(codes.t)
+    s2 = torch.empty_like(sc.t)
+    M.mxfp4_quant_pack(dev(x), c2, s2, block=block, rule=rule)
+    assert np.array_equal(host(c2), co) and np.array_equal(host(s2), so)
+
+
+# ------------------------------------------------------ the five workloads
+
+def test_tiny_qat_linear(oracle):
+    """fp32 weight 32x64 and input 4x64 ~ N(0,1): row-wise block-32 QDQ with
+    the clip mask, then the clipped-STE backward of a ones gradient."""
+    w, xin = W.tiny_qat(0)
+    for a in (w, xin):
+        rows, cols = a.shape
+        y = torch.empty(a.shape, dtype=torch.float32, device="cuda")
+        m = torch.empty((rows, cols // 32), dtype=torch.int32, device="cuda")
+        M.mxfp4_qdq_fwd(dev(a), M.ROW, y_row=y, mask_row=m)
+        ones = torch.ones(a.shape, dtype=torch.float32, device="cuda")
+        gi = torch.empty_like(ones)
+        M.mxfp4_ste_bwd(ones, m, gi, layout=M.ROW)
+        torch.cuda.synchronize()
+        yo, clip, _ = oracle.qdq_rows(a, 32)
+        assert np.array_equal(host(y), yo)
+        assert np.array_equal(host(gi), oracle.ste_bwd(np.ones_like(a), clip))
+        assert np.array_equal(host(gi), 1.0 - clip.astype(np.float32))
+
+
+def test_weight_4k_full(oracle):
+    """bf16 4096x4096 weight with outliers, zero blocks and planted blocks:
+    full parity of y, bitmap and the STE gradient."""
+    x, g, manifest = W.weight_4k()
+    rows, cols = x.shape
+    y = torch.empty(x.shape, dtype=torch.bfloat16, device="cuda")
+    m = torch.empty((rows, cols // 32), dtype=torch.int32, device="cuda")
+    xd, gd = dev(x), dev(g)
+    M.mxfp4_qdq_fwd(xd, M.ROW, y_row=y, mask_row=m)
+    gi = torch.empty_like(gd)
+    M.mxfp4_ste_bwd(gd, m, gi, layout=M.ROW)
+    torch.cuda.synchronize()
+    yo, clip, _ = oracle.qdq_rows(x, 32)
+    assert np.array_equal(host(y), yo)
+    assert np.array_equal(unpack_row_bitmap(host(m), cols)[0], clip)
+    assert np.array_equal(host(gi), oracle.ste_bwd(g, clip))
+    assert len(manifest) > 0 and clip.any()
+
+
+def test_act_dual_sampled(oracle):
+    """bf16 16384x8192 Student-t activation, dual direction in one launch:
+    sampled rows (row view) and sampled column strips (column view)."""
+    x = W.act_dual()
+    rows, cols = x.shape
+    yr = torch.empty(x.shape, dtype=torch.bfloat16, device="cuda")
+    yc = torch.empty_like(yr)
+    mr = torch.empty((rows, cols // 32), dtype=torch.int32, device="cuda")
+    mc = torch.empty((rows // 32, cols), dtype=torch.int32, device="cuda")
+    M.mxfp4_qdq_fwd(dev(x), M.ROW | M.COL, y_row=yr, mask_row=mr, y_col=yc, mask_col=mc)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(0)
+    ri = np.sort(g.choice(rows, 512, replace=False))
+    yo, co, _ = oracle.qdq_rows(x[ri], 32)
+    assert np.array_equal(host(yr[torch.from_numpy(ri).cuda()]), yo)
+    assert np.array_equal(unpack_row_bitmap(host(mr[torch.from_numpy(ri).cuda()]), cols)[0], co)
+    ci = np.sort(g.choice(cols, 256, replace=False))
+    yo, co, _ = oracle.qdq_cols(np.ascontiguousarray(x[:, ci]), 32)
+    cit = torch.from_numpy(ci).cuda()
+    assert np.array_equal(host(yc[:, cit]), yo)
+    assert np.array_equal(unpack_col_bitmap(host(mc[:, cit]), rows)[0], co)
+
+
+def test_moe_grouped_sampled(oracle):
+    """bf16 32768x7168, 8 expert groups (multinomial counts): grouped
+    column-wise block-32 QDQ, sampled column strips against the oracle."""
+    x, counts = W.moe_grouped()
+    rows, cols = x.shape
+    y = torch.empty(x.shape, dtype=torch.bfloat16, device="cuda")
+    sc = torch.empty((M.grouped_scale_rows_max(rows, 32, 8), cols), dtype=torch.uint8, device="cuda")
+    M.mxfp4_grouped_qdq(dev(x), dev(counts), y, scales=sc)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(1)
+    ci = np.sort(g.choice(cols, 128, replace=False))
+    yo, _, eo = oracle.grouped_cols(np.ascontiguousarray(x[:, ci]), counts, 32)
+    cit = torch.from_numpy(ci).cuda()
+    assert np.array_equal(host(y[:, cit]), yo)
+    nbt = eo.shape[0]
+    assert np.array_equal(host(sc[:nbt, cit]), eo)
+    assert (counts % 32 != 0).any()        # ragged group tails exercised
+
+
+@pytest.mark.parametrize("block", [32, 128])
+def test_weight_pack_sampled(oracle, block):
+    """bf16 28672x8192 weight packed row-wise; sampled rows against the
+    oracle, and the decoded sample equals the QDQ values."""
+    x = W.weight_pack()
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((rows, cols // block), dtype=torch.uint8, device="cuda")
+    M.mxfp4_quant_pack(dev(x), codes, sc, block=block)
+    torch.cuda.synchronize()
+    ri = np.sort(np.random.default_rng(2).choice(rows, 1024, replace=False))
+    rit = torch.from_numpy(ri).cuda()
+    co, so = oracle.pack_rows(x[ri], block)
+    assert np.array_equal(host(codes[rit]), co)
+    assert np.array_equal(host(sc[rit]), so)
+    yo, _, _ = oracle.qdq_rows(x[ri], block)
+    assert np.array_equal(oracle.unpack_rows(co, so, cols, block), yo)
+
+
+def test_repeatable():
+    """Two runs give identical bits (no races)."""
+    x = dev(make_x((512, 2048), "bf16", 1))
+    outs = []
+    for _ in range(2):
+        yr = torch.empty_like(x)
+        yc = torch.empty_like(x)
+        M.mxfp4_qdq_fwd(x, M.ROW | M.COL, y_row=yr, y_col=yc)
+        outs.append((yr.clone(), yc.clone()))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
