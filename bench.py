@@ -9,12 +9,15 @@ clipped-STE backward of a bf16 N(0,1) gradient.  Inputs are resident in HBM
 before the timed region; S buffer sets (default 8, >1 GiB in total) are used
 in rotation so every step reads data that is not in the 256 MB Infinity Cache.
 
-Prints one JSON line.  value = algorithmic bytes per second (GB/s = 1e9 B/s):
-forward reads x (2 B/elt) and writes y (2 B) + bitmap (1/8 B); backward reads
-g (2 B) + bitmap (1/8 B) and writes g_in (2 B).  roofline = the forward kernel
-against the 8 TB/s HBM peak, its duration from HIP events around every forward
-launch of the timed loop.  cpu_baseline = the CPU oracle (single thread) on
-the same workload, repeated for about 10 s.
+Prints one JSON line.  value = algorithmic bytes per second (GB/s = 1e9 B/s)
+over K back-to-back steps: forward reads x (2 B/elt) and writes y (2 B) +
+bitmap (1/8 B); backward reads g (2 B) + bitmap (1/8 B) and writes g_in (2 B).
+roofline = the forward kernel against the 8 TB/s HBM peak: its average launch
+duration is timed with HIP events over K back-to-back forward launches right
+after the timed steps; traffic = HBM bytes per launch from the committed
+rocprofv3 FETCH_SIZE / WRITE_SIZE run (null if the kernel source changed).
+cpu_baseline = the CPU oracle (single thread) on the same workload, repeated
+for about 10 s.
 
 --all OUT.json additionally times the other workloads (full sizes) and a
 plain device copy, and writes them to OUT.json (stdout keeps one line).
@@ -61,6 +64,47 @@ def measured_traffic(per_launch_alg_bytes: float):
     if t.get("kernel_source_sha") != kernel_source_sha():
         return None
     return float(t["traffic_bytes_per_launch"])
+
+
+class HipEvents:
+    """hipEvent_t handles recorded straight through the HIP runtime (the one
+    torch has loaded), so timing a launch costs the host about a microsecond."""
+
+    def __init__(self, n):
+        import torch
+        lib = None
+        for path in (os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"),
+                     "libamdhip64.so"):
+            try:
+                lib = ctypes.CDLL(path)
+                break
+            except OSError:
+                continue
+        if lib is None:
+            raise RuntimeError("libamdhip64.so not found")
+        self.lib = lib
+        lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if lib.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e)
+        self.record = lib.hipEventRecord
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def close(self):
+        for e in self.ev:
+            self.lib.hipEventDestroy(e)
 
 
 class Call:
@@ -153,28 +197,37 @@ def main():
         bwd[i % args.sets]()
     torch.cuda.synchronize()
 
+    # Timed region: K steps back to back on one stream, bracketed by two HIP
+    # events (per-kernel events inside the loop would add ~2 us per kernel of
+    # marker overhead to the GPU timeline).
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    hev = HipEvents(6)
+    rec, evs = hev.record, hev.ev
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    t_start.record()
+    rec(evs[0], stream)
     for i in range(K):
         s = i % args.sets
-        e = ev[i]
-        e[0].record()
         fwd[s]()
-        e[1].record()
-        e[2].record()
         bwd[s]()
-        e[3].record()
-    t_end.record()
+    rec(evs[1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    total_ms = t_start.elapsed_time(t_end)
-    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    total_ms = hev.ms(0, 1)
+    # Kernel durations for the roofline: K back-to-back launches of one
+    # kernel between two HIP events (the same rotation of buffer sets); the
+    # per-launch average matches rocprofv3's kernel-trace average.
+    rec(evs[2], stream)
+    for i in range(K):
+        fwd[i % args.sets]()
+    rec(evs[3], stream)
+    for i in range(K):
+        bwd[i % args.sets]()
+    rec(evs[4], stream)
+    torch.cuda.synchronize()
+    fwd_ms = np.array([hev.ms(2, 3) / K])
+    bwd_ms = np.array([hev.ms(3, 4) / K])
+    hev.close()
     ms_per_step = total_ms / K
     value = step_bytes * K / (total_ms * 1e-3) / 1e9
 
@@ -202,8 +255,6 @@ def main():
         "elements_per_s": round(2 * n * K / (total_ms * 1e-3), 1),
         "fwd_us": round(float(fwd_ms.mean()) * 1e3, 3),
         "bwd_us": round(float(bwd_ms.mean()) * 1e3, 3),
-        "fwd_us_median": round(float(np.median(fwd_ms)) * 1e3, 3),
-        "bwd_us_median": round(float(np.median(bwd_ms)) * 1e3, 3),
         "wall_s": round(wall, 4),
         "roofline": {"bound": "hbm", "kernel": "row_fwd_kernel<bf16,32,floor,flat>",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -74,8 +74,17 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v) {
 }
 
 // ---- memory --------------------------------------------------------------
-__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
-__device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+// Streaming 16-byte accesses: every element is read once and written once,
+// so loads and stores are non-temporal (no reuse to keep in the caches).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16(const void *p) {
+  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16(void *p, uint4 v) {
+  u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
+}
 
 __device__ __forceinline__ float bits_f32(uint32_t b) { return __builtin_bit_cast(float, b); }
 

@@ -9,16 +9,18 @@
 // Work split: a "chunk" is 8 consecutive elements of one row (16 bytes of
 // bf16, 32 bytes of fp32) held by one lane; a block is 4 (block 32) or 16
 // (block 128) consecutive lanes, reduced with DPP.  Each thread issues all of
-// its U chunk loads before any arithmetic, and consecutive lanes read
-// consecutive 16-byte pieces, so every load instruction covers one contiguous
-// 1 KiB (bf16) stretch of HBM.
+// its U (1 or 2) chunk loads before any arithmetic, and consecutive lanes
+// read consecutive 16-byte pieces, so every load instruction covers one
+// contiguous 1 KiB (bf16) stretch of HBM.
 #include "mxfp4_device.h"
 #include "mxfp4_kernels.h"
 
 namespace mxfp4 {
 namespace {
 
-constexpr int kRowUnroll = 4;
+// Chunks per thread: 1 for small tensors (more, shorter workgroups overlap
+// their loads and stores better), 2 above kRowBigChunks chunks.
+constexpr int64_t kRowBigChunks = int64_t(8) << 20;
 
 enum { kModeFlat = 0, kModeRowsVec = 1, kModeRowsScalar = 2 };
 
@@ -79,12 +81,11 @@ __device__ __forceinline__ void store_scalar(uint8_t *p, const uint32_t *w, int 
   }
 }
 
-template <int DT, int B, int RULE, int MODE, bool FULL>
+template <int DT, int B, int RULE, int MODE, int U, bool FULL>
 __device__ __forceinline__ void row_fwd_body(const RowArgs &A) {
   constexpr int G = B / 8;
   constexpr int NW = ChunkT<DT>::NW;
   constexpr int ES = ChunkT<DT>::ES;
-  constexpr int U = kRowUnroll;
   const int tid = threadIdx.x;
   const int64_t base = (int64_t)blockIdx.x * (kThreads * U);
 
@@ -175,29 +176,38 @@ __device__ __forceinline__ void row_fwd_body(const RowArgs &A) {
 
 // A workgroup whose chunks are all in range (every one but possibly the
 // last, in the flat layout) takes the branch-free load path.
-template <int DT, int B, int RULE, int MODE>
+template <int DT, int B, int RULE, int MODE, int U>
 __global__ __launch_bounds__(kThreads) void row_fwd_kernel(RowArgs A) {
-  if (MODE == kModeFlat &&
-      (int64_t)(blockIdx.x + 1) * (kThreads * kRowUnroll) <= A.nchunks)
-    row_fwd_body<DT, B, RULE, MODE, true>(A);
+  if (MODE == kModeFlat && (int64_t)(blockIdx.x + 1) * (kThreads * U) <= A.nchunks)
+    row_fwd_body<DT, B, RULE, MODE, U, true>(A);
   else
-    row_fwd_body<DT, B, RULE, MODE, false>(A);
+    row_fwd_body<DT, B, RULE, MODE, U, false>(A);
 }
 
-template <int DT, int B, int RULE>
-hipError_t dispatch_mode(int mode, const RowArgs &a, dim3 grid, hipStream_t st) {
-  switch (mode) {
-    case kModeFlat: hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, kModeFlat>), grid, dim3(kThreads), 0, st, a); break;
-    case kModeRowsVec: hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, kModeRowsVec>), grid, dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, kModeRowsScalar>), grid, dim3(kThreads), 0, st, a); break;
-  }
+template <int DT, int B, int RULE, int MODE>
+hipError_t launch_u(const RowArgs &a, hipStream_t st) {
+  const int u = (MODE == kModeFlat && a.nchunks > kRowBigChunks) ? 2 : 1;
+  const int64_t nwg = (a.nchunks + (int64_t)kThreads * u - 1) / ((int64_t)kThreads * u);
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nwg);
+  if (u == 2) hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, MODE, 2>), grid, dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, MODE, 1>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
+template <int DT, int B, int RULE>
+hipError_t dispatch_mode(int mode, const RowArgs &a, hipStream_t st) {
+  switch (mode) {
+    case kModeFlat: return launch_u<DT, B, RULE, kModeFlat>(a, st);
+    case kModeRowsVec: return launch_u<DT, B, RULE, kModeRowsVec>(a, st);
+    default: return launch_u<DT, B, RULE, kModeRowsScalar>(a, st);
+  }
+}
+
 template <int DT, int B>
-hipError_t dispatch_rule(int rule, int mode, const RowArgs &a, dim3 grid, hipStream_t st) {
-  return rule == kFloor ? dispatch_mode<DT, B, kFloor>(mode, a, grid, st)
-                        : dispatch_mode<DT, B, kAmct>(mode, a, grid, st);
+hipError_t dispatch_rule(int rule, int mode, const RowArgs &a, hipStream_t st) {
+  return rule == kFloor ? dispatch_mode<DT, B, kFloor>(mode, a, st)
+                        : dispatch_mode<DT, B, kAmct>(mode, a, st);
 }
 
 }  // namespace
@@ -225,15 +235,11 @@ hipError_t launch_row_fwd(const RowLaunch &L, hipStream_t st) {
     mode = (L.cols % 8 == 0) ? kModeRowsVec : kModeRowsScalar;
     a.nchunks = L.rows * a.cpr;
   }
-  const int64_t per_wg = (int64_t)kThreads * kRowUnroll;
-  const int64_t nwg = (a.nchunks + per_wg - 1) / per_wg;
-  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
-  dim3 grid((unsigned)nwg);
   if (L.dtype == kBF16)
-    return L.block == 32 ? dispatch_rule<kBF16, 32>(L.rule, mode, a, grid, st)
-                         : dispatch_rule<kBF16, 128>(L.rule, mode, a, grid, st);
-  return L.block == 32 ? dispatch_rule<kF32, 32>(L.rule, mode, a, grid, st)
-                       : dispatch_rule<kF32, 128>(L.rule, mode, a, grid, st);
+    return L.block == 32 ? dispatch_rule<kBF16, 32>(L.rule, mode, a, st)
+                         : dispatch_rule<kBF16, 128>(L.rule, mode, a, st);
+  return L.block == 32 ? dispatch_rule<kF32, 32>(L.rule, mode, a, st)
+                       : dispatch_rule<kF32, 128>(L.rule, mode, a, st);
 }
 
 }  // namespace mxfp4

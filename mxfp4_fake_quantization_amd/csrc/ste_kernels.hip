@@ -16,7 +16,11 @@
 namespace mxfp4 {
 namespace {
 
-constexpr int kSteUnroll = 4;
+// Pieces per thread: 4 for small tensors, 1 above kSteBigChunks pieces
+// (measured on MI355X: short workgroups stream large tensors best, while
+// small launches are dominated by their start-up and prefer more loads in
+// flight per thread).
+constexpr int64_t kSteBigChunks = int64_t(8) << 20;
 enum { kModeFlat = 0, kModeRowsVec = 1, kModeRowsScalar = 2 };
 
 // Clear the elements whose bit is set.  bf16 word k holds elements 2k, 2k+1
@@ -44,11 +48,10 @@ struct SteRowArgs {
   int64_t cols, nchunks, cpr, mask_row_bytes;
 };
 
-template <int DT, int MODE>
+template <int DT, int MODE, int U>
 __global__ __launch_bounds__(kThreads) void ste_row_kernel(SteRowArgs A) {
   constexpr int NW = DT == kBF16 ? 4 : 8;
   constexpr int ES = DT == kBF16 ? 2 : 4;
-  constexpr int U = kSteUnroll;
   const int tid = threadIdx.x;
   const int64_t base = (int64_t)blockIdx.x * (kThreads * U);
   uint32_t w[U][NW];
@@ -207,14 +210,23 @@ hipError_t launch_row(const SteLaunch &L, hipStream_t st) {
     mode = L.cols % 8 == 0 ? kModeRowsVec : kModeRowsScalar;
     a.nchunks = L.rows * a.cpr;
   }
-  const int64_t per = (int64_t)kThreads * kSteUnroll;
+  const int u = a.nchunks > kSteBigChunks ? 1 : 4;
+  const int64_t per = (int64_t)kThreads * u;
   const int64_t nwg = (a.nchunks + per - 1) / per;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   dim3 grid((unsigned)nwg);
-  switch (mode) {
-    case kModeFlat: hipLaunchKernelGGL((ste_row_kernel<DT, kModeFlat>), grid, dim3(kThreads), 0, st, a); break;
-    case kModeRowsVec: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsVec>), grid, dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsScalar>), grid, dim3(kThreads), 0, st, a); break;
+  if (u == 1) {
+    switch (mode) {
+      case kModeFlat: hipLaunchKernelGGL((ste_row_kernel<DT, kModeFlat, 1>), grid, dim3(kThreads), 0, st, a); break;
+      case kModeRowsVec: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsVec, 1>), grid, dim3(kThreads), 0, st, a); break;
+      default: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsScalar, 1>), grid, dim3(kThreads), 0, st, a); break;
+    }
+  } else {
+    switch (mode) {
+      case kModeFlat: hipLaunchKernelGGL((ste_row_kernel<DT, kModeFlat, 4>), grid, dim3(kThreads), 0, st, a); break;
+      case kModeRowsVec: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsVec, 4>), grid, dim3(kThreads), 0, st, a); break;
+      default: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsScalar, 4>), grid, dim3(kThreads), 0, st, a); break;
+    }
   }
   return hipGetLastError();
 }
