@@ -94,6 +94,23 @@ __device__ __forceinline__ void store_piece(uint8_t *p, const uint32_t *w, int n
   }
 }
 
+// Generic snap for the halves of a word whose column max is nonzero but has
+// an exponent field below 5 (FLOOR E8M0 byte 0..2).
+__device__ __forceinline__ void fix_slow_word(uint32_t w, uint32_t cm, uint32_t e8p, uint32_t *y,
+                                           uint32_t *m) {
+  const uint32_t lo = cm & 0xFFFFu, hi = cm >> 16;
+  if (lo != 0 && (lo >> 7) < 5) {
+    HalfOut o = half_bf16_slow(w & 0xFFFFu, e8p & 0xFFu);
+    *y = (*y & 0xFFFF0000u) | o.y;
+    *m = (*m & 0xFFFF0000u) | o.m;
+  }
+  if (hi != 0 && (hi >> 7) < 5) {
+    HalfOut o = half_bf16_slow(w >> 16, (e8p >> 16) & 0xFFu);
+    *y = (*y & 0xFFFFu) | (o.y << 16);
+    *m = (*m & 0xFFFFu) | (o.m << 16);
+  }
+}
+
 // Pick word k = 2*rg (+1) of 8 per-lane words without dynamic indexing.
 __device__ __forceinline__ uint32_t pick4(const uint32_t *v, int sel) {
   uint32_t r = v[0];
@@ -103,8 +120,68 @@ __device__ __forceinline__ uint32_t pick4(const uint32_t *v, int sel) {
   return r;
 }
 
+// Column-direction outputs of one lane: y_col rows and the bitmap words of
+// its columns.  SLOW = true only when some lane of the wave holds a column
+// that needs the generic snap.
+template <int DT, int RULE, bool VEC, bool SLOW>
+__device__ __forceinline__ void col_outputs(const ColArgs &A, const uint32_t (&w)[8][ColT<DT>::NW],
+                                            const uint32_t *pt, const uint32_t *ph, const uint32_t *ps,
+                                            const uint32_t *pe, const uint32_t *cm,
+                                            const BlockParams *cbp, int64_t off0, int64_t rstride,
+                                            int rbase, int64_t len, int ncol, int rg, int64_t c0,
+                                            int64_t wrow, bool slab_live) {
+  constexpr int NW = ColT<DT>::NW;
+    uint32_t acc[NW];  // clip bits of this lane's 8 rows (bf16: bit i / 16+i)
+#pragma unroll
+  for (int k = 0; k < NW; ++k) acc[k] = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t yv[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      if (DT == kBF16) {
+        yv[k] = y_bf16(w[i][k], pt[k], ph[k]);
+        uint32_t mb = m_bf16(w[i][k], ps[k]);
+        if (SLOW && RULE == kFloor) fix_slow_word(w[i][k], cm[k], pe[k], &yv[k], &mb);
+        acc[k] |= mb << i;
+      } else {
+        yv[k] = y_f32(w[i][k], cbp[DT == kF32 ? k : 0]);
+        acc[k] |= m_f32(w[i][k], cbp[DT == kF32 ? k : 0]) << i;
+      }
+    }
+    if (A.y_col && rbase + i < len) store_piece<DT, VEC>(A.y_col + off0 + i * rstride, yv, ncol);
+  }
+  if (A.mask_col) {
+    // column word = OR over the quad of (8-row byte << 8*rg); lane rg then
+    // stores the words of its columns 2rg and 2rg+1
+    uint32_t mw[8];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      if (DT == kBF16) {
+        mw[2 * k] = or_quad((acc[k] & 0xFFu) << (8 * rg));
+        mw[2 * k + 1] = or_quad(((acc[k] >> 16) & 0xFFu) << (8 * rg));
+      } else {
+        mw[k] = or_quad(acc[k] << (8 * rg));
+      }
+    }
+    const uint32_t ev[4] = {mw[0], mw[2], mw[4], mw[6]};
+    const uint32_t od[4] = {mw[1], mw[3], mw[5], mw[7]};
+    const uint32_t a0 = pick4(ev, rg), a1 = pick4(od, rg);
+    const int64_t cw = c0 + 2 * rg;
+    if (slab_live) {
+      uint32_t *dst = A.mask_col + wrow * A.cols + cw;
+      if (VEC) {
+        if (cw + 1 < A.cols) *reinterpret_cast<uint2 *>(dst) = make_uint2(a0, a1);
+      } else {
+        if (cw < A.cols) dst[0] = a0;
+        if (cw + 1 < A.cols) dst[1] = a1;
+      }
+    }
+  }
+}
+
 template <int DT, int B, int RULE, int KIND, bool VEC>
-__global__ __launch_bounds__(kThreads) void col_fwd_kernel(ColArgs A) {
+__global__ __launch_bounds__(kThreads, 4) void col_fwd_kernel(ColArgs A) {
   constexpr int NW = ColT<DT>::NW;
   constexpr int ES = ColT<DT>::ES;
   constexpr int WX = B == 32 ? 4 : 1;  // waves side by side
@@ -140,14 +217,25 @@ __global__ __launch_bounds__(kThreads) void col_fwd_kernel(ColArgs A) {
   const int64_t crem = A.cols - c0;
   const int ncol = crem >= 8 ? 8 : (crem > 0 ? (int)crem : 0);
   const int slab = 32 * wy;
+  const int rbase = slab + 8 * rg;            // first row of this lane in the block-row
+  const int64_t rstride = A.cols * ES;        // bytes per row
+  const int64_t off0 = ((start + rbase) * A.cols + c0) * ES;
 
   // ---- load 8 rows x 8 columns per lane ---------------------------------
+  // A wave whose 32 rows and 128 columns are all inside the tensor issues its
+  // eight loads unconditionally, so all of them are in flight together (a
+  // load under a per-lane branch is waited for before the branch closes).
   uint32_t w[8][NW];
+  const bool full = VEC && slab + 32 <= len && col0 + kWaveCols <= A.cols;  // wave-uniform
+  if (full) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int rr = slab + 8 * rg + i;
-    const int n = rr < len ? ncol : 0;
-    load_piece<DT, VEC>(w[i], A.x + ((start + rr) * A.cols + c0) * ES, n);
+    for (int i = 0; i < 8; ++i) load_piece<DT, true>(w[i], A.x + off0 + i * rstride, 8);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = rbase + i < len ? ncol : 0;
+      load_piece<DT, VEC>(w[i], A.x + off0 + i * rstride, n);
+    }
   }
 
   // ---- column direction ---------------------------------------------------
@@ -179,20 +267,24 @@ __global__ __launch_bounds__(kThreads) void col_fwd_kernel(ColArgs A) {
     }
   }
 
-  // per-column parameters
-  uint32_t pt[NW], ph[NW], ps[NW], pe[NW];  // bf16: packed halves; fp32: per column
-  uint32_t slow_any = 0;
+  // per-column parameters: bf16 packed per word (E8M0 bytes in bits 0-7 and
+  // 16-23), fp32 one block per column
+  uint32_t pt[NW], ph[NW], ps[NW], pe[NW];
+  bool slow_any = false;
   BlockParams cbp[DT == kF32 ? 8 : 1];
 #pragma unroll
   for (int k = 0; k < NW; ++k) {
-    if (DT == kBF16) {
+    if (DT == kBF16 && RULE == kFloor) {
+      const PackedParams q = floor_params_pk(cm[k]);
+      pt[k] = q.t2; ph[k] = q.h2; ps[k] = q.s2; pe[k] = q.e8;
+      slow_any = slow_any || q.slow;
+    } else if (DT == kBF16) {
       const BlockParams lo = block_params<DT, RULE>(cm[k] & 0xFFFFu, A.sf);
       const BlockParams hi = block_params<DT, RULE>(cm[k] >> 16, A.sf);
       pt[k] = lo.t025 | (hi.t025 << 16);
       ph[k] = lo.half | (hi.half << 16);
       ps[k] = lo.six | (hi.six << 16);
-      pe[k] = lo.e8 | (hi.e8 << 16) | (lo.slow ? 0x100u : 0u) | (hi.slow ? 0x1000000u : 0u);
-      slow_any |= (lo.slow || hi.slow) ? 1u : 0u;
+      pe[k] = lo.e8 | (hi.e8 << 16);
     } else {
       cbp[DT == kF32 ? k : 0] = block_params<DT, RULE>(cm[k], A.sf);
       pe[k] = cbp[DT == kF32 ? k : 0].e8;
@@ -203,58 +295,12 @@ __global__ __launch_bounds__(kThreads) void col_fwd_kernel(ColArgs A) {
   const int64_t wrow = bt * (B / 32) + wy;  // bitmap word-row of this slab
 
   if (A.y_col || A.mask_col) {
-    uint32_t macc[8];  // per column: bits of this lane's 8 rows
-#pragma unroll
-    for (int k = 0; k < 8; ++k) macc[k] = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t yv[NW];
-      const int rr = slab + 8 * rg + i;
-#pragma unroll
-      for (int k = 0; k < NW; ++k) {
-        if (DT == kBF16) {
-          yv[k] = y_bf16(w[i][k], pt[k], ph[k]);
-          uint32_t mb = m_bf16(w[i][k], ps[k]);
-          if (slow_any && (pe[k] & 0x1000100u)) {
-            if (pe[k] & 0x100u) {
-              HalfOut o = half_bf16_slow(w[i][k] & 0xFFFFu, pe[k] & 0xFFu);
-              yv[k] = (yv[k] & 0xFFFF0000u) | o.y;
-              mb = (mb & 0xFFFF0000u) | o.m;
-            }
-            if (pe[k] & 0x1000000u) {
-              HalfOut o = half_bf16_slow(w[i][k] >> 16, (pe[k] >> 16) & 0xFFu);
-              yv[k] = (yv[k] & 0xFFFFu) | (o.y << 16);
-              mb = (mb & 0xFFFFu) | (o.m << 16);
-            }
-          }
-          macc[2 * k] |= (mb & 1u) << i;
-          macc[2 * k + 1] |= (mb >> 16) << i;
-        } else {
-          yv[k] = y_f32(w[i][k], cbp[DT == kF32 ? k : 0]);
-          macc[k] |= m_f32(w[i][k], cbp[DT == kF32 ? k : 0]) << i;
-        }
-      }
-      if (A.y_col && rr < len) store_piece<DT, VEC>(A.y_col + ((start + rr) * A.cols + c0) * ES, yv, ncol);
-    }
-    if (A.mask_col) {
-      uint32_t mw[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) mw[k] = or_quad(macc[k] << (8 * rg));
-      // lane rg stores the words of columns 2rg and 2rg+1
-      const uint32_t ev[4] = {mw[0], mw[2], mw[4], mw[6]};
-      const uint32_t od[4] = {mw[1], mw[3], mw[5], mw[7]};
-      const uint32_t a0 = pick4(ev, rg), a1 = pick4(od, rg);
-      const int64_t cw = c0 + 2 * rg;
-      if (slab_live) {
-        uint32_t *dst = A.mask_col + wrow * A.cols + cw;
-        if (VEC) {
-          if (cw + 1 < A.cols) *reinterpret_cast<uint2 *>(dst) = make_uint2(a0, a1);
-        } else {
-          if (cw < A.cols) dst[0] = a0;
-          if (cw + 1 < A.cols) dst[1] = a1;
-        }
-      }
-    }
+    if (__builtin_expect(__any(slow_any), 0))
+      col_outputs<DT, RULE, VEC, true>(A, w, pt, ph, ps, pe, cm, cbp, off0, rstride, rbase, len, ncol,
+                                       rg, c0, wrow, slab_live);
+    else
+      col_outputs<DT, RULE, VEC, false>(A, w, pt, ph, ps, pe, cm, cbp, off0, rstride, rbase, len, ncol,
+                                        rg, c0, wrow, slab_live);
   }
   if (A.scales_col && rg == 0 && wy == 0) {
     uint8_t *dst = A.scales_col + bt * A.cols + c0;
@@ -274,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void col_fwd_kernel(ColArgs A) {
     uint32_t rw[8];  // row-bitmap partial words
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int rr = slab + 8 * rg + i;
+      const int rr = rbase + i;
       uint32_t am;
       if (DT == kBF16) {
         uint32_t m = pk_max(pk_max(w[i][0] & 0x7FFF7FFFu, w[i][1] & 0x7FFF7FFFu),
@@ -287,12 +333,16 @@ __global__ __launch_bounds__(kThreads) void col_fwd_kernel(ColArgs A) {
       }
       am = B == 32 ? max_stride4_row(am) : max_stride4_wave(am);
       const BlockParams bp = block_params<DT, RULE>(am, A.sf);
+      const bool rslow = __builtin_expect(__any(bp.slow), 0);
       if (A.y_row) {
         uint32_t yv[NW];
-        chunk_y<DT>(w[i], bp, yv);
-        if (rr < len) store_piece<DT, VEC>(A.y_row + ((start + rr) * A.cols + c0) * ES, yv, ncol);
+        if (rslow) chunk_y<DT, true>(w[i], bp, yv);
+        else chunk_y<DT, false>(w[i], bp, yv);
+        if (rr < len) store_piece<DT, VEC>(A.y_row + off0 + i * rstride, yv, ncol);
       }
-      rw[i] = A.mask_row ? or_stride4_row(chunk_mask<DT>(w[i], bp) << (8 * (cc & 3))) : 0;
+      uint32_t mbyte = 0;
+      if (A.mask_row) mbyte = rslow ? chunk_mask<DT, true>(w[i], bp) : chunk_mask<DT, false>(w[i], bp);
+      rw[i] = A.mask_row ? or_stride4_row(mbyte << (8 * (cc & 3))) : 0;
       if (A.scales_row && (cc % G_ROW) == 0 && rr < len && ncol > 0)
         A.scales_row[(start + rr) * A.nb_row + c0 / B] = (uint8_t)bp.e8;
     }
@@ -303,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void col_fwd_kernel(ColArgs A) {
       const int64_t wi = c0 >> 5;
       const uint32_t lo = pick4(rw, j);
       const uint32_t hi = pick4(rw + 4, j);
-      const int r_lo = slab + 8 * rg + j, r_hi = r_lo + 4;
+      const int r_lo = rbase + j, r_hi = r_lo + 4;
       if (wi < A.nw_row) {
         if (r_lo < len) A.mask_row[(start + r_lo) * A.nw_row + wi] = lo;
         if (r_hi < len) A.mask_row[(start + r_hi) * A.nw_row + wi] = hi;

@@ -108,42 +108,49 @@ __device__ __forceinline__ uint32_t pk_min_v(uint32_t a, uint32_t b) {
   asm("v_pk_min_u16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
+// min(x, 1) on both halves with the inline constant 1 (op_sel_hi:[1,0] makes
+// the high half read the constant too), so no register holds 0x00010001.
+__device__ __forceinline__ uint32_t pk_min1(uint32_t a) {
+  uint32_t r;
+  asm("v_pk_min_u16 %0, %1, 1 op_sel_hi:[1,0]" : "=v"(r) : "v"(a));
+  return r;
+}
 
 // ---- per-word outputs, bf16 (two elements per register) -------------------
 // Parameters are packed per half (t2 = T025 - tau, h2 = HALF, s2 = SIX), so a
 // register may hold two elements of one block or of two different blocks.
 // y bits with the input's sign (-0.0 -> +0.0)
 __device__ __forceinline__ uint32_t y_bf16(uint32_t w, uint32_t t2, uint32_t h2) {
-  const uint32_t one2 = 0x00010001u;
   uint32_t a = w & 0x7FFF7FFFu;
   uint32_t u = pk_subsat(a, t2);
   uint32_t r = pk_add(u, 0x001F001Fu) & 0xFFC0FFC0u;
   uint32_t h = pk_min(pk_subsat(r, 0x01000100u), 0x01400140u);
-  uint32_t z = pk_min_v(u, one2);
-  uint32_t c = pk_min_v(pk_subsat(u, 0x00C000C0u), one2);
+  uint32_t z = pk_min1(u);
+  uint32_t c = pk_min1(pk_subsat(u, 0x00C000C0u));
   return pk_mad(c, 0x00800080u, pk_mad(z, h2, h)) | sign_bf16(w);
 }
 // clip bits: bit 0 (low element) and bit 16 (high element)
 __device__ __forceinline__ uint32_t m_bf16(uint32_t w, uint32_t s2) {
-  return pk_min_v(pk_subsat(w & 0x7FFF7FFFu, s2), 0x00010001u);
+  return pk_min1(pk_subsat(w & 0x7FFF7FFFu, s2));
 }
 // nibbles sign<<3 | code in bits 0-3 and 16-19
 __device__ __forceinline__ uint32_t n_bf16(uint32_t w, uint32_t t2) {
-  const uint32_t one2 = 0x00010001u;
   uint32_t a = w & 0x7FFF7FFFu;
   uint32_t u = pk_subsat(a, t2);
   uint32_t r = pk_add(u, 0x001F001Fu) & 0xFFC0FFC0u;
   uint32_t h = pk_min(pk_subsat(r, 0x01000100u), 0x01400140u);
-  uint32_t z = pk_min_v(u, one2);
-  uint32_t c = pk_min_v(pk_subsat(u, 0x00C000C0u), one2);
+  uint32_t z = pk_min1(u);
+  uint32_t c = pk_min1(pk_subsat(u, 0x00C000C0u));
   return pk_add(pk_add(z, c), pk_shr(h, 6)) | (sign_bf16(w) >> 12);
 }
+
+
 
 // Generic snap of one half (FLOOR blocks with E8M0 byte 0..2).
 struct HalfOut {
   uint32_t y, m, n;
 };
-__device__ __noinline__ HalfOut half_bf16_slow(uint32_t bits16, uint32_t e8) {
+__device__ __forceinline__ HalfOut half_bf16_slow(uint32_t bits16, uint32_t e8) {
   uint32_t a = bits16 & 0x7FFFu;
   uint32_t sg = (bits16 & 0x8000u) && a ? 0x8000u : 0u;
   uint32_t idx;
@@ -189,13 +196,17 @@ __device__ __forceinline__ uint32_t pack_mask_bf16(const uint32_t m[4]) {
 }
 
 // ---- whole 8-element chunk with one block's parameters (row direction) ----
-template <int DT>
+// SLOW = false: closed form only (the caller has checked that no lane of the
+// wave holds a block that needs the generic snap); SLOW = true: lanes whose
+// block needs it take the generic threshold count.  Keeping the two apart
+// leaves the common path free of calls and of the generic code.
+template <int DT, bool SLOW>
 __device__ __forceinline__ void chunk_y(const uint32_t *w, const BlockParams &bp, uint32_t *y) {
   if (DT == kBF16) {
     const uint32_t t2 = splat16(bp.t025), h2 = splat16(bp.half);
 #pragma unroll
     for (int k = 0; k < 4; ++k) y[k] = y_bf16(w[k], t2, h2);
-    if (bp.slow) {
+    if (SLOW && bp.slow) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         HalfOut lo = half_bf16_slow(w[k] & 0xFFFFu, bp.e8), hi = half_bf16_slow(w[k] >> 16, bp.e8);
@@ -203,18 +214,20 @@ __device__ __forceinline__ void chunk_y(const uint32_t *w, const BlockParams &bp
       }
     }
   } else {
+    BlockParams q = bp;
+    if (!SLOW) q.slow = false;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) y[k] = y_f32(w[k], bp);
+    for (int k = 0; k < 8; ++k) y[k] = y_f32(w[k], q);
   }
 }
-template <int DT>
+template <int DT, bool SLOW>
 __device__ __forceinline__ uint32_t chunk_mask(const uint32_t *w, const BlockParams &bp) {
   if (DT == kBF16) {
     uint32_t m[4];
     const uint32_t s2 = splat16(bp.six);
 #pragma unroll
     for (int k = 0; k < 4; ++k) m[k] = m_bf16(w[k], s2);
-    if (bp.slow) {
+    if (SLOW && bp.slow) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         HalfOut lo = half_bf16_slow(w[k] & 0xFFFFu, bp.e8), hi = half_bf16_slow(w[k] >> 16, bp.e8);
@@ -223,19 +236,21 @@ __device__ __forceinline__ uint32_t chunk_mask(const uint32_t *w, const BlockPar
     }
     return pack_mask_bf16(m);
   }
+  BlockParams q = bp;
+  if (!SLOW) q.slow = false;
   uint32_t byte = 0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) byte |= m_f32(w[k], bp) << k;
+  for (int k = 0; k < 8; ++k) byte |= m_f32(w[k], q) << k;
   return byte;
 }
-template <int DT>
+template <int DT, bool SLOW>
 __device__ __forceinline__ uint32_t chunk_codes(const uint32_t *w, const BlockParams &bp) {
   if (DT == kBF16) {
     uint32_t n[4];
     const uint32_t t2 = splat16(bp.t025);
 #pragma unroll
     for (int k = 0; k < 4; ++k) n[k] = n_bf16(w[k], t2);
-    if (bp.slow) {
+    if (SLOW && bp.slow) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         HalfOut lo = half_bf16_slow(w[k] & 0xFFFFu, bp.e8), hi = half_bf16_slow(w[k] >> 16, bp.e8);
@@ -244,9 +259,11 @@ __device__ __forceinline__ uint32_t chunk_codes(const uint32_t *w, const BlockPa
     }
     return pack_nibbles_bf16(n);
   }
+  BlockParams q = bp;
+  if (!SLOW) q.slow = false;
   uint32_t nib = 0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) nib |= n_f32(w[k], bp) << (4 * k);
+  for (int k = 0; k < 8; ++k) nib |= n_f32(w[k], q) << (4 * k);
   return nib;
 }
 

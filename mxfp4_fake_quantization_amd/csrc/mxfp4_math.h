@@ -69,6 +69,10 @@ MXFP4_HD uint32_t pk_shr(uint32_t a, unsigned s) {
   u16x2 sh = {(unsigned short)s, (unsigned short)s};
   return as_u32(as_u16x2(a) >> sh);
 }
+MXFP4_HD uint32_t pk_shl7(uint32_t a) {
+  u16x2 sh = {7, 7};
+  return as_u32(as_u16x2(a) << sh);
+}
 MXFP4_HD uint32_t splat16(uint32_t v) { return (v & 0xFFFFu) | (v << 16); }
 
 MXFP4_HD uint32_t subsat32(uint32_t a, uint32_t b) { return a > b ? a - b : 0u; }
@@ -115,6 +119,26 @@ MXFP4_HD BlockParams floor_params(uint32_t amax) {
   p.half = p.t025 + 2 * Q;
   p.six = p.t025 + 9 * Q;
   p.slow = (amax != 0) && (eb < 5);
+  return p;
+}
+
+// FLOOR parameters of two bf16 columns at once (one per half of cm, the
+// packed column maxima): E8M0 bytes, T025, HALF, SIX, and the halves that
+// need the generic snap (nonzero max with an exponent field below 5).
+struct PackedParams {
+  uint32_t e8, t2, h2, s2;
+  bool slow;
+};
+MXFP4_HD PackedParams floor_params_pk(uint32_t cm) {
+  PackedParams p;
+  const uint32_t eb = pk_shr(cm, 7);
+  p.e8 = pk_subsat(eb, 0x00020002u);
+  p.t2 = pk_shl7(pk_subsat(pk_max(eb, 0x00050005u), 0x00040004u));
+  p.h2 = pk_add(p.t2, 0x00800080u);
+  p.s2 = pk_add(p.t2, 0x02400240u);
+  // slow <=> 0 < cm_half < 5 << 7, i.e. (cm_half - 1) mod 2^16 < 639
+  const uint32_t m1 = pk_sub(cm, 0x00010001u);
+  p.slow = (m1 & 0xFFFFu) < 639u || (m1 >> 16) < 639u;
   return p;
 }
 
@@ -211,17 +235,23 @@ MXFP4_HD uint32_t lin_to_bits(uint32_t L) {
 
 // Snap one magnitude (32-bit, low bits) for E8M0 byte e8 in {0,1,2}: count the
 // midpoints m*2^k (m = n/4, n = 1 3 5 7 10 14 20) that |x| exceeds, then
-// return the bits of code*2^k (code*4 = 0 2 4 6 8 12 16 24).
+// return the bits of code*2^k (code*4 = 0 2 4 6 8 12 16 24, i.e. 2*idx for
+// idx < 2 and (2 + idx%2) << idx/2 above).
 template <int DT>
 MXFP4_HD uint32_t slow_snap(uint32_t a, uint32_t e8, uint32_t *idx_out) {
   constexpr int MB = Fmt<DT>::MB;
   const unsigned sh = e8 + MB - 3;  // 2^(k-2) in subnormal units
-  const uint32_t n[7] = {1, 3, 5, 7, 10, 14, 20};
-  const uint32_t c4[8] = {0, 2, 4, 6, 8, 12, 16, 24};
   uint32_t idx = 0;
-  for (int i = 0; i < 7; ++i) idx += (a > lin_to_bits<DT>(n[i] << sh)) ? 1u : 0u;
+  idx += (a > lin_to_bits<DT>(1u << sh)) ? 1u : 0u;
+  idx += (a > lin_to_bits<DT>(3u << sh)) ? 1u : 0u;
+  idx += (a > lin_to_bits<DT>(5u << sh)) ? 1u : 0u;
+  idx += (a > lin_to_bits<DT>(7u << sh)) ? 1u : 0u;
+  idx += (a > lin_to_bits<DT>(10u << sh)) ? 1u : 0u;
+  idx += (a > lin_to_bits<DT>(14u << sh)) ? 1u : 0u;
+  idx += (a > lin_to_bits<DT>(20u << sh)) ? 1u : 0u;
   if (idx_out) *idx_out = idx;
-  return lin_to_bits<DT>(c4[idx] << sh);
+  const uint32_t c4 = idx < 2 ? 2 * idx : (2 + (idx & 1)) << (idx >> 1);
+  return lin_to_bits<DT>(c4 << sh);
 }
 template <int DT>
 MXFP4_HD uint32_t slow_six(uint32_t e8) {

@@ -81,6 +81,47 @@ __device__ __forceinline__ void store_scalar(uint8_t *p, const uint32_t *w, int 
   }
 }
 
+// Outputs of one chunk: y, bitmap byte, packed nibbles (scales are written by
+// the caller).  SLOW selects the variant that can handle generic-snap blocks.
+template <int DT, int G, int MODE, int U, bool FULL, bool SLOW>
+__device__ __forceinline__ void row_emit(const RowArgs &A, const uint32_t *wv, const BlockParams &bp,
+                                         int64_t off, int64_t row, int64_t cr, int nval, int64_t idx) {
+  constexpr int NW = ChunkT<DT>::NW;
+  constexpr int ES = ChunkT<DT>::ES;
+  const uint32_t emit = A.emit;
+    const bool live = nval > 0;
+    if (emit & kEmitY) {
+      uint32_t yv[NW];
+      chunk_y<DT, SLOW>(wv, bp, yv);
+      uint8_t *dst = A.y + off * ES;
+      if (MODE == kModeRowsScalar) {
+        if (live) store_scalar<DT>(dst, yv, nval);
+      } else if (nval == 8) {
+        store_vec<DT>(dst, yv);
+      }
+    }
+    if (emit & kEmitMask) {
+      const uint32_t byte = chunk_mask<DT, SLOW>(wv, bp);
+      if (MODE == kModeFlat) {
+        if (live) A.mask[cr] = (uint8_t)byte;
+      } else if (idx < A.nchunks && cr < A.mask_row_bytes) {
+        A.mask[row * A.mask_row_bytes + cr] = (uint8_t)byte;
+      }
+    }
+    if (emit & kEmitCodes) {
+      const uint32_t nib = chunk_codes<DT, SLOW>(wv, bp);
+      if (MODE == kModeFlat) {
+        if (live) reinterpret_cast<uint32_t *>(A.codes)[cr] = nib;
+      } else if (MODE == kModeRowsVec) {
+        if (nval == 8)
+          *reinterpret_cast<uint32_t *>(A.codes + row * A.code_row_bytes + 4 * cr) = nib;
+      } else if (live) {
+        uint8_t *dst = A.codes + row * A.code_row_bytes + 4 * cr;
+        for (int j = 0; j < (nval + 1) / 2; ++j) dst[j] = (uint8_t)(nib >> (8 * j));
+      }
+    }
+}
+
 template <int DT, int B, int RULE, int MODE, int U, bool FULL>
 __device__ __forceinline__ void row_fwd_body(const RowArgs &A) {
   constexpr int G = B / 8;
@@ -119,7 +160,6 @@ __device__ __forceinline__ void row_fwd_body(const RowArgs &A) {
     }
   }
 
-  const uint32_t emit = A.emit;
 #pragma unroll
   for (int s = 0; s < U; ++s) {
     // block max of the magnitude bits (integer max == float max for finite x)
@@ -136,38 +176,13 @@ __device__ __forceinline__ void row_fwd_body(const RowArgs &A) {
     am = group_max<G>(am);
     const BlockParams bp = block_params<DT, RULE>(am, A.sf);
 
-    const bool live = nval[s] > 0;
-    if (emit & kEmitY) {
-      uint32_t yv[NW];
-      chunk_y<DT>(w[s], bp, yv);
-      uint8_t *dst = A.y + off[s] * ES;
-      if (MODE == kModeRowsScalar) {
-        if (live) store_scalar<DT>(dst, yv, nval[s]);
-      } else if (nval[s] == 8) {
-        store_vec<DT>(dst, yv);
-      }
-    }
-    if (emit & kEmitMask) {
-      const uint32_t byte = chunk_mask<DT>(w[s], bp);
-      if (MODE == kModeFlat) {
-        if (live) A.mask[cr[s]] = (uint8_t)byte;
-      } else if (base + s * kThreads + tid < A.nchunks && cr[s] < A.mask_row_bytes) {
-        A.mask[row[s] * A.mask_row_bytes + cr[s]] = (uint8_t)byte;
-      }
-    }
-    if (emit & kEmitCodes) {
-      const uint32_t nib = chunk_codes<DT>(w[s], bp);
-      if (MODE == kModeFlat) {
-        if (live) reinterpret_cast<uint32_t *>(A.codes)[cr[s]] = nib;
-      } else if (MODE == kModeRowsVec) {
-        if (nval[s] == 8)
-          *reinterpret_cast<uint32_t *>(A.codes + row[s] * A.code_row_bytes + 4 * cr[s]) = nib;
-      } else if (live) {
-        uint8_t *dst = A.codes + row[s] * A.code_row_bytes + 4 * cr[s];
-        for (int j = 0; j < (nval[s] + 1) / 2; ++j) dst[j] = (uint8_t)(nib >> (8 * j));
-      }
-    }
-    if ((emit & kEmitScales) && (tid % G) == 0 && base + s * kThreads + tid < A.nchunks) {
+    if (__builtin_expect(__any(bp.slow), 0))
+      row_emit<DT, G, MODE, U, FULL, true>(A, w[s], bp, off[s], row[s], cr[s], nval[s],
+                                          base + s * kThreads + tid);
+    else
+      row_emit<DT, G, MODE, U, FULL, false>(A, w[s], bp, off[s], row[s], cr[s], nval[s],
+                                           base + s * kThreads + tid);
+    if ((A.emit & kEmitScales) && (tid % G) == 0 && base + s * kThreads + tid < A.nchunks) {
       const int64_t bi = MODE == kModeFlat ? cr[s] / G : row[s] * A.nb + cr[s] / G;
       A.scales[bi] = (uint8_t)bp.e8;
     }

@@ -48,8 +48,8 @@ struct SteRowArgs {
   int64_t cols, nchunks, cpr, mask_row_bytes;
 };
 
-template <int DT, int MODE, int U>
-__global__ __launch_bounds__(kThreads) void ste_row_kernel(SteRowArgs A) {
+template <int DT, int MODE, int U, bool FULL>
+__device__ __forceinline__ void ste_row_body(const SteRowArgs &A) {
   constexpr int NW = DT == kBF16 ? 4 : 8;
   constexpr int ES = DT == kBF16 ? 2 : 4;
   const int tid = threadIdx.x;
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void ste_row_kernel(SteRowArgs A) {
     int64_t mb;
     if (MODE == kModeFlat) {
       off[s] = i * 8;
-      nval[s] = i < A.nchunks ? 8 : 0;
+      nval[s] = (FULL || i < A.nchunks) ? 8 : 0;
       mb = i;
     } else {
       const int64_t r = i / A.cpr, c = i - r * A.cpr;
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void ste_row_kernel(SteRowArgs A) {
 #pragma unroll
     for (int k = 0; k < NW; ++k) w[s][k] = 0;
     bits[s] = 0;
-    if (nval[s] > 0) {
+    if (FULL || nval[s] > 0) {
       const uint8_t *p = A.g + off[s] * ES;
       if (MODE != kModeRowsScalar) {
         uint4 v = ld16(p);
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void ste_row_kernel(SteRowArgs A) {
   }
 #pragma unroll
   for (int s = 0; s < U; ++s) {
-    if (nval[s] == 0) continue;
+    if (!FULL && nval[s] == 0) continue;
     apply_bits<DT>(w[s], bits[s]);
     uint8_t *p = A.gi + off[s] * ES;
     if (MODE != kModeRowsScalar) {
@@ -109,6 +109,15 @@ __global__ __launch_bounds__(kThreads) void ste_row_kernel(SteRowArgs A) {
       }
     }
   }
+}
+
+// Workgroups whose pieces are all in range (flat layout) load unconditionally.
+template <int DT, int MODE, int U>
+__global__ __launch_bounds__(kThreads) void ste_row_kernel(SteRowArgs A) {
+  if (MODE == kModeFlat && (int64_t)(blockIdx.x + 1) * (kThreads * U) <= A.nchunks)
+    ste_row_body<DT, MODE, U, true>(A);
+  else
+    ste_row_body<DT, MODE, U, false>(A);
 }
 
 struct SteColArgs {
@@ -161,6 +170,33 @@ __global__ __launch_bounds__(kThreads) void ste_col_kernel(SteColArgs A) {
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) mw[k] = k < ncol ? mp[k] : 0;
+  }
+  if (VEC && len == 32 && ncol == 8 && c0 - 8 * cc + 128 <= A.cols) {
+    // full slab for this wave: all loads first, no per-lane branches
+    const int64_t rstride = A.cols * ES;
+    const uint8_t *p0 = A.g + ((start + 8 * rg) * A.cols + c0) * ES;
+    uint8_t *q0 = A.gi + ((start + 8 * rg) * A.cols + c0) * ES;
+    uint32_t w[8][NW];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint4 v = ld16(p0 + i * rstride);
+      w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
+      if (DT == kF32) {
+        uint4 v2 = ld16(p0 + i * rstride + 16);
+        w[i][4] = v2.x; w[i][5] = v2.y; w[i][6] = v2.z; w[i][7] = v2.w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = 8 * rg + i;
+      uint32_t bits = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) bits |= ((mw[k] >> rr) & 1u) << k;
+      apply_bits<DT>(w[i], bits);
+      st16(q0 + i * rstride, make_uint4(w[i][0], w[i][1], w[i][2], w[i][3]));
+      if (DT == kF32) st16(q0 + i * rstride + 16, make_uint4(w[i][4], w[i][5], w[i][6], w[i][7]));
+    }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {

@@ -81,3 +81,22 @@ extern "C" int host_qdq_rows(int dtype, int64_t rows, int64_t cols, int block, i
     }
   return 0;
 }
+
+// Packed FLOOR parameters of two bf16 columns vs the scalar rule, for every
+// 16-bit max in the low half against a sweep of high halves.  Returns the
+// number of mismatches.
+extern "C" int host_check_packed_params(void) {
+  int bad = 0;
+  const uint32_t his[] = {0, 1, 0x7F, 0x80, 0x27F, 0x280, 0x3F80, 0x7F7F};
+  for (uint32_t lo = 0; lo < 0x8000; ++lo)
+    for (uint32_t hi : his) {
+      const PackedParams p = floor_params_pk(lo | (hi << 16));
+      const BlockParams a = floor_params<kBF16>(lo), b = floor_params<kBF16>(hi);
+      bad += (p.e8 != (a.e8 | (b.e8 << 16)));
+      bad += (p.t2 != (a.t025 | (b.t025 << 16)));
+      bad += (p.h2 != (a.half | (b.half << 16)));
+      bad += (p.s2 != (a.six | (b.six << 16)));
+      bad += (p.slow != (a.slow || b.slow));
+    }
+  return bad;
+}

@@ -136,3 +136,8 @@ def test_fp32_exhaustive_mantissa_sweep(host, oracle):
             compare(host, oracle, blocks, 32, "floor")
             if k >= -30:
                 compare(host, oracle, blocks, 32, "amct")
+
+
+def test_packed_column_params_match_scalar_rule(host):
+    host.host_check_packed_params.restype = ctypes.c_int
+    assert host.host_check_packed_params() == 0
