@@ -111,13 +111,13 @@ __device__ __forceinline__ void fix_slow_word(uint32_t w, uint32_t cm, uint32_t 
   }
 }
 
-// Pick word k = 2*rg (+1) of 8 per-lane words without dynamic indexing.
-__device__ __forceinline__ uint32_t pick4(const uint32_t *v, int sel) {
-  uint32_t r = v[0];
-  r = sel == 1 ? v[1] : r;
-  r = sel == 2 ? v[2] : r;
-  r = sel == 3 ? v[3] : r;
-  return r;
+// One of four values by a lane-varying index, as register selects (an array
+// indexed by a lane value would be placed in LDS by the compiler).
+__device__ __forceinline__ uint32_t pick4(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3,
+                                          int sel) {
+  const uint32_t lo = (sel & 1) ? v1 : v0;
+  const uint32_t hi = (sel & 1) ? v3 : v2;
+  return (sel & 2) ? hi : lo;
 }
 
 // Column-direction outputs of one lane: y_col rows and the bitmap words of
@@ -164,17 +164,18 @@ __device__ __forceinline__ void col_outputs(const ColArgs &A, const uint32_t (&w
         mw[k] = or_quad(acc[k] << (8 * rg));
       }
     }
-    const uint32_t ev[4] = {mw[0], mw[2], mw[4], mw[6]};
-    const uint32_t od[4] = {mw[1], mw[3], mw[5], mw[7]};
-    const uint32_t a0 = pick4(ev, rg), a1 = pick4(od, rg);
-    const int64_t cw = c0 + 2 * rg;
-    if (slab_live) {
-      uint32_t *dst = A.mask_col + wrow * A.cols + cw;
+    // every lane of the quad now holds the 8 words; lane rg == 0 writes them
+    if (slab_live && rg == 0) {
+      uint32_t *dst = A.mask_col + wrow * A.cols + c0;
       if (VEC) {
-        if (cw + 1 < A.cols) *reinterpret_cast<uint2 *>(dst) = make_uint2(a0, a1);
+        if (ncol == 8) {
+          *reinterpret_cast<uint4 *>(dst) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+          *reinterpret_cast<uint4 *>(dst + 4) = make_uint4(mw[4], mw[5], mw[6], mw[7]);
+        }
       } else {
-        if (cw < A.cols) dst[0] = a0;
-        if (cw + 1 < A.cols) dst[1] = a1;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k < ncol) dst[k] = mw[k];
       }
     }
   }
@@ -200,13 +201,9 @@ __global__ __launch_bounds__(kThreads, 4) void col_fwd_kernel(ColArgs A) {
 
   int64_t start, len;
   if (KIND == kKindGrouped) {
-    __shared__ int64_t s_blk[2];
-    if (wave == 0)
-      find_block_row(A.group_list, A.num_groups, A.list_type, A.rows, B == 32 ? 5 : 7, bt, s_blk);
-    __syncthreads();
-    start = s_blk[0];
-    len = s_blk[1];
-    if (len <= 0) return;  // whole workgroup: past the last block-row
+    block_row_uniform(A.group_list, A.num_groups, A.list_type, A.rows, B == 32 ? 5 : 7, bt, &start,
+                      &len);
+    if (len <= 0) return;  // every wave of the workgroup decodes the same block-row
   } else {
     start = bt * B;
     len = A.rows - start < B ? A.rows - start : B;
@@ -351,8 +348,8 @@ __global__ __launch_bounds__(kThreads, 4) void col_fwd_kernel(ColArgs A) {
       // rows j and j + 4
       const int j = cc & 3;
       const int64_t wi = c0 >> 5;
-      const uint32_t lo = pick4(rw, j);
-      const uint32_t hi = pick4(rw + 4, j);
+      const uint32_t lo = pick4(rw[0], rw[1], rw[2], rw[3], j);
+      const uint32_t hi = pick4(rw[4], rw[5], rw[6], rw[7], j);
       const int r_lo = rbase + j, r_hi = r_lo + 4;
       if (wi < A.nw_row) {
         if (r_lo < len) A.mask_row[(start + r_lo) * A.nw_row + wi] = lo;

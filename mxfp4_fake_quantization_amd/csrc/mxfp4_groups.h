@@ -5,8 +5,10 @@
 // normalize_group_list turns counts into cumulative sums).  Column blocks
 // restart at every group start, so block-row t (numbered group by group,
 // ceil(c_g / block) per group) covers rows [start, start + len) with
-// len <= block.  One wave scans the list (64 groups per step) and the result
-// is shared through LDS; no host synchronisation is needed.
+// len <= block.  Every wave decodes the list itself: one vector load brings
+// 64 entries into the lanes, then a wave-uniform loop walks them in scalar
+// registers (v_readlane), so no LDS, no barrier and no host synchronisation
+// are involved.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,73 +16,46 @@
 
 namespace mxfp4 {
 
-template <typename T>
-__device__ __forceinline__ T wave_incl_scan_add(T v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    T u = __shfl_up(v, off, 64);
-    if (lane >= off) v += u;
-  }
-  return v;
-}
-__device__ __forceinline__ int64_t wave_incl_scan_max(int64_t v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int64_t u = __shfl_up(v, off, 64);
-    if (lane >= off) v = v > u ? v : u;
-  }
-  return v;
+__device__ __forceinline__ int64_t lane_i64(int64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), lane);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Group ends are clamped into [previous end, rows]: an inconsistent list
-// (negative counts, decreasing ends, a total above rows) never leads to an
-// out-of-range row.  Called by all 64 lanes of one wave; lane 0 writes
-// out[0] = start, out[1] = len (len 0: t is past the last block-row).
-__device__ __forceinline__ void find_block_row(const int64_t *gl, int num_groups, int list_type,
-                                               int64_t rows, int block_log2, int64_t t,
-                                               int64_t *out) {
+// Wave-uniform result: *start and *len of block-row t (len 0 past the end).
+// Group ends are clamped into [previous end, rows].
+__device__ __forceinline__ void block_row_uniform(const int64_t *gl, int num_groups, int list_type,
+                                                  int64_t rows, int block_log2, int64_t t,
+                                                  int64_t *start, int64_t *len) {
   const int lane = (int)__lane_id();
-  const int64_t block = (int64_t)1 << block_log2;
-  int64_t carry_cum = 0, carry_end = 0, carry_b = 0;
-  int64_t start = 0, len = 0;
-  bool found = false;
-  for (int base = 0; base < num_groups && !found; base += 64) {
+  int64_t prev_end = 0, cum = 0, brow = 0;
+  *start = 0;
+  *len = 0;
+  for (int base = 0; base < num_groups; base += 64) {
     const int g = base + lane;
-    const bool valid = g < num_groups;
-    const int64_t raw = valid ? gl[g] : 0;
-    int64_t top;
-    if (list_type == 1) {
-      const int64_t inc = valid && raw > 0 ? raw : 0;
-      top = carry_cum + wave_incl_scan_add<int64_t>(inc, lane);
-      carry_cum = __shfl(top, 63, 64);
-    } else {
-      top = wave_incl_scan_max(valid ? raw : INT64_MIN, lane);
+    const int64_t mine = g < num_groups ? gl[g] : 0;
+    const int n = num_groups - base < 64 ? num_groups - base : 64;
+    for (int j = 0; j < n; ++j) {
+      const int64_t raw = lane_i64(mine, j);
+      int64_t end;
+      if (list_type == 1) {
+        cum += raw > 0 ? raw : 0;
+        end = cum;
+      } else {
+        end = raw;
+      }
+      end = end > prev_end ? end : prev_end;
+      end = end < rows ? end : rows;
+      const int64_t nb = (end - prev_end + ((int64_t)1 << block_log2) - 1) >> block_log2;
+      if (t < brow + nb) {
+        *start = prev_end + ((t - brow) << block_log2);
+        const int64_t rem = end - *start;
+        *len = rem < ((int64_t)1 << block_log2) ? rem : ((int64_t)1 << block_log2);
+        return;
+      }
+      brow += nb;
+      prev_end = end;
     }
-    int64_t end = top > carry_end ? top : carry_end;
-    end = end < rows ? end : rows;
-    int64_t prev = __shfl_up(end, 1, 64);
-    if (lane == 0) prev = carry_end;
-    const int64_t nb = valid ? (end - prev + block - 1) >> block_log2 : 0;
-    const int64_t bend = carry_b + wave_incl_scan_add<int64_t>(nb, lane);
-    const int64_t bstart = bend - nb;
-    const bool hit = valid && nb > 0 && t >= bstart && t < bend;
-    if (hit) {
-      start = prev + ((t - bstart) << block_log2);
-      len = end - start < block ? end - start : block;
-    }
-    const uint64_t any = __ballot(hit);
-    if (any) {
-      const int src = __ffsll((unsigned long long)any) - 1;
-      start = __shfl(start, src, 64);
-      len = __shfl(len, src, 64);
-      found = true;
-    }
-    carry_end = __shfl(end, 63, 64);
-    carry_b = __shfl(bend, 63, 64);
-  }
-  if (lane == 0) {
-    out[0] = start;
-    out[1] = found ? len : 0;
   }
 }
 

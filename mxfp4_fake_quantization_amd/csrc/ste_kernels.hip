@@ -140,15 +140,15 @@ __global__ __launch_bounds__(kThreads) void ste_col_kernel(SteColArgs A) {
   const int64_t ct = blockIdx.x - ts * A.nct;
   int64_t start, len;
   if (GROUPED) {
-    __shared__ int64_t s_blk[2];
     const int sub_log2 = A.block_log2 - 5;  // 32-row slabs per block-row (log2)
     const int64_t t = ts >> sub_log2;
     const int64_t q = ts - (t << sub_log2);
-    if (wave == 0) find_block_row(A.group_list, A.num_groups, A.list_type, A.rows, A.block_log2, t, s_blk);
-    __syncthreads();
-    start = s_blk[0] + 32 * q;
-    len = s_blk[1] - 32 * q;
-    if (len <= 0) return;  // whole workgroup
+    int64_t bstart, blen;
+    block_row_uniform(A.group_list, A.num_groups, A.list_type, A.rows, A.block_log2, t, &bstart,
+                      &blen);
+    start = bstart + 32 * q;
+    len = blen - 32 * q;
+    if (len <= 0) return;
     if (len > 32) len = 32;
   } else {
     start = 32 * ts;
