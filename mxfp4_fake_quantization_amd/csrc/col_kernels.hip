@@ -30,6 +30,17 @@ namespace mxfp4 {
 namespace {
 
 enum { kKindCol = 0, kKindDual = 1, kKindGrouped = 2 };
+// Minimum workgroups per CU requested from the compiler, which caps the
+// VGPRs (3 -> 168, 4 -> 128); chosen by measurement on MI355X.
+#ifndef MXFP4_COL_MINWG
+#define MXFP4_COL_MINWG 3
+#endif
+#ifndef MXFP4_DUAL_MINWG
+#define MXFP4_DUAL_MINWG 3
+#endif
+#ifndef MXFP4_GROUPED_MINWG
+#define MXFP4_GROUPED_MINWG 4
+#endif
 constexpr int kWaveCols = 128;
 
 struct ColArgs {
@@ -182,7 +193,10 @@ __device__ __forceinline__ void col_outputs(const ColArgs &A, const uint32_t (&w
 }
 
 template <int DT, int B, int RULE, int KIND, bool VEC>
-__global__ __launch_bounds__(kThreads, 4) void col_fwd_kernel(ColArgs A) {
+__global__ __launch_bounds__(kThreads, KIND == kKindDual      ? MXFP4_DUAL_MINWG
+                                       : KIND == kKindGrouped ? MXFP4_GROUPED_MINWG
+                                                              : MXFP4_COL_MINWG)
+void col_fwd_kernel(ColArgs A) {
   constexpr int NW = ColT<DT>::NW;
   constexpr int ES = ColT<DT>::ES;
   constexpr int WX = B == 32 ? 4 : 1;  // waves side by side

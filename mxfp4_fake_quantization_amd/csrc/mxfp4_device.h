@@ -86,6 +86,17 @@ __device__ __forceinline__ void st16(void *p, uint4 v) {
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
 }
 
+// Small stores (bitmap bytes, packed-code words, scale bytes); a
+// non-temporal hint measured no faster for them on MI355X, so it is off.
+#ifndef MXFP4_NT_SMALL
+#define MXFP4_NT_SMALL 0
+#endif
+template <typename T>
+__device__ __forceinline__ void st_small(T *p, T v) {
+  if (MXFP4_NT_SMALL) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 __device__ __forceinline__ float bits_f32(uint32_t b) { return __builtin_bit_cast(float, b); }
 
 // Block parameters for one block (or column) from its max magnitude bits.

@@ -20,7 +20,20 @@ namespace {
 
 // Chunks per thread: 1 for small tensors (more, shorter workgroups overlap
 // their loads and stores better), 2 above kRowBigChunks chunks.
+#ifndef MXFP4_ROW_U_SMALL
+#define MXFP4_ROW_U_SMALL 1
+#endif
+#ifndef MXFP4_ROW_U_BIG
+#define MXFP4_ROW_U_BIG 2
+#endif
+#ifndef MXFP4_PACK_U
+#define MXFP4_PACK_U 2
+#endif
 constexpr int64_t kRowBigChunks = int64_t(8) << 20;
+#ifndef MXFP4_ROW_THREADS
+#define MXFP4_ROW_THREADS 256
+#endif
+constexpr int kRowThreads = MXFP4_ROW_THREADS;  // threads per workgroup
 
 enum { kModeFlat = 0, kModeRowsVec = 1, kModeRowsScalar = 2 };
 
@@ -103,18 +116,18 @@ __device__ __forceinline__ void row_emit(const RowArgs &A, const uint32_t *wv, c
     if (emit & kEmitMask) {
       const uint32_t byte = chunk_mask<DT, SLOW>(wv, bp);
       if (MODE == kModeFlat) {
-        if (live) A.mask[cr] = (uint8_t)byte;
+        if (live) st_small(A.mask + cr, (uint8_t)byte);
       } else if (idx < A.nchunks && cr < A.mask_row_bytes) {
-        A.mask[row * A.mask_row_bytes + cr] = (uint8_t)byte;
+        st_small(A.mask + row * A.mask_row_bytes + cr, (uint8_t)byte);
       }
     }
     if (emit & kEmitCodes) {
       const uint32_t nib = chunk_codes<DT, SLOW>(wv, bp);
       if (MODE == kModeFlat) {
-        if (live) reinterpret_cast<uint32_t *>(A.codes)[cr] = nib;
+        if (live) st_small(reinterpret_cast<uint32_t *>(A.codes) + cr, nib);
       } else if (MODE == kModeRowsVec) {
         if (nval == 8)
-          *reinterpret_cast<uint32_t *>(A.codes + row * A.code_row_bytes + 4 * cr) = nib;
+          st_small(reinterpret_cast<uint32_t *>(A.codes + row * A.code_row_bytes + 4 * cr), nib);
       } else if (live) {
         uint8_t *dst = A.codes + row * A.code_row_bytes + 4 * cr;
         for (int j = 0; j < (nval + 1) / 2; ++j) dst[j] = (uint8_t)(nib >> (8 * j));
@@ -128,14 +141,14 @@ __device__ __forceinline__ void row_fwd_body(const RowArgs &A) {
   constexpr int NW = ChunkT<DT>::NW;
   constexpr int ES = ChunkT<DT>::ES;
   const int tid = threadIdx.x;
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * U);
+  const int64_t base = (int64_t)blockIdx.x * (kRowThreads * U);
 
   uint32_t w[U][NW];
   int64_t off[U], row[U], cr[U];
   int nval[U];
 #pragma unroll
   for (int s = 0; s < U; ++s) {
-    const int64_t i = base + s * kThreads + tid;
+    const int64_t i = base + s * kRowThreads + tid;
     if (MODE == kModeFlat) {
       row[s] = 0;
       cr[s] = i;
@@ -178,13 +191,13 @@ __device__ __forceinline__ void row_fwd_body(const RowArgs &A) {
 
     if (__builtin_expect(__any(bp.slow), 0))
       row_emit<DT, G, MODE, U, FULL, true>(A, w[s], bp, off[s], row[s], cr[s], nval[s],
-                                          base + s * kThreads + tid);
+                                          base + s * kRowThreads + tid);
     else
       row_emit<DT, G, MODE, U, FULL, false>(A, w[s], bp, off[s], row[s], cr[s], nval[s],
-                                           base + s * kThreads + tid);
-    if ((A.emit & kEmitScales) && (tid % G) == 0 && base + s * kThreads + tid < A.nchunks) {
+                                           base + s * kRowThreads + tid);
+    if ((A.emit & kEmitScales) && (tid % G) == 0 && base + s * kRowThreads + tid < A.nchunks) {
       const int64_t bi = MODE == kModeFlat ? cr[s] / G : row[s] * A.nb + cr[s] / G;
-      A.scales[bi] = (uint8_t)bp.e8;
+      st_small(A.scales + bi, (uint8_t)bp.e8);
     }
   }
 }
@@ -192,8 +205,8 @@ __device__ __forceinline__ void row_fwd_body(const RowArgs &A) {
 // A workgroup whose chunks are all in range (every one but possibly the
 // last, in the flat layout) takes the branch-free load path.
 template <int DT, int B, int RULE, int MODE, int U>
-__global__ __launch_bounds__(kThreads) void row_fwd_kernel(RowArgs A) {
-  if (MODE == kModeFlat && (int64_t)(blockIdx.x + 1) * (kThreads * U) <= A.nchunks)
+__global__ __launch_bounds__(kRowThreads) void row_fwd_kernel(RowArgs A) {
+  if (MODE == kModeFlat && (int64_t)(blockIdx.x + 1) * (kRowThreads * U) <= A.nchunks)
     row_fwd_body<DT, B, RULE, MODE, U, true>(A);
   else
     row_fwd_body<DT, B, RULE, MODE, U, false>(A);
@@ -201,12 +214,18 @@ __global__ __launch_bounds__(kThreads) void row_fwd_kernel(RowArgs A) {
 
 template <int DT, int B, int RULE, int MODE>
 hipError_t launch_u(const RowArgs &a, hipStream_t st) {
-  const int u = (MODE == kModeFlat && a.nchunks > kRowBigChunks) ? 2 : 1;
-  const int64_t nwg = (a.nchunks + (int64_t)kThreads * u - 1) / ((int64_t)kThreads * u);
+  int u = 1;
+  if (MODE == kModeFlat)
+    u = (a.emit & kEmitCodes) ? MXFP4_PACK_U
+                              : (a.nchunks > kRowBigChunks ? MXFP4_ROW_U_BIG : MXFP4_ROW_U_SMALL);
+  const int64_t nwg = (a.nchunks + (int64_t)kRowThreads * u - 1) / ((int64_t)kRowThreads * u);
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nwg);
-  if (u == 2) hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, MODE, 2>), grid, dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, MODE, 1>), grid, dim3(kThreads), 0, st, a);
+  switch (u) {
+    case 4: hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, MODE, 4>), grid, dim3(kRowThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, MODE, 2>), grid, dim3(kRowThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, MODE, 1>), grid, dim3(kRowThreads), 0, st, a); break;
+  }
   return hipGetLastError();
 }
 

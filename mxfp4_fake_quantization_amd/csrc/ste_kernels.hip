@@ -16,11 +16,21 @@
 namespace mxfp4 {
 namespace {
 
-// Pieces per thread: 4 for small tensors, 1 above kSteBigChunks pieces
+// Pieces per thread: 2 for small tensors, 1 above kSteBigChunks pieces
 // (measured on MI355X: short workgroups stream large tensors best, while
 // small launches are dominated by their start-up and prefer more loads in
 // flight per thread).
+#ifndef MXFP4_STE_U_SMALL
+#define MXFP4_STE_U_SMALL 2
+#endif
+#ifndef MXFP4_STE_U_BIG
+#define MXFP4_STE_U_BIG 1
+#endif
 constexpr int64_t kSteBigChunks = int64_t(8) << 20;
+#ifndef MXFP4_STE_THREADS
+#define MXFP4_STE_THREADS 256
+#endif
+constexpr int kSteThreads = MXFP4_STE_THREADS;  // threads per workgroup (row walk)
 enum { kModeFlat = 0, kModeRowsVec = 1, kModeRowsScalar = 2 };
 
 // Clear the elements whose bit is set.  bf16 word k holds elements 2k, 2k+1
@@ -53,14 +63,14 @@ __device__ __forceinline__ void ste_row_body(const SteRowArgs &A) {
   constexpr int NW = DT == kBF16 ? 4 : 8;
   constexpr int ES = DT == kBF16 ? 2 : 4;
   const int tid = threadIdx.x;
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * U);
+  const int64_t base = (int64_t)blockIdx.x * (kSteThreads * U);
   uint32_t w[U][NW];
   uint32_t bits[U];
   int64_t off[U];
   int nval[U];
 #pragma unroll
   for (int s = 0; s < U; ++s) {
-    const int64_t i = base + s * kThreads + tid;
+    const int64_t i = base + s * kSteThreads + tid;
     int64_t mb;
     if (MODE == kModeFlat) {
       off[s] = i * 8;
@@ -113,8 +123,8 @@ __device__ __forceinline__ void ste_row_body(const SteRowArgs &A) {
 
 // Workgroups whose pieces are all in range (flat layout) load unconditionally.
 template <int DT, int MODE, int U>
-__global__ __launch_bounds__(kThreads) void ste_row_kernel(SteRowArgs A) {
-  if (MODE == kModeFlat && (int64_t)(blockIdx.x + 1) * (kThreads * U) <= A.nchunks)
+__global__ __launch_bounds__(kSteThreads) void ste_row_kernel(SteRowArgs A) {
+  if (MODE == kModeFlat && (int64_t)(blockIdx.x + 1) * (kSteThreads * U) <= A.nchunks)
     ste_row_body<DT, MODE, U, true>(A);
   else
     ste_row_body<DT, MODE, U, false>(A);
@@ -246,22 +256,28 @@ hipError_t launch_row(const SteLaunch &L, hipStream_t st) {
     mode = L.cols % 8 == 0 ? kModeRowsVec : kModeRowsScalar;
     a.nchunks = L.rows * a.cpr;
   }
-  const int u = a.nchunks > kSteBigChunks ? 1 : 4;
-  const int64_t per = (int64_t)kThreads * u;
+  const int u = a.nchunks > kSteBigChunks ? MXFP4_STE_U_BIG : MXFP4_STE_U_SMALL;
+  const int64_t per = (int64_t)kSteThreads * u;
   const int64_t nwg = (a.nchunks + per - 1) / per;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   dim3 grid((unsigned)nwg);
-  if (u == 1) {
+  if (u == 2) {
     switch (mode) {
-      case kModeFlat: hipLaunchKernelGGL((ste_row_kernel<DT, kModeFlat, 1>), grid, dim3(kThreads), 0, st, a); break;
-      case kModeRowsVec: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsVec, 1>), grid, dim3(kThreads), 0, st, a); break;
-      default: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsScalar, 1>), grid, dim3(kThreads), 0, st, a); break;
+      case kModeFlat: hipLaunchKernelGGL((ste_row_kernel<DT, kModeFlat, 2>), grid, dim3(kSteThreads), 0, st, a); break;
+      case kModeRowsVec: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsVec, 2>), grid, dim3(kSteThreads), 0, st, a); break;
+      default: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsScalar, 2>), grid, dim3(kSteThreads), 0, st, a); break;
+    }
+  } else if (u == 1) {
+    switch (mode) {
+      case kModeFlat: hipLaunchKernelGGL((ste_row_kernel<DT, kModeFlat, 1>), grid, dim3(kSteThreads), 0, st, a); break;
+      case kModeRowsVec: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsVec, 1>), grid, dim3(kSteThreads), 0, st, a); break;
+      default: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsScalar, 1>), grid, dim3(kSteThreads), 0, st, a); break;
     }
   } else {
     switch (mode) {
-      case kModeFlat: hipLaunchKernelGGL((ste_row_kernel<DT, kModeFlat, 4>), grid, dim3(kThreads), 0, st, a); break;
-      case kModeRowsVec: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsVec, 4>), grid, dim3(kThreads), 0, st, a); break;
-      default: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsScalar, 4>), grid, dim3(kThreads), 0, st, a); break;
+      case kModeFlat: hipLaunchKernelGGL((ste_row_kernel<DT, kModeFlat, 4>), grid, dim3(kSteThreads), 0, st, a); break;
+      case kModeRowsVec: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsVec, 4>), grid, dim3(kSteThreads), 0, st, a); break;
+      default: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsScalar, 4>), grid, dim3(kSteThreads), 0, st, a); break;
     }
   }
   return hipGetLastError();
