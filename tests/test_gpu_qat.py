@@ -1,0 +1,90 @@
+"""GPU checks of the QAT wrapper: forward values and STE gradients through
+autograd equal the oracle's QDQ and masked gradients; the QAT Linear's
+gradients match a float reference built from the oracle's quantized
+operands; the amct PR's minimal validation (Linear(64, 32), W4A4, sum
+backward, finite gradients) passes."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("clip", [False, True])
+@pytest.mark.parametrize("block", [32, 128])
+def test_fake_quant_forward_backward(oracle, dtype, clip, block):
+    from mxfp4_fake_quantization_amd.qat import mxfp4_fake_quant
+    g = np.random.default_rng(block + clip)
+    a = (g.standard_t(3, size=(3, 5, 256)) * 0.05).astype(np.float32)
+    x_np = W.f32_to_bf16_bits(a) if dtype == "bf16" else a
+    up_np = g.standard_normal(a.shape).astype(np.float32)
+    up_np = W.f32_to_bf16_bits(up_np) if dtype == "bf16" else up_np
+    x = dev(x_np).requires_grad_(True)
+    y = mxfp4_fake_quant(x, block_size=block, clip_grad=clip)
+    y.backward(dev(up_np))
+    yo, cl, _ = oracle.qdq_rows(x_np.reshape(-1, 256), block)
+    assert np.array_equal(host(y.detach()).reshape(-1, 256), yo)
+    want = oracle.ste_bwd(up_np.reshape(-1, 256), cl if clip else None)
+    assert np.array_equal(host(x.grad).reshape(-1, 256), want)
+
+
+def test_qat_linear_gradients_match_reference(oracle):
+    from mxfp4_fake_quantization_amd.qat import MXFP4QATConfig, MXFP4QATLinear
+    torch.manual_seed(0)
+    cfg = MXFP4QATConfig(quantize_input=True, clip_grad=True)
+    lin = MXFP4QATLinear(96, 40, config=cfg).cuda()
+    x = torch.randn(7, 96, device="cuda") * 3
+    x.requires_grad_(True)
+    out = lin(x)
+    out.square().sum().backward()
+    # reference in fp32 on the CPU from the oracle's quantized operands / masks
+    w_np = lin.weight.detach().cpu().numpy()
+    x_np = x.detach().cpu().numpy()
+    wq, wm, _ = oracle.qdq_rows(w_np, 32)
+    xq, xm, _ = oracle.qdq_rows(x_np, 32)
+    wq_t, xq_t = torch.from_numpy(wq), torch.from_numpy(xq)
+    ref_out = xq_t @ wq_t.T + lin.bias.detach().cpu()
+    assert torch.allclose(out.detach().cpu(), ref_out, rtol=1e-5, atol=1e-4)
+    dy = 2 * ref_out
+    gw = (dy.T @ xq_t) * torch.from_numpy(~wm).float()
+    gx = (dy @ wq_t) * torch.from_numpy(~xm).float()
+    assert torch.allclose(lin.weight.grad.cpu(), gw, rtol=1e-4, atol=1e-3)
+    assert torch.allclose(x.grad.cpu(), gx, rtol=1e-4, atol=1e-3)
+    assert torch.allclose(lin.bias.grad.cpu(), dy.sum(0), rtol=1e-4, atol=1e-3)
+
+
+def test_minimal_validation_scenario():
+    """The PR's own check: Linear(64, 32) converted with quantize_input=True,
+    forward on randn(4, 64), sum().backward(), finite weight gradient."""
+    from mxfp4_fake_quantization_amd.qat import MXFP4QATConfig, MXFP4QATLinear, convert_to_mxfp4_qat
+    torch.manual_seed(0)
+    model = torch.nn.Sequential(torch.nn.Linear(64, 32)).cuda()
+    convert_to_mxfp4_qat(model, MXFP4QATConfig(quantize_input=True))
+    assert isinstance(model[0], MXFP4QATLinear)
+    model(torch.randn(4, 64, device="cuda")).sum().backward()
+    assert torch.isfinite(model[0].weight.grad).all()
+    assert model[0].weight.grad.abs().sum() > 0
+
+
+def test_bf16_qat_step_runs():
+    from mxfp4_fake_quantization_amd.qat import MXFP4QATConfig, convert_to_mxfp4_qat
+    torch.manual_seed(1)
+    model = torch.nn.Sequential(torch.nn.Linear(256, 128), torch.nn.GELU(),
+                                torch.nn.Linear(128, 64)).cuda().to(torch.bfloat16)
+    convert_to_mxfp4_qat(model, MXFP4QATConfig(quantize_input=True, clip_grad=True, block_size=128))
+    opt = torch.optim.SGD(model.parameters(), lr=1e-2)
+    x = torch.randn(16, 256, device="cuda", dtype=torch.bfloat16)
+    loss = model(x).float().square().mean()
+    loss.backward()
+    opt.step()
+    assert all(torch.isfinite(p).all() for p in model.parameters())
