@@ -40,8 +40,11 @@ def _load():
         lib.oracle_ste_bwd.argtypes = [i32, i64, vp, vp, vp]
         lib.oracle_pack_rows.argtypes = [i32, i64, i64, i32, i32, f32, vp, vp, vp]
         lib.oracle_unpack_rows.argtypes = [i32, i64, i64, i32, vp, vp, vp]
+        lib.oracle_pack_kmajor.argtypes = [i32, i64, i64, i32, i32, f32, vp, vp, i32, i32, i64,
+                                           vp, vp]
         for fn in ("oracle_qdq_rows", "oracle_qdq_cols", "oracle_grouped_cols",
-                   "oracle_ste_bwd", "oracle_pack_rows", "oracle_unpack_rows"):
+                   "oracle_ste_bwd", "oracle_pack_rows", "oracle_unpack_rows",
+                   "oracle_pack_kmajor"):
             getattr(lib, fn).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -153,3 +156,29 @@ def unpack_rows(codes: np.ndarray, scales: np.ndarray, cols: int, block: int = 3
                                       _ptr(scales), _ptr(y)),
            "unpack_rows")
     return y
+
+
+def pack_kmajor(x: np.ndarray, block: int = 32, rule="floor", scale_factor: float = 6.0,
+                group_list=None, list_type: int = 1, k_blocks=None, fill: int = 0xA5):
+    """K-major packed form of column-wise (group_list None) or grouped blocks.
+
+    Returns (codes_t[cols, k_blocks*block/2], scales_t[cols, k_blocks], nbt); block-rows
+    at or past nbt keep the `fill` byte (not touched)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    if group_list is None:
+        gl, ng = None, 0
+        counts = [rows]
+    else:
+        gl = np.ascontiguousarray(np.asarray(group_list, dtype=np.int64))
+        ng = len(gl)
+        counts = gl if list_type == 1 else np.diff(np.concatenate([[0], gl]))
+    nbt = int(sum(-(-int(c) // block) for c in counts if c > 0))
+    kb = nbt if k_blocks is None else int(k_blocks)
+    codes = np.full((cols, kb * block // 2), fill, np.uint8)
+    scales = np.full((cols, kb), fill, np.uint8)
+    _check(_load().oracle_pack_kmajor(_dtype_code(x), rows, cols, block, _rule_code(rule),
+                                      scale_factor, _ptr(x), _ptr(gl), ng, list_type, kb,
+                                      _ptr(codes), _ptr(scales)),
+           "pack_kmajor")
+    return codes, scales, nbt

@@ -17,7 +17,8 @@
  * The grouped (per-expert) column-wise blocking follows the MindSpore
  * hyper-parallel page "fake_w4a8_gmm_func.py" (normalize_group_list: counts
  * -> cumulative sums), and the packed form follows the sglang "mxfp4_npu.py"
- * page (two FP4 codes per byte).
+ * page (two FP4 codes per byte); oracle_pack_kmajor stores the column-wise /
+ * grouped operand in that packed form with the reduction dimension contiguous.
  *
  * Two scale rules ("profiles"):
  *   FLOOR (default): k = floor(log2 amax) - 2, clamped below at -127; an
@@ -289,5 +290,80 @@ int oracle_unpack_rows(int dtype, int64_t rows, int64_t cols, int block,
       put_elem(dtype, y, r * cols + c, v);
     }
   }
+  return 0;
+}
+
+/* K-major ("transposed") packed form of column-wise or grouped blocks: the
+ * operand layout an MX matrix product reads along its reduction dimension
+ * (the hyper-parallel page's col_data / col_scale directional operand, stored
+ * packed two codes per byte as on the sglang page).  Column c of x becomes
+ * row c of codes_t: K-position p = t*block + o holds x row start_t + o of
+ * block-row t when o < len_t, else a padding code 0; bytes pair K-positions
+ * (2j, 2j+1) with 2j in the low nibble.  Block-rows are those of
+ * oracle_qdq_cols (group_list NULL: block t is rows t*block .. t*block +
+ * block - 1, the last one possibly short) or of oracle_grouped_cols (blocks
+ * restart at every group start).
+ *   codes_t  [cols, k_blocks * block / 2] bytes,
+ *   scales_t [cols, k_blocks] E8M0 bytes (k + 127).
+ * Block-rows t >= NBT (the number the blocking yields) are not touched.
+ * Returns 1 for bad sizes (k_blocks < NBT, odd block) or an inconsistent
+ * group list, as oracle_grouped_cols does. */
+int oracle_pack_kmajor(int dtype, int64_t rows, int64_t cols, int block, int rule,
+                       float sf, const void *x, const int64_t *group_list,
+                       int num_groups, int list_type, int64_t k_blocks,
+                       uint8_t *codes_t, uint8_t *scales_t) {
+  if (block <= 0 || (block & 1) || rows < 0 || cols < 0 || k_blocks < 0) return 1;
+  if (group_list && num_groups < 1) return 1;
+  int64_t *idx = (int64_t *)malloc(sizeof(int64_t) * (size_t)block);
+  uint8_t *nib = (uint8_t *)calloc((size_t)(rows * cols) + 1, 1);
+  if (!idx || !nib) {
+    free(idx);
+    free(nib);
+    return 2;
+  }
+  /* block-row list: (start, len) per block-row, in order */
+  int64_t nbt = 0, start = 0;
+  int ng = group_list ? num_groups : 1;
+  int64_t *bstart = (int64_t *)malloc(sizeof(int64_t) * (size_t)(rows / block + ng + 1));
+  int64_t *blen = (int64_t *)malloc(sizeof(int64_t) * (size_t)(rows / block + ng + 1));
+  if (!bstart || !blen) {
+    free(idx); free(nib); free(bstart); free(blen);
+    return 2;
+  }
+  for (int g = 0; g < ng; ++g) {
+    int64_t end = !group_list ? rows : (list_type == 1 ? start + group_list[g] : group_list[g]);
+    if (end < start || end > rows) {
+      free(idx); free(nib); free(bstart); free(blen);
+      return 1;
+    }
+    for (int64_t r0 = start; r0 < end; r0 += block) {
+      bstart[nbt] = r0;
+      blen[nbt] = (end - r0) < block ? (end - r0) : block;
+      ++nbt;
+    }
+    start = end;
+  }
+  if (nbt > k_blocks) {
+    free(idx); free(nib); free(bstart); free(blen);
+    return 1;
+  }
+  int64_t ldk = k_blocks * block / 2; /* bytes per row of codes_t */
+  for (int64_t t = 0; t < nbt; ++t) {
+    int n = (int)blen[t];
+    for (int64_t c = 0; c < cols; ++c) {
+      for (int j = 0; j < n; ++j) idx[j] = (bstart[t] + j) * cols + c;
+      int k = qdq_block(dtype, rule, sf, x, idx, n, NULL, NULL, nib);
+      scales_t[c * k_blocks + t] = (uint8_t)(k + 127);
+      for (int o = 0; o < block; o += 2) {
+        uint8_t lo = o < n ? nib[idx[o]] : 0;
+        uint8_t hi = o + 1 < n ? nib[idx[o + 1]] : 0;
+        codes_t[c * ldk + (t * block + o) / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+  free(idx);
+  free(nib);
+  free(bstart);
+  free(blen);
   return 0;
 }

@@ -32,6 +32,11 @@ MUTANTS = {
                       "for (int64_t r0 = start; r0 < end; r0 = (r0 / block + 1) * block, ++brow) {"),
     "ste_negative_zero": ("if (clip && clip[i]) g = 0.0;", "if (clip && clip[i]) g = -0.0;"),
     "nibble_order": ("codes[r * half + t] = (uint8_t)(lo | (hi << 4));", "codes[r * half + t] = (uint8_t)(hi | (lo << 4));"),
+    "kmajor_nibble_order": ("codes_t[c * ldk + (t * block + o) / 2] = (uint8_t)(lo | (hi << 4));",
+                            "codes_t[c * ldk + (t * block + o) / 2] = (uint8_t)(hi | (lo << 4));"),
+    "kmajor_scale_layout": ("scales_t[c * k_blocks + t] = ", "scales_t[t * cols + c] = "),
+    "kmajor_pad_code": ("uint8_t lo = o < n ? nib[idx[o]] : 0;", "uint8_t lo = o < n ? nib[idx[o]] : 8;"),
+    "kmajor_leading_dim": ("int64_t ldk = k_blocks * block / 2;", "int64_t ldk = nbt * block / 2;"),
     "e8m0_bias": ("if (e8m0) e8m0[r * nb + b] = (uint8_t)(k + 127);", "if (e8m0) e8m0[r * nb + b] = (uint8_t)(k + 128);"),
 }
 

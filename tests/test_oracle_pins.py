@@ -411,6 +411,121 @@ def test_pack_nibble_order_and_codes(oracle):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unpack_every_nibble_and_scale_byte(oracle, dtype):
+    """Decoding is (-1)^s * code * 2^(e8 - 127) for every nibble and every E8M0
+    byte: exact (all such values fit fp32 and bf16, subnormals included) up to
+    overflow, which gives +-inf (code * 2^(e8-127) > max finite)."""
+    nib = np.arange(16, dtype=np.uint8)
+    codes = np.repeat((nib | (nib << 4))[None, :], 256, axis=0)        # 256 x 16 bytes
+    codes = np.ascontiguousarray(codes[:, :16])
+    scales = np.arange(256, dtype=np.uint8)[:, None]                 # one 32-block per row
+    want = np.empty((256, 32), np.float64)
+    for e8 in range(256):
+        for j in range(32):
+            n = j // 2
+            v = CODES[n & 7] * math.ldexp(1.0, e8 - 127)
+            want[e8, j] = -v if n & 8 else v
+    with np.errstate(over="ignore"):
+        w32 = want.astype(np.float32)
+    got = oracle.unpack_rows(codes, scales, 32, 32, np.float32 if dtype == "f32" else np.uint16)
+    if dtype == "f32":
+        assert np.array_equal(got.view(np.uint32), w32.view(np.uint32))
+    else:
+        assert np.array_equal(got, W.f32_to_bf16_bits(w32))
+        # exactness in bf16: the decoded value round-trips unless it overflowed
+        fin = np.isfinite(w32)
+        assert np.array_equal(W.bf16_bits_to_f32(got)[fin], w32[fin])
+    assert np.isinf(w32[253, 2 * 7]) and np.isfinite(w32[252, 2 * 7])   # 6 * 2^126 overflows
+
+
+def test_kmajor_hand_worked(oracle):
+    """A column [1, -2, 3, 0.5] with 4-row blocks (oracle-only block size):
+    amax 3 -> FLOOR k = floor(log2 3) - 2 = -1, scale 0.5, so x/scale =
+    [2, -4, 6, 1] -> codes 4, 8|6, 7, 2 -> bytes 0xE4, 0x27, E8M0 126.  The
+    second column is all zero: k = -127, E8M0 0, codes 0."""
+    x = f32([[1.0, 0.0], [-2.0, 0.0], [3.0, 0.0], [0.5, 0.0]])
+    codes, sc, nbt = oracle.pack_kmajor(x, 4, "floor")
+    assert nbt == 1
+    assert codes.tolist() == [[0xE4, 0x27], [0x00, 0x00]]
+    assert sc.tolist() == [[126], [0]]
+
+
+def _pad_t(a, kp):
+    """Transpose and zero-pad the K (row) dimension to kp."""
+    t = np.zeros((a.shape[1], kp), a.dtype)
+    t[:, :a.shape[0]] = a.T
+    return t
+
+
+@pytest.mark.parametrize("block", [32, 128])
+@pytest.mark.parametrize("rule", ["floor", "amct"])
+@pytest.mark.parametrize("rows", [64 * 4, 64 * 4 + 37])
+def test_kmajor_is_pack_of_padded_transpose(oracle, block, rule, rows):
+    """Dense K-major codes are the row-wise packing of x^T with K zero-padded to
+    whole blocks (zeros never change a block max and encode as +0), and they
+    decode to the column-wise QDQ values."""
+    g = np.random.default_rng(45)
+    x = W.f32_to_bf16_bits((g.standard_t(3, size=(rows, 20)) * 0.1).astype(np.float32))
+    codes, sc, nbt = oracle.pack_kmajor(x, block, rule)
+    kp = nbt * block
+    assert nbt == -(-rows // block)
+    c2, s2 = oracle.pack_rows(_pad_t(x, kp), block, rule)
+    assert np.array_equal(codes, c2) and np.array_equal(sc, s2)
+    yc, _, ec = oracle.qdq_cols(x, block, rule)
+    assert np.array_equal(sc, ec.T)
+    dec = oracle.unpack_rows(codes, sc, kp, block)
+    assert np.array_equal(dec[:, :rows], yc.T)
+    assert (dec[:, rows:] == 0).all()
+
+
+@pytest.mark.parametrize("block", [32, 128])
+def test_kmajor_grouped_is_per_group_pack(oracle, block):
+    """Grouped K-major: each group's slab packed on its own (K zero-padded to
+    whole blocks), concatenated along K; decodes to grouped_cols' values."""
+    g = np.random.default_rng(46)
+    x = W.f32_to_bf16_bits((g.standard_t(4, size=(700, 12))).astype(np.float32))
+    counts = W.ragged_counts(700, 6, seed=5, zero_groups=1)
+    kb = -(-700 // block) + len(counts) - 1
+    codes, sc, nbt = oracle.pack_kmajor(x, block, "floor", group_list=counts, k_blocks=kb)
+    codes0, sc0, _ = oracle.pack_kmajor(x, block, "floor", group_list=np.cumsum(counts),
+                                        list_type=0, k_blocks=kb)
+    assert np.array_equal(codes, codes0) and np.array_equal(sc, sc0)
+    start, t = 0, 0
+    for c in counts:
+        nb = -(-int(c) // block)
+        if nb:
+            c2, s2 = oracle.pack_rows(_pad_t(x[start:start + c], nb * block), block)
+            assert np.array_equal(codes[:, t * block // 2:(t + nb) * block // 2], c2)
+            assert np.array_equal(sc[:, t:t + nb], s2)
+        start += int(c)
+        t += nb
+    assert t == nbt <= kb
+    assert (codes[:, nbt * block // 2:] == 0xA5).all() and (sc[:, nbt:] == 0xA5).all()
+    yg, _, eg = oracle.grouped_cols(x, counts, block)
+    assert np.array_equal(sc[:, :nbt], eg.T)
+    dec = oracle.unpack_rows(np.ascontiguousarray(codes[:, :nbt * block // 2]),
+                             np.ascontiguousarray(sc[:, :nbt]), nbt * block, block)
+    start, t = 0, 0
+    for c in counts:
+        c = int(c)
+        if c:
+            assert np.array_equal(dec[:, t * block:t * block + c], yg[start:start + c].T)
+            assert (dec[:, t * block + c:(t + -(-c // block)) * block] == 0).all()
+        start += c
+        t += -(-c // block)
+
+
+def test_kmajor_rejects_bad_sizes(oracle):
+    x = np.zeros((70, 4), np.uint16)
+    with pytest.raises(ValueError):
+        oracle.pack_kmajor(x, 32, k_blocks=2)                  # needs 3 block-rows
+    with pytest.raises(ValueError):
+        oracle.pack_kmajor(x, 32, group_list=[30, 41], k_blocks=4)
+    c, s, nbt = oracle.pack_kmajor(x, 32, group_list=[1, 0, 69], k_blocks=4)
+    assert nbt == 4
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_ste_backward(oracle, dtype):
     g = np.random.default_rng(61)
     x32 = (g.standard_t(3, size=(16, 96)) * 0.02).astype(np.float32)
