@@ -333,6 +333,18 @@ def bench_all(M, lib, W, torch, args):
         pcalls = [Call(lib.mxfp4_quant_pack, ctypes.byref(dp), vp(xs[i].data_ptr()), vp(codes[i].data_ptr()),
                        vp(scs[i].data_ptr()), None, None, stream) for i in range(2)]
         rec(f"pack_28672x8192_b{blk}", R * C * (2 + 0.5 + 1 / blk), R * C, _time_calls(torch, pcalls, 30))
+        # K-major packed operand of the same weight (blocks along its 28672 rows)
+        kb = R // blk
+        kc = [torch.empty((C, kb * blk // 2), dtype=torch.uint8, device="cuda") for _ in range(2)]
+        ks = [torch.empty((C, kb), dtype=torch.uint8, device="cuda") for _ in range(2)]
+        kcalls = [Call(lib.mxfp4_quant_pack_kmajor, ctypes.byref(dp), vp(xs[i].data_ptr()), None, 0, 1, kb,
+                       vp(kc[i].data_ptr()), vp(ks[i].data_ptr()), stream) for i in range(2)]
+        rec(f"kmajor_28672x8192_b{blk}", R * C * (2 + 0.5 + 1 / blk), R * C, _time_calls(torch, kcalls, 30))
+        del kc, ks
+        # decode of the row-wise packed form back to bf16
+        dcalls = [Call(lib.mxfp4_dequant, ctypes.byref(dp), vp(codes[i].data_ptr()), vp(scs[i].data_ptr()),
+                       vp(ys[i].data_ptr()), stream) for i in range(2)]
+        rec(f"dequant_28672x8192_b{blk}", R * C * (0.5 + 1 / blk + 2), R * C, _time_calls(torch, dcalls, 30))
         del codes, scs
     del xs, ys, mk
 
@@ -364,7 +376,16 @@ def bench_all(M, lib, W, torch, args):
     calls = [Call(lib.mxfp4_grouped_qdq, ctypes.byref(d), vp(xs[i].data_ptr()), vp(gl.data_ptr()), 8, 1,
                   vp(ys[i].data_ptr()), None, None, stream) for i in range(2)]
     rec("grouped_32768x7168_y", R * C * 4.0, R * C, _time_calls(torch, calls, 30))
-    del xs, ys
+    del ys
+    # grouped K-major packed operand (block-rows padded per group)
+    nbt = int(sum(-(-int(c) // 32) for c in counts))
+    kb = M.kmajor_k_blocks(R, 32, len(counts))
+    kc = [torch.empty((C, kb * 16), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ks = [torch.empty((C, kb), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    kcalls = [Call(lib.mxfp4_quant_pack_kmajor, ctypes.byref(d), vp(xs[i].data_ptr()), vp(gl.data_ptr()), 8, 1,
+                   kb, vp(kc[i].data_ptr()), vp(ks[i].data_ptr()), stream) for i in range(2)]
+    rec("kmajor_grouped_32768x7168", R * C * 2 + C * nbt * (16 + 1), R * C, _time_calls(torch, kcalls, 30))
+    del xs, kc, ks
     return out
 
 

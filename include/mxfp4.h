@@ -173,6 +173,56 @@ mxfp4_status_t mxfp4_grouped_qdq(const mxfp4_desc_t *desc, const void *x,
                                  uint32_t *mask_opt, uint8_t *scales_opt,
                                  void *stream);
 
+/*
+ * K-major packed operand of column-wise or grouped blocks: the hyper-parallel
+ * page's column-direction operand (col_data / col_scale of the grouped W4A8
+ * matmul), stored packed as on the sglang page (float4_e2m1fn_x2: two FP4
+ * codes per byte), with the reduction dimension (the rows of x) contiguous,
+ * i.e. the row-wise packed form of x^T with K padded to whole blocks.
+ *   group_list NULL: dense column-wise blocks (rows t*block .. t*block +
+ *     block - 1, the last one possibly short), NBT = ceil(rows/block);
+ *   group_list non-NULL: grouped blocks exactly as mxfp4_grouped_qdq numbers
+ *     them (same group_list / num_groups / group_list_type contract).
+ *   codes_t  [cols, k_blocks * block / 2] bytes: byte j of row c holds K
+ *            positions 2j (low nibble) and 2j+1 (high nibble); K position
+ *            t*block + o is x[start_t + o, c] for o < len_t and a padding code
+ *            0 otherwise.  Row c starts at c * k_blocks * block / 2 bytes.
+ *   scales_t [cols, k_blocks] E8M0 bytes, scale of block-row t of column c at
+ *            c * k_blocks + t.
+ * k_blocks (the K extent in blocks, >= NBT) must be >= ceil(rows/block)
+ * (dense) or >= ceil(rows/block) + num_groups - 1, the most block-rows any
+ * group split can produce (grouped); block-rows t >= NBT are not touched.
+ * Values and scales are those of mxfp4_qdq_fwd(axis = MXFP4_COL) /
+ * mxfp4_grouped_qdq: decoding codes_t with mxfp4_dequant (rows = cols of x,
+ * cols = k_blocks * block) gives their y transposed, with zeros at padding.
+ * codes_t 16-byte aligned; scales_t any alignment; no aliasing.
+ */
+mxfp4_status_t mxfp4_quant_pack_kmajor(const mxfp4_desc_t *desc, const void *x,
+                                       const int64_t *group_list,
+                                       int32_t num_groups,
+                                       int32_t group_list_type,
+                                       int64_t k_blocks, uint8_t *codes_t,
+                                       uint8_t *scales_t, void *stream);
+
+/*
+ * Decode (dequantize) the packed form back to values: y[r, c] =
+ * (-1)^s * code * 2^(e8 - 127) with the nibble of element c of row r and the
+ * E8M0 byte of its block (the sglang page's packed storage read back; the
+ * inverse of mxfp4_quant_pack).  desc->rows x desc->cols is y's shape,
+ * desc->dtype its dtype (MXFP4_BF16 or MXFP4_F32), desc->block the block of
+ * the scales; desc->rule and scale_factor are ignored.
+ *   codes  [rows, ceil(cols/2)] (mxfp4_quant_pack layout; K-major codes_t
+ *          with rows = cols of x and cols = k_blocks * block),
+ *   scales [rows, ceil(cols/block)].
+ * Every byte pattern decodes: results are exact (all such values, subnormals
+ * included, fit bf16 and fp32) except that values above the largest finite
+ * become +-inf (E8M0 >= 253 with large codes); 0xFF is decoded by the same
+ * formula.  A sign bit on code 0 gives -0.0.
+ * codes and y 16-byte aligned; scales any alignment; no aliasing.
+ */
+mxfp4_status_t mxfp4_dequant(const mxfp4_desc_t *desc, const uint8_t *codes,
+                             const uint8_t *scales, void *y, void *stream);
+
 /* Message for the calling thread's most recent failed call ("" if none). */
 const char *mxfp4_last_error(void);
 

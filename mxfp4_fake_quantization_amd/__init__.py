@@ -16,6 +16,9 @@ argument and enqueue on torch's current stream:
                      scale_factor=6.0)
     mxfp4_grouped_qdq(x, group_list, y, mask=None, scales=None, block=32,
                       rule="floor", scale_factor=6.0, group_list_type=1)
+    mxfp4_quant_pack_kmajor(x, codes_t, scales_t, block=32, rule="floor",
+                            scale_factor=6.0, group_list=None, group_list_type=1)
+    mxfp4_dequant(codes, scales, y, block=32)
 
 Tensor conventions: x / y / grads are bfloat16 or float32, 2-D contiguous
 (higher ranks are viewed as rows x last-dim); bitmaps are int32 tensors (the
@@ -32,8 +35,10 @@ import torch
 __all__ = [
     "ROW", "COL", "GROUPED", "FLOOR", "AMCT",
     "mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
+    "mxfp4_quant_pack_kmajor", "mxfp4_dequant",
     "mxfp4_last_error", "mxfp4_version", "library_path",
     "row_mask_shape", "col_mask_shape", "grouped_mask_rows_max", "grouped_scale_rows_max",
+    "kmajor_k_blocks",
 ]
 
 ROW, COL, GROUPED = 1, 2, 4
@@ -68,8 +73,10 @@ def _load():
         lib.mxfp4_ste_bwd.argtypes = [dp, i32, vp, vp, vp, vp, i32, i32, vp]
         lib.mxfp4_quant_pack.argtypes = [dp, vp, vp, vp, vp, vp, vp]
         lib.mxfp4_grouped_qdq.argtypes = [dp, vp, vp, i32, i32, vp, vp, vp, vp]
+        lib.mxfp4_quant_pack_kmajor.argtypes = [dp, vp, vp, i32, i32, ctypes.c_int64, vp, vp, vp]
+        lib.mxfp4_dequant.argtypes = [dp, vp, vp, vp, vp]
         for f in ("mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
-                  "mxfp4_version"):
+                  "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp4_version"):
             getattr(lib, f).restype = ctypes.c_int32
         lib.mxfp4_last_error.restype = ctypes.c_char_p
         lib.mxfp4_last_error.argtypes = []
@@ -204,6 +211,39 @@ def mxfp4_grouped_qdq(x, group_list, y, mask=None, scales=None, block=32, rule="
     _check(st, "mxfp4_grouped_qdq")
 
 
+def mxfp4_quant_pack_kmajor(x, codes_t, scales_t, block=32, rule="floor", scale_factor=6.0,
+                            group_list=None, group_list_type=1):
+    """K-major packed operand of column-wise (group_list None) or grouped
+    blocks: codes_t [cols, k_blocks * block / 2] and scales_t [cols, k_blocks]
+    uint8, k_blocks being scales_t's second dimension (see kmajor_k_blocks)."""
+    rows, cols = _shape2d(x)
+    if scales_t is None or scales_t.dim() != 2 or scales_t.shape[0] != cols:
+        raise ValueError(f"scales_t must be [cols={cols}, k_blocks]")
+    k_blocks = int(scales_t.shape[1])
+    if codes_t is None or tuple(codes_t.shape) != (cols, k_blocks * int(block) // 2):
+        raise ValueError(f"codes_t must be [{cols}, {k_blocks * int(block) // 2}]")
+    d = _desc(x, block, rule, scale_factor)
+    n_groups = group_list.numel() if group_list is not None else 0
+    st = _load().mxfp4_quant_pack_kmajor(ctypes.byref(d), _ptr(x), _ptr(group_list, "i64"),
+                                         n_groups, int(group_list_type), k_blocks,
+                                         _ptr(codes_t, "u8"), _ptr(scales_t, "u8"), _stream())
+    _check(st, "mxfp4_quant_pack_kmajor")
+
+
+def mxfp4_dequant(codes, scales, y, block=32):
+    """Decode packed codes [rows, ceil(cols/2)] + E8M0 scales [rows,
+    ceil(cols/block)] into y [rows, cols] (bfloat16 or float32)."""
+    rows, cols = _shape2d(y)
+    if codes is None or tuple(codes.shape) != (rows, (cols + 1) // 2):
+        raise ValueError(f"codes must be [{rows}, {(cols + 1) // 2}]")
+    if scales is None or tuple(scales.shape) != (rows, -(-cols // int(block))):
+        raise ValueError(f"scales must be [{rows}, {-(-cols // int(block))}]")
+    d = _Desc(_dtype(y), int(block), FLOOR, 0, rows, cols, 6.0, 0)
+    st = _load().mxfp4_dequant(ctypes.byref(d), _ptr(codes, "u8"), _ptr(scales, "u8"), _ptr(y),
+                               _stream())
+    _check(st, "mxfp4_dequant")
+
+
 # ------------------------------------------------------------ shapes
 
 def row_mask_shape(rows: int, cols: int):
@@ -220,3 +260,13 @@ def grouped_scale_rows_max(rows: int, block: int, num_groups: int) -> int:
 
 def grouped_mask_rows_max(rows: int, block: int, num_groups: int) -> int:
     return grouped_scale_rows_max(rows, block, num_groups) * (block // 32)
+
+
+def kmajor_k_blocks(rows: int, block: int, num_groups=None) -> int:
+    """Smallest k_blocks mxfp4_quant_pack_kmajor accepts: ceil(rows/block)
+    dense, ceil(rows/block) + num_groups - 1 grouped (the most block-rows any
+    split of `rows` into num_groups groups produces)."""
+    nb = -(-rows // block)
+    if num_groups is None or rows == 0:
+        return nb
+    return nb + int(num_groups) - 1

@@ -192,8 +192,54 @@ mxfp4_status_t mxfp4_grouped_qdq(const mxfp4_desc_t *desc, const void *x,
   return hip_status(mxfp4::launch_col_fwd(L, static_cast<hipStream_t>(stream)), "grouped launch");
 }
 
+mxfp4_status_t mxfp4_quant_pack_kmajor(const mxfp4_desc_t *desc, const void *x,
+                                       const int64_t *group_list, int32_t num_groups,
+                                       int32_t group_list_type, int64_t k_blocks,
+                                       uint8_t *codes_t, uint8_t *scales_t, void *stream) {
+  int64_t n;
+  MXFP4_TRY(check_desc(desc, true, &n));
+  MXFP4_TRY(check_ptr(x, 16, "x"));
+  MXFP4_TRY(check_ptr(codes_t, 16, "codes_t"));
+  MXFP4_TRY(check_ptr(scales_t, 1, "scales_t"));
+  const int64_t nb = (desc->rows + desc->block - 1) / desc->block;
+  int64_t need = nb;
+  if (group_list) {
+    if (!aligned(group_list, 8)) return fail(MXFP4_EINVAL, "group_list is not 8-byte aligned");
+    if (num_groups < 1) return fail(MXFP4_EINVAL, "num_groups must be >= 1 (got %d)", num_groups);
+    if (group_list_type != 0 && group_list_type != 1)
+      return fail(MXFP4_EINVAL, "group_list_type must be 0 or 1 (got %d)", group_list_type);
+    need = desc->rows > 0 ? nb + num_groups - 1 : 0;
+  }
+  if (k_blocks < need)
+    return fail(MXFP4_EINVAL, "k_blocks %lld is below the %lld block-rows the blocking can produce",
+                (long long)k_blocks, (long long)need);
+  if (desc->cols > 0 && k_blocks > INT64_MAX / 4 / desc->block / desc->cols)
+    return fail(MXFP4_EINVAL, "cols * k_blocks * block overflows");
+  if (!distinct({x, codes_t, scales_t, group_list}))
+    return fail(MXFP4_EINVAL, "outputs alias each other, x or group_list");
+  if (n == 0) return ok();
+  mxfp4::KmLaunch L{desc->dtype, desc->block, desc->rule, desc->rows, desc->cols,
+                    desc->scale_factor, x, group_list, num_groups, group_list_type,
+                    k_blocks, codes_t, scales_t};
+  return hip_status(mxfp4::launch_kmajor_pack(L, static_cast<hipStream_t>(stream)),
+                    "K-major pack launch");
+}
+
+mxfp4_status_t mxfp4_dequant(const mxfp4_desc_t *desc, const uint8_t *codes,
+                             const uint8_t *scales, void *y, void *stream) {
+  int64_t n;
+  MXFP4_TRY(check_desc(desc, false, &n));
+  MXFP4_TRY(check_ptr(codes, 16, "codes"));
+  MXFP4_TRY(check_ptr(scales, 1, "scales"));
+  MXFP4_TRY(check_ptr(y, 16, "y"));
+  if (!distinct({codes, scales, y})) return fail(MXFP4_EINVAL, "codes, scales and y must not alias");
+  if (n == 0) return ok();
+  mxfp4::DqLaunch L{desc->dtype, desc->block, desc->rows, desc->cols, codes, scales, y};
+  return hip_status(mxfp4::launch_dequant(L, static_cast<hipStream_t>(stream)), "dequant launch");
+}
+
 const char *mxfp4_last_error(void) { return g_last_error.c_str(); }
 
-int32_t mxfp4_version(void) { return 100; }
+int32_t mxfp4_version(void) { return 101; }
 
 }  // extern "C"

@@ -61,34 +61,7 @@ struct ColArgs {
 };
 
 template <int DT>
-struct ColT {
-  static constexpr int NW = DT == kBF16 ? 4 : 8;  // words per 8-element piece
-  static constexpr int ES = DT == kBF16 ? 2 : 4;
-};
-
-template <int DT, bool VEC>
-__device__ __forceinline__ void load_piece(uint32_t *w, const uint8_t *p, int n) {
-  constexpr int NW = ColT<DT>::NW;
-  if (VEC) {
-    if (n == 8) {
-      uint4 v = ld16(p);
-      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-      if (DT == kF32) {
-        uint4 v2 = ld16(p + 16);
-        w[4] = v2.x; w[5] = v2.y; w[6] = v2.z; w[7] = v2.w;
-      }
-      return;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < NW; ++k) w[k] = 0;
-  if (!VEC) {
-    for (int j = 0; j < n; ++j) {
-      if (DT == kBF16) w[j >> 1] |= (uint32_t)reinterpret_cast<const uint16_t *>(p)[j] << (16 * (j & 1));
-      else w[j] = reinterpret_cast<const uint32_t *>(p)[j];
-    }
-  }
-}
+using ColT = PieceT<DT>;
 
 template <int DT, bool VEC>
 __device__ __forceinline__ void store_piece(uint8_t *p, const uint32_t *w, int n) {

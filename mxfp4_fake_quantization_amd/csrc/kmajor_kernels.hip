@@ -1,0 +1,451 @@
+// kmajor_kernels.hip -- packed MXFP4 operands laid out along the reduction
+// dimension, and decoding of packed codes back to values, on gfx950.
+//
+// K-major pack: column-wise (or per-expert grouped) blocks of x [rows, cols]
+// are quantized and stored as the row-wise packed form of x^T: codes_t
+// [cols, k_blocks * block / 2] (two FP4 codes per byte, the lower K position
+// in the low nibble) and scales_t [cols, k_blocks] E8M0 bytes.  This is the
+// column-direction operand (col_data / col_scale) of the hyper-parallel
+// page's grouped W4A8 matmul, stored packed as on the sglang page, so an MX
+// matrix product reads each column's blocks as contiguous 16-byte (block 32)
+// or 64-byte (block 128) pieces along K.  K position t*block + o is x row
+// start_t + o of block-row t while o < len_t, else a padding code 0.
+//
+// Tiling: a workgroup owns 256 K positions x 64 columns.  Lane (cg, rq), with
+// cg = lane & 7 and rq = 8*wave + (lane >> 3), holds K positions 8rq .. 8rq+7
+// (8 consecutive rows of x, one block-row) of columns 8cg .. 8cg+7, loaded as
+// one 16-byte bf16 piece per row, so 8 lanes read a whole 128-byte row
+// segment.  Then
+//   - a 32-row block is 4 lanes at distance 8: column max by DPP row_ror:8
+//     and ds_swizzle xor 16; a 128-row block spans two waves, which exchange
+//     their maxima through LDS;
+//   - the 8 nibbles of one column in one lane form one 32-bit word at byte
+//     4*rq of the column's 128-byte line of codes, so every line of codes_t
+//     is written whole by one workgroup.
+//
+// Decode: codes [rows, ceil(cols/2)] + scales [rows, ceil(cols/block)] ->
+// values [rows, cols] in bf16 or fp32; K-major codes decode with rows = the
+// columns of x and cols = k_blocks * block.
+#include "mxfp4_device.h"
+#include "mxfp4_groups.h"
+#include "mxfp4_kernels.h"
+
+namespace mxfp4 {
+namespace {
+
+constexpr int kKTile = 256;  // K positions per workgroup
+constexpr int kCTile = 64;   // columns per workgroup
+// Minimum workgroups per CU requested from the compiler (caps the VGPRs).
+#ifndef MXFP4_KMAJOR_MINWG
+#define MXFP4_KMAJOR_MINWG 3
+#endif
+// 8-element chunks per lane of the flat decode kernel.
+#ifndef MXFP4_DQ_U
+#define MXFP4_DQ_U 4
+#endif
+
+struct KmArgs {
+  const uint8_t *x;
+  uint8_t *codes;   // [cols, ldk]
+  uint8_t *scales;  // [cols, k_blocks]
+  const int64_t *group_list;
+  int64_t rows, cols, k_blocks, ldk;
+  int64_t nct;  // column tiles
+  int num_groups, list_type;
+  float sf;
+};
+
+// Nibbles of a word of two bf16 columns, with the generic snap for a half
+// whose column max needs it (FLOOR E8M0 byte 0..2).
+__device__ __forceinline__ uint32_t fix_slow_nib(uint32_t w, uint32_t cm, uint32_t e8p, uint32_t n) {
+  const uint32_t lo = cm & 0xFFFFu, hi = cm >> 16;
+  if (lo != 0 && (lo >> 7) < 5) n = (n & 0xFFFF0000u) | half_bf16_slow(w & 0xFFFFu, e8p & 0xFFu).n;
+  if (hi != 0 && (hi >> 7) < 5) n = (n & 0xFFFFu) | (half_bf16_slow(w >> 16, (e8p >> 16) & 0xFFu).n << 16);
+  return n;
+}
+
+// Generic-snap nibbles of 8 fp32 rows of one column (E8M0 byte 0..2).  Out
+// of line: inlined for all 64 elements of a lane it would spill; it runs
+// only after every load of the lane has been consumed.
+__device__ __noinline__ uint32_t slow_column_f32(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                                 uint32_t a4, uint32_t a5, uint32_t a6, uint32_t a7,
+                                                 uint32_t e8) {
+  const uint32_t a[8] = {a0, a1, a2, a3, a4, a5, a6, a7};
+  uint32_t v = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t idx;
+    slow_snap<kF32>(a[i] & 0x7FFFFFFFu, e8, &idx);
+    v |= (idx | (sign_f32(a[i]) >> 28)) << (4 * i);
+  }
+  return v;
+}
+
+// The lane's 8 code words (one per column, K position 8rq + i in bits
+// 4i..4i+3).  SLOW = true only when some lane of the wave holds a column that
+// needs the generic snap.
+template <int DT, int RULE, bool SLOW>
+__device__ __forceinline__ void code_words(const uint32_t (&w)[8][PieceT<DT>::NW], const uint32_t *pt,
+                                           const uint32_t *pe, const uint32_t *cm,
+                                           const BlockParams *cbp, uint32_t (&out)[8]) {
+  if (DT == kBF16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t lo = 0, hi = 0;  // rows 0-3 / 4-7; column 2k in bits 0-15, 2k+1 in 16-31
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t n = n_bf16(w[i][k], pt[k]);
+        if (SLOW && RULE == kFloor) n = fix_slow_nib(w[i][k], cm[k], pe[k], n);
+        if (i < 4) lo |= n << (4 * i);
+        else hi |= n << (4 * (i - 4));
+      }
+      out[2 * k] = (lo & 0xFFFFu) | (hi << 16);
+      out[2 * k + 1] = (lo >> 16) | (hi & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      BlockParams q = cbp[k];
+      q.slow = false;
+      uint32_t v = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v |= n_f32(w[i][k], q) << (4 * i);
+      if (SLOW && cbp[k].slow)
+        v = slow_column_f32(w[0][k], w[1][k], w[2][k], w[3][k], w[4][k], w[5][k], w[6][k], w[7][k],
+                            cbp[k].e8);
+      out[k] = v;
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t colmax_step(uint32_t a, uint32_t b) {
+  return DT == kBF16 ? pk_max(a, b) : max32(a, b);
+}
+
+template <int DT, int B, int RULE, bool GROUPED, bool VEC>
+__global__ __launch_bounds__(kThreads, MXFP4_KMAJOR_MINWG) void kmajor_pack_kernel(KmArgs A) {
+  constexpr int NW = PieceT<DT>::NW;
+  constexpr int ES = PieceT<DT>::ES;
+  constexpr int LB = B == 32 ? 5 : 7;
+  constexpr uint32_t ABS = DT == kBF16 ? 0x7FFF7FFFu : 0x7FFFFFFFu;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int cg = lane & 7;
+  const int rql = lane >> 3;
+  const int rq = 8 * wave + rql;
+  const int64_t kt = blockIdx.x / A.nct;
+  const int64_t ct = blockIdx.x - kt * A.nct;
+  const int64_t kpos = kt * kKTile + 8 * rq;  // first K position of this lane
+  const int64_t bt = kpos >> LB;              // its block-row
+  const int o0 = (int)(kpos & (B - 1));       // offset inside the block
+
+  int64_t start, len;
+  if (GROUPED) {
+    // wave-uniform lookups: a wave covers 64 K positions, i.e. two 32-row
+    // block-rows or half of a 128-row one
+    const int64_t btw = (kt * kKTile + 64 * wave) >> LB;
+    block_row_uniform(A.group_list, A.num_groups, A.list_type, A.rows, LB, btw, &start, &len);
+    if (B == 32) {
+      int64_t s1, l1;
+      block_row_uniform(A.group_list, A.num_groups, A.list_type, A.rows, LB, btw + 1, &s1, &l1);
+      if (rql >= 4) {
+        start = s1;
+        len = l1;
+      }
+    }
+    if (bt >= A.k_blocks) len = 0;
+  } else {
+    start = bt << LB;
+    const int64_t rem = A.rows - start;
+    len = rem <= 0 ? 0 : (rem < B ? rem : B);
+  }
+
+  const int64_t col0 = ct * kCTile;
+  const int64_t c0 = col0 + 8 * cg;
+  const int64_t crem = A.cols - c0;
+  const int ncol = crem >= 8 ? 8 : (crem > 0 ? (int)crem : 0);
+  const int64_t rrem = len - o0;
+  const int nrow = rrem >= 8 ? 8 : (rrem > 0 ? (int)rrem : 0);
+  const int64_t rstride = A.cols * ES;
+  const uint8_t *src = A.x + ((start + o0) * A.cols + c0) * ES;
+
+  // ---- load 8 rows x 8 columns ------------------------------------------
+  // A wave whose rows and columns are all inside the tensor issues its eight
+  // loads unconditionally, so they are all in flight together.
+  uint32_t w[8][NW];
+  const bool full = VEC && col0 + kCTile <= A.cols && __all(nrow == 8);
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) load_piece<DT, true>(w[i], src + i * rstride, 8);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) load_piece<DT, VEC>(w[i], src + i * rstride, i < nrow ? ncol : 0);
+  }
+
+  // ---- column maxima (padding rows read as +0 and never raise them) -------
+  uint32_t cm[NW];
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = colmax_step<DT>(m, w[i][k] & ABS);
+    m = colmax_step<DT>(m, dpp<kDppRowRor8>(m));  // lane ^ 8
+    m = colmax_step<DT>(m, lane_xor16(m));
+    if (B == 128) m = colmax_step<DT>(m, lane_xor32(m));
+    cm[k] = m;
+  }
+  if (B == 128) {
+    __shared__ uint32_t s_cm[4][8][NW];
+    if (rql == 0) {
+#pragma unroll
+      for (int k = 0; k < NW; ++k) s_cm[wave][cg][k] = cm[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NW; ++k) cm[k] = colmax_step<DT>(cm[k], s_cm[wave ^ 1][cg][k]);
+  }
+
+  // ---- per-column parameters ---------------------------------------------
+  uint32_t pt[NW], pe[NW];
+  BlockParams cbp[DT == kF32 ? 8 : 1];
+  bool slow_any = false;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    if (DT == kBF16 && RULE == kFloor) {
+      const PackedParams q = floor_params_pk(cm[k]);
+      pt[k] = q.t2;
+      pe[k] = q.e8;
+      slow_any = slow_any || q.slow;
+    } else if (DT == kBF16) {
+      const BlockParams lo = block_params<DT, RULE>(cm[k] & 0xFFFFu, A.sf);
+      const BlockParams hi = block_params<DT, RULE>(cm[k] >> 16, A.sf);
+      pt[k] = lo.t025 | (hi.t025 << 16);
+      pe[k] = lo.e8 | (hi.e8 << 16);
+    } else {
+      cbp[DT == kF32 ? k : 0] = block_params<DT, RULE>(cm[k], A.sf);
+      pe[k] = cbp[DT == kF32 ? k : 0].e8;
+      slow_any = slow_any || cbp[DT == kF32 ? k : 0].slow;
+    }
+  }
+
+  uint32_t cw[8];
+  if (__builtin_expect(__any(slow_any), 0)) code_words<DT, RULE, true>(w, pt, pe, cm, cbp, cw);
+  else code_words<DT, RULE, false>(w, pt, pe, cm, cbp, cw);
+
+  // ---- stores --------------------------------------------------------------
+  // Every lane of an existing block-row writes its word, padding included.
+  if (len > 0) {
+    uint8_t *dst = A.codes + c0 * A.ldk + (kpos >> 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < ncol) *reinterpret_cast<uint32_t *>(dst + j * A.ldk) = cw[j];
+    if (o0 == 0) {
+      uint8_t *sd = A.scales + c0 * A.k_blocks + bt;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t e8 = DT == kBF16 ? (pe[j >> 1] >> (16 * (j & 1))) & 0xFFu : pe[j];
+        if (j < ncol) sd[j * A.k_blocks] = (uint8_t)e8;
+      }
+    }
+  }
+}
+
+template <int DT, int B, int RULE, bool GROUPED>
+hipError_t km_launch(bool vec, const KmArgs &a, dim3 grid, hipStream_t st) {
+  if (vec)
+    hipLaunchKernelGGL((kmajor_pack_kernel<DT, B, RULE, GROUPED, true>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((kmajor_pack_kernel<DT, B, RULE, GROUPED, false>), grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int DT, int B>
+hipError_t km_rule(int rule, bool grouped, bool vec, const KmArgs &a, dim3 grid, hipStream_t st) {
+  if (rule == kFloor)
+    return grouped ? km_launch<DT, B, kFloor, true>(vec, a, grid, st)
+                   : km_launch<DT, B, kFloor, false>(vec, a, grid, st);
+  return grouped ? km_launch<DT, B, kAmct, true>(vec, a, grid, st)
+                 : km_launch<DT, B, kAmct, false>(vec, a, grid, st);
+}
+
+// ---- decode ------------------------------------------------------------------
+
+struct DqArgs {
+  const uint8_t *codes;
+  const uint8_t *scales;
+  uint8_t *y;
+  int64_t rows, cols;
+  int64_t half;     // code bytes per row, ceil(cols / 2)
+  int64_t nb;       // scale bytes per row, ceil(cols / block)
+  int64_t nchunks;  // flat kernel: rows * cols / 8
+  int64_t nxr;      // row kernel: workgroups per row
+};
+
+// Eight values (four words; element 2d in the low half of word d) of the code
+// word c (element j in bits 4j..4j+3), E8M0 byte e8.  Closed form for
+// 2 <= e8 <= 252, where every code times 2^(e8-127) is a normal bf16: for
+// code index i >= 1 the magnitude bits are (e8-1)*128 + 64*t(i), t = [-, 0, 2,
+// 3, 4, 5, 6, 7] (one byte-table lookup by v_perm), and 0 for i = 0.
+// SLOW: lanes with other bytes recompute with the generic form.
+template <bool SLOW>
+__device__ __forceinline__ void decode8(uint32_t c, uint32_t e8, uint32_t (&y)[4]) {
+  const uint32_t ev = c & 0x0F0F0F0Fu;         // elements 0 2 4 6
+  const uint32_t od = (c >> 4) & 0x0F0F0F0Fu;  // elements 1 3 5 7
+  const uint32_t e2 = splat16(((e8 - 1u) & 0x1FFu) << 7);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    // byte d of ev -> low half, byte d of od -> high half
+    const uint32_t n2 = __builtin_amdgcn_perm(od, ev, (0x0Cu << 24) | ((4u + d) << 16) | (0x0Cu << 8) | d);
+    const uint32_t i2 = n2 & 0x00070007u;
+    const uint32_t q2 = __builtin_amdgcn_perm(0x07060504u, 0x03020000u, i2);
+    const uint32_t ze = pk_mad(pk_min1(i2), e2, 0u);
+    y[d] = pk_mad(q2, 0x00400040u, ze) | ((n2 << 12) & 0x80008000u);
+  }
+  if (SLOW && (e8 - 2u) > 250u) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t b = (c >> (8 * d)) & 0xFFu;
+      y[d] = decode_bf16_generic(b & 15u, e8) | (decode_bf16_generic(b >> 4, e8) << 16);
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_chunk(uint8_t *p, const uint32_t (&y)[4]) {
+  if (DT == kBF16) {
+    st16(p, make_uint4(y[0], y[1], y[2], y[3]));
+  } else {
+    st16(p, make_uint4(y[0] << 16, y[0] & 0xFFFF0000u, y[1] << 16, y[1] & 0xFFFF0000u));
+    st16(p + 16, make_uint4(y[2] << 16, y[2] & 0xFFFF0000u, y[3] << 16, y[3] & 0xFFFF0000u));
+  }
+}
+
+// cols % block == 0: code word ch covers elements 8ch .. 8ch+7 of the flat
+// tensor, whose block is 8ch / block.
+template <int DT, int LB, int U>
+__global__ __launch_bounds__(kThreads) void dequant_flat_kernel(DqArgs A) {
+  constexpr int ES = PieceT<DT>::ES;
+  const int64_t base = (int64_t)blockIdx.x * (U * kThreads) + threadIdx.x;
+  const bool full = (int64_t)(blockIdx.x + 1) * (U * kThreads) <= A.nchunks;  // workgroup-uniform
+  const uint32_t *cw = reinterpret_cast<const uint32_t *>(A.codes);
+  uint32_t c[U], e[U];
+  bool slow = false;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t ch = base + u * kThreads;
+    c[u] = 0;
+    e[u] = 127;
+    if (full || ch < A.nchunks) {
+      c[u] = __builtin_nontemporal_load(cw + ch);
+      e[u] = A.scales[(ch << 3) >> LB];
+    }
+    slow = slow || (e[u] - 2u) > 250u;
+  }
+  const bool any_slow = __any(slow);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t ch = base + u * kThreads;
+    uint32_t y[4];
+    if (__builtin_expect(any_slow, 0)) decode8<true>(c[u], e[u], y);
+    else decode8<false>(c[u], e[u], y);
+    if (full || ch < A.nchunks) store_chunk<DT>(A.y + ch * (8 * ES), y);
+  }
+}
+
+// Any cols: workgroup = one row segment of 256 chunks of 8 elements (a chunk
+// never straddles a block: blocks are multiples of 8 within the row).
+template <int DT, int LB, bool VEC>
+__global__ __launch_bounds__(kThreads) void dequant_rows_kernel(DqArgs A) {
+  constexpr int ES = PieceT<DT>::ES;
+  const int64_t row = blockIdx.x / A.nxr;
+  const int64_t col = ((blockIdx.x - row * A.nxr) * kThreads + threadIdx.x) * 8;
+  if (col >= A.cols) return;
+  const uint8_t *crow = A.codes + row * A.half;
+  const uint32_t e8 = A.scales[row * A.nb + (col >> LB)];
+  uint8_t *yrow = A.y + row * A.cols * ES;
+  if (VEC) {  // cols % 8 == 0: a whole aligned chunk
+    uint32_t y[4];
+    decode8<true>(*reinterpret_cast<const uint32_t *>(crow + (col >> 1)), e8, y);
+    store_chunk<DT>(yrow + col * ES, y);
+  } else {
+    for (int j = 0; j < 8 && col + j < A.cols; ++j) {
+      const uint32_t b = crow[(col + j) >> 1];
+      const uint32_t v = decode_bf16_generic(((col + j) & 1) ? b >> 4 : b & 15u, e8);
+      if (DT == kBF16) reinterpret_cast<uint16_t *>(yrow)[col + j] = (uint16_t)v;
+      else reinterpret_cast<uint32_t *>(yrow)[col + j] = v << 16;
+    }
+  }
+}
+
+template <int DT, int LB>
+hipError_t dq_launch(const DqArgs &a0, hipStream_t st) {
+  DqArgs a = a0;
+  constexpr int U = MXFP4_DQ_U;
+  if (a.cols % (1 << LB) == 0) {
+    a.nchunks = a.rows * a.cols / 8;
+    const int64_t nwg = (a.nchunks + U * kThreads - 1) / (U * kThreads);
+    if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((dequant_flat_kernel<DT, LB, U>), dim3((unsigned)nwg), dim3(kThreads), 0, st, a);
+  } else {
+    a.nxr = (a.cols + 8 * kThreads - 1) / (8 * kThreads);
+    const int64_t nwg = a.rows * a.nxr;
+    if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (a.cols % 8 == 0)
+      hipLaunchKernelGGL((dequant_rows_kernel<DT, LB, true>), dim3((unsigned)nwg), dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((dequant_rows_kernel<DT, LB, false>), dim3((unsigned)nwg), dim3(kThreads), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_kmajor_pack(const KmLaunch &L, hipStream_t st) {
+  KmArgs a;
+  a.x = static_cast<const uint8_t *>(L.x);
+  a.codes = L.codes;
+  a.scales = L.scales;
+  a.group_list = L.group_list;
+  a.rows = L.rows;
+  a.cols = L.cols;
+  a.k_blocks = L.k_blocks;
+  a.ldk = L.k_blocks * L.block / 2;
+  a.nct = (L.cols + kCTile - 1) / kCTile;
+  a.num_groups = L.num_groups;
+  a.list_type = L.list_type;
+  a.sf = L.sf;
+  const bool grouped = L.group_list != nullptr;
+  // block-rows the grid covers: all that can exist
+  const int64_t nbt = grouped ? L.k_blocks : (L.rows + L.block - 1) / L.block;
+  const int64_t nkt = (nbt * L.block + kKTile - 1) / kKTile;
+  const int64_t nwg = nkt * a.nct;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (nwg == 0) return hipSuccess;
+  const bool vec = L.cols % 8 == 0;
+  dim3 grid((unsigned)nwg);
+  if (L.dtype == kBF16)
+    return L.block == 32 ? km_rule<kBF16, 32>(L.rule, grouped, vec, a, grid, st)
+                         : km_rule<kBF16, 128>(L.rule, grouped, vec, a, grid, st);
+  return L.block == 32 ? km_rule<kF32, 32>(L.rule, grouped, vec, a, grid, st)
+                       : km_rule<kF32, 128>(L.rule, grouped, vec, a, grid, st);
+}
+
+hipError_t launch_dequant(const DqLaunch &L, hipStream_t st) {
+  DqArgs a;
+  a.codes = L.codes;
+  a.scales = L.scales;
+  a.y = static_cast<uint8_t *>(L.y);
+  a.rows = L.rows;
+  a.cols = L.cols;
+  a.half = (L.cols + 1) / 2;
+  a.nb = (L.cols + L.block - 1) / L.block;
+  a.nchunks = 0;
+  a.nxr = 0;
+  if (L.dtype == kBF16) return L.block == 32 ? dq_launch<kBF16, 5>(a, st) : dq_launch<kBF16, 7>(a, st);
+  return L.block == 32 ? dq_launch<kF32, 5>(a, st) : dq_launch<kF32, 7>(a, st);
+}
+
+}  // namespace mxfp4

@@ -51,4 +51,29 @@ struct SteLaunch {
 };
 hipError_t launch_ste_bwd(const SteLaunch &L, hipStream_t stream);
 
+
+// K-major packed form of column-wise / grouped blocks.
+struct KmLaunch {
+  int dtype, block, rule;
+  int64_t rows, cols;
+  float sf;
+  const void *x;
+  const int64_t *group_list;  // NULL: dense column-wise blocks
+  int num_groups, list_type;
+  int64_t k_blocks;
+  uint8_t *codes;   // [cols, k_blocks * block / 2]
+  uint8_t *scales;  // [cols, k_blocks]
+};
+hipError_t launch_kmajor_pack(const KmLaunch &L, hipStream_t stream);
+
+// Decode of row-wise packed codes.
+struct DqLaunch {
+  int dtype, block;
+  int64_t rows, cols;
+  const uint8_t *codes;
+  const uint8_t *scales;
+  void *y;
+};
+hipError_t launch_dequant(const DqLaunch &L, hipStream_t stream);
+
 }  // namespace mxfp4

@@ -259,4 +259,26 @@ MXFP4_HD uint32_t slow_six(uint32_t e8) {
   return lin_to_bits<DT>(24u << (e8 + MB - 3));
 }
 
+
+// ---- decoding a packed nibble --------------------------------------------
+// value = (-1)^s * code * 2^(e8 - 127).  For code index i >= 1 the code is
+// 2^((i>>1) - 1) * (1 + m/2) with m = (i >= 2) & i, so the biased result
+// exponent is Eb = e8 + (i>>1) - 1: normal for 1 <= Eb <= 254, +-inf above
+// (the product exceeds the largest finite value), and for Eb in {-1, 0} the
+// subnormal (2 + m) * 2^(Eb - 128).  For 2 <= e8 <= 252 every code is normal
+// (the closed form the kernels use); this generic form covers every byte.
+// Returns bf16 bits (fp32 bits are these << 16: same exponent range, and
+// every decoded value has at most two significant bits).
+MXFP4_HD uint32_t decode_bf16_generic(uint32_t nib, uint32_t e8) {
+  const uint32_t i = nib & 7u, sg = (nib & 8u) << 12;
+  if (i == 0) return sg;
+  const int eb = (int)e8 + (int)(i >> 1) - 1;
+  const uint32_t m = i >= 2 ? (i & 1u) : 0u;
+  uint32_t mag;
+  if (eb >= 255) mag = 0x7F80u;
+  else if (eb >= 1) mag = ((uint32_t)eb << 7) | (m << 6);
+  else mag = (2u + m) << (5 + eb);  // bf16 subnormal unit 2^-133
+  return mag | sg;
+}
+
 }  // namespace mxfp4

@@ -100,3 +100,14 @@ extern "C" int host_check_packed_params(void) {
     }
   return bad;
 }
+
+// Generic decode of every (nibble, E8M0 byte) pair: out[e8 * 16 + nib] holds
+// bf16 bits, out32 the fp32 bits the kernels derive from them (<< 16).
+extern "C" void host_decode_all(uint16_t *out, uint32_t *out32) {
+  for (uint32_t e8 = 0; e8 < 256; ++e8)
+    for (uint32_t n = 0; n < 16; ++n) {
+      uint32_t v = decode_bf16_generic(n, e8);
+      out[e8 * 16 + n] = (uint16_t)v;
+      out32[e8 * 16 + n] = v << 16;
+    }
+}

@@ -35,6 +35,8 @@ def lib():
     L.mxfp4_ste_bwd.argtypes = [dp, i32, vp, vp, vp, vp, i32, i32, vp]
     L.mxfp4_quant_pack.argtypes = [dp, vp, vp, vp, vp, vp, vp]
     L.mxfp4_grouped_qdq.argtypes = [dp, vp, vp, i32, i32, vp, vp, vp, vp]
+    L.mxfp4_quant_pack_kmajor.argtypes = [dp, vp, vp, i32, i32, ctypes.c_int64, vp, vp, vp]
+    L.mxfp4_dequant.argtypes = [dp, vp, vp, vp, vp]
     L.mxfp4_last_error.restype = ctypes.c_char_p
     return L
 
@@ -44,17 +46,17 @@ def declared_functions():
     return sorted(set(re.findall(r"^\S[^\n(]*?\b(mxfp4_\w+)\s*\(", text, re.M)))
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
-              "mxfp4_last_error", "mxfp4_version"):
+              "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp4_last_error", "mxfp4_version"):
         assert n in names
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mxfp4_version() == 100
+    assert lib.mxfp4_version() == 101
 
 
 def d(dtype=BF16, block=32, rule=0, rows=64, cols=64, sf=6.0, r0=0, r1=0):
@@ -135,6 +137,38 @@ def test_pack_and_grouped_validation(lib):
     assert gq(P(), P(FAKE + 1024), 8, 1, P(FAKE + 1024), None, None, None) == EINVAL  # y aliases list
     D.rows = 0
     assert gq(P(), P(FAKE + 1024), 8, 1, P(FAKE), None, None, None) == OK
+
+
+def test_kmajor_and_dequant_validation(lib):
+    D = d(rows=70, cols=64)
+    km = lambda *a: lib.mxfp4_quant_pack_kmajor(ctypes.byref(D), *a)
+    x, c, s, gl = P(), P(FAKE + 4096), P(FAKE + 8192), P(FAKE + 12288)
+    assert km(x, None, 0, 1, 2, c, s, None) == EINVAL                  # 70 rows need 3 blocks
+    assert b"k_blocks" in lib.mxfp4_last_error()
+    assert km(x, gl, 4, 1, 5, c, s, None) == EINVAL                    # grouped: 3 + 4 - 1
+    assert km(x, gl, 0, 1, 9, c, s, None) == EINVAL                    # num_groups < 1
+    assert km(x, gl, 4, 3, 9, c, s, None) == EINVAL                    # list type
+    assert km(x, P(FAKE + 12292), 4, 1, 9, c, s, None) == EINVAL       # list misaligned
+    assert km(x, None, 0, 1, 3, P(FAKE + 4100), s, None) == EINVAL     # codes misaligned
+    assert km(x, None, 0, 1, 3, None, s, None) == EINVAL
+    assert km(x, None, 0, 1, 3, c, None, None) == EINVAL
+    assert km(x, None, 0, 1, 3, c, c, None) == EINVAL                  # alias
+    assert km(x, None, 0, 1, 1 << 60, c, s, None) == EINVAL            # size overflow
+    D.block = 64
+    assert km(x, None, 0, 1, 3, c, s, None) == EUNSUP
+    D.block, D.rows = 32, 0
+    assert km(x, gl, 4, 1, 0, c, s, None) == OK                        # nothing to do
+    dq = lambda *a: lib.mxfp4_dequant(ctypes.byref(D), *a)
+    D.rows = 4
+    assert dq(None, s, x, None) == EINVAL
+    assert dq(c, None, x, None) == EINVAL
+    assert dq(c, s, None, None) == EINVAL
+    assert dq(c, s, P(FAKE + 8), None) == EINVAL                       # y misaligned
+    assert dq(c, c, x, None) == EINVAL                                 # alias
+    D.dtype = 5
+    assert dq(c, s, x, None) == EUNSUP
+    D.dtype, D.rows = BF16, 0
+    assert dq(c, s, x, None) == OK
 
 
 def test_python_binding_refuses_cpu_tensors():

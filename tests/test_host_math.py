@@ -141,3 +141,18 @@ def test_fp32_exhaustive_mantissa_sweep(host, oracle):
 def test_packed_column_params_match_scalar_rule(host):
     host.host_check_packed_params.restype = ctypes.c_int
     assert host.host_check_packed_params() == 0
+
+
+def test_generic_decode_every_nibble_and_byte(host, oracle):
+    """The kernels' generic decode (every E8M0 byte, every nibble) equals the
+    oracle's unpack in bf16 and fp32."""
+    out = np.empty(256 * 16, np.uint16)
+    out32 = np.empty(256 * 16, np.uint32)
+    host.host_decode_all(out.ctypes.data_as(ctypes.c_void_p), out32.ctypes.data_as(ctypes.c_void_p))
+    nib = np.arange(16, dtype=np.uint8)
+    codes = np.repeat((nib[0::2] | (nib[1::2] << 4))[None, :], 256, axis=0)   # 8 bytes = 16 nibbles
+    scales = np.arange(256, dtype=np.uint8)[:, None]
+    want16 = oracle.unpack_rows(codes, scales, 16, 32, np.uint16)
+    want32 = oracle.unpack_rows(codes, scales, 16, 32, np.float32).view(np.uint32)
+    assert np.array_equal(out.reshape(256, 16), want16)
+    assert np.array_equal(out32.reshape(256, 16), want32)
