@@ -41,7 +41,7 @@ constexpr int kCTile = 64;   // columns per workgroup
 #endif
 // 8-element chunks per lane of the flat decode kernel.
 #ifndef MXFP4_DQ_U
-#define MXFP4_DQ_U 4
+#define MXFP4_DQ_U 2
 #endif
 
 struct KmArgs {
@@ -50,7 +50,8 @@ struct KmArgs {
   uint8_t *scales;  // [cols, k_blocks]
   const int64_t *group_list;
   int64_t rows, cols, k_blocks, ldk;
-  int64_t nct;  // column tiles
+  int64_t nct;     // column tiles
+  int64_t ntiles;  // K tiles x column tiles
   int num_groups, list_type;
   float sf;
 };
@@ -91,16 +92,24 @@ __device__ __forceinline__ void code_words(const uint32_t (&w)[8][PieceT<DT>::NW
   if (DT == kBF16) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      uint32_t lo = 0, hi = 0;  // rows 0-3 / 4-7; column 2k in bits 0-15, 2k+1 in 16-31
+      const uint32_t t31 = pt[k] - 0x001F001Fu;
+      uint32_t acc[2];  // rows 0-3 / 4-7; column 2k in bits 0-15, 2k+1 in 16-31
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t n = n_bf16(w[i][k], pt[k]);
-        if (SLOW && RULE == kFloor) n = fix_slow_nib(w[i][k], cm[k], pe[k], n);
-        if (i < 4) lo |= n << (4 * i);
-        else hi |= n << (4 * (i - 4));
+      for (int g = 0; g < 2; ++g) {
+        // nibble of row 4g + r at bits 12-15 / 28-31, shifted into place below
+        uint32_t t[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t x = w[4 * g + r][k];
+          if (SLOW && RULE == kFloor)
+            t[r] = fix_slow_nib(x, cm[k], pe[k], n_bf16(x, pt[k])) << 12;
+          else
+            t[r] = (snap_idx_bf16_tab(x & 0x7FFF7FFFu, t31) << 12) | sign_bf16(x);
+        }
+        acc[g] = (t[0] >> 12) | (t[1] >> 8) | (t[2] >> 4) | t[3];
       }
-      out[2 * k] = (lo & 0xFFFFu) | (hi << 16);
-      out[2 * k + 1] = (lo >> 16) | (hi & 0xFFFF0000u);
+      out[2 * k] = perm_b32(acc[1], acc[0], 0x05040100u);      // low halves
+      out[2 * k + 1] = perm_b32(acc[1], acc[0], 0x07060302u);  // high halves
     }
   } else {
 #pragma unroll
@@ -123,66 +132,101 @@ __device__ __forceinline__ uint32_t colmax_step(uint32_t a, uint32_t b) {
   return DT == kBF16 ? pk_max(a, b) : max32(a, b);
 }
 
+// Where one lane's piece of a tile lives.
+struct KmTile {
+  const uint8_t *src;  // first of its 8 rows at its first column
+  int64_t kt, col0;    // tile: K tile and first column
+  int64_t kpos;        // first K position of the lane
+  int64_t bt;          // its block-row
+  int64_t c0;          // its first column
+  int o0;              // offset of kpos inside the block
+  int nrow, ncol;      // rows / columns of the 8 x 8 piece inside the tensor
+  bool live;           // the block-row exists (every lane of it writes)
+  bool full;           // wave-uniform: all rows and the whole column tile inside
+};
+
+template <int DT, int B, bool GROUPED, bool VEC>
+__device__ __forceinline__ KmTile km_tile(const KmArgs &A, int64_t tile, int wave, int rql, int cg) {
+  constexpr int ES = PieceT<DT>::ES;
+  constexpr int LB = B == 32 ? 5 : 7;
+  KmTile T;
+  T.kt = tile / A.nct;
+  T.col0 = (tile - T.kt * A.nct) * kCTile;
+  T.kpos = T.kt * kKTile + 8 * (8 * wave + rql);
+  T.bt = T.kpos >> LB;
+  T.o0 = (int)(T.kpos & (B - 1));
+  int64_t start, len;
+  if (GROUPED) {
+    // wave-uniform lookups: a wave covers 64 K positions, i.e. two 32-row
+    // block-rows or half of a 128-row one
+    const int64_t btw = (T.kt * kKTile + 64 * wave) >> LB;
+    if (B == 32) {
+      const int64_t tt[2] = {btw, btw + 1};
+      int64_t ss[2], ll[2];
+      block_rows_lookup<2>(A.group_list, A.num_groups, A.list_type, A.rows, LB, tt, ss, ll);
+      start = rql >= 4 ? ss[1] : ss[0];
+      len = rql >= 4 ? ll[1] : ll[0];
+    } else {
+      block_row_uniform(A.group_list, A.num_groups, A.list_type, A.rows, LB, btw, &start, &len);
+    }
+    if (T.bt >= A.k_blocks) len = 0;
+  } else {
+    start = T.bt << LB;
+    const int64_t rem = A.rows - start;
+    len = rem <= 0 ? 0 : (rem < B ? rem : B);
+  }
+  T.c0 = T.col0 + 8 * cg;
+  const int64_t crem = A.cols - T.c0;
+  T.ncol = crem >= 8 ? 8 : (crem > 0 ? (int)crem : 0);
+  const int64_t rrem = len - T.o0;
+  T.nrow = rrem >= 8 ? 8 : (rrem > 0 ? (int)rrem : 0);
+  T.live = len > 0;
+  T.src = A.x + ((start + T.o0) * A.cols + T.c0) * ES;
+  T.full = VEC && T.col0 + kCTile <= A.cols && __all(T.nrow == 8);
+  return T;
+}
+
+// LDS staging of one tile's outputs.  Code words sit [column][K word] with a
+// row stride of 33 words, so the 64 lanes of a staging write fall in distinct
+// banks; scale bytes [column][block-row of the tile]; a live flag per
+// block-row of the tile.
+struct KmStage {
+  uint32_t codes[kCTile][kKTile / 8 + 1];
+  uint8_t scales[kCTile][kKTile / 32];
+  uint8_t live[kKTile / 32];
+};
+
+// One workgroup per tile: load, column maxima, nibbles, then the tile's
+// outputs go through LDS so that 8 lanes store each column's 128-byte line of
+// codes with 16-byte stores and one lane its scale bytes (8 for block 32) in
+// one store, instead of 4-byte and 1-byte pieces scattered by row lanes.
 template <int DT, int B, int RULE, bool GROUPED, bool VEC>
 __global__ __launch_bounds__(kThreads, MXFP4_KMAJOR_MINWG) void kmajor_pack_kernel(KmArgs A) {
   constexpr int NW = PieceT<DT>::NW;
   constexpr int ES = PieceT<DT>::ES;
-  constexpr int LB = B == 32 ? 5 : 7;
   constexpr uint32_t ABS = DT == kBF16 ? 0x7FFF7FFFu : 0x7FFFFFFFu;
+  constexpr int NBT_TILE = kKTile / B;  // block-rows per tile
+  __shared__ uint32_t s_cm[4][8][NW];
+  __shared__ KmStage st;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int cg = lane & 7;
   const int rql = lane >> 3;
-  const int rq = 8 * wave + rql;
-  const int64_t kt = blockIdx.x / A.nct;
-  const int64_t ct = blockIdx.x - kt * A.nct;
-  const int64_t kpos = kt * kKTile + 8 * rq;  // first K position of this lane
-  const int64_t bt = kpos >> LB;              // its block-row
-  const int o0 = (int)(kpos & (B - 1));       // offset inside the block
+  const KmTile T = km_tile<DT, B, GROUPED, VEC>(A, blockIdx.x, wave, rql, cg);
 
-  int64_t start, len;
-  if (GROUPED) {
-    // wave-uniform lookups: a wave covers 64 K positions, i.e. two 32-row
-    // block-rows or half of a 128-row one
-    const int64_t btw = (kt * kKTile + 64 * wave) >> LB;
-    block_row_uniform(A.group_list, A.num_groups, A.list_type, A.rows, LB, btw, &start, &len);
-    if (B == 32) {
-      int64_t s1, l1;
-      block_row_uniform(A.group_list, A.num_groups, A.list_type, A.rows, LB, btw + 1, &s1, &l1);
-      if (rql >= 4) {
-        start = s1;
-        len = l1;
-      }
-    }
-    if (bt >= A.k_blocks) len = 0;
-  } else {
-    start = bt << LB;
-    const int64_t rem = A.rows - start;
-    len = rem <= 0 ? 0 : (rem < B ? rem : B);
-  }
-
-  const int64_t col0 = ct * kCTile;
-  const int64_t c0 = col0 + 8 * cg;
-  const int64_t crem = A.cols - c0;
-  const int ncol = crem >= 8 ? 8 : (crem > 0 ? (int)crem : 0);
-  const int64_t rrem = len - o0;
-  const int nrow = rrem >= 8 ? 8 : (rrem > 0 ? (int)rrem : 0);
+  // ---- load 8 rows x 8 columns --------------------------------------------
+  // A wave whose piece is all inside the tensor issues its eight loads
+  // unconditionally, so they are all in flight together.
   const int64_t rstride = A.cols * ES;
-  const uint8_t *src = A.x + ((start + o0) * A.cols + c0) * ES;
-
-  // ---- load 8 rows x 8 columns ------------------------------------------
-  // A wave whose rows and columns are all inside the tensor issues its eight
-  // loads unconditionally, so they are all in flight together.
   uint32_t w[8][NW];
-  const bool full = VEC && col0 + kCTile <= A.cols && __all(nrow == 8);
-  if (full) {
+  if (T.full) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) load_piece<DT, true>(w[i], src + i * rstride, 8);
+    for (int i = 0; i < 8; ++i) load_piece<DT, true>(w[i], T.src + i * rstride, 8);
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) load_piece<DT, VEC>(w[i], src + i * rstride, i < nrow ? ncol : 0);
+    for (int i = 0; i < 8; ++i) load_piece<DT, VEC>(w[i], T.src + i * rstride, i < T.nrow ? T.ncol : 0);
   }
 
   // ---- column maxima (padding rows read as +0 and never raise them) -------
@@ -198,7 +242,6 @@ __global__ __launch_bounds__(kThreads, MXFP4_KMAJOR_MINWG) void kmajor_pack_kern
     cm[k] = m;
   }
   if (B == 128) {
-    __shared__ uint32_t s_cm[4][8][NW];
     if (rql == 0) {
 #pragma unroll
       for (int k = 0; k < NW; ++k) s_cm[wave][cg][k] = cm[k];
@@ -235,26 +278,55 @@ __global__ __launch_bounds__(kThreads, MXFP4_KMAJOR_MINWG) void kmajor_pack_kern
   if (__builtin_expect(__any(slow_any), 0)) code_words<DT, RULE, true>(w, pt, pe, cm, cbp, cw);
   else code_words<DT, RULE, false>(w, pt, pe, cm, cbp, cw);
 
-  // ---- stores --------------------------------------------------------------
-  // Every lane of an existing block-row writes its word, padding included.
-  if (len > 0) {
-    uint8_t *dst = A.codes + c0 * A.ldk + (kpos >> 1);
+  // ---- stage in LDS ----------------------------------------------------------
+  const int kw = 8 * wave + rql;  // K word of the lane inside the tile
+  const int bl = (8 * kw) / B;    // block-row of the lane inside the tile
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.codes[8 * cg + j][kw] = cw[j];
+  if (T.o0 == 0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (j < ncol) *reinterpret_cast<uint32_t *>(dst + j * A.ldk) = cw[j];
-    if (o0 == 0) {
-      uint8_t *sd = A.scales + c0 * A.k_blocks + bt;
+      st.scales[8 * cg + j][bl] = (uint8_t)(DT == kBF16 ? (pe[j >> 1] >> (16 * (j & 1))) : pe[j]);
+    if (cg == 0) st.live[bl] = T.live;
+  }
+  __syncthreads();
+
+  // ---- stores ------------------------------------------------------------------
+  // 8 consecutive lanes write one column's 128 bytes of codes (a 16-byte chunk
+  // is 32 K positions, inside one block-row); a block-row past the blocking's
+  // end is not written.
+  const int64_t kbyte = T.kt * (kKTile / 2);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t e8 = DT == kBF16 ? (pe[j >> 1] >> (16 * (j & 1))) & 0xFFu : pe[j];
-        if (j < ncol) sd[j * A.k_blocks] = (uint8_t)e8;
-      }
+  for (int r = 0; r < (kCTile * kKTile / 32) / kThreads; ++r) {
+    const int chunk = tid + r * kThreads;
+    const int c = chunk >> 3, q = chunk & 7;
+    const int64_t col = T.col0 + c;
+    if (col < A.cols && st.live[(32 * q) / B]) {
+      const uint32_t *s = &st.codes[c][4 * q];
+      st16(A.codes + col * A.ldk + kbyte + 16 * q, make_uint4(s[0], s[1], s[2], s[3]));
+    }
+  }
+  if (tid < kCTile && T.col0 + tid < A.cols) {
+    uint8_t *sd = A.scales + (T.col0 + tid) * A.k_blocks + T.kt * NBT_TILE;
+    bool all_live = true;
+#pragma unroll
+    for (int b = 0; b < NBT_TILE; ++b) all_live = all_live && st.live[b];
+    if (NBT_TILE == 8 && all_live && ((uintptr_t)sd & 7) == 0) {
+      uint64_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) v |= (uint64_t)st.scales[tid][b] << (8 * b);
+      *reinterpret_cast<uint64_t *>(sd) = v;
+    } else {
+#pragma unroll
+      for (int b = 0; b < NBT_TILE; ++b)
+        if (st.live[b]) sd[b] = st.scales[tid][b];
     }
   }
 }
 
 template <int DT, int B, int RULE, bool GROUPED>
-hipError_t km_launch(bool vec, const KmArgs &a, dim3 grid, hipStream_t st) {
+hipError_t km_launch(bool vec, const KmArgs &a, hipStream_t st) {
+  const dim3 grid((unsigned)a.ntiles);
   if (vec)
     hipLaunchKernelGGL((kmajor_pack_kernel<DT, B, RULE, GROUPED, true>), grid, dim3(kThreads), 0, st, a);
   else
@@ -263,12 +335,10 @@ hipError_t km_launch(bool vec, const KmArgs &a, dim3 grid, hipStream_t st) {
 }
 
 template <int DT, int B>
-hipError_t km_rule(int rule, bool grouped, bool vec, const KmArgs &a, dim3 grid, hipStream_t st) {
+hipError_t km_rule(int rule, bool grouped, bool vec, const KmArgs &a, hipStream_t st) {
   if (rule == kFloor)
-    return grouped ? km_launch<DT, B, kFloor, true>(vec, a, grid, st)
-                   : km_launch<DT, B, kFloor, false>(vec, a, grid, st);
-  return grouped ? km_launch<DT, B, kAmct, true>(vec, a, grid, st)
-                 : km_launch<DT, B, kAmct, false>(vec, a, grid, st);
+    return grouped ? km_launch<DT, B, kFloor, true>(vec, a, st) : km_launch<DT, B, kFloor, false>(vec, a, st);
+  return grouped ? km_launch<DT, B, kAmct, true>(vec, a, st) : km_launch<DT, B, kAmct, false>(vec, a, st);
 }
 
 // ---- decode ------------------------------------------------------------------
@@ -421,16 +491,15 @@ hipError_t launch_kmajor_pack(const KmLaunch &L, hipStream_t st) {
   // block-rows the grid covers: all that can exist
   const int64_t nbt = grouped ? L.k_blocks : (L.rows + L.block - 1) / L.block;
   const int64_t nkt = (nbt * L.block + kKTile - 1) / kKTile;
-  const int64_t nwg = nkt * a.nct;
-  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (nwg == 0) return hipSuccess;
+  a.ntiles = nkt * a.nct;
+  if (a.ntiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (a.ntiles == 0) return hipSuccess;
   const bool vec = L.cols % 8 == 0;
-  dim3 grid((unsigned)nwg);
   if (L.dtype == kBF16)
-    return L.block == 32 ? km_rule<kBF16, 32>(L.rule, grouped, vec, a, grid, st)
-                         : km_rule<kBF16, 128>(L.rule, grouped, vec, a, grid, st);
-  return L.block == 32 ? km_rule<kF32, 32>(L.rule, grouped, vec, a, grid, st)
-                       : km_rule<kF32, 128>(L.rule, grouped, vec, a, grid, st);
+    return L.block == 32 ? km_rule<kBF16, 32>(L.rule, grouped, vec, a, st)
+                         : km_rule<kBF16, 128>(L.rule, grouped, vec, a, st);
+  return L.block == 32 ? km_rule<kF32, 32>(L.rule, grouped, vec, a, st)
+                       : km_rule<kF32, 128>(L.rule, grouped, vec, a, st);
 }
 
 hipError_t launch_dequant(const DqLaunch &L, hipStream_t st) {

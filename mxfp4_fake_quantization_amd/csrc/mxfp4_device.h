@@ -290,9 +290,9 @@ template <int DT, bool SLOW>
 __device__ __forceinline__ uint32_t chunk_codes(const uint32_t *w, const BlockParams &bp) {
   if (DT == kBF16) {
     uint32_t n[4];
-    const uint32_t t2 = splat16(bp.t025);
+    const uint32_t t31 = splat16(bp.t025 - 31u);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) n[k] = n_bf16(w[k], t2);
+    for (int k = 0; k < 4; ++k) n[k] = snap_idx_bf16_tab(w[k] & 0x7FFF7FFFu, t31) | (sign_bf16(w[k]) >> 12);
     if (SLOW && bp.slow) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {

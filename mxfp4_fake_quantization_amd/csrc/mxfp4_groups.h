@@ -5,10 +5,17 @@
 // normalize_group_list turns counts into cumulative sums).  Column blocks
 // restart at every group start, so block-row t (numbered group by group,
 // ceil(c_g / block) per group) covers rows [start, start + len) with
-// len <= block.  Every wave decodes the list itself: one vector load brings
-// 64 entries into the lanes, then a wave-uniform loop walks them in scalar
-// registers (v_readlane), so no LDS, no barrier and no host synchronisation
-// are involved.
+// len <= block.
+//
+// Every wave decodes the list itself, without LDS, barriers or host
+// synchronisation.  Short lists are walked in scalar registers.  Long ones are
+// scanned 64 groups per step: one vector load puts group g in lane g, 64-bit
+// prefix scans over the wave give each group's end row and its cumulative
+// block-row count, and a ballot of "cumulative count <= t" counts the groups
+// that end before block-row t, i.e. names the group holding it, at a cost
+// that does not grow with t's position.  Group ends are clamped into
+// [previous end, rows] (negative counts count as 0), so any list gives
+// in-range block-rows.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,20 +29,57 @@ __device__ __forceinline__ int64_t lane_i64(int64_t v, int lane) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Wave-uniform result: *start and *len of block-row t (len 0 past the end).
-// Group ends are clamped into [previous end, rows].
-__device__ __forceinline__ void block_row_uniform(const int64_t *gl, int num_groups, int list_type,
-                                                  int64_t rows, int block_log2, int64_t t,
-                                                  int64_t *start, int64_t *len) {
+__device__ __forceinline__ int64_t shfl_up_i64(int64_t v, int d) {
+  const int lo = __shfl_up((int)(uint32_t)v, d);
+  const int hi = __shfl_up((int)(uint32_t)((uint64_t)v >> 32), d);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Inclusive prefix sum / max over the 64 lanes of the wave.
+__device__ __forceinline__ int64_t scan_add_i64(int64_t v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t u = shfl_up_i64(v, d);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+__device__ __forceinline__ int64_t scan_max_i64(int64_t v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t u = shfl_up_i64(v, d);
+    if (lane >= d) v = u > v ? u : v;
+  }
+  return v;
+}
+
+// Up to this many groups the list is walked in scalar registers (latency
+// grows with the group count but starts low); longer lists use the scan.
+#ifndef MXFP4_GROUP_WALK_MAX
+#define MXFP4_GROUP_WALK_MAX 32
+#endif
+
+// Scalar walk: one vector load brings 64 entries into the lanes, then a
+// wave-uniform loop reads them back (v_readlane) and resolves every requested
+// block-row in one pass.
+template <int NT>
+__device__ __forceinline__ void block_rows_walk(const int64_t *gl, int num_groups, int list_type,
+                                                int64_t rows, int block_log2, const int64_t (&t)[NT],
+                                                int64_t (&start)[NT], int64_t (&len)[NT]) {
   const int lane = (int)__lane_id();
+  const int64_t B = (int64_t)1 << block_log2;
   int64_t prev_end = 0, cum = 0, brow = 0;
-  *start = 0;
-  *len = 0;
-  for (int base = 0; base < num_groups; base += 64) {
+  int left = NT;
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    start[i] = 0;
+    len[i] = 0;
+  }
+  for (int base = 0; base < num_groups && left > 0; base += 64) {
     const int g = base + lane;
     const int64_t mine = g < num_groups ? gl[g] : 0;
     const int n = num_groups - base < 64 ? num_groups - base : 64;
-    for (int j = 0; j < n; ++j) {
+    for (int j = 0; j < n && left > 0; ++j) {
       const int64_t raw = lane_i64(mine, j);
       int64_t end;
       if (list_type == 1) {
@@ -46,17 +90,88 @@ __device__ __forceinline__ void block_row_uniform(const int64_t *gl, int num_gro
       }
       end = end > prev_end ? end : prev_end;
       end = end < rows ? end : rows;
-      const int64_t nb = (end - prev_end + ((int64_t)1 << block_log2) - 1) >> block_log2;
-      if (t < brow + nb) {
-        *start = prev_end + ((t - brow) << block_log2);
-        const int64_t rem = end - *start;
-        *len = rem < ((int64_t)1 << block_log2) ? rem : ((int64_t)1 << block_log2);
-        return;
+      const int64_t nb = (end - prev_end + B - 1) >> block_log2;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        if (len[i] == 0 && t[i] >= brow && t[i] < brow + nb) {  // wave-uniform
+          start[i] = prev_end + ((t[i] - brow) << block_log2);
+          const int64_t rem = end - start[i];
+          len[i] = rem < B ? rem : B;
+          --left;
+        }
       }
       brow += nb;
       prev_end = end;
     }
   }
+}
+
+// Wave-uniform lookup of NT block-rows t[0..NT-1] (wave-uniform values):
+// start[i], len[i] (len 0 past the last block-row).
+template <int NT>
+__device__ __forceinline__ void block_rows_lookup(const int64_t *gl, int num_groups, int list_type,
+                                                  int64_t rows, int block_log2, const int64_t (&t)[NT],
+                                                  int64_t (&start)[NT], int64_t (&len)[NT]) {
+  if (num_groups <= MXFP4_GROUP_WALK_MAX) {
+    block_rows_walk<NT>(gl, num_groups, list_type, rows, block_log2, t, start, len);
+    return;
+  }
+  const int lane = (int)__lane_id();
+  const int64_t B = (int64_t)1 << block_log2;
+  int64_t carry_end = 0, carry_blk = 0;
+  bool done[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    start[i] = 0;
+    len[i] = 0;
+    done[i] = false;
+  }
+  for (int base = 0; base < num_groups; base += 64) {
+    const int g = base + lane;
+    const bool valid = g < num_groups;
+    const int64_t raw = valid ? gl[g] : 0;
+    // end row of group g, clamped into [previous end, rows]
+    int64_t end;
+    if (list_type == 1) {
+      end = carry_end + scan_add_i64(valid && raw > 0 ? raw : 0, lane);
+    } else {
+      end = scan_max_i64(valid ? raw : 0, lane);
+      end = end > carry_end ? end : carry_end;
+    }
+    end = end < rows ? end : rows;
+    int64_t prev = shfl_up_i64(end, 1);
+    if (lane == 0) prev = carry_end;
+    const int64_t nb = valid ? (end - prev + B - 1) >> block_log2 : 0;
+    const int64_t cum = carry_blk + scan_add_i64(nb, lane);  // block-rows through group g
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      if (done[i]) continue;  // wave-uniform
+      const uint64_t before = __ballot(valid && cum <= t[i]);
+      const int gi = (int)__popcll(before);  // first group whose blocks reach past t
+      if (gi < 64 && base + gi < num_groups) {
+        const int64_t gprev = lane_i64(prev, gi);
+        const int64_t gend = lane_i64(end, gi);
+        const int64_t gfirst = lane_i64(cum - nb, gi);
+        start[i] = gprev + ((t[i] - gfirst) << block_log2);
+        const int64_t rem = gend - start[i];
+        len[i] = rem < B ? rem : B;
+        done[i] = true;
+      }
+    }
+    carry_end = lane_i64(end, 63);
+    carry_blk = lane_i64(cum, 63);
+  }
+}
+
+// One block-row.
+__device__ __forceinline__ void block_row_uniform(const int64_t *gl, int num_groups, int list_type,
+                                                  int64_t rows, int block_log2, int64_t t,
+                                                  int64_t *start, int64_t *len) {
+  const int64_t tt[1] = {t};
+  int64_t s[1], l[1];
+  block_rows_lookup<1>(gl, num_groups, list_type, rows, block_log2, tt, s, l);
+  *start = s[0];
+  *len = l[0];
 }
 
 }  // namespace mxfp4

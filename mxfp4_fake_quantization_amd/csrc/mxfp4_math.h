@@ -193,6 +193,39 @@ MXFP4_HD uint32_t snap_idx_bf16(uint32_t a, uint32_t t025p2) {
   return pk_add(pk_add(z, c), pk_shr(h, 6));
 }
 
+// Byte permute of the 8-byte pool {hi:lo} (bytes 0-3 from lo, 4-7 from hi):
+// result byte i = pool[sel byte i] for selector values 0..7, 0x00 for 12
+// (v_perm_b32; the host form covers exactly these values).
+MXFP4_HD uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_perm(hi, lo, sel);
+#else
+  const uint64_t pool = ((uint64_t)hi << 32) | lo;
+  uint32_t r = 0;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b = (sel >> (8 * i)) & 0xFFu;
+    const uint32_t v = b < 8 ? (uint32_t)(pool >> (8 * b)) & 0xFFu : 0u;  // 12 -> 0x00
+    r |= v << (8 * i);
+  }
+  return r;
+#endif
+}
+
+// E2M1 codes of two bf16 magnitudes by table: with u = sat(a - T) as in
+// snap_idx_bf16 (T = T025 - tau) and v = ceil(u / (Q/2)) (Q/2 = 32), the
+// thresholds 0.25 0.75 1.25 1.75 2.5 3.5 5 (times 2^k) are passed exactly when
+// v >= 1, 7, 10, 12, 14, 16, 18, so
+//   idx = L[min(v, 7)] + min((v - 8) >> 1 saturated at 0, 5),
+//   L = {0, 1, 1, 1, 1, 1, 1, 2} (one v_perm lookup for both halves).
+// t31 = T - 31 per half (T >= 127 for every block that takes the closed
+// form), which folds the ceiling into the saturated subtraction.
+MXFP4_HD uint32_t snap_idx_bf16_tab(uint32_t a, uint32_t t31) {
+  const uint32_t v = pk_shr(pk_subsat(a, t31), 5);
+  const uint32_t lo = perm_b32(0x02010101u, 0x01010100u, pk_min(v, 0x00070007u));
+  const uint32_t hi = pk_min(pk_shr(pk_subsat(v, 0x00080008u), 1), 0x00050005u);
+  return pk_add(lo, hi);
+}
+
 // sign bit kept for negative non-zero inputs only (-0.0 -> +0.0)
 MXFP4_HD uint32_t sign_bf16(uint32_t p) { return p & pk_sub(p, 0x00010001u) & 0x80008000u; }
 MXFP4_HD uint32_t mask_bits_bf16(uint32_t a, uint32_t six2) {

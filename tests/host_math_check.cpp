@@ -111,3 +111,23 @@ extern "C" void host_decode_all(uint16_t *out, uint32_t *out32) {
       out32[e8 * 16 + n] = v << 16;
     }
 }
+
+// Table-based packed E2M1 index vs the closed form, for every bf16 magnitude
+// in both halves and every closed-form T (FLOOR T025 for E8M0 3..252, AMCT
+// T025 - 1 for 97..254).  Returns the number of mismatches.
+extern "C" int host_check_idx_table(void) {
+  int bad = 0;
+  for (uint32_t e8 = 3; e8 <= 254; ++e8) {
+    for (int tau = 0; tau <= 1; ++tau) {
+      if (tau == 1 && e8 < 97) continue;
+      if (tau == 0 && e8 > 252) continue;
+      const uint32_t t = ((e8 - 2) << 7) - (uint32_t)tau;
+      const uint32_t t2 = splat16(t), t31 = splat16(t - 31);
+      for (uint32_t a = 0; a < 0x8000; ++a) {
+        const uint32_t p = a | ((a ^ 0x1234u) & 0x7FFFu) << 16;
+        bad += snap_idx_bf16_tab(p, t31) != snap_idx_bf16(p, t2);
+      }
+    }
+  }
+  return bad;
+}

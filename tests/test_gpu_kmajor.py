@@ -35,13 +35,13 @@ def make_x(shape, dtype, seed):
     return W.f32_to_bf16_bits(a) if dtype == "bf16" else a
 
 
-def run_kmajor(x, block, rule, kb, counts=None, list_type=1):
+def run_kmajor(x, block, rule, kb, counts=None, list_type=1, raw_list=False):
     rows, cols = x.shape
     codes = Guarded((cols, kb * block // 2), torch.uint8, fill=FILL)
     sc = Guarded((cols, kb), torch.uint8, fill=FILL)
     gl = None
     if counts is not None:
-        gl = dev(np.asarray(counts if list_type == 1 else np.cumsum(counts), np.int64))
+        gl = dev(np.asarray(counts if list_type == 1 or raw_list else np.cumsum(counts), np.int64))
     M.mxfp4_quant_pack_kmajor(dev(x), codes.t, sc.t, block=block, rule=rule, group_list=gl,
                               group_list_type=list_type)
     torch.cuda.synchronize()
@@ -64,7 +64,9 @@ DENSE_SHAPES = [(1, 1), (37, 8), (256, 64), (300, 72), (513, 129), (1000, 136), 
 @pytest.mark.parametrize("shape", DENSE_SHAPES)
 def test_kmajor_dense(oracle, dtype, block, rule, shape):
     x = make_x(shape, dtype, seed=shape[0] + shape[1])
-    kb = M.kmajor_k_blocks(shape[0], block) + (3 if shape[1] % 2 else 0)   # some with spare blocks
+    # minimal k_blocks, minimal + spare blocks, and the aligned default
+    kb = (M.kmajor_k_blocks(shape[0], block, align=False) + 3 if shape[1] % 2 else
+          M.kmajor_k_blocks(shape[0], block, align=shape[0] % 2 == 0))
     c, s = run_kmajor(x, block, rule, kb)
     co, so, _ = oracle.pack_kmajor(x, block, rule, k_blocks=kb, fill=FILL)
     assert np.array_equal(c, co)
@@ -98,6 +100,8 @@ GROUP_CASES = [
     (1000, 520, None),
     (33, 8, [33]),
     (300, 66, [0, 0, 300, 0]),
+    (1500, 40, 40),     # 40 groups: decoded by the wave scan
+    (3000, 24, 100),    # 100 groups: two 64-group scan steps
 ]
 
 
@@ -108,16 +112,34 @@ GROUP_CASES = [
 @pytest.mark.parametrize("list_type", [1, 0])
 def test_kmajor_grouped(oracle, dtype, block, rule, case, list_type):
     rows, cols, counts = GROUP_CASES[case]
-    if counts is None:
-        counts = W.ragged_counts(rows, 9, seed=case, zero_groups=2)
+    if counts is None or isinstance(counts, int):
+        counts = W.ragged_counts(rows, counts or 9, seed=case, zero_groups=2 if counts is None else 7)
     counts = np.asarray(counts, np.int64)
     x = make_x((rows, cols), dtype, seed=case + 70)
-    kb = M.kmajor_k_blocks(rows, block, len(counts)) + case % 2
+    kb = M.kmajor_k_blocks(rows, block, len(counts), align=case % 2 == 0) + case % 3 // 2
     c, s = run_kmajor(x, block, rule, kb, counts, list_type)
     co, so, nbt = oracle.pack_kmajor(x, block, rule, group_list=counts, k_blocks=kb, fill=FILL)
     assert np.array_equal(c, co)
     assert np.array_equal(s, so)
     assert (c[:, nbt * block // 2:] == FILL).all()          # block-rows past NBT untouched
+
+
+@pytest.mark.parametrize("list_type,gl", [(1, [100, -5, 50, 400]), (0, [100, 50, 250, 400]),
+                                          (0, [-7, 33, 20, 300])])
+@pytest.mark.parametrize("block", [32, 128])
+def test_kmajor_inconsistent_list_is_clamped(oracle, list_type, gl, block):
+    """An inconsistent group list is clamped (negative counts are 0, ends into
+    [previous end, rows]); the operand equals the oracle's for the clamped list."""
+    from test_gpu_parity import clamp_group_list
+    rows, cols = 300, 72
+    x = make_x((rows, cols), "bf16", 13)
+    counts = clamp_group_list(gl, rows, list_type)
+    kb = M.kmajor_k_blocks(rows, block, len(gl))
+    c, s = run_kmajor(x, block, "floor", kb, np.asarray(gl, np.int64), list_type=list_type,
+                      raw_list=True)
+    co, so, _ = oracle.pack_kmajor(x, block, "floor", group_list=counts, k_blocks=kb, fill=FILL)
+    assert np.array_equal(c, co)
+    assert np.array_equal(s, so)
 
 
 def test_kmajor_decodes_to_column_qdq(oracle):
@@ -134,7 +156,7 @@ def test_kmajor_decodes_to_column_qdq(oracle):
     yo, _, _ = oracle.qdq_cols(x, 32)
     yh = host(y)
     assert np.array_equal(yh[:, :300], yo.T)
-    assert (yh[:, 300:] == 0).all()
+    assert (yh[:, 300:320] == 0).all()       # padding of the short last block (block-rows past it untouched)
 
 
 # ------------------------------------------------------------------ decode

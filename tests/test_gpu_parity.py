@@ -189,6 +189,8 @@ GROUP_CASES = [
     (97, 40, [0, 97]),
     (1000, 520, None),
     (33, 8, [33]),
+    (1500, 40, 40),     # 40 groups: decoded by the wave scan
+    (3000, 24, 100),    # 100 groups: two 64-group scan steps
 ]
 
 
@@ -199,8 +201,8 @@ GROUP_CASES = [
 @pytest.mark.parametrize("list_type", [1, 0])
 def test_grouped(oracle, dtype, block, rule, case, list_type):
     rows, cols, counts = GROUP_CASES[case]
-    if counts is None:
-        counts = W.ragged_counts(rows, 9, seed=case, zero_groups=2)
+    if counts is None or isinstance(counts, int):
+        counts = W.ragged_counts(rows, counts or 9, seed=case, zero_groups=2 if counts is None else 7)
     counts = np.asarray(counts, np.int64)
     gl = counts if list_type == 1 else np.cumsum(counts)
     x = make_x((rows, cols), dtype, seed=case + 50)
@@ -223,6 +225,58 @@ def test_grouped(oracle, dtype, block, rule, case, list_type):
     assert (sh[nbt:] == 0x5A).all()
     for g in (y, m, s):
         g.check_tail()
+
+
+def clamp_group_list(gl, rows, list_type):
+    """The documented treatment of an inconsistent group list: negative counts
+    count as 0, every end is clamped into [previous end, rows]."""
+    prev, cum, counts = 0, 0, []
+    for v in gl:
+        if list_type == 1:
+            cum += max(int(v), 0)
+            end = min(cum, rows)
+        else:
+            end = min(max(int(v), prev), rows)
+        counts.append(end - prev)
+        prev = end
+    return np.asarray(counts, np.int64)
+
+
+LONG_BAD = [5, -3, 0] * 23 + [40]   # 70 entries: the scan path, counts past rows
+
+
+@pytest.mark.parametrize("list_type,gl", [(1, [100, -5, 50, 400]), (0, [100, 50, 250, 400]),
+                                          (1, [0, 0, 301]), (0, [-7, 33, 20, 300]),
+                                          (1, LONG_BAD), (0, list(np.cumsum(LONG_BAD)[::-1]))])
+@pytest.mark.parametrize("block", [32, 128])
+def test_grouped_inconsistent_list_is_clamped(oracle, list_type, gl, block):
+    """Counts that go negative, run past rows or ends that decrease are
+    clamped (in range by construction), for the QDQ, its bitmap and the STE."""
+    rows, cols = 300, 72
+    x = make_x((rows, cols), "bf16", 11)
+    counts = clamp_group_list(gl, rows, list_type)
+    G = len(gl)
+    y = Guarded((rows, cols), torch.bfloat16)
+    m = Guarded((M.grouped_mask_rows_max(rows, block, G), cols), torch.int32, fill=0)
+    s = Guarded((M.grouped_scale_rows_max(rows, block, G), cols), torch.uint8, fill=0x5A)
+    gld = dev(np.asarray(gl, np.int64))
+    M.mxfp4_grouped_qdq(dev(x), gld, y.t, m.t, s.t, block=block, group_list_type=list_type)
+    g = make_x((rows, cols), "bf16", 12)
+    gi = Guarded((rows, cols), torch.bfloat16)
+    M.mxfp4_ste_bwd(dev(g), m.t, gi.t, M.GROUPED, block=block, group_list=gld,
+                    group_list_type=list_type)
+    torch.cuda.synchronize()
+    total = int(counts.sum())
+    yo, co, eo = oracle.grouped_cols(x[:total], counts, block)
+    assert np.array_equal(host(y.t)[:total], yo)
+    nbt = eo.shape[0]
+    assert np.array_equal(host(s.t)[:nbt], eo)
+    assert (host(s.t)[nbt:] == 0x5A).all()
+    bits, clean = unpack_grouped_bitmap(host(m.t)[: nbt * (block // 32)], total, counts, block)
+    assert np.array_equal(bits, co) and clean
+    assert np.array_equal(host(gi.t)[:total], oracle.ste_bwd(g[:total], co))
+    for b in (y, m, s, gi):
+        b.check_tail()
 
 
 def test_grouped_rows_past_total_untouched(oracle):

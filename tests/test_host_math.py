@@ -156,3 +156,10 @@ def test_generic_decode_every_nibble_and_byte(host, oracle):
     want32 = oracle.unpack_rows(codes, scales, 16, 32, np.float32).view(np.uint32)
     assert np.array_equal(out.reshape(256, 16), want16)
     assert np.array_equal(out32.reshape(256, 16), want32)
+
+
+def test_table_index_equals_closed_form(host):
+    """The kernels' table-based E2M1 index (one byte-permute lookup) equals the
+    closed form for every bf16 magnitude under every closed-form scale, both
+    tie rules (host emulation of the byte permute)."""
+    assert host.host_check_idx_table() == 0
