@@ -23,7 +23,8 @@ argument and enqueue on torch's current stream:
 Tensor conventions: x / y / grads are bfloat16 or float32, 2-D contiguous
 (higher ranks are viewed as rows x last-dim); bitmaps are int32 tensors (the
 uint32 bit patterns); scales and codes are uint8; group_list is int64 on the
-device.  The alloc_* helpers allocate outputs of the documented shapes.
+device, or a CPU tensor / sequence, which is validated (counts >= 0 summing
+to rows, or non-decreasing ends ending at rows) and copied to the device.  The alloc_* helpers allocate outputs of the documented shapes.
 """
 from __future__ import annotations
 
@@ -166,6 +167,27 @@ def _same_elems(x, *ys):
 
 # ------------------------------------------------------------ entry points
 
+def _group_list(group_list, rows: int, group_list_type: int):
+    """group_list on the device as is; a CPU tensor (or sequence) is checked
+    first -- counts >= 0 summing to rows (type 1), non-decreasing ends ending
+    at rows (type 0), the caller's contract the device cannot check without a
+    synchronisation -- then copied to the current device."""
+    if group_list is None or (isinstance(group_list, torch.Tensor) and group_list.is_cuda):
+        return group_list
+    gl = torch.as_tensor(group_list, dtype=torch.int64)
+    if gl.dim() != 1 or gl.numel() < 1:
+        raise ValueError("group_list must be a non-empty 1-D list of int64")
+    v = gl.tolist()
+    if group_list_type == 1:
+        if min(v) < 0 or sum(v) != rows:
+            raise ValueError(f"group counts must be >= 0 and sum to rows={rows}, got sum {sum(v)}")
+    elif group_list_type == 0:
+        if v[0] < 0 or any(b < a for a, b in zip(v, v[1:])) or v[-1] != rows:
+            raise ValueError(f"cumulative group ends must be non-decreasing and end at rows={rows}")
+    return gl.to(device=torch.cuda.current_device())
+
+
+
 def mxfp4_qdq_fwd(x, axis=ROW, y_row=None, mask_row=None, scales_row=None, y_col=None,
                   mask_col=None, scales_col=None, block=32, rule="floor", scale_factor=6.0):
     """Fused QDQ forward (+ clip bitmap, + E8M0 scales); see include/mxfp4.h."""
@@ -182,6 +204,7 @@ def mxfp4_ste_bwd(grad_out, mask, grad_in, layout=ROW, block=32, group_list=None
     """Clipped (mask given) or plain (mask None) STE backward."""
     _same_elems(grad_out, grad_in)
     d = _desc(grad_out, block, "floor", 6.0)
+    group_list = _group_list(group_list, d.rows, group_list_type)
     n_groups = group_list.numel() if group_list is not None else 0
     st = _load().mxfp4_ste_bwd(ctypes.byref(d), int(layout), _ptr(grad_out), _ptr(mask, "mask"),
                                _ptr(grad_in), _ptr(group_list, "i64"), n_groups,
@@ -205,6 +228,7 @@ def mxfp4_grouped_qdq(x, group_list, y, mask=None, scales=None, block=32, rule="
     or cumulative row ends (type 0), int64 on the device."""
     _same_elems(x, y)
     d = _desc(x, block, rule, scale_factor)
+    group_list = _group_list(group_list, d.rows, group_list_type)
     st = _load().mxfp4_grouped_qdq(ctypes.byref(d), _ptr(x), _ptr(group_list, "i64"),
                                    group_list.numel(), int(group_list_type), _ptr(y),
                                    _ptr(mask, "mask"), _ptr(scales, "u8"), _stream())
@@ -223,6 +247,7 @@ def mxfp4_quant_pack_kmajor(x, codes_t, scales_t, block=32, rule="floor", scale_
     if codes_t is None or tuple(codes_t.shape) != (cols, k_blocks * int(block) // 2):
         raise ValueError(f"codes_t must be [{cols}, {k_blocks * int(block) // 2}]")
     d = _desc(x, block, rule, scale_factor)
+    group_list = _group_list(group_list, rows, group_list_type)
     n_groups = group_list.numel() if group_list is not None else 0
     st = _load().mxfp4_quant_pack_kmajor(ctypes.byref(d), _ptr(x), _ptr(group_list, "i64"),
                                          n_groups, int(group_list_type), k_blocks,

@@ -11,17 +11,18 @@
 // or 64-byte (block 128) pieces along K.  K position t*block + o is x row
 // start_t + o of block-row t while o < len_t, else a padding code 0.
 //
-// Tiling: a workgroup owns 256 K positions x 64 columns.  Lane (cg, rq), with
-// cg = lane & 7 and rq = 8*wave + (lane >> 3), holds K positions 8rq .. 8rq+7
-// (8 consecutive rows of x, one block-row) of columns 8cg .. 8cg+7, loaded as
-// one 16-byte bf16 piece per row, so 8 lanes read a whole 128-byte row
-// segment.  Then
-//   - a 32-row block is 4 lanes at distance 8: column max by DPP row_ror:8
-//     and ds_swizzle xor 16; a 128-row block spans two waves, which exchange
-//     their maxima through LDS;
+// Tiling: a workgroup (8 waves) owns 256 K positions x 128 columns.  Lane
+// (cg, rq), with cg = lane & 15 and rq = 4*wave + (lane >> 4), holds K
+// positions 8rq .. 8rq+7 (8 consecutive rows of x, inside one block-row) of
+// columns 8cg .. 8cg+7, loaded as one 16-byte bf16 piece per row, so 16 lanes
+// read a 256-byte row segment.  Then
+//   - a 32-row block is one wave (lanes at distance 16): column max by
+//     ds_swizzle xor 16 and ds_bpermute xor 32; a 128-row block spans 4 waves,
+//     which combine their maxima through LDS;
 //   - the 8 nibbles of one column in one lane form one 32-bit word at byte
-//     4*rq of the column's 128-byte line of codes, so every line of codes_t
-//     is written whole by one workgroup.
+//     4*rq of the column's 128-byte line of codes; the words are staged in LDS
+//     and each line of codes_t is written whole, by 8 lanes with 16-byte
+//     stores.
 //
 // Decode: codes [rows, ceil(cols/2)] + scales [rows, ceil(cols/block)] ->
 // values [rows, cols] in bf16 or fp32; K-major codes decode with rows = the
@@ -33,11 +34,13 @@
 namespace mxfp4 {
 namespace {
 
-constexpr int kKTile = 256;  // K positions per workgroup
-constexpr int kCTile = 64;   // columns per workgroup
-// Minimum workgroups per CU requested from the compiler (caps the VGPRs).
+constexpr int kKTile = 256;      // K positions per workgroup
+constexpr int kCTile = 128;      // columns per workgroup
+constexpr int kKmThreads = 512;  // 8 waves, each 32 K positions x 128 columns
+// Minimum waves per SIMD requested from the compiler (4 caps the VGPRs at 128,
+// i.e. two 8-wave workgroups per CU).
 #ifndef MXFP4_KMAJOR_MINWG
-#define MXFP4_KMAJOR_MINWG 3
+#define MXFP4_KMAJOR_MINWG 4
 #endif
 // 8-element chunks per lane of the flat decode kernel.
 #ifndef MXFP4_DQ_U
@@ -152,23 +155,13 @@ __device__ __forceinline__ KmTile km_tile(const KmArgs &A, int64_t tile, int wav
   KmTile T;
   T.kt = tile / A.nct;
   T.col0 = (tile - T.kt * A.nct) * kCTile;
-  T.kpos = T.kt * kKTile + 8 * (8 * wave + rql);
+  T.kpos = T.kt * kKTile + 8 * (4 * wave + rql);
   T.bt = T.kpos >> LB;
   T.o0 = (int)(T.kpos & (B - 1));
   int64_t start, len;
   if (GROUPED) {
-    // wave-uniform lookups: a wave covers 64 K positions, i.e. two 32-row
-    // block-rows or half of a 128-row one
-    const int64_t btw = (T.kt * kKTile + 64 * wave) >> LB;
-    if (B == 32) {
-      const int64_t tt[2] = {btw, btw + 1};
-      int64_t ss[2], ll[2];
-      block_rows_lookup<2>(A.group_list, A.num_groups, A.list_type, A.rows, LB, tt, ss, ll);
-      start = rql >= 4 ? ss[1] : ss[0];
-      len = rql >= 4 ? ll[1] : ll[0];
-    } else {
-      block_row_uniform(A.group_list, A.num_groups, A.list_type, A.rows, LB, btw, &start, &len);
-    }
+    // a wave covers 32 K positions: one block-row, the same for every lane
+    block_row_uniform(A.group_list, A.num_groups, A.list_type, A.rows, LB, T.bt, &start, &len);
     if (T.bt >= A.k_blocks) len = 0;
   } else {
     start = T.bt << LB;
@@ -186,39 +179,45 @@ __device__ __forceinline__ KmTile km_tile(const KmArgs &A, int64_t tile, int wav
   return T;
 }
 
-// LDS staging of one tile's outputs.  Code words sit [column][K word] with a
-// row stride of 33 words, so the 64 lanes of a staging write fall in distinct
-// banks; scale bytes [column][block-row of the tile]; a live flag per
-// block-row of the tile.
+// LDS staging of one tile's outputs.  Code word (column c, K word kw) sits at
+// codes[c][4 * ((kw >> 2) ^ ((c >> 3) & 7)) + (kw & 3)]: 16-byte chunks of a
+// column row are XOR-swizzled by the column's group, so the 64 lanes of a
+// staging write (16 column groups x 4 K words) spread over all banks, and the
+// 8 lanes that read one column's 8 chunks (ds_read_b128) hit distinct banks.
 struct KmStage {
-  uint32_t codes[kCTile][kKTile / 8 + 1];
+  uint32_t codes[kCTile][kKTile / 8] __attribute__((aligned(16)));
   uint8_t scales[kCTile][kKTile / 32];
   uint8_t live[kKTile / 32];
 };
 
-// One workgroup per tile: load, column maxima, nibbles, then the tile's
+__device__ __forceinline__ int km_slot(int c, int kw) {
+  return c * (kKTile / 8) + 4 * ((kw >> 2) ^ ((c >> 3) & 7)) + (kw & 3);
+}
+
+// One workgroup per tile: load, column maxima, nibbles; then the tile's
 // outputs go through LDS so that 8 lanes store each column's 128-byte line of
 // codes with 16-byte stores and one lane its scale bytes (8 for block 32) in
 // one store, instead of 4-byte and 1-byte pieces scattered by row lanes.
 template <int DT, int B, int RULE, bool GROUPED, bool VEC>
-__global__ __launch_bounds__(kThreads, MXFP4_KMAJOR_MINWG) void kmajor_pack_kernel(KmArgs A) {
+__global__ __launch_bounds__(kKmThreads, MXFP4_KMAJOR_MINWG) void kmajor_pack_kernel(KmArgs A) {
   constexpr int NW = PieceT<DT>::NW;
   constexpr int ES = PieceT<DT>::ES;
   constexpr uint32_t ABS = DT == kBF16 ? 0x7FFF7FFFu : 0x7FFFFFFFu;
   constexpr int NBT_TILE = kKTile / B;  // block-rows per tile
-  __shared__ uint32_t s_cm[4][8][NW];
+  __shared__ uint32_t s_cm[kKmThreads / 64][16][NW];
   __shared__ KmStage st;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int cg = lane & 7;
-  const int rql = lane >> 3;
+  const int cg = lane & 15;
+  const int rql = lane >> 4;
   const KmTile T = km_tile<DT, B, GROUPED, VEC>(A, blockIdx.x, wave, rql, cg);
 
   // ---- load 8 rows x 8 columns --------------------------------------------
   // A wave whose piece is all inside the tensor issues its eight loads
-  // unconditionally, so they are all in flight together.
+  // unconditionally, so they are all in flight together; 16 lanes read one
+  // 256-byte (bf16) row segment.
   const int64_t rstride = A.cols * ES;
   uint32_t w[8][NW];
   if (T.full) {
@@ -230,15 +229,16 @@ __global__ __launch_bounds__(kThreads, MXFP4_KMAJOR_MINWG) void kmajor_pack_kern
   }
 
   // ---- column maxima (padding rows read as +0 and never raise them) -------
+  // a 32-row block is the wave's 4 lane rows (lanes cg, cg+16, cg+32, cg+48);
+  // a 128-row block is 4 consecutive waves, combined through LDS
   uint32_t cm[NW];
 #pragma unroll
   for (int k = 0; k < NW; ++k) {
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = colmax_step<DT>(m, w[i][k] & ABS);
-    m = colmax_step<DT>(m, dpp<kDppRowRor8>(m));  // lane ^ 8
     m = colmax_step<DT>(m, lane_xor16(m));
-    if (B == 128) m = colmax_step<DT>(m, lane_xor32(m));
+    m = colmax_step<DT>(m, lane_xor32(m));
     cm[k] = m;
   }
   if (B == 128) {
@@ -247,8 +247,11 @@ __global__ __launch_bounds__(kThreads, MXFP4_KMAJOR_MINWG) void kmajor_pack_kern
       for (int k = 0; k < NW; ++k) s_cm[wave][cg][k] = cm[k];
     }
     __syncthreads();
+    const int w0 = wave & ~3;
 #pragma unroll
-    for (int k = 0; k < NW; ++k) cm[k] = colmax_step<DT>(cm[k], s_cm[wave ^ 1][cg][k]);
+    for (int k = 0; k < NW; ++k)
+      cm[k] = colmax_step<DT>(colmax_step<DT>(s_cm[w0][cg][k], s_cm[w0 + 1][cg][k]),
+                              colmax_step<DT>(s_cm[w0 + 2][cg][k], s_cm[w0 + 3][cg][k]));
   }
 
   // ---- per-column parameters ---------------------------------------------
@@ -279,10 +282,10 @@ __global__ __launch_bounds__(kThreads, MXFP4_KMAJOR_MINWG) void kmajor_pack_kern
   else code_words<DT, RULE, false>(w, pt, pe, cm, cbp, cw);
 
   // ---- stage in LDS ----------------------------------------------------------
-  const int kw = 8 * wave + rql;  // K word of the lane inside the tile
+  const int kw = 4 * wave + rql;  // K word of the lane inside the tile
   const int bl = (8 * kw) / B;    // block-row of the lane inside the tile
 #pragma unroll
-  for (int j = 0; j < 8; ++j) st.codes[8 * cg + j][kw] = cw[j];
+  for (int j = 0; j < 8; ++j) (&st.codes[0][0])[km_slot(8 * cg + j, kw)] = cw[j];
   if (T.o0 == 0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -297,13 +300,13 @@ __global__ __launch_bounds__(kThreads, MXFP4_KMAJOR_MINWG) void kmajor_pack_kern
   // end is not written.
   const int64_t kbyte = T.kt * (kKTile / 2);
 #pragma unroll
-  for (int r = 0; r < (kCTile * kKTile / 32) / kThreads; ++r) {
-    const int chunk = tid + r * kThreads;
+  for (int r = 0; r < (kCTile * kKTile / 32) / kKmThreads; ++r) {
+    const int chunk = tid + r * kKmThreads;
     const int c = chunk >> 3, q = chunk & 7;
     const int64_t col = T.col0 + c;
     if (col < A.cols && st.live[(32 * q) / B]) {
-      const uint32_t *s = &st.codes[c][4 * q];
-      st16(A.codes + col * A.ldk + kbyte + 16 * q, make_uint4(s[0], s[1], s[2], s[3]));
+      const uint4 v = *reinterpret_cast<const uint4 *>(&(&st.codes[0][0])[km_slot(c, 4 * q)]);
+      st16(A.codes + col * A.ldk + kbyte + 16 * q, v);
     }
   }
   if (tid < kCTile && T.col0 + tid < A.cols) {
@@ -328,9 +331,9 @@ template <int DT, int B, int RULE, bool GROUPED>
 hipError_t km_launch(bool vec, const KmArgs &a, hipStream_t st) {
   const dim3 grid((unsigned)a.ntiles);
   if (vec)
-    hipLaunchKernelGGL((kmajor_pack_kernel<DT, B, RULE, GROUPED, true>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((kmajor_pack_kernel<DT, B, RULE, GROUPED, true>), grid, dim3(kKmThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((kmajor_pack_kernel<DT, B, RULE, GROUPED, false>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((kmajor_pack_kernel<DT, B, RULE, GROUPED, false>), grid, dim3(kKmThreads), 0, st, a);
   return hipGetLastError();
 }
 

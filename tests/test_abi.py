@@ -177,3 +177,19 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 32, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         M.mxfp4_qdq_fwd(x, M.ROW, y_row=torch.empty_like(x))
+
+
+def test_cpu_group_list_is_validated_before_any_gpu_work():
+    """A CPU group_list is checked on the host (the device cannot check the
+    sum without a synchronisation): counts must be >= 0 and sum to rows."""
+    import mxfp4_fake_quantization_amd as M
+    with pytest.raises(ValueError, match="sum to rows"):
+        M._group_list([10, 20], 31, 1)
+    with pytest.raises(ValueError, match="sum to rows"):
+        M._group_list([40, -9], 31, 1)
+    with pytest.raises(ValueError, match="non-decreasing"):
+        M._group_list([20, 10, 31], 31, 0)
+    with pytest.raises(ValueError, match="non-decreasing"):
+        M._group_list([10, 30], 31, 0)
+    with pytest.raises(ValueError):
+        M._group_list([], 0, 1)

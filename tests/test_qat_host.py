@@ -40,3 +40,4 @@ def test_w4a16_default_has_no_input_quantizer():
     lin = MXFP4QATLinear(64, 32)
     assert lin.weight_quantizer is not None and lin.input_quantizer is None
     assert "block_size=32" in repr(lin.weight_quantizer)
+
