@@ -367,3 +367,104 @@ int oracle_pack_kmajor(int dtype, int64_t rows, int64_t cols, int block, int rul
   free(blen);
   return 0;
 }
+
+/* ---- MXFP8 (the grad_output operand of the W4A8 grouped matmul) ------------
+ * The hyper-parallel page quantizes grad_output with npu_dynamic_mx_quant for
+ * the NN / NT products but does not define it; this follows the OCP
+ * Microscaling (MX) v1.0 conversion: blocks of 32 along the last dimension,
+ * shared scale X = 2^k with k = floor(log2 amax) - emax (emax = exponent of
+ * the element format's largest normal: E4M3 8, E5M2 15; the same rule with
+ * emax = 2 is this file's FLOOR rule for E2M1), clamped below at -127
+ * (amax = 0 gives k = -127); every element is x / X rounded to the nearest
+ * value of the element format, ties to even, saturating at the largest normal
+ * (E4M3 448, E5M2 57344).  Signs follow IEEE conversion: a negative value
+ * that rounds to zero, and -0.0, give -0 (byte 0x80).
+ * fmt 0: E4M3 (bias 7, 3 mantissa bits, no infinities, 0x7F/0xFF NaN);
+ * fmt 1: E5M2 (bias 15, 2 mantissa bits). */
+static void fp8_params(int fmt, int *mb, int *bias, double *maxn, int *emax) {
+  if (fmt == 0) {
+    *mb = 3; *bias = 7; *maxn = 448.0; *emax = 8;
+  } else {
+    *mb = 2; *bias = 15; *maxn = 57344.0; *emax = 15;
+  }
+}
+
+/* Encode |v| (already divided by the scale) as a sign-less fp8 code. */
+static uint8_t fp8_encode_mag(int fmt, double a) {
+  int mb, bias, emax;
+  double maxn;
+  fp8_params(fmt, &mb, &bias, &maxn, &emax);
+  const int emin = 1 - bias; /* exponent of the smallest normal */
+  if (a >= maxn) a = maxn;   /* saturation */
+  if (a == 0.0) return 0;
+  int e;
+  (void)frexp(a, &e);
+  e -= 1; /* a = m * 2^e, 1 <= m < 2 */
+  const int eq = e < emin ? emin : e;
+  const double quantum = ldexp(1.0, eq - mb);
+  double q = rint(a / quantum) * quantum; /* exact division; rint = ties to even */
+  if (q > maxn) q = maxn;
+  if (q == 0.0) return 0;
+  (void)frexp(q, &e);
+  e -= 1;
+  if (e < emin) /* subnormal: exponent field 0 */
+    return (uint8_t)(q / ldexp(1.0, emin - mb));
+  return (uint8_t)(((e + bias) << mb) | (int)((q / ldexp(1.0, e) - 1.0) * (1 << mb)));
+}
+
+/* Row-wise MXFP8: q [rows, cols] bytes, scales [rows, ceil(cols/32)] E8M0. */
+int oracle_mxfp8_rows(int dtype, int64_t rows, int64_t cols, int fmt, const void *x,
+                      uint8_t *q, uint8_t *scales) {
+  if (rows < 0 || cols < 0 || (fmt != 0 && fmt != 1)) return 1;
+  int mb, bias, emax;
+  double maxn;
+  fp8_params(fmt, &mb, &bias, &maxn, &emax);
+  const int64_t nb = (cols + 31) / 32;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const int64_t c0 = b * 32;
+      const int n = (int)((cols - c0) < 32 ? (cols - c0) : 32);
+      double amax = 0.0;
+      for (int j = 0; j < n; ++j) {
+        const double a = fabs(get_elem(dtype, x, r * cols + c0 + j));
+        if (a > amax) amax = a;
+      }
+      int k = -127;
+      if (amax > 0.0) {
+        int e;
+        (void)frexp(amax, &e);
+        k = (e - 1) - emax;
+        if (k < -127) k = -127;
+      }
+      scales[r * nb + b] = (uint8_t)(k + 127);
+      const double scale = ldexp(1.0, k);
+      for (int j = 0; j < n; ++j) {
+        const double v = get_elem(dtype, x, r * cols + c0 + j) / scale; /* exact */
+        const uint8_t m = fp8_encode_mag(fmt, fabs(v));
+        q[r * cols + c0 + j] = (uint8_t)(m | (signbit(v) ? 0x80 : 0));
+      }
+    }
+  }
+  return 0;
+}
+
+/* Decode MXFP8 back to values: (-1)^s * element(code) * 2^(e8 - 127). */
+int oracle_mxfp8_decode(int dtype, int64_t rows, int64_t cols, int fmt, const uint8_t *q,
+                        const uint8_t *scales, void *y) {
+  if (rows < 0 || cols < 0 || (fmt != 0 && fmt != 1)) return 1;
+  int mb, bias, emax;
+  double maxn;
+  fp8_params(fmt, &mb, &bias, &maxn, &emax);
+  const int64_t nb = (cols + 31) / 32;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      const uint8_t b = q[r * cols + c];
+      const int ef = (b & 0x7F) >> mb, m = b & ((1 << mb) - 1);
+      double v = ef == 0 ? ldexp((double)m, 1 - bias - mb)
+                         : ldexp(1.0 + (double)m / (1 << mb), ef - bias);
+      v *= ldexp(1.0, (int)scales[r * nb + c / 32] - 127);
+      if (b & 0x80) v = -v;
+      put_elem(dtype, y, r * cols + c, v);
+    }
+  return 0;
+}

@@ -37,6 +37,11 @@ MUTANTS = {
     "kmajor_scale_layout": ("scales_t[c * k_blocks + t] = ", "scales_t[t * cols + c] = "),
     "kmajor_pad_code": ("uint8_t lo = o < n ? nib[idx[o]] : 0;", "uint8_t lo = o < n ? nib[idx[o]] : 8;"),
     "kmajor_leading_dim": ("int64_t ldk = k_blocks * block / 2;", "int64_t ldk = nbt * block / 2;"),
+    "mxfp8_ties_away": ("double q = rint(a / quantum) * quantum;", "double q = round(a / quantum) * quantum;"),
+    "mxfp8_emax": ("*mb = 3; *bias = 7; *maxn = 448.0; *emax = 8;", "*mb = 3; *bias = 7; *maxn = 448.0; *emax = 7;"),
+    "mxfp8_e4m3_max_480": ("*mb = 3; *bias = 7; *maxn = 448.0;", "*mb = 3; *bias = 7; *maxn = 480.0;"),
+    "mxfp8_zero_sign": ("q[r * cols + c0 + j] = (uint8_t)(m | (signbit(v) ? 0x80 : 0));", "q[r * cols + c0 + j] = (uint8_t)(m | (v < 0 && m ? 0x80 : 0));"),
+    "mxfp8_subnormal_quantum": ("const int emin = 1 - bias; /* exponent of the smallest normal */", "const int emin = -bias;"),
     "e8m0_bias": ("if (e8m0) e8m0[r * nb + b] = (uint8_t)(k + 127);", "if (e8m0) e8m0[r * nb + b] = (uint8_t)(k + 128);"),
 }
 

@@ -559,3 +559,99 @@ def test_clip_fraction_statistic(oracle):
     _, cf, _ = oracle.qdq_rows(x, 32, "floor")
     assert abs(ca[:, 0].mean() - 0.5) < 0.01
     assert abs(cf[:, 0].mean() - math.log2(8 / 6)) < 0.01
+
+
+# ------------------------------------------------------------- MXFP8 (OCP MX)
+
+def fp8_table(fmt):
+    """Value of every non-NaN, finite fp8 code (decoded from the bit fields)."""
+    mb, bias = (3, 7) if fmt == "e4m3" else (2, 15)
+    vals = {}
+    for c in range(256):
+        s, ef, m = c >> 7, (c & 0x7F) >> mb, c & ((1 << mb) - 1)
+        if fmt == "e4m3" and (c & 0x7F) == 0x7F:
+            continue                                   # NaN
+        if fmt == "e5m2" and ef == 31:
+            continue                                   # inf / NaN
+        v = (m / (1 << mb)) * 2.0 ** (1 - bias) if ef == 0 else (1 + m / (1 << mb)) * 2.0 ** (ef - bias)
+        vals[c] = -v if s else v
+    return vals
+
+
+def fp8_nearest(v, fmt):
+    """Brute-force RNE: nearest code by value, ties to the even code, saturated
+    at the largest finite value; zero keeps the sign of v."""
+    tab = fp8_table(fmt)
+    codes = np.array([c for c in tab if c < 0x80], np.int64)
+    mags = np.array([tab[c] for c in codes])
+    a = np.minimum(np.abs(v), mags.max())
+    d = np.abs(a[:, None] - mags[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    even = cand & ((codes[None, :] & 1) == 0)
+    pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+    return (codes[pick] | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("j", [0, -5, 20, -118, 100])
+def test_mxfp8_every_bf16_value_against_brute_force(oracle, fmt, j):
+    """Every bf16 value v with |v| below a block maximum M = 1.5 * 2^j, in a
+    block holding M: the scale is 2^(j - emax) and each code is the nearest
+    fp8 value of v / scale (ties to even, saturating)."""
+    emax = 8 if fmt == "e4m3" else 15
+    M = np.float32(1.5 * 2.0 ** j)
+    allb = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    v = W.bf16_bits_to_f32(allb)
+    v = v[np.isfinite(v) & (np.abs(v) <= M)]
+    n = -(-v.size // 31) * 31
+    vv = np.zeros(n, np.float32)
+    vv[: v.size] = v
+    x = np.concatenate([np.full((n // 31, 1), M, np.float32), vv.reshape(-1, 31)], axis=1)
+    xb = W.f32_to_bf16_bits(x)
+    q, e8 = oracle.mxfp8_rows(xb, fmt)
+    k = max(j - emax, -127)                    # the scale exponent's lower clamp
+    assert (e8 == k + 127).all()
+    want = fp8_nearest(x[:, 1:].astype(np.float64).reshape(-1) / 2.0 ** k, fmt)
+    assert np.array_equal(q[:, 1:].reshape(-1), want)
+
+
+def test_mxfp8_hand_worked(oracle):
+    """amax 1.0: k = 0 - 8, scale 2^-8 (E8M0 119); 1.0 -> 256 = 1.0*2^8 -> 0x78;
+    0.3 -> 76.8 -> nearest of {72, 80} = 80 = 1.25*2^6 -> 0x6A (sign 0xEA);
+    -0.0 -> 0x80; 1e-5 -> 0.00256 -> one subnormal step 2^-9 -> 0x01.
+    A block with maximum 1.99 (scaled 509.4) saturates to 448 -> 0x7E."""
+    x = np.zeros((2, 32), np.float32)
+    x[0, :6] = [1.0, 0.3, -0.3, 0.0, -0.0, 1e-5]
+    x[1, 0] = 1.99
+    q, e8 = oracle.mxfp8_rows(x, "e4m3")
+    assert list(q[0, :6]) == [0x78, 0x6A, 0xEA, 0x00, 0x80, 0x01]
+    assert e8[0, 0] == 119 and e8[1, 0] == 119
+    assert q[1, 0] == 0x7E
+
+
+def test_mxfp8_scale_rule_and_decode(oracle):
+    """E8M0 byte = floor(log2 amax) - emax + 127, clamped at 0 (zero and tiny
+    blocks); decoding the codes gives values within half a code step, or the
+    largest normal times the scale where the element saturated."""
+    g = np.random.default_rng(81)
+    x = (g.standard_t(3, size=(64, 96)) * np.exp2(g.uniform(-30, 30, (64, 1)))).astype(np.float32)
+    x[0] = 0.0
+    x[1, :] = 2.0 ** -140                      # fp32 subnormal block maximum
+    for fmt, emax in (("e4m3", 8), ("e5m2", 15)):
+        q, e8 = oracle.mxfp8_rows(x, fmt)
+        amax = np.abs(x.reshape(64, 3, 32)).max(axis=2)
+        with np.errstate(divide="ignore"):
+            want = np.floor(np.log2(amax)) - emax + 127
+        want = np.where(np.isfinite(want), want, 0)
+        want = np.where(amax > 0, np.maximum(want, 0), 0)
+        assert np.array_equal(e8, want.astype(np.uint8))
+        y = oracle.mxfp8_decode(q, e8, fmt, np.float32).astype(np.float64)
+        step = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(x), 1e-300))) - (3 if fmt == "e4m3" else 2))
+        sub = 2.0 ** (e8.astype(np.float64) - 127 + (-9 if fmt == "e4m3" else -16))
+        tol = np.maximum(step, np.repeat(sub, 32, axis=1)) / 2
+        maxn = 448.0 if fmt == "e4m3" else 57344.0
+        scale = np.repeat(2.0 ** (e8.astype(np.float64) - 127), 32, axis=1)
+        tol = np.maximum(tol, np.abs(x) - maxn * scale)     # saturated elements
+        assert (np.abs(y - x) <= tol * (1 + 1e-12)).all()
+        assert (np.abs(y) <= maxn * scale).all()
