@@ -385,7 +385,14 @@ def bench_all(M, lib, W, torch, args):
     kcalls = [Call(lib.mxfp4_quant_pack_kmajor, ctypes.byref(d), vp(xs[i].data_ptr()), vp(gl.data_ptr()), 8, 1,
                    kb, vp(kc[i].data_ptr()), vp(ks[i].data_ptr()), stream) for i in range(2)]
     rec("kmajor_grouped_32768x7168", R * C * 2 + C * nbt * (16 + 1), R * C, _time_calls(torch, kcalls, 30))
-    del xs, kc, ks
+    del kc, ks
+    # MXFP8 (E4M3) of a grad_output of the same shape
+    q8 = [torch.empty((R, C), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    s8 = [torch.empty((R, C // 32), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    mcalls = [Call(lib.mxfp8_quant, ctypes.byref(d), 0, vp(xs[i].data_ptr()), vp(q8[i].data_ptr()),
+                   vp(s8[i].data_ptr()), stream) for i in range(2)]
+    rec("mxfp8_e4m3_32768x7168", R * C * (2 + 1 + 1 / 32), R * C, _time_calls(torch, mcalls, 30))
+    del xs, q8, s8
     return out
 
 

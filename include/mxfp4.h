@@ -80,6 +80,7 @@ typedef enum {
 enum { MXFP4_F32 = 0, MXFP4_BF16 = 1 };                 /* element dtype      */
 enum { MXFP4_ROW = 1, MXFP4_COL = 2, MXFP4_GROUPED = 4 }; /* axis / layout bits */
 enum { MXFP4_RULE_FLOOR = 0, MXFP4_RULE_AMCT = 1 };      /* scale + tie rule   */
+enum { MXFP8_E4M3 = 0, MXFP8_E5M2 = 1 };                 /* MXFP8 element type */
 
 typedef struct mxfp4_desc {
   int32_t dtype;        /* MXFP4_BF16 or MXFP4_F32                             */
@@ -222,6 +223,24 @@ mxfp4_status_t mxfp4_quant_pack_kmajor(const mxfp4_desc_t *desc, const void *x,
  */
 mxfp4_status_t mxfp4_dequant(const mxfp4_desc_t *desc, const uint8_t *codes,
                              const uint8_t *scales, void *y, void *stream);
+
+/*
+ * MXFP8 quantization of the grad_output operand of the W4A8 grouped matmul
+ * (the hyper-parallel page's npu_dynamic_mx_quant for the NN / NT products,
+ * which it does not define; this is the OCP Microscaling v1.0 conversion):
+ * blocks of 32 along each row (desc->block must be 32), E8M0 scale byte
+ * e8 = max(floor(log2 amax) - emax + 127, 0) with emax 8 (MXFP8_E4M3) or 15
+ * (MXFP8_E5M2), an all-zero block giving 0; each element is x / 2^(e8-127)
+ * rounded to the nearest fp8 value, ties to even, saturating at 448 (E4M3) /
+ * 57344 (E5M2), so no NaN / infinity code is produced; -0.0 and negative
+ * values that round to zero give -0 (0x80).
+ *   q      [rows, cols] fp8 bytes (OCP E4M3 bias 7 / E5M2 bias 15),
+ *   scales [rows, ceil(cols/32)] E8M0 bytes.
+ * desc->rule and scale_factor are ignored.  x and q 16-byte aligned, scales
+ * any alignment, no aliasing.
+ */
+mxfp4_status_t mxfp8_quant(const mxfp4_desc_t *desc, int32_t fmt, const void *x,
+                           uint8_t *q, uint8_t *scales, void *stream);
 
 /* Message for the calling thread's most recent failed call ("" if none). */
 const char *mxfp4_last_error(void);

@@ -19,6 +19,7 @@ argument and enqueue on torch's current stream:
     mxfp4_quant_pack_kmajor(x, codes_t, scales_t, block=32, rule="floor",
                             scale_factor=6.0, group_list=None, group_list_type=1)
     mxfp4_dequant(codes, scales, y, block=32)
+    mxfp8_quant(x, q, scales, fmt="e4m3")
 
 Tensor conventions: x / y / grads are bfloat16 or float32, 2-D contiguous
 (higher ranks are viewed as rows x last-dim); bitmaps are int32 tensors (the
@@ -36,7 +37,7 @@ import torch
 __all__ = [
     "ROW", "COL", "GROUPED", "FLOOR", "AMCT",
     "mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
-    "mxfp4_quant_pack_kmajor", "mxfp4_dequant",
+    "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant",
     "mxfp4_last_error", "mxfp4_version", "library_path",
     "row_mask_shape", "col_mask_shape", "grouped_mask_rows_max", "grouped_scale_rows_max",
     "kmajor_k_blocks",
@@ -76,8 +77,9 @@ def _load():
         lib.mxfp4_grouped_qdq.argtypes = [dp, vp, vp, i32, i32, vp, vp, vp, vp]
         lib.mxfp4_quant_pack_kmajor.argtypes = [dp, vp, vp, i32, i32, ctypes.c_int64, vp, vp, vp]
         lib.mxfp4_dequant.argtypes = [dp, vp, vp, vp, vp]
+        lib.mxfp8_quant.argtypes = [dp, i32, vp, vp, vp, vp]
         for f in ("mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
-                  "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp4_version"):
+                  "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant", "mxfp4_version"):
             getattr(lib, f).restype = ctypes.c_int32
         lib.mxfp4_last_error.restype = ctypes.c_char_p
         lib.mxfp4_last_error.argtypes = []
@@ -267,6 +269,25 @@ def mxfp4_dequant(codes, scales, y, block=32):
     st = _load().mxfp4_dequant(ctypes.byref(d), _ptr(codes, "u8"), _ptr(scales, "u8"), _ptr(y),
                                _stream())
     _check(st, "mxfp4_dequant")
+
+
+_FP8 = {"e4m3": 0, "e5m2": 1}
+
+
+def mxfp8_quant(x, q, scales, fmt="e4m3"):
+    """MXFP8 (OCP MX, blocks of 32 along the last dim): q uint8 with x's
+    shape, scales uint8 [rows, ceil(cols/32)]."""
+    if fmt not in _FP8:
+        raise ValueError(f"fmt must be 'e4m3' or 'e5m2', got {fmt!r}")
+    rows, cols = _shape2d(x)
+    if q is None or q.numel() != x.numel():
+        raise ValueError("q must have x's number of elements")
+    if scales is None or scales.numel() != rows * (-(-cols // 32)):
+        raise ValueError(f"scales must hold {rows} x {-(-cols // 32)} bytes")
+    d = _Desc(_dtype(x), 32, FLOOR, 0, rows, cols, 6.0, 0)
+    st = _load().mxfp8_quant(ctypes.byref(d), _FP8[fmt], _ptr(x), _ptr(q, "u8"), _ptr(scales, "u8"),
+                             _stream())
+    _check(st, "mxfp8_quant")
 
 
 # ------------------------------------------------------------ shapes

@@ -76,4 +76,16 @@ struct DqLaunch {
 };
 hipError_t launch_dequant(const DqLaunch &L, hipStream_t stream);
 
+
+// MXFP8 (OCP MX) row-wise quantization.
+enum { kE4M3 = 0, kE5M2 = 1 };
+struct Mx8Launch {
+  int dtype, fmt;
+  int64_t rows, cols;
+  const void *x;
+  uint8_t *q;       // [rows, cols] fp8 bytes
+  uint8_t *scales;  // [rows, ceil(cols/32)] E8M0
+};
+hipError_t launch_mxfp8_rows(const Mx8Launch &L, hipStream_t stream);
+
 }  // namespace mxfp4

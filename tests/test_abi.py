@@ -37,19 +37,21 @@ def lib():
     L.mxfp4_grouped_qdq.argtypes = [dp, vp, vp, i32, i32, vp, vp, vp, vp]
     L.mxfp4_quant_pack_kmajor.argtypes = [dp, vp, vp, i32, i32, ctypes.c_int64, vp, vp, vp]
     L.mxfp4_dequant.argtypes = [dp, vp, vp, vp, vp]
+    L.mxfp8_quant.argtypes = [dp, i32, vp, vp, vp, vp]
     L.mxfp4_last_error.restype = ctypes.c_char_p
     return L
 
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\S[^\n(]*?\b(mxfp4_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\S[^\n(]*?\b(mxfp[48]_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
-              "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp4_last_error", "mxfp4_version"):
+              "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant", "mxfp4_last_error",
+              "mxfp4_version"):
         assert n in names
 
 
@@ -169,6 +171,22 @@ def test_kmajor_and_dequant_validation(lib):
     assert dq(c, s, x, None) == EUNSUP
     D.dtype, D.rows = BF16, 0
     assert dq(c, s, x, None) == OK
+
+
+def test_mxfp8_validation(lib):
+    D = d(rows=8, cols=64)
+    m8 = lambda *a: lib.mxfp8_quant(ctypes.byref(D), *a)
+    x, q, s = P(), P(FAKE + 4096), P(FAKE + 8192)
+    assert m8(2, x, q, s, None) == EINVAL                   # unknown fmt
+    assert m8(0, None, q, s, None) == EINVAL
+    assert m8(0, x, None, s, None) == EINVAL
+    assert m8(0, x, q, None, None) == EINVAL
+    assert m8(0, x, P(FAKE + 4100), s, None) == EINVAL     # q misaligned
+    assert m8(0, x, q, q, None) == EINVAL                   # alias
+    D.block = 128
+    assert m8(0, x, q, s, None) == EUNSUP                   # MX blocks are 32
+    D.block, D.rows = 32, 0
+    assert m8(1, x, q, s, None) == OK
 
 
 def test_python_binding_refuses_cpu_tensors():
