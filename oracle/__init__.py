@@ -16,7 +16,7 @@ import numpy as np
 
 from . import build as _build
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 FLOOR, AMCT = 0, 1
 
 _lib = None
@@ -44,9 +44,11 @@ def _load():
                                            vp, vp]
         lib.oracle_mxfp8_rows.argtypes = [i32, i64, i64, i32, vp, vp, vp]
         lib.oracle_mxfp8_decode.argtypes = [i32, i64, i64, i32, vp, vp, vp]
+        lib.oracle_grouped_matmul.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, i32, vp]
         for fn in ("oracle_qdq_rows", "oracle_qdq_cols", "oracle_grouped_cols",
                    "oracle_ste_bwd", "oracle_pack_rows", "oracle_unpack_rows",
-                   "oracle_pack_kmajor", "oracle_mxfp8_rows", "oracle_mxfp8_decode"):
+                   "oracle_pack_kmajor", "oracle_mxfp8_rows", "oracle_mxfp8_decode",
+                   "oracle_grouped_matmul"):
             getattr(lib, fn).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -57,7 +59,9 @@ def _dtype_code(x: np.ndarray) -> int:
         return F32
     if x.dtype == np.uint16:
         return BF16
-    raise TypeError(f"oracle arrays are float32 or uint16 (bf16 bits), got {x.dtype}")
+    if x.dtype == np.float64:
+        return F64
+    raise TypeError(f"oracle arrays are float32, uint16 (bf16 bits) or float64, got {x.dtype}")
 
 
 def _ptr(a):
@@ -209,3 +213,40 @@ def mxfp8_decode(q: np.ndarray, scales: np.ndarray, fmt: str = "e4m3", dtype=np.
     _check(_load().oracle_mxfp8_decode(_dtype_code(y), rows, cols, FP8_FORMATS[fmt], _ptr(q),
                                        _ptr(scales), _ptr(y)), "mxfp8_decode")
     return y
+
+
+GROUP_M, GROUP_K = 0, 2
+
+
+def grouped_matmul(left: np.ndarray, right: np.ndarray, group_list=None, group_type: int = GROUP_M,
+                   list_type: int = 1, out=None):
+    """Grouped matrix product of decoded operand values (float64).
+
+    group_type GROUP_M: left [M, K], right [G, K, N] -> out [M, N] (rows past the groups'
+    total keep `out`'s values; a new `out` starts as NaN).
+    group_type GROUP_K: left [M, K], right [K, N] -> out [G, M, N].
+    group_list None: one group covering the split dimension."""
+    left = np.ascontiguousarray(left, dtype=np.float64)
+    right = np.ascontiguousarray(right, dtype=np.float64)
+    M, K = left.shape
+    N = right.shape[-1]
+    split = M if group_type == GROUP_M else K
+    if group_list is None:
+        gl, lt = np.array([split], np.int64), 1
+    else:
+        gl, lt = np.ascontiguousarray(np.asarray(group_list, dtype=np.int64)), list_type
+    G = len(gl)
+    if group_type == GROUP_M:
+        if right.ndim == 2:
+            right = right[None]
+        assert right.shape == (G, K, N), (right.shape, G, K, N)
+        shape = (M, N)
+    else:
+        assert right.shape == (K, N), (right.shape, K, N)
+        shape = (G, M, N)
+    if out is None:
+        out = np.full(shape, np.nan)
+    assert out.shape == shape and out.dtype == np.float64 and out.flags.c_contiguous
+    _check(_load().oracle_grouped_matmul(group_type, M, N, K, _ptr(left), _ptr(right), _ptr(gl), G,
+                                         lt, _ptr(out)), "grouped_matmul")
+    return out

@@ -19,6 +19,9 @@
  * -> cumulative sums), and the packed form follows the sglang "mxfp4_npu.py"
  * page (two FP4 codes per byte); oracle_pack_kmajor stores the column-wise /
  * grouped operand in that packed form with the reduction dimension contiguous.
+ * oracle_grouped_matmul is the grouped matrix product that consumes these
+ * operands (the hyper-parallel page's grouped_matmul, NN / NT / TN), computed
+ * from decoded values with exact products and extended-precision sums.
  *
  * Two scale rules ("profiles"):
  *   FLOOR (default): k = floor(log2 amax) - 2, clamped below at -127; an
@@ -48,6 +51,7 @@
 
 #define OR_F32 0
 #define OR_BF16 1
+#define OR_F64 2 /* decoded operand values for the matrix product */
 #define OR_FLOOR 0
 #define OR_AMCT 1
 
@@ -63,6 +67,7 @@ static const float kMinScaleRaw = 0x1p-30f;
 /* ---- element access ------------------------------------------------------ */
 
 static double get_elem(int dtype, const void *p, int64_t i) {
+  if (dtype == OR_F64) return ((const double *)p)[i];
   if (dtype == OR_F32) return (double)((const float *)p)[i];
   /* bf16 is the upper half of an IEEE binary32: widening is exact. */
   uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16;
@@ -72,6 +77,10 @@ static double get_elem(int dtype, const void *p, int64_t i) {
 }
 
 static void put_elem(int dtype, void *p, int64_t i, double v) {
+  if (dtype == OR_F64) {
+    ((double *)p)[i] = v;
+    return;
+  }
   float f = (float)v; /* exact for every value this oracle produces */
   if (dtype == OR_F32) {
     ((float *)p)[i] = f;
@@ -466,5 +475,65 @@ int oracle_mxfp8_decode(int dtype, int64_t rows, int64_t cols, int fmt, const ui
       if (b & 0x80) v = -v;
       put_elem(dtype, y, r * cols + c, v);
     }
+  return 0;
+}
+
+/* ---- grouped MX matrix product ------------------------------------------- */
+
+/* The grouped matmul that consumes the directional operands (hyper-parallel
+ * page, FakeW4A8GroupedLinear: grouped_matmul hands the operands chosen by
+ * _select_operands to the NPU grouped matmul together with group_list and
+ * group_type).  It is computed from the decoded operand values (the MX
+ * decoders above, output type OR_F64): every product of two decoded elements
+ * is exact in double, and the sums run in long double, so the result is the
+ * exact sum to well below fp32 rounding.
+ *
+ *   group_type 0 -- groups split the rows (the NN forward and the NT input
+ *     gradient: tokens of expert g times expert g's weight):
+ *       left [M, K], right [G, K, N], out [M, N];
+ *       out[m, n] = sum_k left[m, k] * right[g(m), k, n] for every row m of
+ *       group g; rows past the last group end are not touched.
+ *   group_type 2 -- groups split the reduction dimension (the TN weight
+ *     gradient: expert g's tokens of x^T times the same tokens of dy):
+ *       left [M, K], right [K, N], out [G, M, N];
+ *       out[g, m, n] = sum over k in group g of left[m, k] * right[k, n].
+ *
+ * group_list holds per-group counts (list_type 1, normalize_group_list turns
+ * them into cumulative sums) or cumulative ends (list_type 0) along the split
+ * dimension.  Returns 1 for bad sizes, a group_type other than 0 or 2, or an
+ * inconsistent list (negative count, decreasing ends, or past the split
+ * dimension). */
+int oracle_grouped_matmul(int group_type, int64_t M, int64_t N, int64_t K,
+                          const double *left, const double *right,
+                          const int64_t *group_list, int num_groups, int list_type,
+                          double *out) {
+  if (M < 0 || N < 0 || K < 0 || num_groups < 1) return 1;
+  if (group_type != 0 && group_type != 2) return 1;
+  const int64_t split = group_type == 0 ? M : K;
+  int64_t start = 0;
+  for (int g = 0; g < num_groups; ++g) {
+    const int64_t end = list_type == 1 ? start + group_list[g] : group_list[g];
+    if (end < start || end > split) return 1;
+    if (group_type == 0) {
+      const double *w = right + (int64_t)g * K * N;
+      for (int64_t m = start; m < end; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+          long double acc = 0.0L;
+          for (int64_t k = 0; k < K; ++k)
+            acc += (long double)left[m * K + k] * (long double)w[k * N + n];
+          out[m * N + n] = (double)acc;
+        }
+    } else {
+      double *o = out + (int64_t)g * M * N;
+      for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+          long double acc = 0.0L;
+          for (int64_t k = start; k < end; ++k)
+            acc += (long double)left[m * K + k] * (long double)right[k * N + n];
+          o[m * N + n] = (double)acc;
+        }
+    }
+    start = end;
+  }
   return 0;
 }

@@ -42,6 +42,14 @@ MUTANTS = {
     "mxfp8_e4m3_max_480": ("*mb = 3; *bias = 7; *maxn = 448.0;", "*mb = 3; *bias = 7; *maxn = 480.0;"),
     "mxfp8_zero_sign": ("q[r * cols + c0 + j] = (uint8_t)(m | (signbit(v) ? 0x80 : 0));", "q[r * cols + c0 + j] = (uint8_t)(m | (v < 0 && m ? 0x80 : 0));"),
     "mxfp8_subnormal_quantum": ("const int emin = 1 - bias; /* exponent of the smallest normal */", "const int emin = -bias;"),
+    "gmm_group_weight": ("const double *w = right + (int64_t)g * K * N;", "const double *w = right + (int64_t)(g > 0 ? g - 1 : 0) * K * N;"),
+    "gmm_list_type": ("const int64_t end = list_type == 1 ? start + group_list[g] : group_list[g];",
+                      "const int64_t end = list_type == 1 ? group_list[g] : group_list[g];"),
+    "gmm_reduction_range": ("for (int64_t k = start; k < end; ++k)", "for (int64_t k = 0; k < end; ++k)"),
+    "gmm_transposed_right": ("acc += (long double)left[m * K + k] * (long double)w[k * N + n];",
+                             "acc += (long double)left[m * K + k] * (long double)w[(n * K + k) % (K * N)];"),
+    "gmm_double_sum": ("long double acc = 0.0L;\n          for (int64_t k = 0; k < K; ++k)", "double acc = 0.0;\n          for (int64_t k = 0; k < K; ++k)"),
+    "gmm_group_out_stride": ("double *o = out + (int64_t)g * M * N;", "double *o = out + (int64_t)g * M;"),
     "e8m0_bias": ("if (e8m0) e8m0[r * nb + b] = (uint8_t)(k + 127);", "if (e8m0) e8m0[r * nb + b] = (uint8_t)(k + 128);"),
 }
 

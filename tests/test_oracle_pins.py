@@ -655,3 +655,121 @@ def test_mxfp8_scale_rule_and_decode(oracle):
         tol = np.maximum(tol, np.abs(x) - maxn * scale)     # saturated elements
         assert (np.abs(y - x) <= tol * (1 + 1e-12)).all()
         assert (np.abs(y) <= maxn * scale).all()
+
+
+# ---- grouped matrix product ---------------------------------------------------
+
+GOLDEN_GMM = os.path.join(os.path.dirname(__file__), "golden", "grouped_matmul.json")
+
+
+def test_grouped_matmul_hand_worked(oracle):
+    with open(GOLDEN_GMM) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        out = oracle.grouped_matmul(np.array(c["left"], float), np.array(c["right"], float),
+                                    c["group_list"], c["group_type"], c["list_type"])
+        exp = np.array([[np.nan if v is None else v for v in row] for row in c["out"]]
+                       if c["group_type"] == 0 else c["out"], float)
+        assert np.array_equal(out, exp, equal_nan=True), c["name"]
+
+
+def _counts_to_ends(counts):
+    return np.cumsum(counts)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_grouped_matmul_rows_against_library(oracle, seed):
+    """group_type 0: every group's rows equal a library product of that slice
+    with the group's own right operand; list types agree; rows past the total
+    keep their old values."""
+    g = np.random.default_rng(seed)
+    M, K, N, G = 37, 23, 11, 5
+    counts = g.multinomial(M - 4, np.ones(G) / G)
+    counts[2] = 0
+    left = g.standard_normal((M, K))
+    right = g.standard_normal((G, K, N))
+    out = oracle.grouped_matmul(left, right, counts, oracle.GROUP_M, 1)
+    out0 = oracle.grouped_matmul(left, right, _counts_to_ends(counts), oracle.GROUP_M, 0)
+    assert np.array_equal(out, out0, equal_nan=True)
+    s = 0
+    for gi, c in enumerate(counts):
+        np.testing.assert_allclose(out[s:s + c], left[s:s + c] @ right[gi], rtol=1e-13, atol=1e-13)
+        s += c
+    assert np.isnan(out[s:]).all()
+    one = oracle.grouped_matmul(left, right[1], None, oracle.GROUP_M)
+    np.testing.assert_allclose(one, left @ right[1], rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_grouped_matmul_reduction_against_library(oracle, seed):
+    """group_type 2: out[g] is a library product over group g's slice of the
+    reduction dimension; the groups' sum is the product over every covered
+    index."""
+    g = np.random.default_rng(seed)
+    M, K, N, G = 13, 41, 9, 4
+    counts = g.multinomial(K - 3, np.ones(G) / G)
+    counts[0] = 0
+    left = g.standard_normal((M, K))
+    right = g.standard_normal((K, N))
+    out = oracle.grouped_matmul(left, right, counts, oracle.GROUP_K, 1)
+    assert out.shape == (G, M, N)
+    s = 0
+    for gi, c in enumerate(counts):
+        np.testing.assert_allclose(out[gi], left[:, s:s + c] @ right[s:s + c], rtol=1e-13, atol=1e-13)
+        s += c
+    np.testing.assert_allclose(out.sum(0), left[:, :s] @ right[:s], rtol=1e-12, atol=1e-12)
+    out0 = oracle.grouped_matmul(left, right, _counts_to_ends(counts), oracle.GROUP_K, 0)
+    assert np.array_equal(out, out0)
+
+
+def test_grouped_matmul_sum_is_exact_beyond_double(oracle):
+    """Sums run in extended precision: 2^60 + 1 - 2^60 = 1 in every layout."""
+    left = np.array([[2.0 ** 60, 1.0, -(2.0 ** 60)]])
+    right = np.ones((3, 1))
+    assert oracle.grouped_matmul(left, right[None], [1], oracle.GROUP_M)[0, 0] == 1.0
+    assert oracle.grouped_matmul(left, right, [3], oracle.GROUP_K)[0, 0, 0] == 1.0
+
+
+def test_grouped_matmul_mx_operands_scale_exactly(oracle):
+    """On decoded MX operands (MXFP8 rows times MXFP4 rows), raising one
+    row's E8M0 byte by one doubles exactly that output row, and raising one
+    weight column's byte doubles exactly that output column."""
+    g = np.random.default_rng(5)
+    M, K, N = 6, 64, 5
+    x = W.f32_to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    w = W.f32_to_bf16_bits(g.standard_normal((N, K)).astype(np.float32))
+    q, sa = oracle.mxfp8_rows(x)
+    codes, sb = oracle.pack_rows(w)
+    def prod(sa_, sb_):
+        a = oracle.mxfp8_decode(q, sa_, "e4m3", np.float64)
+        b = oracle.unpack_rows(codes, sb_, K, 32, np.float64)
+        return oracle.grouped_matmul(a, b.T.copy()[None], None, oracle.GROUP_M)
+    base = prod(sa, sb)
+    sa2 = sa.copy()
+    sa2[3] += 1
+    r = prod(sa2, sb)
+    assert np.array_equal(r[3], 2 * base[3]) and np.array_equal(np.delete(r, 3, 0), np.delete(base, 3, 0))
+    sb2 = sb.copy()
+    sb2[1] += 1
+    r = prod(sa, sb2)
+    assert np.array_equal(r[:, 1], 2 * base[:, 1]) and np.array_equal(np.delete(r, 1, 1), np.delete(base, 1, 1))
+
+
+def test_grouped_matmul_rejects_bad_lists(oracle):
+    left, right = np.ones((4, 3)), np.ones((2, 3, 2))
+    for gl, lt in (([3, 2], 1), ([-1, 5], 1), ([3, 2], 0), ([2, 5], 0)):
+        with pytest.raises(ValueError):
+            oracle.grouped_matmul(left, right, gl, oracle.GROUP_M, lt)
+    with pytest.raises(ValueError):
+        oracle.grouped_matmul(left, np.ones((3, 2)), [1, 3], oracle.GROUP_K, 1)
+
+
+def test_decoders_float64_match_float32(oracle):
+    g = np.random.default_rng(8)
+    x = W.f32_to_bf16_bits(g.standard_normal((7, 96)).astype(np.float32))
+    q, s = oracle.mxfp8_rows(x)
+    assert np.array_equal(oracle.mxfp8_decode(q, s, "e4m3", np.float64),
+                          oracle.mxfp8_decode(q, s, "e4m3", np.float32).astype(np.float64))
+    c, s4 = oracle.pack_rows(x)
+    assert np.array_equal(oracle.unpack_rows(c, s4, 96, 32, np.float64),
+                          oracle.unpack_rows(c, s4, 96, 32, np.float32).astype(np.float64))
