@@ -81,6 +81,10 @@ enum { MXFP4_F32 = 0, MXFP4_BF16 = 1 };                 /* element dtype      */
 enum { MXFP4_ROW = 1, MXFP4_COL = 2, MXFP4_GROUPED = 4 }; /* axis / layout bits */
 enum { MXFP4_RULE_FLOOR = 0, MXFP4_RULE_AMCT = 1 };      /* scale + tie rule   */
 enum { MXFP8_E4M3 = 0, MXFP8_E5M2 = 1 };                 /* MXFP8 element type */
+/* element formats of the grouped matmul operands, group split, output type */
+enum { MXGEMM_E4M3 = 0, MXGEMM_E5M2 = 1, MXGEMM_E2M1 = 4 };
+enum { MXGEMM_GROUP_ROWS = 0, MXGEMM_GROUP_K = 2 };
+enum { MXGEMM_OUT_BF16 = 0, MXGEMM_OUT_F32 = 1 };
 
 typedef struct mxfp4_desc {
   int32_t dtype;        /* MXFP4_BF16 or MXFP4_F32                             */
@@ -241,6 +245,62 @@ mxfp4_status_t mxfp4_dequant(const mxfp4_desc_t *desc, const uint8_t *codes,
  */
 mxfp4_status_t mxfp8_quant(const mxfp4_desc_t *desc, int32_t fmt, const void *x,
                            uint8_t *q, uint8_t *scales, void *stream);
+
+/*
+ * One MX operand of the grouped matmul: element codes stored with the
+ * reduction dimension K contiguous, and E8M0 scales (value of element k of
+ * row r = decode(code) * 2^(scale[r, k / block] - 127)).
+ */
+typedef struct mxfp4_mx_operand {
+  const void *data;        /* device, 16-byte aligned: [rows, ld] bytes.  MXGEMM_E4M3 /
+                              MXGEMM_E5M2: one OCP fp8 code per byte; MXGEMM_E2M1: two
+                              codes per byte, low nibble = even K (mxfp4_quant_pack /
+                              mxfp4_quant_pack_kmajor layout)                          */
+  const uint8_t *scales;   /* device: [rows, ld_scales] E8M0 bytes                     */
+  int32_t fmt;             /* MXGEMM_E4M3, MXGEMM_E5M2 or MXGEMM_E2M1                  */
+  int32_t block;           /* elements per scale along K: 32 or 128                    */
+  int64_t ld;              /* bytes between rows of data, multiple of 16               */
+  int64_t ld_scales;       /* bytes between rows of scales                             */
+  int64_t group_stride;    /* MXGEMM_GROUP_ROWS right operand: bytes from group g's
+                              data to group g+1's (0 for one shared matrix)           */
+  int64_t group_stride_scales;  /* the same for the scales                           */
+} mxfp4_mx_operand_t;
+
+/*
+ * Grouped MX matrix product, the consumer of the directional operands (the
+ * hyper-parallel page's FakeW4A8GroupedLinear.grouped_matmul with the
+ * operands _select_operands picks for the NN, NT and TN layouts).  Both
+ * operands are K-contiguous, so every layout is, per group,
+ *     C[m, n] = sum_k A[m, k] * B[n, k]
+ * with A MXFP8 (a->fmt E4M3 or E5M2) and B MXFP4 (E2M1) or MXFP8, products
+ * of decoded values summed in fp32 by the matrix cores and rounded once to
+ * the output type (bf16 round-to-nearest-even, or fp32).
+ *   group_type MXGEMM_GROUP_ROWS (NN forward: A = row-wise MXFP8 tokens, B_g =
+ *     the K-major column-wise weight of expert g; NT input gradient: A =
+ *     row-wise MXFP8 grad_output, B_g = the row-wise weight): group_list
+ *     splits A's M rows; rows of group g use B_g = b->data + g *
+ *     b->group_stride (scales likewise).  A [M, K], B [G][N, K], C [M, ldc];
+ *     rows past the groups' total are not written.  group_list NULL: one
+ *     group of all M rows.  K % 32 == 0.
+ *   group_type MXGEMM_GROUP_K (TN weight gradient: A = x^T and B = dy^T,
+ *     both column-wise grouped operands in the K-major layout of
+ *     mxfp4_quant_pack_kmajor): group_list (required) splits the K tokens;
+ *     group g occupies the 32-blocks starting at sum_{h<g} ceil(c_h / 32), in
+ *     both operands, and positions past c_g in its last block hold zero
+ *     codes.  A [M, k_blocks*32], B [N, k_blocks*32] (codes), C [G][M, ldc];
+ *     an empty group writes zeros.  Both blocks 32; group spans are clamped
+ *     to k_blocks.
+ * group_list: device int64 counts (group_list_type 1) or cumulative ends
+ * (type 0), clamped as in mxfp4_grouped_qdq.  out_dtype MXGEMM_OUT_BF16 /
+ * MXGEMM_OUT_F32; c aligned to its element size, ldc >= N.  ld >= the bytes
+ * of one row of K, ld_scales >= its blocks, and ld * 256 < 2^32.  Nothing is
+ * allocated; the kernels run on `stream`.
+ */
+mxfp4_status_t mxfp4_grouped_matmul(int32_t group_type, int64_t M, int64_t N, int64_t K,
+                                    const mxfp4_mx_operand_t *a, const mxfp4_mx_operand_t *b,
+                                    const int64_t *group_list, int32_t num_groups,
+                                    int32_t group_list_type, int64_t k_blocks,
+                                    int32_t out_dtype, void *c, int64_t ldc, void *stream);
 
 /* Message for the calling thread's most recent failed call ("" if none). */
 const char *mxfp4_last_error(void);

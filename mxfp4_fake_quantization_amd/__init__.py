@@ -58,6 +58,13 @@ class _Desc(ctypes.Structure):
                 ("scale_factor", ctypes.c_float), ("reserved1", ctypes.c_int32)]
 
 
+class _MxOperand(ctypes.Structure):
+    """mxfp4_mx_operand_t (include/mxfp4.h)."""
+    _fields_ = [("data", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("fmt", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("ld", ctypes.c_int64), ("ld_scales", ctypes.c_int64),
+                ("group_stride", ctypes.c_int64), ("group_stride_scales", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -78,8 +85,13 @@ def _load():
         lib.mxfp4_quant_pack_kmajor.argtypes = [dp, vp, vp, i32, i32, ctypes.c_int64, vp, vp, vp]
         lib.mxfp4_dequant.argtypes = [dp, vp, vp, vp, vp]
         lib.mxfp8_quant.argtypes = [dp, i32, vp, vp, vp, vp]
+        op = ctypes.POINTER(_MxOperand)
+        i64 = ctypes.c_int64
+        lib.mxfp4_grouped_matmul.argtypes = [i32, i64, i64, i64, op, op, vp, i32, i32, i64, i32, vp,
+                                             i64, vp]
         for f in ("mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
-                  "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant", "mxfp4_version"):
+                  "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant", "mxfp4_version",
+                  "mxfp4_grouped_matmul"):
             getattr(lib, f).restype = ctypes.c_int32
         lib.mxfp4_last_error.restype = ctypes.c_char_p
         lib.mxfp4_last_error.argtypes = []
@@ -288,6 +300,79 @@ def mxfp8_quant(x, q, scales, fmt="e4m3"):
     st = _load().mxfp8_quant(ctypes.byref(d), _FP8[fmt], _ptr(x), _ptr(q, "u8"), _ptr(scales, "u8"),
                              _stream())
     _check(st, "mxfp8_quant")
+
+
+MX_FORMATS = {"e4m3": 0, "e5m2": 1, "e2m1": 4}
+GROUP_ROWS, GROUP_K = 0, 2
+
+
+def _operand(data, scales, fmt, block, group_stride=None):
+    if fmt not in MX_FORMATS:
+        raise ValueError(f"fmt must be one of {sorted(MX_FORMATS)}, got {fmt!r}")
+    for t, what in ((data, "data"), (scales, "scales")):
+        if t is None or t.dim() not in (2, 3):
+            raise ValueError(f"operand {what} must be a 2-D or 3-D uint8 tensor")
+    if data.dim() != scales.dim():
+        raise ValueError("operand data and scales must have the same rank")
+    if group_stride is not None:
+        gs, gss = (int(v) for v in group_stride)
+    elif data.dim() == 3:
+        gs, gss = data.shape[1] * data.shape[2], scales.shape[1] * scales.shape[2]
+    else:
+        gs, gss = 0, 0
+    return _MxOperand(_ptr(data, "u8").value, _ptr(scales, "u8").value, MX_FORMATS[fmt], int(block),
+                      data.shape[-1], scales.shape[-1], gs, gss)
+
+
+def mxfp4_grouped_matmul(a, a_scales, b, b_scales, c, K=None, group_list=None, group_type=GROUP_ROWS,
+                         group_list_type=1, a_fmt="e4m3", b_fmt="e2m1", a_block=32, b_block=32,
+                         k_blocks=None, b_group_stride=None):
+    """Grouped MX matmul C = A . B^T per group (include/mxfp4.h).
+
+    a [M, lda] fp8 codes + a_scales [M, ldas]; b [N, ldb] or [G, N, ldb] codes +
+    b_scales of the same rank (b_group_stride = (data bytes, scale bytes) overrides
+    the per-group strides); c bf16 / f32 [M, N] (rows-split groups) or [G, M, N]
+    (K-split groups).  K defaults to a's row length (rows-split) or the group total
+    (K-split, where k_blocks defaults to a's row length / 32)."""
+    if c is None or c.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("c must be a bfloat16 or float32 tensor")
+    M = a.shape[0]
+    ldc = c.shape[-1]
+    if group_type == GROUP_ROWS:
+        if c.dim() != 2 or c.shape[0] != M:
+            raise ValueError(f"c must be [M={M}, N]")
+        N = b.shape[-2]
+        if K is None:
+            K = a.shape[1]
+        gl = _group_list(group_list, M, group_list_type)
+        kb = 0
+    else:
+        if group_list is None:
+            raise ValueError("groups that split K need a group_list")
+        N = b.shape[-2]
+        gl_cpu = group_list
+        if K is None:
+            v = torch.as_tensor(group_list, dtype=torch.int64).tolist() if not (
+                isinstance(group_list, torch.Tensor) and group_list.is_cuda) else None
+            if v is None:
+                raise ValueError("K (the token total) is required with a device group_list")
+            K = sum(v) if group_list_type == 1 else v[-1]
+        gl = _group_list(gl_cpu, int(K), group_list_type)
+        kb = a.shape[1] // 32 if k_blocks is None else int(k_blocks)
+        if c.dim() != 3 or c.shape[1] != M:
+            raise ValueError(f"c must be [G, M={M}, N]")
+    if c.shape[-1] != N:
+        raise ValueError(f"c's last dim must be N={N}")
+    ng = 0 if gl is None else gl.numel()
+    if group_type == GROUP_K and c.shape[0] != ng:
+        raise ValueError(f"c must hold one [M, N] matrix per group ({ng})")
+    oa = _operand(a, a_scales, a_fmt, a_block)
+    ob = _operand(b, b_scales, b_fmt, b_block, b_group_stride)
+    out = 1 if c.dtype == torch.float32 else 0
+    st = _load().mxfp4_grouped_matmul(int(group_type), M, N, int(K), ctypes.byref(oa), ctypes.byref(ob),
+                                      _ptr(gl, "i64"), ng, int(group_list_type), kb, out, _ptr(c), ldc,
+                                      _stream())
+    _check(st, "mxfp4_grouped_matmul")
 
 
 # ------------------------------------------------------------ shapes

@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libmxfp4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["api.hip", "row_kernels.hip", "col_kernels.hip", "ste_kernels.hip",
-           "kmajor_kernels.hip", "mxfp8_kernels.hip"]
+           "kmajor_kernels.hip", "mxfp8_kernels.hip", "mxgemm_kernels.hip"]
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

@@ -255,8 +255,95 @@ mxfp4_status_t mxfp8_quant(const mxfp4_desc_t *desc, int32_t fmt, const void *x,
   return hip_status(mxfp4::launch_mxfp8_rows(L, static_cast<hipStream_t>(stream)), "MXFP8 launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+mxfp4_status_t check_operand(const mxfp4_mx_operand_t *o, const char *what, bool rows_split, int64_t K,
+                             int64_t k_blocks, bool is_a) {
+  if (!o) return fail(MXFP4_EINVAL, "%s is NULL", what);
+  if (is_a ? (o->fmt != MXGEMM_E4M3 && o->fmt != MXGEMM_E5M2)
+           : (o->fmt != MXGEMM_E4M3 && o->fmt != MXGEMM_E5M2 && o->fmt != MXGEMM_E2M1))
+    return fail(MXFP4_EUNSUPPORTED, "%s->fmt %d is not supported", what, o->fmt);
+  if (o->block != 32 && o->block != 128)
+    return fail(MXFP4_EUNSUPPORTED, "%s->block %d is not 32 or 128", what, o->block);
+  if (!rows_split && o->block != 32)
+    return fail(MXFP4_EUNSUPPORTED, "%s->block must be 32 when groups split K", what);
+  MXFP4_TRY(check_ptr(o->data, 16, what));
+  if (!o->scales) return fail(MXFP4_EINVAL, "%s->scales is NULL", what);
+  const int64_t kel = rows_split ? K : k_blocks * 32;  // K extent of a row
+  const int64_t row_bytes = o->fmt == MXGEMM_E2M1 ? kel / 2 : kel;
+  const int64_t nblk = (kel + o->block - 1) / o->block;
+  if (o->ld % 16 != 0 || o->ld < row_bytes)
+    return fail(MXFP4_EINVAL, "%s->ld %lld must be a multiple of 16 and >= %lld", what, (long long)o->ld,
+                (long long)row_bytes);
+  if (o->ld > (int64_t)1 << 24) return fail(MXFP4_EUNSUPPORTED, "%s->ld is above 2^24 bytes", what);
+  if (o->ld_scales < nblk || o->ld_scales > (int64_t)1 << 24)
+    return fail(MXFP4_EINVAL, "%s->ld_scales %lld must be >= %lld (and below 2^24)", what,
+                (long long)o->ld_scales, (long long)nblk);
+  if (o->group_stride < 0 || o->group_stride_scales < 0 || o->group_stride % 16 != 0)
+    return fail(MXFP4_EINVAL, "%s group strides must be >= 0 (data: a multiple of 16)", what);
+  return MXFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mxfp4_status_t mxfp4_grouped_matmul(int32_t group_type, int64_t M, int64_t N, int64_t K,
+                                    const mxfp4_mx_operand_t *a, const mxfp4_mx_operand_t *b,
+                                    const int64_t *group_list, int32_t num_groups,
+                                    int32_t group_list_type, int64_t k_blocks, int32_t out_dtype,
+                                    void *c, int64_t ldc, void *stream) {
+  if (group_type != MXGEMM_GROUP_ROWS && group_type != MXGEMM_GROUP_K)
+    return fail(MXFP4_EINVAL, "group_type %d is not MXGEMM_GROUP_ROWS or MXGEMM_GROUP_K", group_type);
+  const bool rows = group_type == MXGEMM_GROUP_ROWS;
+  if (M < 0 || N < 0 || K < 0) return fail(MXFP4_EINVAL, "negative shape");
+  if (rows && K % 32 != 0) return fail(MXFP4_EINVAL, "K %lld is not a multiple of 32", (long long)K);
+  if (!rows && (k_blocks < 0 || !group_list))
+    return fail(MXFP4_EINVAL, "groups that split K need a group_list and k_blocks >= 0");
+  if (group_list && (num_groups < 1 || (group_list_type != 0 && group_list_type != 1)))
+    return fail(MXFP4_EINVAL, "num_groups must be >= 1 and group_list_type 0 or 1");
+  MXFP4_TRY(check_opt(group_list, 8, "group_list"));
+  MXFP4_TRY(check_operand(a, "a", rows, K, k_blocks, true));
+  MXFP4_TRY(check_operand(b, "b", rows, K, k_blocks, false));
+  if (out_dtype != MXGEMM_OUT_BF16 && out_dtype != MXGEMM_OUT_F32)
+    return fail(MXFP4_EUNSUPPORTED, "out_dtype %d is not MXGEMM_OUT_BF16 or MXGEMM_OUT_F32", out_dtype);
+  MXFP4_TRY(check_ptr(c, out_dtype == MXGEMM_OUT_F32 ? 4 : 2, "c"));
+  if (ldc < N) return fail(MXFP4_EINVAL, "ldc %lld < N %lld", (long long)ldc, (long long)N);
+  if (M == 0 || N == 0) return ok();
+  if (rows && K == 0) return fail(MXFP4_EUNSUPPORTED, "K must be > 0 when groups split rows");
+  mxfp4::GemmLaunch L{};
+  L.group_type = group_type;
+  L.a_fmt = a->fmt;
+  L.b_fmt = b->fmt;
+  L.a_block = a->block;
+  L.b_block = b->block;
+  L.out_f32 = out_dtype == MXGEMM_OUT_F32;
+  L.M = M;
+  L.N = N;
+  L.K = K;
+  L.k_blocks = k_blocks;
+  L.a = static_cast<const uint8_t *>(a->data);
+  L.as = a->scales;
+  L.b = static_cast<const uint8_t *>(b->data);
+  L.bs = b->scales;
+  L.lda = a->ld;
+  L.ldas = a->ld_scales;
+  L.ldb = b->ld;
+  L.ldbs = b->ld_scales;
+  L.b_gs = rows ? b->group_stride : 0;
+  L.b_gss = rows ? b->group_stride_scales : 0;
+  L.ldc = ldc;
+  L.c = c;
+  L.group_list = group_list;
+  L.num_groups = group_list ? num_groups : 1;
+  L.list_type = group_list_type;
+  return hip_status(mxfp4::launch_mx_gemm(L, static_cast<hipStream_t>(stream)), "grouped matmul launch");
+}
+
 const char *mxfp4_last_error(void) { return g_last_error.c_str(); }
 
-int32_t mxfp4_version(void) { return 101; }
+int32_t mxfp4_version(void) { return 102; }
 
 }  // extern "C"

@@ -65,7 +65,8 @@ __device__ __forceinline__ int64_t scan_max_i64(int64_t v, int lane) {
 template <int NT>
 __device__ __forceinline__ void block_rows_walk(const int64_t *gl, int num_groups, int list_type,
                                                 int64_t rows, int block_log2, const int64_t (&t)[NT],
-                                                int64_t (&start)[NT], int64_t (&len)[NT]) {
+                                                int64_t (&start)[NT], int64_t (&len)[NT],
+                                                int (&grp)[NT]) {
   const int lane = (int)__lane_id();
   const int64_t B = (int64_t)1 << block_log2;
   int64_t prev_end = 0, cum = 0, brow = 0;
@@ -74,6 +75,7 @@ __device__ __forceinline__ void block_rows_walk(const int64_t *gl, int num_group
   for (int i = 0; i < NT; ++i) {
     start[i] = 0;
     len[i] = 0;
+    grp[i] = 0;
   }
   for (int base = 0; base < num_groups && left > 0; base += 64) {
     const int g = base + lane;
@@ -97,6 +99,7 @@ __device__ __forceinline__ void block_rows_walk(const int64_t *gl, int num_group
           start[i] = prev_end + ((t[i] - brow) << block_log2);
           const int64_t rem = end - start[i];
           len[i] = rem < B ? rem : B;
+          grp[i] = base + j;
           --left;
         }
       }
@@ -107,13 +110,15 @@ __device__ __forceinline__ void block_rows_walk(const int64_t *gl, int num_group
 }
 
 // Wave-uniform lookup of NT block-rows t[0..NT-1] (wave-uniform values):
-// start[i], len[i] (len 0 past the last block-row).
+// start[i], len[i] (len 0 past the last block-row) and the group grp[i]
+// holding it.
 template <int NT>
 __device__ __forceinline__ void block_rows_lookup(const int64_t *gl, int num_groups, int list_type,
                                                   int64_t rows, int block_log2, const int64_t (&t)[NT],
-                                                  int64_t (&start)[NT], int64_t (&len)[NT]) {
+                                                  int64_t (&start)[NT], int64_t (&len)[NT],
+                                                  int (&grp)[NT]) {
   if (num_groups <= MXFP4_GROUP_WALK_MAX) {
-    block_rows_walk<NT>(gl, num_groups, list_type, rows, block_log2, t, start, len);
+    block_rows_walk<NT>(gl, num_groups, list_type, rows, block_log2, t, start, len, grp);
     return;
   }
   const int lane = (int)__lane_id();
@@ -124,6 +129,7 @@ __device__ __forceinline__ void block_rows_lookup(const int64_t *gl, int num_gro
   for (int i = 0; i < NT; ++i) {
     start[i] = 0;
     len[i] = 0;
+    grp[i] = 0;
     done[i] = false;
   }
   for (int base = 0; base < num_groups; base += 64) {
@@ -155,6 +161,7 @@ __device__ __forceinline__ void block_rows_lookup(const int64_t *gl, int num_gro
         start[i] = gprev + ((t[i] - gfirst) << block_log2);
         const int64_t rem = gend - start[i];
         len[i] = rem < B ? rem : B;
+        grp[i] = base + gi;
         done[i] = true;
       }
     }
@@ -163,15 +170,55 @@ __device__ __forceinline__ void block_rows_lookup(const int64_t *gl, int num_gro
   }
 }
 
-// One block-row.
+// One block-row (and optionally the group holding it).
 __device__ __forceinline__ void block_row_uniform(const int64_t *gl, int num_groups, int list_type,
                                                   int64_t rows, int block_log2, int64_t t,
-                                                  int64_t *start, int64_t *len) {
+                                                  int64_t *start, int64_t *len, int *group = nullptr) {
   const int64_t tt[1] = {t};
   int64_t s[1], l[1];
-  block_rows_lookup<1>(gl, num_groups, list_type, rows, block_log2, tt, s, l);
+  int g[1];
+  block_rows_lookup<1>(gl, num_groups, list_type, rows, block_log2, tt, s, l, g);
   *start = s[0];
   *len = l[0];
+  if (group) *group = g[0];
+}
+
+// Span of group g in a layout where every group starts on a block boundary
+// (ceil(c_h / block) blocks per group h, numbered group by group): first
+// block *kb_start and block count *nb (0 for an empty group or g past the
+// list).  Ends are clamped as above; wave-uniform.
+__device__ __forceinline__ void group_block_span(const int64_t *gl, int num_groups, int list_type,
+                                                 int64_t rows, int block_log2, int g,
+                                                 int64_t *kb_start, int64_t *nb_out) {
+  const int lane = (int)__lane_id();
+  const int64_t B = (int64_t)1 << block_log2;
+  int64_t carry_end = 0, carry_blk = 0;
+  *kb_start = 0;
+  *nb_out = 0;
+  for (int base = 0; base < num_groups && base <= g; base += 64) {
+    const int gg = base + lane;
+    const bool valid = gg < num_groups;
+    const int64_t raw = valid ? gl[gg] : 0;
+    int64_t end;
+    if (list_type == 1) {
+      end = carry_end + scan_add_i64(valid && raw > 0 ? raw : 0, lane);
+    } else {
+      end = scan_max_i64(valid ? raw : 0, lane);
+      end = end > carry_end ? end : carry_end;
+    }
+    end = end < rows ? end : rows;
+    int64_t prev = shfl_up_i64(end, 1);
+    if (lane == 0) prev = carry_end;
+    const int64_t nb = valid ? (end - prev + B - 1) >> block_log2 : 0;
+    const int64_t cum = carry_blk + scan_add_i64(nb, lane);
+    if (g < base + 64) {
+      *kb_start = lane_i64(cum - nb, g - base);
+      *nb_out = lane_i64(nb, g - base);
+      return;
+    }
+    carry_end = lane_i64(end, 63);
+    carry_blk = lane_i64(cum, 63);
+  }
 }
 
 }  // namespace mxfp4

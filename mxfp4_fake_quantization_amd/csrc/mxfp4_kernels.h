@@ -88,4 +88,20 @@ struct Mx8Launch {
 };
 hipError_t launch_mxfp8_rows(const Mx8Launch &L, hipStream_t stream);
 
+// Grouped MX matrix product C = A . B^T (both operands K-contiguous).
+// Element formats as the MFMA format codes: 0 E4M3, 1 E5M2, 4 E2M1.
+enum { kFmtE4M3 = 0, kFmtE5M2 = 1, kFmtE2M1 = 4 };
+struct GemmLaunch {
+  int group_type;        // 0: groups split rows of A (B per group); 2: groups split K
+  int a_fmt, b_fmt, a_block, b_block, out_f32;
+  int64_t M, N, K, k_blocks;
+  const uint8_t *a, *as;  // [M, lda] codes, [M, ldas] E8M0
+  const uint8_t *b, *bs;  // [N, ldb] codes, [N, ldbs] E8M0 (+ g * b_gs / b_gss)
+  int64_t lda, ldas, ldb, ldbs, b_gs, b_gss, ldc;
+  void *c;
+  const int64_t *group_list;
+  int num_groups, list_type;
+};
+hipError_t launch_mx_gemm(const GemmLaunch &L, hipStream_t stream);
+
 }  // namespace mxfp4

@@ -1,0 +1,362 @@
+// mxgemm_kernels.hip -- grouped MX matrix product on gfx950 scaled MFMA.
+//
+// The hyper-parallel page's FakeW4A8GroupedLinear hands its directional
+// operands to a grouped matmul in three layouts: NN (forward: tokens x the
+// column-wise weight view), NT (input gradient: grad_output x the row-wise
+// weight view, transposed) and TN (weight gradient: column-wise x^T times
+// column-wise grad_output, per expert).  With both operands stored with the
+// reduction dimension K contiguous, all three are one product per group,
+//     C[m, n] = sum_k A[m, k] * B[n, k],
+// where A is MXFP8 (E4M3 / E5M2 bytes + E8M0 per 32 or 128 along K) and B is
+// MXFP4 (E2M1 nibble pairs, low nibble = even K) or MXFP8.  Groups either
+// split the rows of A and pick B_g (NN / NT), or split K into block-aligned
+// spans with one output matrix per group (TN).
+//
+// One v_mfma_scale_f32_32x32x64_f8f6f4 multiplies a 32x64 A slice by a 64x32
+// B slice, applying the E8M0 scales of both in the matrix core: lane l
+// supplies row / column l % 32 and K half h = l / 32, one scale byte per lane
+// for K-block h.  Measured operand layout of the instruction (A fp8: bytes
+// 0-15 are K 16h..16h+15, bytes 16-31 are K 32+16h..; B fp4: nibble j is K
+// 32h+j; result register v of lane l is row 8(v/4) + 4h + v%4, column l%32).
+//
+// Work split: a 256-thread workgroup computes a (64 WM) x (64 WN) tile as
+// 2 x 2 waves of WM x WN MFMA tiles, stepping K by 128.  Both operand slices
+// go global -> registers -> LDS (double-buffered, XOR-swizzled 16-byte
+// slots, conflict-free for 16- and 32-lane read phases) while the previous
+// step's MFMAs run; scale bytes are read per lane straight from global
+// memory.  Blocks past a K range load as zero codes with scale 2^0, rows and
+// columns past the tile edge load a valid neighbour and are not stored.
+#include "mxfp4_device.h"
+#include "mxfp4_groups.h"
+#include "mxfp4_kernels.h"
+
+namespace mxfp4 {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGemmThreads = 256;
+
+struct GemmArgs {
+  const uint8_t *a, *as, *b, *bs;
+  void *c;
+  int64_t lda, ldas, ldb, ldbs, b_gs, b_gss, ldc;
+  int64_t M, N, K;
+  int64_t k_blocks;      // reduction-split groups: K-block capacity of the operands
+  const int64_t *gl;
+  int G, list_type, group_type, out_f32;
+  int a_sb, b_sb;        // log2(scale block / 32): 0 or 2
+  int64_t tiles_m, tiles_n, total;
+};
+
+// slot swizzles: conflict-free ds_read_b128 for 8 or 16 consecutive rows
+__device__ __forceinline__ int swz_a(int r, int c) { return (c ^ ((r ^ (r >> 3)) & 7)) << 4; }
+__device__ __forceinline__ int swz_b4(int n, int c) { return (c ^ (((n >> 1) ^ (n >> 2)) & 3)) << 4; }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Workgroup id -> tile id such that each XCD (workgroups are dealt to the 8
+// XCDs round-robin) runs a contiguous range of tiles and shares its L2.
+__device__ __forceinline__ int64_t xcd_tile(int64_t id, int64_t total) {
+  const int64_t q = total >> 3, r = total & 7;
+  const int64_t x = id & 7, loc = id >> 3;
+  return x < r ? x * (q + 1) + loc : r * (q + 1) + (x - r) * q + loc;
+}
+
+template <int AF, int BF, int WM, int WN>
+__global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
+  constexpr int BM = 64 * WM, BN = 64 * WN;
+  constexpr bool B4 = BF == kFmtE2M1;
+  constexpr int BROW = B4 ? 64 : 128;        // B bytes per row per K step
+  constexpr int A_LD = BM / 32;              // 16-byte A loads per thread per step
+  constexpr int B_LD = B4 ? BN / 64 : BN / 32;
+  __shared__ __align__(16) uint8_t sA[2][BM * 128];
+  __shared__ __align__(16) uint8_t sB[2][BN * BROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int64_t tile = xcd_tile(blockIdx.x, P.total);
+
+  // ---- tile -> rows, columns, K range, operand and output bases ----
+  int64_t m0, mlen, n0, kb0, kb1;
+  const uint8_t *bbase = P.b, *bsbase = P.bs;
+  int64_t cbase = 0;  // element offset of the output matrix
+  if (P.group_type == 0) {
+    const int64_t tm = tile / P.tiles_n;
+    n0 = (tile - tm * P.tiles_n) * BN;
+    int g = 0;
+    if (P.gl) {
+      block_row_uniform(P.gl, P.G, P.list_type, P.M, __builtin_ctz(BM), tm, &m0, &mlen, &g);
+    } else {
+      m0 = tm * BM;
+      mlen = P.M - m0 < BM ? P.M - m0 : BM;
+    }
+    if (mlen <= 0) return;  // past the groups' total (workgroup-uniform)
+    bbase += (int64_t)g * P.b_gs;
+    bsbase += (int64_t)g * P.b_gss;
+    kb0 = 0;
+    kb1 = (P.K + 31) >> 5;
+  } else {
+    const int64_t per = P.tiles_m * P.tiles_n;
+    const int g = (int)(tile / per);
+    const int64_t r = tile - (int64_t)g * per;
+    const int64_t tm = r / P.tiles_n;
+    m0 = tm * BM;
+    mlen = P.M - m0 < BM ? P.M - m0 : BM;
+    n0 = (r - tm * P.tiles_n) * BN;
+    int64_t nb;
+    group_block_span(P.gl, P.G, P.list_type, P.K, 5, g, &kb0, &nb);
+    kb1 = kb0 + nb < P.k_blocks ? kb0 + nb : P.k_blocks;
+    if (kb0 > kb1) kb0 = kb1;
+    cbase = (int64_t)g * P.M * P.ldc;
+  }
+  const int64_t nlen = P.N - n0 < BN ? P.N - n0 : BN;
+
+  // ---- per-thread load offsets (32-bit, from per-tile bases) ----
+  const uint8_t *abase = P.a + m0 * P.lda;
+  const uint8_t *asbase = P.as + m0 * P.ldas;
+  bbase += n0 * P.ldb;
+  bsbase += n0 * P.ldbs;
+  const int ar = tid >> 3, ac = tid & 7;                 // A: 32 rows x 8 slots per pass
+  const int br = B4 ? tid >> 2 : tid >> 3;               // B: 64 x 4 (fp4) / 32 x 8 (fp8)
+  const int bc = B4 ? tid & 3 : tid & 7;
+  uint32_t aoff[A_LD], boff[B_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int row = ar + 32 * i;
+    aoff[i] = (uint32_t)((row < mlen ? row : mlen - 1) * P.lda) + 16 * ac;
+  }
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int row = br + (B4 ? 64 : 32) * i;
+    boff[i] = (uint32_t)((row < nlen ? row : nlen - 1) * P.ldb) + 16 * bc;
+  }
+  // scale rows of this lane's MFMA tiles
+  const int wr0 = (wave >> 1) * 32 * WM, wc0 = (wave & 1) * 32 * WN;
+  uint32_t asoff[WM], bsoff[WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+    const int row = wr0 + 32 * i + l32;
+    asoff[i] = (uint32_t)((row < mlen ? row : mlen - 1) * P.ldas);
+  }
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    const int row = wc0 + 32 * j + l32;
+    bsoff[j] = (uint32_t)((row < nlen ? row : nlen - 1) * P.ldbs);
+  }
+
+  u32x4 ra[A_LD], rb[B_LD];
+  uint32_t sa[WM], sb[WN];  // byte s: scale of K-block 2s + h of the step
+  uint8_t xa[WM][2], xb[WN][2];
+  bool in0 = false, in1 = false, ain = false, bin = false;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+  // K step starting at block kb: global -> registers (codes) and scale bytes.
+  // Blocks at or past kb1 read block kb1 - 1 (in bounds) and are replaced by
+  // zero codes / scale 2^0, so the loads carry no branches.
+  auto load_step = [&](int64_t kb) {
+    const int64_t last = kb1 - 1;
+    // one block per thread slot: 16-byte slot ac of A holds K 16ac..16ac+15,
+    // slot bc of B holds K 32bc.. (fp4) or 16bc.. (fp8)
+    const int64_t ablk = kb + (ac >> 1), bblk = B4 ? kb + bc : kb + (bc >> 1);
+    ain = ablk < kb1;
+    bin = bblk < kb1;
+    const int64_t at = ain ? (kb << 5) : (last << 5) - 16 * ac;
+    const int64_t bt = bin ? (kb << (B4 ? 4 : 5)) : (B4 ? (last << 4) - 16 * bc : (last << 5) - 16 * bc);
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4 *>(abase + at + aoff[i]);
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) rb[i] = *reinterpret_cast<const u32x4 *>(bbase + bt + boff[i]);
+    const int64_t b0 = kb + h, b1 = kb + 2 + h;
+    in0 = b0 < kb1;
+    in1 = b1 < kb1;
+    const uint8_t *as0 = asbase + ((in0 ? b0 : last) >> P.a_sb), *as1 = asbase + ((in1 ? b1 : last) >> P.a_sb);
+    const uint8_t *bs0 = bsbase + ((in0 ? b0 : last) >> P.b_sb), *bs1 = bsbase + ((in1 ? b1 : last) >> P.b_sb);
+#pragma unroll
+    for (int i = 0; i < WM; ++i) xa[i][0] = as0[asoff[i]], xa[i][1] = as1[asoff[i]];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) xb[j][0] = bs0[bsoff[j]], xb[j][1] = bs1[bsoff[j]];
+  };
+  // raw scale bytes -> one register per tile (byte s: K-block 2s + h);
+  // done after the MFMAs so that their wait does not stall the step
+  auto finish_scales = [&]() {
+#pragma unroll
+    for (int i = 0; i < WM; ++i) sa[i] = (in0 ? (uint32_t)xa[i][0] : 127u) | ((in1 ? (uint32_t)xa[i][1] : 127u) << 8);
+#pragma unroll
+    for (int j = 0; j < WN; ++j) sb[j] = (in0 ? (uint32_t)xb[j][0] : 127u) | ((in1 ? (uint32_t)xb[j][1] : 127u) << 8);
+  };
+  auto store_step = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      const int row = ar + 32 * i;
+      *reinterpret_cast<u32x4 *>(&sA[buf][row * 128 + swz_a(row, ac)]) = ain ? ra[i] : zero4;
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const int row = br + (B4 ? 64 : 32) * i;
+      const int off = B4 ? row * 64 + swz_b4(row, bc) : row * 128 + swz_a(row, bc);
+      *reinterpret_cast<u32x4 *>(&sB[buf][off]) = bin ? rb[i] : zero4;
+    }
+  };
+
+  v16f acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int64_t nsteps = (kb1 - kb0 + 3) >> 2;
+  uint32_t csa[WM], csb[WN];  // scales of the step being computed
+  if (nsteps > 0) {
+    load_step(kb0);
+    finish_scales();
+    store_step(0);
+  }
+  __syncthreads();
+  for (int64_t st = 0; st < nsteps; ++st) {
+    const int buf = (int)(st & 1);
+#pragma unroll
+    for (int i = 0; i < WM; ++i) csa[i] = sa[i];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) csb[j] = sb[j];
+    // prefetch the next step (the last iteration re-reads clamped, in-bounds
+    // blocks that are never used: no branch splits the loop body)
+    load_step(kb0 + 4 * (st + 1));
+
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      v8i fa[WM], fb[WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        const int r = wr0 + 32 * i + l32;
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(&sA[buf][r * 128 + swz_a(r, 4 * s + h)]);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(&sA[buf][r * 128 + swz_a(r, 4 * s + 2 + h)]);
+        fa[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int n = wc0 + 32 * j + l32;
+        if (B4) {
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(&sB[buf][n * 64 + swz_b4(n, 2 * s + h)]);
+          fb[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        } else {
+          const u32x4 lo = *reinterpret_cast<const u32x4 *>(&sB[buf][n * 128 + swz_a(n, 4 * s + h)]);
+          const u32x4 hi = *reinterpret_cast<const u32x4 *>(&sB[buf][n * 128 + swz_a(n, 4 * s + 2 + h)]);
+          fb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fa[i], fb[j], acc[i][j], AF, BF, 0, (int)((csa[i] >> (8 * s)) & 0xFFu), 0,
+              (int)((csb[j] >> (8 * s)) & 0xFFu));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the waits for the prefetch after the MFMAs
+    finish_scales();
+    store_step(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: row 8(v/4) + 4h + v%4, column l32 of each 32x32 tile ----
+  auto store = [&](int64_t off, float v) {
+    if (P.out_f32) static_cast<float *>(P.c)[off] = v;
+    else static_cast<uint16_t *>(P.c)[off] = f32_to_bf16_rne(v);
+  };
+  const int64_t cb = cbase + m0 * P.ldc + n0;
+  if (mlen == BM && nlen == BN) {
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wr0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          store(cb + row * P.ldc + wc0 + 32 * j + l32, acc[i][j][v]);
+        }
+  } else {
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int col = wc0 + 32 * j + l32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wr0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (row < mlen && col < nlen) store(cb + row * P.ldc + col, acc[i][j][v]);
+        }
+      }
+  }
+}
+
+template <int AF, int BF>
+hipError_t gemm_launch(const GemmArgs &a0, hipStream_t st) {
+  constexpr int WM = 4, WN = 4;
+  GemmArgs a = a0;
+  const int64_t BM = 64 * WM, BN = 64 * WN;
+  a.tiles_n = (a.N + BN - 1) / BN;
+  if (a.group_type == 0) {
+    // upper bound of the M tiles: every group adds at most one partial tile
+    a.tiles_m = (a.M + BM - 1) / BM + (a.gl ? a.G : 0);
+    a.total = a.tiles_m * a.tiles_n;
+  } else {
+    a.tiles_m = (a.M + BM - 1) / BM;
+    a.total = a.tiles_m * a.tiles_n * a.G;
+  }
+  if (a.total <= 0) return hipSuccess;
+  if (a.total > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((mxgemm_kernel<AF, BF, WM, WN>), dim3((unsigned)a.total), dim3(kGemmThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int AF>
+hipError_t gemm_launch_b(int bf, const GemmArgs &a, hipStream_t st) {
+  switch (bf) {
+    case kFmtE4M3: return gemm_launch<AF, kFmtE4M3>(a, st);
+    case kFmtE5M2: return gemm_launch<AF, kFmtE5M2>(a, st);
+    default: return gemm_launch<AF, kFmtE2M1>(a, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mx_gemm(const GemmLaunch &L, hipStream_t st) {
+  GemmArgs a{};
+  a.a = L.a;
+  a.as = L.as;
+  a.b = L.b;
+  a.bs = L.bs;
+  a.c = L.c;
+  a.lda = L.lda;
+  a.ldas = L.ldas;
+  a.ldb = L.ldb;
+  a.ldbs = L.ldbs;
+  a.b_gs = L.b_gs;
+  a.b_gss = L.b_gss;
+  a.ldc = L.ldc;
+  a.M = L.M;
+  a.N = L.N;
+  a.K = L.K;
+  a.k_blocks = L.k_blocks;
+  a.gl = L.group_list;
+  a.G = L.num_groups;
+  a.list_type = L.list_type;
+  a.group_type = L.group_type;
+  a.out_f32 = L.out_f32;
+  a.a_sb = L.a_block == 128 ? 2 : 0;
+  a.b_sb = L.b_block == 128 ? 2 : 0;
+  return L.a_fmt == kFmtE4M3 ? gemm_launch_b<kFmtE4M3>(L.b_fmt, a, st) : gemm_launch_b<kFmtE5M2>(L.b_fmt, a, st);
+}
+
+}  // namespace mxfp4

@@ -24,6 +24,12 @@ class Desc(ctypes.Structure):
                 ("scale_factor", ctypes.c_float), ("reserved1", ctypes.c_int32)]
 
 
+class Operand(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("fmt", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("ld", ctypes.c_int64), ("ld_scales", ctypes.c_int64),
+                ("group_stride", ctypes.c_int64), ("group_stride_scales", ctypes.c_int64)]
+
+
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
@@ -38,6 +44,9 @@ def lib():
     L.mxfp4_quant_pack_kmajor.argtypes = [dp, vp, vp, i32, i32, ctypes.c_int64, vp, vp, vp]
     L.mxfp4_dequant.argtypes = [dp, vp, vp, vp, vp]
     L.mxfp8_quant.argtypes = [dp, i32, vp, vp, vp, vp]
+    i64 = ctypes.c_int64
+    op = ctypes.POINTER(Operand)
+    L.mxfp4_grouped_matmul.argtypes = [i32, i64, i64, i64, op, op, vp, i32, i32, i64, i32, vp, i64, vp]
     L.mxfp4_last_error.restype = ctypes.c_char_p
     return L
 
@@ -50,15 +59,15 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
-              "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant", "mxfp4_last_error",
-              "mxfp4_version"):
+              "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant", "mxfp4_grouped_matmul",
+              "mxfp4_last_error", "mxfp4_version"):
         assert n in names
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mxfp4_version() == 101
+    assert lib.mxfp4_version() == 102
 
 
 def d(dtype=BF16, block=32, rule=0, rows=64, cols=64, sf=6.0, r0=0, r1=0):
@@ -187,6 +196,44 @@ def test_mxfp8_validation(lib):
     assert m8(0, x, q, s, None) == EUNSUP                   # MX blocks are 32
     D.block, D.rows = 32, 0
     assert m8(1, x, q, s, None) == OK
+
+
+def test_grouped_matmul_validation(lib):
+    """Every bad argument is refused on the host; M == 0 or N == 0 returns OK
+    without a launch."""
+    def ops(afmt=0, bfmt=4, ab=32, bb=32, lda=256, ldas=8, ldb=128, ldbs=8, gs=0, gss=0, adata=FAKE):
+        return (Operand(adata, FAKE + 65536, afmt, ab, lda, ldas, 0, 0),
+                Operand(FAKE + 131072, FAKE + 196608, bfmt, bb, ldb, ldbs, gs, gss))
+
+    def mm(gt=0, M=64, N=64, K=256, a=None, b=None, gl=None, ng=0, lt=1, kb=0, out=0, c=FAKE + 262144,
+           ldc=64):
+        if a is None:
+            a, b = ops()
+        return lib.mxfp4_grouped_matmul(gt, M, N, K, ctypes.byref(a), ctypes.byref(b),
+                                        None if gl is None else P(gl), ng, lt, kb, out, P(c), ldc, None)
+
+    assert mm(gt=1) == EINVAL                                   # unknown group_type
+    assert mm(K=100) == EINVAL                                  # K not a multiple of 32
+    assert mm(M=-1) == EINVAL
+    assert mm(*(), **{"a": ops(afmt=4)[0], "b": ops()[1]}) == EUNSUP   # A must be fp8
+    assert mm(a=ops()[0], b=ops(bfmt=2)[1]) == EUNSUP           # unknown B format
+    assert mm(a=ops(ab=64)[0], b=ops()[1]) == EUNSUP            # scale block 64
+    assert mm(a=ops(lda=255)[0], b=ops()[1]) == EINVAL          # ld not a multiple of 16
+    assert mm(a=ops(lda=240)[0], b=ops()[1]) == EINVAL          # ld shorter than K bytes
+    assert mm(a=ops()[0], b=ops(ldb=112)[1]) == EINVAL          # fp4 row is K/2 bytes
+    assert mm(a=ops(ldas=7)[0], b=ops()[1]) == EINVAL           # too few scale bytes
+    assert mm(a=ops(adata=FAKE + 8)[0], b=ops()[1]) == EINVAL   # misaligned data
+    assert mm(a=ops()[0], b=ops(gs=8)[1]) == EINVAL             # group stride not 16-aligned
+    assert mm(out=2) == EUNSUP
+    assert mm(c=FAKE + 1) == EINVAL                             # misaligned output
+    assert mm(ldc=63) == EINVAL
+    assert mm(gl=FAKE, ng=0) == EINVAL                          # list without groups
+    assert mm(gl=FAKE, ng=2, lt=3) == EINVAL
+    assert mm(gt=2, gl=None, kb=8) == EINVAL                    # K-split needs a list
+    a, b = ops(ab=128, bb=128)
+    assert mm(gt=2, a=a, b=b, gl=FAKE, ng=1, kb=8) == EUNSUP     # K-split needs blocks of 32
+    assert mm(gt=2, gl=FAKE, ng=1, kb=8, a=ops(lda=240)[0], b=ops()[1]) == EINVAL  # ld < k_blocks*32
+    assert mm(M=0) == OK and mm(N=0) == OK                       # nothing to launch
 
 
 def test_python_binding_refuses_cpu_tensors():

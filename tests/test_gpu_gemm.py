@@ -1,0 +1,311 @@
+"""GPU parity of the grouped MX matmul (C = A . B^T per group, A MXFP8, B MXFP4
+or MXFP8) through the C-ABI binding, against the oracle's grouped product of
+decoded operands.
+
+Exact cases: operand codes and scales drawn so that every partial sum is a
+multiple of one power of two below 2^24 of it, so any fp32 summation order
+is exact and the GPU result must equal the oracle bit for bit (fp32 output)
+or its bf16 rounding (bf16 output).  Realistic cases: operands from the
+oracle's quantizers (MXFP8 rows of activations / grad_output, K-major or
+row-packed MXFP4 weights), compared within the fp32 summation bound
+|err| <= K * 2^-24 * sum_k |a_k b_k| (plus half a bf16 ulp for bf16 output).
+Covered: rows-split groups (counts and cumulative ends, empty groups, a
+total short of M with untouched rows, 40 groups), no group list, K tails
+that are not a multiple of the 128-wide K step, 128-element scale blocks,
+E5M2 / E4M3 / E2M1 operands, K-split groups (TN) with padded spans, and the
+full-size MoE forward on sampled outputs."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import Guarded, dev, host
+
+pytestmark = pytest.mark.gpu
+
+M_ = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    global M_
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mxfp4_fake_quantization_amd as mod
+    mod._load()
+    M_ = mod
+    yield
+
+
+# ---- operand decoding through the oracle ---------------------------------------
+
+def expand_scales(s, block, K):
+    """per-block scales -> per-32 scales over K (the oracle decoders take 32)."""
+    if block == 32:
+        return np.ascontiguousarray(s[..., : -(-K // 32)])
+    return np.ascontiguousarray(np.repeat(s, block // 32, axis=-1)[..., : -(-K // 32)])
+
+
+def decode(oracle, codes, scales, fmt, block, K):
+    """[rows, K] float64 values of a K-contiguous operand."""
+    rows = codes.shape[0]
+    if fmt == "e2m1":
+        return oracle.unpack_rows(np.ascontiguousarray(codes[:, : K // 2]), np.ascontiguousarray(
+            scales[:, : -(-K // block)]), K, block, np.float64)
+    return oracle.mxfp8_decode(np.ascontiguousarray(codes[:, :K]), expand_scales(scales, block, K), fmt,
+                               np.float64).reshape(rows, K)
+
+
+# ---- exact operands ------------------------------------------------------------
+
+def exact_fp8_codes(g, shape, fmt, max_exp_steps=4):
+    """fp8 codes of magnitude 0 or in [1, 16) (E4M3: multiples of 1/8; E5M2: 1/4), random sign."""
+    if fmt == "e4m3":
+        mags = [0] + [(e << 3) | m for e in range(7, 7 + max_exp_steps) for m in range(8)]
+    else:
+        mags = [0] + [(e << 2) | m for e in range(15, 15 + max_exp_steps) for m in range(4)]
+    c = np.asarray(mags, np.uint8)[g.integers(0, len(mags), shape)]
+    return c | (g.integers(0, 2, shape).astype(np.uint8) << 7)
+
+
+def exact_operands(g, rows, K, fmt, block, lo=126, hi=128, ld=None, groups=None, steps=4):
+    kb = -(-K // block)
+    ld_bytes = (K // 2 if fmt == "e2m1" else K) if ld is None else ld
+    lead = () if groups is None else (groups,)
+    if fmt == "e2m1":
+        codes = g.integers(0, 256, lead + (rows, ld_bytes)).astype(np.uint8)
+    else:
+        codes = exact_fp8_codes(g, lead + (rows, ld_bytes), fmt, steps)
+    scales = g.integers(lo, hi + 1, lead + (rows, kb)).astype(np.uint8)
+    return codes, scales
+
+
+def run_rows(a, sa, b, sb, M, N, K, gl=None, lt=1, a_fmt="e4m3", b_fmt="e2m1", a_block=32, b_block=32,
+             out=torch.float32):
+    c = Guarded((M, N), out, fill=0x7F)
+    # a device list: the binding passes it as is (a total short of M is allowed)
+    gld = None if gl is None else torch.tensor(list(gl), dtype=torch.int64, device="cuda")
+    M_.mxfp4_grouped_matmul(dev(a), dev(sa), dev(b), dev(sb), c.t, K=K,
+                            group_list=gld, group_list_type=lt,
+                            a_fmt=a_fmt, b_fmt=b_fmt, a_block=a_block, b_block=b_block)
+    torch.cuda.synchronize()
+    c.check_tail()
+    return host(c.t)
+
+
+def oracle_rows(oracle, a, sa, b, sb, M, N, K, gl, lt, a_fmt, b_fmt, a_block, b_block):
+    A = decode(oracle, a, sa, a_fmt, a_block, K)
+    if b.ndim == 2:
+        b, sb = b[None], sb[None]
+    Bv = np.stack([decode(oracle, b[i], sb[i], b_fmt, b_block, K).T for i in range(b.shape[0])])
+    if gl is None:
+        return oracle.grouped_matmul(A, Bv[0][None], None, oracle.GROUP_M)
+    G = len(gl)
+    return oracle.grouped_matmul(A, Bv[:G], gl, oracle.GROUP_M, lt)
+
+
+def bf16_of(x64):
+    return W.f32_to_bf16_bits(x64.astype(np.float32))
+
+
+ROWS_CASES = [
+    # name, M, N, K, group list, list type, a fmt, b fmt, a block, b block
+    ("counts_empty_group", 300, 200, 256, [100, 0, 137, 63], 1, "e4m3", "e2m1", 32, 32),
+    ("ends_short_total", 250, 96, 128, [50, 50, 180], 0, "e4m3", "e2m1", 32, 32),
+    ("no_list_k_tail", 257, 33, 96, None, 1, "e4m3", "e2m1", 32, 32),
+    ("block128_both", 130, 260, 384, [64, 66], 1, "e4m3", "e2m1", 128, 128),
+    ("block128_a_k_tail", 70, 64, 160, None, 1, "e4m3", "e2m1", 128, 32),
+    ("e5m2_a", 200, 130, 192, [1, 198, 1], 1, "e5m2", "e2m1", 32, 32),
+    ("fp8_b_e4m3", 180, 140, 256, [90, 90], 1, "e4m3", "e4m3", 32, 32),
+    ("fp8_b_e5m2", 100, 50, 64, [30, 70], 1, "e4m3", "e5m2", 32, 32),
+    ("tiny", 1, 1, 32, None, 1, "e4m3", "e2m1", 32, 32),
+    ("forty_groups", 700, 72, 128, "forty", 1, "e4m3", "e2m1", 32, 32),
+]
+
+
+@pytest.mark.parametrize("case", ROWS_CASES, ids=[c[0] for c in ROWS_CASES])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_rows_split_exact(oracle, case, out):
+    name, M, N, K, gl, lt, af, bf, ab, bb = case
+    g = np.random.default_rng(zlib.crc32(name.encode()))
+    if gl == "forty":
+        gl = W.ragged_counts(M, 40, seed=3, zero_groups=6).tolist()
+    G = 1 if gl is None else len(gl)
+    # fp8 x fp8: scales >= 2^0 and magnitudes < 4 keep every partial sum exact in fp32
+    lo, steps = (127, 2) if bf != "e2m1" else (126, 4)
+    a, sa = exact_operands(g, M, K, af, ab, lo=lo, steps=steps)
+    b, sb = exact_operands(g, N, K, bf, bb, lo=lo, groups=G, steps=steps)
+    if gl is None:
+        b, sb = b[0], sb[0]
+    otype = torch.float32 if out == "f32" else torch.bfloat16
+    got = run_rows(a, sa, b, sb, M, N, K, gl, lt, af, bf, ab, bb, otype)
+    exp = oracle_rows(oracle, a, sa, b, sb, M, N, K, gl, lt, af, bf, ab, bb)
+    covered = ~np.isnan(exp[:, 0])
+    if out == "f32":
+        assert np.array_equal(got[covered], exp[covered].astype(np.float32))
+        untouched = got[~covered].view(np.uint32)
+        assert (untouched == 0x7F7F7F7F).all()
+    else:
+        assert np.array_equal(got[covered], bf16_of(exp[covered]))
+        assert (got[~covered] == 0x7F7F).all()
+
+
+def test_rows_split_group_stride_override(oracle):
+    """Experts packed side by side along K in one [N, G*K/2] matrix (one K-major
+    pack of the stacked weights): B_g found through an explicit group stride."""
+    g = np.random.default_rng(11)
+    M, N, K, G = 160, 96, 128, 3
+    gl = [40, 70, 50]
+    a, sa = exact_operands(g, M, K, "e4m3", 32)
+    b, sb = exact_operands(g, N, K * G, "e2m1", 32)        # [N, G*K/2], [N, G*K/32]
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    M_.mxfp4_grouped_matmul(dev(a), dev(sa), dev(b), dev(sb), c, K=K, group_list=gl,
+                            b_group_stride=(K // 2, K // 32))
+    torch.cuda.synchronize()
+    bg = np.stack([b[:, i * K // 2:(i + 1) * K // 2] for i in range(G)])
+    sg = np.stack([sb[:, i * K // 32:(i + 1) * K // 32] for i in range(G)])
+    exp = oracle_rows(oracle, a, sa, bg, sg, M, N, K, gl, 1, "e4m3", "e2m1", 32, 32)
+    assert np.array_equal(host(c), exp.astype(np.float32))
+
+
+# ---- K-split groups (TN) --------------------------------------------------------
+
+TN_CASES = [
+    # name, M, N, token counts, k_blocks, b fmt
+    ("fp8_fp8", 130, 70, [45, 0, 100, 31], 8, "e4m3"),
+    ("fp8_fp4", 64, 96, [32, 1, 95], 9, "e2m1"),
+    ("one_group_long", 40, 300, [600], 19, "e4m3"),
+    ("all_empty", 33, 20, [0, 0], 2, "e4m3"),
+]
+
+
+@pytest.mark.parametrize("case", TN_CASES, ids=[c[0] for c in TN_CASES])
+@pytest.mark.parametrize("lt", [1, 0])
+def test_k_split_exact(oracle, case, lt):
+    name, M, N, counts, kb, bf = case
+    g = np.random.default_rng(len(name) * 31 + M)
+    blocks = [-(-c // 32) for c in counts]
+    assert sum(blocks) <= kb
+    Kp = kb * 32
+    a, sa = exact_operands(g, M, Kp, "e4m3", 32, lo=127, steps=2)
+    b, sb = exact_operands(g, N, Kp, bf, 32, lo=127, steps=2)
+    # positions past each group's count inside its last block hold zero codes
+    pos = 0
+    for c, nb in zip(counts, blocks):
+        lo_, hi_ = 32 * pos + c, 32 * (pos + nb)
+        a[:, lo_:hi_] = 0
+        if bf == "e2m1":
+            bb = b.copy()
+            nib = np.stack([bb & 15, bb >> 4], -1).reshape(N, Kp)
+            nib[:, lo_:hi_] = 0
+            b = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+        else:
+            b[:, lo_:hi_] = 0
+        pos += nb
+    gl = counts if lt == 1 else np.cumsum(counts).tolist()
+    c = Guarded((len(counts), M, N), torch.float32, fill=0x7F)
+    M_.mxfp4_grouped_matmul(dev(a), dev(sa), dev(b), dev(sb), c.t, K=sum(counts), group_list=gl,
+                            group_type=M_.GROUP_K, group_list_type=lt, b_fmt=bf, k_blocks=kb)
+    torch.cuda.synchronize()
+    c.check_tail()
+    A = decode(oracle, a, sa, "e4m3", 32, Kp)
+    B = decode(oracle, b, sb, bf, 32, Kp)
+    padded = [32 * nb for nb in blocks]
+    exp = oracle.grouped_matmul(A, B.T.copy(), padded, oracle.GROUP_K, 1)
+    assert np.array_equal(host(c.t), exp.astype(np.float32))
+
+
+# ---- realistic operands from the oracle's quantizers ------------------------------
+
+def tol_check(got, exp, mag, K, bf16):
+    err = np.abs(got.astype(np.float64) - exp)
+    bound = K * 2.0 ** -24 * mag + 1e-30
+    if bf16:
+        bound = bound + np.abs(exp) * 2.0 ** -8
+    bad = err > bound
+    assert not bad.any(), f"{bad.sum()} outputs outside the bound; worst {np.max(err - bound)}"
+
+
+def test_nn_forward_from_quantizers(oracle):
+    """NN: MXFP8 rows of bf16 tokens times the K-major (column-wise) MXFP4 pack
+    of each expert's [K, N] weight."""
+    g = np.random.default_rng(21)
+    M, K, N, G = 384, 512, 192, 3
+    gl = [100, 200, 84]
+    x = W.f32_to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    w = W.f32_to_bf16_bits((g.standard_normal((G, K, N)) * 0.02).astype(np.float32))
+    q, sa = oracle.mxfp8_rows(x)
+    packs = [oracle.pack_kmajor(w[i], 32) for i in range(G)]
+    b = np.stack([p[0] for p in packs])
+    sb = np.stack([p[1] for p in packs])
+    for out in (torch.float32, torch.bfloat16):
+        got = run_rows(q, sa, b, sb, M, N, K, gl, 1, out=out)
+        A = decode(oracle, q, sa, "e4m3", 32, K)
+        Bv = np.stack([decode(oracle, b[i], sb[i], "e2m1", 32, K).T for i in range(G)])
+        exp = oracle.grouped_matmul(A, Bv, gl, oracle.GROUP_M)
+        mag = oracle.grouped_matmul(np.abs(A), np.abs(Bv), gl, oracle.GROUP_M)
+        if out == torch.bfloat16:
+            got = W.bf16_bits_to_f32(got)
+        tol_check(got, exp, mag, K, out == torch.bfloat16)
+
+
+def test_nt_input_grad_from_quantizers(oracle):
+    """NT: MXFP8 rows of grad_output [M, N] times the row-wise MXFP4 pack of
+    each expert's [K, N] weight (blocks along N), giving dX [M, K]."""
+    g = np.random.default_rng(22)
+    M, K, N, G = 200, 320, 256, 2
+    gl = [77, 123]
+    dy = W.f32_to_bf16_bits(g.standard_normal((M, N)).astype(np.float32))
+    w = W.f32_to_bf16_bits((g.standard_normal((G, K, N)) * 0.02).astype(np.float32))
+    q, sa = oracle.mxfp8_rows(dy)
+    packs = [oracle.pack_rows(w[i], 32) for i in range(G)]
+    b = np.stack([p[0] for p in packs])                      # [G, K, N/2]
+    sb = np.stack([p[1] for p in packs])                     # [G, K, N/32]
+    got = run_rows(q, sa, b, sb, M, K, N, gl, 1)
+    A = decode(oracle, q, sa, "e4m3", 32, N)
+    Bv = np.stack([decode(oracle, b[i], sb[i], "e2m1", 32, N).T for i in range(G)])
+    exp = oracle.grouped_matmul(A, Bv, gl, oracle.GROUP_M)
+    mag = oracle.grouped_matmul(np.abs(A), np.abs(Bv), gl, oracle.GROUP_M)
+    tol_check(got, exp, mag, N, False)
+
+
+def test_moe_forward_full_size_sampled(oracle):
+    """The MoE forward at full size (tokens 32768 x hidden 7168 in 8 experts,
+    expert width 2048): the GPU quantizes (MXFP8 rows, K-major MXFP4 weights)
+    and multiplies; sampled rows and columns are checked against the oracle
+    quantizing and multiplying the same rows and weight columns."""
+    x, counts = W.moe_grouped()
+    w = W.moe_expert_weights()
+    G, K, N = w.shape
+    Mt = x.shape[0]
+    xd = dev(x)
+    q = torch.empty((Mt, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((Mt, K // 32), dtype=torch.uint8, device="cuda")
+    M_.mxfp8_quant(xd, q, sa)
+    kb = K // 32
+    b = torch.empty((G, N, kb * 16), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((G, N, kb), dtype=torch.uint8, device="cuda")
+    for i in range(G):
+        M_.mxfp4_quant_pack_kmajor(dev(w[i]), b[i], sb[i], block=32)
+    c = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda")
+    M_.mxfp4_grouped_matmul(q, sa, b, sb, c, group_list=counts.tolist())
+    torch.cuda.synchronize()
+    rs = np.random.default_rng(12)
+    rows = np.sort(rs.choice(Mt, 48, replace=False))
+    cols = np.sort(rs.choice(N, 40, replace=False))
+    got = W.bf16_bits_to_f32(host(c[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]))
+    ends = np.cumsum(counts)
+    grp = np.searchsorted(ends, rows, side="right")
+    qo, so = oracle.mxfp8_rows(x[rows])
+    A = decode(oracle, qo, so, "e4m3", 32, K)
+    exp = np.empty((len(rows), len(cols)))
+    mag = np.empty_like(exp)
+    for gi in np.unique(grp):
+        sel = grp == gi
+        co, sco, _ = oracle.pack_kmajor(np.ascontiguousarray(w[gi][:, cols]), 32)
+        Bv = decode(oracle, co, sco, "e2m1", 32, K).T
+        exp[sel] = A[sel] @ Bv
+        mag[sel] = np.abs(A[sel]) @ np.abs(Bv)
+    tol_check(got, exp, mag, K, True)

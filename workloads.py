@@ -165,6 +165,14 @@ def weight_pack(seed: int = 5, rows: int = 28672, cols: int = 8192):
     return f32_to_bf16_bits(x)
 
 
+def moe_expert_weights(seed: int = 6, groups: int = 8, k: int = 7168, n: int = 2048):
+    """bf16 expert weights W[g] of shape [k, n] (x @ W[g]), ~ N(0, 0.02^2): the
+    weight side of the grouped MoE layer (hidden 7168 -> expert width 2048)."""
+    g = _rng(seed)
+    w = g.standard_normal((groups, k, n), dtype=np.float32) * np.float32(SIGMA_W)
+    return f32_to_bf16_bits(w)
+
+
 def ragged_counts(rows: int, groups: int, seed: int, zero_groups: int = 0) -> np.ndarray:
     """Random per-group row counts summing to `rows`, some groups empty."""
     g = _rng(seed)
