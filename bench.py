@@ -37,6 +37,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 matrix peak
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_fwd_weight4k_traffic.json")
 KERNEL_SOURCES = ["mxfp4_fake_quantization_amd/csrc/row_kernels.hip",
@@ -146,6 +147,8 @@ def main():
     ap.add_argument("--sets", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all", metavar="OUT", default=None)
+    ap.add_argument("--gemm", metavar="OUT", default=None,
+                    help="time only the grouped MX matmuls (NN / NT / TN of the MoE layer) into OUT")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a 512 MiB device copy (rocprofv3 counter calibration)")
     args = ap.parse_args()
@@ -168,6 +171,12 @@ def main():
         return
 
     lib = M._load()
+    if args.gemm:
+        res = bench_gemm(M, W, torch, {})
+        with open(args.gemm, "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res))
+        return
     x_np, g_np, _ = W.weight_4k()
     rows, cols = x_np.shape
     n = rows * cols
@@ -392,7 +401,74 @@ def bench_all(M, lib, W, torch, args):
     mcalls = [Call(lib.mxfp8_quant, ctypes.byref(d), 0, vp(xs[i].data_ptr()), vp(q8[i].data_ptr()),
                    vp(s8[i].data_ptr()), stream) for i in range(2)]
     rec("mxfp8_e4m3_32768x7168", R * C * (2 + 1 + 1 / 32), R * C, _time_calls(torch, mcalls, 30))
-    del xs, q8, s8
+    del xs
+
+    del q8, s8
+    bench_gemm(M, W, torch, out, gl, counts)
+    return out
+
+
+def bench_gemm(M, W, torch, out, gl=None, counts=None):
+    """Grouped MX matmul of the MoE layer (tokens 32768 x hidden 7168, 8
+    experts of width 2048): NN forward (MXFP8 rows x K-major MXFP4 weights),
+    NT input gradient and TN weight gradient, 2*M*K*N flops each."""
+    if counts is None:
+        xg, counts = W.moe_grouped()
+        gl = torch.from_numpy(counts).cuda()
+    else:
+        xg = W.moe_grouped()[0]
+    R, C = xg.shape
+    x = torch.from_numpy(xg).view(torch.bfloat16).cuda()
+    q8 = [torch.empty((R, C), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    s8 = [torch.empty((R, C // 32), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    for i in range(2):
+        M.mxfp8_quant(x, q8[i], s8[i])
+    del x
+
+    def tens(np_arr):
+        return torch.from_numpy(np_arr).view(torch.bfloat16).cuda()
+
+    def rec_mm(name, flops, t):
+        med, best = t
+        out[name] = {"flops": flops, "median_us": round(med * 1e6, 2), "best_us": round(best * 1e6, 2),
+                     "TFLOPs": round(flops / med / 1e12, 1),
+                     "pct_fp8_mfma_peak": round(100 * flops / med / 1e12 / MFMA_FP8_PEAK_TFLOPS, 2)}
+
+    wt = W.moe_expert_weights()
+    G, K, N = wt.shape
+    kbw = K // 32
+    bw = torch.empty((G, N, kbw * 16), dtype=torch.uint8, device="cuda")
+    sw = torch.empty((G, N, kbw), dtype=torch.uint8, device="cuda")
+    for i in range(G):
+        M.mxfp4_quant_pack_kmajor(tens(wt[i]), bw[i], sw[i], block=32)
+    cs = [torch.empty((R, N), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    gmm = [lambda i=i: M.mxfp4_grouped_matmul(q8[i], s8[i], bw, sw, cs[i], group_list=gl, group_list_type=1)
+           for i in range(2)]
+    rec_mm("gmm_nn_moe_32768x7168x2048_fp8xfp4", 2.0 * R * K * N, _time_calls(torch, gmm, 20))
+    # NT: grad_output [32768, 2048] (MXFP8) x row-wise MXFP4 weights [7168, 2048] -> dX [32768, 7168]
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    dq = torch.randint(0, 256, (R, N), dtype=torch.uint8, device="cuda", generator=gen) & 0xBF  # finite codes
+    ds = torch.full((R, N // 32), 120, dtype=torch.uint8, device="cuda")
+    bt = torch.randint(0, 256, (G, K, N // 2), dtype=torch.uint8, device="cuda", generator=gen)
+    st = torch.full((G, K, N // 32), 120, dtype=torch.uint8, device="cuda")
+    del cs
+    cx = [torch.empty((R, K), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    gmm = [lambda i=i: M.mxfp4_grouped_matmul(dq, ds, bt, st, cx[i], group_list=gl, group_list_type=1)
+           for i in range(2)]
+    rec_mm("gmm_nt_moe_32768x2048x7168_fp8xfp4", 2.0 * R * K * N, _time_calls(torch, gmm, 20))
+    del cx, bt, st
+    # TN: per expert x_g^T [7168, tokens_g] x dy_g [tokens_g, 2048], both MXFP8 K-major
+    nbt8 = int(sum(-(-int(c) // 32) for c in counts))
+    xa = torch.randint(0, 256, (K, nbt8 * 32), dtype=torch.uint8, device="cuda", generator=gen) & 0xBF
+    xs_ = torch.full((K, nbt8), 120, dtype=torch.uint8, device="cuda")
+    yb = torch.randint(0, 256, (N, nbt8 * 32), dtype=torch.uint8, device="cuda", generator=gen) & 0xBF
+    ys_ = torch.full((N, nbt8), 120, dtype=torch.uint8, device="cuda")
+    cw = [torch.empty((G, K, N), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    gmm = [lambda i=i: M.mxfp4_grouped_matmul(xa, xs_, yb, ys_, cw[i], K=R, group_list=gl, group_list_type=1,
+                                              group_type=M.GROUP_K, b_fmt="e4m3", k_blocks=nbt8)
+           for i in range(2)]
+    rec_mm("gmm_tn_moe_7168x2048_over_32768_fp8xfp8", 2.0 * R * K * N, _time_calls(torch, gmm, 20))
+    del q8, s8, cw, xa, yb
     return out
 
 

@@ -23,9 +23,13 @@
 // 2 x 2 waves of WM x WN MFMA tiles, stepping K by 128.  Both operand slices
 // go global -> registers -> LDS (double-buffered, XOR-swizzled 16-byte
 // slots, conflict-free for 16- and 32-lane read phases) while the previous
-// step's MFMAs run; scale bytes are read per lane straight from global
-// memory.  Blocks past a K range load as zero codes with scale 2^0, rows and
-// columns past the tile edge load a valid neighbour and are not stored.
+// step's MFMAs run.  Scale bytes travel in chunks of 32 K-blocks per tile row
+// (8 steps), also double-buffered in LDS and streamed one coalesced slice per
+// step, so every lane reads its scale bytes with one LDS load per tile.  The
+// loop body is one basic block: prefetch, MFMAs, then the prefetch waits and
+// LDS stores.  Blocks outside a K range load as zero codes with scale 2^0;
+// rows and columns past the tile edge load a valid neighbour and are not
+// stored.
 #include "mxfp4_device.h"
 #include "mxfp4_groups.h"
 #include "mxfp4_kernels.h"
@@ -48,6 +52,7 @@ struct GemmArgs {
   const int64_t *gl;
   int G, list_type, group_type, out_f32;
   int a_sb, b_sb;        // log2(scale block / 32): 0 or 2
+  int s4;                // both scale arrays have dword-aligned rows: dword slice loads
   int64_t tiles_m, tiles_n, total;
 };
 
@@ -70,7 +75,7 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t id, int64_t total) {
   return x < r ? x * (q + 1) + loc : r * (q + 1) + (x - r) * q + loc;
 }
 
-template <int AF, int BF, int WM, int WN>
+template <int AF, int BF, int WM, int WN, bool S4>
 __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
   constexpr int BM = 64 * WM, BN = 64 * WN;
   constexpr bool B4 = BF == kFmtE2M1;
@@ -79,13 +84,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
   constexpr int B_LD = B4 ? BN / 64 : BN / 32;
   __shared__ __align__(16) uint8_t sA[2][BM * 128];
   __shared__ __align__(16) uint8_t sB[2][BN * BROW];
+  __shared__ __align__(16) uint8_t sSA[2][BM * 32];  // scale chunks (32 K-blocks per row)
+  __shared__ __align__(16) uint8_t sSB[2][BN * 32];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int64_t tile = xcd_tile(blockIdx.x, P.total);
 
   // ---- tile -> rows, columns, K range, operand and output bases ----
-  int64_t m0, mlen, n0, kb0, kb1;
+  int64_t m0, mlen, n0, kb0, kb1, klo = 0;  // steps start at kb0; blocks below klo are masked
   const uint8_t *bbase = P.b, *bsbase = P.bs;
   int64_t cbase = 0;  // element offset of the output matrix
   if (P.group_type == 0) {
@@ -115,6 +122,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
     group_block_span(P.gl, P.G, P.list_type, P.K, 5, g, &kb0, &nb);
     kb1 = kb0 + nb < P.k_blocks ? kb0 + nb : P.k_blocks;
     if (kb0 > kb1) kb0 = kb1;
+    // steps start on a multiple of 4 blocks (dword-aligned scale chunks);
+    // the blocks of the previous group in the first step are masked
+    klo = kb0;
+    kb0 &= ~(int64_t)3;
     cbase = (int64_t)g * P.M * P.ldc;
   }
   const int64_t nlen = P.N - n0 < BN ? P.N - n0 : BN;
@@ -138,59 +149,83 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
     const int row = br + (B4 ? 64 : 32) * i;
     boff[i] = (uint32_t)((row < nlen ? row : nlen - 1) * P.ldb) + 16 * bc;
   }
-  // scale rows of this lane's MFMA tiles
   const int wr0 = (wave >> 1) * 32 * WM, wc0 = (wave & 1) * 32 * WN;
-  uint32_t asoff[WM], bsoff[WN];
+
+  // ---- scale bytes: chunks of 32 K-blocks (8 steps) staged in LDS ----
+  // Chunk c holds, for every tile row, the scale bytes of blocks
+  // [kb0 + 32c, kb0 + 32c + 32) (32 bytes, or 8 for 128-element blocks).
+  // While chunk c is in use, chunk c + 1 arrives one 1/8 slice per step:
+  // step 8c + p loads rows [p BM/8, (p+1) BM/8) of A and [p BN/8, ...) of B,
+  // one dword per thread (8 threads per 32-byte row: whole cache lines).
+  const int64_t avb = (kb1 + (1 << P.a_sb) - 1) >> P.a_sb;  // valid scale bytes per row
+  const int64_t bvb = (kb1 + (1 << P.b_sb) - 1) >> P.b_sb;
+  const int sr = tid >> 3, sd = tid & 7;  // slice row, dword
+  constexpr bool ALL_A = BM / 8 >= kGemmThreads / 8, ALL_B = BN / 8 >= kGemmThreads / 8;
+  const bool a_rows = ALL_A || sr < BM / 8, b_rows = ALL_B || sr < BN / 8;
+  // raw slice words (S4: one dword; else four bytes) and their validity; the
+  // select happens when the slice is stored, after the MFMAs
+  uint32_t pa[S4 ? 1 : 4], pb[S4 ? 1 : 4];
+  bool pa_ok = false, pb_ok = false;
+  auto load_slice = [&](int64_t chunk, int piece) {
+    {
+      const int row = piece * (BM / 8) + (a_rows ? sr : 0);
+      const int64_t byte = ((kb0 + 32 * chunk) >> P.a_sb) + 4 * sd;
+      pa_ok = a_rows && 4 * sd < (32 >> P.a_sb) && byte < avb;
+      const uint8_t *rp = asbase + (int64_t)(row < mlen ? row : mlen - 1) * P.ldas;
+      const int64_t at = pa_ok ? byte : avb - 1;
+      if (S4) {
+        pa[0] = *reinterpret_cast<const uint32_t *>(rp + (at & ~(int64_t)3));
+      } else {
 #pragma unroll
-  for (int i = 0; i < WM; ++i) {
-    const int row = wr0 + 32 * i + l32;
-    asoff[i] = (uint32_t)((row < mlen ? row : mlen - 1) * P.ldas);
-  }
+        for (int e = 0; e < (S4 ? 1 : 4); ++e) pa[e] = rp[at + e < avb ? at + e : avb - 1];
+      }
+    }
+    {
+      const int row = piece * (BN / 8) + (b_rows ? sr : 0);
+      const int64_t byte = ((kb0 + 32 * chunk) >> P.b_sb) + 4 * sd;
+      pb_ok = b_rows && 4 * sd < (32 >> P.b_sb) && byte < bvb;
+      const uint8_t *rp = bsbase + (int64_t)(row < nlen ? row : nlen - 1) * P.ldbs;
+      const int64_t at = pb_ok ? byte : bvb - 1;
+      if (S4) {
+        pb[0] = *reinterpret_cast<const uint32_t *>(rp + (at & ~(int64_t)3));
+      } else {
 #pragma unroll
-  for (int j = 0; j < WN; ++j) {
-    const int row = wc0 + 32 * j + l32;
-    bsoff[j] = (uint32_t)((row < nlen ? row : nlen - 1) * P.ldbs);
-  }
+        for (int e = 0; e < (S4 ? 1 : 4); ++e) pb[e] = rp[at + e < bvb ? at + e : bvb - 1];
+      }
+    }
+  };
+  auto store_slice = [&](int sbuf, int piece) {
+    uint32_t va = pa[0], vb = pb[0];
+    if (!S4) {
+#pragma unroll
+      for (int e = 1; e < (S4 ? 1 : 4); ++e) va |= pa[e] << (8 * e), vb |= pb[e] << (8 * e);
+    }
+    if (a_rows)
+      *reinterpret_cast<uint32_t *>(&sSA[sbuf][(piece * (BM / 8) + sr) * 32 + 4 * sd]) = pa_ok ? va : 0x7F7F7F7Fu;
+    if (b_rows)
+      *reinterpret_cast<uint32_t *>(&sSB[sbuf][(piece * (BN / 8) + sr) * 32 + 4 * sd]) = pb_ok ? vb : 0x7F7F7F7Fu;
+  };
 
   u32x4 ra[A_LD], rb[B_LD];
-  uint32_t sa[WM], sb[WN];  // byte s: scale of K-block 2s + h of the step
-  uint8_t xa[WM][2], xb[WN][2];
-  bool in0 = false, in1 = false, ain = false, bin = false;
+  bool ain = false, bin = false;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-  // K step starting at block kb: global -> registers (codes) and scale bytes.
-  // Blocks at or past kb1 read block kb1 - 1 (in bounds) and are replaced by
-  // zero codes / scale 2^0, so the loads carry no branches.
+  // Codes of the K step starting at block kb: global -> registers.  Slots at
+  // or past kb1 read block kb1 - 1 (in bounds) and are zeroed when stored, so
+  // the loads carry no branches.
   auto load_step = [&](int64_t kb) {
     const int64_t last = kb1 - 1;
-    // one block per thread slot: 16-byte slot ac of A holds K 16ac..16ac+15,
-    // slot bc of B holds K 32bc.. (fp4) or 16bc.. (fp8)
+    // 16-byte slot ac of A holds K 16ac..16ac+15; slot bc of B holds K 32bc..
+    // (fp4) or 16bc.. (fp8)
     const int64_t ablk = kb + (ac >> 1), bblk = B4 ? kb + bc : kb + (bc >> 1);
-    ain = ablk < kb1;
-    bin = bblk < kb1;
+    ain = ablk >= klo && ablk < kb1;
+    bin = bblk >= klo && bblk < kb1;
     const int64_t at = ain ? (kb << 5) : (last << 5) - 16 * ac;
     const int64_t bt = bin ? (kb << (B4 ? 4 : 5)) : (B4 ? (last << 4) - 16 * bc : (last << 5) - 16 * bc);
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4 *>(abase + at + aoff[i]);
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) rb[i] = *reinterpret_cast<const u32x4 *>(bbase + bt + boff[i]);
-    const int64_t b0 = kb + h, b1 = kb + 2 + h;
-    in0 = b0 < kb1;
-    in1 = b1 < kb1;
-    const uint8_t *as0 = asbase + ((in0 ? b0 : last) >> P.a_sb), *as1 = asbase + ((in1 ? b1 : last) >> P.a_sb);
-    const uint8_t *bs0 = bsbase + ((in0 ? b0 : last) >> P.b_sb), *bs1 = bsbase + ((in1 ? b1 : last) >> P.b_sb);
-#pragma unroll
-    for (int i = 0; i < WM; ++i) xa[i][0] = as0[asoff[i]], xa[i][1] = as1[asoff[i]];
-#pragma unroll
-    for (int j = 0; j < WN; ++j) xb[j][0] = bs0[bsoff[j]], xb[j][1] = bs1[bsoff[j]];
-  };
-  // raw scale bytes -> one register per tile (byte s: K-block 2s + h);
-  // done after the MFMAs so that their wait does not stall the step
-  auto finish_scales = [&]() {
-#pragma unroll
-    for (int i = 0; i < WM; ++i) sa[i] = (in0 ? (uint32_t)xa[i][0] : 127u) | ((in1 ? (uint32_t)xa[i][1] : 127u) << 8);
-#pragma unroll
-    for (int j = 0; j < WN; ++j) sb[j] = (in0 ? (uint32_t)xb[j][0] : 127u) | ((in1 ? (uint32_t)xb[j][1] : 127u) << 8);
   };
   auto store_step = [&](int buf) {
 #pragma unroll
@@ -215,22 +250,41 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int64_t nsteps = (kb1 - kb0 + 3) >> 2;
-  uint32_t csa[WM], csb[WN];  // scales of the step being computed
   if (nsteps > 0) {
     load_step(kb0);
-    finish_scales();
     store_step(0);
+    for (int piece = 0; piece < 8; ++piece) {
+      load_slice(0, piece);
+      store_slice(0, piece);
+    }
   }
   __syncthreads();
   for (int64_t st = 0; st < nsteps; ++st) {
-    const int buf = (int)(st & 1);
+    const int buf = (int)(st & 1), sbuf = (int)((st >> 3) & 1), piece = (int)(st & 7);
+    const int64_t kb = kb0 + 4 * st;
+    // this step's scale bytes: blocks kb + h (MFMA 0) and kb + 2 + h (MFMA 1)
+    uint32_t csa[WM], csb[WN];
+    {
+      const bool in0 = kb + h >= klo && kb + h < kb1, in1 = kb + 2 + h >= klo && kb + 2 + h < kb1;
+      const int64_t ca = (kb0 + 32 * (st >> 3)) >> P.a_sb, cb = (kb0 + 32 * (st >> 3)) >> P.b_sb;
+      const int qa0 = (int)(((kb + h) >> P.a_sb) - ca), qa1 = (int)(((kb + 2 + h) >> P.a_sb) - ca);
+      const int qb0 = (int)(((kb + h) >> P.b_sb) - cb), qb1 = (int)(((kb + 2 + h) >> P.b_sb) - cb);
 #pragma unroll
-    for (int i = 0; i < WM; ++i) csa[i] = sa[i];
+      for (int i = 0; i < WM; ++i) {
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSA[sbuf][(wr0 + 32 * i + l32) * 32 + (qa0 & ~3)]);
+        csa[i] = (in0 ? (w >> (8 * (qa0 & 3))) & 0xFFu : 127u) | ((in1 ? (w >> (8 * (qa1 & 3))) & 0xFFu : 127u) << 8);
+      }
 #pragma unroll
-    for (int j = 0; j < WN; ++j) csb[j] = sb[j];
-    // prefetch the next step (the last iteration re-reads clamped, in-bounds
-    // blocks that are never used: no branch splits the loop body)
-    load_step(kb0 + 4 * (st + 1));
+      for (int j = 0; j < WN; ++j) {
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSB[sbuf][(wc0 + 32 * j + l32) * 32 + (qb0 & ~3)]);
+        csb[j] = (in0 ? (w >> (8 * (qb0 & 3))) & 0xFFu : 127u) | ((in1 ? (w >> (8 * (qb1 & 3))) & 0xFFu : 127u) << 8);
+      }
+    }
+    // prefetch the next step's codes and a slice of the next scale chunk (the
+    // last iterations re-read clamped, in-bounds data that is never used: no
+    // branch splits the loop body)
+    load_step(kb + 4);
+    load_slice((st >> 3) + 1, piece);
 
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -264,8 +318,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
               (int)((csb[j] >> (8 * s)) & 0xFFu));
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the waits for the prefetch after the MFMAs
-    finish_scales();
     store_step(buf ^ 1);
+    store_slice(sbuf ^ 1, piece);
     __syncthreads();
   }
 
@@ -316,7 +370,10 @@ hipError_t gemm_launch(const GemmArgs &a0, hipStream_t st) {
   }
   if (a.total <= 0) return hipSuccess;
   if (a.total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mxgemm_kernel<AF, BF, WM, WN>), dim3((unsigned)a.total), dim3(kGemmThreads), 0, st, a);
+  if (a.s4)
+    hipLaunchKernelGGL((mxgemm_kernel<AF, BF, WM, WN, true>), dim3((unsigned)a.total), dim3(kGemmThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((mxgemm_kernel<AF, BF, WM, WN, false>), dim3((unsigned)a.total), dim3(kGemmThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -356,6 +413,8 @@ hipError_t launch_mx_gemm(const GemmLaunch &L, hipStream_t st) {
   a.out_f32 = L.out_f32;
   a.a_sb = L.a_block == 128 ? 2 : 0;
   a.b_sb = L.b_block == 128 ? 2 : 0;
+  a.s4 = ((uintptr_t)L.as % 4 == 0 && (uintptr_t)L.bs % 4 == 0 && L.ldas % 4 == 0 && L.ldbs % 4 == 0 &&
+          L.b_gss % 4 == 0);
   return L.a_fmt == kFmtE4M3 ? gemm_launch_b<kFmtE4M3>(L.b_fmt, a, st) : gemm_launch_b<kFmtE5M2>(L.b_fmt, a, st);
 }
 
