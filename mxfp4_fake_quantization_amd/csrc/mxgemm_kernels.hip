@@ -34,6 +34,8 @@
 #include "mxfp4_groups.h"
 #include "mxfp4_kernels.h"
 
+#include <type_traits>
+
 namespace mxfp4 {
 namespace {
 
@@ -41,7 +43,11 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGemmThreads = 256;
+// 8 waves per workgroup (2 per SIMD, so one wave's LDS and address work
+// overlaps the other's MFMAs): 4 x 2 waves of 2 x 4 MFMA tiles = 256 x 256.
+constexpr int kWavesM = 4, kWavesN = 2, kTilesM = 2, kTilesN = 4;
+constexpr int kGemmThreads = 64 * kWavesM * kWavesN;
+constexpr int kBM = 32 * kTilesM * kWavesM, kBN = 32 * kTilesN * kWavesN;
 
 struct GemmArgs {
   const uint8_t *a, *as, *b, *bs;
@@ -75,13 +81,20 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t id, int64_t total) {
   return x < r ? x * (q + 1) + loc : r * (q + 1) + (x - r) * q + loc;
 }
 
-template <int AF, int BF, int WM, int WN, bool S4>
+template <int AF, int BF, bool S4>
 __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
-  constexpr int BM = 64 * WM, BN = 64 * WN;
+  constexpr int WVM = kWavesM, WVN = kWavesN, WM = kTilesM, WN = kTilesN;
+  constexpr int NT = kGemmThreads;
+  constexpr int BM = kBM, BN = kBN;
   constexpr bool B4 = BF == kFmtE2M1;
-  constexpr int BROW = B4 ? 64 : 128;        // B bytes per row per K step
-  constexpr int A_LD = BM / 32;              // 16-byte A loads per thread per step
-  constexpr int B_LD = B4 ? BN / 64 : BN / 32;
+  constexpr int BROW = B4 ? 64 : 128;           // B bytes per row per K step
+  constexpr int A_LD = BM * 8 / NT;             // 16-byte A loads per thread per step
+  constexpr int A_RSTEP = NT / 8;               // rows per A load pass
+  constexpr int B_SLOTS = BROW / 16;
+  constexpr int B_LD = BN * B_SLOTS / NT;
+  constexpr int B_RSTEP = NT / B_SLOTS;
+  static_assert(WVM * WVN * 64 == NT && BM == 32 * WM * WVM && BN == 32 * WN * WVN, "tile shape");
+  static_assert(BM / 8 * 8 == NT / 2 && BN / 8 * 8 == NT / 2, "one scale dword per thread per step");
   __shared__ __align__(16) uint8_t sA[2][BM * 128];
   __shared__ __align__(16) uint8_t sB[2][BN * BROW];
   __shared__ __align__(16) uint8_t sSA[2][BM * 32];  // scale chunks (32 K-blocks per row)
@@ -135,85 +148,85 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
   const uint8_t *asbase = P.as + m0 * P.ldas;
   bbase += n0 * P.ldb;
   bsbase += n0 * P.ldbs;
-  const int ar = tid >> 3, ac = tid & 7;                 // A: 32 rows x 8 slots per pass
-  const int br = B4 ? tid >> 2 : tid >> 3;               // B: 64 x 4 (fp4) / 32 x 8 (fp8)
-  const int bc = B4 ? tid & 3 : tid & 7;
+  const int ar = tid >> 3, ac = tid & 7;                  // A: NT/8 rows x 8 slots per pass
+  const int br = tid / B_SLOTS, bc = tid % B_SLOTS;       // B: NT/B_SLOTS rows x B_SLOTS slots
   uint32_t aoff[A_LD], boff[B_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
-    const int row = ar + 32 * i;
+    const int row = ar + A_RSTEP * i;
     aoff[i] = (uint32_t)((row < mlen ? row : mlen - 1) * P.lda) + 16 * ac;
   }
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
-    const int row = br + (B4 ? 64 : 32) * i;
+    const int row = br + B_RSTEP * i;
     boff[i] = (uint32_t)((row < nlen ? row : nlen - 1) * P.ldb) + 16 * bc;
   }
-  const int wr0 = (wave >> 1) * 32 * WM, wc0 = (wave & 1) * 32 * WN;
+  const int wr0 = (wave / WVN) * 32 * WM, wc0 = (wave % WVN) * 32 * WN;
 
   // ---- scale bytes: chunks of 32 K-blocks (8 steps) staged in LDS ----
   // Chunk c holds, for every tile row, the scale bytes of blocks
   // [kb0 + 32c, kb0 + 32c + 32) (32 bytes, or 8 for 128-element blocks).
   // While chunk c is in use, chunk c + 1 arrives one 1/8 slice per step:
-  // step 8c + p loads rows [p BM/8, (p+1) BM/8) of A and [p BN/8, ...) of B,
-  // one dword per thread (8 threads per 32-byte row: whole cache lines).
-  const int64_t avb = (kb1 + (1 << P.a_sb) - 1) >> P.a_sb;  // valid scale bytes per row
-  const int64_t bvb = (kb1 + (1 << P.b_sb) - 1) >> P.b_sb;
-  const int sr = tid >> 3, sd = tid & 7;  // slice row, dword
-  constexpr bool ALL_A = BM / 8 >= kGemmThreads / 8, ALL_B = BN / 8 >= kGemmThreads / 8;
-  const bool a_rows = ALL_A || sr < BM / 8, b_rows = ALL_B || sr < BN / 8;
-  // raw slice words (S4: one dword; else four bytes) and their validity; the
-  // select happens when the slice is stored, after the MFMAs
-  uint32_t pa[S4 ? 1 : 4], pb[S4 ? 1 : 4];
-  bool pa_ok = false, pb_ok = false;
+  // step 8c + p loads rows [32p, 32p + 32) of A (waves of the first half) or
+  // of B (second half), one dword per thread, 8 threads per 32-byte row.
+  // Bytes outside [klo, kb1) are replaced by 127 (2^0) when stored, so the
+  // MFMAs of masked blocks (zero codes) see a finite scale.
+  const bool sl_b = tid >= NT / 2;
+  const int sr = (tid & (NT / 2 - 1)) >> 3, sd = tid & 7;
+  const int sb_log = sl_b ? P.b_sb : P.a_sb;
+  const int64_t s_lo = klo >> sb_log;                                   // first valid byte
+  const int64_t s_hi = (kb1 + (1 << sb_log) - 1) >> sb_log;            // past the last
+  const uint8_t *s_base = sl_b ? bsbase : asbase;
+  const int64_t s_ld = sl_b ? P.ldbs : P.ldas;
+  const int64_t s_rows = sl_b ? nlen : mlen;
+  uint32_t pv[S4 ? 1 : 4];
+  int64_t pbyte = 0;
   auto load_slice = [&](int64_t chunk, int piece) {
-    {
-      const int row = piece * (BM / 8) + (a_rows ? sr : 0);
-      const int64_t byte = ((kb0 + 32 * chunk) >> P.a_sb) + 4 * sd;
-      pa_ok = a_rows && 4 * sd < (32 >> P.a_sb) && byte < avb;
-      const uint8_t *rp = asbase + (int64_t)(row < mlen ? row : mlen - 1) * P.ldas;
-      const int64_t at = pa_ok ? byte : avb - 1;
-      if (S4) {
-        pa[0] = *reinterpret_cast<const uint32_t *>(rp + (at & ~(int64_t)3));
-      } else {
+    const int row = piece * 32 + sr;
+    pbyte = ((kb0 + 32 * chunk) >> sb_log) + 4 * sd;
+    const uint8_t *rp = s_base + (int64_t)(row < s_rows ? row : s_rows - 1) * s_ld;
+    const int64_t at = pbyte < s_hi ? pbyte : s_hi - 1;  // in bounds (s_hi <= row length)
+    if (S4) {
+      pv[0] = *reinterpret_cast<const uint32_t *>(rp + (at & ~(int64_t)3));
+    } else {
 #pragma unroll
-        for (int e = 0; e < (S4 ? 1 : 4); ++e) pa[e] = rp[at + e < avb ? at + e : avb - 1];
-      }
-    }
-    {
-      const int row = piece * (BN / 8) + (b_rows ? sr : 0);
-      const int64_t byte = ((kb0 + 32 * chunk) >> P.b_sb) + 4 * sd;
-      pb_ok = b_rows && 4 * sd < (32 >> P.b_sb) && byte < bvb;
-      const uint8_t *rp = bsbase + (int64_t)(row < nlen ? row : nlen - 1) * P.ldbs;
-      const int64_t at = pb_ok ? byte : bvb - 1;
-      if (S4) {
-        pb[0] = *reinterpret_cast<const uint32_t *>(rp + (at & ~(int64_t)3));
-      } else {
-#pragma unroll
-        for (int e = 0; e < (S4 ? 1 : 4); ++e) pb[e] = rp[at + e < bvb ? at + e : bvb - 1];
-      }
+      for (int e = 0; e < (S4 ? 1 : 4); ++e) pv[e] = rp[at + e < s_hi ? at + e : s_hi - 1];
     }
   };
   auto store_slice = [&](int sbuf, int piece) {
-    uint32_t va = pa[0], vb = pb[0];
+    uint32_t v = pv[0];
     if (!S4) {
 #pragma unroll
-      for (int e = 1; e < (S4 ? 1 : 4); ++e) va |= pa[e] << (8 * e), vb |= pb[e] << (8 * e);
+      for (int e = 1; e < (S4 ? 1 : 4); ++e) v |= pv[e] << (8 * e);
     }
-    if (a_rows)
-      *reinterpret_cast<uint32_t *>(&sSA[sbuf][(piece * (BM / 8) + sr) * 32 + 4 * sd]) = pa_ok ? va : 0x7F7F7F7Fu;
-    if (b_rows)
-      *reinterpret_cast<uint32_t *>(&sSB[sbuf][(piece * (BN / 8) + sr) * 32 + 4 * sd]) = pb_ok ? vb : 0x7F7F7F7Fu;
+    // keep bytes pbyte + e inside [s_lo, s_hi) and inside the chunk
+    const int64_t lead = s_lo - pbyte, cnt = s_hi - pbyte;
+    const int nlead = lead <= 0 ? 0 : (lead >= 4 ? 4 : (int)lead);
+    int nval = cnt <= 0 ? 0 : (cnt >= 4 ? 4 : (int)cnt);
+    if (4 * sd >= (32 >> sb_log)) nval = 0;
+    const uint32_t hi_m = nval >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nval)) - 1u);
+    const uint32_t lo_m = nlead >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nlead)) - 1u);
+    const uint32_t keep = hi_m & ~lo_m;
+    v = (v & keep) | (0x7F7F7F7Fu & ~keep);
+    uint8_t *dst = sl_b ? &sSB[sbuf][0] : &sSA[sbuf][0];
+    *reinterpret_cast<uint32_t *>(dst + (piece * 32 + sr) * 32 + 4 * sd) = v;
   };
 
   u32x4 ra[A_LD], rb[B_LD];
-  bool ain = false, bin = false;
+  bool ain = true, bin = true;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
-
-  // Codes of the K step starting at block kb: global -> registers.  Slots at
-  // or past kb1 read block kb1 - 1 (in bounds) and are zeroed when stored, so
-  // the loads carry no branches.
-  auto load_step = [&](int64_t kb) {
+  // Codes of the K step starting at block kb: global -> registers.  The
+  // masked form (first and last steps) reads clamped in-bounds addresses and
+  // zeroes slots outside [klo, kb1) when storing.
+  auto load_full = [&](int64_t kb) {
+    const uint8_t *ab = abase + (kb << 5);
+    const uint8_t *bb = bbase + (kb << (B4 ? 4 : 5));
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4 *>(ab + aoff[i]);
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) rb[i] = *reinterpret_cast<const u32x4 *>(bb + boff[i]);
+  };
+  auto load_masked = [&](int64_t kb) {
     const int64_t last = kb1 - 1;
     // 16-byte slot ac of A holds K 16ac..16ac+15; slot bc of B holds K 32bc..
     // (fp4) or 16bc.. (fp8)
@@ -227,17 +240,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) rb[i] = *reinterpret_cast<const u32x4 *>(bbase + bt + boff[i]);
   };
-  auto store_step = [&](int buf) {
+  auto store_codes = [&](int buf, bool masked) {
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-      const int row = ar + 32 * i;
-      *reinterpret_cast<u32x4 *>(&sA[buf][row * 128 + swz_a(row, ac)]) = ain ? ra[i] : zero4;
+      const int row = ar + A_RSTEP * i;
+      *reinterpret_cast<u32x4 *>(&sA[buf][row * 128 + swz_a(row, ac)]) = (!masked || ain) ? ra[i] : zero4;
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-      const int row = br + (B4 ? 64 : 32) * i;
+      const int row = br + B_RSTEP * i;
       const int off = B4 ? row * 64 + swz_b4(row, bc) : row * 128 + swz_a(row, bc);
-      *reinterpret_cast<u32x4 *>(&sB[buf][off]) = bin ? rb[i] : zero4;
+      *reinterpret_cast<u32x4 *>(&sB[buf][off]) = (!masked || bin) ? rb[i] : zero4;
     }
   };
 
@@ -249,42 +262,35 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int64_t nsteps = (kb1 - kb0 + 3) >> 2;
-  if (nsteps > 0) {
-    load_step(kb0);
-    store_step(0);
-    for (int piece = 0; piece < 8; ++piece) {
-      load_slice(0, piece);
-      store_slice(0, piece);
-    }
-  }
-  __syncthreads();
-  for (int64_t st = 0; st < nsteps; ++st) {
+  // One K step: this step's scales from LDS, the prefetch of step st + 1
+  // (PF: 0 none, 1 unmasked, 2 masked) and a scale slice, the MFMAs, then the
+  // LDS stores of the prefetch and the barrier.
+  auto step = [&](int64_t st, auto pf) {
+    constexpr int PF = decltype(pf)::value;
     const int buf = (int)(st & 1), sbuf = (int)((st >> 3) & 1), piece = (int)(st & 7);
     const int64_t kb = kb0 + 4 * st;
-    // this step's scale bytes: blocks kb + h (MFMA 0) and kb + 2 + h (MFMA 1)
-    uint32_t csa[WM], csb[WN];
+    // scale bytes of blocks kb + h (s = 0) and kb + 2 + h (s = 1)
+    uint32_t csa[WM][2], csb[WN][2];
     {
-      const bool in0 = kb + h >= klo && kb + h < kb1, in1 = kb + 2 + h >= klo && kb + 2 + h < kb1;
       const int64_t ca = (kb0 + 32 * (st >> 3)) >> P.a_sb, cb = (kb0 + 32 * (st >> 3)) >> P.b_sb;
       const int qa0 = (int)(((kb + h) >> P.a_sb) - ca), qa1 = (int)(((kb + 2 + h) >> P.a_sb) - ca);
       const int qb0 = (int)(((kb + h) >> P.b_sb) - cb), qb1 = (int)(((kb + 2 + h) >> P.b_sb) - cb);
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
         const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSA[sbuf][(wr0 + 32 * i + l32) * 32 + (qa0 & ~3)]);
-        csa[i] = (in0 ? (w >> (8 * (qa0 & 3))) & 0xFFu : 127u) | ((in1 ? (w >> (8 * (qa1 & 3))) & 0xFFu : 127u) << 8);
+        csa[i][0] = (w >> (8 * (qa0 & 3))) & 0xFFu;
+        csa[i][1] = (w >> (8 * (qa1 & 3))) & 0xFFu;
       }
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSB[sbuf][(wc0 + 32 * j + l32) * 32 + (qb0 & ~3)]);
-        csb[j] = (in0 ? (w >> (8 * (qb0 & 3))) & 0xFFu : 127u) | ((in1 ? (w >> (8 * (qb1 & 3))) & 0xFFu : 127u) << 8);
+        csb[j][0] = (w >> (8 * (qb0 & 3))) & 0xFFu;
+        csb[j][1] = (w >> (8 * (qb1 & 3))) & 0xFFu;
       }
     }
-    // prefetch the next step's codes and a slice of the next scale chunk (the
-    // last iterations re-read clamped, in-bounds data that is never used: no
-    // branch splits the loop body)
-    load_step(kb + 4);
-    load_slice((st >> 3) + 1, piece);
+    if (PF == 1) load_full(kb + 4);
+    if (PF == 2) load_masked(kb + 4);
+    if (PF != 0) load_slice((st >> 3) + 1, piece);
 
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -313,14 +319,33 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
       for (int i = 0; i < WM; ++i)
 #pragma unroll
         for (int j = 0; j < WN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fa[i], fb[j], acc[i][j], AF, BF, 0, (int)((csa[i] >> (8 * s)) & 0xFFu), 0,
-              (int)((csb[j] >> (8 * s)) & 0xFFu));
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AF, BF, 0,
+                                                                      (int)csa[i][s], 0, (int)csb[j][s]);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the waits for the prefetch after the MFMAs
-    store_step(buf ^ 1);
-    store_slice(sbuf ^ 1, piece);
+    if (PF == 1) store_codes(buf ^ 1, false);
+    if (PF == 2) store_codes(buf ^ 1, true);
+    if (PF != 0) {
+      store_slice(sbuf ^ 1, piece);
+      __syncthreads();
+    }
+  };
+
+  const int64_t nsteps = (kb1 - kb0 + 3) >> 2;
+  if (nsteps > 0) {
+    load_masked(kb0);
+    store_codes(0, true);
+    for (int piece = 0; piece < 8; ++piece) {
+      load_slice(0, piece);
+      store_slice(0, piece);
+    }
     __syncthreads();
+    // only the first and the last step can be partial: the steps in between
+    // are prefetched unmasked
+    int64_t st = 0;
+    for (; st + 2 < nsteps; ++st) step(st, std::integral_constant<int, 1>{});
+    if (st + 1 < nsteps) step(st++, std::integral_constant<int, 2>{});
+    step(st, std::integral_constant<int, 0>{});
   }
 
   // ---- epilogue: row 8(v/4) + 4h + v%4, column l32 of each 32x32 tile ----
@@ -356,9 +381,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
 
 template <int AF, int BF>
 hipError_t gemm_launch(const GemmArgs &a0, hipStream_t st) {
-  constexpr int WM = 4, WN = 4;
   GemmArgs a = a0;
-  const int64_t BM = 64 * WM, BN = 64 * WN;
+  const int64_t BM = kBM, BN = kBN;
   a.tiles_n = (a.N + BN - 1) / BN;
   if (a.group_type == 0) {
     // upper bound of the M tiles: every group adds at most one partial tile
@@ -371,9 +395,9 @@ hipError_t gemm_launch(const GemmArgs &a0, hipStream_t st) {
   if (a.total <= 0) return hipSuccess;
   if (a.total > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (a.s4)
-    hipLaunchKernelGGL((mxgemm_kernel<AF, BF, WM, WN, true>), dim3((unsigned)a.total), dim3(kGemmThreads), 0, st, a);
+    hipLaunchKernelGGL((mxgemm_kernel<AF, BF, true>), dim3((unsigned)a.total), dim3(kGemmThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((mxgemm_kernel<AF, BF, WM, WN, false>), dim3((unsigned)a.total), dim3(kGemmThreads), 0, st, a);
+    hipLaunchKernelGGL((mxgemm_kernel<AF, BF, false>), dim3((unsigned)a.total), dim3(kGemmThreads), 0, st, a);
   return hipGetLastError();
 }
 
