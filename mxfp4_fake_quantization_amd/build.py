@@ -41,6 +41,13 @@ def build() -> str:
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # a kernel whose host-side launch stub was not generated links fine into a
+    # shared library and only fails when loaded: refuse it here
+    r = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in r.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("kernel launch stubs missing from the host objects: " + ", ".join(missing))
     os.replace(tmp, LIB)
     return LIB
 
