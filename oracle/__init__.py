@@ -45,10 +45,11 @@ def _load():
         lib.oracle_mxfp8_rows.argtypes = [i32, i64, i64, i32, vp, vp, vp]
         lib.oracle_mxfp8_decode.argtypes = [i32, i64, i64, i32, vp, vp, vp]
         lib.oracle_grouped_matmul.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, i32, vp]
+        lib.oracle_mxfp8_kmajor.argtypes = [i32, i64, i64, i32, vp, vp, i32, i32, i64, vp, vp]
         for fn in ("oracle_qdq_rows", "oracle_qdq_cols", "oracle_grouped_cols",
                    "oracle_ste_bwd", "oracle_pack_rows", "oracle_unpack_rows",
                    "oracle_pack_kmajor", "oracle_mxfp8_rows", "oracle_mxfp8_decode",
-                   "oracle_grouped_matmul"):
+                   "oracle_grouped_matmul", "oracle_mxfp8_kmajor"):
             getattr(lib, fn).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -213,6 +214,29 @@ def mxfp8_decode(q: np.ndarray, scales: np.ndarray, fmt: str = "e4m3", dtype=np.
     _check(_load().oracle_mxfp8_decode(_dtype_code(y), rows, cols, FP8_FORMATS[fmt], _ptr(q),
                                        _ptr(scales), _ptr(y)), "mxfp8_decode")
     return y
+
+
+def mxfp8_kmajor(x: np.ndarray, fmt: str = "e4m3", group_list=None, list_type: int = 1, k_blocks=None,
+                 fill: int = 0xA5):
+    """K-major MXFP8 of column-wise (group_list None) or grouped 32-row blocks.
+
+    Returns (q_t[cols, k_blocks*32], scales_t[cols, k_blocks], nbt); block-rows at or
+    past nbt keep the `fill` byte (not touched)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    if group_list is None:
+        gl, ng, counts = None, 0, [rows]
+    else:
+        gl = np.ascontiguousarray(np.asarray(group_list, dtype=np.int64))
+        ng = len(gl)
+        counts = gl if list_type == 1 else np.diff(np.concatenate([[0], gl]))
+    nbt = int(sum(-(-int(c) // 32) for c in counts if c > 0))
+    kb = nbt if k_blocks is None else int(k_blocks)
+    q = np.full((cols, kb * 32), fill, np.uint8)
+    s = np.full((cols, kb), fill, np.uint8)
+    _check(_load().oracle_mxfp8_kmajor(_dtype_code(x), rows, cols, FP8_FORMATS[fmt], _ptr(x), _ptr(gl), ng,
+                                       list_type, kb, _ptr(q), _ptr(s)), "mxfp8_kmajor")
+    return q, s, nbt
 
 
 GROUP_M, GROUP_K = 0, 2

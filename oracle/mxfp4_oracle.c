@@ -421,39 +421,111 @@ static uint8_t fp8_encode_mag(int fmt, double a) {
   return (uint8_t)(((e + bias) << mb) | (int)((q / ldexp(1.0, e) - 1.0) * (1 << mb)));
 }
 
+/* One MXFP8 block of the n elements x[idx[0..n-1]] (OCP MX): scale 2^k with
+ * k = floor(log2 amax) - emax, clamped below at -127 (an all-zero block takes
+ * -127); each element x / 2^k (exact) rounded to the nearest fp8 value, ties
+ * to even, saturating; the sign bit is the input's (so -0.0 gives 0x80).
+ * Writes the n codes and returns the E8M0 byte k + 127. */
+static uint8_t mx8_block(int dtype, int fmt, const void *x, const int64_t *idx, int n, uint8_t *codes) {
+  int mb, bias, emax;
+  double maxn;
+  fp8_params(fmt, &mb, &bias, &maxn, &emax);
+  double amax = 0.0;
+  for (int j = 0; j < n; ++j) {
+    const double a = fabs(get_elem(dtype, x, idx[j]));
+    if (a > amax) amax = a;
+  }
+  int k = -127;
+  if (amax > 0.0) {
+    int e;
+    (void)frexp(amax, &e);
+    k = (e - 1) - emax;
+    if (k < -127) k = -127;
+  }
+  const double scale = ldexp(1.0, k);
+  for (int j = 0; j < n; ++j) {
+    const double v = get_elem(dtype, x, idx[j]) / scale; /* exact */
+    const uint8_t m = fp8_encode_mag(fmt, fabs(v));
+    codes[j] = (uint8_t)(m | (signbit(v) ? 0x80 : 0));
+  }
+  return (uint8_t)(k + 127);
+}
+
 /* Row-wise MXFP8: q [rows, cols] bytes, scales [rows, ceil(cols/32)] E8M0. */
 int oracle_mxfp8_rows(int dtype, int64_t rows, int64_t cols, int fmt, const void *x,
                       uint8_t *q, uint8_t *scales) {
   if (rows < 0 || cols < 0 || (fmt != 0 && fmt != 1)) return 1;
-  int mb, bias, emax;
-  double maxn;
-  fp8_params(fmt, &mb, &bias, &maxn, &emax);
   const int64_t nb = (cols + 31) / 32;
+  int64_t idx[32];
   for (int64_t r = 0; r < rows; ++r) {
     for (int64_t b = 0; b < nb; ++b) {
       const int64_t c0 = b * 32;
       const int n = (int)((cols - c0) < 32 ? (cols - c0) : 32);
-      double amax = 0.0;
-      for (int j = 0; j < n; ++j) {
-        const double a = fabs(get_elem(dtype, x, r * cols + c0 + j));
-        if (a > amax) amax = a;
-      }
-      int k = -127;
-      if (amax > 0.0) {
-        int e;
-        (void)frexp(amax, &e);
-        k = (e - 1) - emax;
-        if (k < -127) k = -127;
-      }
-      scales[r * nb + b] = (uint8_t)(k + 127);
-      const double scale = ldexp(1.0, k);
-      for (int j = 0; j < n; ++j) {
-        const double v = get_elem(dtype, x, r * cols + c0 + j) / scale; /* exact */
-        const uint8_t m = fp8_encode_mag(fmt, fabs(v));
-        q[r * cols + c0 + j] = (uint8_t)(m | (signbit(v) ? 0x80 : 0));
-      }
+      for (int j = 0; j < n; ++j) idx[j] = r * cols + c0 + j;
+      scales[r * nb + b] = mx8_block(dtype, fmt, x, idx, n, q + r * cols + c0);
     }
   }
+  return 0;
+}
+
+/* MXFP8 of column-wise blocks of 32 rows (group_list NULL) or of grouped
+ * blocks that restart at every group start (the hyper-parallel page's
+ * grouped quantization for block 32, which feeds the TN weight-gradient
+ * product), stored K-major for that product: column c of x becomes row c of
+ * q_t, K-position 32 t + o holds the code of row start_t + o of block-row t
+ * when o < len_t and 0 otherwise.
+ *   q_t      [cols, k_blocks * 32] fp8 bytes,
+ *   scales_t [cols, k_blocks] E8M0 bytes.
+ * Block-rows t >= NBT (the number the blocking yields) are not touched.
+ * Returns 1 for bad sizes (k_blocks < NBT) or an inconsistent group list
+ * (negative count, decreasing ends, or past rows). */
+int oracle_mxfp8_kmajor(int dtype, int64_t rows, int64_t cols, int fmt, const void *x,
+                        const int64_t *group_list, int num_groups, int list_type, int64_t k_blocks,
+                        uint8_t *q_t, uint8_t *scales_t) {
+  if (rows < 0 || cols < 0 || k_blocks < 0 || (fmt != 0 && fmt != 1)) return 1;
+  if (group_list && num_groups < 1) return 1;
+  /* block-rows: (start, len) */
+  int64_t nbt = 0, cap = rows / 32 + (group_list ? num_groups : 1) + 1;
+  int64_t *bs = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
+  int *bl = (int *)malloc(sizeof(int) * (size_t)cap);
+  if (!bs || !bl) {
+    free(bs);
+    free(bl);
+    return 2;
+  }
+  const int ng = group_list ? num_groups : 1;
+  int64_t start = 0;
+  for (int g = 0; g < ng; ++g) {
+    const int64_t end = !group_list ? rows : (list_type == 1 ? start + group_list[g] : group_list[g]);
+    if (end < start || end > rows) {
+      free(bs);
+      free(bl);
+      return 1;
+    }
+    for (int64_t r0 = start; r0 < end; r0 += 32) {
+      bs[nbt] = r0;
+      bl[nbt] = (int)((end - r0) < 32 ? (end - r0) : 32);
+      ++nbt;
+    }
+    start = end;
+  }
+  if (nbt > k_blocks) {
+    free(bs);
+    free(bl);
+    return 1;
+  }
+  const int64_t ldq = k_blocks * 32;
+  int64_t idx[32];
+  uint8_t codes[32];
+  for (int64_t t = 0; t < nbt; ++t) {
+    for (int64_t c = 0; c < cols; ++c) {
+      for (int j = 0; j < bl[t]; ++j) idx[j] = (bs[t] + j) * cols + c;
+      scales_t[c * k_blocks + t] = mx8_block(dtype, fmt, x, idx, bl[t], codes);
+      for (int o = 0; o < 32; ++o) q_t[c * ldq + t * 32 + o] = o < bl[t] ? codes[o] : 0;
+    }
+  }
+  free(bs);
+  free(bl);
   return 0;
 }
 

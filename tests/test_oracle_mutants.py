@@ -40,7 +40,11 @@ MUTANTS = {
     "mxfp8_ties_away": ("double q = rint(a / quantum) * quantum;", "double q = round(a / quantum) * quantum;"),
     "mxfp8_emax": ("*mb = 3; *bias = 7; *maxn = 448.0; *emax = 8;", "*mb = 3; *bias = 7; *maxn = 448.0; *emax = 7;"),
     "mxfp8_e4m3_max_480": ("*mb = 3; *bias = 7; *maxn = 448.0;", "*mb = 3; *bias = 7; *maxn = 480.0;"),
-    "mxfp8_zero_sign": ("q[r * cols + c0 + j] = (uint8_t)(m | (signbit(v) ? 0x80 : 0));", "q[r * cols + c0 + j] = (uint8_t)(m | (v < 0 && m ? 0x80 : 0));"),
+    "mxfp8_zero_sign": ("codes[j] = (uint8_t)(m | (signbit(v) ? 0x80 : 0));", "codes[j] = (uint8_t)(m | (v < 0 && m ? 0x80 : 0));"),
+    "mxfp8_kmajor_pad_code": ("q_t[c * ldq + t * 32 + o] = o < bl[t] ? codes[o] : 0;", "q_t[c * ldq + t * 32 + o] = o < bl[t] ? codes[o] : 0x80;"),
+    "mxfp8_kmajor_group_restart": ("for (int64_t r0 = start; r0 < end; r0 += 32) {\n      bs[nbt] = r0;", "for (int64_t r0 = start; r0 < end; r0 = (r0 / 32 + 1) * 32) {\n      bs[nbt] = r0;"),
+    "mxfp8_kmajor_scale_layout": ("scales_t[c * k_blocks + t] = mx8_block(", "scales_t[t * cols + c] = mx8_block("),
+    "mxfp8_kmajor_leading_dim": ("const int64_t ldq = k_blocks * 32;", "const int64_t ldq = nbt * 32;"),
     "mxfp8_subnormal_quantum": ("const int emin = 1 - bias; /* exponent of the smallest normal */", "const int emin = -bias;"),
     "gmm_group_weight": ("const double *w = right + (int64_t)g * K * N;", "const double *w = right + (int64_t)(g > 0 ? g - 1 : 0) * K * N;"),
     "gmm_list_type": ("const int64_t end = list_type == 1 ? start + group_list[g] : group_list[g];",

@@ -773,3 +773,70 @@ def test_decoders_float64_match_float32(oracle):
     c, s4 = oracle.pack_rows(x)
     assert np.array_equal(oracle.unpack_rows(c, s4, 96, 32, np.float64),
                           oracle.unpack_rows(c, s4, 96, 32, np.float32).astype(np.float64))
+
+
+# ---- K-major MXFP8 (grouped column-wise operand of the TN product) ------------------
+
+def test_mxfp8_kmajor_hand_worked(oracle):
+    """Three tokens x two columns, groups [2, 1] (E4M3).  Column 0: block {1, 0.5}:
+    amax 1 -> k = 0 - 8, e8 119, codes 256 = 2^8 -> 0x78, 128 -> 0x70; block {7}:
+    k = 2 - 8, e8 121, 7 * 2^6 = 448 -> 0x7E.  Column 1: block {-3, 100}: k = 6 - 8,
+    e8 125, -12 = -1.5 * 2^3 -> 0xD4, 400 lies midway between 384 and 416 -> even
+    mantissa -> 384 -> 0x7C; block {0}: e8 0, code 0.  Every other K position of a
+    block is padding 0."""
+    x = np.array([[1.0, -3.0], [0.5, 100.0], [7.0, 0.0]], np.float32)
+    q, s, nbt = oracle.mxfp8_kmajor(x, "e4m3", [2, 1], 1, k_blocks=3)
+    assert nbt == 2
+    exp_q = np.zeros((2, 64), np.uint8)
+    exp_q[0, [0, 1, 32]] = [0x78, 0x70, 0x7E]
+    exp_q[1, [0, 1, 32]] = [0xD4, 0x7C, 0x00]
+    assert np.array_equal(q[:, :64], exp_q)
+    assert (q[:, 64:] == 0xA5).all() and (s[:, 2] == 0xA5).all()   # block-row 2: untouched
+    assert np.array_equal(s[:, :2], np.array([[119, 121], [125, 0]], np.uint8))
+
+
+@pytest.mark.parametrize("rows", [1, 31, 32, 77, 200])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_mxfp8_kmajor_is_rows_of_transpose(oracle, rows, fmt):
+    """Dense column-wise blocks: the K-major codes are the row-wise MXFP8 of x^T,
+    followed by zero padding up to the block-row boundary; the scales agree."""
+    g = np.random.default_rng(rows)
+    x = W.f32_to_bf16_bits((g.standard_t(3, (rows, 9)) * np.exp2(g.uniform(-20, 20, (1, 9)))).astype(np.float32))
+    nb = -(-rows // 32)
+    q, s, nbt = oracle.mxfp8_kmajor(x, fmt, k_blocks=nb + 3)
+    assert nbt == nb
+    qr, sr = oracle.mxfp8_rows(np.ascontiguousarray(W.bf16_bits_to_f32(x).T.astype(np.float32)), fmt)
+    assert np.array_equal(q[:, :rows], qr)
+    assert (q[:, rows:32 * nb] == 0).all()
+    assert np.array_equal(s[:, :nb], sr)
+    assert (q[:, 32 * nb:] == 0xA5).all() and (s[:, nb:] == 0xA5).all()
+
+
+def test_mxfp8_kmajor_grouped_is_per_group(oracle):
+    """Grouped blocks restart at every group start: each group's block-rows are
+    the dense K-major MXFP8 of that group's rows, placed after the previous
+    groups' block-rows; list types agree."""
+    g = np.random.default_rng(3)
+    counts = np.array([45, 0, 1, 64, 30], np.int64)
+    x = W.f32_to_bf16_bits(g.standard_normal((int(counts.sum()) + 5, 11)).astype(np.float32))
+    nbt = int(sum(-(-int(c) // 32) for c in counts))
+    q, s, n = oracle.mxfp8_kmajor(x, "e4m3", counts, 1, k_blocks=nbt + 2)
+    q0, s0, _ = oracle.mxfp8_kmajor(x, "e4m3", np.cumsum(counts), 0, k_blocks=nbt + 2)
+    assert n == nbt and np.array_equal(q, q0) and np.array_equal(s, s0)
+    r0, b0 = 0, 0
+    for c in counts:
+        nb = -(-int(c) // 32)
+        if c:
+            qg, sg, _ = oracle.mxfp8_kmajor(np.ascontiguousarray(x[r0:r0 + c]), "e4m3")
+            assert np.array_equal(q[:, 32 * b0:32 * (b0 + nb)], qg)
+            assert np.array_equal(s[:, b0:b0 + nb], sg)
+        r0 += int(c)
+        b0 += nb
+
+
+def test_mxfp8_kmajor_rejects_bad_sizes(oracle):
+    x = np.ones((40, 3), np.float32)
+    with pytest.raises(ValueError):
+        oracle.mxfp8_kmajor(x, "e4m3", k_blocks=1)               # needs 2 block-rows
+    with pytest.raises(ValueError):
+        oracle.mxfp8_kmajor(x, "e4m3", [30, 20], 1, k_blocks=4)  # past rows
