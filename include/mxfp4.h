@@ -247,6 +247,30 @@ mxfp4_status_t mxfp8_quant(const mxfp4_desc_t *desc, int32_t fmt, const void *x,
                            uint8_t *q, uint8_t *scales, void *stream);
 
 /*
+ * MXFP8 of column-wise (group_list NULL) or grouped blocks of 32 rows, stored
+ * K-major: the operands of the TN weight-gradient product (the hyper-parallel
+ * page quantizes x and grad_output for it with grouped dynamic quantization
+ * for block 32: blocks run down each column and restart at every expert's
+ * first token, a group's last block may be short).  Element rule as
+ * mxfp8_quant (OCP MX, ties to even, saturating).  Column c of x becomes row
+ * c of q_t; block-row t (numbered group by group) fills K positions
+ * 32 t .. 32 t + 31 of it, positions past a short block's length hold code 0.
+ *   q_t      [cols, k_blocks * 32] fp8 bytes,
+ *   scales_t [cols, k_blocks] E8M0 bytes.
+ * desc->rows x desc->cols is x's shape (rows = tokens), desc->block must be
+ * 32; rule and scale_factor are ignored.  k_blocks >= ceil(rows / 32)
+ * (dense) or ceil(rows / 32) + num_groups - 1 (grouped: the most block-rows
+ * any list yields); block-rows past the ones the list yields are not
+ * written.  group_list: device int64 counts (type 1) or cumulative ends
+ * (type 0), clamped as in mxfp4_grouped_qdq.  x and q_t 16-byte aligned; no
+ * aliasing.  These operands feed mxfp4_grouped_matmul with MXGEMM_GROUP_K.
+ */
+mxfp4_status_t mxfp8_quant_kmajor(const mxfp4_desc_t *desc, int32_t fmt, const void *x,
+                                  const int64_t *group_list, int32_t num_groups,
+                                  int32_t group_list_type, int64_t k_blocks, uint8_t *q_t,
+                                  uint8_t *scales_t, void *stream);
+
+/*
  * One MX operand of the grouped matmul: element codes stored with the
  * reduction dimension K contiguous, and E8M0 scales (value of element k of
  * row r = decode(code) * 2^(scale[r, k / block] - 127)).

@@ -85,13 +85,14 @@ def _load():
         lib.mxfp4_quant_pack_kmajor.argtypes = [dp, vp, vp, i32, i32, ctypes.c_int64, vp, vp, vp]
         lib.mxfp4_dequant.argtypes = [dp, vp, vp, vp, vp]
         lib.mxfp8_quant.argtypes = [dp, i32, vp, vp, vp, vp]
+        lib.mxfp8_quant_kmajor.argtypes = [dp, i32, vp, vp, i32, i32, ctypes.c_int64, vp, vp, vp]
         op = ctypes.POINTER(_MxOperand)
         i64 = ctypes.c_int64
         lib.mxfp4_grouped_matmul.argtypes = [i32, i64, i64, i64, op, op, vp, i32, i32, i64, i32, vp,
                                              i64, vp]
         for f in ("mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
                   "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant", "mxfp4_version",
-                  "mxfp4_grouped_matmul"):
+                  "mxfp4_grouped_matmul", "mxfp8_quant_kmajor"):
             getattr(lib, f).restype = ctypes.c_int32
         lib.mxfp4_last_error.restype = ctypes.c_char_p
         lib.mxfp4_last_error.argtypes = []
@@ -302,6 +303,27 @@ def mxfp8_quant(x, q, scales, fmt="e4m3"):
     _check(st, "mxfp8_quant")
 
 
+def mxfp8_quant_kmajor(x, q_t, scales_t, fmt="e4m3", group_list=None, group_list_type=1):
+    """K-major MXFP8 of column-wise (group_list None) or grouped 32-row blocks:
+    q_t uint8 [cols, k_blocks * 32], scales_t uint8 [cols, k_blocks], k_blocks being
+    scales_t's second dimension (see mxfp8_kmajor_k_blocks)."""
+    if fmt not in _FP8:
+        raise ValueError(f"fmt must be 'e4m3' or 'e5m2', got {fmt!r}")
+    rows, cols = _shape2d(x)
+    if scales_t is None or scales_t.dim() != 2 or scales_t.shape[0] != cols:
+        raise ValueError(f"scales_t must be [cols={cols}, k_blocks]")
+    k_blocks = int(scales_t.shape[1])
+    if q_t is None or tuple(q_t.shape) != (cols, k_blocks * 32):
+        raise ValueError(f"q_t must be [{cols}, {k_blocks * 32}]")
+    d = _Desc(_dtype(x), 32, FLOOR, 0, rows, cols, 6.0, 0)
+    group_list = _group_list(group_list, rows, group_list_type)
+    n_groups = group_list.numel() if group_list is not None else 0
+    st = _load().mxfp8_quant_kmajor(ctypes.byref(d), _FP8[fmt], _ptr(x), _ptr(group_list, "i64"), n_groups,
+                                    int(group_list_type), k_blocks, _ptr(q_t, "u8"), _ptr(scales_t, "u8"),
+                                    _stream())
+    _check(st, "mxfp8_quant_kmajor")
+
+
 MX_FORMATS = {"e4m3": 0, "e5m2": 1, "e2m1": 4}
 GROUP_ROWS, GROUP_K = 0, 2
 
@@ -391,6 +413,21 @@ def grouped_scale_rows_max(rows: int, block: int, num_groups: int) -> int:
 
 def grouped_mask_rows_max(rows: int, block: int, num_groups: int) -> int:
     return grouped_scale_rows_max(rows, block, num_groups) * (block // 32)
+
+
+def mxfp8_kmajor_k_blocks(rows: int, num_groups=None, align: bool = True) -> int:
+    """k_blocks for mxfp8_quant_kmajor: at least ceil(rows/32) (dense) or
+    ceil(rows/32) + num_groups - 1 (grouped).  With align (default) a multiple
+    of 4 blocks (128-byte code rows), plus 4 more when the 32-byte-per-block
+    row stride is a multiple of 4 KiB (see kmajor_k_blocks)."""
+    nb = -(-rows // 32)
+    if num_groups is not None and rows > 0:
+        nb += int(num_groups) - 1
+    if align:
+        nb = -(-nb // 4) * 4
+        if nb and (nb * 32) % 4096 == 0:
+            nb += 4
+    return nb
 
 
 def kmajor_k_blocks(rows: int, block: int, num_groups=None, align: bool = True) -> int:

@@ -342,8 +342,44 @@ mxfp4_status_t mxfp4_grouped_matmul(int32_t group_type, int64_t M, int64_t N, in
   return hip_status(mxfp4::launch_mx_gemm(L, static_cast<hipStream_t>(stream)), "grouped matmul launch");
 }
 
+mxfp4_status_t mxfp8_quant_kmajor(const mxfp4_desc_t *desc, int32_t fmt, const void *x,
+                                  const int64_t *group_list, int32_t num_groups,
+                                  int32_t group_list_type, int64_t k_blocks, uint8_t *q_t,
+                                  uint8_t *scales_t, void *stream) {
+  int64_t n;
+  MXFP4_TRY(check_desc(desc, false, &n));
+  if (desc->block != 32)
+    return fail(MXFP4_EUNSUPPORTED, "MXFP8 blocks are 32 elements (got block %d)", desc->block);
+  if (fmt != MXFP8_E4M3 && fmt != MXFP8_E5M2)
+    return fail(MXFP4_EINVAL, "fmt %d is not MXFP8_E4M3 or MXFP8_E5M2", fmt);
+  MXFP4_TRY(check_ptr(x, 16, "x"));
+  MXFP4_TRY(check_ptr(q_t, 16, "q_t"));
+  MXFP4_TRY(check_ptr(scales_t, 1, "scales_t"));
+  const int64_t nb = (desc->rows + 31) / 32;
+  int64_t need = nb;
+  if (group_list) {
+    if (!aligned(group_list, 8)) return fail(MXFP4_EINVAL, "group_list is not 8-byte aligned");
+    if (num_groups < 1) return fail(MXFP4_EINVAL, "num_groups must be >= 1 (got %d)", num_groups);
+    if (group_list_type != 0 && group_list_type != 1)
+      return fail(MXFP4_EINVAL, "group_list_type must be 0 or 1 (got %d)", group_list_type);
+    need = desc->rows > 0 ? nb + num_groups - 1 : 0;
+  }
+  if (k_blocks < need)
+    return fail(MXFP4_EINVAL, "k_blocks %lld is below the %lld block-rows the blocking can produce",
+                (long long)k_blocks, (long long)need);
+  if (desc->cols > 0 && k_blocks > INT64_MAX / 64 / desc->cols)
+    return fail(MXFP4_EINVAL, "cols * k_blocks * 32 overflows");
+  if (!distinct({x, q_t, scales_t, group_list}))
+    return fail(MXFP4_EINVAL, "outputs alias each other, x or group_list");
+  if (n == 0) return ok();
+  mxfp4::Km8Launch L{desc->dtype, fmt, desc->rows, desc->cols, x, group_list, num_groups,
+                     group_list_type, k_blocks, q_t, scales_t};
+  return hip_status(mxfp4::launch_mxfp8_kmajor(L, static_cast<hipStream_t>(stream)),
+                    "K-major MXFP8 launch");
+}
+
 const char *mxfp4_last_error(void) { return g_last_error.c_str(); }
 
-int32_t mxfp4_version(void) { return 102; }
+int32_t mxfp4_version(void) { return 103; }
 
 }  // extern "C"

@@ -88,6 +88,19 @@ struct Mx8Launch {
 };
 hipError_t launch_mxfp8_rows(const Mx8Launch &L, hipStream_t stream);
 
+// K-major MXFP8 of column-wise / grouped 32-row blocks.
+struct Km8Launch {
+  int dtype, fmt;
+  int64_t rows, cols;
+  const void *x;
+  const int64_t *group_list;  // NULL: dense column-wise blocks
+  int num_groups, list_type;
+  int64_t k_blocks;
+  uint8_t *q;       // [cols, k_blocks * 32]
+  uint8_t *scales;  // [cols, k_blocks]
+};
+hipError_t launch_mxfp8_kmajor(const Km8Launch &L, hipStream_t stream);
+
 // Grouped MX matrix product C = A . B^T (both operands K-contiguous).
 // Element formats as the MFMA format codes: 0 E4M3, 1 E5M2, 4 E2M1.
 enum { kFmtE4M3 = 0, kFmtE5M2 = 1, kFmtE2M1 = 4 };

@@ -15,6 +15,7 @@
 // fp8 conversion (round to nearest even).  8 code bytes per lane leave in one
 // 8-byte store (512 contiguous bytes per wave).
 #include "mxfp4_device.h"
+#include "mxfp4_groups.h"
 #include "mxfp4_kernels.h"
 
 namespace mxfp4 {
@@ -121,7 +122,157 @@ hipError_t mx8_launch(int mode, const Mx8Args &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---- K-major MXFP8 of column-wise / grouped 32-row blocks ---------------------
+//
+// The TN weight-gradient product reduces over tokens, so its two operands
+// (x and grad_output) are quantized in blocks of 32 rows of each column (the
+// hyper-parallel page's grouped quantization for block 32: blocks restart at
+// every expert's first token) and stored with the tokens contiguous: column c
+// becomes row c of q_t, block-row t fills K positions 32t .. 32t + 31 (zero
+// codes past a short block's length).
+//
+// A workgroup takes 4 consecutive block-rows x 64 columns.  Rows arrive with
+// coalesced 16-byte loads into LDS (rows past a block's length as zeros);
+// then every thread owns one (column, block-row): the block max, the exact
+// scaling, the clamp and the hardware fp8 conversion as in the row-wise
+// kernel, and 32 code bytes leave in two 16-byte stores (the 4 block-rows of
+// a column are 4 neighbouring lanes: 128 contiguous bytes).
+
+constexpr int kKm8Cols = 64;
+constexpr int kKm8Blk = 4;
+
+struct Km8Args {
+  const uint8_t *x;
+  uint8_t *q;
+  uint8_t *scales;
+  const int64_t *group_list;
+  int64_t rows, cols, k_blocks, nbt, ntiles_c;
+  int num_groups, list_type;
+};
+
+template <int DT, int FMT>
+__global__ __launch_bounds__(kThreads) void mxfp8_kmajor_kernel(Km8Args A) {
+  constexpr int ES = DT == kBF16 ? 2 : 4;
+  constexpr int ROWB = kKm8Cols * ES;              // bytes of a tile row
+  constexpr int BSTRIDE = 32 * ROWB + 64;          // block stride in LDS (+64: banks)
+  constexpr float MAXN = Fp8T<FMT>::MAXN;
+  __shared__ __align__(16) uint8_t tile[kKm8Blk * BSTRIDE];
+
+  const int tid = threadIdx.x;
+  const int64_t tc = blockIdx.x % A.ntiles_c;
+  const int64_t t0 = (blockIdx.x / A.ntiles_c) * kKm8Blk;
+  const int64_t c0 = tc * kKm8Cols;
+  const int ncol = A.cols - c0 < kKm8Cols ? (int)(A.cols - c0) : kKm8Cols;
+
+  // block-rows t0 .. t0 + 3: first row and length (0 past the last)
+  int64_t start[kKm8Blk], len[kKm8Blk];
+  if (A.group_list) {
+    const int64_t tt[kKm8Blk] = {t0, t0 + 1, t0 + 2, t0 + 3};
+    int grp[kKm8Blk];
+    block_rows_lookup<kKm8Blk>(A.group_list, A.num_groups, A.list_type, A.rows, 5, tt, start, len, grp);
+  } else {
+#pragma unroll
+    for (int b = 0; b < kKm8Blk; ++b) {
+      start[b] = (t0 + b) * 32;
+      const int64_t rem = A.rows - start[b];
+      len[b] = t0 + b < A.nbt ? (rem < 32 ? rem : 32) : 0;
+    }
+  }
+
+  // load: 16 bytes per thread per pass (ROWB / 16 threads per row)
+  constexpr int TPR = ROWB / 16;                   // threads per row
+  constexpr int RPP = kThreads / TPR;              // rows per pass
+  const int lr = tid / TPR, lc = tid % TPR;
+  const bool full_w = ncol == kKm8Cols && (A.cols * ES) % 16 == 0;
+#pragma unroll
+  for (int b = 0; b < kKm8Blk; ++b) {
+#pragma unroll
+    for (int r = lr; r < 32; r += RPP) {
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (r < len[b]) {
+        const uint8_t *src = A.x + ((start[b] + r) * A.cols + c0) * ES + 16 * lc;
+        if (full_w) {
+          v = *reinterpret_cast<const u32x4 *>(src);
+        } else {
+          // ragged right edge or unaligned rows: element by element
+          uint32_t w[4] = {0u, 0u, 0u, 0u};
+          for (int e = 0; e < 16 / ES; ++e) {
+            const int col = lc * (16 / ES) + e;
+            if (col < ncol) {
+              const uint32_t u = ES == 2 ? (uint32_t) * reinterpret_cast<const uint16_t *>(src + e * ES)
+                                         : *reinterpret_cast<const uint32_t *>(src + e * ES);
+              w[(e * ES) / 4] |= ES == 2 ? u << (16 * (e & 1)) : u;
+            }
+          }
+          v = u32x4{w[0], w[1], w[2], w[3]};
+        }
+      }
+      *reinterpret_cast<u32x4 *>(&tile[b * BSTRIDE + r * ROWB + 16 * lc]) = v;
+    }
+  }
+  __syncthreads();
+
+  // compute: lane -> (column, block-row); 4 neighbouring lanes share a column
+  const int b = tid & (kKm8Blk - 1), c = tid >> 2;
+  if (c >= ncol || len[b] == 0) return;
+  float v[32];
+  uint32_t am = 0;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    const uint8_t *p = &tile[b * BSTRIDE + r * ROWB + c * ES];
+    const uint32_t u = ES == 2 ? (uint32_t) * reinterpret_cast<const uint16_t *>(p) << 16
+                               : *reinterpret_cast<const uint32_t *>(p);
+    am = max32(am, u & 0x7FFFFFFFu);
+    v[r] = __builtin_bit_cast(float, u);
+  }
+  const int eb = (int)(am >> 23);  // biased exponent of the block max (0: zero / subnormal)
+  const int e8 = eb - Fp8T<FMT>::EMAX > 0 ? eb - Fp8T<FMT>::EMAX : 0;
+  const float sc = __builtin_bit_cast(float, (uint32_t)(254 - e8) << 23);  // 2^(127 - e8) = 2^-k
+  uint32_t w[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float a0 = __builtin_amdgcn_fmed3f(v[4 * k] * sc, -MAXN, MAXN);
+    const float a1 = __builtin_amdgcn_fmed3f(v[4 * k + 1] * sc, -MAXN, MAXN);
+    const float a2 = __builtin_amdgcn_fmed3f(v[4 * k + 2] * sc, -MAXN, MAXN);
+    const float a3 = __builtin_amdgcn_fmed3f(v[4 * k + 3] * sc, -MAXN, MAXN);
+    w[k] = (uint32_t)cvt2<FMT, true>(a2, a3, cvt2<FMT, false>(a0, a1, 0));
+  }
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  uint8_t *dst = A.q + (c0 + c) * A.k_blocks * 32 + (t0 + b) * 32;
+  *reinterpret_cast<u32x4 *>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+  *reinterpret_cast<u32x4 *>(dst + 16) = u32x4{w[4], w[5], w[6], w[7]};
+  A.scales[(c0 + c) * A.k_blocks + t0 + b] = (uint8_t)e8;
+}
+
 }  // namespace
+
+hipError_t launch_mxfp8_kmajor(const Km8Launch &L, hipStream_t st) {
+  Km8Args a;
+  a.x = static_cast<const uint8_t *>(L.x);
+  a.q = L.q;
+  a.scales = L.scales;
+  a.group_list = L.group_list;
+  a.rows = L.rows;
+  a.cols = L.cols;
+  a.k_blocks = L.k_blocks;
+  a.num_groups = L.num_groups;
+  a.list_type = L.list_type;
+  a.nbt = L.group_list ? L.k_blocks : (L.rows + 31) / 32;
+  a.ntiles_c = (L.cols + kKm8Cols - 1) / kKm8Cols;
+  const int64_t ntiles = (a.nbt + kKm8Blk - 1) / kKm8Blk * a.ntiles_c;
+  if (ntiles == 0) return hipSuccess;
+  if (ntiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)ntiles);
+  if (L.dtype == kBF16) {
+    if (L.fmt == kE4M3) hipLaunchKernelGGL((mxfp8_kmajor_kernel<kBF16, kE4M3>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((mxfp8_kmajor_kernel<kBF16, kE5M2>), grid, dim3(kThreads), 0, st, a);
+  } else {
+    if (L.fmt == kE4M3) hipLaunchKernelGGL((mxfp8_kmajor_kernel<kF32, kE4M3>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((mxfp8_kmajor_kernel<kF32, kE5M2>), grid, dim3(kThreads), 0, st, a);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_mxfp8_rows(const Mx8Launch &L, hipStream_t st) {
   Mx8Args a;

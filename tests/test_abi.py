@@ -47,6 +47,7 @@ def lib():
     i64 = ctypes.c_int64
     op = ctypes.POINTER(Operand)
     L.mxfp4_grouped_matmul.argtypes = [i32, i64, i64, i64, op, op, vp, i32, i32, i64, i32, vp, i64, vp]
+    L.mxfp8_quant_kmajor.argtypes = [dp, i32, vp, vp, i32, i32, i64, vp, vp, vp]
     L.mxfp4_last_error.restype = ctypes.c_char_p
     return L
 
@@ -59,7 +60,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
-              "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant", "mxfp4_grouped_matmul",
+              "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant", "mxfp4_grouped_matmul", "mxfp8_quant_kmajor",
               "mxfp4_last_error", "mxfp4_version"):
         assert n in names
 
@@ -67,7 +68,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mxfp4_version() == 102
+    assert lib.mxfp4_version() == 103
 
 
 def d(dtype=BF16, block=32, rule=0, rows=64, cols=64, sf=6.0, r0=0, r1=0):
@@ -234,6 +235,23 @@ def test_grouped_matmul_validation(lib):
     assert mm(gt=2, a=a, b=b, gl=FAKE, ng=1, kb=8) == EUNSUP     # K-split needs blocks of 32
     assert mm(gt=2, gl=FAKE, ng=1, kb=8, a=ops(lda=240)[0], b=ops()[1]) == EINVAL  # ld < k_blocks*32
     assert mm(M=0) == OK and mm(N=0) == OK                       # nothing to launch
+
+
+def test_mxfp8_kmajor_validation(lib):
+    D = d(rows=100, cols=64)
+    km = lambda fmt, x, gl, ng, lt, kb, q, s: lib.mxfp8_quant_kmajor(ctypes.byref(D), fmt, x, gl, ng, lt, kb, q, s, None)
+    x, q, s = P(), P(FAKE + 65536), P(FAKE + 131072)
+    assert km(2, x, None, 0, 1, 4, q, s) == EINVAL                      # unknown fmt
+    assert km(0, x, None, 0, 1, 3, q, s) == EINVAL                      # needs 4 block-rows
+    assert km(0, x, P(FAKE), 3, 1, 5, q, s) == EINVAL                   # grouped: needs 4 + 3 - 1
+    assert km(0, x, P(FAKE), 0, 1, 9, q, s) == EINVAL                   # list without groups
+    assert km(0, x, P(FAKE), 2, 2, 9, q, s) == EINVAL                   # list type
+    assert km(0, x, None, 0, 1, 4, P(FAKE + 65537), s) == EINVAL        # q misaligned
+    assert km(0, x, None, 0, 1, 4, q, q) == EINVAL                      # alias
+    D.block = 128
+    assert km(0, x, None, 0, 1, 4, q, s) == EUNSUP
+    D.block, D.rows = 32, 0
+    assert km(0, x, None, 0, 1, 0, q, s) == OK                          # nothing to do
 
 
 def test_python_binding_refuses_cpu_tensors():

@@ -9,6 +9,7 @@ import torch
 
 import workloads as W
 from gpu_util import Guarded, dev, host
+from mx_tolerance import mx_matmul_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -132,3 +133,136 @@ def test_mxfp8_grad_output_sampled(oracle):
     qo, so = oracle.mxfp8_rows(x[ri])
     assert np.array_equal(host(q[rit]), qo)
     assert np.array_equal(host(s[rit]), so)
+
+
+# ---- K-major MXFP8 (grouped column-wise operand of the TN product) ------------------
+
+def run_kmajor(x, fmt, group_list=None, list_type=1, k_blocks=None, dev_list=False):
+    rows, cols = x.shape
+    if k_blocks is None:
+        k_blocks = M.mxfp8_kmajor_k_blocks(rows, None if group_list is None else len(group_list))
+    q = Guarded((cols, k_blocks * 32), torch.uint8)
+    s = Guarded((cols, k_blocks), torch.uint8)
+    gl = group_list
+    if gl is not None and dev_list:
+        gl = torch.tensor(list(gl), dtype=torch.int64, device="cuda")
+    M.mxfp8_quant_kmajor(dev(x), q.t, s.t, fmt=fmt, group_list=gl, group_list_type=list_type)
+    torch.cuda.synchronize()
+    q.check_tail()
+    s.check_tail()
+    return host(q.t), host(s.t), k_blocks
+
+
+KM_SHAPES = [(1, 1), (31, 7), (32, 64), (100, 130), (257, 64), (64, 1000), (300, 72)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("shape", KM_SHAPES)
+def test_mxfp8_kmajor_dense(oracle, dtype, fmt, shape):
+    g = np.random.default_rng(shape[0] * 13 + shape[1])
+    a = (g.standard_t(3, size=shape) * np.exp2(g.uniform(-30, 30, (1, shape[1])))).astype(np.float32)
+    a.reshape(-1)[::37] = 0.0
+    a.reshape(-1)[5::41] = -0.0
+    x = W.f32_to_bf16_bits(a) if dtype == "bf16" else a
+    q, s, kb = run_kmajor(x, fmt)
+    qo, so, nbt = oracle.mxfp8_kmajor(x, fmt, k_blocks=kb, fill=0xA5)
+    assert np.array_equal(q[:, :32 * nbt], qo[:, :32 * nbt])
+    assert np.array_equal(s[:, :nbt], so[:, :nbt])
+    assert (q[:, 32 * nbt:] == 0xA5).all() and (s[:, nbt:] == 0xA5).all()   # untouched
+
+
+GROUPED = [([45, 0, 1, 64, 30], 1), (list(np.cumsum([45, 0, 1, 64, 30])), 0), ("forty", 1)]
+
+
+@pytest.mark.parametrize("gl,lt", GROUPED, ids=["counts", "ends", "forty"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mxfp8_kmajor_grouped(oracle, gl, lt, dtype):
+    rows, cols = 140, 96
+    if gl == "forty":
+        rows = 700
+        gl = W.ragged_counts(rows, 40, seed=5, zero_groups=6).tolist()
+    g = np.random.default_rng(len(gl) + rows)
+    a = g.standard_normal((rows, cols)).astype(np.float32)
+    x = W.f32_to_bf16_bits(a) if dtype == "bf16" else a
+    q, s, kb = run_kmajor(x, "e4m3", gl, lt)
+    qo, so, nbt = oracle.mxfp8_kmajor(x, "e4m3", gl, lt, k_blocks=kb, fill=0xA5)
+    assert np.array_equal(q, qo) and np.array_equal(s, so)
+
+
+@pytest.mark.parametrize("list_type,gl", [(1, [100, -5, 50, 400]), (0, [100, 50, 250, 400]), (0, [-7, 33, 20, 300])])
+def test_mxfp8_kmajor_inconsistent_list_is_clamped(oracle, list_type, gl):
+    """A device list with negative counts, ends past rows or decreasing ends is
+    clamped into range (the documented treatment), block-rows as the oracle's
+    of the clamped counts."""
+    from test_gpu_parity import clamp_group_list
+    rows, cols = 300, 72
+    x = W.f32_to_bf16_bits(np.random.default_rng(4).standard_normal((rows, cols)).astype(np.float32))
+    q, s, kb = run_kmajor(x, "e4m3", gl, list_type, dev_list=True)
+    counts = clamp_group_list(gl, rows, list_type)
+    qo, so, nbt = oracle.mxfp8_kmajor(np.ascontiguousarray(x[:int(counts.sum())]), "e4m3", counts, 1,
+                                      k_blocks=kb, fill=0xA5)
+    assert np.array_equal(q, qo) and np.array_equal(s, so)
+
+
+def test_mxfp8_kmajor_moe_sampled(oracle):
+    """The grouped MoE activation at full size (32768 tokens x 7168, 8 experts):
+    sampled columns against the oracle (a column's K-major row depends on that
+    column alone)."""
+    x, counts = W.moe_grouped()
+    rows, cols = x.shape
+    kb = M.mxfp8_kmajor_k_blocks(rows, len(counts))
+    q = torch.empty((cols, kb * 32), dtype=torch.uint8, device="cuda")
+    s = torch.empty((cols, kb), dtype=torch.uint8, device="cuda")
+    M.mxfp8_quant_kmajor(dev(x), q, s, group_list=counts.tolist())
+    torch.cuda.synchronize()
+    ci = np.sort(np.random.default_rng(10).choice(cols, 24, replace=False))
+    cit = torch.from_numpy(ci).cuda()
+    qo, so, nbt = oracle.mxfp8_kmajor(np.ascontiguousarray(x[:, ci]), "e4m3", counts, 1, k_blocks=kb)
+    assert np.array_equal(host(q[cit])[:, :32 * nbt], qo[:, :32 * nbt])
+    assert np.array_equal(host(s[cit])[:, :nbt], so[:, :nbt])
+
+
+def test_tn_weight_gradient_end_to_end(oracle):
+    """TN: x and grad_output quantized on the GPU into K-major grouped MXFP8,
+    then the K-split grouped matmul gives each expert's dW = x_g^T dy_g; the
+    operands bit-exact against the oracle's, the products against the oracle's
+    exact sums within the matrix-core bound (mx_tolerance)."""
+    g = np.random.default_rng(17)
+    counts = [70, 0, 33, 97]
+    T, Kin, N = sum(counts), 96, 80
+    x = W.f32_to_bf16_bits(g.standard_normal((T, Kin)).astype(np.float32))
+    dy = W.f32_to_bf16_bits(g.standard_normal((T, N)).astype(np.float32))
+    kb = M.mxfp8_kmajor_k_blocks(T, len(counts))
+    qa = torch.empty((Kin, kb * 32), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((Kin, kb), dtype=torch.uint8, device="cuda")
+    qb = torch.empty((N, kb * 32), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((N, kb), dtype=torch.uint8, device="cuda")
+    M.mxfp8_quant_kmajor(dev(x), qa, sa, group_list=counts)
+    M.mxfp8_quant_kmajor(dev(dy), qb, sb, group_list=counts)
+    c = torch.empty((len(counts), Kin, N), dtype=torch.float32, device="cuda")
+    M.mxfp4_grouped_matmul(qa, sa, qb, sb, c, K=T, group_list=counts, group_type=M.GROUP_K, b_fmt="e4m3",
+                           k_blocks=kb)
+    torch.cuda.synchronize()
+    qao, sao, nbt = oracle.mxfp8_kmajor(x, "e4m3", counts, 1, k_blocks=kb, fill=0)
+    qbo, sbo, _ = oracle.mxfp8_kmajor(dy, "e4m3", counts, 1, k_blocks=kb, fill=0)
+    # the operands themselves are bit-exact
+    assert np.array_equal(host(qa)[:, :32 * nbt], qao[:, :32 * nbt])
+    assert np.array_equal(host(qb)[:, :32 * nbt], qbo[:, :32 * nbt])
+    assert np.array_equal(host(sa)[:, :nbt], sao[:, :nbt]) and np.array_equal(host(sb)[:, :nbt], sbo[:, :nbt])
+    sao[:, nbt:] = 127
+    sbo[:, nbt:] = 127
+    A = oracle.mxfp8_decode(qao, sao, "e4m3", np.float64)
+    B = oracle.mxfp8_decode(qbo, sbo, "e4m3", np.float64)
+    padded = [32 * (-(-cc // 32)) for cc in counts]
+    exp = oracle.grouped_matmul(A, np.ascontiguousarray(B.T), padded, oracle.GROUP_K, 1)
+    got = host(c).astype(np.float64)
+    k0 = 0
+    for gi, pc in enumerate(padded):
+        if pc:
+            bound = mx_matmul_bound(A[:, k0:k0 + pc], B[:, k0:k0 + pc]) + 1e-30
+            ratio = np.abs(got[gi] - exp[gi]) / bound
+            w = np.unravel_index(ratio.argmax(), ratio.shape)
+            assert (ratio <= 1).all(), f"group {gi}: worst error / bound {ratio.max():.3g} at {w}"
+        k0 += pc
+    assert (got[1] == 0).all()   # the empty expert
