@@ -401,9 +401,17 @@ def bench_all(M, lib, W, torch, args):
     mcalls = [Call(lib.mxfp8_quant, ctypes.byref(d), 0, vp(xs[i].data_ptr()), vp(q8[i].data_ptr()),
                    vp(s8[i].data_ptr()), stream) for i in range(2)]
     rec("mxfp8_e4m3_32768x7168", R * C * (2 + 1 + 1 / 32), R * C, _time_calls(torch, mcalls, 30))
-    del xs
-
     del q8, s8
+    # K-major grouped MXFP8 of the same tokens (the TN operand; block-rows
+    # padded per group)
+    kb8 = M.mxfp8_kmajor_k_blocks(R, len(counts))
+    k8 = [torch.empty((C, kb8 * 32), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    t8 = [torch.empty((C, kb8), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    k8calls = [Call(lib.mxfp8_quant_kmajor, ctypes.byref(d), 0, vp(xs[i].data_ptr()), vp(gl.data_ptr()), 8, 1, kb8,
+                    vp(k8[i].data_ptr()), vp(t8[i].data_ptr()), stream) for i in range(2)]
+    rec("mxfp8_kmajor_grouped_32768x7168", R * C * 2 + C * nbt * (32 + 1), R * C, _time_calls(torch, k8calls, 30))
+    del xs, k8, t8
+
     bench_gemm(M, W, torch, out, gl, counts)
     return out
 
