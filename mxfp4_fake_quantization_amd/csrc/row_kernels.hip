@@ -18,22 +18,29 @@
 namespace mxfp4 {
 namespace {
 
-// Chunks per thread: 1 for small tensors (more, shorter workgroups overlap
-// their loads and stores better), 2 above kRowBigChunks chunks.
+// Chunks per thread and workgroup size, measured on MI355X at 4096x4096 and
+// 28672x8192: the y / bitmap forward streams best with one chunk per thread
+// in one-wave workgroups (many short workgroups keep loads and stores
+// overlapped across waves); the packing forward with two chunks per thread
+// in four-wave workgroups.
 #ifndef MXFP4_ROW_U_SMALL
 #define MXFP4_ROW_U_SMALL 1
 #endif
 #ifndef MXFP4_ROW_U_BIG
-#define MXFP4_ROW_U_BIG 2
+#define MXFP4_ROW_U_BIG 1
 #endif
 #ifndef MXFP4_PACK_U
 #define MXFP4_PACK_U 2
 #endif
 constexpr int64_t kRowBigChunks = int64_t(8) << 20;
 #ifndef MXFP4_ROW_THREADS
-#define MXFP4_ROW_THREADS 256
+#define MXFP4_ROW_THREADS 64
 #endif
-constexpr int kRowThreads = MXFP4_ROW_THREADS;  // threads per workgroup
+#ifndef MXFP4_PACK_THREADS
+#define MXFP4_PACK_THREADS 256
+#endif
+constexpr int kRowThreads = MXFP4_ROW_THREADS;    // threads per workgroup, y / bitmap
+constexpr int kPackThreads = MXFP4_PACK_THREADS;  // threads per workgroup, packed codes
 
 enum { kModeFlat = 0, kModeRowsVec = 1, kModeRowsScalar = 2 };
 
@@ -135,20 +142,20 @@ __device__ __forceinline__ void row_emit(const RowArgs &A, const uint32_t *wv, c
     }
 }
 
-template <int DT, int B, int RULE, int MODE, int U, bool FULL>
+template <int DT, int B, int RULE, int MODE, int U, int T, bool FULL>
 __device__ __forceinline__ void row_fwd_body(const RowArgs &A) {
   constexpr int G = B / 8;
   constexpr int NW = ChunkT<DT>::NW;
   constexpr int ES = ChunkT<DT>::ES;
   const int tid = threadIdx.x;
-  const int64_t base = (int64_t)blockIdx.x * (kRowThreads * U);
+  const int64_t base = (int64_t)blockIdx.x * (T * U);
 
   uint32_t w[U][NW];
   int64_t off[U], row[U], cr[U];
   int nval[U];
 #pragma unroll
   for (int s = 0; s < U; ++s) {
-    const int64_t i = base + s * kRowThreads + tid;
+    const int64_t i = base + s * T + tid;
     if (MODE == kModeFlat) {
       row[s] = 0;
       cr[s] = i;
@@ -191,11 +198,11 @@ __device__ __forceinline__ void row_fwd_body(const RowArgs &A) {
 
     if (__builtin_expect(__any(bp.slow), 0))
       row_emit<DT, G, MODE, U, FULL, true>(A, w[s], bp, off[s], row[s], cr[s], nval[s],
-                                          base + s * kRowThreads + tid);
+                                          base + s * T + tid);
     else
       row_emit<DT, G, MODE, U, FULL, false>(A, w[s], bp, off[s], row[s], cr[s], nval[s],
-                                           base + s * kRowThreads + tid);
-    if ((A.emit & kEmitScales) && (tid % G) == 0 && base + s * kRowThreads + tid < A.nchunks) {
+                                           base + s * T + tid);
+    if ((A.emit & kEmitScales) && (tid % G) == 0 && base + s * T + tid < A.nchunks) {
       const int64_t bi = MODE == kModeFlat ? cr[s] / G : row[s] * A.nb + cr[s] / G;
       st_small(A.scales + bi, (uint8_t)bp.e8);
     }
@@ -204,29 +211,31 @@ __device__ __forceinline__ void row_fwd_body(const RowArgs &A) {
 
 // A workgroup whose chunks are all in range (every one but possibly the
 // last, in the flat layout) takes the branch-free load path.
-template <int DT, int B, int RULE, int MODE, int U>
-__global__ __launch_bounds__(kRowThreads) void row_fwd_kernel(RowArgs A) {
-  if (MODE == kModeFlat && (int64_t)(blockIdx.x + 1) * (kRowThreads * U) <= A.nchunks)
-    row_fwd_body<DT, B, RULE, MODE, U, true>(A);
+template <int DT, int B, int RULE, int MODE, int U, int T>
+__global__ __launch_bounds__(T) void row_fwd_kernel(RowArgs A) {
+  if (MODE == kModeFlat && (int64_t)(blockIdx.x + 1) * (T * U) <= A.nchunks)
+    row_fwd_body<DT, B, RULE, MODE, U, T, true>(A);
   else
-    row_fwd_body<DT, B, RULE, MODE, U, false>(A);
+    row_fwd_body<DT, B, RULE, MODE, U, T, false>(A);
+}
+
+template <int DT, int B, int RULE, int MODE, int U, int T>
+hipError_t launch_shape(const RowArgs &a, hipStream_t st) {
+  const int64_t nwg = (a.nchunks + (int64_t)T * U - 1) / ((int64_t)T * U);
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, MODE, U, T>), dim3((unsigned)nwg), dim3(T), 0, st, a);
+  return hipGetLastError();
 }
 
 template <int DT, int B, int RULE, int MODE>
 hipError_t launch_u(const RowArgs &a, hipStream_t st) {
-  int u = 1;
-  if (MODE == kModeFlat)
-    u = (a.emit & kEmitCodes) ? MXFP4_PACK_U
-                              : (a.nchunks > kRowBigChunks ? MXFP4_ROW_U_BIG : MXFP4_ROW_U_SMALL);
-  const int64_t nwg = (a.nchunks + (int64_t)kRowThreads * u - 1) / ((int64_t)kRowThreads * u);
-  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)nwg);
-  switch (u) {
-    case 4: hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, MODE, 4>), grid, dim3(kRowThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, MODE, 2>), grid, dim3(kRowThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((row_fwd_kernel<DT, B, RULE, MODE, 1>), grid, dim3(kRowThreads), 0, st, a); break;
+  if constexpr (MODE == kModeFlat) {
+    if (a.emit & kEmitCodes) return launch_shape<DT, B, RULE, MODE, MXFP4_PACK_U, kPackThreads>(a, st);
+    if (a.nchunks > kRowBigChunks) return launch_shape<DT, B, RULE, MODE, MXFP4_ROW_U_BIG, kRowThreads>(a, st);
+    return launch_shape<DT, B, RULE, MODE, MXFP4_ROW_U_SMALL, kRowThreads>(a, st);
+  } else {
+    return launch_shape<DT, B, RULE, MODE, 1, kRowThreads>(a, st);
   }
-  return hipGetLastError();
 }
 
 template <int DT, int B, int RULE>

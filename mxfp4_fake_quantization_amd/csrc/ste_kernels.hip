@@ -16,19 +16,19 @@
 namespace mxfp4 {
 namespace {
 
-// Pieces per thread: 2 for small tensors, 1 above kSteBigChunks pieces
-// (measured on MI355X: short workgroups stream large tensors best, while
-// small launches are dominated by their start-up and prefer more loads in
-// flight per thread).
+// Pieces per thread and workgroup size (measured on MI355X): one piece per
+// thread in one-wave workgroups streams both the 4096x4096 and the
+// 28672x8192 gradient best; short workgroups keep loads and stores
+// overlapped across waves.
 #ifndef MXFP4_STE_U_SMALL
-#define MXFP4_STE_U_SMALL 2
+#define MXFP4_STE_U_SMALL 1
 #endif
 #ifndef MXFP4_STE_U_BIG
 #define MXFP4_STE_U_BIG 1
 #endif
 constexpr int64_t kSteBigChunks = int64_t(8) << 20;
 #ifndef MXFP4_STE_THREADS
-#define MXFP4_STE_THREADS 256
+#define MXFP4_STE_THREADS 64
 #endif
 constexpr int kSteThreads = MXFP4_STE_THREADS;  // threads per workgroup (row walk)
 enum { kModeFlat = 0, kModeRowsVec = 1, kModeRowsScalar = 2 };
