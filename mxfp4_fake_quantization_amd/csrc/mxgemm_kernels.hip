@@ -19,17 +19,21 @@
 // 0-15 are K 16h..16h+15, bytes 16-31 are K 32+16h..; B fp4: nibble j is K
 // 32h+j; result register v of lane l is row 8(v/4) + 4h + v%4, column l%32).
 //
-// Work split: a 256-thread workgroup computes a (64 WM) x (64 WN) tile as
-// 2 x 2 waves of WM x WN MFMA tiles, stepping K by 128.  Both operand slices
-// go global -> registers -> LDS (double-buffered, XOR-swizzled 16-byte
+// Work split: a 512-thread workgroup computes a 256 x 256 tile as 4 x 2
+// waves of 2 x 4 MFMA tiles (two waves per SIMD, so one wave's LDS and
+// address work overlaps the other's MFMAs), stepping K by 128.  Both operand
+// slices go global -> registers -> LDS (double-buffered, XOR-swizzled 16-byte
 // slots, conflict-free for 16- and 32-lane read phases) while the previous
-// step's MFMAs run.  Scale bytes travel in chunks of 32 K-blocks per tile row
-// (8 steps), also double-buffered in LDS and streamed one coalesced slice per
-// step, so every lane reads its scale bytes with one LDS load per tile.  The
-// loop body is one basic block: prefetch, MFMAs, then the prefetch waits and
-// LDS stores.  Blocks outside a K range load as zero codes with scale 2^0;
-// rows and columns past the tile edge load a valid neighbour and are not
-// stored.
+// step's MFMAs run.  An E2M1 B row holds only 64 bytes per K step, half a
+// 128-byte cache line; B is therefore staged two K steps at a time (one
+// whole line per row, half of the tile's rows loaded during each step), so
+// every B request fetches a full line.  Scale bytes travel in chunks of 32
+// K-blocks per tile row (8 steps), also double-buffered in LDS and streamed
+// one coalesced slice per step, so every lane reads its scale bytes with one
+// LDS load per tile.  The loop body is one basic block: prefetch, MFMAs, then
+// the prefetch waits and LDS stores.  Blocks outside a K range load as zero
+// codes with scale 2^0; rows and columns past the tile edge load a valid
+// neighbour and are not stored.
 #include "mxfp4_device.h"
 #include "mxfp4_groups.h"
 #include "mxfp4_kernels.h"
@@ -87,16 +91,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
   constexpr int NT = kGemmThreads;
   constexpr int BM = kBM, BN = kBN;
   constexpr bool B4 = BF == kFmtE2M1;
-  constexpr int BROW = B4 ? 64 : 128;           // B bytes per row per K step
+  // B4: a 128-byte LDS row holds two K steps (pair) of E2M1 codes; fp8 B:
+  // one K step.  Either way 8 slots of 16 bytes per row.
   constexpr int A_LD = BM * 8 / NT;             // 16-byte A loads per thread per step
-  constexpr int A_RSTEP = NT / 8;               // rows per A load pass
-  constexpr int B_SLOTS = BROW / 16;
-  constexpr int B_LD = BN * B_SLOTS / NT;
-  constexpr int B_RSTEP = NT / B_SLOTS;
+  constexpr int RSTEP = NT / 8;                 // rows per load pass (A and B)
+  constexpr int B_LD = BN * 8 / NT / (B4 ? 2 : 1);  // 16-byte B loads per thread per step
   static_assert(WVM * WVN * 64 == NT && BM == 32 * WM * WVM && BN == 32 * WN * WVN, "tile shape");
   static_assert(BM / 8 * 8 == NT / 2 && BN / 8 * 8 == NT / 2, "one scale dword per thread per step");
   __shared__ __align__(16) uint8_t sA[2][BM * 128];
-  __shared__ __align__(16) uint8_t sB[2][BN * BROW];
+  __shared__ __align__(16) uint8_t sB[2][BN * 128];
   __shared__ __align__(16) uint8_t sSA[2][BM * 32];  // scale chunks (32 K-blocks per row)
   __shared__ __align__(16) uint8_t sSB[2][BN * 32];
 
@@ -144,23 +147,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
   const int64_t nlen = P.N - n0 < BN ? P.N - n0 : BN;
 
   // ---- per-thread load offsets (32-bit, from per-tile bases) ----
+  // Thread (row r, slot c): r = tid / 8 + RSTEP * i, c = tid % 8 (16 bytes).
   const uint8_t *abase = P.a + m0 * P.lda;
   const uint8_t *asbase = P.as + m0 * P.ldas;
   bbase += n0 * P.ldb;
   bsbase += n0 * P.ldbs;
-  const int ar = tid >> 3, ac = tid & 7;                  // A: NT/8 rows x 8 slots per pass
-  const int br = tid / B_SLOTS, bc = tid % B_SLOTS;       // B: NT/B_SLOTS rows x B_SLOTS slots
-  uint32_t aoff[A_LD], boff[B_LD];
+  const int lr = tid >> 3, lc = tid & 7;
+  uint32_t aoff[A_LD], boff[B4 ? 2 : 1][B_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
-    const int row = ar + A_RSTEP * i;
-    aoff[i] = (uint32_t)((row < mlen ? row : mlen - 1) * P.lda) + 16 * ac;
+    const int row = lr + RSTEP * i;
+    aoff[i] = (uint32_t)((row < mlen ? row : mlen - 1) * P.lda) + 16 * lc;
   }
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int row = br + B_RSTEP * i;
-    boff[i] = (uint32_t)((row < nlen ? row : nlen - 1) * P.ldb) + 16 * bc;
-  }
+  for (int t = 0; t < (B4 ? 2 : 1); ++t)
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const int row = t * (BN / 2) + lr + RSTEP * i;  // B4: half t of the rows
+      boff[t][i] = (uint32_t)((row < nlen ? row : nlen - 1) * P.ldb) + 16 * lc;
+    }
   const int wr0 = (wave / WVN) * 32 * WM, wc0 = (wave % WVN) * 32 * WN;
 
   // ---- scale bytes: chunks of 32 K-blocks (8 steps) staged in LDS ----
@@ -212,45 +217,48 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
     *reinterpret_cast<uint32_t *>(dst + (piece * 32 + sr) * 32 + 4 * sd) = v;
   };
 
+  // Codes global -> registers.  A: the K step starting at block kb (slot c =
+  // blocks kb + c/2).  B fp8: the same; B E2M1: half t of the rows of the
+  // pair of steps starting at block kb (slot c = block kb + c).  The masked
+  // forms (steps or pairs that can be partial) read clamped in-bounds
+  // addresses and zero slots outside [klo, kb1) when storing.
   u32x4 ra[A_LD], rb[B_LD];
   bool ain = true, bin = true;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  // Codes of the K step starting at block kb: global -> registers.  The
-  // masked form (first and last steps) reads clamped in-bounds addresses and
-  // zeroes slots outside [klo, kb1) when storing.
-  auto load_full = [&](int64_t kb) {
-    const uint8_t *ab = abase + (kb << 5);
-    const uint8_t *bb = bbase + (kb << (B4 ? 4 : 5));
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4 *>(ab + aoff[i]);
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) rb[i] = *reinterpret_cast<const u32x4 *>(bb + boff[i]);
-  };
-  auto load_masked = [&](int64_t kb) {
-    const int64_t last = kb1 - 1;
-    // 16-byte slot ac of A holds K 16ac..16ac+15; slot bc of B holds K 32bc..
-    // (fp4) or 16bc.. (fp8)
-    const int64_t ablk = kb + (ac >> 1), bblk = B4 ? kb + bc : kb + (bc >> 1);
-    ain = ablk >= klo && ablk < kb1;
-    bin = bblk >= klo && bblk < kb1;
-    const int64_t at = ain ? (kb << 5) : (last << 5) - 16 * ac;
-    const int64_t bt = bin ? (kb << (B4 ? 4 : 5)) : (B4 ? (last << 4) - 16 * bc : (last << 5) - 16 * bc);
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4 *>(abase + at + aoff[i]);
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) rb[i] = *reinterpret_cast<const u32x4 *>(bbase + bt + boff[i]);
-  };
-  auto store_codes = [&](int buf, bool masked) {
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int row = ar + A_RSTEP * i;
-      *reinterpret_cast<u32x4 *>(&sA[buf][row * 128 + swz_a(row, ac)]) = (!masked || ain) ? ra[i] : zero4;
+  constexpr int BSH = B4 ? 4 : 5;  // log2 bytes per 32-element block of B
+  constexpr int BBLK = B4 ? 1 : 2; // slots per block of B
+  auto load_a = [&](int64_t kb, bool masked) {
+    int64_t at = kb << 5;
+    if (masked) {
+      const int64_t ablk = kb + (lc >> 1);
+      ain = ablk >= klo && ablk < kb1;
+      if (!ain) at = ((kb1 - 1) << 5) - 16 * lc;
     }
 #pragma unroll
+    for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const u32x4 *>(abase + at + aoff[i]);
+  };
+  auto load_b = [&](int64_t kb, int t, bool masked) {
+    int64_t bt = kb << BSH;
+    if (masked) {
+      const int64_t bblk = kb + lc / BBLK;
+      bin = bblk >= klo && bblk < kb1;
+      if (!bin) bt = ((kb1 - 1) << BSH) - 16 * lc;
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) rb[i] = *reinterpret_cast<const u32x4 *>(bbase + bt + boff[t][i]);
+  };
+  auto store_a = [&](int buf, bool masked) {
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      const int row = lr + RSTEP * i;
+      *reinterpret_cast<u32x4 *>(&sA[buf][row * 128 + swz_a(row, lc)]) = (!masked || ain) ? ra[i] : zero4;
+    }
+  };
+  auto store_b = [&](int buf, int t, bool masked) {
+#pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-      const int row = br + B_RSTEP * i;
-      const int off = B4 ? row * 64 + swz_b4(row, bc) : row * 128 + swz_a(row, bc);
-      *reinterpret_cast<u32x4 *>(&sB[buf][off]) = (!masked || bin) ? rb[i] : zero4;
+      const int row = t * (BN / 2) + lr + RSTEP * i;
+      *reinterpret_cast<u32x4 *>(&sB[buf][row * 128 + swz_a(row, lc)]) = (!masked || bin) ? rb[i] : zero4;
     }
   };
 
@@ -262,13 +270,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // One K step: this step's scales from LDS, the prefetch of step st + 1
-  // (PF: 0 none, 1 unmasked, 2 masked) and a scale slice, the MFMAs, then the
-  // LDS stores of the prefetch and the barrier.
-  auto step = [&](int64_t st, auto pf) {
-    constexpr int PF = decltype(pf)::value;
+  // One K step: this step's scales from LDS, the prefetches (PA for A and the
+  // scale slice, PB for B; 0 none, 1 unmasked, 2 masked), the MFMAs, then the
+  // LDS stores of the prefetch and the barrier.  fp8 B follows A's step; E2M1
+  // B loads half of the next pair of steps during each step of a pair.
+  auto step = [&](int64_t st, auto pfa, auto pfb) {
+    constexpr int PA = decltype(pfa)::value, PB = decltype(pfb)::value;
     const int buf = (int)(st & 1), sbuf = (int)((st >> 3) & 1), piece = (int)(st & 7);
+    const int bbuf = B4 ? (int)((st >> 1) & 1) : buf;
+    const int t = (int)(st & 1);
     const int64_t kb = kb0 + 4 * st;
+    const int64_t kbn = B4 ? kb0 + 8 * ((st >> 1) + 1) : kb + 4;  // B's prefetch target
     // scale bytes of blocks kb + h (s = 0) and kb + 2 + h (s = 1)
     uint32_t csa[WM][2], csb[WN][2];
     {
@@ -288,9 +300,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
         csb[j][1] = (w >> (8 * (qb1 & 3))) & 0xFFu;
       }
     }
-    if (PF == 1) load_full(kb + 4);
-    if (PF == 2) load_masked(kb + 4);
-    if (PF != 0) load_slice((st >> 3) + 1, piece);
+    if (PA != 0) load_a(kb + 4, PA == 2);
+    if (PB != 0) load_b(kbn, B4 ? t : 0, PB == 2);
+    if (PA != 0) load_slice((st >> 3) + 1, piece);
 
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -307,7 +319,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
       for (int j = 0; j < WN; ++j) {
         const int n = wc0 + 32 * j + l32;
         if (B4) {
-          const u32x4 v = *reinterpret_cast<const u32x4 *>(&sB[buf][n * 64 + swz_b4(n, 2 * s + h)]);
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(&sB[bbuf][n * 128 + swz_a(n, 4 * t + 2 * s + h)]);
           fb[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
         } else {
           const u32x4 lo = *reinterpret_cast<const u32x4 *>(&sB[buf][n * 128 + swz_a(n, 4 * s + h)]);
@@ -323,29 +335,49 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
                                                                       (int)csa[i][s], 0, (int)csb[j][s]);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the waits for the prefetch after the MFMAs
-    if (PF == 1) store_codes(buf ^ 1, false);
-    if (PF == 2) store_codes(buf ^ 1, true);
-    if (PF != 0) {
-      store_slice(sbuf ^ 1, piece);
+    if (PA != 0) store_a(buf ^ 1, PA == 2);
+    if (PB != 0) store_b(bbuf ^ 1, B4 ? t : 0, PB == 2);
+    if (PA != 0 || PB != 0) {
+      if (PA != 0) store_slice(sbuf ^ 1, piece);
       __syncthreads();
     }
   };
 
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   const int64_t nsteps = (kb1 - kb0 + 3) >> 2;
   if (nsteps > 0) {
-    load_masked(kb0);
-    store_codes(0, true);
+    load_a(kb0, true);
+    store_a(0, true);
+#pragma unroll
+    for (int t = 0; t < (B4 ? 2 : 1); ++t) {
+      load_b(kb0, t, true);
+      store_b(0, t, true);
+    }
     for (int piece = 0; piece < 8; ++piece) {
       load_slice(0, piece);
       store_slice(0, piece);
     }
     __syncthreads();
-    // only the first and the last step can be partial: the steps in between
-    // are prefetched unmasked
     int64_t st = 0;
-    for (; st + 2 < nsteps; ++st) step(st, std::integral_constant<int, 1>{});
-    if (st + 1 < nsteps) step(st++, std::integral_constant<int, 2>{});
-    step(st, std::integral_constant<int, 0>{});
+    if (B4) {
+      // only the first and the last step (A) or pair (B) can be partial: the
+      // steps before the last two pairs prefetch unmasked; then straight-line
+      // code for the last (up to four) steps
+      const int64_t npairs = (nsteps + 1) >> 1;
+      if (npairs >= 2) {
+        for (; st < 2 * npairs - 4; ++st) step(st, I1{}, I1{});
+        step(st++, I2{}, I2{});
+        step(st++, I2{}, I2{});
+      }
+      if (nsteps - st == 2) step(st++, I2{}, I0{});
+      step(st, I0{}, I0{});
+    } else {
+      for (; st + 2 < nsteps; ++st) step(st, I1{}, I1{});
+      if (st + 1 < nsteps) step(st++, I2{}, I2{});
+      step(st, I0{}, I0{});
+    }
   }
 
   // ---- epilogue: row 8(v/4) + 4h + v%4, column l32 of each 32x32 tile ----
