@@ -131,15 +131,17 @@ hipError_t mx8_launch(int mode, const Mx8Args &a, hipStream_t st) {
 // becomes row c of q_t, block-row t fills K positions 32t .. 32t + 31 (zero
 // codes past a short block's length).
 //
-// A workgroup takes 4 consecutive block-rows x 64 columns.  Rows arrive with
+// A workgroup takes 4 consecutive block-rows x 128 columns (256-byte bf16 row
+// segments read more efficiently than 128-byte ones).  Rows arrive with
 // coalesced 16-byte loads into LDS (rows past a block's length as zeros);
 // then every thread owns one (column, block-row): the block max, the exact
 // scaling, the clamp and the hardware fp8 conversion as in the row-wise
 // kernel, and 32 code bytes leave in two 16-byte stores (the 4 block-rows of
 // a column are 4 neighbouring lanes: 128 contiguous bytes).
 
-constexpr int kKm8Cols = 64;
+constexpr int kKm8Cols = 128;
 constexpr int kKm8Blk = 4;
+constexpr int kKm8Threads = kKm8Cols * kKm8Blk;  // one thread per (column, block-row)
 
 struct Km8Args {
   const uint8_t *x;
@@ -151,7 +153,7 @@ struct Km8Args {
 };
 
 template <int DT, int FMT>
-__global__ __launch_bounds__(kThreads) void mxfp8_kmajor_kernel(Km8Args A) {
+__global__ __launch_bounds__(kKm8Threads) void mxfp8_kmajor_kernel(Km8Args A) {
   constexpr int ES = DT == kBF16 ? 2 : 4;
   constexpr int ROWB = kKm8Cols * ES;              // bytes of a tile row
   constexpr int BSTRIDE = 32 * ROWB + 64;          // block stride in LDS (+64: banks)
@@ -179,23 +181,45 @@ __global__ __launch_bounds__(kThreads) void mxfp8_kmajor_kernel(Km8Args A) {
     }
   }
 
-  // load: 16 bytes per thread per pass (ROWB / 16 threads per row)
+  // load: 16 bytes per thread per pass (ROWB / 16 threads per row).  With
+  // whole 16-byte pieces (the usual case) every load is issued before any is
+  // stored, rows past a block's length reading the tensor's first bytes and
+  // storing zeros, so a workgroup has all of its 16 KiB (bf16) in flight;
+  // loads under a per-lane branch would each be waited for in turn.
   constexpr int TPR = ROWB / 16;                   // threads per row
-  constexpr int RPP = kThreads / TPR;              // rows per pass
+  constexpr int RPP = kKm8Threads / TPR;           // rows per pass
+  constexpr int NP = 32 / RPP;                     // passes per block
   const int lr = tid / TPR, lc = tid % TPR;
   const bool full_w = ncol == kKm8Cols && (A.cols * ES) % 16 == 0;
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  if (full_w) {
+    u32x4 v[kKm8Blk][NP];
 #pragma unroll
-  for (int b = 0; b < kKm8Blk; ++b) {
+    for (int b = 0; b < kKm8Blk; ++b)
 #pragma unroll
-    for (int r = lr; r < 32; r += RPP) {
-      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (r < len[b]) {
-        const uint8_t *src = A.x + ((start[b] + r) * A.cols + c0) * ES + 16 * lc;
-        if (full_w) {
-          v = *reinterpret_cast<const u32x4 *>(src);
-        } else {
+      for (int p = 0; p < NP; ++p) {
+        const int r = lr + RPP * p;
+        const bool ok = r < len[b];
+        const uint8_t *src = ok ? A.x + ((start[b] + r) * A.cols + c0) * ES + 16 * lc : A.x;
+        v[b][p] = *reinterpret_cast<const u32x4 *>(src);
+      }
+#pragma unroll
+    for (int b = 0; b < kKm8Blk; ++b)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int r = lr + RPP * p;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(&tile[b * BSTRIDE + r * ROWB + 16 * lc]) = r < len[b] ? v[b][p] : z;
+      }
+  } else {
+#pragma unroll
+    for (int b = 0; b < kKm8Blk; ++b) {
+#pragma unroll
+      for (int r = lr; r < 32; r += RPP) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r < len[b]) {
           // ragged right edge or unaligned rows: element by element
+          const uint8_t *src = A.x + ((start[b] + r) * A.cols + c0) * ES + 16 * lc;
           uint32_t w[4] = {0u, 0u, 0u, 0u};
           for (int e = 0; e < 16 / ES; ++e) {
             const int col = lc * (16 / ES) + e;
@@ -207,8 +231,8 @@ __global__ __launch_bounds__(kThreads) void mxfp8_kmajor_kernel(Km8Args A) {
           }
           v = u32x4{w[0], w[1], w[2], w[3]};
         }
+        *reinterpret_cast<u32x4 *>(&tile[b * BSTRIDE + r * ROWB + 16 * lc]) = v;
       }
-      *reinterpret_cast<u32x4 *>(&tile[b * BSTRIDE + r * ROWB + 16 * lc]) = v;
     }
   }
   __syncthreads();
@@ -238,7 +262,6 @@ __global__ __launch_bounds__(kThreads) void mxfp8_kmajor_kernel(Km8Args A) {
     const float a3 = __builtin_amdgcn_fmed3f(v[4 * k + 3] * sc, -MAXN, MAXN);
     w[k] = (uint32_t)cvt2<FMT, true>(a2, a3, cvt2<FMT, false>(a0, a1, 0));
   }
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   uint8_t *dst = A.q + (c0 + c) * A.k_blocks * 32 + (t0 + b) * 32;
   *reinterpret_cast<u32x4 *>(dst) = u32x4{w[0], w[1], w[2], w[3]};
   *reinterpret_cast<u32x4 *>(dst + 16) = u32x4{w[4], w[5], w[6], w[7]};
@@ -265,11 +288,11 @@ hipError_t launch_mxfp8_kmajor(const Km8Launch &L, hipStream_t st) {
   if (ntiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)ntiles);
   if (L.dtype == kBF16) {
-    if (L.fmt == kE4M3) hipLaunchKernelGGL((mxfp8_kmajor_kernel<kBF16, kE4M3>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((mxfp8_kmajor_kernel<kBF16, kE5M2>), grid, dim3(kThreads), 0, st, a);
+    if (L.fmt == kE4M3) hipLaunchKernelGGL((mxfp8_kmajor_kernel<kBF16, kE4M3>), grid, dim3(kKm8Threads), 0, st, a);
+    else hipLaunchKernelGGL((mxfp8_kmajor_kernel<kBF16, kE5M2>), grid, dim3(kKm8Threads), 0, st, a);
   } else {
-    if (L.fmt == kE4M3) hipLaunchKernelGGL((mxfp8_kmajor_kernel<kF32, kE4M3>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((mxfp8_kmajor_kernel<kF32, kE5M2>), grid, dim3(kThreads), 0, st, a);
+    if (L.fmt == kE4M3) hipLaunchKernelGGL((mxfp8_kmajor_kernel<kF32, kE4M3>), grid, dim3(kKm8Threads), 0, st, a);
+    else hipLaunchKernelGGL((mxfp8_kmajor_kernel<kF32, kE5M2>), grid, dim3(kKm8Threads), 0, st, a);
   }
   return hipGetLastError();
 }
