@@ -315,24 +315,34 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
         const u32x4 hi = *reinterpret_cast<const u32x4 *>(&sA[buf][r * 128 + swz_a(r, 4 * s + 2 + h)]);
         fa[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
+      if (B4) {
 #pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        const int n = wc0 + 32 * j + l32;
-        if (B4) {
+        for (int j = 0; j < WN; ++j) {
+          const int n = wc0 + 32 * j + l32;
           const u32x4 v = *reinterpret_cast<const u32x4 *>(&sB[bbuf][n * 128 + swz_a(n, 4 * t + 2 * s + h)]);
           fb[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        } else {
+        }
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AF, BF, 0,
+                                                                        (int)csa[i][s], 0, (int)csb[j][s]);
+      } else {
+        // fp8 B fragments are 8 registers each: one at a time, so that the fp8 x
+        // fp8 form stays close to the register budget
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          const int n = wc0 + 32 * j + l32;
           const u32x4 lo = *reinterpret_cast<const u32x4 *>(&sB[buf][n * 128 + swz_a(n, 4 * s + h)]);
           const u32x4 hi = *reinterpret_cast<const u32x4 *>(&sB[buf][n * 128 + swz_a(n, 4 * s + 2 + h)]);
           fb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+          for (int i = 0; i < WM; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AF, BF, 0,
+                                                                        (int)csa[i][s], 0, (int)csb[j][s]);
         }
       }
-#pragma unroll
-      for (int i = 0; i < WM; ++i)
-#pragma unroll
-        for (int j = 0; j < WN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AF, BF, 0,
-                                                                      (int)csa[i][s], 0, (int)csb[j][s]);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the waits for the prefetch after the MFMAs
     if (PA != 0) store_a(buf ^ 1, PA == 2);
