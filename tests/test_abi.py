@@ -215,6 +215,7 @@ def test_grouped_matmul_validation(lib):
 
     assert mm(gt=1) == EINVAL                                   # unknown group_type
     assert mm(K=100) == EINVAL                                  # K not a multiple of 32
+    assert mm(K=0) == EUNSUP                                    # rows split over an empty K
     assert mm(M=-1) == EINVAL
     assert mm(*(), **{"a": ops(afmt=4)[0], "b": ops()[1]}) == EUNSUP   # A must be fp8
     assert mm(a=ops()[0], b=ops(bfmt=2)[1]) == EUNSUP           # unknown B format
