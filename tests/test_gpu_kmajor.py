@@ -91,6 +91,41 @@ def test_kmajor_edge_blocks(oracle, dtype, rule, block):
     assert np.array_equal(s, so)
 
 
+def tiny_scale_blocks(block):
+    """bf16 columns of `block` rows, each one FLOOR block whose max lies below
+    2^-122 (E8M0 byte 0, 1 or 2: the generic snap): for each of a set of such
+    maxima, every bf16 magnitude up to it with both signs, the max itself at
+    a varying row.  Returns bf16 bits [block, n_blocks]."""
+    blocks = []
+    for amax in (0x0001, 0x0003, 0x0040, 0x007F, 0x0080, 0x00C0, 0x00FF, 0x0100, 0x0155, 0x01FF,
+                 0x0200, 0x0250, 0x027F):
+        mags = np.arange(0, amax + 1, dtype=np.uint16)
+        vals = np.concatenate([mags, mags | np.uint16(0x8000)])
+        per = block - 1
+        for i in range(0, len(vals), per):
+            chunk = list(vals[i:i + per])
+            top = amax if (i // per) % 2 == 0 else amax | 0x8000
+            chunk.insert(min((i // per) % block, len(chunk)), top)
+            b = np.zeros(block, np.uint16)
+            b[:len(chunk)] = chunk
+            blocks.append(b)
+    return np.ascontiguousarray(np.stack(blocks, axis=1))
+
+
+@pytest.mark.parametrize("block", [32, 128])
+def test_kmajor_tiny_scales_every_value(oracle, block):
+    """Every bf16 magnitude (both signs) under FLOOR block maxima below 2^-122,
+    i.e. E8M0 bytes 0-2, where the kernel takes its generic snap."""
+    x = tiny_scale_blocks(block)
+    rows, cols = x.shape
+    kb = M.kmajor_k_blocks(rows, block)
+    c, s = run_kmajor(x, block, "floor", kb)
+    co, so, _ = oracle.pack_kmajor(x, block, "floor", k_blocks=kb, fill=FILL)
+    assert np.array_equal(c, co)
+    assert np.array_equal(s, so)
+    assert (so[:, 0] <= 2).all() and cols > 60
+
+
 # ------------------------------------------------------------------ grouped
 
 GROUP_CASES = [
