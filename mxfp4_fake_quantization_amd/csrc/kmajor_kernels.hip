@@ -67,21 +67,10 @@ struct KmArgs {
 
 // Nibbles of a word of two bf16 columns, with the generic snap for a half
 // whose column max needs it (FLOOR E8M0 byte 0..2).
-// Nibble of one bf16 value of a FLOOR block with E8M0 byte e8 = 0, 1 or 2
-// (scale 2^k, k = e8 - 127).  x * 2^-k is exact and normal in binary32 (bf16
-// values are multiples of 2^-133 and 2^-k >= 2^125; binary32 denormals are
-// kept by these kernels), so the binary32 closed form at unit scale
-// (threshold bits of 0.25) gives its index.  One multiply per value keeps the
-// register footprint of the rare path small.
-__device__ __forceinline__ uint32_t slow_nib_bf16(uint32_t h16, uint32_t e8) {
-  const float v = __builtin_bit_cast(float, (h16 & 0x7FFFu) << 16) * __builtin_bit_cast(float, (254u - e8) << 23);
-  const uint32_t idx = snap_idx_f32(__builtin_bit_cast(uint32_t, v), 0x3E800000u);
-  return idx | ((h16 & 0x8000u) && (h16 & 0x7FFFu) ? 8u : 0u);
-}
 __device__ __forceinline__ uint32_t fix_slow_nib(uint32_t w, uint32_t cm, uint32_t e8p, uint32_t n) {
   const uint32_t lo = cm & 0xFFFFu, hi = cm >> 16;
-  if (lo != 0 && (lo >> 7) < 5) n = (n & 0xFFFF0000u) | slow_nib_bf16(w & 0xFFFFu, e8p & 0xFFu);
-  if (hi != 0 && (hi >> 7) < 5) n = (n & 0xFFFFu) | (slow_nib_bf16(w >> 16, (e8p >> 16) & 0xFFu) << 16);
+  if (lo != 0 && (lo >> 7) < 5) n = (n & 0xFFFF0000u) | half_bf16_slow(w & 0xFFFFu, e8p & 0xFFu).n;
+  if (hi != 0 && (hi >> 7) < 5) n = (n & 0xFFFFu) | (half_bf16_slow(w >> 16, (e8p >> 16) & 0xFFu).n << 16);
   return n;
 }
 

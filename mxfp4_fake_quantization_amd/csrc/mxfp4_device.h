@@ -189,18 +189,27 @@ __device__ __forceinline__ uint32_t n_bf16(uint32_t w, uint32_t t2) {
 
 
 
-// Generic snap of one half (FLOOR blocks with E8M0 byte 0..2).
+// Generic snap of one half (FLOOR blocks with E8M0 byte 0..2, scale 2^k with
+// k = e8 - 127 <= -125).  In binary32, x * 2^-k is exact and normal (bf16
+// values are multiples of 2^-133 and 2^-k >= 2^125; these kernels keep
+// binary32 denormals), so the binary32 closed form at unit scale (threshold
+// bits of 0.25, half 0.5) gives the index and the code value, and
+// code * 2^k is again exact (>= 2^-128, at most two significant bits) with
+// zero low 16 bits.  Two v_ldexp_f32 per value; no per-block tables, which
+// keeps the rare path's registers low.
 struct HalfOut {
   uint32_t y, m, n;
 };
 __device__ __forceinline__ HalfOut half_bf16_slow(uint32_t bits16, uint32_t e8) {
-  uint32_t a = bits16 & 0x7FFFu;
-  uint32_t sg = (bits16 & 0x8000u) && a ? 0x8000u : 0u;
-  uint32_t idx;
+  const uint32_t a = bits16 & 0x7FFFu;
+  const uint32_t sg = (bits16 & 0x8000u) && a ? 0x8000u : 0u;
+  const int k = (int)e8 - 127;
+  const uint32_t v = __builtin_bit_cast(uint32_t, __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, a << 16), -k));
+  const float q = __builtin_amdgcn_ldexpf(__builtin_bit_cast(float, snap_mag_f32(v, 0x3E800000u, 0x3F000000u)), k);
   HalfOut o;
-  o.y = slow_snap<kBF16>(a, e8, &idx) | sg;
-  o.m = a > slow_six<kBF16>(e8) ? 1u : 0u;
-  o.n = idx | (sg >> 12);
+  o.y = (__builtin_bit_cast(uint32_t, q) >> 16) | sg;
+  o.m = v > 0x40C00000u ? 1u : 0u;  // x > 6 * 2^k
+  o.n = snap_idx_f32(v, 0x3E800000u) | (sg >> 12);
   return o;
 }
 
