@@ -350,17 +350,24 @@ def steady_state(M, lib, W, torch, stream, rows=28672, cols=8192, sets=2, reps=2
             "step_frac": round(gbs(2 * per, s_us) / HBM_PEAK_GBS, 4)}
 
 
-def _time_calls(torch, calls, reps, warm=20):
+def _time_calls(torch, calls, reps, warm=20, trials=3):
+    """Per-launch time of back-to-back launches (rotating over `calls`): three
+    trials of `reps` launches between two events on the current stream;
+    returns (median, best) of the trials' per-launch averages, in seconds.
+    Events around every launch would add their own overhead and gaps."""
     for i in range(warm):
         calls[i % len(calls)]()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for i in range(reps):
-        evs[i][0].record()
-        calls[i % len(calls)]()
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    t = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
+    t = []
+    for _ in range(trials):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            calls[i % len(calls)]()
+        b.record()
+        torch.cuda.synchronize()
+        t.append(a.elapsed_time(b) * 1e-3 / reps)
+    t = np.array(t)
     return float(np.median(t)), float(t.min())
 
 
