@@ -66,9 +66,8 @@ struct GemmArgs {
   int64_t tiles_m, tiles_n, total;
 };
 
-// slot swizzles: conflict-free ds_read_b128 for 8 or 16 consecutive rows
+// slot swizzle: conflict-free ds_read_b128 for 8 or 16 consecutive rows
 __device__ __forceinline__ int swz_a(int r, int c) { return (c ^ ((r ^ (r >> 3)) & 7)) << 4; }
-__device__ __forceinline__ int swz_b4(int n, int c) { return (c ^ (((n >> 1) ^ (n >> 2)) & 3)) << 4; }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
