@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import Guarded, dev, host, like_bf16_or_f32
+from gpu_util import Guarded, dev, host
 
 pytestmark = pytest.mark.gpu
 

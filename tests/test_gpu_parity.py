@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import (Guarded, dev, grouped_rows, host, like_bf16_or_f32, unpack_col_bitmap,
+from gpu_util import (Guarded, dev, host, like_bf16_or_f32, unpack_col_bitmap,
                       unpack_grouped_bitmap, unpack_row_bitmap)
 
 pytestmark = pytest.mark.gpu

@@ -1,7 +1,6 @@
 """Host-side checks of the QAT wrapper (no kernel calls): configuration
 validation and module conversion (the amct PR's linear.py behaviour)."""
 import pytest
-import torch
 from torch import nn
 
 from mxfp4_fake_quantization_amd.qat import (MXFP4FakeQuantizer, MXFP4QATConfig, MXFP4QATLinear,
