@@ -35,8 +35,16 @@ namespace mxfp4 {
 namespace {
 
 constexpr int kKTile = 256;      // K positions per workgroup
-constexpr int kCTile = 128;      // columns per workgroup
-constexpr int kKmThreads = 512;  // 8 waves, each 32 K positions x 128 columns
+// Workgroup = 256 K positions x 128 columns per half (8 waves per half, each
+// 32 K positions x 128 columns); bf16 block 32 takes two halves (256-byte
+// row segments read as 512-byte ones: +2-5 % measured on MI355X), the other
+// forms one (block 128 measured equal or slower with two).
+template <int DT, int B>
+struct KmShape {
+  static constexpr int halves = DT == kBF16 && B == 32 ? 2 : 1;
+  static constexpr int ctile = 128 * halves;   // columns per workgroup
+  static constexpr int threads = 512 * halves;
+};
 // Minimum waves per SIMD requested from the compiler: 8 (64 VGPRs, four
 // 8-wave workgroups per CU) for bf16 FLOOR, whose common path fits in 64
 // registers (only the generic snap of tiny blocks spills); 4 (128 VGPRs, two
@@ -155,8 +163,9 @@ struct KmTile {
 };
 
 template <int DT, int B, bool GROUPED, bool VEC>
-__device__ __forceinline__ KmTile km_tile(const KmArgs &A, int64_t tile, int wave, int rql, int cg) {
+__device__ __forceinline__ KmTile km_tile(const KmArgs &A, int64_t tile, int wave, int chalf, int rql, int cg) {
   constexpr int ES = PieceT<DT>::ES;
+  constexpr int kCTile = KmShape<DT, B>::ctile;
   constexpr int LB = B == 32 ? 5 : 7;
   KmTile T;
   T.kt = tile / A.nct;
@@ -174,7 +183,7 @@ __device__ __forceinline__ KmTile km_tile(const KmArgs &A, int64_t tile, int wav
     const int64_t rem = A.rows - start;
     len = rem <= 0 ? 0 : (rem < B ? rem : B);
   }
-  T.c0 = T.col0 + 8 * cg;
+  T.c0 = T.col0 + 128 * chalf + 8 * cg;
   const int64_t crem = A.cols - T.c0;
   T.ncol = crem >= 8 ? 8 : (crem > 0 ? (int)crem : 0);
   const int64_t rrem = len - T.o0;
@@ -190,9 +199,10 @@ __device__ __forceinline__ KmTile km_tile(const KmArgs &A, int64_t tile, int wav
 // column row are XOR-swizzled by the column's group, so the 64 lanes of a
 // staging write (16 column groups x 4 K words) spread over all banks, and the
 // 8 lanes that read one column's 8 chunks (ds_read_b128) hit distinct banks.
+template <int CT>
 struct KmStage {
-  uint32_t codes[kCTile][kKTile / 8] __attribute__((aligned(16)));
-  uint8_t scales[kCTile][kKTile / 32];
+  uint32_t codes[CT][kKTile / 8] __attribute__((aligned(16)));
+  uint8_t scales[CT][kKTile / 32];
   uint8_t live[kKTile / 32];
 };
 
@@ -205,22 +215,26 @@ __device__ __forceinline__ int km_slot(int c, int kw) {
 // codes with 16-byte stores and one lane its scale bytes (8 for block 32) in
 // one store, instead of 4-byte and 1-byte pieces scattered by row lanes.
 template <int DT, int B, int RULE, bool GROUPED, bool VEC>
-__global__ __launch_bounds__(kKmThreads, DT == kBF16 && RULE == kFloor ? MXFP4_KMAJOR_MINWG_BF16_FLOOR
-                                                                     : MXFP4_KMAJOR_MINWG)
+__global__ __launch_bounds__((KmShape<DT, B>::threads),
+                             (DT == kBF16 && RULE == kFloor ? MXFP4_KMAJOR_MINWG_BF16_FLOOR : MXFP4_KMAJOR_MINWG))
 void kmajor_pack_kernel(KmArgs A) {
+  constexpr int kCTile = KmShape<DT, B>::ctile;
+  constexpr int kKmThreads = KmShape<DT, B>::threads;
   constexpr int NW = PieceT<DT>::NW;
   constexpr int ES = PieceT<DT>::ES;
   constexpr uint32_t ABS = DT == kBF16 ? 0x7FFF7FFFu : 0x7FFFFFFFu;
   constexpr int NBT_TILE = kKTile / B;  // block-rows per tile
   __shared__ uint32_t s_cm[kKmThreads / 64][16][NW];
-  __shared__ KmStage st;
+  __shared__ KmStage<kCTile> st;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  const int kwave = wave & 7;   // K slice of the wave (32 positions)
+  const int chalf = wave >> 3;  // its 128-column half of the tile
   const int lane = tid & 63;
   const int cg = lane & 15;
   const int rql = lane >> 4;
-  const KmTile T = km_tile<DT, B, GROUPED, VEC>(A, blockIdx.x, wave, rql, cg);
+  const KmTile T = km_tile<DT, B, GROUPED, VEC>(A, blockIdx.x, kwave, chalf, rql, cg);
 
   // ---- load 8 rows x 8 columns --------------------------------------------
   // A wave whose piece is all inside the tensor issues its eight loads
@@ -290,14 +304,14 @@ void kmajor_pack_kernel(KmArgs A) {
   else code_words<DT, RULE, false>(w, pt, pe, cm, cbp, cw);
 
   // ---- stage in LDS ----------------------------------------------------------
-  const int kw = 4 * wave + rql;  // K word of the lane inside the tile
+  const int kw = 4 * kwave + rql;  // K word of the lane inside the tile
   const int bl = (8 * kw) / B;    // block-row of the lane inside the tile
 #pragma unroll
-  for (int j = 0; j < 8; ++j) (&st.codes[0][0])[km_slot(8 * cg + j, kw)] = cw[j];
+  for (int j = 0; j < 8; ++j) (&st.codes[0][0])[km_slot(128 * chalf + 8 * cg + j, kw)] = cw[j];
   if (T.o0 == 0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      st.scales[8 * cg + j][bl] = (uint8_t)(DT == kBF16 ? (pe[j >> 1] >> (16 * (j & 1))) : pe[j]);
+      st.scales[128 * chalf + 8 * cg + j][bl] = (uint8_t)(DT == kBF16 ? (pe[j >> 1] >> (16 * (j & 1))) : pe[j]);
     if (cg == 0) st.live[bl] = T.live;
   }
   __syncthreads();
@@ -339,9 +353,9 @@ template <int DT, int B, int RULE, bool GROUPED>
 hipError_t km_launch(bool vec, const KmArgs &a, hipStream_t st) {
   const dim3 grid((unsigned)a.ntiles);
   if (vec)
-    hipLaunchKernelGGL((kmajor_pack_kernel<DT, B, RULE, GROUPED, true>), grid, dim3(kKmThreads), 0, st, a);
+    hipLaunchKernelGGL((kmajor_pack_kernel<DT, B, RULE, GROUPED, true>), grid, dim3(KmShape<DT, B>::threads), 0, st, a);
   else
-    hipLaunchKernelGGL((kmajor_pack_kernel<DT, B, RULE, GROUPED, false>), grid, dim3(kKmThreads), 0, st, a);
+    hipLaunchKernelGGL((kmajor_pack_kernel<DT, B, RULE, GROUPED, false>), grid, dim3(KmShape<DT, B>::threads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -494,7 +508,9 @@ hipError_t launch_kmajor_pack(const KmLaunch &L, hipStream_t st) {
   a.cols = L.cols;
   a.k_blocks = L.k_blocks;
   a.ldk = L.k_blocks * L.block / 2;
-  a.nct = (L.cols + kCTile - 1) / kCTile;
+  const int ct = L.dtype == kBF16 ? (L.block == 32 ? KmShape<kBF16, 32>::ctile : KmShape<kBF16, 128>::ctile)
+                                   : (L.block == 32 ? KmShape<kF32, 32>::ctile : KmShape<kF32, 128>::ctile);
+  a.nct = (L.cols + ct - 1) / ct;
   a.num_groups = L.num_groups;
   a.list_type = L.list_type;
   a.sf = L.sf;
