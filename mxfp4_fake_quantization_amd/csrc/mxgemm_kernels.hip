@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
     n0 = (tile - tm * P.tiles_n) * BN;
     int g = 0;
     if (P.gl) {
-      block_row_uniform(P.gl, P.G, P.list_type, P.M, __builtin_ctz(BM), tm, &m0, &mlen, &g);
+      block_row_uniform<false>(P.gl, P.G, P.list_type, P.M, __builtin_ctz(BM), tm, &m0, &mlen, &g);
     } else {
       m0 = tm * BM;
       mlen = P.M - m0 < BM ? P.M - m0 : BM;
