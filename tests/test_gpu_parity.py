@@ -279,6 +279,34 @@ def test_grouped_inconsistent_list_is_clamped(oracle, list_type, gl, block):
         b.check_tail()
 
 
+@pytest.mark.parametrize("G", list(range(1, 34)))
+def test_grouped_every_walk_length(oracle, G):
+    """Every list length the short-list walk reads (1..32 entries, fetched 8,
+    4, 2 and 1 at a time) and the first one decoded by the scan (33), with
+    empty groups: grouped QDQ, its bitmap and scales, and the grouped STE."""
+    rows, cols, block = 260, 24, 32
+    counts = W.ragged_counts(rows, G, seed=200 + G, zero_groups=2)
+    x = make_x((rows, cols), "bf16", 300 + G)
+    nbt = sum(-(-int(c) // block) for c in counts)
+    y = Guarded((rows, cols), torch.bfloat16)
+    m = Guarded((M.grouped_mask_rows_max(rows, block, G), cols), torch.int32, fill=0x5A)
+    s = Guarded((M.grouped_scale_rows_max(rows, block, G), cols), torch.uint8, fill=0x5A)
+    gld = dev(counts)
+    M.mxfp4_grouped_qdq(dev(x), gld, y.t, m.t, s.t, block=block)
+    g = make_x((rows, cols), "bf16", 400 + G)
+    gi = Guarded((rows, cols), torch.bfloat16)
+    M.mxfp4_ste_bwd(dev(g), m.t, gi.t, M.GROUPED, block=block, group_list=gld)
+    torch.cuda.synchronize()
+    yo, co, eo = oracle.grouped_cols(x, counts, block)
+    assert np.array_equal(host(y.t), yo)
+    assert np.array_equal(host(s.t)[:nbt], eo)
+    bits, clean = unpack_grouped_bitmap(host(m.t)[:nbt], rows, counts, block)
+    assert np.array_equal(bits, co) and clean
+    assert np.array_equal(host(gi.t), oracle.ste_bwd(g, co))
+    for b in (y, m, s, gi):
+        b.check_tail()
+
+
 def test_grouped_rows_past_total_untouched(oracle):
     """Rows past the groups' total are not written (caller's contract
     violated on purpose: the list sums to less than rows)."""
