@@ -435,18 +435,21 @@ def kmajor_k_blocks(rows: int, block: int, num_groups=None, align: bool = True) 
     (dense) or ceil(rows/block) + num_groups - 1 (grouped: the most
     block-rows any split of `rows` into num_groups groups produces).  With
     align (default) it is rounded up so every row of codes_t starts on a
-    128-byte line and every row of scales_t on 8 bytes (multiples of 8 blocks
-    of 32, 2 blocks of 128), which the kernel's full-line stores need to stay
-    whole, and a row stride that is a multiple of 4 KiB gets two more lines
-    (on MI355X such strides put one workgroup's 64 column lines on few memory
-    channels: measured 4.0 against 4.9 TB/s at 16 KiB).  The extra block-rows
-    are not touched."""
+    256-byte boundary (multiples of 16 blocks of 32, 4 blocks of 128; the
+    kernel's whole-line stores need at least 128), and a row stride that is a
+    multiple of 4 KiB gets 256 more bytes.  The code-row stride decides how
+    the workgroups' column lines spread over the memory channels; measured on
+    MI355X (bf16, block 32): a 16 KiB stride runs at 4.0 TB/s against 4.9 at
+    neighbouring strides, and for the grouped MoE tokens (32768 x 7168, 8
+    groups) 256-byte rows take 108.8 us against 117.9 us at the 128-byte
+    multiple below them (k_blocks 1040 vs 1032).  The extra block-rows are
+    not touched."""
     nb = -(-rows // block)
     if num_groups is not None and rows > 0:
         nb += int(num_groups) - 1
     if align:
-        step = 8 if block == 32 else 2
+        step = 16 if block == 32 else 4
         nb = -(-nb // step) * step
         if nb and (nb * block // 2) % 4096 == 0:
-            nb += 2 * step
+            nb += step
     return nb
