@@ -277,3 +277,55 @@ def test_cpu_group_list_is_validated_before_any_gpu_work():
         M._group_list([10, 30], 31, 0)
     with pytest.raises(ValueError):
         M._group_list([], 0, 1)
+
+
+ROWS_SET = [0, 1, 31, 32, 33, 127, 128, 300, 4095, 4096, 16384, 28672, 32768, 32769, 65536, 131072]
+
+
+@pytest.mark.parametrize("block", [32, 128])
+@pytest.mark.parametrize("groups", [None, 1, 3, 8, 40])
+def test_kmajor_k_blocks_rule(block, groups):
+    """kmajor_k_blocks: the smallest k_blocks >= the most block-rows the
+    blocking can produce whose codes_t row is a whole number of 256-byte units
+    and not a multiple of 4 KiB (align=False: that minimum itself)."""
+    import mxfp4_fake_quantization_amd as M
+    bpb = block // 2                      # code bytes per block
+    for rows in ROWS_SET:
+        need = -(-rows // block) + ((groups - 1) if groups and rows else 0)
+        assert M.kmajor_k_blocks(rows, block, groups, align=False) == need
+        kb = M.kmajor_k_blocks(rows, block, groups)
+        if need == 0:
+            assert kb == 0
+            continue
+        ok = lambda k: (k * bpb) % 256 == 0 and (k * bpb) % 4096 != 0
+        assert kb >= need and ok(kb)
+        assert not any(ok(k) for k in range(need, kb))
+        assert kb % (8 if block == 32 else 2) == 0          # whole 128-byte code lines
+        assert kb % 8 == 0 or block == 128                  # 8-byte aligned scale rows
+
+
+@pytest.mark.parametrize("groups", [None, 1, 3, 8, 40])
+def test_mxfp8_kmajor_k_blocks_rule(groups):
+    """mxfp8_kmajor_k_blocks: the same with 512-byte code rows (32 bytes per
+    block of 32)."""
+    import mxfp4_fake_quantization_amd as M
+    for rows in ROWS_SET:
+        need = -(-rows // 32) + ((groups - 1) if groups and rows else 0)
+        assert M.mxfp8_kmajor_k_blocks(rows, groups, align=False) == need
+        kb = M.mxfp8_kmajor_k_blocks(rows, groups)
+        if need == 0:
+            assert kb == 0
+            continue
+        ok = lambda k: (k * 32) % 512 == 0 and (k * 32) % 4096 != 0
+        assert kb >= need and ok(kb)
+        assert not any(ok(k) for k in range(need, kb))
+
+
+def test_k_blocks_of_the_measured_shapes():
+    """The values the measured stride tables rest on (MoE tokens 32768 rows in
+    8 groups, the 28672-row weight)."""
+    import mxfp4_fake_quantization_amd as M
+    assert M.kmajor_k_blocks(32768, 32) == M.kmajor_k_blocks(32768, 32, 8) == 1040
+    assert M.kmajor_k_blocks(28672, 32) == 896
+    assert M.kmajor_k_blocks(28672, 128) == 224
+    assert M.mxfp8_kmajor_k_blocks(32768) == M.mxfp8_kmajor_k_blocks(32768, 8) == 1040
