@@ -307,6 +307,28 @@ def test_grouped_every_walk_length(oracle, G):
         b.check_tail()
 
 
+def test_grouped_list_written_by_preceding_kernels(oracle):
+    """A group list computed on the device by the kernel right before the call
+    (bincount of expert ids), then rewritten in place by another kernel and
+    used again: each call sees the list as the stream left it."""
+    rows, cols, G = 400, 40, 8
+    x = make_x((rows, cols), "bf16", 77)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    ids = torch.randint(0, G, (rows,), generator=g, device="cuda")
+    gl = torch.bincount(ids, minlength=G).to(torch.int64)        # device kernels
+    y = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    outs = []
+    for step in range(3):
+        M.mxfp4_grouped_qdq(dev(x), gl, y)
+        outs.append((host(y).copy(), gl.cpu().numpy().copy()))
+        gl.copy_(torch.roll(gl, 1) if step == 0 else gl.flip(0))   # rewritten on the stream
+    torch.cuda.synchronize()
+    assert not np.array_equal(outs[0][1], outs[1][1])
+    for yh, counts in outs:
+        yo, _, _ = oracle.grouped_cols(x, counts, 32)
+        assert np.array_equal(yh, yo)
+
+
 def test_grouped_rows_past_total_untouched(oracle):
     """Rows past the groups' total are not written (caller's contract
     violated on purpose: the list sums to less than rows)."""
