@@ -486,6 +486,29 @@ def bench_all(M, lib, W, torch, args):
     rec("mxfp8_kmajor_grouped_32768x7168", R * C * 2 + C * nbt * (32 + 1), R * C, _time_calls(torch, k8calls, 30))
     del xs, k8, t8
 
+    # the PR's minimal QAT check at its own size: fp32 weight 32x64 and input
+    # 4x64, row-wise block-32 forward (y + bitmap) of both, then the clipped
+    # STE of an all-ones gradient for both; launch-bound, so reported as
+    # latency (four launches per step), not as a fraction of peak
+    tw, tx = W.tiny_qat(0)
+    tcalls = []
+    for arr in (tw, tx):
+        r, c = arr.shape
+        xt = torch.from_numpy(arr).cuda()
+        yt, gt, gi = torch.empty_like(xt), torch.ones_like(xt), torch.empty_like(xt)
+        mt = torch.empty((r, -(-c // 32)), dtype=torch.int32, device="cuda")
+        dt = M._Desc(0, 32, 0, 0, r, c, 6.0, 0)
+        keep = (xt, yt, gt, gi, mt, dt)
+        tcalls.append((Call(lib.mxfp4_qdq_fwd, ctypes.byref(dt), M.ROW, vp(xt.data_ptr()), vp(yt.data_ptr()),
+                            vp(mt.data_ptr()), None, None, None, None, stream),
+                       Call(lib.mxfp4_ste_bwd, ctypes.byref(dt), M.ROW, vp(gt.data_ptr()), vp(mt.data_ptr()),
+                            vp(gi.data_ptr()), None, 0, 1, stream), keep))
+    step = [lambda: (tcalls[0][0](), tcalls[1][0](), tcalls[0][1](), tcalls[1][1]())]
+    med, best = _time_calls(torch, step, 200)
+    out["tiny_qat_w32x64_x4x64_fp32"] = {"step_us": round(med * 1e6, 2), "best_step_us": round(best * 1e6, 2),
+                                         "launches_per_step": 4, "per_launch_us": round(med * 1e6 / 4, 2),
+                                         "bound": "launch latency"}
+
     bench_gemm(M, W, torch, out, gl, counts)
     return out
 
