@@ -9,7 +9,7 @@
 // Work split: a "chunk" is 8 consecutive elements of one row (16 bytes of
 // bf16, 32 bytes of fp32) held by one lane; a block is 4 (block 32) or 16
 // (block 128) consecutive lanes, reduced with DPP.  Each thread issues all of
-// its U (1 or 2) chunk loads before any arithmetic, and consecutive lanes
+// its U (1, 2 or 4) chunk loads before any arithmetic, and consecutive lanes
 // read consecutive 16-byte pieces, so every load instruction covers one
 // contiguous 1 KiB (bf16) stretch of HBM.
 #include "mxfp4_device.h"
@@ -22,7 +22,8 @@ namespace {
 // 28672x8192: the y / bitmap forward streams best with one chunk per thread
 // in one-wave workgroups (many short workgroups keep loads and stores
 // overlapped across waves); the packing forward with two chunks per thread
-// in four-wave workgroups.
+// (four for bf16 block 128: 103 -> 99 us at 28672x8192; an fp32 chunk is
+// already 32 bytes) in four-wave workgroups.
 #ifndef MXFP4_ROW_U_SMALL
 #define MXFP4_ROW_U_SMALL 1
 #endif
@@ -31,6 +32,9 @@ namespace {
 #endif
 #ifndef MXFP4_PACK_U
 #define MXFP4_PACK_U 2
+#endif
+#ifndef MXFP4_PACK_U_B128
+#define MXFP4_PACK_U_B128 4
 #endif
 constexpr int64_t kRowBigChunks = int64_t(8) << 20;
 #ifndef MXFP4_ROW_THREADS
@@ -230,7 +234,9 @@ hipError_t launch_shape(const RowArgs &a, hipStream_t st) {
 template <int DT, int B, int RULE, int MODE>
 hipError_t launch_u(const RowArgs &a, hipStream_t st) {
   if constexpr (MODE == kModeFlat) {
-    if (a.emit & kEmitCodes) return launch_shape<DT, B, RULE, MODE, MXFP4_PACK_U, kPackThreads>(a, st);
+    if (a.emit & kEmitCodes)
+      return launch_shape<DT, B, RULE, MODE, DT == kBF16 && B == 128 ? MXFP4_PACK_U_B128 : MXFP4_PACK_U,
+                          kPackThreads>(a, st);
     if (a.nchunks > kRowBigChunks) return launch_shape<DT, B, RULE, MODE, MXFP4_ROW_U_BIG, kRowThreads>(a, st);
     return launch_shape<DT, B, RULE, MODE, MXFP4_ROW_U_SMALL, kRowThreads>(a, st);
   } else {
