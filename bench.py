@@ -140,7 +140,22 @@ def cpu_baseline(x, g, min_seconds=10.0):
     nbytes = rows * cols * 8.25
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"whole weight_4k workload ({rows}x{cols} bf16 fwd+bwd), {reps} reps, "
-                      f"{dt * 1e3:.1f} ms per step, single-threaded C oracle"}
+                      f"{dt * 1e3:.1f} ms per step, single-threaded C oracle",
+            "host": host_cpu()}
+
+
+def host_cpu() -> str:
+    """CPU model and the cores this process may run on (the oracle uses one)."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}; {len(os.sched_getaffinity(0))} cores available, nproc {os.cpu_count()}"
 
 
 def main():
@@ -160,7 +175,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the hot path has no "
-              "cross-GPU step, and this build runs on a single MI355X.", file=sys.stderr)
+              "cross-GPU step; each GPU would run its own shard independently.", file=sys.stderr)
         sys.exit(2)
 
     import torch
