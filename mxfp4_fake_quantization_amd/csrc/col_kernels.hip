@@ -110,7 +110,7 @@ __device__ __forceinline__ uint32_t pick4(uint32_t v0, uint32_t v1, uint32_t v2,
 template <int DT, int RULE, bool VEC, bool SLOW>
 __device__ __forceinline__ void col_outputs(const ColArgs &A, const uint32_t (&w)[8][ColT<DT>::NW],
                                             const uint32_t *pt, const uint32_t *ph, const uint32_t *ps,
-                                            const uint32_t *pe, const uint32_t *cm,
+                                            const uint32_t *pz, const uint32_t *pe, const uint32_t *cm,
                                             const BlockParams *cbp, int64_t off0, int64_t rstride,
                                             int rbase, int64_t len, int ncol, int rg, int64_t c0,
                                             int64_t wrow, bool slab_live) {
@@ -124,7 +124,7 @@ __device__ __forceinline__ void col_outputs(const ColArgs &A, const uint32_t (&w
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
       if (DT == kBF16) {
-        yv[k] = y_bf16(w[i][k], pt[k], ph[k]);
+        yv[k] = y_bf16(w[i][k], pt[k], ph[k], pz[k]);
         uint32_t mb = m_bf16(w[i][k], ps[k]);
         if (SLOW && RULE == kFloor) fix_slow_word(w[i][k], cm[k], pe[k], &yv[k], &mb);
         acc[k] |= mb << i;
@@ -253,14 +253,14 @@ void col_fwd_kernel(ColArgs A) {
 
   // per-column parameters: bf16 packed per word (E8M0 bytes in bits 0-7 and
   // 16-23), fp32 one block per column
-  uint32_t pt[NW], ph[NW], ps[NW], pe[NW];
+  uint32_t pt[NW], ph[NW], ps[NW], pz[NW], pe[NW];
   bool slow_any = false;
   BlockParams cbp[DT == kF32 ? 8 : 1];
 #pragma unroll
   for (int k = 0; k < NW; ++k) {
     if (DT == kBF16 && RULE == kFloor) {
       const PackedParams q = floor_params_pk(cm[k]);
-      pt[k] = q.t2; ph[k] = q.h2; ps[k] = q.s2; pe[k] = q.e8;
+      pt[k] = q.t2; ph[k] = q.h2; ps[k] = q.s2; pz[k] = 0x7FFF7FFFu; pe[k] = q.e8;
       slow_any = slow_any || q.slow;
     } else if (DT == kBF16) {
       const BlockParams lo = block_params<DT, RULE>(cm[k] & 0xFFFFu, A.sf);
@@ -268,6 +268,7 @@ void col_fwd_kernel(ColArgs A) {
       pt[k] = lo.t025 | (hi.t025 << 16);
       ph[k] = lo.half | (hi.half << 16);
       ps[k] = lo.six | (hi.six << 16);
+      pz[k] = lo.zc | (hi.zc << 16);
       pe[k] = lo.e8 | (hi.e8 << 16);
     } else {
       cbp[DT == kF32 ? k : 0] = block_params<DT, RULE>(cm[k], A.sf);
@@ -280,10 +281,10 @@ void col_fwd_kernel(ColArgs A) {
 
   if (A.y_col || A.mask_col) {
     if (__builtin_expect(__any(slow_any), 0))
-      col_outputs<DT, RULE, VEC, true>(A, w, pt, ph, ps, pe, cm, cbp, off0, rstride, rbase, len, ncol,
+      col_outputs<DT, RULE, VEC, true>(A, w, pt, ph, ps, pz, pe, cm, cbp, off0, rstride, rbase, len, ncol,
                                        rg, c0, wrow, slab_live);
     else
-      col_outputs<DT, RULE, VEC, false>(A, w, pt, ph, ps, pe, cm, cbp, off0, rstride, rbase, len, ncol,
+      col_outputs<DT, RULE, VEC, false>(A, w, pt, ph, ps, pz, pe, cm, cbp, off0, rstride, rbase, len, ncol,
                                         rg, c0, wrow, slab_live);
   }
   if (A.scales_col && rg == 0 && wy == 0) {

@@ -94,7 +94,7 @@ __device__ __noinline__ uint32_t slow_column_f32(uint32_t a0, uint32_t a1, uint3
   for (int i = 0; i < 8; ++i) {
     uint32_t idx;
     slow_snap<kF32>(a[i] & 0x7FFFFFFFu, e8, &idx);
-    v |= (idx | (sign_f32(a[i]) >> 28)) << (4 * i);
+    v |= (idx | (sign_f32(a[i], 0x7FFFFFFFu) >> 28)) << (4 * i);  // FLOOR sign rule
   }
   return v;
 }
@@ -104,7 +104,7 @@ __device__ __noinline__ uint32_t slow_column_f32(uint32_t a0, uint32_t a1, uint3
 // needs the generic snap.
 template <int DT, int RULE, bool SLOW>
 __device__ __forceinline__ void code_words(const uint32_t (&w)[8][PieceT<DT>::NW], const uint32_t *pt,
-                                           const uint32_t *pe, const uint32_t *cm,
+                                           const uint32_t *pz, const uint32_t *pe, const uint32_t *cm,
                                            const BlockParams *cbp, uint32_t (&out)[8]) {
   if (DT == kBF16) {
 #pragma unroll
@@ -119,9 +119,9 @@ __device__ __forceinline__ void code_words(const uint32_t (&w)[8][PieceT<DT>::NW
         for (int r = 0; r < 4; ++r) {
           const uint32_t x = w[4 * g + r][k];
           if (SLOW && RULE == kFloor)
-            t[r] = fix_slow_nib(x, cm[k], pe[k], n_bf16(x, pt[k])) << 12;
+            t[r] = fix_slow_nib(x, cm[k], pe[k], n_bf16(x, pt[k], pz[k])) << 12;
           else
-            t[r] = (snap_idx_bf16_tab(x & 0x7FFF7FFFu, t31) << 12) | sign_bf16(x);
+            t[r] = (snap_idx_bf16_tab(x & 0x7FFF7FFFu, t31) << 12) | sign_bf16(x, pz[k]);
         }
         acc[g] = (t[0] >> 12) | (t[1] >> 8) | (t[2] >> 4) | t[3];
       }
@@ -277,7 +277,7 @@ void kmajor_pack_kernel(KmArgs A) {
   }
 
   // ---- per-column parameters ---------------------------------------------
-  uint32_t pt[NW], pe[NW];
+  uint32_t pt[NW], pz[NW], pe[NW];
   BlockParams cbp[DT == kF32 ? 8 : 1];
   bool slow_any = false;
 #pragma unroll
@@ -285,12 +285,14 @@ void kmajor_pack_kernel(KmArgs A) {
     if (DT == kBF16 && RULE == kFloor) {
       const PackedParams q = floor_params_pk(cm[k]);
       pt[k] = q.t2;
+      pz[k] = 0x7FFF7FFFu;
       pe[k] = q.e8;
       slow_any = slow_any || q.slow;
     } else if (DT == kBF16) {
       const BlockParams lo = block_params<DT, RULE>(cm[k] & 0xFFFFu, A.sf);
       const BlockParams hi = block_params<DT, RULE>(cm[k] >> 16, A.sf);
       pt[k] = lo.t025 | (hi.t025 << 16);
+      pz[k] = lo.zc | (hi.zc << 16);
       pe[k] = lo.e8 | (hi.e8 << 16);
     } else {
       cbp[DT == kF32 ? k : 0] = block_params<DT, RULE>(cm[k], A.sf);
@@ -300,8 +302,8 @@ void kmajor_pack_kernel(KmArgs A) {
   }
 
   uint32_t cw[8];
-  if (__builtin_expect(__any(slow_any), 0)) code_words<DT, RULE, true>(w, pt, pe, cm, cbp, cw);
-  else code_words<DT, RULE, false>(w, pt, pe, cm, cbp, cw);
+  if (__builtin_expect(__any(slow_any), 0)) code_words<DT, RULE, true>(w, pt, pz, pe, cm, cbp, cw);
+  else code_words<DT, RULE, false>(w, pt, pz, pe, cm, cbp, cw);
 
   // ---- stage in LDS ----------------------------------------------------------
   const int kw = 4 * kwave + rql;  // K word of the lane inside the tile

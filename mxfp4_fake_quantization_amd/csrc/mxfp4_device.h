@@ -162,29 +162,29 @@ __device__ __forceinline__ uint32_t pk_min1(uint32_t a) {
 // ---- per-word outputs, bf16 (two elements per register) -------------------
 // Parameters are packed per half (t2 = T025 - tau, h2 = HALF, s2 = SIX), so a
 // register may hold two elements of one block or of two different blocks.
-// y bits with the input's sign (-0.0 -> +0.0)
-__device__ __forceinline__ uint32_t y_bf16(uint32_t w, uint32_t t2, uint32_t h2) {
+// y bits with the sign rule of the block (zc2 = ABS - Z per half)
+__device__ __forceinline__ uint32_t y_bf16(uint32_t w, uint32_t t2, uint32_t h2, uint32_t zc2) {
   uint32_t a = w & 0x7FFF7FFFu;
   uint32_t u = pk_subsat(a, t2);
   uint32_t r = pk_add(u, 0x001F001Fu) & 0xFFC0FFC0u;
   uint32_t h = pk_min(pk_subsat(r, 0x01000100u), 0x01400140u);
   uint32_t z = pk_min1(u);
   uint32_t c = pk_min1(pk_subsat(u, 0x00C000C0u));
-  return pk_mad(c, 0x00800080u, pk_mad(z, h2, h)) | sign_bf16(w);
+  return pk_mad(c, 0x00800080u, pk_mad(z, h2, h)) | sign_bf16(w, zc2);
 }
 // clip bits: bit 0 (low element) and bit 16 (high element)
 __device__ __forceinline__ uint32_t m_bf16(uint32_t w, uint32_t s2) {
   return pk_min1(pk_subsat(w & 0x7FFF7FFFu, s2));
 }
 // nibbles sign<<3 | code in bits 0-3 and 16-19
-__device__ __forceinline__ uint32_t n_bf16(uint32_t w, uint32_t t2) {
+__device__ __forceinline__ uint32_t n_bf16(uint32_t w, uint32_t t2, uint32_t zc2) {
   uint32_t a = w & 0x7FFF7FFFu;
   uint32_t u = pk_subsat(a, t2);
   uint32_t r = pk_add(u, 0x001F001Fu) & 0xFFC0FFC0u;
   uint32_t h = pk_min(pk_subsat(r, 0x01000100u), 0x01400140u);
   uint32_t z = pk_min1(u);
   uint32_t c = pk_min1(pk_subsat(u, 0x00C000C0u));
-  return pk_add(pk_add(z, c), pk_shr(h, 6)) | (sign_bf16(w) >> 12);
+  return pk_add(pk_add(z, c), pk_shr(h, 6)) | (sign_bf16(w, zc2) >> 12);
 }
 
 
@@ -216,8 +216,8 @@ __device__ __forceinline__ HalfOut half_bf16_slow(uint32_t bits16, uint32_t e8) 
 // ---- fp32 (one element per register) -------------------------------------
 __device__ __forceinline__ uint32_t y_f32(uint32_t w, const BlockParams &bp) {
   uint32_t a = w & 0x7FFFFFFFu;
-  if (bp.slow) return slow_snap<kF32>(a, bp.e8, nullptr) | sign_f32(w);
-  return snap_mag_f32(a, bp.t025, bp.half) | sign_f32(w);
+  if (bp.slow) return slow_snap<kF32>(a, bp.e8, nullptr) | sign_f32(w, bp.zc);
+  return snap_mag_f32(a, bp.t025, bp.half) | sign_f32(w, bp.zc);
 }
 __device__ __forceinline__ uint32_t m_f32(uint32_t w, const BlockParams &bp) {
   uint32_t a = w & 0x7FFFFFFFu;
@@ -228,7 +228,7 @@ __device__ __forceinline__ uint32_t n_f32(uint32_t w, const BlockParams &bp) {
   uint32_t idx;
   if (bp.slow) slow_snap<kF32>(a, bp.e8, &idx);
   else idx = snap_idx_f32(a, bp.t025);
-  return idx | (sign_f32(w) >> 28);
+  return idx | (sign_f32(w, bp.zc) >> 28);
 }
 
 // 8 nibbles of a bf16 chunk (four words, element 2d in the low half of word
@@ -255,9 +255,9 @@ __device__ __forceinline__ uint32_t pack_mask_bf16(const uint32_t m[4]) {
 template <int DT, bool SLOW>
 __device__ __forceinline__ void chunk_y(const uint32_t *w, const BlockParams &bp, uint32_t *y) {
   if (DT == kBF16) {
-    const uint32_t t2 = splat16(bp.t025), h2 = splat16(bp.half);
+    const uint32_t t2 = splat16(bp.t025), h2 = splat16(bp.half), z2 = splat16(bp.zc);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) y[k] = y_bf16(w[k], t2, h2);
+    for (int k = 0; k < 4; ++k) y[k] = y_bf16(w[k], t2, h2, z2);
     if (SLOW && bp.slow) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -299,9 +299,9 @@ template <int DT, bool SLOW>
 __device__ __forceinline__ uint32_t chunk_codes(const uint32_t *w, const BlockParams &bp) {
   if (DT == kBF16) {
     uint32_t n[4];
-    const uint32_t t31 = splat16(bp.t025 - 31u);
+    const uint32_t t31 = splat16(bp.t025 - 31u), z2 = splat16(bp.zc);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) n[k] = snap_idx_bf16_tab(w[k] & 0x7FFF7FFFu, t31) | (sign_bf16(w[k]) >> 12);
+    for (int k = 0; k < 4; ++k) n[k] = snap_idx_bf16_tab(w[k] & 0x7FFF7FFFu, t31) | (sign_bf16(w[k], z2) >> 12);
     if (SLOW && bp.slow) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {

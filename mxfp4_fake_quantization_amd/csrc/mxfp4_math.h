@@ -29,6 +29,15 @@
 //   idx = z + c + h/Q                  E2M1 magnitude code 0..7
 // (T025 is a multiple of Q, so rounding u rounds a.)  For E < 3 (only FLOOR
 // blocks with amax < 2^-122) a generic threshold count is used instead.
+//
+// Sign: the output (and the nibble's sign bit) is negative iff x < 0 and
+// |x| > Z, with Z = 0 for FLOOR (exact arithmetic: -0.0 -> +0.0, any other
+// negative keeps its sign).  AMCT follows the pages' binary32 arithmetic,
+// where the sign is that of the rounded quotient fl32(x / 2^k): it underflows
+// to zero (torch.sign 0, output +0) when |x| <= 2^(k-150), so Z = that power
+// of two (0 when no positive value of the dtype is that small).  Kept as an
+// addend zc = ABS - Z: bit 15 (bf16 half) or 31 (fp32) of a + zc is set
+// exactly when a > Z.
 #pragma once
 
 #include <stdint.h>
@@ -100,6 +109,7 @@ struct BlockParams {
   uint32_t t025;  // T025 - tau  (u threshold)
   uint32_t half;  // bits of 0.5 * 2^k
   uint32_t six;   // bits of 6 * 2^k (mask: a > six)
+  uint32_t zc;    // ABS - Z: the sign is kept iff a + zc reaches the sign bit
   bool slow;      // FLOOR with 0 < amax < 2^-122: use the generic snap
 };
 
@@ -118,6 +128,7 @@ MXFP4_HD BlockParams floor_params(uint32_t amax) {
   p.t025 = (ec - 2) << MB;
   p.half = p.t025 + 2 * Q;
   p.six = p.t025 + 9 * Q;
+  p.zc = Fmt<DT>::ABS;
   p.slow = (amax != 0) && (eb < 5);
   return p;
 }
@@ -142,16 +153,34 @@ MXFP4_HD PackedParams floor_params_pk(uint32_t cm) {
   return p;
 }
 
-// AMCT E8M0 byte from the block max: r = fl32(amax / sf) with IEEE division,
-// r = max(r, 2^-30), E = exponent(r) + (mantissa(r) > sqrt(2)), i.e. the
-// nearest integer to log2 r (log2 r is never a half-integer for binary32 r).
-// 0x3504F3 is the largest 23-bit mantissa fraction below sqrt(2) - 1.
+// AMCT E8M0 byte from the block max, as the pages' binary32 arithmetic
+// computes it: r = fl32(amax / sf) (IEEE division), r = max(r, 2^-30),
+// L = log2 r rounded to the nearest binary32, k = L rounded half to even
+// (torch.round).  With r = 2^e * m (m in [1, 2), mantissa field M):
+//   - away from log2 m = 1/2, L rounds to the integer nearest to log2 r,
+//     e + (m > sqrt 2) (0x3504F3 is the largest field below sqrt 2 - 1);
+//   - L is exactly the half-integer e + 1/2 when |log2 m - 1/2| is below half
+//     an ulp of e + 1/2, i.e. 2^(j - 24) with j = floor(log2 |e + 1/2|); then
+//     the tie goes to the even integer, k = e + (e & 1).
+// Those fields M form a window around sqrt 2 that widens with j; with
+// i = j + 1 = floor(log2 |2e + 1|) in 0..7 (e in [-30, 127]) it is
+// [0x3504F3 - lo_i, 0x3504F3 + hi_i], lo = 0 0 0 1 3 7 15 31 and
+// hi = 0 0 1 2 4 8 15 31, found by evaluating 2^(1/2 -+ 2^(j-24)) to 50
+// digits (the byte tables below, one byte per i).
 MXFP4_HD uint32_t amct_e8(float amax_f, float sf) {
   float r = amax_f / sf;
   if (!(r >= 0x1p-30f)) r = 0x1p-30f;
-  uint32_t rb = __builtin_bit_cast(uint32_t, r);
-  uint32_t e = (rb >> 23) + ((rb & 0x7FFFFFu) > 0x3504F3u ? 1u : 0u);
-  return e > 254u ? 254u : e;
+  const uint32_t rb = __builtin_bit_cast(uint32_t, r);
+  const uint32_t eb = rb >> 23, m = rb & 0x7FFFFFu;
+  const int e = (int)eb - 127;
+  const uint32_t t = (uint32_t)(e < 0 ? -(2 * e + 1) : 2 * e + 1);  // |2e + 1|, 1..255
+  const unsigned i = 31u - (unsigned)__builtin_clz(t);
+  const uint32_t lo = (uint32_t)(0x1F0F070301000000ull >> (8 * i)) & 0xFFu;
+  const uint32_t hi = (uint32_t)(0x1F0F080402010000ull >> (8 * i)) & 0xFFu;
+  const bool tie = m + lo >= 0x3504F3u && m <= 0x3504F3u + hi;
+  const uint32_t up = tie ? (uint32_t)(e & 1) : (m > 0x3504F3u ? 1u : 0u);
+  const uint32_t e8 = eb + up;
+  return e8 > 254u ? 254u : e8;
 }
 
 template <int DT>
@@ -164,6 +193,11 @@ MXFP4_HD BlockParams amct_params(uint32_t e8) {
   p.t025 = t025 - 1;
   p.half = t025 + 2 * Q;
   p.six = t025 + 9 * Q;
+  // Z = bits of 2^(k-150) = 2^(e8-277): normal from e8 = 151, a subnormal of
+  // the dtype (unit 2^-133 bf16, 2^-149 fp32) from e8 = 144 / 128, else 0.
+  constexpr uint32_t sub0 = DT == kBF16 ? 144u : 128u;
+  const uint32_t z = e8 >= 151u ? (e8 - 150u) << MB : (e8 >= sub0 ? 1u << (e8 - sub0) : 0u);
+  p.zc = Fmt<DT>::ABS - z;
   p.slow = false;
   return p;
 }
@@ -226,8 +260,11 @@ MXFP4_HD uint32_t snap_idx_bf16_tab(uint32_t a, uint32_t t31) {
   return pk_add(lo, hi);
 }
 
-// sign bit kept for negative non-zero inputs only (-0.0 -> +0.0)
-MXFP4_HD uint32_t sign_bf16(uint32_t p) { return p & pk_sub(p, 0x00010001u) & 0x80008000u; }
+// sign bits kept for negative inputs with |x| > Z (zc2 = ABS - Z per half;
+// FLOOR: Z = 0, so only -0.0 loses its sign)
+MXFP4_HD uint32_t sign_bf16(uint32_t p, uint32_t zc2) {
+  return p & pk_add(p & 0x7FFF7FFFu, zc2) & 0x80008000u;
+}
 MXFP4_HD uint32_t mask_bits_bf16(uint32_t a, uint32_t six2) {
   return pk_min(pk_subsat(a, six2), 0x00010001u);
 }
@@ -251,7 +288,7 @@ MXFP4_HD uint32_t snap_idx_f32(uint32_t a, uint32_t t025p) {
   uint32_t c = min32(subsat32(u, 3 * Q), 1u);
   return z + c + (h >> 22);
 }
-MXFP4_HD uint32_t sign_f32(uint32_t p) { return p & (p - 1u) & 0x80000000u; }
+MXFP4_HD uint32_t sign_f32(uint32_t p, uint32_t zc) { return p & ((p & 0x7FFFFFFFu) + zc) & 0x80000000u; }
 
 // ---- generic snap for FLOOR blocks with E8M0 byte 0, 1 or 2 ------------------
 // Values are handled as integer multiples L of the dtype's smallest subnormal

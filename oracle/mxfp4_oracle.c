@@ -28,21 +28,31 @@
  *                    all-zero block takes k = -127.  Midpoint ties go to the
  *                    lower-magnitude code (a value is snapped by counting the
  *                    midpoints it strictly exceeds).
- *   AMCT:            r = fl32(amax / scale_factor), r = max(r, 2^-30),
- *                    k = nearest integer to log2(r) (fake_quant.py
- *                    _block_scale).  Ties go to the higher-magnitude code,
- *                    as torch.bucketize(..., right=True) does.
+ *   AMCT:            the pages' executed arithmetic on binary32 tensors
+ *                    (fake_quant.py _block_scale, _quant_dequant_torch):
+ *                    r = fl32(amax / scale_factor), r = max(r, 2^-30),
+ *                    L = fl32(log2 r), k = round(L) with halves to even
+ *                    (torch.round); y = fl32(x / 2^k); the code follows
+ *                    from |y| with ties to the higher-magnitude code
+ *                    (torch.bucketize(..., right=True)); the sign is
+ *                    torch.sign(y).
  *
- * Arithmetic: every input element is widened exactly to double.  Division by
- * 2^k, the midpoint comparisons and the product code*2^k are exact in double,
+ * Arithmetic.  FLOOR is exact: every input element is widened exactly to
+ * double, division by 2^k, the midpoint comparisons and code*2^k are exact,
  * and every produced value is exactly representable in the output dtype, so
- * the final narrowing cast does not round.  The only rounded operation of the
- * method is AMCT's fp32 quotient amax/scale_factor, done here in float as the
- * pages do it (fp32 tensors).  Built without fast-math (see build.py).
+ * the final narrowing cast does not round.  AMCT repeats the pages' binary32
+ * steps: the quotient amax/scale_factor, log2 of it (correctly rounded to
+ * binary32; it is exactly a half-integer for some r near sqrt(2)*2^e, and
+ * torch.round then picks the even neighbour), and the element quotient
+ * x/2^k, which is exact unless it is below the normal range.  Built without
+ * fast-math and with the default rounding mode (see build.py).
  *
- * Signs: the pages multiply torch.sign(x/scale) by the code.  sign(+-0) is +0,
- * so a zero input gives +0.0, while a negative input that snaps to code 0
- * gives -0.0.  This oracle writes that out literally.
+ * Signs.  The pages multiply torch.sign(y) by the code, and sign(+-0) is 0,
+ * so an output is negative only if its quotient is.  FLOOR reads the
+ * quotient exactly: a zero input (of either sign) gives +0.0 and a negative
+ * input that snaps to code 0 gives -0.0.  AMCT takes the binary32 quotient
+ * as the pages do: where fl32(x / 2^k) underflows to zero (|x| <= 2^(k-150))
+ * the output is +0.0 even for a negative x.
  */
 #include <math.h>
 #include <stdint.h>
@@ -105,14 +115,16 @@ static int scale_exp_floor(double amax) {
   return k < -127 ? -127 : k;
 }
 
-/* AMCT: power of two nearest to max(fl32(amax/sf), 2^-30) in the log domain.
- * log2(r) of a binary32 r is never a half-integer (that would need
- * r = 2^(k+1/2), irrational), and its distance to the nearest half-integer is
- * far above double log2's error, so lround(log2(r)) is the exact answer. */
+/* AMCT: the pages round log2 of the binary32 raw scale as binary32 tensors
+ * do: log2 rounded to the nearest binary32 (log2l carries 64 significant
+ * bits, far more than that rounding needs), then rounded to an integer with
+ * halves going to the even one (rintf in the default rounding mode, as
+ * torch.round does). */
 static int scale_exp_amct(double amax, float sf) {
   float r = (float)amax / sf; /* amax is a binary32 value: the cast is exact */
   if (r < kMinScaleRaw) r = kMinScaleRaw;
-  return (int)lround(log2((double)r));
+  float l = (float)log2l((long double)r);
+  return (int)rintf(l);
 }
 
 /*
@@ -134,7 +146,11 @@ static int qdq_block(int dtype, int rule, float sf, const void *x,
   double scale = ldexp(1.0, k);
   for (int j = 0; j < n; ++j) {
     double v = get_elem(dtype, x, idx[j]);
-    double q_in = v / scale; /* exact: division by a power of two */
+    double q_in;
+    if (rule == OR_FLOOR)
+      q_in = v / scale; /* exact: division by a power of two */
+    else /* binary32 quotient, as y = x_blocked / scale on float32 tensors */
+      q_in = (double)((float)v / (float)scale);
     double mag = fabs(q_in);
     int code = 0; /* number of midpoints passed = index of the E2M1 code */
     for (int i = 0; i < 7; ++i) {

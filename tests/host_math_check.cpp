@@ -46,11 +46,11 @@ static void run_block(const uint32_t *p, int n, int rule, float sf, uint32_t *y,
       six = bp.six;
     }
     if (DT == kBF16) {
-      uint32_t s2 = sign_bf16(p[j] << 16 | p[j]);
+      uint32_t s2 = sign_bf16(p[j] << 16 | p[j], splat16(bp.zc));
       sgn = s2 & 0x8000u;
       if ((s2 >> 16) != sgn) sgn = 0x4000;  // both halves must agree
     } else {
-      sgn = sign_f32(p[j]);
+      sgn = sign_f32(p[j], bp.zc);
     }
     y[j] = mag | sgn;
     clip[j] = a > six;

@@ -163,3 +163,49 @@ def test_table_index_equals_closed_form(host):
     closed form for every bf16 magnitude under every closed-form scale, both
     tie rules (host emulation of the byte permute)."""
     assert host.host_check_idx_table() == 0
+
+
+@pytest.mark.parametrize("sf", [1.0, 6.0, 7.3])
+def test_amct_binary32_log2_half_integers(host, oracle, sf):
+    """AMCT raw scales whose binary32 log2 may be exactly a half-integer (the
+    mantissas near sqrt(2) in every exponent the rule reaches): the kernels'
+    window test equals the oracle's log2 rounding.  fp32 blocks hold the max
+    and values spread below it."""
+    es = np.arange(-30, 127, dtype=np.int64)
+    ms = np.arange(0x3504F3 - 64, 0x3504F3 + 64, dtype=np.int64)
+    r = (((es[:, None] + 127) << 23) | ms[None, :]).astype(np.uint32).ravel().view(np.float32)
+    with np.errstate(over="ignore"):
+        amax = (r.astype(np.float64) * sf).astype(np.float32)
+    amax = amax[np.isfinite(amax) & (amax < np.float32(2.0 ** 126))]
+    g = np.random.default_rng(5)
+    x = (amax[:, None] * g.uniform(-1, 1, (len(amax), 32))).astype(np.float32)
+    x[:, 0] = amax
+    compare(host, oracle, x, 32, "amct", sf)
+
+
+@pytest.mark.parametrize("sf", [7.3, 5.9, 3.3])
+def test_amct_every_bf16_max_other_scale_factors(host, oracle, sf):
+    """Every positive finite bf16 block max with scale factors that give raw
+    scales with full binary32 mantissas."""
+    b = np.arange(1, 0x7F80, dtype=np.uint16)
+    x = np.zeros((len(b), 32), np.uint16)
+    x[:, 0] = b
+    x[:, 1] = b - (b >> 3)
+    x[:, 2] = (b >> 1) | 0x8000
+    compare(host, oracle, x, 32, "amct", sf)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_amct_sign_of_underflowed_quotient(host, oracle, dtype):
+    """Negative values at and around 2^(k-150) under scales 2^k (k = 16..125):
+    AMCT's output is +0 where the binary32 quotient x / 2^k underflows, -0
+    otherwise; FLOOR keeps -0."""
+    rows = []
+    for k in range(16, 126):
+        t = 2.0 ** (k - 150)
+        rows.append([6 * 2.0 ** k, -t, -t * (1 + 2 ** -7), -2 * t, -t / 2, t, -3 * t, -0.75 * t]
+                    + [0.0] * 24)
+    x32 = np.array(rows, dtype=np.float32)
+    x = x32 if dtype == "f32" else W.f32_to_bf16_bits(x32)
+    for rule in ("floor", "amct"):
+        compare(host, oracle, x, 32, rule)

@@ -17,7 +17,14 @@ MUTANTS = {
     "floor_exponent": ("int k = (e - 1) - 2;", "int k = (e - 1) - 1;"),
     "floor_clamp": ("return k < -127 ? -127 : k;", "return k < -126 ? -126 : k;"),
     "amct_clamp": ("kMinScaleRaw = 0x1p-30f", "kMinScaleRaw = 0x1p-31f"),
-    "amct_round": ("return (int)lround(log2((double)r));", "return (int)floor(log2((double)r));"),
+    "amct_round": ("return (int)rintf(l);", "return (int)floorf(l);"),
+    # the exact nearest integer to log2 r (no binary32 rounding of the log)
+    "amct_exact_log2": ("float l = (float)log2l((long double)r);\n  return (int)rintf(l);",
+                        "return (int)lround(log2((double)r));"),
+    # torch.round sends halves to even, C's roundf away from zero
+    "amct_round_half_away": ("return (int)rintf(l);", "return (int)roundf(l);"),
+    # AMCT sign from the exact quotient instead of the binary32 one
+    "amct_sign_exact_quotient": ("q_in = (double)((float)v / (float)scale);", "q_in = v / scale;"),
     "codebook_value": ("{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}", "{0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 4.0, 6.0}"),
     "midpoint_value": ("{0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0}", "{0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 4.5}"),
     "mask_strictness": ("(fabs(v) > kE2M1Max * scale)", "(fabs(v) >= kE2M1Max * scale)"),

@@ -49,12 +49,20 @@ def nearest_code(mag, rule):
 
 
 def expected_from_k(x64, k, rule):
-    """Expected QDQ values given the block exponent k, by brute force."""
+    """Expected QDQ values given the block exponent k, by brute force.  The
+    output is negative when the quotient x / 2^k is: exact for floor; for amct
+    the binary32 quotient (numpy float32 division), which is +0 or -0 only
+    when it underflows."""
     scale = np.ldexp(1.0, k)
     idx = nearest_code(np.abs(x64) / scale, rule)
     q = CODES[idx] * scale
-    q = np.where(x64 < 0, -q, q)                               # -0.0 for negative inputs
-    q = np.where(x64 == 0, 0.0, q)                             # sign(+-0) = 0 -> +0
+    if rule == "floor":
+        quot = x64 / scale
+    else:
+        with np.errstate(under="ignore"):
+            quot = (np.asarray(x64, np.float32) / np.asarray(scale, np.float32)).astype(np.float64)
+    q = np.where(quot < 0, -q, q)                              # -0.0 for a negative quotient
+    q = np.where(quot == 0, 0.0, q)                            # sign(+-0) = 0 -> +0
     return q, idx
 
 
@@ -68,7 +76,7 @@ def search_k_floor(amax):
     return out
 
 
-def search_k_amct(r32):
+def search_k_nearest(r32):
     """k with 2^(2k-1) <= r^2 < 2^(2k+1) (i.e. |log2 r - k| < 1/2), by search.
     r^2 of a 24-bit r is exact in double."""
     r = np.asarray(r32, dtype=np.float64)
@@ -78,6 +86,43 @@ def search_k_amct(r32):
         lo, hi = math.ldexp(1.0, 2 * k - 1), math.ldexp(1.0, 2 * k + 1)
         out = np.where((r2 >= lo) & (r2 < hi), k, out)
     assert (out != 10 ** 6).all()
+    return out
+
+
+_LN2 = None
+
+
+def binary32_log2_is_half(r):
+    """Whether log2(r), rounded to the nearest binary32, is exactly a
+    half-integer e + 1/2, decided with 60-digit decimal logarithms: true iff
+    |log2 r - (e + 1/2)| is below half a binary32 ulp of e + 1/2 (log2 r is
+    irrational near there, so it never equals the boundary)."""
+    global _LN2
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = 60
+        if _LN2 is None:
+            _LN2 = Decimal(2).ln()
+        lg = Decimal(float(r)).ln() / _LN2
+        t = Decimal(math.floor(math.log2(float(r)))) + Decimal("0.5")
+        j = math.floor(math.log2(abs(float(t))))
+        return abs(lg - t) < Decimal(2) ** (j - 24), int(t - Decimal("0.5"))
+
+
+def k_amct_pages(r32):
+    """The pages' AMCT exponent round(fl32(log2 r)) (torch.round: halves to
+    even): the nearest integer to log2 r by search, except where the binary32
+    log2 is exactly a half-integer e + 1/2, which goes to the even one of e,
+    e + 1.  Candidates are found with double log2 (within 2^-14 of a half) and
+    decided exactly by binary32_log2_is_half."""
+    r = np.asarray(r32, dtype=np.float32)
+    out = search_k_nearest(r)
+    lg = np.log2(r.astype(np.float64))
+    near = np.abs(lg - np.floor(lg) - 0.5) < 2.0 ** -14
+    for i in np.flatnonzero(near.ravel()):
+        half, e = binary32_log2_is_half(r.ravel()[i])
+        if half:
+            out.ravel()[i] = e + (e & 1)
     return out
 
 
@@ -164,8 +209,9 @@ def test_floor_scale_exhaustive_bf16(oracle):
 
 @pytest.mark.parametrize("sf", [6.0, 4.0, 7.3])
 def test_amct_scale_exhaustive_bf16(oracle, sf):
-    """AMCT exponent: nearest integer to log2(max(fl32(amax/sf), 2^-30)), checked
-    through |log2 r - k| < 1/2  <=>  2^(2k-1) <= r^2 < 2^(2k+1)."""
+    """AMCT exponent: round(fl32(log2(max(fl32(amax/sf), 2^-30)))), checked
+    through |log2 r - k| < 1/2  <=>  2^(2k-1) <= r^2 < 2^(2k+1) away from the
+    binary32 half-integers, which decimal logarithms decide (k_amct_pages)."""
     b, v = all_positive_finite_bf16()
     r = v / np.float32(sf)
     keep = r < np.float32(2.0 ** 126)
@@ -174,7 +220,7 @@ def test_amct_scale_exhaustive_bf16(oracle, sf):
     x = np.zeros((len(b), 32), np.uint16)
     x[:, 31] = b
     _, _, e8 = oracle.qdq_rows(x, 32, "amct", sf)
-    assert np.array_equal(e8[:, 0].astype(np.int64) - 127, search_k_amct(r))
+    assert np.array_equal(e8[:, 0].astype(np.int64) - 127, k_amct_pages(r))
 
 
 def test_amct_scale_random_fp32(oracle):
@@ -184,7 +230,53 @@ def test_amct_scale_random_fp32(oracle):
     x[:, 0] = v
     _, _, e8 = oracle.qdq_rows(x, 32, "amct")
     r = np.maximum(v / np.float32(6.0), np.float32(2.0 ** -30))
-    assert np.array_equal(e8[:, 0].astype(np.int64) - 127, search_k_amct(r))
+    assert np.array_equal(e8[:, 0].astype(np.int64) - 127, k_amct_pages(r))
+
+
+def _window_r():
+    """Every binary32 r = 2^e * m with the mantissa field within 112 of the
+    one nearest sqrt(2), for every exponent the AMCT rule reaches."""
+    es = np.arange(-30, 128, dtype=np.int64)
+    ms = np.arange(0x3504F3 - 56, 0x3504F3 + 56, dtype=np.int64)
+    bits = (((es[:, None] + 127) << 23) | ms[None, :]).astype(np.uint32).ravel()
+    return bits.view(np.float32)
+
+
+def test_amct_binary32_log2_half_integers(oracle):
+    """Where log2 r rounded to binary32 is exactly e + 1/2 (a window of
+    mantissas around sqrt(2) that widens with |e|), the pages' torch.round
+    sends it to the even integer; elsewhere k is the nearest integer.  Blocks
+    with max r and scale_factor 1 give r itself as the raw scale."""
+    r = _window_r()
+    x = np.zeros((len(r), 32), np.float32)
+    x[:, 3] = r
+    _, _, e8 = oracle.qdq_rows(x, 32, "amct", 1.0)
+    want = k_amct_pages(r)
+    assert np.array_equal(e8[:, 0].astype(np.int64) - 127, want)
+    # the windows are not empty: in every exponent at least one r has a binary32
+    # log2 that is a half-integer, and about half of those differ from the
+    # exact nearest integer (odd e rounds up, even e down)
+    differs = want != search_k_nearest(r)
+    assert 100 < differs.sum() < len(r) // 2
+    e = (r.view(np.uint32) >> 23).astype(np.int64) - 127
+    assert set(e[differs] % 2) == {0, 1}
+
+
+def test_amct_scale_matches_torch_binary32_pipeline(oracle):
+    """Cross-check, not a pin: the raw-scale rounding of the pages' code run in
+    torch on float32 tensors (clamp(amax / sf, 2^-30), log2, round) agrees
+    with the oracle on the window values and on random fp32 maxima."""
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(17)
+    wr = _window_r()
+    wr = wr[wr < np.float32(2.0 ** 124)]                 # 6 r stays finite
+    v = np.concatenate([wr * np.float32(6.0), np.exp(g.uniform(-60, 60, 50000)).astype(np.float32)])
+    x = np.zeros((len(v), 32), np.float32)
+    x[:, 9] = v
+    _, _, e8 = oracle.qdq_rows(x, 32, "amct")
+    t = torch.from_numpy(v)
+    k = torch.round(torch.log2(torch.clamp(t / 6.0, min=2.0 ** -30))).to(torch.int64).numpy()
+    assert np.array_equal(e8[:, 0].astype(np.int64) - 127, k)
 
 
 def test_floor_scale_random_fp32(oracle):
@@ -253,7 +345,7 @@ def test_invariants_random_heavy_tailed(oracle, rule, block):
         assert np.array_equal(e8.astype(np.int64) - 127, search_k_floor(xp))
     else:
         r = np.maximum(xp.astype(np.float32) / np.float32(6.0), np.float32(2.0 ** -30))
-        assert np.array_equal(e8.astype(np.int64) - 127, search_k_amct(r))
+        assert np.array_equal(e8.astype(np.int64) - 127, k_amct_pages(r))
     q, idx = expected_from_k(x64, kfull, rule)
     assert np.array_equal(bits32(y), bits32(q.astype(np.float32)))
     assert np.array_equal(clip, np.abs(x64) > 6 * np.ldexp(1.0, kfull))
@@ -297,12 +389,45 @@ def test_zero_blocks(oracle, dtype):
 
 def test_signed_zero_rules(oracle):
     x = f32([[4.0, -1e-3, -0.0, 1e-3, -0.2, 0.0] + [0.0] * 26])
-    y, _, _ = oracle.qdq_rows(x, 32, "floor")
-    b = bits32(y[0])
-    assert b[1] == 0x80000000      # negative value snapping to 0 -> -0.0
-    assert b[2] == 0               # -0.0 -> +0.0
-    assert b[3] == 0 and b[5] == 0
-    assert b[4] == 0x80000000
+    for rule in ("floor", "amct"):
+        y, _, _ = oracle.qdq_rows(x, 32, rule)
+        b = bits32(y[0])
+        assert b[1] == 0x80000000      # negative value snapping to 0 -> -0.0
+        assert b[2] == 0               # -0.0 -> +0.0
+        assert b[3] == 0 and b[5] == 0
+        if rule == "floor":            # (amct's scale 2^-1 gives -0.2 -> -0.25)
+            assert b[4] == 0x80000000
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_amct_sign_of_underflowed_quotient(oracle, dtype):
+    """AMCT takes torch.sign of the binary32 quotient x / 2^k: it is zero, and
+    the output +0.0, when |x| <= 2^(k-150) (at 2^(k-150) exactly the quotient
+    is half the smallest subnormal and rounds to even, i.e. to 0); FLOOR keeps
+    the exact sign, -0.0.  Blocks with max 6 * 2^k (scale 2^k in both rules)
+    for k from 16 to 125 (6 * 2^125 is near the top of the range) hold
+    -2^(k-150) scaled by 1, 1 + 2^-7, 2, 1/2."""
+    rows = []
+    for k in range(16, 126):
+        t = 2.0 ** (k - 150)
+        rows.append([6 * 2.0 ** k, -t, -t * (1 + 2 ** -7), -2 * t, -t / 2, t] + [0.0] * 26)
+    x32 = np.array(rows, dtype=np.float32)            # values below the dtype's range flush to 0
+    x = x32 if dtype == "f32" else W.f32_to_bf16_bits(x32)
+    xv = (x if dtype == "f32" else W.bf16_bits_to_f32(x)).astype(np.float64)
+    for rule in ("floor", "amct"):
+        y, _, e8 = oracle.qdq_rows(x, 32, rule)
+        assert (e8[:, 0].astype(int) - 127 == np.arange(16, 126)).all()
+        ys = (y.view(np.uint32) >> 31) if dtype == "f32" else (y >> 15)
+        neg = xv < 0
+        if rule == "floor":
+            want = neg
+        else:
+            lim = np.ldexp(1.0, np.arange(16, 126) - 150)[:, None]
+            want = neg & (np.abs(xv) > lim)
+        assert np.array_equal(ys.astype(bool), want), rule
+        assert (y.view(np.uint32 if dtype == "f32" else np.uint16)[:, 1:] & (0x7FFFFFFF if dtype == "f32" else 0x7FFF) == 0).all()
+    # both outcomes occur under amct in every dtype
+    assert want.any() and (neg & ~want).any()
 
 
 def test_subnormal_outputs_bf16(oracle):
