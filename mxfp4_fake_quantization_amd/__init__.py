@@ -180,6 +180,23 @@ def _same_elems(x, *ys):
             raise ValueError("outputs must have x's dtype and number of elements")
 
 
+def _need(t, n: int, what: str):
+    """The kernels write (or read) n elements of t: refuse a smaller buffer
+    here, since the C ABI takes bare pointers and cannot see its size."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{what} holds {t.numel()} elements; the call needs {n}")
+
+
+def _block_rows(group_list, rows: int, block: int, group_list_type: int):
+    """Block-rows a grouped call produces: exact for a host list (checked by
+    _group_list), the bound ceil(rows/block) + groups for a device list."""
+    if isinstance(group_list, torch.Tensor) and group_list.is_cuda:
+        return grouped_scale_rows_max(rows, block, group_list.numel())
+    v = torch.as_tensor(group_list, dtype=torch.int64).reshape(-1).tolist()
+    counts = v if group_list_type == 1 else [b - a for a, b in zip([0] + v[:-1], v)]
+    return sum(-(-max(int(c), 0) // block) for c in counts)
+
+
 # ------------------------------------------------------------ entry points
 
 def _group_list(group_list, rows: int, group_list_type: int):
@@ -208,6 +225,11 @@ def mxfp4_qdq_fwd(x, axis=ROW, y_row=None, mask_row=None, scales_row=None, y_col
     """Fused QDQ forward (+ clip bitmap, + E8M0 scales); see include/mxfp4.h."""
     _same_elems(x, y_row, y_col)
     d = _desc(x, block, rule, scale_factor)
+    rows, cols, b = d.rows, d.cols, int(block)
+    _need(mask_row, rows * -(-cols // 32), "mask_row")
+    _need(scales_row, rows * -(-cols // b), "scales_row")
+    _need(mask_col, -(-rows // 32) * cols, "mask_col")
+    _need(scales_col, -(-rows // b) * cols, "scales_col")
     st = _load().mxfp4_qdq_fwd(ctypes.byref(d), int(axis), _ptr(x), _ptr(y_row),
                                _ptr(mask_row, "mask"), _ptr(scales_row, "u8"), _ptr(y_col),
                                _ptr(mask_col, "mask"), _ptr(scales_col, "u8"), _stream())
@@ -219,6 +241,15 @@ def mxfp4_ste_bwd(grad_out, mask, grad_in, layout=ROW, block=32, group_list=None
     """Clipped (mask given) or plain (mask None) STE backward."""
     _same_elems(grad_out, grad_in)
     d = _desc(grad_out, block, "floor", 6.0)
+    rows, cols = d.rows, d.cols
+    if mask is not None:
+        if layout == ROW:
+            _need(mask, rows * -(-cols // 32), "mask")
+        elif layout == COL:
+            _need(mask, -(-rows // 32) * cols, "mask")
+        elif layout == GROUPED and group_list is not None:
+            nbt = _block_rows(group_list, rows, int(block), group_list_type)
+            _need(mask, nbt * (int(block) // 32) * cols, "mask")
     group_list = _group_list(group_list, d.rows, group_list_type)
     n_groups = group_list.numel() if group_list is not None else 0
     st = _load().mxfp4_ste_bwd(ctypes.byref(d), int(layout), _ptr(grad_out), _ptr(mask, "mask"),
@@ -232,6 +263,12 @@ def mxfp4_quant_pack(x, codes, scales, y=None, mask=None, block=32, rule="floor"
     """Packed E2M1 codes (two per byte) + E8M0 scales, row-wise blocks."""
     _same_elems(x, y)
     d = _desc(x, block, rule, scale_factor)
+    rows, cols = d.rows, d.cols
+    if codes is None or scales is None:
+        raise ValueError("codes and scales are required")
+    _need(codes, rows * ((cols + 1) // 2), "codes")
+    _need(scales, rows * -(-cols // int(block)), "scales")
+    _need(mask, rows * -(-cols // 32), "mask")
     st = _load().mxfp4_quant_pack(ctypes.byref(d), _ptr(x), _ptr(codes, "u8"), _ptr(scales, "u8"),
                                   _ptr(y), _ptr(mask, "mask"), _stream())
     _check(st, "mxfp4_quant_pack")
@@ -243,6 +280,11 @@ def mxfp4_grouped_qdq(x, group_list, y, mask=None, scales=None, block=32, rule="
     or cumulative row ends (type 0), int64 on the device."""
     _same_elems(x, y)
     d = _desc(x, block, rule, scale_factor)
+    if group_list is None:
+        raise ValueError("group_list is required")
+    nbt = _block_rows(group_list, d.rows, int(block), group_list_type)
+    _need(mask, nbt * (int(block) // 32) * d.cols, "mask")
+    _need(scales, nbt * d.cols, "scales")
     group_list = _group_list(group_list, d.rows, group_list_type)
     st = _load().mxfp4_grouped_qdq(ctypes.byref(d), _ptr(x), _ptr(group_list, "i64"),
                                    group_list.numel(), int(group_list_type), _ptr(y),
@@ -360,6 +402,17 @@ def mxfp4_grouped_matmul(a, a_scales, b, b_scales, c, K=None, group_list=None, g
         raise ValueError("c must be a bfloat16 or float32 tensor")
     M = a.shape[0]
     ldc = c.shape[-1]
+    # rows of every operand array the kernels read (row lengths are checked by
+    # the library against ld / ld_scales)
+    n_list = 0 if group_list is None else (group_list.numel() if isinstance(group_list, torch.Tensor)
+                                           else len(group_list))
+    if a_scales is None or a_scales.dim() < 2 or a_scales.shape[-2] < M:
+        raise ValueError(f"a_scales must have M={M} rows")
+    if b is None or b_scales is None or b.dim() < 2 or b_scales.dim() < 2 or b_scales.shape[-2] != b.shape[-2]:
+        raise ValueError("b_scales must have as many rows as b")
+    if group_type == GROUP_ROWS and b_group_stride is None and b.dim() == 3:
+        if b.shape[0] < max(n_list, 1) or b_scales.shape[0] < max(n_list, 1):
+            raise ValueError(f"b and b_scales must hold one matrix per group ({max(n_list, 1)})")
     if group_type == GROUP_ROWS:
         if c.dim() != 2 or c.shape[0] != M:
             raise ValueError(f"c must be [M={M}, N]")
@@ -388,6 +441,7 @@ def mxfp4_grouped_matmul(a, a_scales, b, b_scales, c, K=None, group_list=None, g
     ng = 0 if gl is None else gl.numel()
     if group_type == GROUP_K and c.shape[0] != ng:
         raise ValueError(f"c must hold one [M, N] matrix per group ({ng})")
+
     oa = _operand(a, a_scales, a_fmt, a_block)
     ob = _operand(b, b_scales, b_fmt, b_block, b_group_stride)
     out = 1 if c.dtype == torch.float32 else 0

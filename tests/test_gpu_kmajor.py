@@ -242,56 +242,3 @@ def test_dequant_every_nibble_and_byte(oracle, dtype):
     assert np.array_equal(got, want)
 
 
-# ------------------------------------------------------------------ full size
-
-def test_kmajor_weight_pack_sampled(oracle):
-    """bf16 28672x8192 weight as the K-major operand of its backward-data
-    product (blocks of 32 along the 28672 rows); sampled columns against the
-    oracle (columns are independent, so the oracle packs just those)."""
-    x = W.weight_pack()
-    rows, cols = x.shape
-    kb = M.kmajor_k_blocks(rows, 32)
-    codes = torch.empty((cols, kb * 16), dtype=torch.uint8, device="cuda")
-    sc = torch.empty((cols, kb), dtype=torch.uint8, device="cuda")
-    M.mxfp4_quant_pack_kmajor(dev(x), codes, sc)
-    torch.cuda.synchronize()
-    ci = np.sort(np.random.default_rng(3).choice(cols, 96, replace=False))
-    cit = torch.from_numpy(ci).cuda()
-    co, so, _ = oracle.pack_kmajor(np.ascontiguousarray(x[:, ci]), 32, k_blocks=kb)
-    assert np.array_equal(host(codes[cit]), co)
-    assert np.array_equal(host(sc[cit]), so)
-
-
-def test_kmajor_moe_grouped_sampled(oracle):
-    """bf16 32768x7168 tokens in 8 expert groups: the grouped K-major operand
-    of the weight-gradient product; sampled columns against the oracle."""
-    x, counts = W.moe_grouped()
-    rows, cols = x.shape
-    kb = M.kmajor_k_blocks(rows, 32, len(counts))
-    codes = torch.full((cols, kb * 16), FILL, dtype=torch.uint8, device="cuda")
-    sc = torch.full((cols, kb), FILL, dtype=torch.uint8, device="cuda")
-    M.mxfp4_quant_pack_kmajor(dev(x), codes, sc, group_list=dev(counts))
-    torch.cuda.synchronize()
-    ci = np.sort(np.random.default_rng(4).choice(cols, 96, replace=False))
-    cit = torch.from_numpy(ci).cuda()
-    co, so, nbt = oracle.pack_kmajor(np.ascontiguousarray(x[:, ci]), 32, group_list=counts,
-                                     k_blocks=kb, fill=FILL)
-    assert np.array_equal(host(codes[cit]), co)
-    assert np.array_equal(host(sc[cit]), so)
-    assert nbt <= kb
-
-
-def test_dequant_weight_pack_sampled(oracle):
-    """Decode of the bf16 28672x8192 weight's row-wise packed form (GPU pack
-    then GPU decode); sampled rows equal the oracle's QDQ values."""
-    x = W.weight_pack()
-    rows, cols = x.shape
-    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda")
-    sc = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
-    M.mxfp4_quant_pack(dev(x), codes, sc)
-    y = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
-    M.mxfp4_dequant(codes, sc, y)
-    torch.cuda.synchronize()
-    ri = np.sort(np.random.default_rng(5).choice(rows, 512, replace=False))
-    yo, _, _ = oracle.qdq_rows(x[ri], 32)
-    assert np.array_equal(host(y[torch.from_numpy(ri).cuda()]), yo)

@@ -1,8 +1,9 @@
 """GPU parity of the MXFP8 (OCP MX) quantization of grad_output, through the
 C-ABI binding, bit for bit against the oracle: every bf16 value under several
 block maxima, exact fp32 midpoints (ties to even), zero / subnormal /
-saturating blocks, ragged widths (flat, row-vector and scalar launches), and
-a full-size tensor on sampled rows.  Outputs carry a canary past their end."""
+saturating blocks, ragged widths (flat, row-vector and scalar launches); the
+full-size MoE tensors are in test_gpu_full_size.py.  Outputs carry a canary
+past their end."""
 import numpy as np
 import pytest
 import torch
@@ -119,21 +120,6 @@ def test_mxfp8_edge_blocks(oracle):
             assert np.array_equal(s, so) and np.array_equal(q, qo)
 
 
-def test_mxfp8_grad_output_sampled(oracle):
-    """A grad_output-sized bf16 tensor (32768 x 7168, N(0,1) tokens of the MoE
-    layer): sampled rows against the oracle."""
-    x, _ = W.moe_grouped()
-    rows, cols = x.shape
-    q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
-    s = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
-    M.mxfp8_quant(dev(x), q, s)
-    torch.cuda.synchronize()
-    ri = np.sort(np.random.default_rng(9).choice(rows, 512, replace=False))
-    rit = torch.from_numpy(ri).cuda()
-    qo, so = oracle.mxfp8_rows(x[ri])
-    assert np.array_equal(host(q[rit]), qo)
-    assert np.array_equal(host(s[rit]), so)
-
 
 # ---- K-major MXFP8 (grouped column-wise operand of the TN product) ------------------
 
@@ -204,23 +190,6 @@ def test_mxfp8_kmajor_inconsistent_list_is_clamped(oracle, list_type, gl):
                                       k_blocks=kb, fill=0xA5)
     assert np.array_equal(q, qo) and np.array_equal(s, so)
 
-
-def test_mxfp8_kmajor_moe_sampled(oracle):
-    """The grouped MoE activation at full size (32768 tokens x 7168, 8 experts):
-    sampled columns against the oracle (a column's K-major row depends on that
-    column alone)."""
-    x, counts = W.moe_grouped()
-    rows, cols = x.shape
-    kb = M.mxfp8_kmajor_k_blocks(rows, len(counts))
-    q = torch.empty((cols, kb * 32), dtype=torch.uint8, device="cuda")
-    s = torch.empty((cols, kb), dtype=torch.uint8, device="cuda")
-    M.mxfp8_quant_kmajor(dev(x), q, s, group_list=counts.tolist())
-    torch.cuda.synchronize()
-    ci = np.sort(np.random.default_rng(10).choice(cols, 24, replace=False))
-    cit = torch.from_numpy(ci).cuda()
-    qo, so, nbt = oracle.mxfp8_kmajor(np.ascontiguousarray(x[:, ci]), "e4m3", counts, 1, k_blocks=kb)
-    assert np.array_equal(host(q[cit])[:, :32 * nbt], qo[:, :32 * nbt])
-    assert np.array_equal(host(s[cit])[:, :nbt], so[:, :nbt])
 
 
 def test_tn_weight_gradient_end_to_end(oracle):

@@ -1,9 +1,8 @@
 """GPU parity: every output of the HIP library, called through the C-ABI
 binding, equals the CPU oracle bit for bit (tolerance 0 ULP: every produced
 value is exact) on the same seeded inputs.  Small shapes span several tiles
-and ragged tails; the full-size workloads are checked on sampled rows /
-columns (the oracle recomputes exactly those blocks).  Every output buffer
-carries a canary past its end."""
+and ragged tails; the five workloads at full size are in
+test_gpu_full_size.py.  Every output buffer carries a canary past its end."""
 import numpy as np
 import pytest
 import torch
@@ -419,105 +418,11 @@ def test_pack(oracle, dtype, block, rule, shape):
     assert np.array_equal(host(c2), co) and np.array_equal(host(s2), so)
 
 
-# ------------------------------------------------------ the five workloads
-
-def test_tiny_qat_linear(oracle):
-    """fp32 weight 32x64 and input 4x64 ~ N(0,1): row-wise block-32 QDQ with
-    the clip mask, then the clipped-STE backward of a ones gradient."""
-    w, xin = W.tiny_qat(0)
-    for a in (w, xin):
-        rows, cols = a.shape
-        y = torch.empty(a.shape, dtype=torch.float32, device="cuda")
-        m = torch.empty((rows, cols // 32), dtype=torch.int32, device="cuda")
-        M.mxfp4_qdq_fwd(dev(a), M.ROW, y_row=y, mask_row=m)
-        ones = torch.ones(a.shape, dtype=torch.float32, device="cuda")
-        gi = torch.empty_like(ones)
-        M.mxfp4_ste_bwd(ones, m, gi, layout=M.ROW)
-        torch.cuda.synchronize()
-        yo, clip, _ = oracle.qdq_rows(a, 32)
-        assert np.array_equal(host(y), yo)
-        assert np.array_equal(host(gi), oracle.ste_bwd(np.ones_like(a), clip))
-        assert np.array_equal(host(gi), 1.0 - clip.astype(np.float32))
+# ------------------------------------------------------------ repeatability
 
 
-def test_weight_4k_full(oracle):
-    """bf16 4096x4096 weight with outliers, zero blocks and planted blocks:
-    full parity of y, bitmap and the STE gradient."""
-    x, g, manifest = W.weight_4k()
-    rows, cols = x.shape
-    y = torch.empty(x.shape, dtype=torch.bfloat16, device="cuda")
-    m = torch.empty((rows, cols // 32), dtype=torch.int32, device="cuda")
-    xd, gd = dev(x), dev(g)
-    M.mxfp4_qdq_fwd(xd, M.ROW, y_row=y, mask_row=m)
-    gi = torch.empty_like(gd)
-    M.mxfp4_ste_bwd(gd, m, gi, layout=M.ROW)
-    torch.cuda.synchronize()
-    yo, clip, _ = oracle.qdq_rows(x, 32)
-    assert np.array_equal(host(y), yo)
-    assert np.array_equal(unpack_row_bitmap(host(m), cols)[0], clip)
-    assert np.array_equal(host(gi), oracle.ste_bwd(g, clip))
-    assert len(manifest) > 0 and clip.any()
 
 
-def test_act_dual_sampled(oracle):
-    """bf16 16384x8192 Student-t activation, dual direction in one launch:
-    sampled rows (row view) and sampled column strips (column view)."""
-    x = W.act_dual()
-    rows, cols = x.shape
-    yr = torch.empty(x.shape, dtype=torch.bfloat16, device="cuda")
-    yc = torch.empty_like(yr)
-    mr = torch.empty((rows, cols // 32), dtype=torch.int32, device="cuda")
-    mc = torch.empty((rows // 32, cols), dtype=torch.int32, device="cuda")
-    M.mxfp4_qdq_fwd(dev(x), M.ROW | M.COL, y_row=yr, mask_row=mr, y_col=yc, mask_col=mc)
-    torch.cuda.synchronize()
-    g = np.random.default_rng(0)
-    ri = np.sort(g.choice(rows, 512, replace=False))
-    yo, co, _ = oracle.qdq_rows(x[ri], 32)
-    assert np.array_equal(host(yr[torch.from_numpy(ri).cuda()]), yo)
-    assert np.array_equal(unpack_row_bitmap(host(mr[torch.from_numpy(ri).cuda()]), cols)[0], co)
-    ci = np.sort(g.choice(cols, 256, replace=False))
-    yo, co, _ = oracle.qdq_cols(np.ascontiguousarray(x[:, ci]), 32)
-    cit = torch.from_numpy(ci).cuda()
-    assert np.array_equal(host(yc[:, cit]), yo)
-    assert np.array_equal(unpack_col_bitmap(host(mc[:, cit]), rows)[0], co)
-
-
-def test_moe_grouped_sampled(oracle):
-    """bf16 32768x7168, 8 expert groups (multinomial counts): grouped
-    column-wise block-32 QDQ, sampled column strips against the oracle."""
-    x, counts = W.moe_grouped()
-    rows, cols = x.shape
-    y = torch.empty(x.shape, dtype=torch.bfloat16, device="cuda")
-    sc = torch.empty((M.grouped_scale_rows_max(rows, 32, 8), cols), dtype=torch.uint8, device="cuda")
-    M.mxfp4_grouped_qdq(dev(x), dev(counts), y, scales=sc)
-    torch.cuda.synchronize()
-    g = np.random.default_rng(1)
-    ci = np.sort(g.choice(cols, 128, replace=False))
-    yo, _, eo = oracle.grouped_cols(np.ascontiguousarray(x[:, ci]), counts, 32)
-    cit = torch.from_numpy(ci).cuda()
-    assert np.array_equal(host(y[:, cit]), yo)
-    nbt = eo.shape[0]
-    assert np.array_equal(host(sc[:nbt, cit]), eo)
-    assert (counts % 32 != 0).any()        # ragged group tails exercised
-
-
-@pytest.mark.parametrize("block", [32, 128])
-def test_weight_pack_sampled(oracle, block):
-    """bf16 28672x8192 weight packed row-wise; sampled rows against the
-    oracle, and the decoded sample equals the QDQ values."""
-    x = W.weight_pack()
-    rows, cols = x.shape
-    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda")
-    sc = torch.empty((rows, cols // block), dtype=torch.uint8, device="cuda")
-    M.mxfp4_quant_pack(dev(x), codes, sc, block=block)
-    torch.cuda.synchronize()
-    ri = np.sort(np.random.default_rng(2).choice(rows, 1024, replace=False))
-    rit = torch.from_numpy(ri).cuda()
-    co, so = oracle.pack_rows(x[ri], block)
-    assert np.array_equal(host(codes[rit]), co)
-    assert np.array_equal(host(sc[rit]), so)
-    yo, _, _ = oracle.qdq_rows(x[ri], block)
-    assert np.array_equal(oracle.unpack_rows(co, so, cols, block), yo)
 
 
 def test_repeatable():
