@@ -1,6 +1,10 @@
 """Benchmark of the fused MXFP4 fake-quant hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S] [--all OUT.json]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S] [--no-cpu] [--no-large]
+                    [--no-configs] [--all OUT.json] [--gemm OUT.json]
+    python bench.py --profile-run MANIFEST.json      (fixed launch sequence for rocprofv3)
+    python bench.py --summarize KIND DIR MANIFEST.json OUT.md   (rocprofv3 CSV -> table)
+    python bench.py --stamps OUT.json                (per-workgroup start / end clocks)
 
 One step = the whole hot path over one batch of the weight_4k workload: bf16
 4096x4096 weight (N(0, 0.02^2), outliers, zero blocks, planted blocks),
@@ -16,20 +20,29 @@ roofline = the forward kernel against the 8 TB/s HBM peak: its average launch
 duration is timed with HIP events over K back-to-back forward launches right
 after the timed steps; traffic = HBM bytes per launch from the committed
 rocprofv3 FETCH_SIZE / WRITE_SIZE run (null if the kernel source changed).
-cpu_baseline = the CPU oracle (single thread) on the same workload, repeated
-for about 10 s.
-steady_state = the same forward, backward and step on the same distribution
-at 28672x8192 (969 MB per kernel, 2 rotating buffer sets), where the fixed
-start-up and drain of a launch (~2.5 us) no longer weighs; context only, the
-value stays the 4096x4096 step (--no-large skips it).
+cpu_baseline = the CPU oracle (single thread) on the same workload.
 
---all OUT.json additionally times the other workloads (full sizes) and a
-plain device copy, and writes them to OUT.json (stdout keeps one line).
+Also on the line:
+- achievable: streaming probes (libmxfp4_probe.so) that move the forward
+  kernel's bytes in its access pattern with no arithmetic, over the same
+  buffers and rotation: the bandwidth this launch shape can get at this size;
+- steady_state: the same forward, backward and step on the same distribution
+  at 28672x8192 (969 MB per kernel), where a launch's fixed start-up and drain
+  no longer weigh, with its own probe (--no-large skips it);
+- configs: every other workload at full size (tiny QAT latency, dual
+  direction, grouped MoE, packing at blocks 32 and 128), each with GB/s,
+  elements/s, its fraction of the HBM peak and the oracle timed on a bounded
+  sample of the same input (--no-configs skips them).
+
+--all OUT.json additionally times the f-rows (K-major packs, decode, MXFP8,
+column-only, a device copy, the grouped matmuls) and writes them to OUT.json.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import glob
 import hashlib
 import json
 import os
@@ -47,6 +60,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_fwd_weight4k_traffic.json")
 KERNEL_SOURCES = ["mxfp4_fake_quantization_amd/csrc/row_kernels.hip",
                   "mxfp4_fake_quantization_amd/csrc/mxfp4_device.h",
                   "mxfp4_fake_quantization_amd/csrc/mxfp4_math.h"]
+PROBE_LIB = os.path.join(ROOT, "mxfp4_fake_quantization_amd", "libmxfp4_probe.so")
+PROBE_FWD, PROBE_COPY, PROBE_READ, PROBE_WRITE = 0, 1, 2, 3
 
 
 def kernel_source_sha() -> str:
@@ -57,7 +72,7 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(per_launch_alg_bytes: float):
+def measured_traffic():
     """HBM bytes per forward launch from the committed rocprofv3 counter run
     (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
     when the kernel source changed since the counters were taken."""
@@ -73,7 +88,7 @@ def measured_traffic(per_launch_alg_bytes: float):
 
 class HipEvents:
     """hipEvent_t handles recorded straight through the HIP runtime (the one
-    torch has loaded), so timing a launch costs the host about a microsecond."""
+    torch has loaded) on the stream the kernels are launched on."""
 
     def __init__(self, n):
         import torch
@@ -115,8 +130,8 @@ class HipEvents:
 class Call:
     """A pre-marshalled C-ABI call (argument tuple built once)."""
 
-    def __init__(self, fn, *args):
-        self.fn, self.args = fn, args
+    def __init__(self, fn, *args, keep=None):
+        self.fn, self.args, self.keep = fn, args, keep
 
     def __call__(self):
         st = self.fn(*self.args)
@@ -125,23 +140,59 @@ class Call:
             raise RuntimeError(M.mxfp4_last_error())
 
 
-def cpu_baseline(x, g, min_seconds=10.0):
-    import oracle
-    rows, cols = x.shape
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        _, clip, _ = oracle.qdq_rows(x, 32, "floor")
-        oracle.ste_bwd(g, clip)
-        reps += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    dt = (time.perf_counter() - t0) / reps
-    nbytes = rows * cols * 8.25
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole weight_4k workload ({rows}x{cols} bf16 fwd+bwd), {reps} reps, "
-                      f"{dt * 1e3:.1f} ms per step, single-threaded C oracle",
-            "host": host_cpu()}
+class Probe:
+    """The streaming probes of libmxfp4_probe.so."""
+
+    def __init__(self):
+        if not os.path.exists(PROBE_LIB):
+            raise RuntimeError(f"{PROBE_LIB} is not built (python -m mxfp4_fake_quantization_amd.build)")
+        self.lib = ctypes.CDLL(PROBE_LIB)
+        vp = ctypes.c_void_p
+        self.lib.probe_stream.argtypes = [ctypes.c_int, vp, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                          vp, vp]
+        self.lib.probe_stream.restype = ctypes.c_int
+        self.lib.probe_wall_clock_khz.argtypes = [ctypes.c_int]
+        self.lib.probe_wall_clock_khz.restype = ctypes.c_int
+
+    def call(self, kind, src, dst, side, npieces, threads, stream, stamps=None, per_lane=1):
+        vp = ctypes.c_void_p
+        args = (kind, vp(src.data_ptr()) if src is not None else None,
+                vp(dst.data_ptr()) if dst is not None else None,
+                vp(side.data_ptr()) if side is not None else None, npieces, threads, per_lane,
+                vp(stamps.data_ptr()) if stamps is not None else None, stream)
+        fn = self.lib.probe_stream
+
+        def run():
+            st = fn(*args)
+            if st != 0:
+                raise RuntimeError(f"probe_stream failed with hip error {st}")
+        return run
+
+
+class Timer:
+    """Per-launch time of back-to-back launches on the launch stream: `trials`
+    runs of `reps` launches (rotating over the given calls) between two HIP
+    events; events around every launch would add their own gaps."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.hev = HipEvents(2)
+
+    def __call__(self, calls, reps=30, warm=60, trials=3):
+        rec, ev = self.hev.record, self.hev.ev
+        for i in range(warm):
+            calls[i % len(calls)]()
+        self.torch.cuda.synchronize()
+        t = []
+        for _ in range(trials):
+            rec(ev[0], self.stream)
+            for i in range(reps):
+                calls[i % len(calls)]()
+            rec(ev[1], self.stream)
+            self.torch.cuda.synchronize()
+            t.append(self.hev.ms(0, 1) * 1e-3 / reps)
+        t = np.array(t)
+        return float(np.median(t)), float(t.min())
 
 
 def host_cpu() -> str:
@@ -158,70 +209,157 @@ def host_cpu() -> str:
     return f"{model}; {len(os.sched_getaffinity(0))} cores available, nproc {os.cpu_count()}"
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=300)
-    ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--sets", type=int, default=8)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-large", action="store_true",
-                    help="skip the 28672x8192 steady-state forward / backward timing")
-    ap.add_argument("--all", metavar="OUT", default=None)
-    ap.add_argument("--gemm", metavar="OUT", default=None,
-                    help="time only the grouped MX matmuls (NN / NT / TN of the MoE layer) into OUT")
-    ap.add_argument("--calib-copy", action="store_true",
-                    help="run only a 512 MiB device copy (rocprofv3 counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the hot path has no "
-              "cross-GPU step; each GPU would run its own shard independently.", file=sys.stderr)
-        sys.exit(2)
+def repeat_for(fn, min_seconds):
+    """Run fn until min_seconds have passed; returns (seconds per run, runs)."""
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        fn()
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    return (time.perf_counter() - t0) / reps, reps
 
-    import torch
-    import workloads as W
-    import mxfp4_fake_quantization_amd as M
 
-    if args.calib_copy:
-        a = torch.empty(256 << 20, dtype=torch.int16, device="cuda")
-        b = torch.empty_like(a)
-        for _ in range(5):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"calib_copy_bytes_read": a.numel() * 2, "calib_copy_bytes_written": a.numel() * 2}))
-        return
+def oracle_baseline(fn, nbytes, nelem, sample, min_seconds):
+    """The single-threaded C oracle on a bounded sample of a workload: GB/s of
+    the sample's algorithmic bytes (same per-element bytes as the GPU run)."""
+    dt, reps = repeat_for(fn, min_seconds)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "elements_per_s": round(nelem / dt, 1),
+            "sample": f"{sample}; {reps} reps, {dt * 1e3:.1f} ms each, single-threaded C oracle",
+            "host": host_cpu()}
 
-    lib = M._load()
-    if args.gemm:
-        res = bench_gemm(M, W, torch, {})
-        with open(args.gemm, "w") as f:
-            json.dump(res, f, indent=1)
-        print(json.dumps(res))
-        return
+
+def gbs(nbytes, seconds):
+    return nbytes / seconds / 1e9
+
+
+def entry(name, kernel, nbytes, nelem, t, **extra):
+    med, best = t
+    d = {"workload": name, "kernel": kernel, "alg_bytes": int(nbytes), "median_us": round(med * 1e6, 2),
+         "best_us": round(best * 1e6, 2), "GBps": round(gbs(nbytes, med), 1),
+         "elements_per_s": round(nelem / med, 1), "frac": round(gbs(nbytes, med) / HBM_PEAK_GBS, 4)}
+    d.update(extra)
+    return d
+
+
+# ---------------------------------------------------------------- workloads
+# Each builder returns the pre-marshalled launches over its buffer sets plus
+# what describes them; bench_* time them and profile_run replays them.
+
+def bf16_dev(torch, a):
+    return torch.from_numpy(a).view(torch.bfloat16).cuda()
+
+
+def build_weight4k(M, lib, W, torch, stream, sets):
     x_np, g_np, _ = W.weight_4k()
     rows, cols = x_np.shape
+    x0, g0 = bf16_dev(torch, x_np), bf16_dev(torch, g_np)
+    xs = [x0.clone() for _ in range(sets)]
+    gs = [g0.clone() for _ in range(sets)]
+    ys = [torch.empty_like(x0) for _ in range(sets)]
+    gis = [torch.empty_like(g0) for _ in range(sets)]
+    ms = [torch.empty((rows, cols // 32), dtype=torch.int32, device="cuda") for _ in range(sets)]
+    desc = M._Desc(1, 32, 0, 0, rows, cols, 6.0, 0)
+    vp = ctypes.c_void_p
+    fwd = [Call(lib.mxfp4_qdq_fwd, ctypes.byref(desc), M.ROW, vp(xs[s].data_ptr()), vp(ys[s].data_ptr()),
+                vp(ms[s].data_ptr()), None, None, None, None, stream, keep=desc) for s in range(sets)]
+    bwd = [Call(lib.mxfp4_ste_bwd, ctypes.byref(desc), M.ROW, vp(gs[s].data_ptr()), vp(ms[s].data_ptr()),
+                vp(gis[s].data_ptr()), None, 0, 1, stream, keep=desc) for s in range(sets)]
+    return dict(x_np=x_np, g_np=g_np, rows=rows, cols=cols, xs=xs, gs=gs, ys=ys, gis=gis, ms=ms,
+                fwd=fwd, bwd=bwd)
+
+
+def build_tiny(M, lib, W, torch, stream):
+    tw, tx = W.tiny_qat(0)
+    fwd, bwd, keep = [], [], []
+    vp = ctypes.c_void_p
+    for arr in (tw, tx):
+        r, c = arr.shape
+        xt = torch.from_numpy(arr).cuda()
+        yt, gt, gi = torch.empty_like(xt), torch.ones_like(xt), torch.empty_like(xt)
+        mt = torch.empty((r, -(-c // 32)), dtype=torch.int32, device="cuda")
+        dt = M._Desc(0, 32, 0, 0, r, c, 6.0, 0)
+        keep.append((xt, yt, gt, gi, mt, dt))
+        fwd.append(Call(lib.mxfp4_qdq_fwd, ctypes.byref(dt), M.ROW, vp(xt.data_ptr()), vp(yt.data_ptr()),
+                        vp(mt.data_ptr()), None, None, None, None, stream, keep=dt))
+        bwd.append(Call(lib.mxfp4_ste_bwd, ctypes.byref(dt), M.ROW, vp(gt.data_ptr()), vp(mt.data_ptr()),
+                        vp(gi.data_ptr()), None, 0, 1, stream, keep=dt))
+
+    def step():
+        fwd[0]()
+        fwd[1]()
+        bwd[0]()
+        bwd[1]()
+    return dict(tw=tw, tx=tx, step=step, keep=keep)
+
+
+def build_dual(M, lib, W, torch, stream, sets=2):
+    xa = W.act_dual()
+    R, C = xa.shape
+    xs = [bf16_dev(torch, xa) for _ in range(sets)]
+    yr = [torch.empty_like(xs[0]) for _ in range(sets)]
+    yc = [torch.empty_like(xs[0]) for _ in range(sets)]
+    mr = [torch.empty((R, C // 32), dtype=torch.int32, device="cuda") for _ in range(sets)]
+    mc = [torch.empty((R // 32, C), dtype=torch.int32, device="cuda") for _ in range(sets)]
+    d = M._Desc(1, 32, 0, 0, R, C, 6.0, 0)
+    vp = ctypes.c_void_p
+    calls = [Call(lib.mxfp4_qdq_fwd, ctypes.byref(d), M.ROW | M.COL, vp(xs[i].data_ptr()), vp(yr[i].data_ptr()),
+                  vp(mr[i].data_ptr()), None, vp(yc[i].data_ptr()), vp(mc[i].data_ptr()), None, stream, keep=d)
+             for i in range(sets)]
+    return dict(x_np=xa, R=R, C=C, calls=calls, bufs=(xs, yr, yc, mr, mc))
+
+
+def build_grouped(M, lib, W, torch, stream, sets=2, with_mask=False):
+    xg, counts = W.moe_grouped()
+    R, C = xg.shape
+    xs = [bf16_dev(torch, xg) for _ in range(sets)]
+    ys = [torch.empty_like(xs[0]) for _ in range(sets)]
+    gl = torch.from_numpy(counts).cuda()
+    G = len(counts)
+    ms = [torch.empty((M.grouped_mask_rows_max(R, 32, G), C), dtype=torch.int32, device="cuda")
+          for _ in range(sets)] if with_mask else [None] * sets
+    d = M._Desc(1, 32, 0, 0, R, C, 6.0, 0)
+    vp = ctypes.c_void_p
+    calls = [Call(lib.mxfp4_grouped_qdq, ctypes.byref(d), vp(xs[i].data_ptr()), vp(gl.data_ptr()), G, 1,
+                  vp(ys[i].data_ptr()), vp(ms[i].data_ptr()) if with_mask else None, None, stream, keep=d)
+             for i in range(sets)]
+    return dict(x_np=xg, counts=counts, R=R, C=C, calls=calls, bufs=(xs, ys, ms, gl))
+
+
+def build_pack(M, lib, W, torch, stream, block, sets=2, x_np=None):
+    xw = W.weight_pack() if x_np is None else x_np
+    R, C = xw.shape
+    xs = [bf16_dev(torch, xw) for _ in range(sets)]
+    codes = [torch.empty((R, C // 2), dtype=torch.uint8, device="cuda") for _ in range(sets)]
+    scs = [torch.empty((R, C // block), dtype=torch.uint8, device="cuda") for _ in range(sets)]
+    d = M._Desc(1, block, 0, 0, R, C, 6.0, 0)
+    vp = ctypes.c_void_p
+    calls = [Call(lib.mxfp4_quant_pack, ctypes.byref(d), vp(xs[i].data_ptr()), vp(codes[i].data_ptr()),
+                  vp(scs[i].data_ptr()), None, None, stream, keep=d) for i in range(sets)]
+    return dict(x_np=xw, R=R, C=C, calls=calls, bufs=(xs, codes, scs))
+
+
+KERNELS = {
+    "fwd": "row_fwd_kernel<bf16,32,floor,flat,U=1,T=64>",
+    "bwd": "ste_row_kernel<bf16,flat>",
+    "dual": "col_fwd_kernel<bf16,32,floor,dual>",
+    "grouped": "col_fwd_kernel<bf16,32,floor,grouped>",
+    "pack32": "row_fwd_kernel<bf16,32,floor,flat,U=2,T=256> (codes + scales)",
+    "pack128": "row_fwd_kernel<bf16,128,floor,flat,U=4,T=256> (codes + scales)",
+}
+
+
+# ---------------------------------------------------------------- headline
+
+def bench_headline(M, lib, W, torch, stream, args, probe):
+    wk = build_weight4k(M, lib, W, torch, stream, args.sets)
+    rows, cols, fwd, bwd = wk["rows"], wk["cols"], wk["fwd"], wk["bwd"]
     n = rows * cols
     fwd_bytes = n * (2 + 2 + 1 / 8)
     bwd_bytes = n * (2 + 1 / 8 + 2)
     step_bytes = fwd_bytes + bwd_bytes
-
-    xs, gs, ys, ms, gis = [], [], [], [], []
-    x0 = torch.from_numpy(x_np).view(torch.bfloat16).cuda()
-    g0 = torch.from_numpy(g_np).view(torch.bfloat16).cuda()
-    for s in range(args.sets):
-        xs.append(x0.clone())
-        gs.append(g0.clone())
-        ys.append(torch.empty_like(x0))
-        gis.append(torch.empty_like(g0))
-        ms.append(torch.empty((rows, cols // 32), dtype=torch.int32, device="cuda"))
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    desc = M._Desc(1, 32, 0, 0, rows, cols, 6.0, 0)
-    vp = ctypes.c_void_p
-    fwd = [Call(lib.mxfp4_qdq_fwd, ctypes.byref(desc), M.ROW, vp(xs[s].data_ptr()), vp(ys[s].data_ptr()),
-                vp(ms[s].data_ptr()), None, None, None, None, stream) for s in range(args.sets)]
-    bwd = [Call(lib.mxfp4_ste_bwd, ctypes.byref(desc), M.ROW, vp(gs[s].data_ptr()), vp(ms[s].data_ptr()),
-                vp(gis[s].data_ptr()), None, 0, 1, stream) for s in range(args.sets)]
-
     for i in range(args.warmup):
         fwd[i % args.sets]()
         bwd[i % args.sets]()
@@ -231,7 +369,7 @@ def main():
     # events (per-kernel events inside the loop would add ~2 us per kernel of
     # marker overhead to the GPU timeline).
     K = args.steps
-    hev = HipEvents(6)
+    hev = HipEvents(5)
     rec, evs = hev.record, hev.ev
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -255,15 +393,12 @@ def main():
         bwd[i % args.sets]()
     rec(evs[4], stream)
     torch.cuda.synchronize()
-    fwd_ms = np.array([hev.ms(2, 3) / K])
-    bwd_ms = np.array([hev.ms(3, 4) / K])
+    fwd_s = hev.ms(2, 3) / K * 1e-3
+    bwd_s = hev.ms(3, 4) / K * 1e-3
     hev.close()
-    ms_per_step = total_ms / K
-    value = step_bytes * K / (total_ms * 1e-3) / 1e9
+    value = gbs(step_bytes * K, total_ms * 1e-3)
+    achieved = gbs(fwd_bytes, fwd_s)
 
-    fwd_avg_s = float(fwd_ms.mean()) * 1e-3
-    achieved = fwd_bytes / fwd_avg_s / 1e9
-    traffic = measured_traffic(fwd_bytes)
     result = {
         "metric": "fused MXFP4 QDQ+STE GB/s and % of MI355X HBM peak (1 GPU)",
         "value": round(value, 2),
@@ -271,7 +406,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(total_ms / K, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -283,30 +418,39 @@ def main():
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "elements_per_s": round(2 * n * K / (total_ms * 1e-3), 1),
-        "fwd_us": round(float(fwd_ms.mean()) * 1e3, 3),
-        "bwd_us": round(float(bwd_ms.mean()) * 1e3, 3),
+        "fwd_us": round(fwd_s * 1e6, 3),
+        "bwd_us": round(bwd_s * 1e6, 3),
         "wall_s": round(wall, 4),
-        "roofline": {"bound": "hbm", "kernel": "row_fwd_kernel<bf16,32,floor,flat>",
+        "roofline": {"bound": "hbm", "kernel": KERNELS["fwd"],
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
+                     "traffic": measured_traffic(),
                      "alg_bytes_per_launch": fwd_bytes},
     }
-    if args.all:
-        result["other_workloads_file"] = args.all
-        other = bench_all(M, lib, W, torch, args)
-        with open(args.all, "w") as f:
-            json.dump(other, f, indent=1)
-    if not args.no_large:
-        result["steady_state"] = steady_state(M, lib, W, torch, stream)
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(x_np, g_np)
-    else:
-        result["cpu_baseline"] = None
-    print(json.dumps(result), flush=True)
+    # achievable: the probes over the same buffers and rotation
+    timer = Timer(torch, stream)
+    npieces = n * 2 // 16
+    pf = [probe.call(PROBE_FWD, wk["xs"][s], wk["ys"][s], wk["ms"][s], npieces, 64, stream)
+          for s in range(args.sets)]
+    pc = [probe.call(PROBE_COPY, wk["xs"][s], wk["ys"][s], None, npieces, 64, stream)
+          for s in range(args.sets)]
+    reps = max(K, 100)
+    t_pf, t_pc = timer(pf, reps=reps), timer(pc, reps=reps)
+    t_fwd = timer(fwd, reps=reps)
+    result["achievable"] = {
+        "what": "streaming probes over the same 8 rotating buffer sets, one 16-byte piece per lane "
+                "in 64-lane workgroups like the forward, no arithmetic; median of 3 trials",
+        "fwd_pattern": entry("read 16 B + write 16 B + 1 B per piece (the forward's bytes and "
+                             "pattern)", "probe_kernel<fwd>", fwd_bytes, n, t_pf),
+        "copy": entry("read 16 B + write 16 B per piece", "probe_kernel<copy>", n * 4, n, t_pc),
+        "forward_same_trials": entry("the forward kernel, timed the same way", KERNELS["fwd"],
+                                     fwd_bytes, n, t_fwd),
+        "forward_over_probe_time": round(t_fwd[0] / t_pf[0], 4),
+    }
+    return result, wk
 
 
-def steady_state(M, lib, W, torch, stream, rows=28672, cols=8192, sets=2, reps=20, warm=60):
+def steady_state(M, lib, W, torch, stream, probe, rows=28672, cols=8192, sets=2, reps=20, warm=60):
     """Forward (y + bitmap), clipped-STE backward and the step at 28672x8192
     on the weight_4k distribution (seed 2); the upstream gradient is N(0, 1)
     drawn on the device (seed 2).  Back-to-back launches over rotating buffer
@@ -314,7 +458,7 @@ def steady_state(M, lib, W, torch, stream, rows=28672, cols=8192, sets=2, reps=2
     x_np, _, _ = W.weight_4k(rows=rows, cols=cols, with_grad=False)
     n = rows * cols
     per = n * (2 + 2 + 1 / 8)
-    x0 = torch.from_numpy(x_np).view(torch.bfloat16).cuda()
+    x0 = bf16_dev(torch, x_np)
     del x_np
     gen = torch.Generator(device="cuda").manual_seed(2)
     g0 = torch.randn((rows, cols), generator=gen, device="cuda").to(torch.bfloat16)
@@ -329,6 +473,7 @@ def steady_state(M, lib, W, torch, stream, rows=28672, cols=8192, sets=2, reps=2
                 vp(ms[s].data_ptr()), None, None, None, None, stream) for s in range(sets)]
     bwd = [Call(lib.mxfp4_ste_bwd, ctypes.byref(desc), M.ROW, vp(gs[s].data_ptr()), vp(ms[s].data_ptr()),
                 vp(gis[s].data_ptr()), None, 0, 1, stream) for s in range(sets)]
+    pf = [probe.call(PROBE_FWD, xs[s], ys[s], ms[s], n * 2 // 16, 64, stream) for s in range(sets)]
     # Freshly allocated buffers and an idle GPU run the first few dozen
     # launches measurably slower (measured: ~8 % for the first 40); warm up
     # past that, then take the median of three timed trials.
@@ -351,179 +496,203 @@ def steady_state(M, lib, W, torch, stream, rows=28672, cols=8192, sets=2, reps=2
             t.append(hev.ms(0, 1) / reps * 1e3)
         return sorted(t)[1]
 
-    f_us, b_us, s_us = trial([fwd]), trial([bwd]), trial([fwd, bwd])
+    f_us, b_us, s_us, p_us = trial([fwd]), trial([bwd]), trial([fwd, bwd]), trial([pf])
     hev.close()
     del xs, gs, ys, gis, ms, x0, g0
     torch.cuda.empty_cache()
-    gbs = lambda nbytes, us: nbytes / us / 1e3
+    g = lambda nbytes, us: nbytes / us / 1e3
     return {"workload": f"weight_4k distribution at {rows}x{cols}: row-wise block-32 QDQ fwd "
                         "(y + clip bitmap) + clipped-STE bwd",
             "fwd_us": round(f_us, 2), "bwd_us": round(b_us, 2), "step_us": round(s_us, 2),
-            "fwd_GBps": round(gbs(per, f_us), 1), "bwd_GBps": round(gbs(per, b_us), 1),
-            "step_GBps": round(gbs(2 * per, s_us), 1),
-            "fwd_frac": round(gbs(per, f_us) / HBM_PEAK_GBS, 4),
-            "step_frac": round(gbs(2 * per, s_us) / HBM_PEAK_GBS, 4)}
+            "fwd_GBps": round(g(per, f_us), 1), "bwd_GBps": round(g(per, b_us), 1),
+            "step_GBps": round(g(2 * per, s_us), 1),
+            "fwd_frac": round(g(per, f_us) / HBM_PEAK_GBS, 4),
+            "step_frac": round(g(2 * per, s_us) / HBM_PEAK_GBS, 4),
+            "probe_fwd_pattern_us": round(p_us, 2), "probe_fwd_pattern_GBps": round(g(per, p_us), 1),
+            "forward_over_probe_time": round(f_us / p_us, 4)}
 
 
-def _time_calls(torch, calls, reps, warm=20, trials=3):
-    """Per-launch time of back-to-back launches (rotating over `calls`): three
-    trials of `reps` launches between two events on the current stream;
-    returns (median, best) of the trials' per-launch averages, in seconds.
-    Events around every launch would add their own overhead and gaps."""
-    for i in range(warm):
-        calls[i % len(calls)]()
-    torch.cuda.synchronize()
-    t = []
-    for _ in range(trials):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for i in range(reps):
-            calls[i % len(calls)]()
-        b.record()
-        torch.cuda.synchronize()
-        t.append(a.elapsed_time(b) * 1e-3 / reps)
-    t = np.array(t)
-    return float(np.median(t)), float(t.min())
+# ---------------------------------------------------------------- configs
 
-
-def bench_all(M, lib, W, torch, args):
-    """Full-size runs of the other workloads (two buffer sets each, so
-    consecutive launches do not hit the same data) and a device copy."""
-    vp = ctypes.c_void_p
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+def bench_configs(M, lib, W, torch, stream, cpu, cpu_seconds):
+    """Every other workload at full size: GPU time of back-to-back launches
+    over two buffer sets, and the oracle on a bounded sample of the same
+    input."""
+    import oracle
+    timer = Timer(torch, stream)
     out = {}
 
-    def rec(name, nbytes, nelem, t):
-        med, best = t
-        out[name] = {"alg_bytes": nbytes, "median_us": round(med * 1e6, 2), "best_us": round(best * 1e6, 2),
-                     "GBps": round(nbytes / med / 1e9, 1), "pct_peak": round(100 * nbytes / med / 1e9 / HBM_PEAK_GBS, 2),
-                     "elements_per_s": round(nelem / med, 1)}
+    # c1: the tiny QAT check (fp32 W 32x64 and X 4x64): forward y + bitmap of
+    # both, then the clipped STE of an all-ones gradient for both; four
+    # launches, launch-bound, so reported as latency
+    tq = build_tiny(M, lib, W, torch, stream)
+    med, best = timer([tq["step"]], reps=200)
+    c1 = {"workload": "tiny QAT: fp32 W 32x64 + X 4x64, row-wise block-32 QDQ (y + bitmap) then "
+                      "clipped STE of ones, four launches",
+          "kernels": [KERNELS["fwd"].replace("bf16", "f32"), KERNELS["bwd"].replace("bf16", "f32")],
+          "step_us": round(med * 1e6, 2), "best_step_us": round(best * 1e6, 2),
+          "per_launch_us": round(med * 1e6 / 4, 2), "bound": "launch latency",
+          "higher_is_better": False, "unit": "us per step"}
+    if cpu:
+        tw, tx = tq["tw"], tq["tx"]
 
-    # plain device copy of 512 MiB (achievable-bandwidth context)
+        def tiny_oracle():
+            for a in (tw, tx):
+                _, clip, _ = oracle.qdq_rows(a, 32)
+                oracle.ste_bwd(np.ones_like(a), clip)
+        dt, reps = repeat_for(tiny_oracle, min(cpu_seconds, 2.0))
+        c1["cpu_baseline"] = {"value": round(dt * 1e6, 2), "unit": "us per step", "cores": 1,
+                              "kind": "oracle", "higher_is_better": False,
+                              "sample": f"the whole workload, {reps} reps (ctypes calls included)",
+                              "host": host_cpu()}
+    out["c1_tiny_qat"] = c1
+    del tq
+
+    # c3: dual direction, 16384 x 8192 Student-t activation
+    dual = build_dual(M, lib, W, torch, stream)
+    R, C = dual["R"], dual["C"]
+    e = entry(f"act_dual: bf16 {R}x{C} Student-t(3)*0.5, one dual-direction launch: y_row + y_col + "
+              "both bitmaps", KERNELS["dual"], R * C * 6.25, R * C, timer(dual["calls"]))
+    if cpu:
+        xs = dual["x_np"][:1024]
+        e["cpu_baseline"] = oracle_baseline(lambda: (oracle.qdq_rows(xs, 32), oracle.qdq_cols(xs, 32)),
+                                            xs.size * 6.25, xs.size,
+                                            f"rows 0-1023 of the same tensor ({xs.shape[0]}x{xs.shape[1]}), "
+                                            "row-wise and column-wise QDQ with masks", cpu_seconds)
+    out["c3_act_dual"] = e
+    del dual
+    torch.cuda.empty_cache()
+
+    # c4: grouped column-wise, 32768 x 7168 tokens in 8 expert groups
+    grp = build_grouped(M, lib, W, torch, stream)
+    R, C = grp["R"], grp["C"]
+    e = entry(f"moe_grouped: bf16 {R}x{C} N(0,1), 8 multinomial groups, grouped column-wise "
+              "block-32 QDQ (y)", KERNELS["grouped"], R * C * 4.0, R * C, timer(grp["calls"]))
+    grm = build_grouped(M, lib, W, torch, stream, with_mask=True)
+    t_m = timer(grm["calls"])
+    e["with_grouped_bitmap"] = entry("the same, y + GROUPED bitmap", KERNELS["grouped"], R * C * 4.125,
+                                     R * C, t_m)
+    if cpu:
+        xs = np.ascontiguousarray(grp["x_np"][:, :256])
+        counts = grp["counts"]
+        e["cpu_baseline"] = oracle_baseline(lambda: oracle.grouped_cols(xs, counts, 32), xs.size * 4.0,
+                                            xs.size, f"columns 0-255 of the same tensor, all {R} rows and "
+                                            "the same 8 groups", cpu_seconds)
+    out["c4_moe_grouped"] = e
+    del grp, grm
+    torch.cuda.empty_cache()
+
+    # c5: row-wise packing of the 28672 x 8192 weight at blocks 32 and 128
+    xw = None
+    for blk in (32, 128):
+        pk = build_pack(M, lib, W, torch, stream, blk, x_np=xw)
+        xw = pk["x_np"]
+        R, C = pk["R"], pk["C"]
+        e = entry(f"weight_pack: bf16 {R}x{C} N(0,0.02^2) + outliers, row-wise block-{blk} packed codes "
+                  "+ E8M0 bytes", KERNELS[f"pack{blk}"], R * C * (2 + 0.5 + 1 / blk), R * C,
+                  timer(pk["calls"]))
+        if cpu:
+            xs = xw[:1024]
+            e["cpu_baseline"] = oracle_baseline(lambda: oracle.pack_rows(xs, blk), xs.size * (2.5 + 1 / blk),
+                                                xs.size, f"rows 0-1023 of the same tensor, block {blk}",
+                                                cpu_seconds)
+        out[f"c5_weight_pack_b{blk}"] = e
+        del pk
+        torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------- extras (--all)
+
+def bench_all(M, lib, W, torch, stream):
+    """The f-rows at full size (K-major packs, decode, MXFP8, column-only)
+    and a device copy, two buffer sets each."""
+    vp = ctypes.c_void_p
+    timer = Timer(torch, stream)
+    out = {}
+
     a = [torch.empty(256 << 20, dtype=torch.int16, device="cuda") for _ in range(2)]
     b = [torch.empty_like(a[0]) for _ in range(2)]
-    rec("device_copy_512MiB", 2 * a[0].numel() * 2, a[0].numel(),
-        _time_calls(torch, [lambda i=i: b[i].copy_(a[i]) for i in range(2)], 20))
+    out["device_copy_512MiB"] = entry("torch copy_ of 512 MiB", "torch copy", 2 * a[0].numel() * 2,
+                                      a[0].numel(), timer([lambda i=i: b[i].copy_(a[i]) for i in range(2)],
+                                                          reps=20))
     del a, b
 
-    def tens(np_arr):
-        return torch.from_numpy(np_arr).view(torch.bfloat16).cuda()
-
-    # row-wise fwd at the large weight shape (28672 x 8192)
     xw = W.weight_pack()
     R, C = xw.shape
-    xs = [tens(xw) for _ in range(2)]
+    xs = [bf16_dev(torch, xw) for _ in range(2)]
     ys = [torch.empty_like(xs[0]) for _ in range(2)]
     mk = [torch.empty((R, C // 32), dtype=torch.int32, device="cuda") for _ in range(2)]
     d = M._Desc(1, 32, 0, 0, R, C, 6.0, 0)
-    calls = [Call(lib.mxfp4_qdq_fwd, ctypes.byref(d), M.ROW, vp(xs[i].data_ptr()), vp(ys[i].data_ptr()),
-                  vp(mk[i].data_ptr()), None, None, None, None, stream) for i in range(2)]
-    rec("row_fwd_28672x8192_y_mask", R * C * 4.125, R * C, _time_calls(torch, calls, 30))
-    gis = ys
     bcalls = [Call(lib.mxfp4_ste_bwd, ctypes.byref(d), M.ROW, vp(xs[i].data_ptr()), vp(mk[i].data_ptr()),
-                   vp(gis[i].data_ptr()), None, 0, 1, stream) for i in range(2)]
-    rec("ste_bwd_28672x8192", R * C * 4.125, R * C, _time_calls(torch, bcalls, 30))
-    # packed output, block 32 and 128
+                   vp(ys[i].data_ptr()), None, 0, 1, stream) for i in range(2)]
+    out["ste_bwd_28672x8192"] = entry("clipped STE, bf16 28672x8192", KERNELS["bwd"], R * C * 4.125, R * C,
+                                      timer(bcalls))
     for blk in (32, 128):
-        codes = [torch.empty((R, C // 2), dtype=torch.uint8, device="cuda") for _ in range(2)]
-        scs = [torch.empty((R, C // blk), dtype=torch.uint8, device="cuda") for _ in range(2)]
         dp = M._Desc(1, blk, 0, 0, R, C, 6.0, 0)
-        pcalls = [Call(lib.mxfp4_quant_pack, ctypes.byref(dp), vp(xs[i].data_ptr()), vp(codes[i].data_ptr()),
-                       vp(scs[i].data_ptr()), None, None, stream) for i in range(2)]
-        rec(f"pack_28672x8192_b{blk}", R * C * (2 + 0.5 + 1 / blk), R * C, _time_calls(torch, pcalls, 30))
-        # K-major packed operand of the same weight (blocks along its 28672 rows)
         kb = R // blk
         kc = [torch.empty((C, kb * blk // 2), dtype=torch.uint8, device="cuda") for _ in range(2)]
         ks = [torch.empty((C, kb), dtype=torch.uint8, device="cuda") for _ in range(2)]
         kcalls = [Call(lib.mxfp4_quant_pack_kmajor, ctypes.byref(dp), vp(xs[i].data_ptr()), None, 0, 1, kb,
                        vp(kc[i].data_ptr()), vp(ks[i].data_ptr()), stream) for i in range(2)]
-        rec(f"kmajor_28672x8192_b{blk}", R * C * (2 + 0.5 + 1 / blk), R * C, _time_calls(torch, kcalls, 30))
-        del kc, ks
-        # decode of the row-wise packed form back to bf16
+        out[f"kmajor_28672x8192_b{blk}"] = entry(f"K-major pack of the weight, block {blk}", "kmajor_pack_kernel",
+                                                 R * C * (2 + 0.5 + 1 / blk), R * C, timer(kcalls))
+        codes = [torch.empty((R, C // 2), dtype=torch.uint8, device="cuda") for _ in range(2)]
+        scs = [torch.empty((R, C // blk), dtype=torch.uint8, device="cuda") for _ in range(2)]
+        for i in range(2):
+            M.mxfp4_quant_pack(xs[i], codes[i], scs[i], block=blk)
         dcalls = [Call(lib.mxfp4_dequant, ctypes.byref(dp), vp(codes[i].data_ptr()), vp(scs[i].data_ptr()),
                        vp(ys[i].data_ptr()), stream) for i in range(2)]
-        rec(f"dequant_28672x8192_b{blk}", R * C * (0.5 + 1 / blk + 2), R * C, _time_calls(torch, dcalls, 30))
-        del codes, scs
+        out[f"dequant_28672x8192_b{blk}"] = entry(f"decode of the row-wise packed weight, block {blk}",
+                                                  "dequant_flat_kernel", R * C * (0.5 + 1 / blk + 2), R * C,
+                                                  timer(dcalls))
+        del kc, ks, codes, scs
     del xs, ys, mk
+    torch.cuda.empty_cache()
 
-    # dual direction (16384 x 8192)
     xa = W.act_dual()
     R, C = xa.shape
-    xs = [tens(xa) for _ in range(2)]
-    yr = [torch.empty_like(xs[0]) for _ in range(2)]
+    xs = [bf16_dev(torch, xa) for _ in range(2)]
     yc = [torch.empty_like(xs[0]) for _ in range(2)]
-    mr = [torch.empty((R, C // 32), dtype=torch.int32, device="cuda") for _ in range(2)]
     mc = [torch.empty((R // 32, C), dtype=torch.int32, device="cuda") for _ in range(2)]
     d = M._Desc(1, 32, 0, 0, R, C, 6.0, 0)
-    calls = [Call(lib.mxfp4_qdq_fwd, ctypes.byref(d), M.ROW | M.COL, vp(xs[i].data_ptr()), vp(yr[i].data_ptr()),
-                  vp(mr[i].data_ptr()), None, vp(yc[i].data_ptr()), vp(mc[i].data_ptr()), None, stream)
-             for i in range(2)]
-    rec("dual_16384x8192", R * C * 6.25, R * C, _time_calls(torch, calls, 30))
     ccalls = [Call(lib.mxfp4_qdq_fwd, ctypes.byref(d), M.COL, vp(xs[i].data_ptr()), None, None, None,
                    vp(yc[i].data_ptr()), vp(mc[i].data_ptr()), None, stream) for i in range(2)]
-    rec("col_16384x8192_y_mask", R * C * 4.125, R * C, _time_calls(torch, ccalls, 30))
-    del xs, yr, yc, mr, mc
+    out["col_16384x8192_y_mask"] = entry("column-wise y + bitmap, bf16 16384x8192", "col_fwd_kernel<col>",
+                                         R * C * 4.125, R * C, timer(ccalls))
+    del xs, yc, mc
+    torch.cuda.empty_cache()
 
-    # grouped (32768 x 7168, 8 groups)
     xg, counts = W.moe_grouped()
     R, C = xg.shape
-    xs = [tens(xg) for _ in range(2)]
-    ys = [torch.empty_like(xs[0]) for _ in range(2)]
+    xs = [bf16_dev(torch, xg) for _ in range(2)]
     gl = torch.from_numpy(counts).cuda()
     d = M._Desc(1, 32, 0, 0, R, C, 6.0, 0)
-    calls = [Call(lib.mxfp4_grouped_qdq, ctypes.byref(d), vp(xs[i].data_ptr()), vp(gl.data_ptr()), 8, 1,
-                  vp(ys[i].data_ptr()), None, None, stream) for i in range(2)]
-    rec("grouped_32768x7168_y", R * C * 4.0, R * C, _time_calls(torch, calls, 30))
-    del ys
-    # grouped K-major packed operand (block-rows padded per group)
     nbt = int(sum(-(-int(c) // 32) for c in counts))
     kb = M.kmajor_k_blocks(R, 32, len(counts))
     kc = [torch.empty((C, kb * 16), dtype=torch.uint8, device="cuda") for _ in range(2)]
     ks = [torch.empty((C, kb), dtype=torch.uint8, device="cuda") for _ in range(2)]
     kcalls = [Call(lib.mxfp4_quant_pack_kmajor, ctypes.byref(d), vp(xs[i].data_ptr()), vp(gl.data_ptr()), 8, 1,
                    kb, vp(kc[i].data_ptr()), vp(ks[i].data_ptr()), stream) for i in range(2)]
-    rec("kmajor_grouped_32768x7168", R * C * 2 + C * nbt * (16 + 1), R * C, _time_calls(torch, kcalls, 30))
+    out["kmajor_grouped_32768x7168"] = entry("grouped K-major pack of the MoE tokens", "kmajor_pack_kernel",
+                                             R * C * 2 + C * nbt * (16 + 1), R * C, timer(kcalls))
     del kc, ks
-    # MXFP8 (E4M3) of a grad_output of the same shape
     q8 = [torch.empty((R, C), dtype=torch.uint8, device="cuda") for _ in range(2)]
     s8 = [torch.empty((R, C // 32), dtype=torch.uint8, device="cuda") for _ in range(2)]
     mcalls = [Call(lib.mxfp8_quant, ctypes.byref(d), 0, vp(xs[i].data_ptr()), vp(q8[i].data_ptr()),
                    vp(s8[i].data_ptr()), stream) for i in range(2)]
-    rec("mxfp8_e4m3_32768x7168", R * C * (2 + 1 + 1 / 32), R * C, _time_calls(torch, mcalls, 30))
+    out["mxfp8_e4m3_32768x7168"] = entry("row-wise MXFP8 E4M3 of the tokens", "mxfp8_rows_kernel",
+                                         R * C * (2 + 1 + 1 / 32), R * C, timer(mcalls))
     del q8, s8
-    # K-major grouped MXFP8 of the same tokens (the TN operand; block-rows
-    # padded per group)
     kb8 = M.mxfp8_kmajor_k_blocks(R, len(counts))
     k8 = [torch.empty((C, kb8 * 32), dtype=torch.uint8, device="cuda") for _ in range(2)]
     t8 = [torch.empty((C, kb8), dtype=torch.uint8, device="cuda") for _ in range(2)]
-    k8calls = [Call(lib.mxfp8_quant_kmajor, ctypes.byref(d), 0, vp(xs[i].data_ptr()), vp(gl.data_ptr()), 8, 1, kb8,
-                    vp(k8[i].data_ptr()), vp(t8[i].data_ptr()), stream) for i in range(2)]
-    rec("mxfp8_kmajor_grouped_32768x7168", R * C * 2 + C * nbt * (32 + 1), R * C, _time_calls(torch, k8calls, 30))
+    k8calls = [Call(lib.mxfp8_quant_kmajor, ctypes.byref(d), 0, vp(xs[i].data_ptr()), vp(gl.data_ptr()), 8, 1,
+                    kb8, vp(k8[i].data_ptr()), vp(t8[i].data_ptr()), stream) for i in range(2)]
+    out["mxfp8_kmajor_grouped_32768x7168"] = entry("grouped K-major MXFP8 of the tokens", "mxfp8_kmajor_kernel",
+                                                   R * C * 2 + C * nbt * (32 + 1), R * C, timer(k8calls))
     del xs, k8, t8
-
-    # the PR's minimal QAT check at its own size: fp32 weight 32x64 and input
-    # 4x64, row-wise block-32 forward (y + bitmap) of both, then the clipped
-    # STE of an all-ones gradient for both; launch-bound, so reported as
-    # latency (four launches per step), not as a fraction of peak
-    tw, tx = W.tiny_qat(0)
-    tcalls = []
-    for arr in (tw, tx):
-        r, c = arr.shape
-        xt = torch.from_numpy(arr).cuda()
-        yt, gt, gi = torch.empty_like(xt), torch.ones_like(xt), torch.empty_like(xt)
-        mt = torch.empty((r, -(-c // 32)), dtype=torch.int32, device="cuda")
-        dt = M._Desc(0, 32, 0, 0, r, c, 6.0, 0)
-        keep = (xt, yt, gt, gi, mt, dt)
-        tcalls.append((Call(lib.mxfp4_qdq_fwd, ctypes.byref(dt), M.ROW, vp(xt.data_ptr()), vp(yt.data_ptr()),
-                            vp(mt.data_ptr()), None, None, None, None, stream),
-                       Call(lib.mxfp4_ste_bwd, ctypes.byref(dt), M.ROW, vp(gt.data_ptr()), vp(mt.data_ptr()),
-                            vp(gi.data_ptr()), None, 0, 1, stream), keep))
-    step = [lambda: (tcalls[0][0](), tcalls[1][0](), tcalls[0][1](), tcalls[1][1]())]
-    med, best = _time_calls(torch, step, 200)
-    out["tiny_qat_w32x64_x4x64_fp32"] = {"step_us": round(med * 1e6, 2), "best_step_us": round(best * 1e6, 2),
-                                         "launches_per_step": 4, "per_launch_us": round(med * 1e6 / 4, 2),
-                                         "bound": "launch latency"}
-
+    torch.cuda.empty_cache()
     bench_gemm(M, W, torch, out, gl, counts)
     return out
 
@@ -537,16 +706,15 @@ def bench_gemm(M, W, torch, out, gl=None, counts=None):
         gl = torch.from_numpy(counts).cuda()
     else:
         xg = W.moe_grouped()[0]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    timer = Timer(torch, stream)
     R, C = xg.shape
-    x = torch.from_numpy(xg).view(torch.bfloat16).cuda()
+    x = bf16_dev(torch, xg)
     q8 = [torch.empty((R, C), dtype=torch.uint8, device="cuda") for _ in range(2)]
     s8 = [torch.empty((R, C // 32), dtype=torch.uint8, device="cuda") for _ in range(2)]
     for i in range(2):
         M.mxfp8_quant(x, q8[i], s8[i])
     del x
-
-    def tens(np_arr):
-        return torch.from_numpy(np_arr).view(torch.bfloat16).cuda()
 
     def rec_mm(name, flops, t):
         med, best = t
@@ -560,11 +728,11 @@ def bench_gemm(M, W, torch, out, gl=None, counts=None):
     bw = torch.empty((G, N, kbw * 16), dtype=torch.uint8, device="cuda")
     sw = torch.empty((G, N, kbw), dtype=torch.uint8, device="cuda")
     for i in range(G):
-        M.mxfp4_quant_pack_kmajor(tens(wt[i]), bw[i], sw[i], block=32)
+        M.mxfp4_quant_pack_kmajor(bf16_dev(torch, wt[i]), bw[i], sw[i], block=32)
     cs = [torch.empty((R, N), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
     gmm = [lambda i=i: M.mxfp4_grouped_matmul(q8[i], s8[i], bw, sw, cs[i], group_list=gl, group_list_type=1)
            for i in range(2)]
-    rec_mm("gmm_nn_moe_32768x7168x2048_fp8xfp4", 2.0 * R * K * N, _time_calls(torch, gmm, 20))
+    rec_mm("gmm_nn_moe_32768x7168x2048_fp8xfp4", 2.0 * R * K * N, timer(gmm, reps=20))
     # NT: grad_output [32768, 2048] (MXFP8) x row-wise MXFP4 weights [7168, 2048] -> dX [32768, 7168]
     gen = torch.Generator(device="cuda").manual_seed(7)
     dq = torch.randint(0, 256, (R, N), dtype=torch.uint8, device="cuda", generator=gen) & 0xBF  # finite codes
@@ -575,7 +743,7 @@ def bench_gemm(M, W, torch, out, gl=None, counts=None):
     cx = [torch.empty((R, K), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
     gmm = [lambda i=i: M.mxfp4_grouped_matmul(dq, ds, bt, st, cx[i], group_list=gl, group_list_type=1)
            for i in range(2)]
-    rec_mm("gmm_nt_moe_32768x2048x7168_fp8xfp4", 2.0 * R * K * N, _time_calls(torch, gmm, 20))
+    rec_mm("gmm_nt_moe_32768x2048x7168_fp8xfp4", 2.0 * R * K * N, timer(gmm, reps=20))
     del cx, bt, st
     # TN: per expert x_g^T [7168, tokens_g] x dy_g [tokens_g, 2048], both MXFP8 K-major
     nbt8 = int(sum(-(-int(c) // 32) for c in counts))
@@ -587,9 +755,453 @@ def bench_gemm(M, W, torch, out, gl=None, counts=None):
     gmm = [lambda i=i: M.mxfp4_grouped_matmul(xa, xs_, yb, ys_, cw[i], K=R, group_list=gl, group_list_type=1,
                                               group_type=M.GROUP_K, b_fmt="e4m3", k_blocks=nbt8)
            for i in range(2)]
-    rec_mm("gmm_tn_moe_7168x2048_over_32768_fp8xfp8", 2.0 * R * K * N, _time_calls(torch, gmm, 20))
+    rec_mm("gmm_tn_moe_7168x2048_over_32768_fp8xfp8", 2.0 * R * K * N, timer(gmm, reps=20))
     del q8, s8, cw, xa, yb
     return out
+
+
+# ---------------------------------------------------------------- profiling support
+
+PROFILE_LAUNCHES = 10
+PROFILE_WARMUP = 40
+
+
+def profile_run(M, lib, W, torch, stream, probe, manifest_path):
+    """A fixed sequence of launches for rocprofv3: for every workload
+    PROFILE_WARMUP launches (freshly allocated buffers run the first few
+    dozen launches slower), then PROFILE_LAUNCHES measured ones, in the order
+    written to the manifest (label, kernel name fragment, launches,
+    algorithmic bytes per launch), so that the summary can name the workload
+    of every dispatch and leave the warm-up out."""
+    entries = []
+    vp = ctypes.c_void_p
+
+    def run(label, frag, calls, rd, wr, nelem, per_call=1):
+        for phase, n in (("warm-up", PROFILE_WARMUP), ("measured", PROFILE_LAUNCHES)):
+            torch.cuda.synchronize()
+            for i in range(n):
+                calls[i % len(calls)]()
+            torch.cuda.synchronize()
+            entries.append({"label": label, "kernel": frag, "launches": n * per_call, "alg_bytes": rd + wr,
+                            "alg_read": rd, "alg_write": wr, "elements": nelem, "skip": phase == "warm-up",
+                            "kernels_per_call": per_call})
+
+    # calibration of the traffic counters: a plain copy of 512 MiB
+    ca = [torch.empty(256 << 20, dtype=torch.int16, device="cuda") for _ in range(2)]
+    cb = [torch.empty_like(ca[0]) for _ in range(2)]
+    cn = ca[0].numel() * 2
+    run("calibration: probe copy of 512 MiB", "probe_kernel",
+        [probe.call(PROBE_COPY, ca[i], cb[i], None, cn // 16, 256, stream) for i in range(2)], cn, cn, cn // 2)
+    del ca, cb
+    torch.cuda.empty_cache()
+    wk = build_weight4k(M, lib, W, torch, stream, 8)
+    n = wk["rows"] * wk["cols"]
+    run("weight_4k forward (y + bitmap)", "row_fwd_kernel", wk["fwd"], n * 2, n * 2.125, n)
+    run("weight_4k clipped STE", "ste_row_kernel", wk["bwd"], n * 2.125, n * 2, n)
+    pf = [probe.call(PROBE_FWD, wk["xs"][s], wk["ys"][s], wk["ms"][s], n * 2 // 16, 64, stream) for s in range(8)]
+    run("probe: the forward's bytes and pattern, 4096x4096", "probe_kernel", pf, n * 2, n * 2.125, n)
+    del wk, pf
+    tq = build_tiny(M, lib, W, torch, stream)
+    run("tiny QAT step (fwd W, fwd X, STE W, STE X)", "mxfp4", [tq["step"]], 0, 0, 0, per_call=4)
+    del tq
+    dual = build_dual(M, lib, W, torch, stream)
+    n = dual["R"] * dual["C"]
+    run("act_dual dual direction", "col_fwd_kernel", dual["calls"], n * 2, n * 4.25, n)
+    del dual
+    torch.cuda.empty_cache()
+    grp = build_grouped(M, lib, W, torch, stream)
+    n = grp["R"] * grp["C"]
+    R, C, counts = grp["R"], grp["C"], grp["counts"]
+    run("moe_grouped grouped column-wise (y)", "col_fwd_kernel", grp["calls"], n * 2, n * 2, n)
+    xs, gl = grp["bufs"][0], grp["bufs"][3]
+    d = M._Desc(1, 32, 0, 0, R, C, 6.0, 0)
+    nbt = int(sum(-(-int(c) // 32) for c in counts))
+    kb = M.kmajor_k_blocks(R, 32, len(counts))
+    kc = [torch.empty((C, kb * 16), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ks = [torch.empty((C, kb), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    run("moe_grouped K-major pack (grouped, block 32)", "kmajor_pack_kernel",
+        [Call(lib.mxfp4_quant_pack_kmajor, ctypes.byref(d), vp(xs[i].data_ptr()), vp(gl.data_ptr()), len(counts), 1,
+              kb, vp(kc[i].data_ptr()), vp(ks[i].data_ptr()), stream, keep=d) for i in range(2)],
+        R * C * 2, C * nbt * (16 + 1), n)
+    del kc, ks
+    q8 = [torch.empty((R, C), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    s8 = [torch.empty((R, C // 32), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    run("moe tokens row-wise MXFP8 E4M3", "mxfp8_rows_kernel",
+        [Call(lib.mxfp8_quant, ctypes.byref(d), 0, vp(xs[i].data_ptr()), vp(q8[i].data_ptr()), vp(s8[i].data_ptr()),
+              stream, keep=d) for i in range(2)], R * C * 2, R * C * (1 + 1 / 32), n)
+    del q8, s8
+    kb8 = M.mxfp8_kmajor_k_blocks(R, len(counts))
+    k8 = [torch.empty((C, kb8 * 32), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    t8 = [torch.empty((C, kb8), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    run("moe tokens grouped K-major MXFP8 E4M3", "mxfp8_kmajor_kernel",
+        [Call(lib.mxfp8_quant_kmajor, ctypes.byref(d), 0, vp(xs[i].data_ptr()), vp(gl.data_ptr()), len(counts), 1,
+              kb8, vp(k8[i].data_ptr()), vp(t8[i].data_ptr()), stream, keep=d) for i in range(2)],
+        R * C * 2, C * nbt * (32 + 1), n)
+    del grp, xs, k8, t8
+    torch.cuda.empty_cache()
+    xw = None
+    for blk in (32, 128):
+        pk = build_pack(M, lib, W, torch, stream, blk, x_np=xw)
+        xw = pk["x_np"]
+        R, C = pk["R"], pk["C"]
+        n = R * C
+        run(f"weight_pack row-wise pack block {blk}", "row_fwd_kernel", pk["calls"], n * 2, n * (0.5 + 1 / blk), n)
+        xs, codes, scs = pk["bufs"]
+        dp = M._Desc(1, blk, 0, 0, R, C, 6.0, 0)
+        ys = [torch.empty_like(xs[0]) for _ in range(2)]
+        run(f"weight_pack decode block {blk}", "dequant_flat_kernel",
+            [Call(lib.mxfp4_dequant, ctypes.byref(dp), vp(codes[i].data_ptr()), vp(scs[i].data_ptr()),
+                  vp(ys[i].data_ptr()), stream, keep=dp) for i in range(2)], n * (0.5 + 1 / blk), n * 2, n)
+        del ys
+        kb = M.kmajor_k_blocks(R, blk)
+        kc = [torch.empty((C, kb * blk // 2), dtype=torch.uint8, device="cuda") for _ in range(2)]
+        ks = [torch.empty((C, kb), dtype=torch.uint8, device="cuda") for _ in range(2)]
+        run(f"weight_pack K-major pack block {blk}", "kmajor_pack_kernel",
+            [Call(lib.mxfp4_quant_pack_kmajor, ctypes.byref(dp), vp(xs[i].data_ptr()), None, 0, 1, kb,
+                  vp(kc[i].data_ptr()), vp(ks[i].data_ptr()), stream, keep=dp) for i in range(2)],
+            n * 2, n * (0.5 + 1 / blk), n)
+        del pk, xs, codes, scs, kc, ks
+        torch.cuda.empty_cache()
+    with open(manifest_path, "w") as f:
+        json.dump({"launches_per_workload": PROFILE_LAUNCHES, "warmup_per_workload": PROFILE_WARMUP,
+                   "entries": entries}, f, indent=1)
+    print(json.dumps({"profile_run": manifest_path, "workloads": len(entries) // 2}), flush=True)
+
+
+def _read_csv(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath, suffix):
+    hits = sorted(glob.glob(os.path.join(dirpath, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {dirpath}")
+    return hits[-1]
+
+
+def _ours(name):
+    return "mxfp4::" in name or "probe_kernel" in name
+
+
+def summarize(kind, dirpath, manifest_path, out_md, command):
+    """Join rocprofv3 CSV output with the profile-run manifest.  kind 'trace':
+    the kernel trace under dirpath; kind 'pmc': counter collections under one
+    or more comma-separated dirs (one rocprofv3 --pmc run each, merged by
+    dispatch order).  This library's dispatches, in dispatch order, are
+    assigned to the manifest's workloads by their launch counts (warm-up
+    launches are left out of the table).  The trace table lists per workload
+    the kernel, the average duration and GB/s / fraction of peak; the counter
+    table lists the counters per dispatch, and with FETCH_SIZE and WRITE_SIZE
+    the HBM bytes scaled by the calibration copy (its measured read / write
+    bytes over its counters) next to the algorithmic bytes.  A JSON file with
+    the same numbers is written beside OUT_MD."""
+    with open(manifest_path) as f:
+        man = json.load(f)["entries"]
+    need = sum(e["launches"] for e in man)
+    if kind == "trace":
+        rows = _read_csv(_find(dirpath, "kernel_trace.csv"))
+        rows = [r for r in rows if _ours(r["Kernel_Name"])]
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        disp = [(r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), {}) for r in rows]
+    else:
+        disp = None
+        for d in dirpath.split(","):
+            by = {}
+            for r in _read_csv(_find(d, "counter_collection.csv")):
+                if not _ours(r["Kernel_Name"]):
+                    continue
+                e = by.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0, {}])
+                e[2][r["Counter_Name"]] = e[2].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            cur = [tuple(by[k]) for k in sorted(by)]
+            if len(cur) != need:
+                raise SystemExit(f"{len(cur)} library dispatches under {d}, the manifest lists {need}")
+            if disp is None:
+                disp = cur
+            else:
+                for a, b in zip(disp, cur):
+                    if a[0] != b[0]:
+                        raise SystemExit("dispatch order differs between the counter runs")
+                    a[2].update(b[2])
+    if len(disp) != need:
+        raise SystemExit(f"{len(disp)} library dispatches in the profile, the manifest lists {need}")
+    # per workload: the measured dispatches
+    pos, groups = 0, []
+    for e in man:
+        chunk = disp[pos:pos + e["launches"]]
+        pos += e["launches"]
+        for c in chunk:
+            if e["kernel"] not in c[0]:
+                raise SystemExit(f"dispatch {c[0]} does not match workload {e['label']}")
+        if not e.get("skip"):
+            groups.append((e, chunk))
+    what = {"trace": "kernel trace (durations)", "pmc": "counter collection"}[kind]
+    lines = [f"# rocprofv3 {what}: the bench.py profile run", "",
+             "MI355X, ROCm 7.2.  Every workload at full size, one kernel per row: "
+             f"{PROFILE_WARMUP} warm-up launches (left out) then {PROFILE_LAUNCHES} measured ones, "
+             "dispatches named by the run's manifest (bench.py --profile-run).  Algorithmic bytes "
+             "are the inputs read plus the outputs written.", "",
+             "Command (repository root):", "", f"    {command}", ""]
+    js = []
+    if kind == "trace":
+        lines += ["| Workload | Kernel | Launches | Average us | Min us | Algorithmic MB | GB/s | Fraction of 8 TB/s |",
+                  "|---|---|---|---|---|---|---|---|"]
+        for e, chunk in groups:
+            kern = "; ".join(sorted({short_name(c[0]) for c in chunk}))
+            us = np.array([c[1] for c in chunk]) / 1e3
+            if e.get("kernels_per_call", 1) > 1:
+                step = us.reshape(-1, e["kernels_per_call"]).sum(axis=1)
+                lines.append(f"| {e['label']} | {kern} | {len(chunk)} | {step.mean():.2f} per step "
+                             f"({us.mean():.2f} per launch) | {step.min():.2f} per step | — | — | launch-bound |")
+                js.append({"label": e["label"], "kernel": kern, "step_us": float(step.mean())})
+            else:
+                g = e["alg_bytes"] / (us.mean() * 1e-6) / 1e9
+                lines.append(f"| {e['label']} | {kern} | {len(chunk)} | {us.mean():.2f} | {us.min():.2f} | "
+                             f"{e['alg_bytes'] / 1e6:.1f} | {g:.1f} | {g / HBM_PEAK_GBS:.3f} |")
+                js.append({"label": e["label"], "kernel": kern, "avg_us": float(us.mean()),
+                           "alg_bytes": e["alg_bytes"], "GBps": g, "frac": g / HBM_PEAK_GBS})
+    else:
+        names = sorted({c for d in disp for c in d[2]})
+        mean = lambda chunk, n: float(np.mean([c[2].get(n, np.nan) for c in chunk]))
+        fs = ws = None
+        if "FETCH_SIZE" in names and "WRITE_SIZE" in names:
+            cal = [(e, ch) for e, ch in groups if e["label"].startswith("calibration")]
+            if cal:
+                e, ch = cal[0]
+                fs = e["alg_read"] / (mean(ch, "FETCH_SIZE") * 1024)
+                ws = e["alg_write"] / (mean(ch, "WRITE_SIZE") * 1024)
+                lines += [f"Traffic = FETCH_SIZE x {fs:.5f} and WRITE_SIZE x {ws:.5f} (KiB per dispatch "
+                          "scaled by the calibration copy's known bytes over its counters), in MiB.", ""]
+        other = [n for n in names if n not in ("FETCH_SIZE", "WRITE_SIZE")]
+        cols = ["Workload", "Kernel", "Launches"]
+        if fs is not None:
+            cols += ["read MiB", "algorithmic read", "write MiB", "algorithmic write", "traffic / algorithmic"]
+        cols += [f"{n} per dispatch" for n in other]
+        lines += ["| " + " | ".join(cols) + " |", "|" + "---|" * len(cols)]
+        for e, chunk in groups:
+            kern = "; ".join(sorted({short_name(c[0]) for c in chunk}))
+            cells = [e["label"], kern, str(len(chunk))]
+            rec = {"label": e["label"], "kernel": kern}
+            if fs is not None:
+                rd = mean(chunk, "FETCH_SIZE") * 1024 * fs
+                wr = mean(chunk, "WRITE_SIZE") * 1024 * ws
+                alg = e["alg_read"] + e["alg_write"]
+                ratio = (rd + wr) / alg if alg else float("nan")
+                cells += [f"{rd / 2**20:.1f}", f"{e['alg_read'] / 2**20:.1f}", f"{wr / 2**20:.1f}",
+                          f"{e['alg_write'] / 2**20:.1f}", f"{ratio:.4f}"]
+                rec.update({"read_bytes": rd, "write_bytes": wr, "alg_read": e["alg_read"],
+                            "alg_write": e["alg_write"], "traffic_over_alg": ratio,
+                            "fetch_scale": fs, "write_scale": ws})
+            vals = [mean(chunk, n) for n in other]
+            cells += [f"{v:.1f}" for v in vals]
+            rec.update({n: v for n, v in zip(other, vals)})
+            lines.append("| " + " | ".join(cells) + " |")
+            js.append(rec)
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.splitext(out_md)[0] + ".json", "w") as f:
+        json.dump({"command": command, "kind": kind, "kernel_source_sha": kernel_source_sha(), "rows": js}, f,
+                  indent=1)
+    print("\n".join(lines))
+
+
+def traffic_json(summary_json, out_path):
+    """The headline forward's HBM traffic per launch, from a counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated), tagged with the hash of the
+    forward's sources so the bench can tell when it is stale."""
+    with open(summary_json) as f:
+        d = json.load(f)
+    row = next(r for r in d["rows"] if r["label"].startswith("weight_4k forward"))
+    out = {"kernel": KERNELS["fwd"], "workload": "weight_4k 4096x4096 bf16, y + clip bitmap",
+           "kernel_source_sha": d["kernel_source_sha"], "command": d["command"],
+           "read_bytes_per_launch": round(row["read_bytes"]), "write_bytes_per_launch": round(row["write_bytes"]),
+           "traffic_bytes_per_launch": round(row["read_bytes"] + row["write_bytes"]),
+           "alg_bytes_per_launch": row["alg_read"] + row["alg_write"],
+           "traffic_over_alg": round(row["traffic_over_alg"], 5),
+           "fetch_scale": round(row["fetch_scale"], 5), "write_scale": round(row["write_scale"], 5)}
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def short_name(name: str) -> str:
+    """Kernel name without return type, namespaces and parameter list."""
+    s = name.split(" [clone")[0].replace("(anonymous namespace)::", "").replace("mxfp4::", "")
+    if s.startswith("void "):
+        s = s[5:]
+    depth = 0
+    for i, ch in enumerate(s):
+        depth += (ch == "<") - (ch == ">")
+        if ch == "(" and depth == 0:
+            return s[:i].strip()
+    return s.strip()
+
+
+def probe_sweep(M, lib, W, torch, stream, probe, out_path):
+    """The forward-pattern and copy probes over launch shapes (lanes per
+    workgroup x pieces per lane) at 4096x4096 (8 rotating sets) and
+    28672x8192 (2 sets): the best this memory system gives the forward's
+    byte pattern at each size, whatever the launch shape."""
+    timer = Timer(torch, stream)
+    out = {}
+    for rows, cols, sets in ((4096, 4096, 8), (28672, 8192, 2)):
+        n = rows * cols
+        npieces = n * 2 // 16
+        xs = [torch.empty((n,), dtype=torch.bfloat16, device="cuda").normal_() for _ in range(sets)]
+        ys = [torch.empty_like(xs[0]) for _ in range(sets)]
+        ms = [torch.empty((npieces,), dtype=torch.uint8, device="cuda") for _ in range(sets)]
+        res = {}
+        for kind, name, nbytes in ((PROBE_FWD, "fwd_pattern", n * 4.125), (PROBE_COPY, "copy", n * 4.0)):
+            for threads in (64, 128, 256, 512, 1024):
+                for per_lane in (1, 2, 4, 8):
+                    calls = [probe.call(kind, xs[s], ys[s], ms[s] if kind == PROBE_FWD else None, npieces, threads,
+                                        stream, per_lane=per_lane) for s in range(sets)]
+                    med, best = timer(calls, reps=100 if n < 1e8 else 20)
+                    res[f"{name}_t{threads}_u{per_lane}"] = {"us": round(med * 1e6, 2),
+                                                            "GBps": round(gbs(nbytes, med), 1)}
+        best = max(res.items(), key=lambda kv: kv[1]["GBps"] if kv[0].startswith("fwd") else 0)
+        out[f"{rows}x{cols}"] = {"best_fwd_pattern": best, "all": res}
+        del xs, ys, ms
+        torch.cuda.empty_cache()
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps({k: v["best_fwd_pattern"] for k, v in out.items()}))
+
+
+def stamps_run(M, lib, W, torch, stream, probe, out_path, reps=20):
+    """Per-workgroup start / end wall-clock stamps of the forward-pattern probe
+    at 4096x4096 (8 rotating sets, as the headline): how a launch of this
+    shape splits into ramp (workgroups still starting), steady streaming and
+    drain (after the last workgroup started)."""
+    wk = build_weight4k(M, lib, W, torch, stream, 8)
+    n = wk["rows"] * wk["cols"]
+    npieces = n * 2 // 16
+    nwg = npieces // 64
+    khz = probe.lib.probe_wall_clock_khz(torch.cuda.current_device())
+    st = torch.zeros((2 * nwg,), dtype=torch.int64, device="cuda")
+    calls = [probe.call(PROBE_FWD, wk["xs"][s], wk["ys"][s], wk["ms"][s], npieces, 64, stream, stamps=st)
+             for s in range(8)]
+    res = []
+    for i in range(reps):
+        calls[i % 8]()
+        torch.cuda.synchronize()
+        a = st.cpu().numpy().reshape(-1, 2).astype(np.float64) * (1e3 / khz)   # microseconds
+        t0 = a[:, 0].min()
+        s, e = a[:, 0] - t0, a[:, 1] - t0
+        res.append({"span_us": float(e.max()), "last_start_us": float(s.max()),
+                    "median_wg_us": float(np.median(e - s)),
+                    "starts_by_us": np.histogram(s, bins=np.arange(0, np.ceil(e.max()) + 1))[0].tolist(),
+                    "ends_by_us": np.histogram(e, bins=np.arange(0, np.ceil(e.max()) + 1))[0].tolist()})
+    out = {"what": "forward-pattern probe, bf16 4096x4096, 64-lane workgroups, one 16-byte piece per lane, "
+                   f"{nwg} workgroups; stamps from wall_clock64 at {khz} kHz",
+           "wall_clock_khz": khz, "launches": res,
+           "median_span_us": float(np.median([r["span_us"] for r in res])),
+           "median_last_start_us": float(np.median([r["last_start_us"] for r in res]))}
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps({k: out[k] for k in ("median_span_us", "median_last_start_us", "wall_clock_khz")}))
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--sets", type=int, default=8)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
+    ap.add_argument("--no-large", action="store_true",
+                    help="skip the 28672x8192 steady-state forward / backward timing")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=3.0,
+                    help="minimum oracle time per workload sample (the headline's sample takes twice this)")
+    ap.add_argument("--all", metavar="OUT", default=None)
+    ap.add_argument("--gemm", metavar="OUT", default=None,
+                    help="time only the grouped MX matmuls (NN / NT / TN of the MoE layer) into OUT")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run only a 512 MiB device copy (rocprofv3 counter calibration)")
+    ap.add_argument("--profile-run", metavar="MANIFEST", default=None,
+                    help="launch every workload's kernel a fixed number of times and write the manifest")
+    ap.add_argument("--summarize", nargs=4, metavar=("KIND", "DIR", "MANIFEST", "OUT_MD"), default=None,
+                    help="join a rocprofv3 CSV (KIND trace or pmc) under DIR with the manifest into OUT_MD")
+    ap.add_argument("--command", default="", help="the profiling command, recorded by --summarize")
+    ap.add_argument("--traffic-json", nargs=2, metavar=("SUMMARY_JSON", "OUT"), default=None,
+                    help="write the headline forward's traffic file from a counter summary")
+    ap.add_argument("--stamps", metavar="OUT", default=None,
+                    help="per-workgroup clocks of the forward-pattern probe at 4096x4096")
+    ap.add_argument("--probe-sweep", metavar="OUT", default=None,
+                    help="streaming probes over launch shapes at 4096x4096 and 28672x8192")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the hot path has no "
+              "cross-GPU step; each GPU would run its own shard independently.", file=sys.stderr)
+        sys.exit(2)
+    if args.summarize:
+        kind, d, man, out = args.summarize
+        summarize(kind, d, man, out, args.command)
+        return
+    if args.traffic_json:
+        traffic_json(*args.traffic_json)
+        return
+
+    import torch
+    import workloads as W
+    import mxfp4_fake_quantization_amd as M
+
+    if args.calib_copy:
+        a = torch.empty(256 << 20, dtype=torch.int16, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": a.numel() * 2, "calib_copy_bytes_written": a.numel() * 2}))
+        return
+
+    lib = M._load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if args.gemm:
+        res = bench_gemm(M, W, torch, {})
+        with open(args.gemm, "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res))
+        return
+    probe = Probe()
+    if args.profile_run:
+        profile_run(M, lib, W, torch, stream, probe, args.profile_run)
+        return
+    if args.stamps:
+        stamps_run(M, lib, W, torch, stream, probe, args.stamps)
+        return
+    if args.probe_sweep:
+        probe_sweep(M, lib, W, torch, stream, probe, args.probe_sweep)
+        return
+
+    result, wk = bench_headline(M, lib, W, torch, stream, args, probe)
+    x_np, g_np = wk["x_np"], wk["g_np"]
+    del wk
+    torch.cuda.empty_cache()
+    if not args.no_large:
+        result["steady_state"] = steady_state(M, lib, W, torch, stream, probe)
+    if not args.no_configs:
+        result["configs"] = bench_configs(M, lib, W, torch, stream, not args.no_cpu, args.cpu_seconds)
+    if args.all:
+        result["other_workloads_file"] = args.all
+        with open(args.all, "w") as f:
+            json.dump(bench_all(M, lib, W, torch, stream), f, indent=1)
+    if not args.no_cpu:
+        import oracle
+
+        def step():
+            _, clip, _ = oracle.qdq_rows(x_np, 32, "floor")
+            oracle.ste_bwd(g_np, clip)
+        rows, cols = x_np.shape
+        result["cpu_baseline"] = oracle_baseline(step, rows * cols * 8.25, 2 * rows * cols,
+                                                 f"the whole weight_4k workload ({rows}x{cols} bf16 fwd+bwd)",
+                                                 2 * args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

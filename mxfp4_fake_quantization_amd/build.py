@@ -2,8 +2,10 @@
 
     python -m mxfp4_fake_quantization_amd.build
 
-Each .hip file under csrc/ is compiled by hipcc for gfx950 into _build/, then
-linked into mxfp4_fake_quantization_amd/libmxfp4.so.  Packed-FP32 VALU
+Each .hip file of the library under csrc/ is compiled by hipcc for gfx950
+into _build/, then linked into mxfp4_fake_quantization_amd/libmxfp4.so.
+csrc/probe_kernels.hip (streaming probes the benchmark times next to the
+kernels; not part of the C ABI) becomes libmxfp4_probe.so.  Packed-FP32 VALU
 instructions are disabled (-packed-fp32-ops); no fast-math.
 """
 import concurrent.futures as cf
@@ -15,6 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmxfp4.so")
+PROBE_LIB = os.path.join(HERE, "libmxfp4_probe.so")
+PROBE_SOURCES = ["probe_kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["api.hip", "row_kernels.hip", "col_kernels.hip", "ste_kernels.hip",
@@ -34,9 +38,14 @@ def _compile(src: str) -> str:
 
 def build() -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[len(SOURCES):], PROBE_LIB)
+    return _link(objs[:len(SOURCES)], LIB)
+
+
+def _link(objs, lib) -> str:
+    tmp = lib + ".tmp"
     r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
@@ -48,8 +57,8 @@ def build() -> str:
     if missing:
         os.remove(tmp)
         raise RuntimeError("kernel launch stubs missing from the host objects: " + ", ".join(missing))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

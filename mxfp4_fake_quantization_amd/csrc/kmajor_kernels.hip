@@ -194,20 +194,28 @@ __device__ __forceinline__ KmTile km_tile(const KmArgs &A, int64_t tile, int wav
   return T;
 }
 
-// LDS staging of one tile's outputs.  Code word (column c, K word kw) sits at
-// codes[c][4 * ((kw >> 2) ^ ((c >> 3) & 7)) + (kw & 3)]: 16-byte chunks of a
-// column row are XOR-swizzled by the column's group, so the 64 lanes of a
-// staging write (16 column groups x 4 K words) spread over all banks, and the
-// 8 lanes that read one column's 8 chunks (ds_read_b128) hit distinct banks.
+// LDS staging of one tile's outputs.  The 16-byte chunk q (K words 4q ..
+// 4q + 3) of column c's row sits at chunk slot q ^ ((c >> 3) & 7) of the row,
+// and inside the chunk word i sits at i ^ (2 * ((c >> 6) & 1)).  A staging
+// write stores one word per lane for lanes (cg = column group 0..15, K word
+// 4 * wave + rql): the XOR with the group's low three bits spreads the eight
+// groups of a half-wave over the eight chunk slots, the XOR with its fourth
+// bit puts groups cg and cg + 8 on different words of the chunk, so each
+// half-wave's 32 words fall in 32 different banks.  The 8 lanes that read
+// one column's row (ds_read_b128) cover its 32 words, so all banks, and swap
+// the halves back where bit 6 of the column is set.  Scale bytes are staged
+// block-row major ([block-row][column]): a lane writes its eight columns'
+// bytes with one 8-byte store, 16 lanes 128 consecutive bytes.
 template <int CT>
 struct KmStage {
   uint32_t codes[CT][kKTile / 8] __attribute__((aligned(16)));
-  uint8_t scales[CT][kKTile / 32];
+  uint8_t scales[kKTile / 32][CT] __attribute__((aligned(16)));
   uint8_t live[kKTile / 32];
 };
 
+__device__ __forceinline__ int km_chunk(int c, int q) { return c * (kKTile / 8) + 4 * (q ^ ((c >> 3) & 7)); }
 __device__ __forceinline__ int km_slot(int c, int kw) {
-  return c * (kKTile / 8) + 4 * ((kw >> 2) ^ ((c >> 3) & 7)) + (kw & 3);
+  return km_chunk(c, kw >> 2) + ((kw & 3) ^ (((c >> 6) & 1) << 1));
 }
 
 // One workgroup per tile: load, column maxima, nibbles; then the tile's
@@ -224,7 +232,7 @@ void kmajor_pack_kernel(KmArgs A) {
   constexpr int ES = PieceT<DT>::ES;
   constexpr uint32_t ABS = DT == kBF16 ? 0x7FFF7FFFu : 0x7FFFFFFFu;
   constexpr int NBT_TILE = kKTile / B;  // block-rows per tile
-  __shared__ uint32_t s_cm[kKmThreads / 64][16][NW];
+  __shared__ uint32_t s_cm[kKmThreads / 64][NW][16];  // [wave][word][column group]: no bank conflicts
   __shared__ KmStage<kCTile> st;
 
   const int tid = threadIdx.x;
@@ -266,14 +274,14 @@ void kmajor_pack_kernel(KmArgs A) {
   if (B == 128) {
     if (rql == 0) {
 #pragma unroll
-      for (int k = 0; k < NW; ++k) s_cm[wave][cg][k] = cm[k];
+      for (int k = 0; k < NW; ++k) s_cm[wave][k][cg] = cm[k];
     }
     __syncthreads();
     const int w0 = wave & ~3;
 #pragma unroll
     for (int k = 0; k < NW; ++k)
-      cm[k] = colmax_step<DT>(colmax_step<DT>(s_cm[w0][cg][k], s_cm[w0 + 1][cg][k]),
-                              colmax_step<DT>(s_cm[w0 + 2][cg][k], s_cm[w0 + 3][cg][k]));
+      cm[k] = colmax_step<DT>(colmax_step<DT>(s_cm[w0][k][cg], s_cm[w0 + 1][k][cg]),
+                              colmax_step<DT>(s_cm[w0 + 2][k][cg], s_cm[w0 + 3][k][cg]));
   }
 
   // ---- per-column parameters ---------------------------------------------
@@ -311,9 +319,16 @@ void kmajor_pack_kernel(KmArgs A) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) (&st.codes[0][0])[km_slot(128 * chalf + 8 * cg + j, kw)] = cw[j];
   if (T.o0 == 0) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      st.scales[128 * chalf + 8 * cg + j][bl] = (uint8_t)(DT == kBF16 ? (pe[j >> 1] >> (16 * (j & 1))) : pe[j]);
+    // the E8M0 bytes of the lane's 8 columns, in column order
+    uint32_t lo, hi;
+    if (DT == kBF16) {
+      lo = perm_b32(pe[1], pe[0], 0x06040200u);  // bytes 0 and 2 of each packed word
+      hi = perm_b32(pe[3], pe[2], 0x06040200u);
+    } else {
+      lo = pe[0] | (pe[1] << 8) | (pe[2] << 16) | (pe[3] << 24);
+      hi = pe[4] | (pe[5] << 8) | (pe[6] << 16) | (pe[7] << 24);
+    }
+    *reinterpret_cast<uint2 *>(&st.scales[bl][128 * chalf + 8 * cg]) = make_uint2(lo, hi);
     if (cg == 0) st.live[bl] = T.live;
   }
   __syncthreads();
@@ -329,7 +344,8 @@ void kmajor_pack_kernel(KmArgs A) {
     const int c = chunk >> 3, q = chunk & 7;
     const int64_t col = T.col0 + c;
     if (col < A.cols && st.live[(32 * q) / B]) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(&(&st.codes[0][0])[km_slot(c, 4 * q)]);
+      uint4 v = *reinterpret_cast<const uint4 *>(&(&st.codes[0][0])[km_chunk(c, q)]);
+      if ((c >> 6) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
       st16(A.codes + col * A.ldk + kbyte + 16 * q, v);
     }
   }
@@ -341,12 +357,12 @@ void kmajor_pack_kernel(KmArgs A) {
     if (NBT_TILE == 8 && all_live && ((uintptr_t)sd & 7) == 0) {
       uint64_t v = 0;
 #pragma unroll
-      for (int b = 0; b < 8; ++b) v |= (uint64_t)st.scales[tid][b] << (8 * b);
+      for (int b = 0; b < 8; ++b) v |= (uint64_t)st.scales[b][tid] << (8 * b);
       *reinterpret_cast<uint64_t *>(sd) = v;
     } else {
 #pragma unroll
       for (int b = 0; b < NBT_TILE; ++b)
-        if (st.live[b]) sd[b] = st.scales[tid][b];
+        if (st.live[b]) sd[b] = st.scales[b][tid];
     }
   }
 }

@@ -160,7 +160,10 @@ template <int DT, int FMT>
 __global__ __launch_bounds__(kKm8Threads) void mxfp8_kmajor_kernel(Km8Args A) {
   constexpr int ES = DT == kBF16 ? 2 : 4;
   constexpr int ROWB = kKm8Cols * ES;              // bytes of a tile row
-  constexpr int BSTRIDE = 32 * ROWB + 64;          // block stride in LDS (+64: banks)
+  // block stride in LDS: +32 bytes puts the 4 block-rows that a compute-phase
+  // read touches (lanes b = tid & 3) 8 banks apart, so the 32 lanes of a
+  // half-wave (4 block-rows x 8 columns' words) hit 32 different banks
+  constexpr int BSTRIDE = 32 * ROWB + 32;
   constexpr float MAXN = Fp8T<FMT>::MAXN;
   __shared__ __align__(16) uint8_t tile[kKm8Blk * BSTRIDE];
 

@@ -1,0 +1,127 @@
+// probe_kernels.hip -- streaming probes for measurement (libmxfp4_probe.so).
+//
+// Not part of the method or of the C ABI in include/mxfp4.h: these kernels
+// move bytes with the access pattern of the quantization kernels and do no
+// arithmetic, so their time is what the memory system gives that pattern.
+// bench.py reports them as the achievable bandwidth next to the kernels.
+//
+// Per 16-byte piece (a lane's chunk of 8 bf16 elements in the row-wise
+// forward):
+//   kind 0 "fwd"   read 16 B, write 16 B (y) and 1 B (one bitmap byte)
+//   kind 1 "copy"  read 16 B, write 16 B
+//   kind 2 "read"  read 16 B (a word of the sum is stored only if it equals
+//                  a value no input here produces, so nothing is written)
+//   kind 3 "write" write 16 B
+// with non-temporal 16-byte accesses (the quantization kernels' ld16/st16),
+// `per_lane` pieces per lane in workgroups of `threads` lanes (the row-wise
+// forward: one piece, 64 lanes).  With a stamps
+// buffer, the first lane of every workgroup records the 100 MHz wall clock
+// (s_memrealtime) when the workgroup starts and when its stores have been
+// issued: stamps[2 * wg] and stamps[2 * wg + 1].
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// U pieces per lane: piece (blockIdx.x * U + u) * blockDim.x + threadIdx.x, so
+// each of the lane's U accesses is part of one contiguous stretch of
+// 16 * blockDim.x bytes; all U loads are issued before any store.
+template <int KIND, bool STAMP, int U>
+__global__ void probe_kernel(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst,
+                             uint8_t *__restrict__ side, int64_t npieces, uint64_t *stamps) {
+  uint64_t t0 = 0;
+  if (STAMP) t0 = wall_clock64();
+  const int64_t base = (int64_t)blockIdx.x * U * blockDim.x + threadIdx.x;
+  u32x4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = base + (int64_t)u * blockDim.x;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    v[u] = (KIND != 3 && i < npieces) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src) + i) : z;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = base + (int64_t)u * blockDim.x;
+    if (i < npieces) {
+      if (KIND == 3) {
+        const u32x4 w = {(uint32_t)i, 1u, 2u, 3u};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(dst) + i);
+      } else {
+        if (KIND == 0 || KIND == 1) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4 *>(dst) + i);
+        if (KIND == 0) side[i] = (uint8_t)v[u].x;
+        if (KIND == 2) {
+          const uint32_t s = v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+          if (s == 0x9E3779B9u && v[u].x == 0x7F7F7F7Fu) side[i] = 1;
+        }
+      }
+    }
+  }
+  if (STAMP && threadIdx.x == 0) {
+    stamps[2 * (int64_t)blockIdx.x] = t0;
+    stamps[2 * (int64_t)blockIdx.x + 1] = wall_clock64();
+  }
+}
+
+template <int KIND, int U>
+hipError_t launch(const void *src, void *dst, void *side, int64_t npieces, int threads, uint64_t *stamps,
+                  hipStream_t st) {
+  const int64_t per_wg = (int64_t)threads * U;
+  const int64_t nwg = (npieces + per_wg - 1) / per_wg;
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nwg), block((unsigned)threads);
+  auto s = static_cast<const uint8_t *>(src);
+  auto d = static_cast<uint8_t *>(dst);
+  auto m = static_cast<uint8_t *>(side);
+  if (stamps)
+    hipLaunchKernelGGL((probe_kernel<KIND, true, U>), grid, block, 0, st, s, d, m, npieces, stamps);
+  else
+    hipLaunchKernelGGL((probe_kernel<KIND, false, U>), grid, block, 0, st, s, d, m, npieces, stamps);
+  return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_u(int per_lane, const void *src, void *dst, void *side, int64_t npieces, int threads,
+                    uint64_t *stamps, hipStream_t st) {
+  switch (per_lane) {
+    case 1: return launch<KIND, 1>(src, dst, side, npieces, threads, stamps, st);
+    case 2: return launch<KIND, 2>(src, dst, side, npieces, threads, stamps, st);
+    case 4: return launch<KIND, 4>(src, dst, side, npieces, threads, stamps, st);
+    case 8: return launch<KIND, 8>(src, dst, side, npieces, threads, stamps, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+// npieces 16-byte pieces: src and dst hold 16 * npieces bytes (16-byte
+// aligned), side npieces bytes (kinds 0 and 2), stamps 2 * ceil(npieces /
+// (threads * per_lane)) words when not NULL.  threads: 64, 128, 256, 512 or
+// 1024; per_lane: 1, 2, 4 or 8.  Returns a hipError_t value (0 on success).
+extern "C" int probe_stream(int kind, const void *src, void *dst, void *side, int64_t npieces, int threads,
+                            int per_lane, uint64_t *stamps, void *stream) {
+  if (threads != 64 && threads != 128 && threads != 256 && threads != 512 && threads != 1024)
+    return (int)hipErrorInvalidValue;
+  if (npieces < 0) return (int)hipErrorInvalidValue;
+  if (kind != 3 && !src) return (int)hipErrorInvalidValue;
+  if (kind != 2 && !dst) return (int)hipErrorInvalidValue;
+  if ((kind == 0 || kind == 2) && !side) return (int)hipErrorInvalidValue;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) return (int)hipErrorInvalidValue;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (kind) {
+    case 0: return (int)launch_u<0>(per_lane, src, dst, side, npieces, threads, stamps, st);
+    case 1: return (int)launch_u<1>(per_lane, src, dst, side, npieces, threads, stamps, st);
+    case 2: return (int)launch_u<2>(per_lane, src, dst, side, npieces, threads, stamps, st);
+    case 3: return (int)launch_u<3>(per_lane, src, dst, side, npieces, threads, stamps, st);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+// Frequency of the clock behind wall_clock64(), in kHz.
+extern "C" int probe_wall_clock_khz(int device) {
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) != hipSuccess) return -1;
+  return khz;
+}
