@@ -121,7 +121,8 @@ __device__ __forceinline__ void code_words(const uint32_t (&w)[8][PieceT<DT>::NW
           if (SLOW && RULE == kFloor)
             t[r] = fix_slow_nib(x, cm[k], pe[k], n_bf16(x, pt[k], pz[k])) << 12;
           else
-            t[r] = (snap_idx_bf16_tab(x & 0x7FFF7FFFu, t31) << 12) | sign_bf16(x, pz[k]);
+            t[r] = (snap_idx_bf16_tab(x & 0x7FFF7FFFu, t31) << 12) |
+                   (RULE == kFloor ? sign_bf16_floor(x) : sign_bf16(x, pz[k]));
         }
         acc[g] = (t[0] >> 12) | (t[1] >> 8) | (t[2] >> 4) | t[3];
       }
@@ -309,6 +310,17 @@ void kmajor_pack_kernel(KmArgs A) {
     }
   }
 
+  // the E8M0 bytes of the lane's 8 columns, in column order (packed before
+  // the code words so the per-column bytes need no registers meanwhile)
+  uint32_t sc_lo, sc_hi;
+  if (DT == kBF16) {
+    sc_lo = perm_b32(pe[1], pe[0], 0x06040200u);  // bytes 0 and 2 of each packed word
+    sc_hi = perm_b32(pe[3], pe[2], 0x06040200u);
+  } else {
+    sc_lo = pe[0] | (pe[1] << 8) | (pe[2] << 16) | (pe[3] << 24);
+    sc_hi = pe[4] | (pe[5] << 8) | (pe[6] << 16) | (pe[7] << 24);
+  }
+
   uint32_t cw[8];
   if (__builtin_expect(__any(slow_any), 0)) code_words<DT, RULE, true>(w, pt, pz, pe, cm, cbp, cw);
   else code_words<DT, RULE, false>(w, pt, pz, pe, cm, cbp, cw);
@@ -319,16 +331,7 @@ void kmajor_pack_kernel(KmArgs A) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) (&st.codes[0][0])[km_slot(128 * chalf + 8 * cg + j, kw)] = cw[j];
   if (T.o0 == 0) {
-    // the E8M0 bytes of the lane's 8 columns, in column order
-    uint32_t lo, hi;
-    if (DT == kBF16) {
-      lo = perm_b32(pe[1], pe[0], 0x06040200u);  // bytes 0 and 2 of each packed word
-      hi = perm_b32(pe[3], pe[2], 0x06040200u);
-    } else {
-      lo = pe[0] | (pe[1] << 8) | (pe[2] << 16) | (pe[3] << 24);
-      hi = pe[4] | (pe[5] << 8) | (pe[6] << 16) | (pe[7] << 24);
-    }
-    *reinterpret_cast<uint2 *>(&st.scales[bl][128 * chalf + 8 * cg]) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2 *>(&st.scales[bl][128 * chalf + 8 * cg]) = make_uint2(sc_lo, sc_hi);
     if (cg == 0) st.live[bl] = T.live;
   }
   __syncthreads();

@@ -265,6 +265,9 @@ MXFP4_HD uint32_t snap_idx_bf16_tab(uint32_t a, uint32_t t31) {
 MXFP4_HD uint32_t sign_bf16(uint32_t p, uint32_t zc2) {
   return p & pk_add(p & 0x7FFF7FFFu, zc2) & 0x80008000u;
 }
+// the FLOOR case (Z = 0) in fewer registers: bit 15 of p - 1 is set for every
+// negative half but -0.0
+MXFP4_HD uint32_t sign_bf16_floor(uint32_t p) { return p & pk_sub(p, 0x00010001u) & 0x80008000u; }
 MXFP4_HD uint32_t mask_bits_bf16(uint32_t a, uint32_t six2) {
   return pk_min(pk_subsat(a, six2), 0x00010001u);
 }

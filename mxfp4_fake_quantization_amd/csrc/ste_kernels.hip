@@ -239,6 +239,15 @@ __global__ __launch_bounds__(kThreads) void ste_col_kernel(SteColArgs A) {
   }
 }
 
+template <int DT, int U>
+void ste_row_launch(int mode, dim3 grid, const SteRowArgs &a, hipStream_t st) {
+  switch (mode) {
+    case kModeFlat: hipLaunchKernelGGL((ste_row_kernel<DT, kModeFlat, U>), grid, dim3(kSteThreads), 0, st, a); break;
+    case kModeRowsVec: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsVec, U>), grid, dim3(kSteThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsScalar, U>), grid, dim3(kSteThreads), 0, st, a); break;
+  }
+}
+
 template <int DT>
 hipError_t launch_row(const SteLaunch &L, hipStream_t st) {
   SteRowArgs a;
@@ -260,25 +269,13 @@ hipError_t launch_row(const SteLaunch &L, hipStream_t st) {
   const int64_t per = (int64_t)kSteThreads * u;
   const int64_t nwg = (a.nchunks + per - 1) / per;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
-  dim3 grid((unsigned)nwg);
-  if (u == 2) {
-    switch (mode) {
-      case kModeFlat: hipLaunchKernelGGL((ste_row_kernel<DT, kModeFlat, 2>), grid, dim3(kSteThreads), 0, st, a); break;
-      case kModeRowsVec: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsVec, 2>), grid, dim3(kSteThreads), 0, st, a); break;
-      default: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsScalar, 2>), grid, dim3(kSteThreads), 0, st, a); break;
-    }
-  } else if (u == 1) {
-    switch (mode) {
-      case kModeFlat: hipLaunchKernelGGL((ste_row_kernel<DT, kModeFlat, 1>), grid, dim3(kSteThreads), 0, st, a); break;
-      case kModeRowsVec: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsVec, 1>), grid, dim3(kSteThreads), 0, st, a); break;
-      default: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsScalar, 1>), grid, dim3(kSteThreads), 0, st, a); break;
-    }
-  } else {
-    switch (mode) {
-      case kModeFlat: hipLaunchKernelGGL((ste_row_kernel<DT, kModeFlat, 4>), grid, dim3(kSteThreads), 0, st, a); break;
-      case kModeRowsVec: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsVec, 4>), grid, dim3(kSteThreads), 0, st, a); break;
-      default: hipLaunchKernelGGL((ste_row_kernel<DT, kModeRowsScalar, 4>), grid, dim3(kSteThreads), 0, st, a); break;
-    }
+  const dim3 grid((unsigned)nwg);
+  switch (u) {
+    case 1: ste_row_launch<DT, 1>(mode, grid, a, st); break;
+    case 2: ste_row_launch<DT, 2>(mode, grid, a, st); break;
+    case 4: ste_row_launch<DT, 4>(mode, grid, a, st); break;
+    case 8: ste_row_launch<DT, 8>(mode, grid, a, st); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
