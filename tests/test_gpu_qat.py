@@ -1,8 +1,9 @@
-"""GPU checks of the QAT wrapper: forward values and STE gradients through
+"""GPU checks of the QAT layer: forward values and STE gradients through
 autograd equal the oracle's QDQ and masked gradients; the QAT Linear's
-gradients match a float reference built from the oracle's quantized
-operands; the amct PR's minimal validation (Linear(64, 32), W4A4, sum
-backward, finite gradients) passes."""
+output and gradients match a float reference built from the oracle's
+quantized operands and masks; the amct PR's minimal validation (Linear(64,
+32), W4A4, sum backward, finite gradients) passes through its entry-point
+names; a bf16 training step runs."""
 import numpy as np
 import pytest
 import torch
@@ -22,27 +23,38 @@ def need_gpu():
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("clip", [False, True])
 @pytest.mark.parametrize("block", [32, 128])
-def test_fake_quant_forward_backward(oracle, dtype, clip, block):
-    from mxfp4_fake_quantization_amd.qat import mxfp4_fake_quant
+@pytest.mark.parametrize("rule", ["floor", "amct"])
+def test_fake_quant_forward_backward(oracle, dtype, clip, block, rule):
+    from mxfp4_fake_quantization_amd.qat import MXFP4Spec, fake_quant
     g = np.random.default_rng(block + clip)
     a = (g.standard_t(3, size=(3, 5, 256)) * 0.05).astype(np.float32)
     x_np = W.f32_to_bf16_bits(a) if dtype == "bf16" else a
     up_np = g.standard_normal(a.shape).astype(np.float32)
     up_np = W.f32_to_bf16_bits(up_np) if dtype == "bf16" else up_np
     x = dev(x_np).requires_grad_(True)
-    y = mxfp4_fake_quant(x, block_size=block, clip_grad=clip)
+    y = fake_quant(x, MXFP4Spec(block=block, rule=rule, clipped=clip))
     y.backward(dev(up_np))
-    yo, cl, _ = oracle.qdq_rows(x_np.reshape(-1, 256), block)
+    yo, cl, _ = oracle.qdq_rows(x_np.reshape(-1, 256), block, rule)
     assert np.array_equal(host(y.detach()).reshape(-1, 256), yo)
     want = oracle.ste_bwd(up_np.reshape(-1, 256), cl if clip else None)
     assert np.array_equal(host(x.grad).reshape(-1, 256), want)
 
 
+def test_pr_fake_quant_name(oracle):
+    from mxfp4_fake_quantization_amd.qat import mxfp4_fake_quant
+    a = np.random.default_rng(3).standard_normal((8, 64)).astype(np.float32)
+    x = dev(a).requires_grad_(True)
+    y = mxfp4_fake_quant(x, block_size=32, clip_grad=True)
+    y.sum().backward()
+    yo, cl, _ = oracle.qdq_rows(a, 32)
+    assert np.array_equal(host(y.detach()), yo)
+    assert np.array_equal(host(x.grad), 1.0 - cl.astype(np.float32))
+
+
 def test_qat_linear_gradients_match_reference(oracle):
-    from mxfp4_fake_quantization_amd.qat import MXFP4QATConfig, MXFP4QATLinear
+    from mxfp4_fake_quantization_amd.qat import QATLinear, QATPolicy
     torch.manual_seed(0)
-    cfg = MXFP4QATConfig(quantize_input=True, clip_grad=True)
-    lin = MXFP4QATLinear(96, 40, config=cfg).cuda()
+    lin = QATLinear(96, 40, policy=QATPolicy.w4a4(clipped=True)).cuda()
     x = torch.randn(7, 96, device="cuda") * 3
     x.requires_grad_(True)
     out = lin(x)
@@ -77,11 +89,11 @@ def test_minimal_validation_scenario():
 
 
 def test_bf16_qat_step_runs():
-    from mxfp4_fake_quantization_amd.qat import MXFP4QATConfig, convert_to_mxfp4_qat
+    from mxfp4_fake_quantization_amd.qat import QATPolicy, quantize_model
     torch.manual_seed(1)
     model = torch.nn.Sequential(torch.nn.Linear(256, 128), torch.nn.GELU(),
                                 torch.nn.Linear(128, 64)).cuda().to(torch.bfloat16)
-    convert_to_mxfp4_qat(model, MXFP4QATConfig(quantize_input=True, clip_grad=True, block_size=128))
+    quantize_model(model, QATPolicy.w4a4(clipped=True, block=128))
     opt = torch.optim.SGD(model.parameters(), lr=1e-2)
     x = torch.randn(16, 256, device="cuda", dtype=torch.bfloat16)
     loss = model(x).float().square().mean()

@@ -1,42 +1,105 @@
-"""Host-side checks of the QAT wrapper (no kernel calls): configuration
-validation and module conversion (the amct PR's linear.py behaviour)."""
+"""Host-side checks of the QAT layer (no kernel calls): spec and policy
+validation, and model conversion -- the behaviour the amct PR's README
+states for its Linear: the layer's parameters are the float layer's own
+objects, the state_dict is unchanged, named paths stay in float with their
+subtrees, and converting twice changes nothing."""
 import pytest
+import torch
 from torch import nn
 
-from mxfp4_fake_quantization_amd.qat import (MXFP4FakeQuantizer, MXFP4QATConfig, MXFP4QATLinear,
-                                             convert_to_mxfp4_qat)
+from mxfp4_fake_quantization_amd.qat import (FakeQuant, MXFP4FakeQuantizer, MXFP4QATConfig, MXFP4QATLinear,
+                                             MXFP4Spec, QATLinear, QATPolicy, convert_to_mxfp4_qat,
+                                             quantize_model)
 
 
-def test_config_validation():
-    MXFP4QATConfig()
-    for bad in (dict(block_size=16), dict(block_size=0), dict(scale_factor=0.0),
-                dict(scale_factor=-1.0), dict(rule="round")):
+def test_spec_validation():
+    MXFP4Spec()
+    MXFP4Spec(block=128, rule="amct", scale_factor=7.0, clipped=True)
+    for bad in (dict(block=16), dict(block=0), dict(scale_factor=0.0), dict(scale_factor=-1.0),
+                dict(rule="round")):
         with pytest.raises(ValueError):
-            MXFP4QATConfig(**bad)
+            MXFP4Spec(**bad)
     with pytest.raises(ValueError):
         MXFP4FakeQuantizer(block_size=64)
+    with pytest.raises(ValueError):
+        MXFP4QATConfig(scale_factor=0)
 
 
-def test_convert_replaces_linears_and_keeps_parameters():
-    model = nn.Sequential(nn.Linear(64, 32), nn.ReLU(),
-                          nn.Sequential(nn.Linear(32, 16), nn.Linear(16, 8)))
-    model.add_module("lm_head", nn.Linear(8, 4))
-    w0 = model[0].weight
-    keys = set(model.state_dict())
-    convert_to_mxfp4_qat(model, MXFP4QATConfig(quantize_input=True), skip_names=("lm_head",))
-    assert isinstance(model[0], MXFP4QATLinear)
-    assert isinstance(model[2][0], MXFP4QATLinear) and isinstance(model[2][1], MXFP4QATLinear)
-    assert type(model.lm_head) is nn.Linear
-    assert model[0].weight is w0                      # parameters adopted, not copied
-    assert set(model.state_dict()) == keys            # stateless quantizers
-    assert model[0].input_quantizer is not None and model[0].weight_quantizer is not None
-    before = [id(m) for m in model.modules()]
-    convert_to_mxfp4_qat(model, skip_names=("lm_head",))   # idempotent
-    assert [id(m) for m in model.modules()] == before
+def test_policies():
+    p = QATPolicy.w4a16(block=128)
+    assert p.weight == MXFP4Spec(block=128) and p.activation is None
+    p = QATPolicy.w4a4(clipped=True)
+    assert p.weight == p.activation == MXFP4Spec(clipped=True)
+    c = MXFP4QATConfig(quantize_input=True, clip_grad=True, block_size=128, rule="amct", scale_factor=5.0)
+    assert c.weight == c.activation == MXFP4Spec(128, "amct", 5.0, True)
+    assert MXFP4QATConfig().activation is None and MXFP4QATConfig(quantize_weight=False).weight is None
 
 
-def test_w4a16_default_has_no_input_quantizer():
-    lin = MXFP4QATLinear(64, 32)
-    assert lin.weight_quantizer is not None and lin.input_quantizer is None
-    assert "block_size=32" in repr(lin.weight_quantizer)
+class Block(nn.Module):
+    def __init__(self):
+        super().__init__()
+        self.up = nn.Linear(32, 16)
+        self.act = nn.ReLU()
+        self.down = nn.Linear(16, 8)
 
+
+class LinearWithChild(nn.Linear):
+    """A Linear subclass with a child Linear: the child goes away with it."""
+
+    def __init__(self):
+        super().__init__(8, 8)
+        self.side = nn.Linear(8, 8)
+
+
+def model():
+    m = nn.Sequential(nn.Linear(64, 32), Block(), LinearWithChild())
+    m.add_module("lm_head", nn.Linear(8, 4))
+    m.lm_head.add_module("inner", nn.Linear(4, 4))   # under an excluded path
+    return m
+
+
+def test_quantize_model_swaps_linears_and_keeps_state():
+    m = model()
+    params = {n: p for n, p in m.named_parameters()}
+    sd = {k: v.clone() for k, v in m.state_dict().items()}
+    quantize_model(m, QATPolicy.w4a4(), exclude=("lm_head",))
+    assert isinstance(m[0], QATLinear) and isinstance(m[1].up, QATLinear) and isinstance(m[1].down, QATLinear)
+    assert isinstance(m[2], QATLinear) and not hasattr(m[2], "side")       # its subtree went with it
+    assert type(m.lm_head) is nn.Linear and type(m.lm_head.inner) is nn.Linear
+    assert m[0].weight is params["0.weight"] and m[1].down.bias is params["1.down.bias"]
+    assert m[0].policy == QATPolicy.w4a4()
+    # the state_dict is the float model's (minus the dropped child of the subclass)
+    new = m.state_dict()
+    assert set(new) == {k for k in sd if not k.startswith("2.side.")}
+    assert all(torch.equal(new[k], sd[k]) for k in new)
+    # converting again changes nothing
+    before = [id(x) for x in m.modules()]
+    quantize_model(m, QATPolicy.w4a16(), exclude=("lm_head",))
+    assert [id(x) for x in m.modules()] == before and m[0].policy == QATPolicy.w4a4()
+
+
+def test_shared_linear_becomes_one_qat_layer():
+    shared = nn.Linear(16, 16)
+    m = nn.Sequential(shared, nn.ReLU(), shared)
+    quantize_model(m)
+    assert isinstance(m[0], QATLinear) and m[0] is m[2] and m[0].weight is shared.weight
+
+
+def test_wrap_and_defaults():
+    lin = nn.Linear(64, 32, bias=False).eval()
+    q = QATLinear.wrap(lin, QATPolicy.w4a16(block=128))
+    assert q.bias is None and q.weight is lin.weight and not q.training
+    assert (q.in_features, q.out_features) == (64, 32)
+    assert set(q.state_dict()) == {"weight"}
+    d = QATLinear(64, 32)
+    assert d.policy.weight == MXFP4Spec() and d.policy.activation is None   # W4A16
+    assert "block=32" in repr(FakeQuant()) and not list(FakeQuant().parameters())
+    assert MXFP4QATLinear is QATLinear and MXFP4QATLinear.from_linear(lin).weight is lin.weight
+
+
+def test_pr_entry_points():
+    m = model()
+    convert_to_mxfp4_qat(m, MXFP4QATConfig(quantize_input=True), skip_names=("lm_head", "down"))
+    assert isinstance(m[0], QATLinear) and type(m[1].down) is nn.Linear and type(m.lm_head) is nn.Linear
+    assert m[0].policy.activation is not None
+    assert isinstance(MXFP4FakeQuantizer(clip_grad=True), FakeQuant)
