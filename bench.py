@@ -61,7 +61,8 @@ KERNEL_SOURCES = ["mxfp4_fake_quantization_amd/csrc/row_kernels.hip",
                   "mxfp4_fake_quantization_amd/csrc/mxfp4_device.h",
                   "mxfp4_fake_quantization_amd/csrc/mxfp4_math.h"]
 PROBE_LIB = os.path.join(ROOT, "mxfp4_fake_quantization_amd", "libmxfp4_probe.so")
-PROBE_FWD, PROBE_COPY, PROBE_READ, PROBE_WRITE = 0, 1, 2, 3
+PROBE_FWD, PROBE_COPY, PROBE_READ, PROBE_WRITE, PROBE_DUAL, PROBE_PACK = 0, 1, 2, 3, 4, 5
+PROBE_SHAPES = ((64, 1), (256, 1), (256, 4), (512, 8))   # (lanes per workgroup, pieces per lane)
 
 
 def kernel_source_sha() -> str:
@@ -369,7 +370,7 @@ def bench_headline(M, lib, W, torch, stream, args, probe):
     # events (per-kernel events inside the loop would add ~2 us per kernel of
     # marker overhead to the GPU timeline).
     K = args.steps
-    hev = HipEvents(5)
+    hev = HipEvents(2)
     rec, evs = hev.record, hev.ev
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -382,20 +383,15 @@ def bench_headline(M, lib, W, torch, stream, args, probe):
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total_ms = hev.ms(0, 1)
-    # Kernel durations for the roofline: K back-to-back launches of one
-    # kernel between two HIP events (the same rotation of buffer sets); the
-    # per-launch average matches rocprofv3's kernel-trace average.
-    rec(evs[2], stream)
-    for i in range(K):
-        fwd[i % args.sets]()
-    rec(evs[3], stream)
-    for i in range(K):
-        bwd[i % args.sets]()
-    rec(evs[4], stream)
-    torch.cuda.synchronize()
-    fwd_s = hev.ms(2, 3) / K * 1e-3
-    bwd_s = hev.ms(3, 4) / K * 1e-3
     hev.close()
+    # Kernel durations for the roofline: back-to-back launches of one kernel
+    # between two HIP events (the same rotation of buffer sets), median of
+    # three trials of max(K, 200) launches; the per-launch average matches
+    # rocprofv3's kernel-trace average.
+    timer = Timer(torch, stream)
+    reps = max(K, 200)
+    t_fwd, t_bwd = timer(fwd, reps=reps), timer(bwd, reps=reps)
+    fwd_s, bwd_s = t_fwd[0], t_bwd[0]
     value = gbs(step_bytes * K, total_ms * 1e-3)
     achieved = gbs(fwd_bytes, fwd_s)
 
@@ -428,23 +424,20 @@ def bench_headline(M, lib, W, torch, stream, args, probe):
                      "alg_bytes_per_launch": fwd_bytes},
     }
     # achievable: the probes over the same buffers and rotation
-    timer = Timer(torch, stream)
     npieces = n * 2 // 16
     pf = [probe.call(PROBE_FWD, wk["xs"][s], wk["ys"][s], wk["ms"][s], npieces, 64, stream)
           for s in range(args.sets)]
     pc = [probe.call(PROBE_COPY, wk["xs"][s], wk["ys"][s], None, npieces, 64, stream)
           for s in range(args.sets)]
-    reps = max(K, 100)
     t_pf, t_pc = timer(pf, reps=reps), timer(pc, reps=reps)
-    t_fwd = timer(fwd, reps=reps)
     result["achievable"] = {
         "what": "streaming probes over the same 8 rotating buffer sets, one 16-byte piece per lane "
                 "in 64-lane workgroups like the forward, no arithmetic; median of 3 trials",
         "fwd_pattern": entry("read 16 B + write 16 B + 1 B per piece (the forward's bytes and "
                              "pattern)", "probe_kernel<fwd>", fwd_bytes, n, t_pf),
         "copy": entry("read 16 B + write 16 B per piece", "probe_kernel<copy>", n * 4, n, t_pc),
-        "forward_same_trials": entry("the forward kernel, timed the same way", KERNELS["fwd"],
-                                     fwd_bytes, n, t_fwd),
+        "forward_same_trials": entry("the forward kernel, timed the same way (its roofline timing)",
+                                     KERNELS["fwd"], fwd_bytes, n, t_fwd),
         "forward_over_probe_time": round(t_fwd[0] / t_pf[0], 4),
     }
     return result, wk
@@ -514,7 +507,22 @@ def steady_state(M, lib, W, torch, stream, probe, rows=28672, cols=8192, sets=2,
 
 # ---------------------------------------------------------------- configs
 
-def bench_configs(M, lib, W, torch, stream, cpu, cpu_seconds):
+def probe_best(probe, timer, stream, kind, srcs, dsts, sides, npieces, nbytes, what):
+    """The probe of one byte mix over a config's own buffers (two sets), for
+    a few launch shapes; the best is what the memory system gives that mix at
+    that size, whatever the shape."""
+    res = {}
+    for threads, per_lane in PROBE_SHAPES:
+        calls = [probe.call(kind, srcs[i], dsts[i], sides[i] if sides else None, npieces, threads, stream,
+                            per_lane=per_lane) for i in range(len(srcs))]
+        med, _ = timer(calls)
+        res[f"t{threads}_u{per_lane}"] = round(gbs(nbytes, med), 1)
+    best = max(res, key=res.get)
+    return {"what": what, "best_shape": best, "GBps": res[best], "frac": round(res[best] / HBM_PEAK_GBS, 4),
+            "by_shape_GBps": res}
+
+
+def bench_configs(M, lib, W, torch, stream, probe, cpu, cpu_seconds):
     """Every other workload at full size: GPU time of back-to-back launches
     over two buffer sets, and the oracle on a bounded sample of the same
     input."""
@@ -553,6 +561,10 @@ def bench_configs(M, lib, W, torch, stream, cpu, cpu_seconds):
     R, C = dual["R"], dual["C"]
     e = entry(f"act_dual: bf16 {R}x{C} Student-t(3)*0.5, one dual-direction launch: y_row + y_col + "
               "both bitmaps", KERNELS["dual"], R * C * 6.25, R * C, timer(dual["calls"]))
+    xs_, yr_, yc_ = dual["bufs"][0], dual["bufs"][1], dual["bufs"][2]
+    e["achievable"] = probe_best(probe, timer, stream, PROBE_DUAL, xs_, yr_, yc_, R * C * 2 // 16, R * C * 6.0,
+                                 "probe reading 2 B and writing 4 B per element (the two y views, no bitmaps) "
+                                 "over the same buffers")
     if cpu:
         xs = dual["x_np"][:1024]
         e["cpu_baseline"] = oracle_baseline(lambda: (oracle.qdq_rows(xs, 32), oracle.qdq_cols(xs, 32)),
@@ -568,6 +580,9 @@ def bench_configs(M, lib, W, torch, stream, cpu, cpu_seconds):
     R, C = grp["R"], grp["C"]
     e = entry(f"moe_grouped: bf16 {R}x{C} N(0,1), 8 multinomial groups, grouped column-wise "
               "block-32 QDQ (y)", KERNELS["grouped"], R * C * 4.0, R * C, timer(grp["calls"]))
+    e["achievable"] = probe_best(probe, timer, stream, PROBE_COPY, grp["bufs"][0], grp["bufs"][1], None,
+                                 R * C * 2 // 16, R * C * 4.0,
+                                 "probe copying 2 B per element (read x, write y) over the same buffers")
     grm = build_grouped(M, lib, W, torch, stream, with_mask=True)
     t_m = timer(grm["calls"])
     e["with_grouped_bitmap"] = entry("the same, y + GROUPED bitmap", KERNELS["grouped"], R * C * 4.125,
@@ -591,6 +606,11 @@ def bench_configs(M, lib, W, torch, stream, cpu, cpu_seconds):
         e = entry(f"weight_pack: bf16 {R}x{C} N(0,0.02^2) + outliers, row-wise block-{blk} packed codes "
                   "+ E8M0 bytes", KERNELS[f"pack{blk}"], R * C * (2 + 0.5 + 1 / blk), R * C,
                   timer(pk["calls"]))
+        if blk == 32:
+            e["achievable"] = probe_best(probe, timer, stream, PROBE_PACK, pk["bufs"][0], pk["bufs"][1], None,
+                                         R * C * 2 // 16, R * C * 2.5,
+                                         "probe reading 2 B and writing 0.5 B per element (the codes, no "
+                                         "scales) over the same buffers")
         if cpu:
             xs = xw[:1024]
             e["cpu_baseline"] = oracle_baseline(lambda: oracle.pack_rows(xs, blk), xs.size * (2.5 + 1 / blk),
@@ -1184,7 +1204,7 @@ def main():
     if not args.no_large:
         result["steady_state"] = steady_state(M, lib, W, torch, stream, probe)
     if not args.no_configs:
-        result["configs"] = bench_configs(M, lib, W, torch, stream, not args.no_cpu, args.cpu_seconds)
+        result["configs"] = bench_configs(M, lib, W, torch, stream, probe, not args.no_cpu, args.cpu_seconds)
     if args.all:
         result["other_workloads_file"] = args.all
         with open(args.all, "w") as f:

@@ -232,14 +232,16 @@ mxfp4_status_t mxfp4_dequant(const mxfp4_desc_t *desc, const uint8_t *codes,
  * MXFP8 quantization of the grad_output operand of the W4A8 grouped matmul
  * (the hyper-parallel page's npu_dynamic_mx_quant for the NN / NT products,
  * which it does not define; this is the OCP Microscaling v1.0 conversion):
- * blocks of 32 along each row (desc->block must be 32), E8M0 scale byte
+ * blocks of desc->block elements along each row -- 32, the MX block, or 128,
+ * the block of the page's block-128 mode, whose quantizer quantizes
+ * activations and grad_output in blocks of 128 --, E8M0 scale byte
  * e8 = max(floor(log2 amax) - emax + 127, 0) with emax 8 (MXFP8_E4M3) or 15
  * (MXFP8_E5M2), an all-zero block giving 0; each element is x / 2^(e8-127)
  * rounded to the nearest fp8 value, ties to even, saturating at 448 (E4M3) /
  * 57344 (E5M2), so no NaN / infinity code is produced; -0.0 and negative
  * values that round to zero give -0 (0x80).
  *   q      [rows, cols] fp8 bytes (OCP E4M3 bias 7 / E5M2 bias 15),
- *   scales [rows, ceil(cols/32)] E8M0 bytes.
+ *   scales [rows, ceil(cols/block)] E8M0 bytes.
  * desc->rule and scale_factor are ignored.  x and q 16-byte aligned, scales
  * any alignment, no aliasing.
  */

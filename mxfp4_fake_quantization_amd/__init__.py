@@ -329,17 +329,18 @@ def mxfp4_dequant(codes, scales, y, block=32):
 _FP8 = {"e4m3": 0, "e5m2": 1}
 
 
-def mxfp8_quant(x, q, scales, fmt="e4m3"):
-    """MXFP8 (OCP MX, blocks of 32 along the last dim): q uint8 with x's
-    shape, scales uint8 [rows, ceil(cols/32)]."""
+def mxfp8_quant(x, q, scales, fmt="e4m3", block=32):
+    """MXFP8 (OCP MX element rule, blocks of 32 -- or 128 -- along the last
+    dim): q uint8 with x's shape, scales uint8 [rows, ceil(cols/block)]."""
     if fmt not in _FP8:
         raise ValueError(f"fmt must be 'e4m3' or 'e5m2', got {fmt!r}")
     rows, cols = _shape2d(x)
     if q is None or q.numel() != x.numel():
         raise ValueError("q must have x's number of elements")
-    if scales is None or scales.numel() != rows * (-(-cols // 32)):
-        raise ValueError(f"scales must hold {rows} x {-(-cols // 32)} bytes")
-    d = _Desc(_dtype(x), 32, FLOOR, 0, rows, cols, 6.0, 0)
+    nb = -(-cols // int(block))
+    if scales is None or scales.numel() != rows * nb:
+        raise ValueError(f"scales must hold {rows} x {nb} bytes")
+    d = _Desc(_dtype(x), int(block), FLOOR, 0, rows, cols, 6.0, 0)
     st = _load().mxfp8_quant(ctypes.byref(d), _FP8[fmt], _ptr(x), _ptr(q, "u8"), _ptr(scales, "u8"),
                              _stream())
     _check(st, "mxfp8_quant")

@@ -242,8 +242,6 @@ mxfp4_status_t mxfp8_quant(const mxfp4_desc_t *desc, int32_t fmt, const void *x,
                            uint8_t *scales, void *stream) {
   int64_t n;
   MXFP4_TRY(check_desc(desc, false, &n));
-  if (desc->block != 32)
-    return fail(MXFP4_EUNSUPPORTED, "MXFP8 blocks are 32 elements (got block %d)", desc->block);
   if (fmt != MXFP8_E4M3 && fmt != MXFP8_E5M2)
     return fail(MXFP4_EINVAL, "fmt %d is not MXFP8_E4M3 or MXFP8_E5M2", fmt);
   MXFP4_TRY(check_ptr(x, 16, "x"));
@@ -251,7 +249,7 @@ mxfp4_status_t mxfp8_quant(const mxfp4_desc_t *desc, int32_t fmt, const void *x,
   MXFP4_TRY(check_ptr(scales, 1, "scales"));
   if (!distinct({x, q, scales})) return fail(MXFP4_EINVAL, "x, q and scales must not alias");
   if (n == 0) return ok();
-  mxfp4::Mx8Launch L{desc->dtype, fmt, desc->rows, desc->cols, x, q, scales};
+  mxfp4::Mx8Launch L{desc->dtype, fmt, desc->rows, desc->cols, x, q, scales, desc->block};
   return hip_status(mxfp4::launch_mxfp8_rows(L, static_cast<hipStream_t>(stream)), "MXFP8 launch");
 }
 

@@ -84,7 +84,8 @@ struct Mx8Launch {
   int64_t rows, cols;
   const void *x;
   uint8_t *q;       // [rows, cols] fp8 bytes
-  uint8_t *scales;  // [rows, ceil(cols/32)] E8M0
+  uint8_t *scales;  // [rows, ceil(cols/block)] E8M0
+  int block;        // 32 or 128
 };
 hipError_t launch_mxfp8_rows(const Mx8Launch &L, hipStream_t stream);
 

@@ -3,13 +3,14 @@
 //
 // The hyper-parallel page feeds grad_output to the W4A8 grouped matmul through
 // npu_dynamic_mx_quant (the "ordinary MXFP8 GMM contract"); this is the OCP
-// Microscaling conversion: blocks of 32 along each row, one E8M0 scale 2^k per
-// block with k = floor(log2 amax) - emax (E4M3 8, E5M2 15), clamped below at
-// -127, and every element x / 2^k rounded to nearest, ties to even,
+// Microscaling conversion: blocks of 32 along each row (128 in the page's
+// block-128 mode, whose quantizer works in blocks of 128), one E8M0 scale 2^k
+// per block with k = floor(log2 amax) - emax (E4M3 8, E5M2 15), clamped below
+// at -127, and every element x / 2^k rounded to nearest, ties to even,
 // saturating at the format's largest normal.
 //
 // Work split: a lane holds 8 consecutive elements of a row (one 16-byte bf16
-// load), a block is 4 lanes (DPP max).  The scale exponent comes from the
+// load), a block is 4 lanes (16 for blocks of 128; DPP max).  The scale exponent comes from the
 // exponent field of the block max, so x * 2^-k is an exact fp32 product; it is
 // clamped to +-max with v_med3_f32 and converted two at a time by the hardware
 // fp8 conversion (round to nearest even).  8 code bytes per lane leave in one
@@ -50,7 +51,7 @@ __device__ __forceinline__ int cvt2(float a, float b, int old) {
 // against 121 us with four waves, 123 us with one and 120 us with eight.
 constexpr int kMx8Threads = 128;
 
-template <int DT, int FMT, int MODE>
+template <int DT, int FMT, int MODE, int G>
 __global__ __launch_bounds__(kMx8Threads) void mxfp8_rows_kernel(Mx8Args A) {
   constexpr int NW = PieceT<DT>::NW;
   constexpr int ES = PieceT<DT>::ES;
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(kMx8Threads) void mxfp8_rows_kernel(Mx8Args A) {
 #pragma unroll
     for (int k = 0; k < NW; ++k) am = max32(am, w[k] & 0x7FFFFFFFu);
   }
-  am = group_max<4>(am);
+  am = group_max<G>(am);
   const int eb = (int)(am >> 23);  // biased exponent of the block max (0: zero / subnormal)
   const int e8 = eb - Fp8T<FMT>::EMAX > 0 ? eb - Fp8T<FMT>::EMAX : 0;
   const float s = __builtin_bit_cast(float, (uint32_t)(254 - e8) << 23);  // 2^(127 - e8) = 2^-k
@@ -107,23 +108,28 @@ __global__ __launch_bounds__(kMx8Threads) void mxfp8_rows_kernel(Mx8Args A) {
     const uint64_t pk = (uint64_t)(uint32_t)lo | ((uint64_t)(uint32_t)hi << 32);
     for (int j = 0; j < nval; ++j) dst[j] = (uint8_t)(pk >> (8 * j));
   }
-  if ((threadIdx.x & 3) == 0 && i < A.nchunks) {
-    const int64_t bi = MODE == kMx8Flat ? cr >> 2 : row * A.nb + (cr >> 2);
+  if ((threadIdx.x & (G - 1)) == 0 && i < A.nchunks) {
+    const int64_t bi = MODE == kMx8Flat ? cr / G : row * A.nb + cr / G;
     if (MODE == kMx8Flat || cr * 8 < A.cols) A.scales[bi] = (uint8_t)e8;
   }
 }
 
-template <int DT, int FMT>
-hipError_t mx8_launch(int mode, const Mx8Args &a, hipStream_t st) {
+template <int DT, int FMT, int G>
+hipError_t mx8_launch_g(int mode, const Mx8Args &a, hipStream_t st) {
   const int64_t nwg = (a.nchunks + kMx8Threads - 1) / kMx8Threads;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)nwg);
   switch (mode) {
-    case kMx8Flat: hipLaunchKernelGGL((mxfp8_rows_kernel<DT, FMT, kMx8Flat>), grid, dim3(kMx8Threads), 0, st, a); break;
-    case kMx8RowsVec: hipLaunchKernelGGL((mxfp8_rows_kernel<DT, FMT, kMx8RowsVec>), grid, dim3(kMx8Threads), 0, st, a); break;
-    default: hipLaunchKernelGGL((mxfp8_rows_kernel<DT, FMT, kMx8RowsScalar>), grid, dim3(kMx8Threads), 0, st, a); break;
+    case kMx8Flat: hipLaunchKernelGGL((mxfp8_rows_kernel<DT, FMT, kMx8Flat, G>), grid, dim3(kMx8Threads), 0, st, a); break;
+    case kMx8RowsVec: hipLaunchKernelGGL((mxfp8_rows_kernel<DT, FMT, kMx8RowsVec, G>), grid, dim3(kMx8Threads), 0, st, a); break;
+    default: hipLaunchKernelGGL((mxfp8_rows_kernel<DT, FMT, kMx8RowsScalar, G>), grid, dim3(kMx8Threads), 0, st, a); break;
   }
   return hipGetLastError();
+}
+
+template <int DT, int FMT>
+hipError_t mx8_launch(int block, int mode, const Mx8Args &a, hipStream_t st) {
+  return block == 128 ? mx8_launch_g<DT, FMT, 16>(mode, a, st) : mx8_launch_g<DT, FMT, 4>(mode, a, st);
 }
 
 // ---- K-major MXFP8 of column-wise / grouped 32-row blocks ---------------------
@@ -310,19 +316,20 @@ hipError_t launch_mxfp8_rows(const Mx8Launch &L, hipStream_t st) {
   a.q = L.q;
   a.scales = L.scales;
   a.cols = L.cols;
-  a.nb = (L.cols + 31) / 32;
-  a.cpr = a.nb * 4;
+  a.nb = (L.cols + L.block - 1) / L.block;
+  a.cpr = a.nb * (L.block / 8);
   int mode;
-  if (L.cols % 32 == 0) {
+  if (L.cols % L.block == 0) {
     mode = kMx8Flat;
     a.nchunks = L.rows * L.cols / 8;
   } else {
     mode = L.cols % 8 == 0 ? kMx8RowsVec : kMx8RowsScalar;
     a.nchunks = L.rows * a.cpr;
   }
+  const int b = L.block;
   if (L.dtype == kBF16)
-    return L.fmt == kE4M3 ? mx8_launch<kBF16, kE4M3>(mode, a, st) : mx8_launch<kBF16, kE5M2>(mode, a, st);
-  return L.fmt == kE4M3 ? mx8_launch<kF32, kE4M3>(mode, a, st) : mx8_launch<kF32, kE5M2>(mode, a, st);
+    return L.fmt == kE4M3 ? mx8_launch<kBF16, kE4M3>(b, mode, a, st) : mx8_launch<kBF16, kE5M2>(b, mode, a, st);
+  return L.fmt == kE4M3 ? mx8_launch<kF32, kE4M3>(b, mode, a, st) : mx8_launch<kF32, kE5M2>(b, mode, a, st);
 }
 
 }  // namespace mxfp4

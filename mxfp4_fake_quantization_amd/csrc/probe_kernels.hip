@@ -12,6 +12,9 @@
 //   kind 2 "read"  read 16 B (a word of the sum is stored only if it equals
 //                  a value no input here produces, so nothing is written)
 //   kind 3 "write" write 16 B
+//   kind 4 "dual"  read 16 B, write 16 B to dst and 16 B to side (the dual
+//                  launch's two y views, without its bitmaps)
+//   kind 5 "pack"  read 16 B, write 4 B (the packed codes of 8 elements)
 // with non-temporal 16-byte accesses (the quantization kernels' ld16/st16),
 // `per_lane` pieces per lane in workgroups of `threads` lanes (the row-wise
 // forward: one piece, 64 lanes).  With a stamps
@@ -48,8 +51,12 @@ __global__ void probe_kernel(const uint8_t *__restrict__ src, uint8_t *__restric
       if (KIND == 3) {
         const u32x4 w = {(uint32_t)i, 1u, 2u, 3u};
         __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(dst) + i);
+      } else if (KIND == 5) {
+        reinterpret_cast<uint32_t *>(dst)[i] = v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
       } else {
-        if (KIND == 0 || KIND == 1) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4 *>(dst) + i);
+        if (KIND == 0 || KIND == 1 || KIND == 4)
+          __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4 *>(dst) + i);
+        if (KIND == 4) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4 *>(side) + i);
         if (KIND == 0) side[i] = (uint8_t)v[u].x;
         if (KIND == 2) {
           const uint32_t s = v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
@@ -97,7 +104,8 @@ hipError_t launch_u(int per_lane, const void *src, void *dst, void *side, int64_
 }  // namespace
 
 // npieces 16-byte pieces: src and dst hold 16 * npieces bytes (16-byte
-// aligned), side npieces bytes (kinds 0 and 2), stamps 2 * ceil(npieces /
+// aligned; dst 4 * npieces for kind 5), side npieces bytes (kinds 0 and 2) or
+// 16 * npieces (kind 4, 16-byte aligned), stamps 2 * ceil(npieces /
 // (threads * per_lane)) words when not NULL.  threads: 64, 128, 256, 512 or
 // 1024; per_lane: 1, 2, 4 or 8.  Returns a hipError_t value (0 on success).
 extern "C" int probe_stream(int kind, const void *src, void *dst, void *side, int64_t npieces, int threads,
@@ -107,14 +115,17 @@ extern "C" int probe_stream(int kind, const void *src, void *dst, void *side, in
   if (npieces < 0) return (int)hipErrorInvalidValue;
   if (kind != 3 && !src) return (int)hipErrorInvalidValue;
   if (kind != 2 && !dst) return (int)hipErrorInvalidValue;
-  if ((kind == 0 || kind == 2) && !side) return (int)hipErrorInvalidValue;
+  if ((kind == 0 || kind == 2 || kind == 4) && !side) return (int)hipErrorInvalidValue;
   if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) return (int)hipErrorInvalidValue;
+  if (kind == 4 && (reinterpret_cast<uintptr_t>(side) & 15)) return (int)hipErrorInvalidValue;
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (kind) {
     case 0: return (int)launch_u<0>(per_lane, src, dst, side, npieces, threads, stamps, st);
     case 1: return (int)launch_u<1>(per_lane, src, dst, side, npieces, threads, stamps, st);
     case 2: return (int)launch_u<2>(per_lane, src, dst, side, npieces, threads, stamps, st);
     case 3: return (int)launch_u<3>(per_lane, src, dst, side, npieces, threads, stamps, st);
+    case 4: return (int)launch_u<4>(per_lane, src, dst, side, npieces, threads, stamps, st);
+    case 5: return (int)launch_u<5>(per_lane, src, dst, side, npieces, threads, stamps, st);
     default: return (int)hipErrorInvalidValue;
   }
 }

@@ -42,8 +42,8 @@ def _load():
         lib.oracle_unpack_rows.argtypes = [i32, i64, i64, i32, vp, vp, vp]
         lib.oracle_pack_kmajor.argtypes = [i32, i64, i64, i32, i32, f32, vp, vp, i32, i32, i64,
                                            vp, vp]
-        lib.oracle_mxfp8_rows.argtypes = [i32, i64, i64, i32, vp, vp, vp]
-        lib.oracle_mxfp8_decode.argtypes = [i32, i64, i64, i32, vp, vp, vp]
+        lib.oracle_mxfp8_rows.argtypes = [i32, i64, i64, i32, i32, vp, vp, vp]
+        lib.oracle_mxfp8_decode.argtypes = [i32, i64, i64, i32, i32, vp, vp, vp]
         lib.oracle_grouped_matmul.argtypes = [i32, i64, i64, i64, vp, vp, vp, i32, i32, vp]
         lib.oracle_mxfp8_kmajor.argtypes = [i32, i64, i64, i32, vp, vp, i32, i32, i64, vp, vp]
         for fn in ("oracle_qdq_rows", "oracle_qdq_cols", "oracle_grouped_cols",
@@ -194,24 +194,25 @@ def pack_kmajor(x: np.ndarray, block: int = 32, rule="floor", scale_factor: floa
 FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
 
 
-def mxfp8_rows(x: np.ndarray, fmt: str = "e4m3"):
-    """Row-wise MXFP8 (blocks of 32).  Returns (q[rows, cols] bytes, e8m0[rows, ceil(cols/32)])."""
+def mxfp8_rows(x: np.ndarray, fmt: str = "e4m3", block: int = 32):
+    """Row-wise MXFP8 (blocks of 32 or 128).  Returns (q[rows, cols] bytes,
+    e8m0[rows, ceil(cols/block)])."""
     x = np.ascontiguousarray(x)
     rows, cols = x.shape
     q = np.empty((rows, cols), np.uint8)
-    e8 = np.empty((rows, -(-cols // 32)), np.uint8)
-    _check(_load().oracle_mxfp8_rows(_dtype_code(x), rows, cols, FP8_FORMATS[fmt], _ptr(x), _ptr(q),
+    e8 = np.empty((rows, -(-cols // block)), np.uint8)
+    _check(_load().oracle_mxfp8_rows(_dtype_code(x), rows, cols, FP8_FORMATS[fmt], block, _ptr(x), _ptr(q),
                                      _ptr(e8)), "mxfp8_rows")
     return q, e8
 
 
-def mxfp8_decode(q: np.ndarray, scales: np.ndarray, fmt: str = "e4m3", dtype=np.float32):
-    """Decode MXFP8 bytes + E8M0 scales back to values of `dtype`."""
+def mxfp8_decode(q: np.ndarray, scales: np.ndarray, fmt: str = "e4m3", dtype=np.float32, block: int = 32):
+    """Decode MXFP8 bytes + E8M0 scales (one per `block` elements) back to values of `dtype`."""
     q = np.ascontiguousarray(q, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
     rows, cols = q.shape
     y = np.empty((rows, cols), dtype)
-    _check(_load().oracle_mxfp8_decode(_dtype_code(y), rows, cols, FP8_FORMATS[fmt], _ptr(q),
+    _check(_load().oracle_mxfp8_decode(_dtype_code(y), rows, cols, FP8_FORMATS[fmt], block, _ptr(q),
                                        _ptr(scales), _ptr(y)), "mxfp8_decode")
     return y
 

@@ -467,16 +467,19 @@ static uint8_t mx8_block(int dtype, int fmt, const void *x, const int64_t *idx, 
   return (uint8_t)(k + 127);
 }
 
-/* Row-wise MXFP8: q [rows, cols] bytes, scales [rows, ceil(cols/32)] E8M0. */
-int oracle_mxfp8_rows(int dtype, int64_t rows, int64_t cols, int fmt, const void *x,
+/* Row-wise MXFP8 with blocks of `block` elements (32, the OCP MX block, or
+ * 128: the hyper-parallel page's block-128 mode quantizes activations and
+ * grad_output with its quantizer's block size): q [rows, cols] bytes,
+ * scales [rows, ceil(cols/block)] E8M0. */
+int oracle_mxfp8_rows(int dtype, int64_t rows, int64_t cols, int fmt, int block, const void *x,
                       uint8_t *q, uint8_t *scales) {
-  if (rows < 0 || cols < 0 || (fmt != 0 && fmt != 1)) return 1;
-  const int64_t nb = (cols + 31) / 32;
-  int64_t idx[32];
+  if (rows < 0 || cols < 0 || (fmt != 0 && fmt != 1) || (block != 32 && block != 128)) return 1;
+  const int64_t nb = (cols + block - 1) / block;
+  int64_t idx[128];
   for (int64_t r = 0; r < rows; ++r) {
     for (int64_t b = 0; b < nb; ++b) {
-      const int64_t c0 = b * 32;
-      const int n = (int)((cols - c0) < 32 ? (cols - c0) : 32);
+      const int64_t c0 = b * block;
+      const int n = (int)((cols - c0) < block ? (cols - c0) : block);
       for (int j = 0; j < n; ++j) idx[j] = r * cols + c0 + j;
       scales[r * nb + b] = mx8_block(dtype, fmt, x, idx, n, q + r * cols + c0);
     }
@@ -545,21 +548,22 @@ int oracle_mxfp8_kmajor(int dtype, int64_t rows, int64_t cols, int fmt, const vo
   return 0;
 }
 
-/* Decode MXFP8 back to values: (-1)^s * element(code) * 2^(e8 - 127). */
-int oracle_mxfp8_decode(int dtype, int64_t rows, int64_t cols, int fmt, const uint8_t *q,
+/* Decode MXFP8 back to values: (-1)^s * element(code) * 2^(e8 - 127), one
+ * E8M0 byte per `block` elements of a row. */
+int oracle_mxfp8_decode(int dtype, int64_t rows, int64_t cols, int fmt, int block, const uint8_t *q,
                         const uint8_t *scales, void *y) {
-  if (rows < 0 || cols < 0 || (fmt != 0 && fmt != 1)) return 1;
+  if (rows < 0 || cols < 0 || (fmt != 0 && fmt != 1) || block <= 0) return 1;
   int mb, bias, emax;
   double maxn;
   fp8_params(fmt, &mb, &bias, &maxn, &emax);
-  const int64_t nb = (cols + 31) / 32;
+  const int64_t nb = (cols + block - 1) / block;
   for (int64_t r = 0; r < rows; ++r)
     for (int64_t c = 0; c < cols; ++c) {
       const uint8_t b = q[r * cols + c];
       const int ef = (b & 0x7F) >> mb, m = b & ((1 << mb) - 1);
       double v = ef == 0 ? ldexp((double)m, 1 - bias - mb)
                          : ldexp(1.0 + (double)m / (1 << mb), ef - bias);
-      v *= ldexp(1.0, (int)scales[r * nb + c / 32] - 127);
+      v *= ldexp(1.0, (int)scales[r * nb + c / block] - 127);
       if (b & 0x80) v = -v;
       put_elem(dtype, y, r * cols + c, v);
     }

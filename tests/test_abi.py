@@ -193,9 +193,11 @@ def test_mxfp8_validation(lib):
     assert m8(0, x, q, None, None) == EINVAL
     assert m8(0, x, P(FAKE + 4100), s, None) == EINVAL     # q misaligned
     assert m8(0, x, q, q, None) == EINVAL                   # alias
-    D.block = 128
-    assert m8(0, x, q, s, None) == EUNSUP                   # MX blocks are 32
-    D.block, D.rows = 32, 0
+    D.block = 64
+    assert m8(0, x, q, s, None) == EUNSUP                   # blocks of 32 or 128
+    D.block, D.rows = 128, 0
+    assert m8(1, x, q, s, None) == OK                       # block 128 accepted (nothing to do)
+    D.block = 32
     assert m8(1, x, q, s, None) == OK
 
 

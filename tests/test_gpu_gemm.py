@@ -231,6 +231,8 @@ def tol_check(got, exp, bound, bf16):
     ratio = err / bound
     w = np.unravel_index(ratio.argmax(), ratio.shape)
     assert (ratio <= 1).all(), f"worst error / bound {ratio.max():.3g} at {w}: got {got[w]!r} exact {exp[w]!r}"
+    print(f"worst error / bound {ratio.max():.4f} (error {err[w]:.3g} at {w}, exact {exp[w]:.6g})")
+    return float(ratio.max())
 
 
 def rows_bound(A, Bv, gl):
@@ -323,3 +325,123 @@ def test_moe_forward_full_size_sampled(oracle):
         exp[sel] = A[sel] @ Bk.T
         bound[sel] = mx_matmul_bound(A[sel], Bk)
     tol_check(got, exp, bound, True)
+
+
+def test_block128_nn_forward_from_quantizers(oracle):
+    """Block-128 mode, forward (NN): the page's block-128 branch feeds the
+    activation's and the weight's row-wise views (the weight kept in its
+    native [G, N, K] layout, out x in, so the row-wise blocks run along K).
+    The GPU quantizes x in MXFP8 blocks of 128 and each expert's weight in
+    MXFP4 row-wise blocks of 128 (both bit-exact against the oracle), then
+    the grouped matmul with 128-element scale blocks gives y [M, N] within the
+    matrix-core bound of the oracle's exact product of the decoded operands."""
+    g = np.random.default_rng(31)
+    M, K, N, G = 384, 512, 256, 3
+    gl = [100, 200, 84]
+    x = W.f32_to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    w = W.f32_to_bf16_bits((g.standard_normal((G, N, K)) * 0.02).astype(np.float32))
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 128), dtype=torch.uint8, device="cuda")
+    M_.mxfp8_quant(dev(x), qa, sa, block=128)
+    b = torch.empty((G, N, K // 2), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((G, N, K // 128), dtype=torch.uint8, device="cuda")
+    for i in range(G):
+        M_.mxfp4_quant_pack(dev(w[i]), b[i], sb[i], block=128)
+    qo, so = oracle.mxfp8_rows(x, "e4m3", 128)
+    assert np.array_equal(host(qa), qo) and np.array_equal(host(sa), so)
+    packs = [oracle.pack_rows(w[i], 128) for i in range(G)]
+    bo, sbo = np.stack([p[0] for p in packs]), np.stack([p[1] for p in packs])
+    assert np.array_equal(host(b), bo) and np.array_equal(host(sb), sbo)
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    M_.mxfp4_grouped_matmul(qa, sa, b, sb, c, group_list=gl, a_block=128, b_block=128)
+    torch.cuda.synchronize()
+    A = decode(oracle, qo, so, "e4m3", 128, K)
+    Bv = np.stack([decode(oracle, bo[i], sbo[i], "e2m1", 128, K).T for i in range(G)])
+    exp = oracle.grouped_matmul(A, Bv, gl, oracle.GROUP_M)
+    tol_check(host(c), exp, rows_bound(A, Bv, gl), False)
+
+
+def test_block128_nt_input_grad_from_quantizers(oracle):
+    """Block-128 mode, input gradient (NT): grad_output's row-wise view times
+    the weight's column-wise companion (blocks of 128 along N, the dim the
+    product reduces over), dX [M, K] = dY [M, N] . W_g [N, K].  The GPU
+    quantizes dY in MXFP8 blocks of 128 and stores each expert's column-wise
+    MXFP4 blocks K-major (reduction dim contiguous), both bit-exact against
+    the oracle, then the grouped matmul with 128-element blocks."""
+    g = np.random.default_rng(32)
+    M, K, N, G = 300, 192, 384, 2
+    gl = [123, 177]
+    dy = W.f32_to_bf16_bits(g.standard_normal((M, N)).astype(np.float32))
+    w = W.f32_to_bf16_bits((g.standard_normal((G, N, K)) * 0.02).astype(np.float32))
+    qa = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, N // 128), dtype=torch.uint8, device="cuda")
+    M_.mxfp8_quant(dev(dy), qa, sa, block=128)
+    kb = M_.kmajor_k_blocks(N, 128)
+    b = torch.empty((G, K, kb * 64), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((G, K, kb), dtype=torch.uint8, device="cuda")
+    for i in range(G):
+        M_.mxfp4_quant_pack_kmajor(dev(w[i]), b[i], sb[i], block=128)
+    qo, so = oracle.mxfp8_rows(dy, "e4m3", 128)
+    assert np.array_equal(host(qa), qo) and np.array_equal(host(sa), so)
+    packs = [oracle.pack_kmajor(w[i], 128, k_blocks=kb) for i in range(G)]
+    hb, hsb = host(b), host(sb)
+    nbt = N // 128
+    for i in range(G):
+        assert np.array_equal(hb[i][:, : nbt * 64], packs[i][0][:, : nbt * 64])
+        assert np.array_equal(hsb[i][:, :nbt], packs[i][1][:, :nbt])
+    c = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    M_.mxfp4_grouped_matmul(qa, sa, b, sb, c, K=N, group_list=gl, a_block=128, b_block=128)
+    torch.cuda.synchronize()
+    A = decode(oracle, qo, so, "e4m3", 128, N)
+    Bv = np.stack([decode(oracle, packs[i][0], packs[i][1], "e2m1", 128, N).T for i in range(G)])
+    exp = oracle.grouped_matmul(A, Bv, gl, oracle.GROUP_M)
+    tol_check(W.bf16_bits_to_f32(host(c)), exp, rows_bound(A, Bv, gl), True)
+
+
+def test_block128_weight_gradient_is_refused():
+    """The block-128 TN product (ordinary, not grouped, quantization along
+    tokens, so blocks straddle expert boundaries) is not built: groups that
+    split K take 32-element blocks only."""
+    a = torch.zeros((64, 128), dtype=torch.uint8, device="cuda")
+    sa = torch.full((64, 1), 127, dtype=torch.uint8, device="cuda")
+    b = torch.zeros((32, 128), dtype=torch.uint8, device="cuda")
+    sb = torch.full((32, 1), 127, dtype=torch.uint8, device="cuda")
+    c = torch.empty((2, 64, 32), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="block"):
+        M_.mxfp4_grouped_matmul(a, sa, b, sb, c, K=128, group_list=[64, 64], group_type=M_.GROUP_K,
+                                a_block=128, b_block=128, b_fmt="e4m3", k_blocks=1)
+
+
+def test_matrix_core_group_adder():
+    """The accuracy model behind the matmul's tolerance, pinned on the
+    hardware: the products of each aligned group of 8 K positions are added in
+    a reduced-precision adder aligned to the group's largest product, and the
+    group sums are accumulated in fp32.  E4M3 operands, unit scales, K = 32:
+      C[0, 0]: 448 * 1 and seven 2^-5 * 2^-4 = 2^-9 products in the same group
+               -> 448 exactly (the small products vanish in the group adder);
+      C[1, 0]: the same seven products in the next group (K 8..14) -> the exact
+               sum 448 + 7 * 2^-9 (group sums add in fp32);
+      C[r, 1]: the seven small products alone -> 7 * 2^-9 exactly;
+      C[r, 2]: 448 alone -> 448."""
+    E448, ONE, A_SMALL, B_SMALL = 0x7E, 0x38, 0x10, 0x18      # 448, 1, 2^-5, 2^-4 in E4M3
+    K = 32
+    a = np.zeros((2, K), np.uint8)
+    a[:, 0] = E448
+    a[0, 1:8] = A_SMALL
+    a[1, 8:15] = A_SMALL
+    b = np.zeros((3, K), np.uint8)
+    b[0, 0] = ONE
+    b[0, 1:] = B_SMALL
+    b[1, 1:] = B_SMALL
+    b[2, 0] = ONE
+    sa = np.full((2, 1), 127, np.uint8)
+    sb = np.full((3, 1), 127, np.uint8)
+    c = torch.full((2, 3), -1.0, dtype=torch.float32, device="cuda")
+    M_.mxfp4_grouped_matmul(dev(a), dev(sa), dev(b), dev(sb), c, a_fmt="e4m3", b_fmt="e4m3")
+    torch.cuda.synchronize()
+    got = host(c)
+    small = 7 * 2.0 ** -9
+    assert got[0, 0] == 448.0                     # 448 + 7 * 2^-9 is representable in fp32, yet lost
+    assert got[1, 0] == 448.0 + small             # different groups: exact
+    assert got[0, 1] == small and got[1, 1] == small
+    assert got[0, 2] == 448.0 and got[1, 2] == 448.0

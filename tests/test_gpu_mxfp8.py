@@ -28,11 +28,11 @@ def lib():
     yield
 
 
-def run(x, fmt):
+def run(x, fmt, block=32):
     rows, cols = x.shape
     q = Guarded((rows, cols), torch.uint8)
-    s = Guarded((rows, -(-cols // 32)), torch.uint8)
-    M.mxfp8_quant(dev(x), q.t, s.t, fmt=fmt)
+    s = Guarded((rows, -(-cols // block)), torch.uint8)
+    M.mxfp8_quant(dev(x), q.t, s.t, fmt=fmt, block=block)
     torch.cuda.synchronize()
     q.check_tail()
     s.check_tail()
@@ -94,7 +94,8 @@ SHAPES = [(1, 1), (3, 7), (5, 32), (9, 77), (17, 200), (33, 96), (64, 4096), (13
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("shape", SHAPES)
-def test_mxfp8_shapes(oracle, dtype, fmt, shape):
+@pytest.mark.parametrize("block", [32, 128])
+def test_mxfp8_shapes(oracle, dtype, fmt, shape, block):
     g = np.random.default_rng(shape[0] * 7 + shape[1])
     a = (g.standard_t(3, size=shape) * np.exp2(g.uniform(-40, 40, (shape[0], 1)))).astype(np.float32)
     a.reshape(-1)[::53] = 0.0
@@ -103,10 +104,31 @@ def test_mxfp8_shapes(oracle, dtype, fmt, shape):
         a[1] = 2.0 ** -140                   # fp32 subnormal block maxima
         a[2] = 0.0                           # all-zero row
     x = W.f32_to_bf16_bits(a) if dtype == "bf16" else a
-    q, s = run(x, fmt)
-    qo, so = oracle.mxfp8_rows(x, fmt)
+    q, s = run(x, fmt, block)
+    qo, so = oracle.mxfp8_rows(x, fmt, block)
     assert np.array_equal(s, so)
     assert np.array_equal(q, qo)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_mxfp8_block128_every_bf16_value(oracle, fmt):
+    """Every finite bf16 value in blocks of 128 whose maximum sits in any of
+    the four 32-element quarters (the block-128 maximum spans 16 lanes)."""
+    allb = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    v = W.bf16_bits_to_f32(allb)
+    v = v[np.isfinite(v) & (np.abs(v) <= 2.0 ** 20)]
+    n = -(-v.size // 127) * 127
+    vv = np.zeros(n, np.float32)
+    vv[: v.size] = v
+    body = vv.reshape(-1, 127)
+    x = np.zeros((body.shape[0], 128), np.float32)
+    pos = 32 * (np.arange(body.shape[0]) % 4) + 7
+    for r in range(body.shape[0]):
+        x[r] = np.insert(body[r], pos[r], np.float32(1.5 * 2.0 ** 20))
+    xb = W.f32_to_bf16_bits(x)
+    q, s = run(xb, fmt, 128)
+    qo, so = oracle.mxfp8_rows(xb, fmt, 128)
+    assert np.array_equal(s, so) and np.array_equal(q, qo)
 
 
 def test_mxfp8_edge_blocks(oracle):

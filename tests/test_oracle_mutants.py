@@ -52,6 +52,9 @@ MUTANTS = {
     "mxfp8_kmajor_group_restart": ("for (int64_t r0 = start; r0 < end; r0 += 32) {\n      bs[nbt] = r0;", "for (int64_t r0 = start; r0 < end; r0 = (r0 / 32 + 1) * 32) {\n      bs[nbt] = r0;"),
     "mxfp8_kmajor_scale_layout": ("scales_t[c * k_blocks + t] = mx8_block(", "scales_t[t * cols + c] = mx8_block("),
     "mxfp8_kmajor_leading_dim": ("const int64_t ldq = k_blocks * 32;", "const int64_t ldq = nbt * 32;"),
+    "mxfp8_block128_max_of_first_32": ("const int n = (int)((cols - c0) < block ? (cols - c0) : block);\n      for (int j = 0; j < n; ++j) idx[j] = r * cols + c0 + j;\n      scales[r * nb + b] = mx8_block(",
+                                       "const int n = (int)((cols - c0) < 32 ? (cols - c0) : 32);\n      for (int j = 0; j < n; ++j) idx[j] = r * cols + c0 + j;\n      scales[r * nb + b] = mx8_block("),
+    "mxfp8_decode_block": ("v *= ldexp(1.0, (int)scales[r * nb + c / block] - 127);", "v *= ldexp(1.0, (int)scales[r * nb + c / 32] - 127);"),
     "mxfp8_subnormal_quantum": ("const int emin = 1 - bias; /* exponent of the smallest normal */", "const int emin = -bias;"),
     "gmm_group_weight": ("const double *w = right + (int64_t)g * K * N;", "const double *w = right + (int64_t)(g > 0 ? g - 1 : 0) * K * N;"),
     "gmm_list_type": ("const int64_t end = list_type == 1 ? start + group_list[g] : group_list[g];",

@@ -782,6 +782,38 @@ def test_mxfp8_scale_rule_and_decode(oracle):
         assert (np.abs(y) <= maxn * scale).all()
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_mxfp8_block128(oracle, fmt):
+    """Blocks of 128 (the block-128 mode's activation / grad_output
+    quantization): the E8M0 byte follows the block-128 maximum wherever in the
+    block it sits, each code is the brute-force nearest fp8 value of x / 2^k
+    (ties to even, saturating), ragged rows end in a short block, and decoding
+    with one scale per 128 elements gives x / 2^k's code times 2^k."""
+    emax = 8 if fmt == "e4m3" else 15
+    g = np.random.default_rng(83)
+    rows, cols = 48, 3 * 128 + 40
+    x = (g.standard_t(3, size=(rows, cols)) * np.exp2(g.uniform(-20, 20, (rows, 1)))).astype(np.float32)
+    # put each row's largest element in a different 32-element sub-block of its block
+    for r in range(rows):
+        x[r, 128 + 32 * (r % 4) + 5] = np.abs(x[r]).max() * 3
+    q, e8 = oracle.mxfp8_rows(x, fmt, block=128)
+    assert e8.shape == (rows, 4)
+    pad = np.zeros((rows, 4 * 128), np.float64)
+    pad[:, :cols] = np.abs(x)
+    amax = pad.reshape(rows, 4, 128).max(axis=2)
+    want_e8 = np.maximum(np.floor(np.log2(amax)) - emax + 127, 0).astype(np.uint8)
+    assert np.array_equal(e8, want_e8)
+    k = np.repeat(e8.astype(np.int64) - 127, 128, axis=1)[:, :cols]
+    want = fp8_nearest(x.astype(np.float64).reshape(-1) / np.exp2(k.reshape(-1)), fmt)
+    assert np.array_equal(q.reshape(-1), want)
+    y = oracle.mxfp8_decode(q, e8, fmt, np.float64, block=128)
+    y32 = oracle.mxfp8_decode(q, np.repeat(e8, 4, axis=1)[:, : -(-cols // 32)], fmt, np.float64)
+    assert np.array_equal(y, y32)                      # one scale per 128 = the same scale per 32
+    tab = fp8_table(fmt)
+    vals = np.array([tab[int(c)] for c in want])
+    assert np.array_equal(y.reshape(-1), vals * np.exp2(k.reshape(-1)))
+
+
 # ---- grouped matrix product ---------------------------------------------------
 
 GOLDEN_GMM = os.path.join(os.path.dirname(__file__), "golden", "grouped_matmul.json")
