@@ -139,6 +139,20 @@ mxfp4_status_t mxfp4_ste_bwd(const mxfp4_desc_t *desc, int32_t layout,
                              void *stream);
 
 /*
+ * The saturation mask as the pages give it (fake_quant.py
+ * mxfp4_saturation_mask: a bool tensor of x's shape, true where |x| > 6 * 2^k
+ * of the element's block): expands a ROW or COL bitmap written by
+ * mxfp4_qdq_fwd / mxfp4_quant_pack into rows x cols bytes, row-major,
+ * 1 where the bit is set and 0 elsewhere (the byte values of a torch.bool
+ * tensor).  layout: MXFP4_ROW (mask [rows, ceil(cols/32)] words, 4-byte
+ * aligned) or MXFP4_COL (mask [ceil(rows/32), cols] words).  out: rows * cols
+ * bytes, any alignment, must not overlap mask.
+ */
+mxfp4_status_t mxfp4_mask_to_bool(int32_t layout, int64_t rows, int64_t cols,
+                                  const uint32_t *mask, uint8_t *out,
+                                  void *stream);
+
+/*
  * Real quantization to the packed MXFP4 form (the sglang page's
  * "float4_e2m1fn_x2": two FP4 codes per byte), row-wise blocks.
  *   codes  [rows, ceil(cols/2)] bytes: element 2t in the low nibble, 2t+1 in

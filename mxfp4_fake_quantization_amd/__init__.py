@@ -38,6 +38,7 @@ __all__ = [
     "ROW", "COL", "GROUPED", "FLOOR", "AMCT",
     "mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
     "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant",
+    "mxfp4_mask_to_bool", "mxfp4_saturation_mask",
     "mxfp4_last_error", "mxfp4_version", "library_path",
     "row_mask_shape", "col_mask_shape", "grouped_mask_rows_max", "grouped_scale_rows_max",
     "kmajor_k_blocks",
@@ -80,6 +81,7 @@ def _load():
         dp = ctypes.POINTER(_Desc)
         lib.mxfp4_qdq_fwd.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.mxfp4_ste_bwd.argtypes = [dp, i32, vp, vp, vp, vp, i32, i32, vp]
+        lib.mxfp4_mask_to_bool.argtypes = [i32, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
         lib.mxfp4_quant_pack.argtypes = [dp, vp, vp, vp, vp, vp, vp]
         lib.mxfp4_grouped_qdq.argtypes = [dp, vp, vp, i32, i32, vp, vp, vp, vp]
         lib.mxfp4_quant_pack_kmajor.argtypes = [dp, vp, vp, i32, i32, ctypes.c_int64, vp, vp, vp]
@@ -92,7 +94,7 @@ def _load():
                                              i64, vp]
         for f in ("mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
                   "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant", "mxfp4_version",
-                  "mxfp4_grouped_matmul", "mxfp8_quant_kmajor"):
+                  "mxfp4_grouped_matmul", "mxfp8_quant_kmajor", "mxfp4_mask_to_bool"):
             getattr(lib, f).restype = ctypes.c_int32
         lib.mxfp4_last_error.restype = ctypes.c_char_p
         lib.mxfp4_last_error.argtypes = []
@@ -153,6 +155,8 @@ def _ptr(t, kind=None):
         raise ValueError(f"scales / codes are uint8 tensors, got {t.dtype}")
     if kind == "i64" and t.dtype != torch.int64:
         raise ValueError(f"group_list is an int64 tensor, got {t.dtype}")
+    if kind == "bool" and t.dtype != torch.bool:
+        raise ValueError(f"the expanded mask is a bool tensor, got {t.dtype}")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -256,6 +260,41 @@ def mxfp4_ste_bwd(grad_out, mask, grad_in, layout=ROW, block=32, group_list=None
                                _ptr(grad_in), _ptr(group_list, "i64"), n_groups,
                                int(group_list_type), _stream())
     _check(st, "mxfp4_ste_bwd")
+
+
+def mxfp4_mask_to_bool(mask, rows: int, cols: int, layout=ROW, out=None):
+    """A ROW or COL saturation bitmap as a bool tensor [rows, cols] (true where
+    the forward clipped); ``out`` (bool, contiguous) is filled when given."""
+    rows, cols = int(rows), int(cols)
+    if layout == ROW:
+        _need(mask, rows * -(-cols // 32), "mask")
+    elif layout == COL:
+        _need(mask, -(-rows // 32) * cols, "mask")
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.bool, device=mask.device)
+    _need(out, rows * cols, "out")
+    st = _load().mxfp4_mask_to_bool(int(layout), rows, cols, _ptr(mask, "mask"), _ptr(out, "bool"),
+                                    _stream())
+    _check(st, "mxfp4_mask_to_bool")
+    return out
+
+
+def mxfp4_saturation_mask(x, block=32, rule="floor", scale_factor=6.0, axis=ROW):
+    """The pages' saturation mask: a bool tensor of x's shape, true where
+    |x| > 6 * 2^k of the element's block (blocks along the last dimension for
+    ROW, along the first of the flattened 2-D view for COL).  One forward pass
+    writes the bitmap, one more expands it."""
+    rows, cols = _shape2d(x)
+    if axis == ROW:
+        mask = torch.empty(row_mask_shape(rows, cols), dtype=torch.int32, device=x.device)
+        mxfp4_qdq_fwd(x, ROW, mask_row=mask, block=block, rule=rule, scale_factor=scale_factor)
+    elif axis == COL:
+        mask = torch.empty(col_mask_shape(rows, cols), dtype=torch.int32, device=x.device)
+        mxfp4_qdq_fwd(x, COL, mask_col=mask, block=block, rule=rule, scale_factor=scale_factor)
+    else:
+        raise ValueError(f"axis must be ROW or COL, got {axis}")
+    out = torch.empty(x.shape, dtype=torch.bool, device=x.device)
+    return mxfp4_mask_to_bool(mask, rows, cols, axis, out=out)
 
 
 def mxfp4_quant_pack(x, codes, scales, y=None, mask=None, block=32, rule="floor",

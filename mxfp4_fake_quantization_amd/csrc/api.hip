@@ -152,6 +152,21 @@ mxfp4_status_t mxfp4_ste_bwd(const mxfp4_desc_t *desc, int32_t layout, const voi
   return hip_status(mxfp4::launch_ste_bwd(L, static_cast<hipStream_t>(stream)), "STE backward launch");
 }
 
+mxfp4_status_t mxfp4_mask_to_bool(int32_t layout, int64_t rows, int64_t cols, const uint32_t *mask,
+                                  uint8_t *out, void *stream) {
+  if (layout != MXFP4_ROW && layout != MXFP4_COL)
+    return fail(MXFP4_EINVAL, "layout %d is not MXFP4_ROW or MXFP4_COL", layout);
+  if (rows < 0 || cols < 0) return fail(MXFP4_EINVAL, "negative shape %lld x %lld", (long long)rows,
+                                        (long long)cols);
+  if (cols > 0 && rows > INT64_MAX / 32 / cols) return fail(MXFP4_EINVAL, "rows * cols overflows");
+  MXFP4_TRY(check_ptr(mask, 4, "mask"));
+  if (!out) return fail(MXFP4_EINVAL, "out is NULL");
+  if ((const void *)mask == (const void *)out) return fail(MXFP4_EINVAL, "out aliases mask");
+  if (rows * cols == 0) return ok();
+  return hip_status(mxfp4::launch_mask_bool(layout, rows, cols, mask, out, static_cast<hipStream_t>(stream)),
+                    "mask expansion launch");
+}
+
 mxfp4_status_t mxfp4_quant_pack(const mxfp4_desc_t *desc, const void *x, uint8_t *codes,
                                 uint8_t *scales, void *y_opt, uint32_t *mask_opt, void *stream) {
   int64_t n;
@@ -378,6 +393,6 @@ mxfp4_status_t mxfp8_quant_kmajor(const mxfp4_desc_t *desc, int32_t fmt, const v
 
 const char *mxfp4_last_error(void) { return g_last_error.c_str(); }
 
-int32_t mxfp4_version(void) { return 103; }
+int32_t mxfp4_version(void) { return 104; }
 
 }  // extern "C"

@@ -50,6 +50,9 @@ struct SteLaunch {
   int num_groups, list_type;
 };
 hipError_t launch_ste_bwd(const SteLaunch &L, hipStream_t stream);
+// ROW / COL saturation bitmap -> one 0/1 byte per element (layout 1 or 2).
+hipError_t launch_mask_bool(int layout, int64_t rows, int64_t cols, const uint32_t *mask, uint8_t *out,
+                            hipStream_t stream);
 
 
 // K-major packed form of column-wise / grouped blocks.

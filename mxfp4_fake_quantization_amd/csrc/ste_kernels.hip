@@ -310,6 +310,43 @@ hipError_t launch_col(const SteLaunch &L, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Saturation bitmap (ROW or COL layout) -> one byte per element, 1 where
+// the bit is set and 0 elsewhere, in x's row-major order: the pages' bool
+// mask.  A lane writes 16 consecutive bytes of the flat output (one 16-byte
+// store when the output is 16-byte aligned and the 16 bytes are in range).
+constexpr int kBoolThreads = 256;
+
+template <int LAYOUT>
+__global__ void __launch_bounds__(kBoolThreads)
+    mask_bool_kernel(const uint32_t *__restrict__ mask, uint8_t *__restrict__ out, int64_t cols,
+                     int64_t words_per_row, int64_t n, bool vec) {
+  const int64_t f0 = ((int64_t)blockIdx.x * kBoolThreads + threadIdx.x) * 16;
+  if (f0 >= n) return;
+  int64_t r = f0 / cols, c = f0 - r * cols;
+  const int64_t left = n - f0;
+  uint32_t b[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j < left) {
+      const uint32_t w = LAYOUT == 1 ? mask[r * words_per_row + (c >> 5)] : mask[(r >> 5) * cols + c];
+      const uint32_t bit = (w >> (LAYOUT == 1 ? (c & 31) : (r & 31))) & 1u;
+      b[j >> 2] |= bit << (8 * (j & 3));
+      if (++c == cols) {
+        c = 0;
+        ++r;
+      }
+    }
+  }
+  if (vec && left >= 16) {
+    const u32x4 v = {b[0], b[1], b[2], b[3]};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(out + f0));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < left) out[f0 + j] = (uint8_t)(b[j >> 2] >> (8 * (j & 3)));
+  }
+}
+
 }  // namespace
 
 hipError_t launch_ste_bwd(const SteLaunch &L, hipStream_t st) {
@@ -317,6 +354,23 @@ hipError_t launch_ste_bwd(const SteLaunch &L, hipStream_t st) {
   if (L.mask == nullptr || L.layout == 1)
     return L.dtype == kBF16 ? launch_row<kBF16>(L, st) : launch_row<kF32>(L, st);
   return L.dtype == kBF16 ? launch_col<kBF16>(L, st) : launch_col<kF32>(L, st);
+}
+
+hipError_t launch_mask_bool(int layout, int64_t rows, int64_t cols, const uint32_t *mask, uint8_t *out,
+                            hipStream_t st) {
+  const int64_t n = rows * cols;
+  const int64_t nwg = (n + 16 * kBoolThreads - 1) / (16 * kBoolThreads);
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const bool vec = (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+  const int64_t wpr = (cols + 31) / 32;
+  if (layout == 1)
+    hipLaunchKernelGGL((mask_bool_kernel<1>), dim3((unsigned)nwg), dim3(kBoolThreads), 0, st, mask, out, cols, wpr,
+                       n, vec);
+  else
+    hipLaunchKernelGGL((mask_bool_kernel<2>), dim3((unsigned)nwg), dim3(kBoolThreads), 0, st, mask, out, cols, wpr,
+                       n, vec);
+  return hipGetLastError();
 }
 
 }  // namespace mxfp4

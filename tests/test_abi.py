@@ -48,6 +48,7 @@ def lib():
     op = ctypes.POINTER(Operand)
     L.mxfp4_grouped_matmul.argtypes = [i32, i64, i64, i64, op, op, vp, i32, i32, i64, i32, vp, i64, vp]
     L.mxfp8_quant_kmajor.argtypes = [dp, i32, vp, vp, i32, i32, i64, vp, vp, vp]
+    L.mxfp4_mask_to_bool.argtypes = [i32, i64, i64, vp, vp, vp]
     L.mxfp4_last_error.restype = ctypes.c_char_p
     return L
 
@@ -61,14 +62,14 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
               "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant", "mxfp4_grouped_matmul", "mxfp8_quant_kmajor",
-              "mxfp4_last_error", "mxfp4_version"):
+              "mxfp4_mask_to_bool", "mxfp4_last_error", "mxfp4_version"):
         assert n in names
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mxfp4_version() == 103
+    assert lib.mxfp4_version() == 104
 
 
 def d(dtype=BF16, block=32, rule=0, rows=64, cols=64, sf=6.0, r0=0, r1=0):
@@ -131,6 +132,21 @@ def test_ste_bwd_validation(lib):
     assert g(COL, P(), P(FAKE + 4), P(FAKE + 128), None, 0, 1, None) == EINVAL  # col bitmap 16B
     D.block = 64
     assert g(ROW, P(), None, P(FAKE + 128), None, 0, 1, None) == EUNSUP
+
+
+def test_mask_to_bool_validation(lib):
+    m = lib.mxfp4_mask_to_bool
+    assert m(ROW, 0, 64, P(), P(FAKE + 1), None) == OK               # empty: nothing launched
+    assert m(COL, 64, 0, P(), P(FAKE + 1), None) == OK
+    assert m(GROUPED, 4, 4, P(), P(FAKE + 64), None) == EINVAL       # GROUPED needs its group list
+    assert m(3, 4, 4, P(), P(FAKE + 64), None) == EINVAL
+    assert m(ROW, -1, 4, P(), P(FAKE + 64), None) == EINVAL
+    assert m(ROW, 1 << 40, 1 << 30, P(), P(FAKE + 64), None) == EINVAL   # overflow
+    assert m(ROW, 4, 4, None, P(FAKE + 64), None) == EINVAL
+    assert m(ROW, 4, 4, P(FAKE + 2), P(FAKE + 64), None) == EINVAL   # misaligned bitmap
+    assert m(ROW, 4, 4, P(), None, None) == EINVAL
+    assert m(ROW, 4, 4, P(), P(FAKE), None) == EINVAL                # out aliases mask
+    assert b"alias" in lib.mxfp4_last_error()
 
 
 def test_pack_and_grouped_validation(lib):
