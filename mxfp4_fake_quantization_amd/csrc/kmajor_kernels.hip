@@ -11,16 +11,17 @@
 // or 64-byte (block 128) pieces along K.  K position t*block + o is x row
 // start_t + o of block-row t while o < len_t, else a padding code 0.
 //
-// Tiling: a workgroup (8 waves) owns 256 K positions x 128 columns.  Lane
-// (cg, rq), with cg = lane & 15 and rq = 4*wave + (lane >> 4), holds K
-// positions 8rq .. 8rq+7 (8 consecutive rows of x, inside one block-row) of
-// columns 8cg .. 8cg+7, loaded as one 16-byte bf16 piece per row, so 16 lanes
-// read a 256-byte row segment.  Then
+// Tiling: a workgroup (8 waves) owns 256 K positions x 16 CPL columns, CPL
+// = 8 columns per lane for bf16 and 4 for fp32 (one 16-byte piece per row
+// either way).  Lane (cg, rq), with cg = lane & 15 and rq = 4*wave + (lane >>
+// 4), holds K positions 8rq .. 8rq+7 (8 consecutive rows of x, inside one
+// block-row) of columns CPL*cg .. CPL*cg + CPL-1, loaded as one 16-byte piece
+// per row, so 16 lanes read a 256-byte row segment.  Then
 //   - a 32-row block is one wave (lanes at distance 16): column max by
 //     ds_swizzle xor 16 and ds_bpermute xor 32; a 128-row block spans 4 waves,
 //     which combine their maxima through LDS;
 //   - the 8 nibbles of one column in one lane form one 32-bit word at byte
-//     4*rq of the column's 128-byte line of codes; the words are staged in LDS
+//     4*rq of the column's 128-byte line of codes (CPL words per lane); the words are staged in LDS
 //     and each line of codes_t is written whole, by 8 lanes with 16-byte
 //     stores.
 //
@@ -41,10 +42,36 @@ constexpr int kKTile = 256;      // K positions per workgroup
 // forms one (block 128 measured equal or slower with two).
 template <int DT, int B>
 struct KmShape {
+  static constexpr int cpl = DT == kBF16 ? 8 : 4;     // columns per lane (16 bytes of a row)
+  static constexpr int lcpl = DT == kBF16 ? 3 : 2;    // log2(cpl)
   static constexpr int halves = DT == kBF16 && B == 32 ? 2 : 1;
-  static constexpr int ctile = 128 * halves;   // columns per workgroup
+  static constexpr int chalf = 16 * cpl;              // columns per half
+  static constexpr int ctile = chalf * halves;        // columns per workgroup
   static constexpr int threads = 512 * halves;
 };
+// A lane's row piece: 16 bytes = 4 words (two bf16 columns or one fp32
+// column per word).
+constexpr int kKmNW = 4;
+
+// Columns c0 .. c0 + n - 1 of one row (n <= CPL) into 4 words; zeros past n.
+// VEC (16-byte aligned pieces, whole column groups): n is CPL or 0.
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_row16(uint32_t (&w)[kKmNW], const uint8_t *p, int n) {
+  constexpr int CPL = DT == kBF16 ? 8 : 4;
+  if (VEC && n == CPL) {
+    const uint4 v = ld16(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < kKmNW; ++k) w[k] = 0;
+  if (!VEC) {
+    for (int j = 0; j < n; ++j) {
+      if (DT == kBF16) w[j >> 1] |= (uint32_t)reinterpret_cast<const uint16_t *>(p)[j] << (16 * (j & 1));
+      else w[j] = reinterpret_cast<const uint32_t *>(p)[j];
+    }
+  }
+}
 // Minimum waves per SIMD requested from the compiler: 8 (64 VGPRs, four
 // 8-wave workgroups per CU) for bf16 FLOOR, whose common path fits in 64
 // registers (only the generic snap of tiny blocks spills); 4 (128 VGPRs, two
@@ -99,11 +126,11 @@ __device__ __noinline__ uint32_t slow_column_f32(uint32_t a0, uint32_t a1, uint3
   return v;
 }
 
-// The lane's 8 code words (one per column, K position 8rq + i in bits
-// 4i..4i+3).  SLOW = true only when some lane of the wave holds a column that
-// needs the generic snap.
+// The lane's code words (one per column: 8 for bf16, 4 for fp32; K position
+// 8rq + i in bits 4i..4i+3).  SLOW = true only when some lane of the wave
+// holds a column that needs the generic snap.
 template <int DT, int RULE, bool SLOW>
-__device__ __forceinline__ void code_words(const uint32_t (&w)[8][PieceT<DT>::NW], const uint32_t *pt,
+__device__ __forceinline__ void code_words(const uint32_t (&w)[8][kKmNW], const uint32_t *pt,
                                            const uint32_t *pz, const uint32_t *pe, const uint32_t *cm,
                                            const BlockParams *cbp, uint32_t (&out)[8]) {
   if (DT == kBF16) {
@@ -131,7 +158,7 @@ __device__ __forceinline__ void code_words(const uint32_t (&w)[8][PieceT<DT>::NW
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 4; ++k) {
       BlockParams q = cbp[k];
       q.slow = false;
       uint32_t v = 0;
@@ -184,9 +211,10 @@ __device__ __forceinline__ KmTile km_tile(const KmArgs &A, int64_t tile, int wav
     const int64_t rem = A.rows - start;
     len = rem <= 0 ? 0 : (rem < B ? rem : B);
   }
-  T.c0 = T.col0 + 128 * chalf + 8 * cg;
+  constexpr int CPL = KmShape<DT, B>::cpl;
+  T.c0 = T.col0 + KmShape<DT, B>::chalf * chalf + CPL * cg;
   const int64_t crem = A.cols - T.c0;
-  T.ncol = crem >= 8 ? 8 : (crem > 0 ? (int)crem : 0);
+  T.ncol = crem >= CPL ? CPL : (crem > 0 ? (int)crem : 0);
   const int64_t rrem = len - T.o0;
   T.nrow = rrem >= 8 ? 8 : (rrem > 0 ? (int)rrem : 0);
   T.live = len > 0;
@@ -195,18 +223,19 @@ __device__ __forceinline__ KmTile km_tile(const KmArgs &A, int64_t tile, int wav
   return T;
 }
 
-// LDS staging of one tile's outputs.  The 16-byte chunk q (K words 4q ..
-// 4q + 3) of column c's row sits at chunk slot q ^ ((c >> 3) & 7) of the row,
-// and inside the chunk word i sits at i ^ (2 * ((c >> 6) & 1)).  A staging
+// LDS staging of one tile's outputs.  With g = c >> LC the column group of
+// column c (LC = log2 of the columns per lane), the 16-byte chunk q (K words
+// 4q .. 4q + 3) of column c's row sits at chunk slot q ^ (g & 7) of the row,
+// and inside the chunk word i sits at i ^ (2 * ((g >> 3) & 1)).  A staging
 // write stores one word per lane for lanes (cg = column group 0..15, K word
 // 4 * wave + rql): the XOR with the group's low three bits spreads the eight
 // groups of a half-wave over the eight chunk slots, the XOR with its fourth
 // bit puts groups cg and cg + 8 on different words of the chunk, so each
 // half-wave's 32 words fall in 32 different banks.  The 8 lanes that read
 // one column's row (ds_read_b128) cover its 32 words, so all banks, and swap
-// the halves back where bit 6 of the column is set.  Scale bytes are staged
-// block-row major ([block-row][column]): a lane writes its eight columns'
-// bytes with one 8-byte store, 16 lanes 128 consecutive bytes.
+// the halves back where bit 3 of the group is set.  Scale bytes are staged
+// block-row major ([block-row][column]): a lane writes its columns' bytes
+// with one 8-byte (bf16) or 4-byte (fp32) store, 16 lanes consecutive bytes.
 template <int CT>
 struct KmStage {
   uint32_t codes[CT][kKTile / 8] __attribute__((aligned(16)));
@@ -214,9 +243,11 @@ struct KmStage {
   uint8_t live[kKTile / 32];
 };
 
-__device__ __forceinline__ int km_chunk(int c, int q) { return c * (kKTile / 8) + 4 * (q ^ ((c >> 3) & 7)); }
+template <int LC>
+__device__ __forceinline__ int km_chunk(int c, int q) { return c * (kKTile / 8) + 4 * (q ^ ((c >> LC) & 7)); }
+template <int LC>
 __device__ __forceinline__ int km_slot(int c, int kw) {
-  return km_chunk(c, kw >> 2) + ((kw & 3) ^ (((c >> 6) & 1) << 1));
+  return km_chunk<LC>(c, kw >> 2) + ((kw & 3) ^ (((c >> (LC + 3)) & 1) << 1));
 }
 
 // One workgroup per tile: load, column maxima, nibbles; then the tile's
@@ -229,8 +260,9 @@ __global__ __launch_bounds__((KmShape<DT, B>::threads),
 void kmajor_pack_kernel(KmArgs A) {
   constexpr int kCTile = KmShape<DT, B>::ctile;
   constexpr int kKmThreads = KmShape<DT, B>::threads;
-  constexpr int NW = PieceT<DT>::NW;
+  constexpr int NW = kKmNW;
   constexpr int ES = PieceT<DT>::ES;
+  constexpr int CPL = KmShape<DT, B>::cpl, LC = KmShape<DT, B>::lcpl;
   constexpr uint32_t ABS = DT == kBF16 ? 0x7FFF7FFFu : 0x7FFFFFFFu;
   constexpr int NBT_TILE = kKTile / B;  // block-rows per tile
   __shared__ uint32_t s_cm[kKmThreads / 64][NW][16];  // [wave][word][column group]: no bank conflicts
@@ -253,10 +285,10 @@ void kmajor_pack_kernel(KmArgs A) {
   uint32_t w[8][NW];
   if (T.full) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) load_piece<DT, true>(w[i], T.src + i * rstride, 8);
+    for (int i = 0; i < 8; ++i) load_row16<DT, true>(w[i], T.src + i * rstride, CPL);
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) load_piece<DT, VEC>(w[i], T.src + i * rstride, i < T.nrow ? T.ncol : 0);
+    for (int i = 0; i < 8; ++i) load_row16<DT, VEC>(w[i], T.src + i * rstride, i < T.nrow ? T.ncol : 0);
   }
 
   // ---- column maxima (padding rows read as +0 and never raise them) -------
@@ -287,7 +319,7 @@ void kmajor_pack_kernel(KmArgs A) {
 
   // ---- per-column parameters ---------------------------------------------
   uint32_t pt[NW], pz[NW], pe[NW];
-  BlockParams cbp[DT == kF32 ? 8 : 1];
+  BlockParams cbp[DT == kF32 ? 4 : 1];
   bool slow_any = false;
 #pragma unroll
   for (int k = 0; k < NW; ++k) {
@@ -312,13 +344,12 @@ void kmajor_pack_kernel(KmArgs A) {
 
   // the E8M0 bytes of the lane's 8 columns, in column order (packed before
   // the code words so the per-column bytes need no registers meanwhile)
-  uint32_t sc_lo, sc_hi;
+  uint32_t sc_lo, sc_hi = 0;
   if (DT == kBF16) {
     sc_lo = perm_b32(pe[1], pe[0], 0x06040200u);  // bytes 0 and 2 of each packed word
     sc_hi = perm_b32(pe[3], pe[2], 0x06040200u);
   } else {
     sc_lo = pe[0] | (pe[1] << 8) | (pe[2] << 16) | (pe[3] << 24);
-    sc_hi = pe[4] | (pe[5] << 8) | (pe[6] << 16) | (pe[7] << 24);
   }
 
   uint32_t cw[8];
@@ -329,9 +360,12 @@ void kmajor_pack_kernel(KmArgs A) {
   const int kw = 4 * kwave + rql;  // K word of the lane inside the tile
   const int bl = (8 * kw) / B;    // block-row of the lane inside the tile
 #pragma unroll
-  for (int j = 0; j < 8; ++j) (&st.codes[0][0])[km_slot(128 * chalf + 8 * cg + j, kw)] = cw[j];
+  for (int j = 0; j < CPL; ++j)
+    (&st.codes[0][0])[km_slot<LC>(KmShape<DT, B>::chalf * chalf + CPL * cg + j, kw)] = cw[j];
   if (T.o0 == 0) {
-    *reinterpret_cast<uint2 *>(&st.scales[bl][128 * chalf + 8 * cg]) = make_uint2(sc_lo, sc_hi);
+    uint8_t *sp = &st.scales[bl][KmShape<DT, B>::chalf * chalf + CPL * cg];
+    if (DT == kBF16) *reinterpret_cast<uint2 *>(sp) = make_uint2(sc_lo, sc_hi);
+    else *reinterpret_cast<uint32_t *>(sp) = sc_lo;
     if (cg == 0) st.live[bl] = T.live;
   }
   __syncthreads();
@@ -347,8 +381,8 @@ void kmajor_pack_kernel(KmArgs A) {
     const int c = chunk >> 3, q = chunk & 7;
     const int64_t col = T.col0 + c;
     if (col < A.cols && st.live[(32 * q) / B]) {
-      uint4 v = *reinterpret_cast<const uint4 *>(&(&st.codes[0][0])[km_chunk(c, q)]);
-      if ((c >> 6) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+      uint4 v = *reinterpret_cast<const uint4 *>(&(&st.codes[0][0])[km_chunk<LC>(c, q)]);
+      if ((c >> (LC + 3)) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
       st16(A.codes + col * A.ldk + kbyte + 16 * q, v);
     }
   }
@@ -542,7 +576,7 @@ hipError_t launch_kmajor_pack(const KmLaunch &L, hipStream_t st) {
   a.ntiles = nkt * a.nct;
   if (a.ntiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (a.ntiles == 0) return hipSuccess;
-  const bool vec = L.cols % 8 == 0;
+  const bool vec = L.cols % (L.dtype == kBF16 ? 8 : 4) == 0;  // 16-byte aligned row pieces
   if (L.dtype == kBF16)
     return L.block == 32 ? km_rule<kBF16, 32>(L.rule, grouped, vec, a, st)
                          : km_rule<kBF16, 128>(L.rule, grouped, vec, a, st);

@@ -69,3 +69,23 @@ def test_bf16_common_paths_do_not_spill(asm, name):
     assert found, f"no bf16 kernels matched in {name}"
     spilled = {k: v for k, v in found.items() if v}
     assert not spilled, f"scratch accesses on the common path: {spilled}"
+
+
+def test_fp32_kmajor_pack_touches_no_scratch(asm):
+    """The fp32 K-major pack holds 8 rows x 4 columns per lane (one 16-byte
+    piece per row, as bf16 does with 8 columns): no scratch anywhere, the
+    generic snap included (with 8 fp32 columns per lane it spilled)."""
+    out, cur, n = {}, None, 0
+    for line in asm["kmajor_kernels"].split("\n"):
+        m = re.match(r"^(_Z\S+):", line)
+        if m:
+            if cur:
+                out[cur] = n
+            cur, n = m.group(1), 0
+        elif cur and "scratch_" in line:
+            n += 1
+    if cur:
+        out[cur] = n
+    fp32 = {k: v for k, v in out.items() if re.search(r"kmajor_pack_kernelILi0E", k)}
+    assert len(fp32) == 16, sorted(fp32)
+    assert not any(fp32.values()), {k: v for k, v in fp32.items() if v}
