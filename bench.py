@@ -154,6 +154,21 @@ class Probe:
         self.lib.probe_stream.restype = ctypes.c_int
         self.lib.probe_wall_clock_khz.argtypes = [ctypes.c_int]
         self.lib.probe_wall_clock_khz.restype = ctypes.c_int
+        self.lib.probe_cu_rate.argtypes = [ctypes.c_int, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                           vp, vp]
+        self.lib.probe_cu_rate.restype = ctypes.c_int
+
+    def cu_rate(self, kind, buf, win, nwin, passes, nwg, out, stream):
+        vp = ctypes.c_void_p
+        args = (kind, vp(buf.data_ptr()) if buf is not None else None, win, nwin, passes, nwg,
+                vp(out.data_ptr()), stream)
+        fn = self.lib.probe_cu_rate
+
+        def run():
+            st = fn(*args)
+            if st != 0:
+                raise RuntimeError(f"probe_cu_rate failed with hip error {st}")
+        return run
 
     def call(self, kind, src, dst, side, npieces, threads, stream, stamps=None, per_lane=1):
         vp = ctypes.c_void_p
@@ -786,25 +801,40 @@ PROFILE_LAUNCHES = 10
 PROFILE_WARMUP = 40
 
 
-def profile_run(M, lib, W, torch, stream, probe, manifest_path):
+def profile_run(M, lib, W, torch, stream, probe, manifest_path, which="streaming"):
     """A fixed sequence of launches for rocprofv3: for every workload
     PROFILE_WARMUP launches (freshly allocated buffers run the first few
     dozen launches slower), then PROFILE_LAUNCHES measured ones, in the order
     written to the manifest (label, kernel name fragment, launches,
-    algorithmic bytes per launch), so that the summary can name the workload
-    of every dispatch and leave the warm-up out."""
+    algorithmic bytes per launch, flops for the matmul), so that the summary
+    can name the workload of every dispatch and leave the warm-up out.
+    which: 'streaming' (the quantization kernels), 'gemm' (the grouped
+    matmul's three layouts on the MoE layer) or 'all'; every set starts with
+    the calibration copy."""
     entries = []
     vp = ctypes.c_void_p
 
-    def run(label, frag, calls, rd, wr, nelem, per_call=1):
+    def run(label, frag, calls, rd, wr, nelem, per_call=1, flops=None, setup=False):
+        if setup:  # each call once, listed (and left out of the tables) so that dispatches stay aligned
+            torch.cuda.synchronize()
+            for c in calls:
+                c()
+            torch.cuda.synchronize()
+            entries.append({"label": label, "kernel": frag, "launches": len(calls) * per_call, "alg_bytes": 0,
+                            "alg_read": 0, "alg_write": 0, "elements": 0, "skip": True,
+                            "kernels_per_call": per_call})
+            return
         for phase, n in (("warm-up", PROFILE_WARMUP), ("measured", PROFILE_LAUNCHES)):
             torch.cuda.synchronize()
             for i in range(n):
                 calls[i % len(calls)]()
             torch.cuda.synchronize()
-            entries.append({"label": label, "kernel": frag, "launches": n * per_call, "alg_bytes": rd + wr,
-                            "alg_read": rd, "alg_write": wr, "elements": nelem, "skip": phase == "warm-up",
-                            "kernels_per_call": per_call})
+            e = {"label": label, "kernel": frag, "launches": n * per_call, "alg_bytes": rd + wr,
+                 "alg_read": rd, "alg_write": wr, "elements": nelem, "skip": phase == "warm-up",
+                 "kernels_per_call": per_call}
+            if flops:
+                e["flops"] = flops
+            entries.append(e)
 
     # calibration of the traffic counters: a plain copy of 512 MiB
     ca = [torch.empty(256 << 20, dtype=torch.int16, device="cuda") for _ in range(2)]
@@ -814,6 +844,70 @@ def profile_run(M, lib, W, torch, stream, probe, manifest_path):
         [probe.call(PROBE_COPY, ca[i], cb[i], None, cn // 16, 256, stream) for i in range(2)], cn, cn, cn // 2)
     del ca, cb
     torch.cuda.empty_cache()
+    if which in ("streaming", "all"):
+        profile_streaming(M, lib, W, torch, stream, probe, run)
+    if which in ("gemm", "all"):
+        profile_gemm(M, W, torch, run)
+    with open(manifest_path, "w") as f:
+        json.dump({"launches_per_workload": PROFILE_LAUNCHES, "warmup_per_workload": PROFILE_WARMUP,
+                   "entries": entries}, f, indent=1)
+    print(json.dumps({"profile_run": manifest_path, "workloads": len(entries) // 2}), flush=True)
+
+
+def profile_gemm(M, W, torch, run):
+    """The grouped matmul on the MoE layer (tokens 32768 x hidden 7168, 8
+    experts of width 2048): NN forward, NT input gradient, TN weight gradient,
+    with the operands of bench_gemm.  Algorithmic bytes: every operand byte
+    (codes and scales) read once, the output written once."""
+    xg, counts = W.moe_grouped()
+    gl = torch.from_numpy(counts).cuda()
+    R, K = xg.shape
+    x = bf16_dev(torch, xg)
+    q8 = [torch.empty((R, K), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    s8 = [torch.empty((R, K // 32), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    run("setup: MXFP8 of the tokens", "mxfp8_rows_kernel",
+        [lambda i=i: M.mxfp8_quant(x, q8[i], s8[i]) for i in range(2)], 0, 0, 0, setup=True)
+    del x
+    wt = W.moe_expert_weights()
+    G, _, N = wt.shape
+    bw = torch.empty((G, N, K // 2), dtype=torch.uint8, device="cuda")
+    sw = torch.empty((G, N, K // 32), dtype=torch.uint8, device="cuda")
+    run("setup: K-major MXFP4 expert weights", "kmajor_pack_kernel",
+        [lambda g=g: M.mxfp4_quant_pack_kmajor(bf16_dev(torch, wt[g]), bw[g], sw[g], block=32) for g in range(G)],
+        0, 0, 0, setup=True)
+    flops = 2.0 * R * K * N
+    cs = [torch.empty((R, N), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    run("grouped matmul NN forward: MXFP8 tokens x K-major MXFP4 experts", "mxgemm_kernel",
+        [lambda i=i: M.mxfp4_grouped_matmul(q8[i], s8[i], bw, sw, cs[i], group_list=gl, group_list_type=1)
+         for i in range(2)], R * K * (1 + 1 / 32) + G * N * K * (0.5 + 1 / 32), R * N * 2, R * K, flops=flops)
+    del cs, q8, s8
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    dq = torch.randint(0, 256, (R, N), dtype=torch.uint8, device="cuda", generator=gen) & 0xBF
+    ds = torch.full((R, N // 32), 120, dtype=torch.uint8, device="cuda")
+    bt = torch.randint(0, 256, (G, K, N // 2), dtype=torch.uint8, device="cuda", generator=gen)
+    st = torch.full((G, K, N // 32), 120, dtype=torch.uint8, device="cuda")
+    cx = [torch.empty((R, K), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    run("grouped matmul NT input gradient: MXFP8 grad x row-packed MXFP4 experts", "mxgemm_kernel",
+        [lambda i=i: M.mxfp4_grouped_matmul(dq, ds, bt, st, cx[i], group_list=gl, group_list_type=1)
+         for i in range(2)], R * N * (1 + 1 / 32) + G * K * N * (0.5 + 1 / 32), R * K * 2, R * K, flops=flops)
+    del cx, bt, st, dq, ds
+    nbt8 = int(sum(-(-int(c) // 32) for c in counts))
+    xa = torch.randint(0, 256, (K, nbt8 * 32), dtype=torch.uint8, device="cuda", generator=gen) & 0xBF
+    xs_ = torch.full((K, nbt8), 120, dtype=torch.uint8, device="cuda")
+    yb = torch.randint(0, 256, (N, nbt8 * 32), dtype=torch.uint8, device="cuda", generator=gen) & 0xBF
+    ys_ = torch.full((N, nbt8), 120, dtype=torch.uint8, device="cuda")
+    cw = [torch.empty((G, K, N), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    run("grouped matmul TN weight gradient: K-major MXFP8 tokens x K-major MXFP8 grad", "mxgemm_kernel",
+        [lambda i=i: M.mxfp4_grouped_matmul(xa, xs_, yb, ys_, cw[i], K=R, group_list=gl, group_list_type=1,
+                                            group_type=M.GROUP_K, b_fmt="e4m3", k_blocks=nbt8) for i in range(2)],
+        (K + N) * nbt8 * 33, G * K * N * 2, R * K, flops=flops)
+    del cw, xa, yb
+    torch.cuda.empty_cache()
+
+
+def profile_streaming(M, lib, W, torch, stream, probe, run):
+    """The quantization kernels of every workload (profile_run's default set)."""
+    vp = ctypes.c_void_p
     wk = build_weight4k(M, lib, W, torch, stream, 8)
     n = wk["rows"] * wk["cols"]
     run("weight_4k forward (y + bitmap)", "row_fwd_kernel", wk["fwd"], n * 2, n * 2.125, n)
@@ -882,10 +976,6 @@ def profile_run(M, lib, W, torch, stream, probe, manifest_path):
             n * 2, n * (0.5 + 1 / blk), n)
         del pk, xs, codes, scs, kc, ks
         torch.cuda.empty_cache()
-    with open(manifest_path, "w") as f:
-        json.dump({"launches_per_workload": PROFILE_LAUNCHES, "warmup_per_workload": PROFILE_WARMUP,
-                   "entries": entries}, f, indent=1)
-    print(json.dumps({"profile_run": manifest_path, "workloads": len(entries) // 2}), flush=True)
 
 
 def _read_csv(path):
@@ -964,7 +1054,8 @@ def summarize(kind, dirpath, manifest_path, out_md, command):
              "Command (repository root):", "", f"    {command}", ""]
     js = []
     if kind == "trace":
-        lines += ["| Workload | Kernel | Launches | Average us | Min us | Algorithmic MB | GB/s | Fraction of 8 TB/s |",
+        lines += ["| Workload | Kernel | Launches | Average us | Min us | Algorithmic MB | GB/s (matmul: TFLOP/s) "
+                  "| Fraction of peak (8 TB/s; matmul: 5.0 PFLOP/s fp8) |",
                   "|---|---|---|---|---|---|---|---|"]
         for e, chunk in groups:
             kern = "; ".join(sorted({short_name(c[0]) for c in chunk}))
@@ -974,6 +1065,13 @@ def summarize(kind, dirpath, manifest_path, out_md, command):
                 lines.append(f"| {e['label']} | {kern} | {len(chunk)} | {step.mean():.2f} per step "
                              f"({us.mean():.2f} per launch) | {step.min():.2f} per step | — | — | launch-bound |")
                 js.append({"label": e["label"], "kernel": kern, "step_us": float(step.mean())})
+            elif e.get("flops"):
+                tf = e["flops"] / (us.mean() * 1e-6) / 1e12
+                lines.append(f"| {e['label']} | {kern} | {len(chunk)} | {us.mean():.2f} | {us.min():.2f} | "
+                             f"{e['alg_bytes'] / 1e6:.1f} | {tf:.1f} TFLOP/s | {tf / MFMA_FP8_PEAK_TFLOPS:.3f} |")
+                js.append({"label": e["label"], "kernel": kern, "avg_us": float(us.mean()),
+                           "alg_bytes": e["alg_bytes"], "flops": e["flops"], "TFLOPs": tf,
+                           "frac": tf / MFMA_FP8_PEAK_TFLOPS})
             else:
                 g = e["alg_bytes"] / (us.mean() * 1e-6) / 1e9
                 lines.append(f"| {e['label']} | {kern} | {len(chunk)} | {us.mean():.2f} | {us.min():.2f} | "
@@ -1055,6 +1153,43 @@ def short_name(name: str) -> str:
         if ch == "(" and depth == 0:
             return s[:i].strip()
     return s.strip()
+
+
+def cu_probes(torch, stream, probe, out_md, command):
+    """Per-CU rates of the memory paths a tiled matmul uses, one 512-thread
+    workgroup per CU (256 workgroups): 16-byte loads from an L2-resident
+    window and from HBM, and ds_read_b128 / ds_write_b128 in the grouped
+    matmul's LDS patterns.  Writes OUT_MD and a JSON file beside it."""
+    timer = Timer(torch, stream)
+    nwg = 256
+    out = torch.empty((nwg * 512 * 4,), dtype=torch.int32, device="cuda")
+    buf = torch.randint(0, 2 ** 31, (1 << 28,), dtype=torch.int32, device="cuda")   # 1 GiB = 2^26 pieces
+    rows = []
+    cases = [("16-byte loads, 1 MiB window shared by all workgroups (L2-resident)", 0, 65536, 1, 16),
+             ("16-byte loads, 512 KiB window per 8 workgroups (L2-resident)", 0, 32768, 8, 16),
+             ("16-byte loads, 4 MiB per workgroup, 1 GiB in all (HBM)", 0, 262144, 256, 1),
+             ("ds_read_b128, matmul fragment pattern (XOR-swizzled rows)", 1, 0, 0, 2000),
+             ("ds_read_b128, 16 lanes on 256 contiguous bytes", 2, 0, 0, 2000),
+             ("ds_write_b128, matmul staging pattern", 3, 0, 0, 2000)]
+    for label, kind, win, nwin, passes in cases:
+        med, _ = timer([probe.cu_rate(kind, buf if kind == 0 else None, win, nwin, passes, nwg, out, stream)],
+                       reps=5, warm=2)
+        nbytes = nwg * win * 16 * passes if kind == 0 else nwg * 512 * 16 * 8 * passes
+        per_cu = nbytes / med / 1e9 / nwg
+        rows.append({"probe": label, "us": med * 1e6, "bytes": nbytes, "B_per_ns_per_CU": per_cu,
+                     "B_per_clock_at_2.4GHz": per_cu / 2.4, "TBps_all_CUs": nbytes / med / 1e12})
+        print(json.dumps(rows[-1]), flush=True)
+    lines = ["# Per-CU rates of loads and LDS accesses (the grouped matmul's memory paths)", "",
+             "MI355X, one 512-thread workgroup per CU (256 workgroups, 96-160 KiB of LDS each), times from HIP "
+             "events over 5 launches.", "", "Command (repository root):", "", f"    {command}", "",
+             "| Probe | us | B/ns per CU | B/clock per CU (2.4 GHz) | TB/s, all CUs |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['probe']} | {r['us']:.1f} | {r['B_per_ns_per_CU']:.1f} | "
+                     f"{r['B_per_clock_at_2.4GHz']:.1f} | {r['TBps_all_CUs']:.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.splitext(out_md)[0] + ".json", "w") as f:
+        json.dump({"command": command, "rows": rows}, f, indent=1)
 
 
 def probe_sweep(M, lib, W, torch, stream, probe, out_path):
@@ -1143,6 +1278,8 @@ def main():
                     help="run only a 512 MiB device copy (rocprofv3 counter calibration)")
     ap.add_argument("--profile-run", metavar="MANIFEST", default=None,
                     help="launch every workload's kernel a fixed number of times and write the manifest")
+    ap.add_argument("--profile-set", choices=("streaming", "gemm", "all"), default="streaming",
+                    help="which kernels --profile-run launches (default: the quantization kernels)")
     ap.add_argument("--summarize", nargs=4, metavar=("KIND", "DIR", "MANIFEST", "OUT_MD"), default=None,
                     help="join a rocprofv3 CSV (KIND trace or pmc) under DIR with the manifest into OUT_MD")
     ap.add_argument("--command", default="", help="the profiling command, recorded by --summarize")
@@ -1150,6 +1287,8 @@ def main():
                     help="write the headline forward's traffic file from a counter summary")
     ap.add_argument("--stamps", metavar="OUT", default=None,
                     help="per-workgroup clocks of the forward-pattern probe at 4096x4096")
+    ap.add_argument("--cu-probes", metavar="OUT_MD", default=None,
+                    help="per-CU rates of L2 / HBM loads and LDS reads / writes (the matmul's memory paths)")
     ap.add_argument("--probe-sweep", metavar="OUT", default=None,
                     help="streaming probes over launch shapes at 4096x4096 and 28672x8192")
     args = ap.parse_args()
@@ -1188,13 +1327,16 @@ def main():
         return
     probe = Probe()
     if args.profile_run:
-        profile_run(M, lib, W, torch, stream, probe, args.profile_run)
+        profile_run(M, lib, W, torch, stream, probe, args.profile_run, args.profile_set)
         return
     if args.stamps:
         stamps_run(M, lib, W, torch, stream, probe, args.stamps)
         return
     if args.probe_sweep:
         probe_sweep(M, lib, W, torch, stream, probe, args.probe_sweep)
+        return
+    if args.cu_probes:
+        cu_probes(torch, stream, probe, args.cu_probes, args.command or f"python3 bench.py --cu-probes {args.cu_probes}")
         return
 
     result, wk = bench_headline(M, lib, W, torch, stream, args, probe)

@@ -136,3 +136,100 @@ extern "C" int probe_wall_clock_khz(int device) {
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) != hipSuccess) return -1;
   return khz;
 }
+
+// ---- per-CU rates ------------------------------------------------------------
+// 512-thread workgroups holding 96 KiB (kind 0) or 160 KiB (kinds 1-3) of LDS,
+// so one runs per CU.
+//   kind 0 "load": each workgroup reads `passes` times a window of `win`
+//          16-byte pieces starting at piece (blockIdx.x % nwin) * win, U = 4
+//          loads per lane in flight; one XOR per lane to out.  A window
+//          shared by all workgroups stays in L2 (per-CU rate from L2); a
+//          window per workgroup over a large buffer streams from HBM.
+//   kind 1 "lds_read_swizzled": per wave `passes` x 8 ds_read_b128 in the
+//          grouped matmul's fragment pattern (row l % 32 of a 32-row tile,
+//          XOR-swizzled 16-byte slot), rotating over 16 KiB windows.
+//   kind 2 "lds_read_linear": the same with 16 lanes reading 256 contiguous
+//          bytes.
+//   kind 3 "lds_write": 8 ds_write_b128 per wave and pass in the matmul's
+//          staging pattern (8 lanes per 128-byte row, swizzled slots).
+// All offsets stay inside the buffer / the LDS array; out holds
+// gridDim.x * 512 16-byte pieces.
+namespace {
+
+__device__ __forceinline__ int swz16(int r, int c) { return (c ^ ((r ^ (r >> 3)) & 7)) << 4; }
+
+__global__ __launch_bounds__(512, 1) void cu_load_kernel(const u32x4 *__restrict__ buf, int64_t win, int64_t nwin,
+                                                         int passes, u32x4 *__restrict__ out) {
+  extern __shared__ uint8_t dyn[];
+  const int t = threadIdx.x;
+  const u32x4 *w = buf + (int64_t)(blockIdx.x % nwin) * win;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  constexpr int U = 4;
+  for (int p = 0; p < passes; ++p) {
+    for (int64_t b = 0; b + 512 * U <= win; b += 512 * U) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = w[b + u * 512 + t];
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc ^= v[u];
+    }
+  }
+  if (acc.x == 0x9E3779B9u && acc.y == 0x7F7F7F7Fu) dyn[t] = 1;  // keeps the LDS allocation
+  out[(int64_t)blockIdx.x * 512 + t] = acc;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(512, 1) void cu_lds_kernel(int passes, u32x4 *__restrict__ out) {
+  __shared__ __align__(16) uint8_t s[160 * 1024];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  for (int i = tid; i < 160 * 1024 / 16; i += 512) reinterpret_cast<u32x4 *>(s)[i] = u32x4{(unsigned)i, 1u, 2u, 3u};
+  __syncthreads();
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int it = 0; it < passes; ++it) {
+    const int base = ((it + wave) & 7) * 16384;
+    if (KIND == 1) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = (k & 3) * 32 + l32;
+        acc ^= *reinterpret_cast<const u32x4 *>(&s[base + r * 128 + swz16(r, (k >> 2) * 4 + h)]);
+      }
+    } else if (KIND == 2) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc ^= *reinterpret_cast<const u32x4 *>(&s[base + k * 1024 + lane * 16]);
+    } else {
+      const int lr = tid >> 3, lc = tid & 7;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int row = (lr + 64 * (k & 1)) & 127;
+        *reinterpret_cast<u32x4 *>(&s[base + row * 128 + swz16(row, lc)]) = acc + u32x4{(unsigned)k, 0u, 0u, 0u};
+        acc.x += 1u;
+      }
+    }
+  }
+  __syncthreads();
+  if (KIND == 3) acc ^= reinterpret_cast<const u32x4 *>(s)[tid];
+  out[(int64_t)blockIdx.x * 512 + tid] = acc;
+}
+
+}  // namespace
+
+// kind 0: buf holds nwin * win 16-byte pieces (16-byte aligned); kinds 1-3
+// ignore buf, win and nwin.  Returns a hipError_t value (0 on success).
+extern "C" int probe_cu_rate(int kind, const void *buf, int64_t win, int64_t nwin, int passes, int nwg, void *out,
+                             void *stream) {
+  if (nwg <= 0 || passes < 0 || !out || (kind == 0 && (!buf || win <= 0 || nwin <= 0)))
+    return (int)hipErrorInvalidValue;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  u32x4 *o = static_cast<u32x4 *>(out);
+  switch (kind) {
+    case 0:
+      hipLaunchKernelGGL(cu_load_kernel, dim3(nwg), dim3(512), 96 * 1024, st, static_cast<const u32x4 *>(buf), win,
+                         nwin, passes, o);
+      break;
+    case 1: hipLaunchKernelGGL(cu_lds_kernel<1>, dim3(nwg), dim3(512), 0, st, passes, o); break;
+    case 2: hipLaunchKernelGGL(cu_lds_kernel<2>, dim3(nwg), dim3(512), 0, st, passes, o); break;
+    case 3: hipLaunchKernelGGL(cu_lds_kernel<3>, dim3(nwg), dim3(512), 0, st, passes, o); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
