@@ -19,9 +19,11 @@
 // 0-15 are K 16h..16h+15, bytes 16-31 are K 32+16h..; B fp4: nibble j is K
 // 32h+j; result register v of lane l is row 8(v/4) + 4h + v%4, column l%32).
 //
-// Work split: a 512-thread workgroup computes a 256 x 256 tile as 4 x 2
-// waves of 2 x 4 MFMA tiles (two waves per SIMD, so one wave's LDS and
-// address work overlaps the other's MFMAs), stepping K by 128.  Both operand
+// Work split (GemmShape below): with E2M1 B a 512-thread workgroup computes
+// a 256 x 256 tile as 4 x 2 waves of 2 x 4 MFMA tiles (two waves per SIMD, so
+// one wave's LDS and address work overlaps the other's MFMAs); with fp8 B a
+// 256-thread workgroup computes 128 x 128 as 2 x 2 waves of 2 x 2 tiles, two
+// workgroups per CU.  K advances by 128 per step.  Both operand
 // slices go global -> registers -> LDS (double-buffered, XOR-swizzled 16-byte
 // slots, conflict-free for 16- and 32-lane read phases) while the previous
 // step's MFMAs run.  An E2M1 B row holds only 64 bytes per K step, half a
@@ -47,11 +49,22 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// 8 waves per workgroup (2 per SIMD, so one wave's LDS and address work
-// overlaps the other's MFMAs): 4 x 2 waves of 2 x 4 MFMA tiles = 256 x 256.
-constexpr int kWavesM = 4, kWavesN = 2, kTilesM = 2, kTilesN = 4;
-constexpr int kGemmThreads = 64 * kWavesM * kWavesN;
-constexpr int kBM = 32 * kTilesM * kWavesM, kBN = 32 * kTilesN * kWavesN;
+// Tile shape by the format of B.  E2M1 B: 8 waves per workgroup (2 per
+// SIMD, so one wave's LDS and address work overlaps the other's MFMAs), 4 x 2
+// waves of 2 x 4 MFMA tiles = 256 x 256, one workgroup per CU (160 KiB of
+// LDS).  fp8 B, whose fragments are twice as large: 4 waves of 2 x 2 MFMA
+// tiles = 128 x 128, two workgroups per CU (80 KiB of LDS each), which keeps
+// every value in registers (the 256 x 256 form spilled 41-44 dwords per lane)
+// and measured 793 -> 755 us on the MoE weight gradient; for E2M1 B the
+// smaller tile measured slower (NN 589 -> 630 us, NT 657 -> 752 us).
+template <int BF>
+struct GemmShape {
+  static constexpr bool small = BF != kFmtE2M1;
+  static constexpr int wavesM = small ? 2 : 4, wavesN = 2, tilesM = 2, tilesN = small ? 2 : 4;
+  static constexpr int threads = 64 * wavesM * wavesN;
+  static constexpr int BM = 32 * tilesM * wavesM, BN = 32 * tilesN * wavesN;
+  static constexpr int per_cu = small ? 2 : 1;  // workgroups per CU
+};
 
 struct GemmArgs {
   const uint8_t *a, *as, *b, *bs;
@@ -85,10 +98,11 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t id, int64_t total) {
 }
 
 template <int AF, int BF, bool S4>
-__global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
-  constexpr int WVM = kWavesM, WVN = kWavesN, WM = kTilesM, WN = kTilesN;
-  constexpr int NT = kGemmThreads;
-  constexpr int BM = kBM, BN = kBN;
+__global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void mxgemm_kernel(GemmArgs P) {
+  using Sh = GemmShape<BF>;
+  constexpr int WVM = Sh::wavesM, WVN = Sh::wavesN, WM = Sh::tilesM, WN = Sh::tilesN;
+  constexpr int NT = Sh::threads;
+  constexpr int BM = Sh::BM, BN = Sh::BN;
   constexpr bool B4 = BF == kFmtE2M1;
   // B4: a 128-byte LDS row holds two K steps (pair) of E2M1 codes; fp8 B:
   // one K step.  Either way 8 slots of 16 bytes per row.
@@ -171,8 +185,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
   // Chunk c holds, for every tile row, the scale bytes of blocks
   // [kb0 + 32c, kb0 + 32c + 32) (32 bytes, or 8 for 128-element blocks).
   // While chunk c is in use, chunk c + 1 arrives one 1/8 slice per step:
-  // step 8c + p loads rows [32p, 32p + 32) of A (waves of the first half) or
-  // of B (second half), one dword per thread, 8 threads per 32-byte row.
+  // step 8c + p loads rows [Rp, Rp + R) of A (waves of the first half) or of
+  // B (second half), R = NT / 16 rows (a tile has 8R rows), one dword per
+  // thread, 8 threads per 32-byte row.
   // Bytes outside [klo, kb1) are replaced by 127 (2^0) when stored, so the
   // MFMAs of masked blocks (zero codes) see a finite scale.
   const bool sl_b = tid >= NT / 2;
@@ -186,7 +201,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
   uint32_t pv[S4 ? 1 : 4];
   int64_t pbyte = 0;
   auto load_slice = [&](int64_t chunk, int piece) {
-    const int row = piece * 32 + sr;
+    const int row = piece * (NT / 16) + sr;
     pbyte = ((kb0 + 32 * chunk) >> sb_log) + 4 * sd;
     const uint8_t *rp = s_base + (int64_t)(row < s_rows ? row : s_rows - 1) * s_ld;
     const int64_t at = pbyte < s_hi ? pbyte : s_hi - 1;  // in bounds (s_hi <= row length)
@@ -213,7 +228,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
     const uint32_t keep = hi_m & ~lo_m;
     v = (v & keep) | (0x7F7F7F7Fu & ~keep);
     uint8_t *dst = sl_b ? &sSB[sbuf][0] : &sSA[sbuf][0];
-    *reinterpret_cast<uint32_t *>(dst + (piece * 32 + sr) * 32 + 4 * sd) = v;
+    *reinterpret_cast<uint32_t *>(dst + (piece * (NT / 16) + sr) * 32 + 4 * sd) = v;
   };
 
   // Codes global -> registers.  A: the K step starting at block kb (slot c =
@@ -423,7 +438,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void mxgemm_kernel(GemmArgs P) {
 template <int AF, int BF>
 hipError_t gemm_launch(const GemmArgs &a0, hipStream_t st) {
   GemmArgs a = a0;
-  const int64_t BM = kBM, BN = kBN;
+  const int64_t BM = GemmShape<BF>::BM, BN = GemmShape<BF>::BN;
+  const dim3 block(GemmShape<BF>::threads);
   a.tiles_n = (a.N + BN - 1) / BN;
   if (a.group_type == 0) {
     // upper bound of the M tiles: every group adds at most one partial tile
@@ -436,9 +452,9 @@ hipError_t gemm_launch(const GemmArgs &a0, hipStream_t st) {
   if (a.total <= 0) return hipSuccess;
   if (a.total > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (a.s4)
-    hipLaunchKernelGGL((mxgemm_kernel<AF, BF, true>), dim3((unsigned)a.total), dim3(kGemmThreads), 0, st, a);
+    hipLaunchKernelGGL((mxgemm_kernel<AF, BF, true>), dim3((unsigned)a.total), block, 0, st, a);
   else
-    hipLaunchKernelGGL((mxgemm_kernel<AF, BF, false>), dim3((unsigned)a.total), dim3(kGemmThreads), 0, st, a);
+    hipLaunchKernelGGL((mxgemm_kernel<AF, BF, false>), dim3((unsigned)a.total), block, 0, st, a);
   return hipGetLastError();
 }
 
