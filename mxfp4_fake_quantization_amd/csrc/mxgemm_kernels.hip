@@ -89,6 +89,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Tile id -> (M-tile, N-tile) in bands of `band` M-tiles walked N-tile by
+// N-tile, so that the tiles an XCD runs at the same time cover a few M-tiles
+// and a few N-tiles instead of one M-tile's whole row of N-tiles (whose
+// weights would not stay in its L2).
+__device__ __forceinline__ void band_tile(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t band, int64_t *tm,
+                                          int64_t *tn) {
+  const int64_t b = t / (band * tiles_n);
+  const int64_t r = t - b * band * tiles_n;
+  const int64_t rows = tiles_m - b * band < band ? tiles_m - b * band : band;
+  *tn = r / rows;
+  *tm = b * band + (r - *tn * rows);
+}
+
 // Workgroup id -> tile id such that each XCD (workgroups are dealt to the 8
 // XCDs round-robin) runs a contiguous range of tiles and shares its L2.
 __device__ __forceinline__ int64_t xcd_tile(int64_t id, int64_t total) {
@@ -125,8 +138,17 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   const uint8_t *bbase = P.b, *bsbase = P.bs;
   int64_t cbase = 0;  // element offset of the output matrix
   if (P.group_type == 0) {
-    const int64_t tm = tile / P.tiles_n;
-    n0 = (tile - tm * P.tiles_n) * BN;
+    // a row of more than 8 N-tiles (NT: 28) goes in bands of 4 M-tiles (its
+    // weight re-reads 9.0x -> 5.4x the unique bytes, time unchanged); 8 or
+    // fewer (NN) keep the row order, whose re-reads are lower (2.0x vs 2.7x)
+    int64_t tm, tn;
+    if (P.tiles_n > 8) {
+      band_tile(tile, P.tiles_m, P.tiles_n, 4, &tm, &tn);
+    } else {
+      tm = tile / P.tiles_n;
+      tn = tile - tm * P.tiles_n;
+    }
+    n0 = tn * BN;
     int g = 0;
     if (P.gl) {
       block_row_uniform<false>(P.gl, P.G, P.list_type, P.M, __builtin_ctz(BM), tm, &m0, &mlen, &g);
@@ -143,10 +165,13 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
     const int64_t per = P.tiles_m * P.tiles_n;
     const int g = (int)(tile / per);
     const int64_t r = tile - (int64_t)g * per;
-    const int64_t tm = r / P.tiles_n;
+    // bands of 8 M-tiles (TN on the MoE layer: re-reads 10.2x -> 5.1x the
+    // unique bytes, 809 -> 773 us)
+    int64_t tm, tn;
+    band_tile(r, P.tiles_m, P.tiles_n, 8, &tm, &tn);
     m0 = tm * BM;
     mlen = P.M - m0 < BM ? P.M - m0 : BM;
-    n0 = (r - tm * P.tiles_n) * BN;
+    n0 = tn * BN;
     int64_t nb;
     group_block_span(P.gl, P.G, P.list_type, P.K, 5, g, &kb0, &nb);
     kb1 = kb0 + nb < P.k_blocks ? kb0 + nb : P.k_blocks;
