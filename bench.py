@@ -308,7 +308,20 @@ def build_tiny(M, lib, W, torch, stream):
         fwd[1]()
         bwd[0]()
         bwd[1]()
-    return dict(tw=tw, tx=tx, step=step, keep=keep)
+
+    # the same step in two launches: both forwards, then both STEs
+    d0 = keep[0][5]
+    fitems = (M._RowItem * 2)(*[M._RowItem(xt.data_ptr(), yt.data_ptr(), mt.data_ptr(), None, xt.shape[0],
+                                           xt.shape[1]) for (xt, yt, gt, gi, mt, dt) in keep])
+    bitems = (M._SteItem * 2)(*[M._SteItem(gt.data_ptr(), mt.data_ptr(), gi.data_ptr(), gt.shape[0], gt.shape[1])
+                                for (xt, yt, gt, gi, mt, dt) in keep])
+    fb = Call(lib.mxfp4_qdq_fwd_rows_batch, ctypes.byref(d0), 2, fitems, stream, keep=(d0, fitems))
+    bb = Call(lib.mxfp4_ste_bwd_rows_batch, ctypes.byref(d0), 2, bitems, stream, keep=(d0, bitems))
+
+    def step_batched():
+        fb()
+        bb()
+    return dict(tw=tw, tx=tx, step=step, step_batched=step_batched, keep=keep)
 
 
 def build_dual(M, lib, W, torch, stream, sets=2):
@@ -546,16 +559,22 @@ def bench_configs(M, lib, W, torch, stream, probe, cpu, cpu_seconds):
     out = {}
 
     # c1: the tiny QAT check (fp32 W 32x64 and X 4x64): forward y + bitmap of
-    # both, then the clipped STE of an all-ones gradient for both; four
-    # launches, launch-bound, so reported as latency
+    # both, then the clipped STE of an all-ones gradient for both; launch-bound,
+    # so reported as latency: both forwards in one batched launch, both STEs in
+    # another (a QAT layer quantizes its weight and input together), and the
+    # same step as four single-tensor launches beside it
     tq = build_tiny(M, lib, W, torch, stream)
-    med, best = timer([tq["step"]], reps=200)
-    c1 = {"workload": "tiny QAT: fp32 W 32x64 + X 4x64, row-wise block-32 QDQ (y + bitmap) then "
-                      "clipped STE of ones, four launches",
-          "kernels": [KERNELS["fwd"].replace("bf16", "f32"), KERNELS["bwd"].replace("bf16", "f32")],
+    med, best = timer([tq["step_batched"]], reps=200)
+    med4, best4 = timer([tq["step"]], reps=200)
+    c1 = {"workload": "tiny QAT: fp32 W 32x64 + X 4x64, row-wise block-32 QDQ (y + bitmap) of both in one "
+                      "batched launch, then the clipped STE of ones for both in another",
+          "kernels": ["row_fwd_batch_kernel<f32,32,floor>", "ste_row_batch_kernel<f32>"],
           "step_us": round(med * 1e6, 2), "best_step_us": round(best * 1e6, 2),
-          "per_launch_us": round(med * 1e6 / 4, 2), "bound": "launch latency",
-          "higher_is_better": False, "unit": "us per step"}
+          "per_launch_us": round(med * 1e6 / 2, 2), "bound": "launch latency",
+          "higher_is_better": False, "unit": "us per step",
+          "four_launches": {"step_us": round(med4 * 1e6, 2), "best_step_us": round(best4 * 1e6, 2),
+                            "kernels": [KERNELS["fwd"].replace("bf16", "f32"),
+                                        KERNELS["bwd"].replace("bf16", "f32")]}}
     if cpu:
         tw, tx = tq["tw"], tq["tx"]
 
@@ -916,7 +935,8 @@ def profile_streaming(M, lib, W, torch, stream, probe, run):
     run("probe: the forward's bytes and pattern, 4096x4096", "probe_kernel", pf, n * 2, n * 2.125, n)
     del wk, pf
     tq = build_tiny(M, lib, W, torch, stream)
-    run("tiny QAT step (fwd W, fwd X, STE W, STE X)", "mxfp4", [tq["step"]], 0, 0, 0, per_call=4)
+    run("tiny QAT step (fwd W + X batched, STE W + X batched)", "mxfp4", [tq["step_batched"]], 0, 0, 0,
+        per_call=2)
     del tq
     dual = build_dual(M, lib, W, torch, stream)
     n = dual["R"] * dual["C"]

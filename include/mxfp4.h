@@ -139,6 +139,50 @@ mxfp4_status_t mxfp4_ste_bwd(const mxfp4_desc_t *desc, int32_t layout,
                              void *stream);
 
 /*
+ * Several small tensors in one launch.  A QAT layer fake-quantizes its
+ * weight and its input in the same forward (the amct PR page's
+ * MXFP4QATLinear.forward: Q(x), then Q(W), then F.linear) and runs the STE
+ * of both in its backward; for small layers each of those launches costs
+ * more than its bytes.  These two calls take up to MXFP4_BATCH_MAX row-wise
+ * tensors per launch with the single-tensor calls' semantics, layouts and
+ * checks, tensor by tensor.  desc->dtype, block, rule and scale_factor are
+ * shared by all items; desc->rows and cols are ignored (each item carries
+ * its own).  items is a host array of n items, read during the call.  Items
+ * with rows * cols == 0 are skipped without looking at their pointers.
+ * Outputs of different items must not overlap (distinct pointers are
+ * checked).
+ */
+#define MXFP4_BATCH_MAX 8
+
+typedef struct mxfp4_row_item {
+  const void *x;      /* rows x cols of desc->dtype                          */
+  void *y;            /* QDQ values (may equal x) or NULL                     */
+  uint32_t *mask;     /* ROW bitmap or NULL                                    */
+  uint8_t *scales;    /* ROW E8M0 bytes or NULL (at least one output)          */
+  int64_t rows;
+  int64_t cols;
+} mxfp4_row_item_t;
+
+/* mxfp4_qdq_fwd with axis = MXFP4_ROW for each item. */
+mxfp4_status_t mxfp4_qdq_fwd_rows_batch(const mxfp4_desc_t *desc, int32_t n,
+                                        const mxfp4_row_item_t *items,
+                                        void *stream);
+
+typedef struct mxfp4_ste_item {
+  const void *grad_out;  /* rows x cols of desc->dtype                       */
+  const uint32_t *mask;  /* ROW bitmap, or NULL for the plain STE            */
+  void *grad_in;         /* may equal grad_out                               */
+  int64_t rows;
+  int64_t cols;
+} mxfp4_ste_item_t;
+
+/* mxfp4_ste_bwd with layout = MXFP4_ROW for each item (desc->rule and
+ * scale_factor are ignored; a plain in-place item does nothing). */
+mxfp4_status_t mxfp4_ste_bwd_rows_batch(const mxfp4_desc_t *desc, int32_t n,
+                                        const mxfp4_ste_item_t *items,
+                                        void *stream);
+
+/*
  * The saturation mask as the pages give it (fake_quant.py
  * mxfp4_saturation_mask: a bool tensor of x's shape, true where |x| > 6 * 2^k
  * of the element's block): expands a ROW or COL bitmap written by

@@ -38,7 +38,7 @@ __all__ = [
     "ROW", "COL", "GROUPED", "FLOOR", "AMCT",
     "mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
     "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant",
-    "mxfp4_mask_to_bool", "mxfp4_saturation_mask",
+    "mxfp4_mask_to_bool", "mxfp4_saturation_mask", "mxfp4_qdq_fwd_rows_batch", "mxfp4_ste_bwd_rows_batch",
     "mxfp4_last_error", "mxfp4_version", "library_path",
     "row_mask_shape", "col_mask_shape", "grouped_mask_rows_max", "grouped_scale_rows_max",
     "kmajor_k_blocks",
@@ -66,6 +66,19 @@ class _MxOperand(ctypes.Structure):
                 ("group_stride", ctypes.c_int64), ("group_stride_scales", ctypes.c_int64)]
 
 
+class _RowItem(ctypes.Structure):
+    """mxfp4_row_item_t (include/mxfp4.h)."""
+    _fields_ = [("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("mask", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class _SteItem(ctypes.Structure):
+    """mxfp4_ste_item_t (include/mxfp4.h)."""
+    _fields_ = [("grad_out", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("grad_in", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+BATCH_MAX = 8
 _lib = None
 
 
@@ -82,6 +95,8 @@ def _load():
         lib.mxfp4_qdq_fwd.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.mxfp4_ste_bwd.argtypes = [dp, i32, vp, vp, vp, vp, i32, i32, vp]
         lib.mxfp4_mask_to_bool.argtypes = [i32, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
+        lib.mxfp4_qdq_fwd_rows_batch.argtypes = [dp, i32, ctypes.POINTER(_RowItem), vp]
+        lib.mxfp4_ste_bwd_rows_batch.argtypes = [dp, i32, ctypes.POINTER(_SteItem), vp]
         lib.mxfp4_quant_pack.argtypes = [dp, vp, vp, vp, vp, vp, vp]
         lib.mxfp4_grouped_qdq.argtypes = [dp, vp, vp, i32, i32, vp, vp, vp, vp]
         lib.mxfp4_quant_pack_kmajor.argtypes = [dp, vp, vp, i32, i32, ctypes.c_int64, vp, vp, vp]
@@ -94,7 +109,8 @@ def _load():
                                              i64, vp]
         for f in ("mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
                   "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant", "mxfp4_version",
-                  "mxfp4_grouped_matmul", "mxfp8_quant_kmajor", "mxfp4_mask_to_bool"):
+                  "mxfp4_grouped_matmul", "mxfp8_quant_kmajor", "mxfp4_mask_to_bool",
+                  "mxfp4_qdq_fwd_rows_batch", "mxfp4_ste_bwd_rows_batch"):
             getattr(lib, f).restype = ctypes.c_int32
         lib.mxfp4_last_error.restype = ctypes.c_char_p
         lib.mxfp4_last_error.argtypes = []
@@ -238,6 +254,50 @@ def mxfp4_qdq_fwd(x, axis=ROW, y_row=None, mask_row=None, scales_row=None, y_col
                                _ptr(mask_row, "mask"), _ptr(scales_row, "u8"), _ptr(y_col),
                                _ptr(mask_col, "mask"), _ptr(scales_col, "u8"), _stream())
     _check(st, "mxfp4_qdq_fwd")
+
+
+def mxfp4_qdq_fwd_rows_batch(xs, ys=None, masks=None, scales=None, block=32, rule="floor", scale_factor=6.0):
+    """Row-wise QDQ forward of up to BATCH_MAX tensors (same dtype) in one
+    launch; ys / masks / scales are lists aligned with xs (None entries, or
+    None for the whole list, leave that output out)."""
+    n = len(xs)
+    if not 1 <= n <= BATCH_MAX:
+        raise ValueError(f"1 to {BATCH_MAX} tensors per batch, got {n}")
+    ys, masks, scales = ([None] * n if v is None else list(v) for v in (ys, masks, scales))
+    if not len(ys) == len(masks) == len(scales) == n:
+        raise ValueError("ys, masks and scales must have one entry per tensor")
+    d = _desc(xs[0], block, rule, scale_factor)
+    items = (_RowItem * n)()
+    for i, x in enumerate(xs):
+        if _dtype(x) != d.dtype:
+            raise ValueError("all tensors of a batch must have the same dtype")
+        _same_elems(x, ys[i])
+        rows, cols = _shape2d(x)
+        _need(masks[i], rows * -(-cols // 32), "mask")
+        _need(scales[i], rows * -(-cols // int(block)), "scales")
+        items[i] = _RowItem(_ptr(x), _ptr(ys[i]), _ptr(masks[i], "mask"), _ptr(scales[i], "u8"), rows, cols)
+    _check(_load().mxfp4_qdq_fwd_rows_batch(ctypes.byref(d), n, items, _stream()), "mxfp4_qdq_fwd_rows_batch")
+
+
+def mxfp4_ste_bwd_rows_batch(grads_out, masks, grads_in, block=32):
+    """STE backward of up to BATCH_MAX gradients (same dtype) with ROW
+    bitmaps (None: plain STE) in one launch."""
+    n = len(grads_out)
+    if not 1 <= n <= BATCH_MAX:
+        raise ValueError(f"1 to {BATCH_MAX} tensors per batch, got {n}")
+    masks = [None] * n if masks is None else list(masks)
+    if not len(masks) == len(grads_in) == n:
+        raise ValueError("masks and grads_in must have one entry per gradient")
+    d = _desc(grads_out[0], block, "floor", 6.0)
+    items = (_SteItem * n)()
+    for i, g in enumerate(grads_out):
+        if _dtype(g) != d.dtype:
+            raise ValueError("all tensors of a batch must have the same dtype")
+        _same_elems(g, grads_in[i])
+        rows, cols = _shape2d(g)
+        _need(masks[i], rows * -(-cols // 32), "mask")
+        items[i] = _SteItem(_ptr(g), _ptr(masks[i], "mask"), _ptr(grads_in[i]), rows, cols)
+    _check(_load().mxfp4_ste_bwd_rows_batch(ctypes.byref(d), n, items, _stream()), "mxfp4_ste_bwd_rows_batch")
 
 
 def mxfp4_ste_bwd(grad_out, mask, grad_in, layout=ROW, block=32, group_list=None,

@@ -152,6 +152,81 @@ mxfp4_status_t mxfp4_ste_bwd(const mxfp4_desc_t *desc, int32_t layout, const voi
   return hip_status(mxfp4::launch_ste_bwd(L, static_cast<hipStream_t>(stream)), "STE backward launch");
 }
 
+mxfp4_status_t mxfp4_qdq_fwd_rows_batch(const mxfp4_desc_t *desc, int32_t n, const mxfp4_row_item_t *items,
+                                        void *stream) {
+  if (n < 1 || n > MXFP4_BATCH_MAX) return fail(MXFP4_EINVAL, "n %d is not in [1, %d]", n, MXFP4_BATCH_MAX);
+  if (!items) return fail(MXFP4_EINVAL, "items is NULL");
+  mxfp4_desc_t d0 = desc ? *desc : mxfp4_desc_t{};
+  d0.rows = 0;
+  d0.cols = 0;
+  int64_t n0;
+  MXFP4_TRY(check_desc(desc ? &d0 : nullptr, true, &n0));
+  mxfp4::RowLaunch L[MXFP4_BATCH_MAX];
+  const void *outs[3 * MXFP4_BATCH_MAX];
+  int m = 0, no = 0;
+  for (int i = 0; i < n; ++i) {
+    const mxfp4_row_item_t &it = items[i];
+    mxfp4_desc_t d = d0;
+    d.rows = it.rows;
+    d.cols = it.cols;
+    int64_t ne;
+    MXFP4_TRY(check_desc(&d, true, &ne));
+    if (ne == 0) continue;  // an empty item is skipped whatever its pointers
+    MXFP4_TRY(check_ptr(it.x, 16, "items[].x"));
+    MXFP4_TRY(check_opt(it.y, 16, "items[].y"));
+    MXFP4_TRY(check_opt(it.mask, 4, "items[].mask"));
+    if (!it.y && !it.mask && !it.scales) return fail(MXFP4_EINVAL, "items[%d] has no output", i);
+    if (!distinct({it.y == it.x ? nullptr : it.x, it.y, it.mask, it.scales}))
+      return fail(MXFP4_EINVAL, "items[%d]: outputs alias each other or x", i);
+    for (const void *o : {(const void *)it.y, (const void *)it.mask, (const void *)it.scales}) {
+      if (!o) continue;
+      for (int k = 0; k < no; ++k)
+        if (outs[k] == o) return fail(MXFP4_EINVAL, "items[%d] shares an output with another item", i);
+      outs[no++] = o;
+    }
+    L[m++] = mxfp4::RowLaunch{desc->dtype, desc->block, desc->rule, it.rows, it.cols, desc->scale_factor,
+                              it.x, it.y, it.mask, it.scales, nullptr};
+  }
+  if (m == 0) return ok();
+  return hip_status(mxfp4::launch_row_fwd_batch(L, m, static_cast<hipStream_t>(stream)), "batched forward launch");
+}
+
+mxfp4_status_t mxfp4_ste_bwd_rows_batch(const mxfp4_desc_t *desc, int32_t n, const mxfp4_ste_item_t *items,
+                                        void *stream) {
+  if (n < 1 || n > MXFP4_BATCH_MAX) return fail(MXFP4_EINVAL, "n %d is not in [1, %d]", n, MXFP4_BATCH_MAX);
+  if (!items) return fail(MXFP4_EINVAL, "items is NULL");
+  mxfp4_desc_t d0 = desc ? *desc : mxfp4_desc_t{};
+  d0.rows = 0;
+  d0.cols = 0;
+  int64_t n0;
+  MXFP4_TRY(check_desc(desc ? &d0 : nullptr, false, &n0));
+  mxfp4::SteLaunch L[MXFP4_BATCH_MAX];
+  const void *outs[MXFP4_BATCH_MAX];
+  int m = 0, no = 0;
+  for (int i = 0; i < n; ++i) {
+    const mxfp4_ste_item_t &it = items[i];
+    mxfp4_desc_t d = d0;
+    d.rows = it.rows;
+    d.cols = it.cols;
+    int64_t ne;
+    MXFP4_TRY(check_desc(&d, false, &ne));
+    if (ne == 0) continue;  // an empty item is skipped whatever its pointers
+    MXFP4_TRY(check_ptr(it.grad_out, 16, "items[].grad_out"));
+    MXFP4_TRY(check_ptr(it.grad_in, 16, "items[].grad_in"));
+    MXFP4_TRY(check_opt(it.mask, 4, "items[].mask"));
+    if (it.mask && (it.mask == it.grad_out || it.mask == it.grad_in))
+      return fail(MXFP4_EINVAL, "items[%d]: mask aliases a gradient", i);
+    for (int k = 0; k < no; ++k)
+      if (outs[k] == it.grad_in) return fail(MXFP4_EINVAL, "items[%d] shares grad_in with another item", i);
+    outs[no++] = it.grad_in;
+    if (!it.mask && it.grad_in == it.grad_out) continue;
+    L[m++] = mxfp4::SteLaunch{desc->dtype, desc->block, MXFP4_ROW, it.rows, it.cols, it.grad_out, it.mask,
+                              it.grad_in, nullptr, 0, 1};
+  }
+  if (m == 0) return ok();
+  return hip_status(mxfp4::launch_ste_row_batch(L, m, static_cast<hipStream_t>(stream)), "batched STE launch");
+}
+
 mxfp4_status_t mxfp4_mask_to_bool(int32_t layout, int64_t rows, int64_t cols, const uint32_t *mask,
                                   uint8_t *out, void *stream) {
   if (layout != MXFP4_ROW && layout != MXFP4_COL)
@@ -393,6 +468,6 @@ mxfp4_status_t mxfp8_quant_kmajor(const mxfp4_desc_t *desc, int32_t fmt, const v
 
 const char *mxfp4_last_error(void) { return g_last_error.c_str(); }
 
-int32_t mxfp4_version(void) { return 104; }
+int32_t mxfp4_version(void) { return 105; }
 
 }  // extern "C"

@@ -21,6 +21,10 @@ struct RowLaunch {
   uint8_t *codes;
 };
 hipError_t launch_row_fwd(const RowLaunch &L, hipStream_t stream);
+// Up to kBatchMax row-wise forwards in one launch (same dtype, block, rule
+// and scale factor; y / mask / scales only).
+constexpr int kBatchMax = 8;
+hipError_t launch_row_fwd_batch(const RowLaunch *L, int n, hipStream_t stream);
 
 // Column-wise / dual-direction / grouped forward (block-row tiles).
 struct ColLaunch {
@@ -50,6 +54,8 @@ struct SteLaunch {
   int num_groups, list_type;
 };
 hipError_t launch_ste_bwd(const SteLaunch &L, hipStream_t stream);
+// Up to kBatchMax STE backwards with ROW bitmaps (or none) in one launch.
+hipError_t launch_ste_row_batch(const SteLaunch *L, int n, hipStream_t stream);
 // ROW / COL saturation bitmap -> one 0/1 byte per element (layout 1 or 2).
 hipError_t launch_mask_bool(int layout, int64_t rows, int64_t cols, const uint32_t *mask, uint8_t *out,
                             hipStream_t stream);

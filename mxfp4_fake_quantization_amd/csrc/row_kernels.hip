@@ -147,12 +147,12 @@ __device__ __forceinline__ void row_emit(const RowArgs &A, const uint32_t *wv, c
 }
 
 template <int DT, int B, int RULE, int MODE, int U, int T, bool FULL>
-__device__ __forceinline__ void row_fwd_body(const RowArgs &A) {
+__device__ __forceinline__ void row_fwd_body(const RowArgs &A, int64_t wg) {
   constexpr int G = B / 8;
   constexpr int NW = ChunkT<DT>::NW;
   constexpr int ES = ChunkT<DT>::ES;
   const int tid = threadIdx.x;
-  const int64_t base = (int64_t)blockIdx.x * (T * U);
+  const int64_t base = wg * (T * U);
 
   uint32_t w[U][NW];
   int64_t off[U], row[U], cr[U];
@@ -218,9 +218,36 @@ __device__ __forceinline__ void row_fwd_body(const RowArgs &A) {
 template <int DT, int B, int RULE, int MODE, int U, int T>
 __global__ __launch_bounds__(T) void row_fwd_kernel(RowArgs A) {
   if (MODE == kModeFlat && (int64_t)(blockIdx.x + 1) * (T * U) <= A.nchunks)
-    row_fwd_body<DT, B, RULE, MODE, U, T, true>(A);
+    row_fwd_body<DT, B, RULE, MODE, U, T, true>(A, blockIdx.x);
   else
-    row_fwd_body<DT, B, RULE, MODE, U, T, false>(A);
+    row_fwd_body<DT, B, RULE, MODE, U, T, false>(A, blockIdx.x);
+}
+
+// Several tensors in one launch (small tensors are launch-bound): tensor j
+// owns workgroups [wg0[j], wg0[j + 1]); each runs the single-tensor body in
+// its own layout mode.
+struct RowBatchArgs {
+  RowArgs item[kBatchMax];
+  int64_t wg0[kBatchMax + 1];
+  int mode[kBatchMax];
+  int n;
+};
+
+template <int DT, int B, int RULE>
+__global__ __launch_bounds__(kRowThreads) void row_fwd_batch_kernel(RowBatchArgs P) {
+  const int64_t w = blockIdx.x;
+  int j = 0;
+  while (j + 1 < P.n && w >= P.wg0[j + 1]) ++j;
+  const RowArgs &A = P.item[j];
+  const int64_t wg = w - P.wg0[j];
+  switch (P.mode[j]) {
+    case kModeFlat:
+      if ((wg + 1) * kRowThreads <= A.nchunks) row_fwd_body<DT, B, RULE, kModeFlat, 1, kRowThreads, true>(A, wg);
+      else row_fwd_body<DT, B, RULE, kModeFlat, 1, kRowThreads, false>(A, wg);
+      break;
+    case kModeRowsVec: row_fwd_body<DT, B, RULE, kModeRowsVec, 1, kRowThreads, false>(A, wg); break;
+    default: row_fwd_body<DT, B, RULE, kModeRowsScalar, 1, kRowThreads, false>(A, wg); break;
+  }
 }
 
 template <int DT, int B, int RULE, int MODE, int U, int T>
@@ -259,10 +286,8 @@ hipError_t dispatch_rule(int rule, int mode, const RowArgs &a, hipStream_t st) {
                         : dispatch_mode<DT, B, kAmct>(mode, a, st);
 }
 
-}  // namespace
-
-hipError_t launch_row_fwd(const RowLaunch &L, hipStream_t st) {
-  RowArgs a;
+// Kernel arguments and layout mode of one tensor.
+int row_args(const RowLaunch &L, RowArgs &a) {
   a.x = static_cast<const uint8_t *>(L.x);
   a.y = static_cast<uint8_t *>(L.y);
   a.mask = reinterpret_cast<uint8_t *>(L.mask);
@@ -276,19 +301,54 @@ hipError_t launch_row_fwd(const RowLaunch &L, hipStream_t st) {
   a.sf = L.sf;
   a.emit = (L.y ? kEmitY : 0) | (L.mask ? kEmitMask : 0) | (L.scales ? kEmitScales : 0) |
            (L.codes ? kEmitCodes : 0);
-  int mode;
   if (L.cols % L.block == 0) {
-    mode = kModeFlat;
     a.nchunks = L.rows * L.cols / 8;
-  } else {
-    mode = (L.cols % 8 == 0) ? kModeRowsVec : kModeRowsScalar;
-    a.nchunks = L.rows * a.cpr;
+    return kModeFlat;
   }
+  a.nchunks = L.rows * a.cpr;
+  return (L.cols % 8 == 0) ? kModeRowsVec : kModeRowsScalar;
+}
+
+template <int DT, int B>
+hipError_t batch_rule(int rule, dim3 grid, const RowBatchArgs &p, hipStream_t st) {
+  if (rule == kFloor)
+    hipLaunchKernelGGL((row_fwd_batch_kernel<DT, B, kFloor>), grid, dim3(kRowThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((row_fwd_batch_kernel<DT, B, kAmct>), grid, dim3(kRowThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_row_fwd(const RowLaunch &L, hipStream_t st) {
+  RowArgs a;
+  const int mode = row_args(L, a);
   if (L.dtype == kBF16)
     return L.block == 32 ? dispatch_rule<kBF16, 32>(L.rule, mode, a, st)
                          : dispatch_rule<kBF16, 128>(L.rule, mode, a, st);
   return L.block == 32 ? dispatch_rule<kF32, 32>(L.rule, mode, a, st)
                        : dispatch_rule<kF32, 128>(L.rule, mode, a, st);
+}
+
+hipError_t launch_row_fwd_batch(const RowLaunch *L, int n, hipStream_t st) {
+  if (n < 1 || n > kBatchMax) return hipErrorInvalidValue;
+  RowBatchArgs p{};
+  p.n = n;
+  int64_t wg = 0;
+  for (int j = 0; j < n; ++j) {
+    p.mode[j] = row_args(L[j], p.item[j]);
+    p.wg0[j] = wg;
+    wg += (p.item[j].nchunks + kRowThreads - 1) / kRowThreads;
+  }
+  for (int j = n; j <= kBatchMax; ++j) p.wg0[j] = wg;
+  for (int j = n; j < kBatchMax; ++j) p.mode[j] = kModeFlat;
+  if (wg == 0) return hipSuccess;
+  if (wg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wg);
+  const int dt = L[0].dtype, b = L[0].block, rule = L[0].rule;
+  if (dt == kBF16)
+    return b == 32 ? batch_rule<kBF16, 32>(rule, grid, p, st) : batch_rule<kBF16, 128>(rule, grid, p, st);
+  return b == 32 ? batch_rule<kF32, 32>(rule, grid, p, st) : batch_rule<kF32, 128>(rule, grid, p, st);
 }
 
 }  // namespace mxfp4

@@ -59,11 +59,11 @@ struct SteRowArgs {
 };
 
 template <int DT, int MODE, int U, bool FULL>
-__device__ __forceinline__ void ste_row_body(const SteRowArgs &A) {
+__device__ __forceinline__ void ste_row_body(const SteRowArgs &A, int64_t wg) {
   constexpr int NW = DT == kBF16 ? 4 : 8;
   constexpr int ES = DT == kBF16 ? 2 : 4;
   const int tid = threadIdx.x;
-  const int64_t base = (int64_t)blockIdx.x * (kSteThreads * U);
+  const int64_t base = wg * (kSteThreads * U);
   uint32_t w[U][NW];
   uint32_t bits[U];
   int64_t off[U];
@@ -125,9 +125,35 @@ __device__ __forceinline__ void ste_row_body(const SteRowArgs &A) {
 template <int DT, int MODE, int U>
 __global__ __launch_bounds__(kSteThreads) void ste_row_kernel(SteRowArgs A) {
   if (MODE == kModeFlat && (int64_t)(blockIdx.x + 1) * (kSteThreads * U) <= A.nchunks)
-    ste_row_body<DT, MODE, U, true>(A);
+    ste_row_body<DT, MODE, U, true>(A, blockIdx.x);
   else
-    ste_row_body<DT, MODE, U, false>(A);
+    ste_row_body<DT, MODE, U, false>(A, blockIdx.x);
+}
+
+// Several gradients in one launch: tensor j owns workgroups [wg0[j],
+// wg0[j + 1]), one piece per lane, in its own layout mode.
+struct SteBatchArgs {
+  SteRowArgs item[kBatchMax];
+  int64_t wg0[kBatchMax + 1];
+  int mode[kBatchMax];
+  int n;
+};
+
+template <int DT>
+__global__ __launch_bounds__(kSteThreads) void ste_row_batch_kernel(SteBatchArgs P) {
+  const int64_t w = blockIdx.x;
+  int j = 0;
+  while (j + 1 < P.n && w >= P.wg0[j + 1]) ++j;
+  const SteRowArgs &A = P.item[j];
+  const int64_t wg = w - P.wg0[j];
+  switch (P.mode[j]) {
+    case kModeFlat:
+      if ((wg + 1) * kSteThreads <= A.nchunks) ste_row_body<DT, kModeFlat, 1, true>(A, wg);
+      else ste_row_body<DT, kModeFlat, 1, false>(A, wg);
+      break;
+    case kModeRowsVec: ste_row_body<DT, kModeRowsVec, 1, false>(A, wg); break;
+    default: ste_row_body<DT, kModeRowsScalar, 1, false>(A, wg); break;
+  }
 }
 
 struct SteColArgs {
@@ -248,23 +274,26 @@ void ste_row_launch(int mode, dim3 grid, const SteRowArgs &a, hipStream_t st) {
   }
 }
 
-template <int DT>
-hipError_t launch_row(const SteLaunch &L, hipStream_t st) {
-  SteRowArgs a;
+// Kernel arguments and layout mode of one gradient (ROW bitmap or none).
+int ste_row_args(const SteLaunch &L, SteRowArgs &a) {
   a.g = static_cast<const uint8_t *>(L.g);
   a.gi = static_cast<uint8_t *>(L.g_in);
   a.mask = reinterpret_cast<const uint8_t *>(L.mask);
   a.cols = L.cols;
   a.cpr = (L.cols + 7) / 8;
   a.mask_row_bytes = 4 * ((L.cols + 31) / 32);
-  int mode;
   if (L.cols % 32 == 0) {
-    mode = kModeFlat;
     a.nchunks = L.rows * L.cols / 8;
-  } else {
-    mode = L.cols % 8 == 0 ? kModeRowsVec : kModeRowsScalar;
-    a.nchunks = L.rows * a.cpr;
+    return kModeFlat;
   }
+  a.nchunks = L.rows * a.cpr;
+  return L.cols % 8 == 0 ? kModeRowsVec : kModeRowsScalar;
+}
+
+template <int DT>
+hipError_t launch_row(const SteLaunch &L, hipStream_t st) {
+  SteRowArgs a;
+  const int mode = ste_row_args(L, a);
   const int u = a.nchunks > kSteBigChunks ? MXFP4_STE_U_BIG : MXFP4_STE_U_SMALL;
   const int64_t per = (int64_t)kSteThreads * u;
   const int64_t nwg = (a.nchunks + per - 1) / per;
@@ -370,6 +399,27 @@ hipError_t launch_mask_bool(int layout, int64_t rows, int64_t cols, const uint32
   else
     hipLaunchKernelGGL((mask_bool_kernel<2>), dim3((unsigned)nwg), dim3(kBoolThreads), 0, st, mask, out, cols, wpr,
                        n, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_ste_row_batch(const SteLaunch *L, int n, hipStream_t st) {
+  if (n < 1 || n > kBatchMax) return hipErrorInvalidValue;
+  SteBatchArgs p{};
+  p.n = n;
+  int64_t wg = 0;
+  for (int j = 0; j < n; ++j) {
+    p.mode[j] = ste_row_args(L[j], p.item[j]);
+    p.wg0[j] = wg;
+    wg += (p.item[j].nchunks + kSteThreads - 1) / kSteThreads;
+  }
+  for (int j = n; j <= kBatchMax; ++j) p.wg0[j] = wg;
+  if (wg == 0) return hipSuccess;
+  if (wg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wg);
+  if (L[0].dtype == kBF16)
+    hipLaunchKernelGGL(ste_row_batch_kernel<kBF16>, grid, dim3(kSteThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL(ste_row_batch_kernel<kF32>, grid, dim3(kSteThreads), 0, st, p);
   return hipGetLastError();
 }
 

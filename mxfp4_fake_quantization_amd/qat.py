@@ -35,7 +35,7 @@ import torch
 import torch.nn.functional as F
 from torch import nn
 
-from . import ROW, mxfp4_qdq_fwd, mxfp4_ste_bwd
+from . import ROW, mxfp4_qdq_fwd, mxfp4_qdq_fwd_rows_batch, mxfp4_ste_bwd, mxfp4_ste_bwd_rows_batch
 
 __all__ = ["MXFP4Spec", "QATPolicy", "QATLinear", "FakeQuant", "fake_quant", "quantize_model",
            "mxfp4_fake_quant", "MXFP4FakeQuantizer", "MXFP4QATConfig", "MXFP4QATLinear",
@@ -97,6 +97,53 @@ class _FakeQuantSTE(torch.autograd.Function):
         grad_in = torch.empty_like(g)
         mxfp4_ste_bwd(g, mask, grad_in, layout=ROW, block=ctx.spec.block)
         return grad_in, None
+
+
+class _FakeQuantPairSTE(torch.autograd.Function):
+    """Two tensors under specs that share block, rule and scale factor (the
+    layer's input and weight): one batched forward launch, one batched STE
+    launch for the clipped ones."""
+
+    @staticmethod
+    def forward(ctx, a, b, sa: MXFP4Spec, sb: MXFP4Spec):
+        ts = [a.contiguous(), b.contiguous()]
+        ys = [torch.empty_like(t) for t in ts]
+        masks = []
+        for t, sp in zip(ts, (sa, sb)):
+            if sp.clipped:
+                cols = t.shape[-1]
+                rows = t.numel() // cols if cols else 0
+                masks.append(torch.empty((rows, -(-cols // 32)), dtype=torch.int32, device=t.device))
+            else:
+                masks.append(None)
+        mxfp4_qdq_fwd_rows_batch(ts, ys, masks, block=sa.block, rule=sa.rule, scale_factor=sa.scale_factor)
+        ctx.block = sa.block
+        ctx.clipped = (sa.clipped, sb.clipped)
+        ctx.save_for_backward(*[m for m in masks if m is not None])
+        return ys[0], ys[1]
+
+    @staticmethod
+    def backward(ctx, ga, gb):
+        saved = list(ctx.saved_tensors)
+        masks = [saved.pop(0) if c else None for c in ctx.clipped]
+        outs, gs, gis, ms = [ga, gb], [], [], []
+        for i, (g, m) in enumerate(zip((ga, gb), masks)):
+            if g is None or m is None:
+                continue                               # plain STE (or no gradient): unchanged
+            g = g.contiguous()
+            gi = torch.empty_like(g)
+            gs.append(g)
+            gis.append(gi)
+            ms.append(m)
+            outs[i] = gi
+        if gs:
+            mxfp4_ste_bwd_rows_batch(gs, ms, gis, block=ctx.block)
+        return outs[0], outs[1], None, None
+
+
+def _pairable(a: torch.Tensor, b: torch.Tensor, sa: MXFP4Spec, sb: MXFP4Spec) -> bool:
+    return (a.dtype == b.dtype and a.dtype in (torch.bfloat16, torch.float32) and a.dim() > 0 and b.dim() > 0
+            and (sa.block, sa.rule, sa.scale_factor) == (sb.block, sb.rule, sb.scale_factor))
 
 
 def fake_quant(x: torch.Tensor, spec: MXFP4Spec = MXFP4Spec()) -> torch.Tensor:
@@ -170,8 +217,11 @@ class QATLinear(nn.Linear):
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         p = self.policy
-        xq = x if p.activation is None else p.activation(x)
-        wq = self.weight if p.weight is None else p.weight(self.weight)
+        if p.activation is not None and p.weight is not None and _pairable(x, self.weight, p.activation, p.weight):
+            xq, wq = _FakeQuantPairSTE.apply(x, self.weight, p.activation, p.weight)  # one launch each way
+        else:
+            xq = x if p.activation is None else p.activation(x)
+            wq = self.weight if p.weight is None else p.weight(self.weight)
         return F.linear(xq, wq, self.bias)
 
     def extra_repr(self) -> str:

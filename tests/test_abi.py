@@ -49,6 +49,8 @@ def lib():
     L.mxfp4_grouped_matmul.argtypes = [i32, i64, i64, i64, op, op, vp, i32, i32, i64, i32, vp, i64, vp]
     L.mxfp8_quant_kmajor.argtypes = [dp, i32, vp, vp, i32, i32, i64, vp, vp, vp]
     L.mxfp4_mask_to_bool.argtypes = [i32, i64, i64, vp, vp, vp]
+    L.mxfp4_qdq_fwd_rows_batch.argtypes = [dp, i32, vp, vp]
+    L.mxfp4_ste_bwd_rows_batch.argtypes = [dp, i32, vp, vp]
     L.mxfp4_last_error.restype = ctypes.c_char_p
     return L
 
@@ -62,14 +64,15 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mxfp4_qdq_fwd", "mxfp4_ste_bwd", "mxfp4_quant_pack", "mxfp4_grouped_qdq",
               "mxfp4_quant_pack_kmajor", "mxfp4_dequant", "mxfp8_quant", "mxfp4_grouped_matmul", "mxfp8_quant_kmajor",
-              "mxfp4_mask_to_bool", "mxfp4_last_error", "mxfp4_version"):
+              "mxfp4_mask_to_bool", "mxfp4_qdq_fwd_rows_batch", "mxfp4_ste_bwd_rows_batch",
+              "mxfp4_last_error", "mxfp4_version"):
         assert n in names
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mxfp4_version() == 104
+    assert lib.mxfp4_version() == 105
 
 
 def d(dtype=BF16, block=32, rule=0, rows=64, cols=64, sf=6.0, r0=0, r1=0):
@@ -147,6 +150,47 @@ def test_mask_to_bool_validation(lib):
     assert m(ROW, 4, 4, P(), None, None) == EINVAL
     assert m(ROW, 4, 4, P(), P(FAKE), None) == EINVAL                # out aliases mask
     assert b"alias" in lib.mxfp4_last_error()
+
+
+class RowItem(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("mask", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class SteItem(ctypes.Structure):
+    _fields_ = [("grad_out", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("grad_in", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+def test_batch_validation(lib):
+    fb = lambda desc, items: lib.mxfp4_qdq_fwd_rows_batch(
+        ctypes.byref(desc) if desc is not None else None, len(items), (RowItem * max(len(items), 1))(*items), None)
+    sb = lambda desc, items: lib.mxfp4_ste_bwd_rows_batch(
+        ctypes.byref(desc) if desc is not None else None, len(items), (SteItem * max(len(items), 1))(*items), None)
+    F = FAKE
+    empty = RowItem(F, F + 64, None, None, 0, 64)
+    assert fb(d(), [empty]) == OK                                              # empty item: nothing launched
+    assert fb(d(), [empty, RowItem(F + 128, F + 192, None, None, 4, 0)]) == OK
+    assert fb(d(), []) == EINVAL                                               # n = 0
+    assert fb(d(), [empty] * 9) == EINVAL                                      # n > 8
+    assert fb(None, [empty]) == EINVAL
+    assert fb(d(block=64), [empty]) == EUNSUP
+    assert fb(d(), [RowItem(None, None, None, None, 0, 64)]) == OK             # empty: pointers not read
+    assert fb(d(), [RowItem(F, None, None, None, 4, 64)]) == EINVAL            # no output
+    assert fb(d(), [RowItem(F + 8, F + 64, None, None, 4, 64)]) == EINVAL      # misaligned x
+    assert fb(d(), [RowItem(F, F + 64, F + 2, None, 4, 64)]) == EINVAL         # misaligned bitmap
+    assert fb(d(), [RowItem(F, F + 64, None, None, -1, 64)]) == EINVAL
+    assert fb(d(), [RowItem(F, F + 64, None, None, 4, 64),
+                    RowItem(F + 256, F + 64, None, None, 4, 64)]) == EINVAL    # shared y
+    assert b"shares" in lib.mxfp4_last_error()
+    assert lib.mxfp4_qdq_fwd_rows_batch(ctypes.byref(d()), 1, None, None) == EINVAL
+    se = SteItem(F, None, F + 64, 0, 64)
+    assert sb(d(), [se]) == OK
+    assert sb(d(), [SteItem(F, None, F, 16, 64)]) == OK                        # plain, in place: no launch
+    assert sb(d(), [se] * 9) == EINVAL
+    assert sb(d(), [SteItem(F, F, F + 64, 4, 64)]) == EINVAL                   # mask aliases grad_out
+    assert sb(d(), [SteItem(F, None, F + 64, 4, 64), SteItem(F + 128, None, F + 64, 4, 64)]) == EINVAL
+    assert sb(d(), [SteItem(F, None, F + 72, 4, 64)]) == EINVAL                # misaligned grad_in
 
 
 def test_pack_and_grouped_validation(lib):

@@ -100,3 +100,26 @@ def test_bf16_qat_step_runs():
     loss.backward()
     opt.step()
     assert all(torch.isfinite(p).all() for p in model.parameters())
+
+
+@pytest.mark.parametrize("act_clipped", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_qat_linear_pair_launch_equals_separate_calls(act_clipped, dtype):
+    """A layer whose input and weight specs share block, rule and scale factor
+    quantizes both in one batched launch and runs their STEs in another; the
+    outputs and gradients are bit-identical to the per-tensor path."""
+    from mxfp4_fake_quantization_amd.qat import MXFP4Spec, QATLinear, QATPolicy, fake_quant
+    torch.manual_seed(3)
+    pol = QATPolicy(weight=MXFP4Spec(clipped=True), activation=MXFP4Spec(clipped=act_clipped))
+    lin = QATLinear(96, 40, policy=pol).cuda().to(dtype)
+    x = (torch.randn(2, 7, 96, device="cuda") * 3).to(dtype).requires_grad_(True)
+    out = lin(x)
+    up = torch.randn_like(out)
+    out.backward(up)
+    x2 = x.detach().clone().requires_grad_(True)
+    w2 = lin.weight.detach().clone().requires_grad_(True)
+    out2 = torch.nn.functional.linear(fake_quant(x2, pol.activation), fake_quant(w2, pol.weight), lin.bias.detach())
+    out2.backward(up)
+    assert torch.equal(out, out2)
+    assert torch.equal(x.grad, x2.grad)
+    assert torch.equal(lin.weight.grad, w2.grad)
