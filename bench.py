@@ -287,15 +287,20 @@ def build_weight4k(M, lib, W, torch, stream, sets):
                 fwd=fwd, bwd=bwd)
 
 
-def build_tiny(M, lib, W, torch, stream):
+def build_tiny(M, lib, W, torch, stream, keep_from=None):
+    """The tiny QAT step's calls on `stream`; keep_from reuses another
+    build's buffers."""
     tw, tx = W.tiny_qat(0)
     fwd, bwd, keep = [], [], []
     vp = ctypes.c_void_p
-    for arr in (tw, tx):
+    for k, arr in enumerate((tw, tx)):
         r, c = arr.shape
-        xt = torch.from_numpy(arr).cuda()
-        yt, gt, gi = torch.empty_like(xt), torch.ones_like(xt), torch.empty_like(xt)
-        mt = torch.empty((r, -(-c // 32)), dtype=torch.int32, device="cuda")
+        if keep_from is not None:
+            xt, yt, gt, gi, mt, _ = keep_from["keep"][k]
+        else:
+            xt = torch.from_numpy(arr).cuda()
+            yt, gt, gi = torch.empty_like(xt), torch.ones_like(xt), torch.empty_like(xt)
+            mt = torch.empty((r, -(-c // 32)), dtype=torch.int32, device="cuda")
         dt = M._Desc(0, 32, 0, 0, r, c, 6.0, 0)
         keep.append((xt, yt, gt, gi, mt, dt))
         fwd.append(Call(lib.mxfp4_qdq_fwd, ctypes.byref(dt), M.ROW, vp(xt.data_ptr()), vp(yt.data_ptr()),
@@ -566,6 +571,7 @@ def bench_configs(M, lib, W, torch, stream, probe, cpu, cpu_seconds):
     tq = build_tiny(M, lib, W, torch, stream)
     med, best = timer([tq["step_batched"]], reps=200)
     med4, best4 = timer([tq["step"]], reps=200)
+
     c1 = {"workload": "tiny QAT: fp32 W 32x64 + X 4x64, row-wise block-32 QDQ (y + bitmap) of both in one "
                       "batched launch, then the clipped STE of ones for both in another",
           "kernels": ["row_fwd_batch_kernel<f32,32,floor>", "ste_row_batch_kernel<f32>"],
