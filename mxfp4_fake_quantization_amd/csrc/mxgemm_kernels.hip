@@ -210,9 +210,10 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   // Chunk c holds, for every tile row, the scale bytes of blocks
   // [kb0 + 32c, kb0 + 32c + 32) (32 bytes, or 8 for 128-element blocks).
   // While chunk c is in use, chunk c + 1 arrives one 1/8 slice per step:
-  // step 8c + p loads rows [Rp, Rp + R) of A (waves of the first half) or of
-  // B (second half), R = NT / 16 rows (a tile has 8R rows), one dword per
-  // thread, 8 threads per 32-byte row.
+  // step 8c + p stores rows [Rp, Rp + R) of A (waves of the first half) or
+  // of B (second half), R = NT / 16 rows (a tile has 8R rows), one dword per
+  // thread, 8 threads per 32-byte row, loaded from global memory during the
+  // step before.
   // Bytes outside [klo, kb1) are replaced by 127 (2^0) when stored, so the
   // MFMAs of masked blocks (zero codes) see a finite scale.
   const bool sl_b = tid >= NT / 2;
@@ -223,11 +224,13 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   const uint8_t *s_base = sl_b ? bsbase : asbase;
   const int64_t s_ld = sl_b ? P.ldbs : P.ldas;
   const int64_t s_rows = sl_b ? nlen : mlen;
-  uint32_t pv[S4 ? 1 : 4];
-  int64_t pbyte = 0;
+  // A slice is loaded one step before it is stored (pv: loaded during the
+  // previous step, pc: its bytes as one dword, being stored), so that the
+  // step's last wait for its loads does not wait for the scattered scale rows.
+  uint32_t pv[S4 ? 1 : 4], pc;
   auto load_slice = [&](int64_t chunk, int piece) {
     const int row = piece * (NT / 16) + sr;
-    pbyte = ((kb0 + 32 * chunk) >> sb_log) + 4 * sd;
+    const int64_t pbyte = ((kb0 + 32 * chunk) >> sb_log) + 4 * sd;
     const uint8_t *rp = s_base + (int64_t)(row < s_rows ? row : s_rows - 1) * s_ld;
     const int64_t at = pbyte < s_hi ? pbyte : s_hi - 1;  // in bounds (s_hi <= row length)
     if (S4) {
@@ -237,12 +240,14 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
       for (int e = 0; e < (S4 ? 1 : 4); ++e) pv[e] = rp[at + e < s_hi ? at + e : s_hi - 1];
     }
   };
-  auto store_slice = [&](int sbuf, int piece) {
-    uint32_t v = pv[0];
-    if (!S4) {
+  auto take_slice = [&]() {
+    pc = pv[0];
 #pragma unroll
-      for (int e = 1; e < (S4 ? 1 : 4); ++e) v |= pv[e] << (8 * e);
-    }
+    for (int e = 1; e < (S4 ? 1 : 4); ++e) pc |= pv[e] << (8 * e);
+  };
+  auto store_slice = [&](int64_t chunk, int sbuf, int piece) {
+    const int64_t pbyte = ((kb0 + 32 * chunk) >> sb_log) + 4 * sd;
+    uint32_t v = pc;
     // keep bytes pbyte + e inside [s_lo, s_hi) and inside the chunk
     const int64_t lead = s_lo - pbyte, cnt = s_hi - pbyte;
     const int nlead = lead <= 0 ? 0 : (lead >= 4 ? 4 : (int)lead);
@@ -320,32 +325,40 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
     const int t = (int)(st & 1);
     const int64_t kb = kb0 + 4 * st;
     const int64_t kbn = B4 ? kb0 + 8 * ((st >> 1) + 1) : kb + 4;  // B's prefetch target
-    // scale bytes of blocks kb + h (s = 0) and kb + 2 + h (s = 1)
+    // scale bytes of blocks kb + h (s = 0) and kb + 2 + h (s = 1), each as
+    // byte 0 of a register: the MFMA reads only that byte (op_sel 0), so the
+    // dword is shifted, not masked (32-element blocks: the s = 1 byte is 2
+    // bytes further; 128-element blocks: one byte serves both)
     uint32_t csa[WM][2], csb[WN][2];
     {
       const int64_t ca = (kb0 + 32 * (st >> 3)) >> P.a_sb, cb = (kb0 + 32 * (st >> 3)) >> P.b_sb;
-      const int qa0 = (int)(((kb + h) >> P.a_sb) - ca), qa1 = (int)(((kb + 2 + h) >> P.a_sb) - ca);
-      const int qb0 = (int)(((kb + h) >> P.b_sb) - cb), qb1 = (int)(((kb + 2 + h) >> P.b_sb) - cb);
+      const int qa0 = (int)(((kb + h) >> P.a_sb) - ca), qb0 = (int)(((kb + h) >> P.b_sb) - cb);
+      const int sha = 8 * (qa0 & 3), shb = 8 * (qb0 & 3);
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
         const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSA[sbuf][(wr0 + 32 * i + l32) * 32 + (qa0 & ~3)]);
-        csa[i][0] = (w >> (8 * (qa0 & 3))) & 0xFFu;
-        csa[i][1] = (w >> (8 * (qa1 & 3))) & 0xFFu;
+        csa[i][0] = w >> sha;
+        csa[i][1] = P.a_sb ? csa[i][0] : csa[i][0] >> 16;
       }
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSB[sbuf][(wc0 + 32 * j + l32) * 32 + (qb0 & ~3)]);
-        csb[j][0] = (w >> (8 * (qb0 & 3))) & 0xFFu;
-        csb[j][1] = (w >> (8 * (qb1 & 3))) & 0xFFu;
+        csb[j][0] = w >> shb;
+        csb[j][1] = P.b_sb ? csb[j][0] : csb[j][0] >> 16;
       }
     }
     if (PA != 0) load_a(kb + 4, PA == 2);
     if (PB != 0) load_b(kbn, B4 ? t : 0, PB == 2);
-    if (PA != 0) load_slice((st >> 3) + 1, piece);
+    if (PA != 0) {
+      take_slice();
+      load_slice(((st + 1) >> 3) + 1, (int)((st + 1) & 7));
+    }
 
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      __builtin_amdgcn_sched_barrier(0);
+      // memory operations stay in their half; address and mask arithmetic may
+      // move between the MFMAs
+      __builtin_amdgcn_sched_barrier(0x6);
       v8i fa[WM], fb[WN];
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
@@ -383,11 +396,11 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
         }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep the waits for the prefetch after the MFMAs
+    __builtin_amdgcn_sched_barrier(0x6);  // keep the waits for the prefetch after the MFMAs
     if (PA != 0) store_a(buf ^ 1, PA == 2);
     if (PB != 0) store_b(bbuf ^ 1, B4 ? t : 0, PB == 2);
     if (PA != 0 || PB != 0) {
-      if (PA != 0) store_slice(sbuf ^ 1, piece);
+      if (PA != 0) store_slice((st >> 3) + 1, sbuf ^ 1, piece);
       __syncthreads();
     }
   };
@@ -406,9 +419,11 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
     }
     for (int piece = 0; piece < 8; ++piece) {
       load_slice(0, piece);
-      store_slice(0, piece);
+      take_slice();
+      store_slice(0, 0, piece);
     }
     __syncthreads();
+    load_slice(1, 0);  // stored during step 0
     int64_t st = 0;
     if (B4) {
       // only the first and the last step (A) or pair (B) can be partial: the
