@@ -79,6 +79,9 @@ struct GemmArgs {
   int64_t tiles_m, tiles_n, total;
 };
 
+typedef const uint8_t __attribute__((address_space(1))) *gp8;
+typedef const uint32_t __attribute__((address_space(1))) *gp32;
+
 // slot swizzle: conflict-free ds_read_b128 for 8 or 16 consecutive rows
 __device__ __forceinline__ int swz_a(int r, int c) { return (c ^ ((r ^ (r >> 3)) & 7)) << 4; }
 
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   bbase += n0 * P.ldb;
   bsbase += n0 * P.ldbs;
   const int lr = tid >> 3, lc = tid & 7;
-  uint32_t aoff[A_LD], boff[B4 ? 2 : 1][B_LD];
+  uint32_t aoff[A_LD], boff0[B_LD], boff1[B_LD];  // boff1: E2M1 B, second half of the rows
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
     const int row = lr + RSTEP * i;
@@ -202,7 +205,9 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       const int row = t * (BN / 2) + lr + RSTEP * i;  // B4: half t of the rows
-      boff[t][i] = (uint32_t)((row < nlen ? row : nlen - 1) * P.ldb) + 16 * lc;
+      const uint32_t o = (uint32_t)((row < nlen ? row : nlen - 1) * P.ldb) + 16 * lc;
+      if (t) boff1[i] = o;
+      else boff0[i] = o;
     }
   const int wr0 = (wave / WVN) * 32 * WM, wc0 = (wave % WVN) * 32 * WN;
 
@@ -216,25 +221,31 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   // step before.
   // Bytes outside [klo, kb1) are replaced by 127 (2^0) when stored, so the
   // MFMAs of masked blocks (zero codes) see a finite scale.
+  // A wave loads either A or B slices: the values below are wave-uniform and
+  // kept in scalar registers.  Row offsets fit 32 bits (rows <= 256, scale
+  // row strides <= 2^24 bytes).
   const bool sl_b = tid >= NT / 2;
   const int sr = (tid & (NT / 2 - 1)) >> 3, sd = tid & 7;
-  const int sb_log = sl_b ? P.b_sb : P.a_sb;
-  const int64_t s_lo = klo >> sb_log;                                   // first valid byte
-  const int64_t s_hi = (kb1 + (1 << sb_log) - 1) >> sb_log;            // past the last
-  const uint8_t *s_base = sl_b ? bsbase : asbase;
-  const int64_t s_ld = sl_b ? P.ldbs : P.ldas;
-  const int64_t s_rows = sl_b ? nlen : mlen;
+  const int sb_log = __builtin_amdgcn_readfirstlane(sl_b ? P.b_sb : P.a_sb);
+  const int s_lo = (int)(klo >> sb_log);                                // first valid byte
+  const int s_hi = (int)((kb1 + (1 << sb_log) - 1) >> sb_log);         // past the last
+  const uint64_t sbp = (uint64_t)(sl_b ? bsbase : asbase);
+  const gp8 s_base = (gp8)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(sbp >> 32)) << 32) |
+                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sbp));
+  const uint32_t s_ld = (uint32_t)__builtin_amdgcn_readfirstlane((int)(sl_b ? P.ldbs : P.ldas));
+  const int s_rows = __builtin_amdgcn_readfirstlane((int)(sl_b ? nlen : mlen));
   // A slice is loaded one step before it is stored (pv: loaded during the
   // previous step, pc: its bytes as one dword, being stored), so that the
   // step's last wait for its loads does not wait for the scattered scale rows.
   uint32_t pv[S4 ? 1 : 4], pc;
   auto load_slice = [&](int64_t chunk, int piece) {
-    const int row = piece * (NT / 16) + sr;
-    const int64_t pbyte = ((kb0 + 32 * chunk) >> sb_log) + 4 * sd;
-    const uint8_t *rp = s_base + (int64_t)(row < s_rows ? row : s_rows - 1) * s_ld;
-    const int64_t at = pbyte < s_hi ? pbyte : s_hi - 1;  // in bounds (s_hi <= row length)
+    const int rw = piece * (NT / 16) + sr;
+    const int row = rw < s_rows ? rw : s_rows - 1;
+    const int pbyte = (int)((kb0 + 32 * chunk) >> sb_log) + 4 * sd;
+    const gp8 rp = s_base + (uint32_t)row * s_ld;
+    const int at = pbyte < s_hi ? pbyte : s_hi - 1;  // in bounds (s_hi <= row length)
     if (S4) {
-      pv[0] = *reinterpret_cast<const uint32_t *>(rp + (at & ~(int64_t)3));
+      pv[0] = *(gp32)(rp + (at & ~3));
     } else {
 #pragma unroll
       for (int e = 0; e < (S4 ? 1 : 4); ++e) pv[e] = rp[at + e < s_hi ? at + e : s_hi - 1];
@@ -246,12 +257,12 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
     for (int e = 1; e < (S4 ? 1 : 4); ++e) pc |= pv[e] << (8 * e);
   };
   auto store_slice = [&](int64_t chunk, int sbuf, int piece) {
-    const int64_t pbyte = ((kb0 + 32 * chunk) >> sb_log) + 4 * sd;
+    const int pbyte = (int)((kb0 + 32 * chunk) >> sb_log) + 4 * sd;
     uint32_t v = pc;
     // keep bytes pbyte + e inside [s_lo, s_hi) and inside the chunk
-    const int64_t lead = s_lo - pbyte, cnt = s_hi - pbyte;
-    const int nlead = lead <= 0 ? 0 : (lead >= 4 ? 4 : (int)lead);
-    int nval = cnt <= 0 ? 0 : (cnt >= 4 ? 4 : (int)cnt);
+    const int lead = s_lo - pbyte, cnt = s_hi - pbyte;
+    const int nlead = lead <= 0 ? 0 : (lead >= 4 ? 4 : lead);
+    int nval = cnt <= 0 ? 0 : (cnt >= 4 ? 4 : cnt);
     if (4 * sd >= (32 >> sb_log)) nval = 0;
     const uint32_t hi_m = nval >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nval)) - 1u);
     const uint32_t lo_m = nlead >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nlead)) - 1u);
@@ -289,7 +300,7 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
       if (!bin) bt = ((kb1 - 1) << BSH) - 16 * lc;
     }
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) rb[i] = *reinterpret_cast<const u32x4 *>(bbase + bt + boff[t][i]);
+    for (int i = 0; i < B_LD; ++i) rb[i] = *reinterpret_cast<const u32x4 *>(bbase + bt + (B4 && t ? boff1[i] : boff0[i]));
   };
   auto store_a = [&](int buf, bool masked) {
 #pragma unroll
@@ -331,18 +342,20 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
     // bytes further; 128-element blocks: one byte serves both)
     uint32_t csa[WM][2], csb[WN][2];
     {
-      const int64_t ca = (kb0 + 32 * (st >> 3)) >> P.a_sb, cb = (kb0 + 32 * (st >> 3)) >> P.b_sb;
-      const int qa0 = (int)(((kb + h) >> P.a_sb) - ca), qb0 = (int)(((kb + h) >> P.b_sb) - cb);
-      const int sha = 8 * (qa0 & 3), shb = 8 * (qb0 & 3);
+      // kb0 is a multiple of 4: 32-element blocks kb .. kb + 3 are bytes
+      // 4 * piece .. 4 * piece + 3 of the chunk row, a 128-element block's
+      // byte is byte piece
+      const int qa = P.a_sb ? (piece & 4) : 4 * piece, qb = P.b_sb ? (piece & 4) : 4 * piece;
+      const int sha = P.a_sb ? 8 * (piece & 3) : 8 * h, shb = P.b_sb ? 8 * (piece & 3) : 8 * h;
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
-        const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSA[sbuf][(wr0 + 32 * i + l32) * 32 + (qa0 & ~3)]);
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSA[sbuf][(wr0 + 32 * i + l32) * 32 + qa]);
         csa[i][0] = w >> sha;
         csa[i][1] = P.a_sb ? csa[i][0] : csa[i][0] >> 16;
       }
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
-        const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSB[sbuf][(wc0 + 32 * j + l32) * 32 + (qb0 & ~3)]);
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSB[sbuf][(wc0 + 32 * j + l32) * 32 + qb]);
         csb[j][0] = w >> shb;
         csb[j][1] = P.b_sb ? csb[j][0] : csb[j][0] >> 16;
       }

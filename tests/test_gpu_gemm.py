@@ -174,12 +174,42 @@ def test_rows_split_group_stride_override(oracle):
 
 # ---- K-split groups (TN) --------------------------------------------------------
 
+MULTI_CHUNK_CASES = [
+    # name, M, N, K, group list, a block, b block
+    ("b128_both", 300, 260, 2176, [150, 150], 128, 128),
+    ("b128_a_only", 200, 130, 2176, [77, 123], 128, 32),
+    ("b128_a_k_tail", 150, 96, 2144, [70, 80], 128, 32),
+    ("b32_k_tail", 160, 100, 2144, [100, 60], 32, 32),
+    ("b32_aligned", 260, 70, 3072, [130, 0, 130], 32, 32),
+]
+
+
+@pytest.mark.parametrize("case", MULTI_CHUNK_CASES, ids=[c[0] for c in MULTI_CHUNK_CASES])
+def test_rows_split_multi_chunk(oracle, case):
+    """K spans several 1024-element scale chunks (the kernel stages scale
+    bytes 32 blocks of 32 at a time): 128- and 32-element scale blocks, K
+    tails, scale rows that are and are not a multiple of 4 bytes.  fp8
+    magnitudes below 2 keep every partial sum of up to 2176 products exact
+    in fp32."""
+    name, M, N, K, gl, ab, bb = case
+    g = np.random.default_rng(zlib.crc32(name.encode()))
+    a, sa = exact_operands(g, M, K, "e4m3", ab, lo=126, steps=1)
+    b, sb = exact_operands(g, N, K, "e2m1", bb, lo=126, groups=len(gl), steps=1)
+    got = run_rows(a, sa, b, sb, M, N, K, gl, 1, "e4m3", "e2m1", ab, bb, torch.float32)
+    exp = oracle_rows(oracle, a, sa, b, sb, M, N, K, gl, 1, "e4m3", "e2m1", ab, bb)
+    covered = ~np.isnan(exp[:, 0])
+    assert np.array_equal(got[covered], exp[covered].astype(np.float32))
+
+
 TN_CASES = [
     # name, M, N, token counts, k_blocks, b fmt
     ("fp8_fp8", 130, 70, [45, 0, 100, 31], 8, "e4m3"),
     ("fp8_fp4", 64, 96, [32, 1, 95], 9, "e2m1"),
     ("one_group_long", 40, 300, [600], 19, "e4m3"),
     ("all_empty", 33, 20, [0, 0], 2, "e4m3"),
+    # groups over more than one 32-block scale chunk (dword and byte scale rows)
+    ("multi_chunk_fp8", 64, 80, [1100, 700, 333], 68, "e4m3"),
+    ("multi_chunk_fp4", 96, 64, [1500, 31, 600], 67, "e2m1"),
 ]
 
 
