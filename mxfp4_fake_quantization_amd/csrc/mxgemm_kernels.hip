@@ -360,12 +360,18 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
         csb[j][1] = P.b_sb ? csb[j][0] : csb[j][0] >> 16;
       }
     }
-    if (PA != 0) load_a(kb + 4, PA == 2);
-    if (PB != 0) load_b(kbn, B4 ? t : 0, PB == 2);
-    if (PA != 0) {
-      take_slice();
-      load_slice(((st + 1) >> 3) + 1, (int)((st + 1) & 7));
-    }
+    // the next step's global loads: with fp8 B before the first fragment
+    // reads; with E2M1 B right after them, so that the reads' latency covers
+    // issuing the loads (2 % faster on the MoE layer)
+    auto prefetch = [&]() {
+      if (PA != 0) load_a(kb + 4, PA == 2);
+      if (PB != 0) load_b(kbn, B4 ? t : 0, PB == 2);
+      if (PA != 0) {
+        take_slice();
+        load_slice(((st + 1) >> 3) + 1, (int)((st + 1) & 7));
+      }
+    };
+    if (!B4) prefetch();
 
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -387,12 +393,19 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
           const u32x4 v = *reinterpret_cast<const u32x4 *>(&sB[bbuf][n * 128 + swz_a(n, 4 * t + 2 * s + h)]);
           fb[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
         }
+        if (s == 0) prefetch();
 #pragma unroll
         for (int i = 0; i < WM; ++i)
 #pragma unroll
           for (int j = 0; j < WN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AF, BF, 0,
                                                                         (int)csa[i][s], 0, (int)csb[j][s]);
+        if (s == 0 && PA == 1 && PB == 1) {
+          // in this order: the fragment reads, the prefetch loads, the MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * WM + WN, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, A_LD + B_LD + 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, WM * WN, 0);
+        }
       } else {
         // fp8 B fragments are 8 registers each: one at a time, so that the fp8 x
         // fp8 form stays close to the register budget
