@@ -24,13 +24,14 @@
 // one wave's LDS and address work overlaps the other's MFMAs); with fp8 B a
 // 256-thread workgroup computes 128 x 128 as 2 x 2 waves of 2 x 2 tiles, two
 // workgroups per CU.  K advances by 128 per step.  Both operand
-// slices go global -> registers -> LDS (double-buffered, XOR-swizzled 16-byte
-// slots, conflict-free for 16- and 32-lane read phases) while the previous
-// step's MFMAs run.  An E2M1 B row holds only 64 bytes per K step, half a
+// slices go global -> registers -> LDS (double-buffered, 128-byte rows at a
+// 144-byte stride: conflict-free 16-lane read phases, and every fragment
+// read is a per-lane base plus an immediate) while the previous step's
+// MFMAs run.  An E2M1 B row holds only 64 bytes per K step, half a
 // 128-byte cache line; B is therefore staged two K steps at a time (one
 // whole line per row, half of the tile's rows loaded during each step), so
-// every B request fetches a full line.  Scale bytes travel in chunks of 32
-// K-blocks per tile row (8 steps), also double-buffered in LDS and streamed
+// every B request fetches a full line.  Scale bytes travel in chunks of 16
+// K-blocks per tile row (4 steps), also double-buffered in LDS and streamed
 // one coalesced slice per step, so every lane reads its scale bytes with one
 // LDS load per tile.  The loop body is one basic block: prefetch, MFMAs, then
 // the prefetch waits and LDS stores.  Blocks outside a K range load as zero
@@ -82,9 +83,6 @@ struct GemmArgs {
 typedef const uint8_t __attribute__((address_space(1))) *gp8;
 typedef const uint32_t __attribute__((address_space(1))) *gp32;
 
-// slot swizzle: conflict-free ds_read_b128 for 8 or 16 consecutive rows
-__device__ __forceinline__ int swz_a(int r, int c) { return (c ^ ((r ^ (r >> 3)) & 7)) << 4; }
-
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
@@ -127,10 +125,14 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   constexpr int B_LD = BN * 8 / NT / (B4 ? 2 : 1);  // 16-byte B loads per thread per step
   static_assert(WVM * WVN * 64 == NT && BM == 32 * WM * WVM && BN == 32 * WN * WVN, "tile shape");
   static_assert(BM / 8 * 8 == NT / 2 && BN / 8 * 8 == NT / 2, "one scale dword per thread per step");
-  __shared__ __align__(16) uint8_t sA[2][BM * 128];
-  __shared__ __align__(16) uint8_t sB[2][BN * 128];
-  __shared__ __align__(16) uint8_t sSA[2][BM * 32];  // scale chunks (32 K-blocks per row)
-  __shared__ __align__(16) uint8_t sSB[2][BN * 32];
+  // operand rows of 128 bytes at a 144-byte stride: 16 lanes reading the
+  // same 16-byte slot of 16 consecutive rows hit all 64 banks once, and a
+  // lane's slot offsets are immediates
+  constexpr int RS = 144;
+  __shared__ __align__(16) uint8_t sA[2][BM * RS];
+  __shared__ __align__(16) uint8_t sB[2][BN * RS];
+  __shared__ __align__(16) uint8_t sSA[2][BM * 16];  // scale chunks (16 K-blocks per row)
+  __shared__ __align__(16) uint8_t sSB[2][BN * 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -211,13 +213,13 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
     }
   const int wr0 = (wave / WVN) * 32 * WM, wc0 = (wave % WVN) * 32 * WN;
 
-  // ---- scale bytes: chunks of 32 K-blocks (8 steps) staged in LDS ----
+  // ---- scale bytes: chunks of 16 K-blocks (4 steps) staged in LDS ----
   // Chunk c holds, for every tile row, the scale bytes of blocks
-  // [kb0 + 32c, kb0 + 32c + 32) (32 bytes, or 8 for 128-element blocks).
-  // While chunk c is in use, chunk c + 1 arrives one 1/8 slice per step:
-  // step 8c + p stores rows [Rp, Rp + R) of A (waves of the first half) or
-  // of B (second half), R = NT / 16 rows (a tile has 8R rows), one dword per
-  // thread, 8 threads per 32-byte row, loaded from global memory during the
+  // [kb0 + 16c, kb0 + 16c + 16) (16 bytes, or 4 for 128-element blocks).
+  // While chunk c is in use, chunk c + 1 arrives one quarter per step:
+  // step 4c + p stores rows [Rp, Rp + R) of A (waves of the first half) or
+  // of B (second half), R = NT / 8 rows (a tile has 4R rows), one dword per
+  // thread, 4 threads per 16-byte row, loaded from global memory during the
   // step before.
   // Bytes outside [klo, kb1) are replaced by 127 (2^0) when stored, so the
   // MFMAs of masked blocks (zero codes) see a finite scale.
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   // kept in scalar registers.  Row offsets fit 32 bits (rows <= 256, scale
   // row strides <= 2^24 bytes).
   const bool sl_b = tid >= NT / 2;
-  const int sr = (tid & (NT / 2 - 1)) >> 3, sd = tid & 7;
+  const int sr = (tid & (NT / 2 - 1)) >> 2, sd = tid & 3;
   const int sb_log = __builtin_amdgcn_readfirstlane(sl_b ? P.b_sb : P.a_sb);
   const int s_lo = (int)(klo >> sb_log);                                // first valid byte
   const int s_hi = (int)((kb1 + (1 << sb_log) - 1) >> sb_log);         // past the last
@@ -239,9 +241,9 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   // step's last wait for its loads does not wait for the scattered scale rows.
   uint32_t pv[S4 ? 1 : 4], pc;
   auto load_slice = [&](int64_t chunk, int piece) {
-    const int rw = piece * (NT / 16) + sr;
+    const int rw = piece * (NT / 8) + sr;
     const int row = rw < s_rows ? rw : s_rows - 1;
-    const int pbyte = (int)((kb0 + 32 * chunk) >> sb_log) + 4 * sd;
+    const int pbyte = (int)((kb0 + 16 * chunk) >> sb_log) + 4 * sd;
     const gp8 rp = s_base + (uint32_t)row * s_ld;
     const int at = pbyte < s_hi ? pbyte : s_hi - 1;  // in bounds (s_hi <= row length)
     if (S4) {
@@ -257,19 +259,19 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
     for (int e = 1; e < (S4 ? 1 : 4); ++e) pc |= pv[e] << (8 * e);
   };
   auto store_slice = [&](int64_t chunk, int sbuf, int piece) {
-    const int pbyte = (int)((kb0 + 32 * chunk) >> sb_log) + 4 * sd;
+    const int pbyte = (int)((kb0 + 16 * chunk) >> sb_log) + 4 * sd;
     uint32_t v = pc;
     // keep bytes pbyte + e inside [s_lo, s_hi) and inside the chunk
     const int lead = s_lo - pbyte, cnt = s_hi - pbyte;
     const int nlead = lead <= 0 ? 0 : (lead >= 4 ? 4 : lead);
     int nval = cnt <= 0 ? 0 : (cnt >= 4 ? 4 : cnt);
-    if (4 * sd >= (32 >> sb_log)) nval = 0;
+    if (4 * sd >= (16 >> sb_log)) nval = 0;
     const uint32_t hi_m = nval >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nval)) - 1u);
     const uint32_t lo_m = nlead >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nlead)) - 1u);
     const uint32_t keep = hi_m & ~lo_m;
     v = (v & keep) | (0x7F7F7F7Fu & ~keep);
     uint8_t *dst = sl_b ? &sSB[sbuf][0] : &sSA[sbuf][0];
-    *reinterpret_cast<uint32_t *>(dst + (piece * (NT / 16) + sr) * 32 + 4 * sd) = v;
+    *reinterpret_cast<uint32_t *>(dst + (piece * (NT / 8) + sr) * 16 + 4 * sd) = v;
   };
 
   // Codes global -> registers.  A: the K step starting at block kb (slot c =
@@ -306,14 +308,14 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
       const int row = lr + RSTEP * i;
-      *reinterpret_cast<u32x4 *>(&sA[buf][row * 128 + swz_a(row, lc)]) = (!masked || ain) ? ra[i] : zero4;
+      *reinterpret_cast<u32x4 *>(&sA[buf][row * RS + 16 * lc]) = (!masked || ain) ? ra[i] : zero4;
     }
   };
   auto store_b = [&](int buf, int t, bool masked) {
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       const int row = t * (BN / 2) + lr + RSTEP * i;
-      *reinterpret_cast<u32x4 *>(&sB[buf][row * 128 + swz_a(row, lc)]) = (!masked || bin) ? rb[i] : zero4;
+      *reinterpret_cast<u32x4 *>(&sB[buf][row * RS + 16 * lc]) = (!masked || bin) ? rb[i] : zero4;
     }
   };
 
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   // B loads half of the next pair of steps during each step of a pair.
   auto step = [&](int64_t st, auto pfa, auto pfb) {
     constexpr int PA = decltype(pfa)::value, PB = decltype(pfb)::value;
-    const int buf = (int)(st & 1), sbuf = (int)((st >> 3) & 1), piece = (int)(st & 7);
+    const int buf = (int)(st & 1), sbuf = (int)((st >> 2) & 1), piece = (int)(st & 3);
     const int bbuf = B4 ? (int)((st >> 1) & 1) : buf;
     const int t = (int)(st & 1);
     const int64_t kb = kb0 + 4 * st;
@@ -345,17 +347,17 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
       // kb0 is a multiple of 4: 32-element blocks kb .. kb + 3 are bytes
       // 4 * piece .. 4 * piece + 3 of the chunk row, a 128-element block's
       // byte is byte piece
-      const int qa = P.a_sb ? (piece & 4) : 4 * piece, qb = P.b_sb ? (piece & 4) : 4 * piece;
-      const int sha = P.a_sb ? 8 * (piece & 3) : 8 * h, shb = P.b_sb ? 8 * (piece & 3) : 8 * h;
+      const int qa = P.a_sb ? 0 : 4 * piece, qb = P.b_sb ? 0 : 4 * piece;
+      const int sha = P.a_sb ? 8 * piece : 8 * h, shb = P.b_sb ? 8 * piece : 8 * h;
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
-        const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSA[sbuf][(wr0 + 32 * i + l32) * 32 + qa]);
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSA[sbuf][(wr0 + 32 * i + l32) * 16 + qa]);
         csa[i][0] = w >> sha;
         csa[i][1] = P.a_sb ? csa[i][0] : csa[i][0] >> 16;
       }
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
-        const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSB[sbuf][(wc0 + 32 * j + l32) * 32 + qb]);
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSB[sbuf][(wc0 + 32 * j + l32) * 16 + qb]);
         csb[j][0] = w >> shb;
         csb[j][1] = P.b_sb ? csb[j][0] : csb[j][0] >> 16;
       }
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
       if (PB != 0) load_b(kbn, B4 ? t : 0, PB == 2);
       if (PA != 0) {
         take_slice();
-        load_slice(((st + 1) >> 3) + 1, (int)((st + 1) & 7));
+        load_slice(((st + 1) >> 2) + 1, (int)((st + 1) & 3));
       }
     };
     if (!B4) prefetch();
@@ -382,15 +384,15 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
         const int r = wr0 + 32 * i + l32;
-        const u32x4 lo = *reinterpret_cast<const u32x4 *>(&sA[buf][r * 128 + swz_a(r, 4 * s + h)]);
-        const u32x4 hi = *reinterpret_cast<const u32x4 *>(&sA[buf][r * 128 + swz_a(r, 4 * s + 2 + h)]);
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(&sA[buf][r * RS + 16 * (4 * s + h)]);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(&sA[buf][r * RS + 16 * (4 * s + 2 + h)]);
         fa[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
       if (B4) {
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
           const int n = wc0 + 32 * j + l32;
-          const u32x4 v = *reinterpret_cast<const u32x4 *>(&sB[bbuf][n * 128 + swz_a(n, 4 * t + 2 * s + h)]);
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(&sB[bbuf][n * RS + 16 * (4 * t + 2 * s + h)]);
           fb[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
         }
         if (s == 0) prefetch();
@@ -412,8 +414,8 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
           const int n = wc0 + 32 * j + l32;
-          const u32x4 lo = *reinterpret_cast<const u32x4 *>(&sB[buf][n * 128 + swz_a(n, 4 * s + h)]);
-          const u32x4 hi = *reinterpret_cast<const u32x4 *>(&sB[buf][n * 128 + swz_a(n, 4 * s + 2 + h)]);
+          const u32x4 lo = *reinterpret_cast<const u32x4 *>(&sB[buf][n * RS + 16 * (4 * s + h)]);
+          const u32x4 hi = *reinterpret_cast<const u32x4 *>(&sB[buf][n * RS + 16 * (4 * s + 2 + h)]);
           fb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 #pragma unroll
           for (int i = 0; i < WM; ++i)
@@ -426,7 +428,7 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
     if (PA != 0) store_a(buf ^ 1, PA == 2);
     if (PB != 0) store_b(bbuf ^ 1, B4 ? t : 0, PB == 2);
     if (PA != 0 || PB != 0) {
-      if (PA != 0) store_slice((st >> 3) + 1, sbuf ^ 1, piece);
+      if (PA != 0) store_slice((st >> 2) + 1, sbuf ^ 1, piece);
       __syncthreads();
     }
   };
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
       load_b(kb0, t, true);
       store_b(0, t, true);
     }
-    for (int piece = 0; piece < 8; ++piece) {
+    for (int piece = 0; piece < 4; ++piece) {
       load_slice(0, piece);
       take_slice();
       store_slice(0, 0, piece);
