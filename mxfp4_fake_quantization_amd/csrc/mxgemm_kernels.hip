@@ -111,6 +111,12 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t id, int64_t total) {
   return x < r ? x * (q + 1) + loc : r * (q + 1) + (x - r) * q + loc;
 }
 
+// One scaled MFMA taking byte OS of each scale register.
+template <int AF, int BF, int OS>
+__device__ __forceinline__ v16f mfma_sel(v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, AF, BF, OS, (int)sa, OS, (int)sb);
+}
+
 template <int AF, int BF, bool S4>
 __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void mxgemm_kernel(GemmArgs P) {
   using Sh = GemmShape<BF>;
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   auto load_slice = [&](int64_t chunk, int piece) {
     const int rw = piece * (NT / 8) + sr;
     const int row = rw < s_rows ? rw : s_rows - 1;
-    const int pbyte = (int)((kb0 + 16 * chunk) >> sb_log) + 4 * sd;
+    const int pbyte = (int)((kb0 + 16 * chunk) >> sb_log) + (sb_log ? 0 : 4 * sd);
     const gp8 rp = s_base + (uint32_t)row * s_ld;
     const int at = pbyte < s_hi ? pbyte : s_hi - 1;  // in bounds (s_hi <= row length)
     if (S4) {
@@ -259,17 +265,20 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
     for (int e = 1; e < (S4 ? 1 : 4); ++e) pc |= pv[e] << (8 * e);
   };
   auto store_slice = [&](int64_t chunk, int sbuf, int piece) {
-    const int pbyte = (int)((kb0 + 16 * chunk) >> sb_log) + 4 * sd;
+    const int pbyte = (int)((kb0 + 16 * chunk) >> sb_log) + (sb_log ? 0 : 4 * sd);
     uint32_t v = pc;
-    // keep bytes pbyte + e inside [s_lo, s_hi) and inside the chunk
+    // keep bytes pbyte + e inside [s_lo, s_hi)
     const int lead = s_lo - pbyte, cnt = s_hi - pbyte;
     const int nlead = lead <= 0 ? 0 : (lead >= 4 ? 4 : lead);
-    int nval = cnt <= 0 ? 0 : (cnt >= 4 ? 4 : cnt);
-    if (4 * sd >= (16 >> sb_log)) nval = 0;
+    const int nval = cnt <= 0 ? 0 : (cnt >= 4 ? 4 : cnt);
     const uint32_t hi_m = nval >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nval)) - 1u);
     const uint32_t lo_m = nlead >= 4 ? 0xFFFFFFFFu : ((1u << (8 * nlead)) - 1u);
     const uint32_t keep = hi_m & ~lo_m;
     v = (v & keep) | (0x7F7F7F7Fu & ~keep);
+    // 128-element blocks: the chunk's 4 bytes are one per step; thread sd
+    // writes step sd's byte once per 32-element block, so that a chunk row
+    // reads the same way for both block sizes
+    if (sb_log) v = ((v >> (8 * sd)) & 0xFFu) * 0x01010101u;
     uint8_t *dst = sl_b ? &sSB[sbuf][0] : &sSA[sbuf][0];
     *reinterpret_cast<uint32_t *>(dst + (piece * (NT / 8) + sr) * 16 + 4 * sd) = v;
   };
@@ -331,37 +340,26 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   // scale slice, PB for B; 0 none, 1 unmasked, 2 masked), the MFMAs, then the
   // LDS stores of the prefetch and the barrier.  fp8 B follows A's step; E2M1
   // B loads half of the next pair of steps during each step of a pair.
-  auto step = [&](int64_t st, auto pfa, auto pfb) {
+  auto step = [&](int64_t st, auto pfa, auto pfb, auto ph) {
     constexpr int PA = decltype(pfa)::value, PB = decltype(pfb)::value;
-    const int buf = (int)(st & 1), sbuf = (int)((st >> 2) & 1), piece = (int)(st & 3);
-    const int bbuf = B4 ? (int)((st >> 1) & 1) : buf;
-    const int t = (int)(st & 1);
+    constexpr int PH = decltype(ph)::value;  // st % 8 when known at compile time, else -1
+    const int ph8 = PH >= 0 ? PH : (int)(st & 7);
+    const int buf = ph8 & 1, sbuf = (ph8 >> 2) & 1, piece = ph8 & 3;
+    const int bbuf = B4 ? (ph8 >> 1) & 1 : buf;
+    const int t = ph8 & 1;
     const int64_t kb = kb0 + 4 * st;
     const int64_t kbn = B4 ? kb0 + 8 * ((st >> 1) + 1) : kb + 4;  // B's prefetch target
-    // scale bytes of blocks kb + h (s = 0) and kb + 2 + h (s = 1), each as
-    // byte 0 of a register: the MFMA reads only that byte (op_sel 0), so the
-    // dword is shifted, not masked (32-element blocks: the s = 1 byte is 2
-    // bytes further; 128-element blocks: one byte serves both)
-    uint32_t csa[WM][2], csb[WN][2];
-    {
-      // kb0 is a multiple of 4: 32-element blocks kb .. kb + 3 are bytes
-      // 4 * piece .. 4 * piece + 3 of the chunk row, a 128-element block's
-      // byte is byte piece
-      const int qa = P.a_sb ? 0 : 4 * piece, qb = P.b_sb ? 0 : 4 * piece;
-      const int sha = P.a_sb ? 8 * piece : 8 * h, shb = P.b_sb ? 8 * piece : 8 * h;
+    // scale bytes of blocks kb + h (s = 0) and kb + 2 + h (s = 1): bytes
+    // 4 * piece + h and 4 * piece + 2 + h of the chunk row (kb0 is a
+    // multiple of 4), shifted down by h bytes into bytes 0 and 2 of one
+    // register, which the MFMAs of the two halves pick with op_sel 0 and 2
+    uint32_t csa[WM], csb[WN];
 #pragma unroll
-      for (int i = 0; i < WM; ++i) {
-        const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSA[sbuf][(wr0 + 32 * i + l32) * 16 + qa]);
-        csa[i][0] = w >> sha;
-        csa[i][1] = P.a_sb ? csa[i][0] : csa[i][0] >> 16;
-      }
+    for (int i = 0; i < WM; ++i)
+      csa[i] = *reinterpret_cast<const uint32_t *>(&sSA[sbuf][(wr0 + 32 * i + l32) * 16 + 4 * piece]) >> (8 * h);
 #pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        const uint32_t w = *reinterpret_cast<const uint32_t *>(&sSB[sbuf][(wc0 + 32 * j + l32) * 16 + qb]);
-        csb[j][0] = w >> shb;
-        csb[j][1] = P.b_sb ? csb[j][0] : csb[j][0] >> 16;
-      }
-    }
+    for (int j = 0; j < WN; ++j)
+      csb[j] = *reinterpret_cast<const uint32_t *>(&sSB[sbuf][(wc0 + 32 * j + l32) * 16 + 4 * piece]) >> (8 * h);
     // the next step's global loads: with fp8 B before the first fragment
     // reads; with E2M1 B right after them, so that the reads' latency covers
     // issuing the loads (2 % faster on the MoE layer)
@@ -400,8 +398,8 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
         for (int i = 0; i < WM; ++i)
 #pragma unroll
           for (int j = 0; j < WN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AF, BF, 0,
-                                                                        (int)csa[i][s], 0, (int)csb[j][s]);
+            acc[i][j] = s == 0 ? mfma_sel<AF, BF, 0>(fa[i], fb[j], acc[i][j], csa[i], csb[j])
+                               : mfma_sel<AF, BF, 2>(fa[i], fb[j], acc[i][j], csa[i], csb[j]);
         if (s == 0 && PA == 1 && PB == 1) {
           // in this order: the fragment reads, the prefetch loads, the MFMAs
           __builtin_amdgcn_sched_group_barrier(0x100, 2 * WM + WN, 0);
@@ -419,8 +417,8 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
           fb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 #pragma unroll
           for (int i = 0; i < WM; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AF, BF, 0,
-                                                                        (int)csa[i][s], 0, (int)csb[j][s]);
+            acc[i][j] = s == 0 ? mfma_sel<AF, BF, 0>(fa[i], fb[j], acc[i][j], csa[i], csb[j])
+                               : mfma_sel<AF, BF, 2>(fa[i], fb[j], acc[i][j], csa[i], csb[j]);
         }
       }
     }
@@ -436,6 +434,21 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
+  using R = std::integral_constant<int, -1>;
+  // eight unmasked steps from a multiple of 8: every buffer index and byte
+  // offset of a step is then a compile-time constant (87 instead of 161
+  // instructions per step for fp8 B; the E2M1 form keeps its rolled loop,
+  // whose unrolled copy spilled the addresses the compiler hoisted)
+  auto eight = [&](int64_t s8) {
+    step(s8, I1{}, I1{}, std::integral_constant<int, 0>{});
+    step(s8 + 1, I1{}, I1{}, std::integral_constant<int, 1>{});
+    step(s8 + 2, I1{}, I1{}, std::integral_constant<int, 2>{});
+    step(s8 + 3, I1{}, I1{}, std::integral_constant<int, 3>{});
+    step(s8 + 4, I1{}, I1{}, std::integral_constant<int, 4>{});
+    step(s8 + 5, I1{}, I1{}, std::integral_constant<int, 5>{});
+    step(s8 + 6, I1{}, I1{}, std::integral_constant<int, 6>{});
+    step(s8 + 7, I1{}, I1{}, std::integral_constant<int, 7>{});
+  };
   const int64_t nsteps = (kb1 - kb0 + 3) >> 2;
   if (nsteps > 0) {
     load_a(kb0, true);
@@ -459,16 +472,17 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
       // code for the last (up to four) steps
       const int64_t npairs = (nsteps + 1) >> 1;
       if (npairs >= 2) {
-        for (; st < 2 * npairs - 4; ++st) step(st, I1{}, I1{});
-        step(st++, I2{}, I2{});
-        step(st++, I2{}, I2{});
+        for (; st < 2 * npairs - 4; ++st) step(st, I1{}, I1{}, R{});
+        step(st++, I2{}, I2{}, R{});
+        step(st++, I2{}, I2{}, R{});
       }
-      if (nsteps - st == 2) step(st++, I2{}, I0{});
-      step(st, I0{}, I0{});
+      if (nsteps - st == 2) step(st++, I2{}, I0{}, R{});
+      step(st, I0{}, I0{}, R{});
     } else {
-      for (; st + 2 < nsteps; ++st) step(st, I1{}, I1{});
-      if (st + 1 < nsteps) step(st++, I2{}, I2{});
-      step(st, I0{}, I0{});
+      for (; st + 10 <= nsteps; st += 8) eight(st);
+      for (; st + 2 < nsteps; ++st) step(st, I1{}, I1{}, R{});
+      if (st + 1 < nsteps) step(st++, I2{}, I2{}, R{});
+      step(st, I0{}, I0{}, R{});
     }
   }
 
