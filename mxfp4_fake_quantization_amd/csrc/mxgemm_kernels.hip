@@ -32,9 +32,11 @@
 // whole line per row, half of the tile's rows loaded during each step), so
 // every B request fetches a full line.  Scale bytes travel in chunks of 16
 // K-blocks per tile row (4 steps), also double-buffered in LDS and streamed
-// one coalesced slice per step, so every lane reads its scale bytes with one
-// LDS load per tile.  The loop body is one basic block: prefetch, MFMAs, then
-// the prefetch waits and LDS stores.  Blocks outside a K range load as zero
+// one coalesced slice per step, so every lane reads a tile row's scale bytes
+// for a whole step with one LDS load (the two K halves take bytes 0 and 2 of
+// that register through the MFMA's op_sel).  The loop body is one basic
+// block: the next step's global loads, the fragment reads and MFMAs, then
+// the prefetch's LDS stores and one barrier.  Blocks outside a K range load as zero
 // codes with scale 2^0; rows and columns past the tile edge load a valid
 // neighbour and are not stored.
 #include "mxfp4_device.h"
