@@ -52,21 +52,19 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Tile shape by the format of B.  E2M1 B: 8 waves per workgroup (2 per
-// SIMD, so one wave's LDS and address work overlaps the other's MFMAs), 4 x 2
-// waves of 2 x 4 MFMA tiles = 256 x 256, one workgroup per CU (160 KiB of
-// LDS).  fp8 B, whose fragments are twice as large: 4 waves of 2 x 2 MFMA
-// tiles = 128 x 128, two workgroups per CU (80 KiB of LDS each), which keeps
-// every value in registers (the 256 x 256 form spilled 41-44 dwords per lane)
-// and measured 793 -> 755 us on the MoE weight gradient; for E2M1 B the
-// smaller tile measured slower (NN 589 -> 630 us, NT 657 -> 752 us).
+// Tile shape (both B formats): 8 waves per workgroup (2 per SIMD, so one
+// wave's LDS and address work overlaps the other's MFMAs), 4 x 2 waves of
+// 2 x 4 MFMA tiles = 256 x 256, one workgroup per CU (160 KiB of LDS).  The
+// fp8-B form (fragments twice as large) used 128 x 128 tiles, two workgroups
+// per CU, while its 256 x 256 form spilled; with the scale and address
+// registers trimmed it fits (no scratch) and measured 644 -> 566 us on the
+// MoE weight gradient.
 template <int BF>
 struct GemmShape {
-  static constexpr bool small = BF != kFmtE2M1;
-  static constexpr int wavesM = small ? 2 : 4, wavesN = 2, tilesM = 2, tilesN = small ? 2 : 4;
+  static constexpr int wavesM = 4, wavesN = 2, tilesM = 2, tilesN = 4;
   static constexpr int threads = 64 * wavesM * wavesN;
   static constexpr int BM = 32 * tilesM * wavesM, BN = 32 * tilesN * wavesN;
-  static constexpr int per_cu = small ? 2 : 1;  // workgroups per CU
+  static constexpr int per_cu = 1;  // workgroups per CU
 };
 
 struct GemmArgs {
@@ -178,10 +176,11 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
     const int64_t per = P.tiles_m * P.tiles_n;
     const int g = (int)(tile / per);
     const int64_t r = tile - (int64_t)g * per;
-    // bands of 8 M-tiles (TN on the MoE layer: re-reads 10.2x -> 5.1x the
-    // unique bytes, 809 -> 773 us)
+    // bands of 4 M-tiles (TN on the MoE layer, 256 x 256 tiles: 578 us with
+    // bands of 8, 565 with 2, 561 with 4; with the earlier 128 x 128 tiles
+    // bands of 8 took the re-reads from 10.2x to 5.1x the unique bytes)
     int64_t tm, tn;
-    band_tile(r, P.tiles_m, P.tiles_n, 8, &tm, &tn);
+    band_tile(r, P.tiles_m, P.tiles_n, 4, &tm, &tn);
     m0 = tm * BM;
     mlen = P.M - m0 < BM ? P.M - m0 : BM;
     n0 = tn * BN;
@@ -342,13 +341,11 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   // scale slice, PB for B; 0 none, 1 unmasked, 2 masked), the MFMAs, then the
   // LDS stores of the prefetch and the barrier.  fp8 B follows A's step; E2M1
   // B loads half of the next pair of steps during each step of a pair.
-  auto step = [&](int64_t st, auto pfa, auto pfb, auto ph) {
+  auto step = [&](int64_t st, auto pfa, auto pfb) {
     constexpr int PA = decltype(pfa)::value, PB = decltype(pfb)::value;
-    constexpr int PH = decltype(ph)::value;  // st % 8 when known at compile time, else -1
-    const int ph8 = PH >= 0 ? PH : (int)(st & 7);
-    const int buf = ph8 & 1, sbuf = (ph8 >> 2) & 1, piece = ph8 & 3;
-    const int bbuf = B4 ? (ph8 >> 1) & 1 : buf;
-    const int t = ph8 & 1;
+    const int buf = (int)(st & 1), sbuf = (int)((st >> 2) & 1), piece = (int)(st & 3);
+    const int bbuf = B4 ? (int)((st >> 1) & 1) : buf;
+    const int t = (int)(st & 1);
     const int64_t kb = kb0 + 4 * st;
     const int64_t kbn = B4 ? kb0 + 8 * ((st >> 1) + 1) : kb + 4;  // B's prefetch target
     // scale bytes of blocks kb + h (s = 0) and kb + 2 + h (s = 1): bytes
@@ -436,21 +433,6 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  using R = std::integral_constant<int, -1>;
-  // eight unmasked steps from a multiple of 8: every buffer index and byte
-  // offset of a step is then a compile-time constant (87 instead of 161
-  // instructions per step for fp8 B; the E2M1 form keeps its rolled loop,
-  // whose unrolled copy spilled the addresses the compiler hoisted)
-  auto eight = [&](int64_t s8) {
-    step(s8, I1{}, I1{}, std::integral_constant<int, 0>{});
-    step(s8 + 1, I1{}, I1{}, std::integral_constant<int, 1>{});
-    step(s8 + 2, I1{}, I1{}, std::integral_constant<int, 2>{});
-    step(s8 + 3, I1{}, I1{}, std::integral_constant<int, 3>{});
-    step(s8 + 4, I1{}, I1{}, std::integral_constant<int, 4>{});
-    step(s8 + 5, I1{}, I1{}, std::integral_constant<int, 5>{});
-    step(s8 + 6, I1{}, I1{}, std::integral_constant<int, 6>{});
-    step(s8 + 7, I1{}, I1{}, std::integral_constant<int, 7>{});
-  };
   const int64_t nsteps = (kb1 - kb0 + 3) >> 2;
   if (nsteps > 0) {
     load_a(kb0, true);
@@ -474,17 +456,16 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
       // code for the last (up to four) steps
       const int64_t npairs = (nsteps + 1) >> 1;
       if (npairs >= 2) {
-        for (; st < 2 * npairs - 4; ++st) step(st, I1{}, I1{}, R{});
-        step(st++, I2{}, I2{}, R{});
-        step(st++, I2{}, I2{}, R{});
+        for (; st < 2 * npairs - 4; ++st) step(st, I1{}, I1{});
+        step(st++, I2{}, I2{});
+        step(st++, I2{}, I2{});
       }
-      if (nsteps - st == 2) step(st++, I2{}, I0{}, R{});
-      step(st, I0{}, I0{}, R{});
+      if (nsteps - st == 2) step(st++, I2{}, I0{});
+      step(st, I0{}, I0{});
     } else {
-      for (; st + 10 <= nsteps; st += 8) eight(st);
-      for (; st + 2 < nsteps; ++st) step(st, I1{}, I1{}, R{});
-      if (st + 1 < nsteps) step(st++, I2{}, I2{}, R{});
-      step(st, I0{}, I0{}, R{});
+      for (; st + 2 < nsteps; ++st) step(st, I1{}, I1{});
+      if (st + 1 < nsteps) step(st++, I2{}, I2{});
+      step(st, I0{}, I0{});
     }
   }
 

@@ -1,5 +1,6 @@
 """Host-side check of the compiled gfx950 kernels (no GPU): the streaming
-kernels' common paths for bf16 keep everything in registers.  Register
+kernels' common paths for bf16 and every grouped-matmul kernel keep
+everything in registers.  Register
 spills go to scratch memory, whose stores are HBM writes the algorithmic
 bytes do not count (a spill of five registers in the K-major pack once added
 40 % to its writes).  Each source is compiled to gfx950 assembly and, for
@@ -18,6 +19,7 @@ CSRC = os.path.join(ROOT, "mxfp4_fake_quantization_amd", "csrc")
 HIPCC = "/opt/rocm/bin/hipcc"
 # kernel name fragment -> symbol pattern of its bf16 (DT = 1) vector forms
 FILES = {
+    "mxgemm_kernels": r"mxgemm_kernel",
     "row_kernels": r"row_fwd_kernelILi1E",
     "col_kernels": r"col_fwd_kernelILi1E.*Lb1EEEv",
     "ste_kernels": r"ste_(row|col)_kernelILi1E",
@@ -89,3 +91,23 @@ def test_fp32_kmajor_pack_touches_no_scratch(asm):
     fp32 = {k: v for k, v in out.items() if re.search(r"kmajor_pack_kernelILi0E", k)}
     assert len(fp32) == 16, sorted(fp32)
     assert not any(fp32.values()), {k: v for k, v in fp32.items() if v}
+
+
+def test_matmul_kernels_touch_no_scratch(asm):
+    """Every grouped-matmul instantiation (fp8 or E2M1 B, dword-aligned scale
+    rows or not) keeps its accumulators, prefetch and addresses in registers:
+    no scratch access anywhere in the kernel."""
+    out, cur, n = {}, None, 0
+    for line in asm["mxgemm_kernels"].split("\n"):
+        m = re.match(r"^(_Z\S+):", line)
+        if m:
+            if cur:
+                out[cur] = n
+            cur, n = m.group(1), 0
+        elif cur and "scratch_" in line:
+            n += 1
+    if cur:
+        out[cur] = n
+    gemm = {k: v for k, v in out.items() if "mxgemm_kernel" in k}
+    assert len(gemm) == 12, sorted(gemm)
+    assert not any(gemm.values()), {k: v for k, v in gemm.items() if v}
