@@ -77,6 +77,7 @@ struct GemmArgs {
   int G, list_type, group_type, out_f32;
   int a_sb, b_sb;        // log2(scale block / 32): 0 or 2
   int s4;                // both scale arrays have dword-aligned rows: dword slice loads
+  int c16;               // bf16 output with 16-byte aligned rows: whole tiles stored through LDS
   int64_t tiles_m, tiles_n, total;
 };
 
@@ -475,7 +476,32 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
     else static_cast<uint16_t *>(P.c)[off] = f32_to_bf16_rne(v);
   };
   const int64_t cb = cbase + m0 * P.ldc + n0;
-  if (mlen == BM && nlen == BN) {
+  if (P.c16 && mlen == BM && nlen == BN) {
+    // bf16 tile staged in LDS (rows 0-127 in the A buffers, 128-255 in the B
+    // buffers, 528-byte row stride) and written as 16-byte row pieces: 16
+    // stores per lane instead of 128 two-byte ones
+    constexpr int OS = 528;
+    __syncthreads();  // every wave is past its last fragment read
+    uint8_t *half = wr0 < 128 ? &sA[0][0] : &sB[0][0];
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = (wr0 & 127) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          *reinterpret_cast<uint16_t *>(half + r * OS + 2 * (wc0 + 32 * j + l32)) = f32_to_bf16_rne(acc[i][j][v]);
+        }
+    __syncthreads();
+    const int ch = tid & 31;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int row = (tid >> 5) + 16 * k;
+      const uint8_t *src = (k < 8 ? &sA[0][0] : &sB[0][0]) + (row & 127) * OS + 16 * ch;
+      *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(P.c) + cb + row * P.ldc + 8 * ch) =
+          *reinterpret_cast<const u32x4 *>(src);
+    }
+  } else if (mlen == BM && nlen == BN) {
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
@@ -561,6 +587,7 @@ hipError_t launch_mx_gemm(const GemmLaunch &L, hipStream_t st) {
   a.b_sb = L.b_block == 128 ? 2 : 0;
   a.s4 = ((uintptr_t)L.as % 4 == 0 && (uintptr_t)L.bs % 4 == 0 && L.ldas % 4 == 0 && L.ldbs % 4 == 0 &&
           L.b_gss % 4 == 0);
+  a.c16 = !L.out_f32 && (uintptr_t)L.c % 16 == 0 && L.ldc % 8 == 0;
   return L.a_fmt == kFmtE4M3 ? gemm_launch_b<kFmtE4M3>(L.b_fmt, a, st) : gemm_launch_b<kFmtE5M2>(L.b_fmt, a, st);
 }
 
