@@ -32,7 +32,9 @@ Also on the line:
 - configs: every other workload at full size (tiny QAT latency, dual
   direction, grouped MoE, packing at blocks 32 and 128), each with GB/s,
   elements/s, its fraction of the HBM peak and the oracle timed on a bounded
-  sample of the same input (--no-configs skips them).
+  sample of the same input (--no-configs skips them);
+- grouped_matmul: the grouped MX matmul of the MoE layer (NN / NT / TN), in
+  TFLOP/s against the 5.0 PFLOP/s dense fp8 matrix peak (with the configs).
 
 --all OUT.json additionally times the f-rows (K-major packs, decode, MXFP8,
 column-only, a device copy, the grouped matmuls) and writes them to OUT.json.
@@ -1373,6 +1375,14 @@ def main():
         result["steady_state"] = steady_state(M, lib, W, torch, stream, probe)
     if not args.no_configs:
         result["configs"] = bench_configs(M, lib, W, torch, stream, probe, not args.no_cpu, args.cpu_seconds)
+        torch.cuda.empty_cache()
+        result["grouped_matmul"] = {
+            "workload": "MoE layer, synthetic: tokens 32768 x hidden 7168, 8 experts of width 2048 "
+                        "(NN forward, NT input gradient, TN weight gradient; 0.962 TFLOP each)",
+            "bound": "mfma", "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "layouts": bench_gemm(M, W, torch, {}),
+        }
+        torch.cuda.empty_cache()
     if args.all:
         result["other_workloads_file"] = args.all
         with open(args.all, "w") as f:
