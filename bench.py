@@ -885,7 +885,9 @@ def profile_gemm(M, W, torch, run):
     """The grouped matmul on the MoE layer (tokens 32768 x hidden 7168, 8
     experts of width 2048): NN forward, NT input gradient, TN weight gradient,
     with the operands of bench_gemm.  Algorithmic bytes: every operand byte
-    (codes and scales) read once, the output written once."""
+    (codes and scales) read once, the output written once.  The NN call is
+    two dispatches: the full rounds of 256 x 256 tiles and the tail's 128 x
+    128 tiles."""
     xg, counts = W.moe_grouped()
     gl = torch.from_numpy(counts).cuda()
     R, K = xg.shape
@@ -906,7 +908,8 @@ def profile_gemm(M, W, torch, run):
     cs = [torch.empty((R, N), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
     run("grouped matmul NN forward: MXFP8 tokens x K-major MXFP4 experts", "mxgemm_kernel",
         [lambda i=i: M.mxfp4_grouped_matmul(q8[i], s8[i], bw, sw, cs[i], group_list=gl, group_list_type=1)
-         for i in range(2)], R * K * (1 + 1 / 32) + G * N * K * (0.5 + 1 / 32), R * N * 2, R * K, flops=flops)
+         for i in range(2)], R * K * (1 + 1 / 32) + G * N * K * (0.5 + 1 / 32), R * N * 2, R * K, flops=flops,
+        per_call=2)
     del cs, q8, s8
     gen = torch.Generator(device="cuda").manual_seed(7)
     dq = torch.randint(0, 256, (R, N), dtype=torch.uint8, device="cuda", generator=gen) & 0xBF
@@ -1030,7 +1033,7 @@ def summarize(kind, dirpath, manifest_path, out_md, command):
     assigned to the manifest's workloads by their launch counts (warm-up
     launches are left out of the table).  The trace table lists per workload
     the kernel, the average duration and GB/s / fraction of peak; the counter
-    table lists the counters per dispatch, and with FETCH_SIZE and WRITE_SIZE
+    table lists the counters per call (summed over a call's dispatches), and with FETCH_SIZE and WRITE_SIZE
     the HBM bytes scaled by the calibration copy (its measured read / write
     bytes over its counters) next to the algorithmic bytes.  A JSON file with
     the same numbers is written beside OUT_MD."""
@@ -1088,8 +1091,21 @@ def summarize(kind, dirpath, manifest_path, out_md, command):
         for e, chunk in groups:
             kern = "; ".join(sorted({short_name(c[0]) for c in chunk}))
             us = np.array([c[1] for c in chunk]) / 1e3
-            if e.get("kernels_per_call", 1) > 1:
-                step = us.reshape(-1, e["kernels_per_call"]).sum(axis=1)
+            kpc = e.get("kernels_per_call", 1)
+            if kpc > 1 and e.get("flops"):
+                # one call = several dispatches (the matmul's full rounds and its tail)
+                call = us.reshape(-1, kpc).sum(axis=1)
+                parts = " + ".join(f"{v:.2f}" for v in us.reshape(-1, kpc).mean(axis=0))
+                tf = e["flops"] / (call.mean() * 1e-6) / 1e12
+                lines.append(f"| {e['label']} | {kern} | {len(chunk)} | {call.mean():.2f} per call ({parts}) | "
+                             f"{call.min():.2f} per call | {e['alg_bytes'] / 1e6:.1f} | {tf:.1f} TFLOP/s | "
+                             f"{tf / MFMA_FP8_PEAK_TFLOPS:.3f} |")
+                js.append({"label": e["label"], "kernel": kern, "avg_us": float(call.mean()),
+                           "avg_us_by_dispatch": [float(v) for v in us.reshape(-1, kpc).mean(axis=0)],
+                           "alg_bytes": e["alg_bytes"], "flops": e["flops"], "TFLOPs": tf,
+                           "frac": tf / MFMA_FP8_PEAK_TFLOPS})
+            elif kpc > 1:
+                step = us.reshape(-1, kpc).sum(axis=1)
                 lines.append(f"| {e['label']} | {kern} | {len(chunk)} | {step.mean():.2f} per step "
                              f"({us.mean():.2f} per launch) | {step.min():.2f} per step | — | — | launch-bound |")
                 js.append({"label": e["label"], "kernel": kern, "step_us": float(step.mean())})
@@ -1108,7 +1124,15 @@ def summarize(kind, dirpath, manifest_path, out_md, command):
                            "alg_bytes": e["alg_bytes"], "GBps": g, "frac": g / HBM_PEAK_GBS})
     else:
         names = sorted({c for d in disp for c in d[2]})
-        mean = lambda chunk, n: float(np.mean([c[2].get(n, np.nan) for c in chunk]))
+        kpc_of = {}
+
+        def mean(chunk, n):
+            # per call: the dispatches of one call summed (one dispatch per call for most workloads)
+            v = np.array([c[2].get(n, np.nan) for c in chunk])
+            k = kpc_of.get(id(chunk), 1)
+            return float(v.reshape(-1, k).sum(axis=1).mean())
+        for e, ch in groups:
+            kpc_of[id(ch)] = e.get("kernels_per_call", 1)
         fs = ws = None
         if "FETCH_SIZE" in names and "WRITE_SIZE" in names:
             cal = [(e, ch) for e, ch in groups if e["label"].startswith("calibration")]
@@ -1122,7 +1146,7 @@ def summarize(kind, dirpath, manifest_path, out_md, command):
         cols = ["Workload", "Kernel", "Launches"]
         if fs is not None:
             cols += ["read MiB", "algorithmic read", "write MiB", "algorithmic write", "traffic / algorithmic"]
-        cols += [f"{n} per dispatch" for n in other]
+        cols += [f"{n} per call" for n in other]
         lines += ["| " + " | ".join(cols) + " |", "|" + "---|" * len(cols)]
         for e, chunk in groups:
             kern = "; ".join(sorted({short_name(c[0]) for c in chunk}))

@@ -19,11 +19,15 @@
 // 0-15 are K 16h..16h+15, bytes 16-31 are K 32+16h..; B fp4: nibble j is K
 // 32h+j; result register v of lane l is row 8(v/4) + 4h + v%4, column l%32).
 //
-// Work split (GemmShape below): with E2M1 B a 512-thread workgroup computes
-// a 256 x 256 tile as 4 x 2 waves of 2 x 4 MFMA tiles (two waves per SIMD, so
-// one wave's LDS and address work overlaps the other's MFMAs); with fp8 B a
-// 256-thread workgroup computes 128 x 128 as 2 x 2 waves of 2 x 2 tiles, two
-// workgroups per CU.  K advances by 128 per step.  Both operand
+// Work split (GemmShape below): a 512-thread workgroup computes a 256 x 256
+// tile as 4 x 2 waves of 2 x 4 MFMA tiles (two waves per SIMD, so one
+// wave's LDS and address work overlaps the other's MFMAs), one workgroup per
+// CU.  A row-split product of at most 8 N-tiles per row whose tiles leave a
+// last round at most half full (with one tile per CU, R tiles = full rounds
+// + R mod CUs) runs the full rounds in one launch, dealt to the XCDs by the
+// real tile count, and the tail in a second launch of 128 x 128 tiles (2 x 2
+// waves of 2 x 2 MFMA tiles, two workgroups per CU), four per big tile, so
+// that the tail spreads over more CUs.  K advances by 128 per step.  Both operand
 // slices go global -> registers -> LDS (double-buffered, 128-byte rows at a
 // 144-byte stride: conflict-free 16-lane read phases, and every fragment
 // read is a per-lane base plus an immediate) while the previous step's
@@ -43,6 +47,7 @@
 #include "mxfp4_groups.h"
 #include "mxfp4_kernels.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace mxfp4 {
@@ -59,13 +64,18 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // per CU, while its 256 x 256 form spilled; with the scale and address
 // registers trimmed it fits (no scratch) and measured 644 -> 566 us on the
 // MoE weight gradient.
-template <int BF>
+// SMALL: 128 x 128 tiles (2 x 2 waves of 2 x 2 MFMA tiles, 4 waves, two
+// workgroups per CU) for the tail of a row-split product: the last, partly
+// filled round of 256 x 256 tiles, each cut into four.
+template <int BF, bool SMALL = false>
 struct GemmShape {
-  static constexpr int wavesM = 4, wavesN = 2, tilesM = 2, tilesN = 4;
+  static constexpr int wavesM = SMALL ? 2 : 4, wavesN = 2, tilesM = 2, tilesN = SMALL ? 2 : 4;
   static constexpr int threads = 64 * wavesM * wavesN;
   static constexpr int BM = 32 * tilesM * wavesM, BN = 32 * tilesN * wavesN;
-  static constexpr int per_cu = 1;  // workgroups per CU
+  static constexpr int per_cu = SMALL ? 2 : 1;  // workgroups per CU
 };
+// Row-split products are tiled in 256 x 256 units whatever the shape.
+constexpr int kBigLog = 8;
 
 struct GemmArgs {
   const uint8_t *a, *as, *b, *bs;
@@ -78,6 +88,7 @@ struct GemmArgs {
   int a_sb, b_sb;        // log2(scale block / 32): 0 or 2
   int s4;                // both scale arrays have dword-aligned rows: dword slice loads
   int c16;               // bf16 output with 16-byte aligned rows: whole tiles stored through LDS
+  int ncu;               // compute units of the device (row-split tail decision)
   int64_t tiles_m, tiles_n, total;
 };
 
@@ -112,15 +123,26 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t id, int64_t total) {
   return x < r ? x * (q + 1) + loc : r * (q + 1) + (x - r) * q + loc;
 }
 
+// Workgroup id -> slot in [0, total) with each XCD given a contiguous, equal
+// share (ids beyond an XCD's share return false).  Unlike xcd_tile, total is
+// the count known only on the device, so the grid may be larger.
+__device__ __forceinline__ bool xcd_slot(int64_t id, int64_t total, int64_t *slot) {
+  const int64_t q = total >> 3, r = total & 7;
+  const int64_t x = id & 7, loc = id >> 3;
+  if (loc >= (x < r ? q + 1 : q)) return false;
+  *slot = x < r ? x * (q + 1) + loc : r * (q + 1) + (x - r) * q + loc;
+  return true;
+}
+
 // One scaled MFMA taking byte OS of each scale register.
 template <int AF, int BF, int OS>
 __device__ __forceinline__ v16f mfma_sel(v8i a, v8i b, v16f c, uint32_t sa, uint32_t sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, AF, BF, OS, (int)sa, OS, (int)sb);
 }
 
-template <int AF, int BF, bool S4>
-__global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void mxgemm_kernel(GemmArgs P) {
-  using Sh = GemmShape<BF>;
+template <int AF, int BF, bool S4, bool SMALL>
+__global__ __launch_bounds__((GemmShape<BF, SMALL>::threads), (GemmShape<BF, SMALL>::per_cu)) void mxgemm_kernel(GemmArgs P) {
+  using Sh = GemmShape<BF, SMALL>;
   constexpr int WVM = Sh::wavesM, WVN = Sh::wavesN, WM = Sh::tilesM, WN = Sh::tilesN;
   constexpr int NT = Sh::threads;
   constexpr int BM = Sh::BM, BN = Sh::BN;
@@ -143,37 +165,73 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  const int64_t tile = xcd_tile(blockIdx.x, P.total);
 
   // ---- tile -> rows, columns, K range, operand and output bases ----
   int64_t m0, mlen, n0, kb0, kb1, klo = 0;  // steps start at kb0; blocks below klo are masked
   const uint8_t *bbase = P.b, *bsbase = P.bs;
   int64_t cbase = 0;  // element offset of the output matrix
   if (P.group_type == 0) {
-    // a row of more than 8 N-tiles (NT: 28) goes in bands of 4 M-tiles (its
-    // weight re-reads 9.0x -> 5.4x the unique bytes, time unchanged); 8 or
-    // fewer (NN) keep the row order, whose re-reads are lower (2.0x vs 2.7x)
-    int64_t tm, tn;
-    if (P.tiles_n > 8) {
-      band_tile(tile, P.tiles_m, P.tiles_n, 4, &tm, &tn);
+    // The grid is sized for an upper bound of the 256 x 256 tiles.  Rows of
+    // at most 8 N-tiles (NN on the MoE layer) are walked in row order: the
+    // groups give the real tile count R; with one big tile per CU, R = full
+    // rounds + a tail T = R mod CUs, and a tail of at most half a round goes
+    // to the SMALL launch as four 128 x 128 tiles per big tile while the other
+    // tiles are dealt to the XCDs in equal contiguous shares of the real
+    // count.  Rows of more than 8 N-tiles (NT: 28) go in bands of 4 M-tiles
+    // over the upper bound (weight re-reads 9.0x -> 5.4x the unique bytes,
+    // time unchanged), dealt by xcd_tile, with no tail launch: the tail
+    // split measured 2 % slower there (NT on the MoE layer 526 -> 537 us).
+    int64_t v, sub = 0, tm, tn;
+    if (P.tiles_n <= 8) {
+      int64_t rm;
+      if (P.gl) {
+        int64_t before, last;
+        group_block_span(P.gl, P.G, P.list_type, P.M, kBigLog, P.G - 1, &before, &last);
+        rm = before + last;
+      } else {
+        rm = (P.M + 255) >> kBigLog;
+      }
+      const int64_t R = rm * P.tiles_n;
+      const int64_t T = R % P.ncu;
+      const bool split = T > 0 && 2 * T <= P.ncu;
+      const int64_t DP = split ? R - T : R;
+      if (!SMALL) {
+        if (!xcd_slot(blockIdx.x, DP, &v)) return;
+      } else {
+        int64_t s;
+        if (!split || !xcd_slot(blockIdx.x, 4 * T, &s)) return;
+        v = DP + (s >> 2);
+        sub = s & 3;
+      }
+      tm = v / P.tiles_n;
+      tn = v - tm * P.tiles_n;
     } else {
-      tm = tile / P.tiles_n;
-      tn = tile - tm * P.tiles_n;
+      if (SMALL) return;
+      v = xcd_tile(blockIdx.x, P.total);
+      band_tile(v, P.tiles_m, P.tiles_n, 4, &tm, &tn);
     }
-    n0 = tn * BN;
+    n0 = tn << kBigLog;
     int g = 0;
     if (P.gl) {
-      block_row_uniform<false>(P.gl, P.G, P.list_type, P.M, __builtin_ctz(BM), tm, &m0, &mlen, &g);
+      block_row_uniform<false>(P.gl, P.G, P.list_type, P.M, kBigLog, tm, &m0, &mlen, &g);
     } else {
-      m0 = tm * BM;
-      mlen = P.M - m0 < BM ? P.M - m0 : BM;
+      m0 = tm << kBigLog;
+      mlen = P.M - m0 < 256 ? P.M - m0 : 256;
     }
-    if (mlen <= 0) return;  // past the groups' total (workgroup-uniform)
+    if (SMALL) {
+      m0 += BM * (sub >> 1);
+      mlen -= BM * (sub >> 1);
+      mlen = mlen < BM ? mlen : BM;
+      n0 += BN * (sub & 1);
+    }
+    if (mlen <= 0 || n0 >= P.N) return;  // workgroup-uniform
     bbase += (int64_t)g * P.b_gs;
     bsbase += (int64_t)g * P.b_gss;
     kb0 = 0;
     kb1 = (P.K + 31) >> 5;
   } else {
+    if (SMALL) return;  // K-split products are launched with the 256 x 256 shape only
+    const int64_t tile = xcd_tile(blockIdx.x, P.total);
     const int64_t per = P.tiles_m * P.tiles_n;
     const int g = (int)(tile / per);
     const int64_t r = tile - (int64_t)g * per;
@@ -477,27 +535,28 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   };
   const int64_t cb = cbase + m0 * P.ldc + n0;
   if (P.c16 && mlen == BM && nlen == BN) {
-    // bf16 tile staged in LDS (rows 0-127 in the A buffers, 128-255 in the B
-    // buffers, 528-byte row stride) and written as 16-byte row pieces: 16
-    // stores per lane instead of 128 two-byte ones
-    constexpr int OS = 528;
+    // bf16 tile staged in LDS (the first half of the rows in the A buffers,
+    // the second in the B buffers, rows of 2 * BN + 16 bytes) and written as
+    // 16-byte row pieces: 16 stores per lane instead of 128 two-byte ones
+    constexpr int OS = 2 * BN + 16, HR = BM / 2, CH = BN / 8, RPI = NT / CH;
+    static_assert(HR * OS <= 2 * BM * RS && HR * OS <= 2 * BN * RS && BM % RPI == 0, "output staging");
     __syncthreads();  // every wave is past its last fragment read
-    uint8_t *half = wr0 < 128 ? &sA[0][0] : &sB[0][0];
+    uint8_t *half = wr0 < HR ? &sA[0][0] : &sB[0][0];
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
       for (int j = 0; j < WN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int r = (wr0 & 127) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          const int r = (wr0 & (HR - 1)) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
           *reinterpret_cast<uint16_t *>(half + r * OS + 2 * (wc0 + 32 * j + l32)) = f32_to_bf16_rne(acc[i][j][v]);
         }
     __syncthreads();
-    const int ch = tid & 31;
+    const int ch = tid % CH;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int row = (tid >> 5) + 16 * k;
-      const uint8_t *src = (k < 8 ? &sA[0][0] : &sB[0][0]) + (row & 127) * OS + 16 * ch;
+    for (int k = 0; k < BM / RPI; ++k) {
+      const int row = tid / CH + RPI * k;
+      const uint8_t *src = (row < HR ? &sA[0][0] : &sB[0][0]) + (row & (HR - 1)) * OS + 16 * ch;
       // non-temporal: the output is not read again by this launch (NN / NT
       // 1-2 % faster on the MoE layer)
       __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(src),
@@ -528,27 +587,59 @@ __global__ __launch_bounds__(GemmShape<BF>::threads, GemmShape<BF>::per_cu) void
   }
 }
 
+template <int AF, int BF, bool SMALL>
+hipError_t gemm_launch_one(const GemmArgs &a, int64_t grid, hipStream_t st) {
+  const dim3 block(GemmShape<BF, SMALL>::threads);
+  if (a.s4)
+    hipLaunchKernelGGL((mxgemm_kernel<AF, BF, true, SMALL>), dim3((unsigned)grid), block, 0, st, a);
+  else
+    hipLaunchKernelGGL((mxgemm_kernel<AF, BF, false, SMALL>), dim3((unsigned)grid), block, 0, st, a);
+  return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int AF, int BF>
 hipError_t gemm_launch(const GemmArgs &a0, hipStream_t st) {
   GemmArgs a = a0;
-  const int64_t BM = GemmShape<BF>::BM, BN = GemmShape<BF>::BN;
-  const dim3 block(GemmShape<BF>::threads);
+  constexpr int64_t BM = GemmShape<BF>::BM, BN = GemmShape<BF>::BN;
+  static_assert(BM == 256 && BN == 256, "row-split tiles are 256 x 256 units");
   a.tiles_n = (a.N + BN - 1) / BN;
   if (a.group_type == 0) {
     // upper bound of the M tiles: every group adds at most one partial tile
     a.tiles_m = (a.M + BM - 1) / BM + (a.gl ? a.G : 0);
     a.total = a.tiles_m * a.tiles_n;
-  } else {
-    a.tiles_m = (a.M + BM - 1) / BM;
-    a.total = a.tiles_m * a.tiles_n * a.G;
+    if (a.total <= 0) return hipSuccess;
+    if (a.total > 0x1FFFFFFF) return hipErrorInvalidValue;
+    a.ncu = device_cus();
+    const int64_t half = a.ncu / 2;
+    // the big tiles (none when even the upper bound is a tail of at most
+    // half a round), then, for rows of at most 8 N-tiles, the tail's small
+    // tiles: 4 per big tile, at most half a round of big tiles (workgroups
+    // without a tile return at once)
+    if (a.total > half || a.tiles_n > 8) {
+      const hipError_t e = gemm_launch_one<AF, BF, false>(a, a.total, st);
+      if (e != hipSuccess) return e;
+    }
+    const int64_t small = 4 * (a.total < half ? a.total : half);
+    return small > 0 && a.tiles_n <= 8 ? gemm_launch_one<AF, BF, true>(a, small, st) : hipSuccess;
   }
+  a.tiles_m = (a.M + BM - 1) / BM;
+  a.total = a.tiles_m * a.tiles_n * a.G;
   if (a.total <= 0) return hipSuccess;
   if (a.total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (a.s4)
-    hipLaunchKernelGGL((mxgemm_kernel<AF, BF, true>), dim3((unsigned)a.total), block, 0, st, a);
-  else
-    hipLaunchKernelGGL((mxgemm_kernel<AF, BF, false>), dim3((unsigned)a.total), block, 0, st, a);
-  return hipGetLastError();
+  return gemm_launch_one<AF, BF, false>(a, a.total, st);
 }
 
 template <int AF>

@@ -172,6 +172,44 @@ def test_rows_split_group_stride_override(oracle):
     assert np.array_equal(host(c), exp.astype(np.float32))
 
 
+BIG_CASES = [
+    # name, group list (None: one group of M rows), M, N, K, output
+    # With 256 CUs: R 256 x 256 tiles = 300 -> 256 big + a tail of 44 cut in 128 x 128 tiles
+    ("tail_split_rows", [4700, 4600, 4864, 4500, 4790, 4800, 4650, 4400, 250], 37554, 512, 128, "bf16"),
+    # 9 N-tiles: bands of 4 M-tiles over the upper bound, no tail launch (R = 279)
+    ("bands_no_tail", [2600, 0, 3001, 1999], 7600, 2304, 64, "f32"),
+    # R = 202, more than half a round: big tiles only
+    ("no_split_partial_round", [6400, 6000, 6300, 6777], 25477, 512, 64, "bf16"),
+    # no list, a partial last N-tile (44 columns): R = 300 -> 256 + 44
+    ("no_list_split", None, 38323, 300, 96, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", BIG_CASES, ids=[c[0] for c in BIG_CASES])
+def test_rows_split_big_tiles_and_tail(oracle, case):
+    """Row-split products with more 256 x 256 tiles than one round: rows of
+    at most 8 N-tiles deal the big tiles to the XCDs by the real tile count
+    and compute a tail of at most half a round as 128 x 128 tiles in a
+    second launch (past half a round, no tail launch); rows of more N-tiles
+    walk bands over the upper bound.  Every element against the oracle
+    (exact operands: every partial sum is exact in fp32)."""
+    name, gl, M, N, K, out = case
+    g = np.random.default_rng(zlib.crc32(name.encode()))
+    G = 1 if gl is None else len(gl)
+    a, sa = exact_operands(g, M, K, "e4m3", 32)
+    b, sb = exact_operands(g, N, K, "e2m1", 32, groups=G)
+    if gl is None:
+        b, sb = b[0], sb[0]
+    otype = torch.float32 if out == "f32" else torch.bfloat16
+    got = run_rows(a, sa, b, sb, M, N, K, gl, 1, "e4m3", "e2m1", 32, 32, otype)
+    exp = oracle_rows(oracle, a, sa, b, sb, M, N, K, gl, 1, "e4m3", "e2m1", 32, 32)
+    assert not np.isnan(exp).any()
+    if out == "f32":
+        assert np.array_equal(got, exp.astype(np.float32))
+    else:
+        assert np.array_equal(got, bf16_of(exp))
+
+
 # ---- K-split groups (TN) --------------------------------------------------------
 
 MULTI_CHUNK_CASES = [
