@@ -182,6 +182,10 @@ BIG_CASES = [
     ("no_split_partial_round", [6400, 6000, 6300, 6777], 25477, 512, 64, "bf16"),
     # no list, a partial last N-tile (44 columns): R = 300 -> 256 + 44
     ("no_list_split", None, 38323, 300, 96, "f32"),
+    # 40 groups (the wave-scan walk of lists longer than 32): R = 320 -> 256 + 64
+    ("forty_groups_split", "forty", 40000, 512, 64, "bf16"),
+    # cumulative ends (group_list_type 0), the first case's list
+    ("tail_split_ends", "ends", 37554, 512, 64, "f32"),
 ]
 
 
@@ -195,14 +199,20 @@ def test_rows_split_big_tiles_and_tail(oracle, case):
     (exact operands: every partial sum is exact in fp32)."""
     name, gl, M, N, K, out = case
     g = np.random.default_rng(zlib.crc32(name.encode()))
+    lt = 1
+    if gl == "forty":
+        gl = [1000 + (37 * i) % 23 - 11 for i in range(40)]
+        gl[-1] += M - sum(gl)
+    elif gl == "ends":
+        gl, lt = np.cumsum(BIG_CASES[0][1]).tolist(), 0
     G = 1 if gl is None else len(gl)
     a, sa = exact_operands(g, M, K, "e4m3", 32)
     b, sb = exact_operands(g, N, K, "e2m1", 32, groups=G)
     if gl is None:
         b, sb = b[0], sb[0]
     otype = torch.float32 if out == "f32" else torch.bfloat16
-    got = run_rows(a, sa, b, sb, M, N, K, gl, 1, "e4m3", "e2m1", 32, 32, otype)
-    exp = oracle_rows(oracle, a, sa, b, sb, M, N, K, gl, 1, "e4m3", "e2m1", 32, 32)
+    got = run_rows(a, sa, b, sb, M, N, K, gl, lt, "e4m3", "e2m1", 32, 32, otype)
+    exp = oracle_rows(oracle, a, sa, b, sb, M, N, K, gl, lt, "e4m3", "e2m1", 32, 32)
     assert not np.isnan(exp).any()
     if out == "f32":
         assert np.array_equal(got, exp.astype(np.float32))
