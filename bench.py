@@ -1194,6 +1194,50 @@ def traffic_json(summary_json, out_path):
     print(json.dumps(out))
 
 
+def summarize_bench_trace(dirpath, bench_json, out_md, command):
+    """A rocprofv3 kernel trace of the plain bench command, per kernel and
+    launch size (grid x workgroup): launches, average / median / min
+    duration; beside it the bench line's own event timing of its roofline
+    kernel, which the trace's average for that kernel at the headline size
+    should match."""
+    rows = [r for r in _read_csv(_find(dirpath, "kernel_trace.csv")) if _ours(r["Kernel_Name"])]
+    groups = {}
+    for r in rows:
+        key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    line = None
+    if bench_json:
+        with open(bench_json) as f:
+            for ln in f:
+                if ln.startswith("{"):
+                    line = json.loads(ln)
+    lines = ["# rocprofv3 kernel trace of the bench command", "",
+             "MI355X, ROCm 7.2.  Every launch of this library's kernels during the default bench run "
+             "(headline steps, the roofline kernel's timing launches, the steady-state and config "
+             "workloads, the streaming probes), grouped by kernel and launch size.", "",
+             "Command (repository root):", "", f"    {command}", ""]
+    if line:
+        rf = line["roofline"]
+        us = rf["alg_bytes_per_launch"] / (rf["achieved"] * 1e3)
+        lines += [f"The bench line of this run: value {line['value']} {line['unit']}, {line['ms_per_step'] * 1e3:.2f} "
+                  f"us per step; roofline kernel `{rf['kernel']}` {us:.2f} us per launch by HIP events "
+                  f"({rf['achieved']} GB/s, frac {rf['frac']}).", ""]
+    lines += ["| Kernel | Grid (threads) | Workgroup | Launches | Average us | Median us | Min us |",
+              "|---|---|---|---|---|---|---|"]
+    js = []
+    for (k, g, w), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        a = np.array(v)
+        lines.append(f"| {k} | {g} | {w} | {len(a)} | {a.mean():.2f} | {np.median(a):.2f} | {a.min():.2f} |")
+        js.append({"kernel": k, "grid": g, "workgroup": w, "launches": len(a), "avg_us": float(a.mean()),
+                   "median_us": float(np.median(a)), "min_us": float(a.min())})
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.splitext(out_md)[0] + ".json", "w") as f:
+        json.dump({"command": command, "kernel_source_sha": kernel_source_sha(), "bench_line": line, "rows": js},
+                  f, indent=1)
+    print("\n".join(lines))
+
+
 def short_name(name: str) -> str:
     """Kernel name without return type, namespaces and parameter list."""
     s = name.split(" [clone")[0].replace("(anonymous namespace)::", "").replace("mxfp4::", "")
@@ -1335,6 +1379,9 @@ def main():
     ap.add_argument("--summarize", nargs=4, metavar=("KIND", "DIR", "MANIFEST", "OUT_MD"), default=None,
                     help="join a rocprofv3 CSV (KIND trace or pmc) under DIR with the manifest into OUT_MD")
     ap.add_argument("--command", default="", help="the profiling command, recorded by --summarize")
+    ap.add_argument("--summarize-bench-trace", nargs=3, metavar=("DIR", "BENCH_JSON", "OUT_MD"), default=None,
+                    help="a rocprofv3 kernel trace of the plain bench command (DIR) with its JSON line "
+                         "(BENCH_JSON) into OUT_MD, per kernel and launch size")
     ap.add_argument("--traffic-json", nargs=2, metavar=("SUMMARY_JSON", "OUT"), default=None,
                     help="write the headline forward's traffic file from a counter summary")
     ap.add_argument("--stamps", metavar="OUT", default=None,
@@ -1351,6 +1398,9 @@ def main():
     if args.summarize:
         kind, d, man, out = args.summarize
         summarize(kind, d, man, out, args.command)
+        return
+    if args.summarize_bench_trace:
+        summarize_bench_trace(*args.summarize_bench_trace, args.command)
         return
     if args.traffic_json:
         traffic_json(*args.traffic_json)
