@@ -79,3 +79,28 @@ def test_counter_summary_and_traffic(tmp_path):
     bench.traffic_json(str(tmp_path / "c.json"), str(tmp_path / "traffic.json"))
     t = json.loads((tmp_path / "traffic.json").read_text())
     assert t["traffic_bytes_per_launch"] == 8448 and t["kernel_source_sha"] == bench.kernel_source_sha()
+
+
+def test_bench_trace_summary(tmp_path):
+    """The plain bench command's trace: this library's launches grouped by
+    kernel and launch size (torch's left out), with the bench line's own
+    roofline timing quoted beside them."""
+    rows, t = [], 1000
+    for name, grid, wg, dur in [(FWD, 2097152, 64, 12000), (TORCH, 64, 64, 5), (FWD, 2097152, 64, 14000),
+                                (FWD, 29360128, 64, 145000), (COPY, 256, 256, 700)]:
+        rows.append([name, grid, wg, t, t + dur])
+        t += 200000
+    write_csv(str(tmp_path / "tr" / "h" / "x_kernel_trace.csv"),
+              ["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp"], rows)
+    line = {"value": 5400.0, "unit": "GB/s", "ms_per_step": 0.0254,
+            "roofline": {"kernel": "row_fwd", "achieved": 5300.0, "alg_bytes_per_launch": 69206016.0,
+                         "frac": 0.6625}}
+    (tmp_path / "b.json").write_text("warm-up text\n" + json.dumps(line) + "\n")
+    out = tmp_path / "bt.md"
+    bench.summarize_bench_trace(str(tmp_path / "tr"), str(tmp_path / "b.json"), str(out), "cmd")
+    d = json.loads((tmp_path / "bt.json").read_text())
+    by = {(r["kernel"], r["grid"]): r for r in d["rows"]}
+    assert len(by) == 3                                   # two sizes of the forward, the probe; no torch
+    small = by[("row_fwd_kernel<1, 32, 0, 0, 1, 64>", 2097152)]
+    assert small["launches"] == 2 and abs(small["avg_us"] - 13.0) < 1e-9
+    assert "13.06 us per launch by HIP events" in out.read_text()   # 69206016 B / 5300 GB/s
