@@ -72,7 +72,11 @@ struct GemmShape {
   static constexpr int wavesM = SMALL ? 2 : 4, wavesN = 2, tilesM = 2, tilesN = SMALL ? 2 : 4;
   static constexpr int threads = 64 * wavesM * wavesN;
   static constexpr int BM = 32 * tilesM * wavesM, BN = 32 * tilesN * wavesN;
-  static constexpr int per_cu = SMALL ? 2 : 1;  // workgroups per CU
+  // minimum waves per SIMD (the second __launch_bounds__ argument): the
+  // 256 x 256 workgroup already puts two on each SIMD; a SMALL workgroup has
+  // one per SIMD, and 2 keeps its registers low enough for two workgroups
+  // per CU (80 KiB of LDS each)
+  static constexpr int per_cu = SMALL ? 2 : 1;
 };
 // Row-split products are tiled in 256 x 256 units whatever the shape.
 constexpr int kBigLog = 8;
