@@ -159,6 +159,8 @@ class Probe:
         self.lib.probe_cu_rate.argtypes = [ctypes.c_int, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                            vp, vp]
         self.lib.probe_cu_rate.restype = ctypes.c_int
+        self.lib.probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+        self.lib.probe_mfma_rate.restype = ctypes.c_int
 
     def cu_rate(self, kind, buf, win, nwin, passes, nwg, out, stream):
         vp = ctypes.c_void_p
@@ -1251,6 +1253,65 @@ def short_name(name: str) -> str:
     return s.strip()
 
 
+def mfma_probe(torch, stream, probe, out_md, command):
+    """Matrix-core rate with no memory traffic (probe_mfma_rate: 8 independent
+    scaled MFMAs per wave and round, register operands), one 512-thread
+    workgroup per CU or on 32 CUs, for about 1 ms and 10 ms, fp8 x fp8 and
+    fp8 x E2M1: TFLOP/s by HIP events (median of three) and the shader clock
+    from the workgroups' s_memtime / s_memrealtime deltas."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    flop_mfma = 2.0 * 32 * 32 * 64
+    rows = []
+    for fmt, fname in ((0, "fp8 x fp8"), (4, "fp8 x E2M1")):
+        for nwg, load in ((ncu, f"{ncu} CUs"), (32, "32 CUs")):
+            for iters in (2400, 24000):
+                out = torch.empty(nwg * 512, dtype=torch.float32, device="cuda")
+                clk = torch.zeros(3 * nwg, dtype=torch.int64, device="cuda")
+                vp = ctypes.c_void_p
+
+                def run():
+                    st = probe.lib.probe_mfma_rate(fmt, iters, nwg, vp(out.data_ptr()), vp(clk.data_ptr()), stream)
+                    if st != 0:
+                        raise RuntimeError(f"probe_mfma_rate failed with hip error {st}")
+                run()
+                torch.cuda.synchronize()
+                ts = []
+                for _ in range(3):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    run()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1) * 1e3)
+                us = sorted(ts)[1]
+                c = clk.cpu().numpy().reshape(nwg, 3).astype(np.float64)
+                mhz = c[:, 0] / (c[:, 1] / 100.0)
+                flops = nwg * 8 * iters * 8 * flop_mfma
+                tf = flops / (us * 1e-6) / 1e12
+                rows.append({"operands": fname, "workgroups": nwg, "load": load, "rounds": iters, "us": round(us, 1),
+                             "TFLOPs": round(tf, 1), "per_CU_fraction_of_2p4GHz_peak":
+                             round(tf / (MFMA_FP8_PEAK_TFLOPS * nwg / ncu), 4),
+                             "clock_MHz_median": round(float(np.median(mhz)), 1),
+                             "clock_MHz_min": round(float(mhz.min()), 1)})
+                print(json.dumps(rows[-1]), flush=True)
+    lines = ["# Matrix-core rate and shader clock with no memory traffic", "",
+             "MI355X, ROCm 7.2.  `probe_mfma_rate` (libmxfp4_probe.so): 512-thread workgroups, one per CU, each wave "
+             "issuing rounds of 8 independent `v_mfma_scale_f32_32x32x64_f8f6f4` on register operands; TFLOP/s by HIP "
+             "events (median of three launches), the shader clock from each workgroup's s_memtime / s_memrealtime "
+             "(100 MHz) deltas.  The fraction is of the 5.0 PFLOP/s dense fp8 figure scaled to the CUs used.", "",
+             "Command (repository root):", "", f"    {command}", "",
+             "| Operands | Workgroups | Rounds | us | TFLOP/s | Fraction of peak (CUs used) | Clock MHz (median) | Clock MHz (min) |",
+             "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['operands']} | {r['workgroups']} | {r['rounds']} | {r['us']} | {r['TFLOPs']} | "
+                     f"{r['per_CU_fraction_of_2p4GHz_peak']} | {r['clock_MHz_median']} | {r['clock_MHz_min']} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.splitext(out_md)[0] + ".json", "w") as f:
+        json.dump({"command": command, "rows": rows}, f, indent=1)
+    print("\n".join(lines))
+
+
 def cu_probes(torch, stream, probe, out_md, command):
     """Per-CU rates of the memory paths a tiled matmul uses, one 512-thread
     workgroup per CU (256 workgroups): 16-byte loads from an L2-resident
@@ -1388,6 +1449,8 @@ def main():
                     help="per-workgroup clocks of the forward-pattern probe at 4096x4096")
     ap.add_argument("--cu-probes", metavar="OUT_MD", default=None,
                     help="per-CU rates of L2 / HBM loads and LDS reads / writes (the matmul's memory paths)")
+    ap.add_argument("--mfma-probe", metavar="OUT_MD", default=None,
+                    help="matrix-core rate and shader clock with register operands (no memory traffic)")
     ap.add_argument("--probe-sweep", metavar="OUT", default=None,
                     help="streaming probes over launch shapes at 4096x4096 and 28672x8192")
     args = ap.parse_args()
@@ -1439,6 +1502,10 @@ def main():
         return
     if args.cu_probes:
         cu_probes(torch, stream, probe, args.cu_probes, args.command or f"python3 bench.py --cu-probes {args.cu_probes}")
+        return
+    if args.mfma_probe:
+        mfma_probe(torch, stream, probe, args.mfma_probe,
+                   args.command or f"python3 bench.py --mfma-probe {args.mfma_probe}")
         return
 
     result, wk = bench_headline(M, lib, W, torch, stream, args, probe)

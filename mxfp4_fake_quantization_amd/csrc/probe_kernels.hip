@@ -233,3 +233,65 @@ extern "C" int probe_cu_rate(int kind, const void *buf, int64_t win, int64_t nwi
   }
   return (int)hipGetLastError();
 }
+
+// ---- matrix-core rate and shader clock ---------------------------------------
+// 512-thread workgroups (two waves per SIMD, one workgroup per CU), each wave
+// issuing `iters` rounds of 8 independent v_mfma_scale_f32_32x32x64_f8f6f4
+// (fp8 A; fp8 or E2M1 B as fmt_b 0 / 4; operands in registers, E8M0 scales
+// 2^0), so the matrix cores stay busy with no memory traffic.  Thread 0 of
+// each workgroup writes its shader-clock cycles (s_memtime) and 100 MHz
+// ticks (s_memrealtime) from start to end, and the start tick, to
+// clocks[3 * blockIdx.x ...]; every lane adds its accumulators to out so that
+// no MFMA is dead.  The values stay finite: products of codes below 2 in
+// magnitude, at most 2^31 of them per accumulator.
+namespace {
+
+typedef int v8i_p __attribute__((ext_vector_type(8)));
+typedef float v16f_p __attribute__((ext_vector_type(16)));
+
+template <int BF>
+__global__ __launch_bounds__(512, 1) void mfma_rate_kernel(int iters, float *__restrict__ out,
+                                                          unsigned long long *__restrict__ clocks) {
+  const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  const int tid = threadIdx.x;
+  // E4M3 codes 0x30..0x37 (0.5 .. 0.94) and E2M1 codes 1..3 (0.5 .. 1.5), by lane
+  const int av = 0x30303030 + 0x01010101 * (tid & 7);
+  const int bv = BF == 4 ? 0x21212121 + 0x01010101 * ((tid >> 3) & 1) : av;
+  v8i_p a = {av, av, av, av, av, av, av, av};
+  v8i_p b = {bv, bv, bv, bv, bv, bv, bv, bv};
+  v16f_p acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[j], 0, BF, 0, 127, 0, 127);
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sum += acc[j][v];
+  out[(int64_t)blockIdx.x * 512 + tid] = sum;
+  if (tid == 0) {
+    const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    clocks[3 * blockIdx.x] = c1 - c0;
+    clocks[3 * blockIdx.x + 1] = r1 - r0;
+    clocks[3 * blockIdx.x + 2] = r0;
+  }
+}
+
+}  // namespace
+
+// fmt_b 0 (fp8 B) or 4 (E2M1 B); out: nwg * 512 floats; clocks: 3 * nwg
+// 64-bit words.  Returns a hipError_t value (0 on success).
+extern "C" int probe_mfma_rate(int fmt_b, int iters, int nwg, void *out, void *clocks, void *stream) {
+  if (nwg <= 0 || iters < 0 || !out || !clocks || (fmt_b != 0 && fmt_b != 4)) return (int)hipErrorInvalidValue;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float *o = static_cast<float *>(out);
+  unsigned long long *c = static_cast<unsigned long long *>(clocks);
+  if (fmt_b == 4) hipLaunchKernelGGL(mfma_rate_kernel<4>, dim3(nwg), dim3(512), 0, st, iters, o, c);
+  else hipLaunchKernelGGL(mfma_rate_kernel<0>, dim3(nwg), dim3(512), 0, st, iters, o, c);
+  return (int)hipGetLastError();
+}
