@@ -625,7 +625,7 @@ hipError_t gemm_launch(const GemmArgs &a0, hipStream_t st) {
     a.tiles_m = (a.M + BM - 1) / BM + (a.gl ? a.G : 0);
     a.total = a.tiles_m * a.tiles_n;
     if (a.total <= 0) return hipSuccess;
-    if (a.total > 0x1FFFFFFF) return hipErrorInvalidValue;
+    if (a.total > 0x7FFFFFFF) return hipErrorInvalidValue;
     a.ncu = device_cus();
     const int64_t half = a.ncu / 2;
     // the big tiles (none when even the upper bound is a tail of at most
