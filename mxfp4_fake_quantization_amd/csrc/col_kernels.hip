@@ -42,6 +42,12 @@ enum { kKindCol = 0, kKindDual = 1, kKindGrouped = 2 };
 #define MXFP4_GROUPED_MINWG 4
 #endif
 constexpr int kWaveCols = 128;
+// Waves side by side in a block-32 workgroup (each 32 rows x 128 columns).
+#ifndef MXFP4_COL_WX
+#define MXFP4_COL_WX 4
+#endif
+template <int B>
+constexpr int col_threads() { return B == 32 ? 64 * MXFP4_COL_WX : 256; }
 
 struct ColArgs {
   const uint8_t *x;
@@ -166,13 +172,13 @@ __device__ __forceinline__ void col_outputs(const ColArgs &A, const uint32_t (&w
 }
 
 template <int DT, int B, int RULE, int KIND, bool VEC>
-__global__ __launch_bounds__(kThreads, KIND == kKindDual      ? MXFP4_DUAL_MINWG
+__global__ __launch_bounds__(col_threads<B>(), KIND == kKindDual      ? MXFP4_DUAL_MINWG
                                        : KIND == kKindGrouped ? MXFP4_GROUPED_MINWG
                                                               : MXFP4_COL_MINWG)
 void col_fwd_kernel(ColArgs A) {
   constexpr int NW = ColT<DT>::NW;
   constexpr int ES = ColT<DT>::ES;
-  constexpr int WX = B == 32 ? 4 : 1;  // waves side by side
+  constexpr int WX = B == 32 ? MXFP4_COL_WX : 1;  // waves side by side
   constexpr int G_ROW = B / 8;         // lanes per row-wise block (dual)
 
   const int tid = threadIdx.x;
@@ -349,8 +355,8 @@ void col_fwd_kernel(ColArgs A) {
 
 template <int DT, int B, int RULE, int KIND>
 hipError_t launch_kind(bool vec, const ColArgs &a, dim3 grid, hipStream_t st) {
-  if (vec) hipLaunchKernelGGL((col_fwd_kernel<DT, B, RULE, KIND, true>), grid, dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL((col_fwd_kernel<DT, B, RULE, KIND, false>), grid, dim3(kThreads), 0, st, a);
+  if (vec) hipLaunchKernelGGL((col_fwd_kernel<DT, B, RULE, KIND, true>), grid, dim3(col_threads<B>()), 0, st, a);
+  else hipLaunchKernelGGL((col_fwd_kernel<DT, B, RULE, KIND, false>), grid, dim3(col_threads<B>()), 0, st, a);
   return hipGetLastError();
 }
 
@@ -383,7 +389,7 @@ hipError_t launch_col_fwd(const ColLaunch &L, hipStream_t st) {
   a.group_list = L.group_list;
   a.rows = L.rows;
   a.cols = L.cols;
-  const int64_t tile_cols = L.block == 32 ? 4 * kWaveCols : kWaveCols;
+  const int64_t tile_cols = L.block == 32 ? MXFP4_COL_WX * kWaveCols : kWaveCols;
   a.nct = (L.cols + tile_cols - 1) / tile_cols;
   a.nw_row = (L.cols + 31) / 32;
   a.nb_row = (L.cols + L.block - 1) / L.block;
