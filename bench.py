@@ -5,6 +5,8 @@
     python bench.py --profile-run MANIFEST.json      (fixed launch sequence for rocprofv3)
     python bench.py --summarize KIND DIR MANIFEST.json OUT.md   (rocprofv3 CSV -> table)
     python bench.py --stamps OUT.json                (per-workgroup start / end clocks)
+    python bench.py --summarize-bench-trace DIR BENCH_JSON OUT.md   (trace of the plain bench command)
+    python bench.py --mfma-probe OUT.md              (matrix-core rate and shader clock, no memory traffic)
 
 One step = the whole hot path over one batch of the weight_4k workload: bf16
 4096x4096 weight (N(0, 0.02^2), outliers, zero blocks, planted blocks),
